@@ -1,0 +1,141 @@
+/*
+ * sv_oracle.h -- CPU oracle for batched speculative-sampling verification.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This header and sv_oracle.c are the plain, slow,
+ * double-precision definition that the GPU library is checked against.  Only
+ * the test-suite, the smoke check and the benchmark's CPU-baseline leg may
+ * load it.  The GPU library shares no code, header, table or constant with it.
+ *
+ * Sources (web pages on the subject; cited by title and section):
+ *  [DScale]  "DScale: Scaling Block-Diffusion Speculative Decoding with
+ *            Adaptive Verification", abstract (aiqbench.com / arxivdaily.com):
+ *            dynamic verify-length (DVL) allocation of scored prefixes into
+ *            half the native verification capacity; fixed-address workspaces.
+ *  [DBLast]  "Pith review of DBLAST: Dependent Block Drafting for Stochastic
+ *            Speculative Decoding" (pith.science):
+ *              - "What carries the argument": latent-mixture proposal
+ *                q_dep(x_1:b|y) = sum_z q(z|y) prod_i q_i(x_i|y,z); a category
+ *                is sampled, its branch decoded greedily, and verification
+ *                conditions on the accepted prefix through the category
+ *                posterior.
+ *              - "Assumptions & free parameters": speculative sampling with
+ *                rejection correction keeps the target distribution for any
+ *                proposal q.
+ *              - "What would settle it": target sampling at T = 1.5, top-p 0.95.
+ *              - Referee report, minor comment 5: experiments use the
+ *                conditional of Eq. (20) (greedy-branch proposal).
+ *              - Reference graph [1], [2]: Leviathan et al., Chen et al.
+ *                (speculative sampling); [18]: nucleus (top-p) sampling.
+ *  [wispaper] "Why does throughput collapse under high concurrency?"
+ *            (wispaper.ai Q&A): verification length tailored from prefix
+ *            survival probabilities (DSpark summary).
+ *  [Philox]  Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as
+ *            1, 2, 3", SC'11 -- Philox4x32-10 (outside the pages; the pages
+ *            name no generator, the counter-based choice is the build's).
+ *
+ * Readings where the pages are silent are listed in the repository's design
+ * notes; each function below states the one it uses.
+ */
+#ifndef SV_ORACLE_H
+#define SV_ORACLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* value types of logit buffers */
+#define ORC_F32 0  /* float32 */
+#define ORC_BF16 1 /* bfloat16, stored as uint16 bit patterns */
+
+/* ---- Philox4x32-10 [Philox] ------------------------------------------- */
+void orc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]);
+/* 24-bit uniform on [0, 1 - 2^-24]: (w >> 8) * 2^-24 */
+double orc_u24(uint32_t w);
+/* out[(r * n_pos + i) * 4 + k] = word k of Philox(ctr = (i, r, 0, 0), key = seed) */
+void orc_uniform_words(uint64_t seed, int32_t R, int32_t n_pos, uint32_t* out);
+
+/* ---- DVL allocation [DScale abstract; wispaper] ------------------------ */
+/* s[r*b+i] = fl32(s[r*b+i-1] * a[r*b+i]); choose the min(budget, R*b) best
+ * (s desc, r asc, i asc); L[r] = number chosen in r; pos_off / tgt_off are
+ * the exclusive scans of L and L+1 (R+1 entries each).  Returns 0, or 1 when
+ * an input lies outside [0, 1] (outputs still written). */
+int orc_dvl(const float* a, int32_t R, int32_t b, int32_t budget,
+            float* s, int32_t* L, int32_t* pos_off, int32_t* tgt_off);
+/* objective sum_r sum_{i<L_r} s[r*b+i] in double */
+double orc_dvl_objective(const float* s, const int32_t* L, int32_t R, int32_t b);
+
+/* ---- target / draft row statistics ----------------------------------- */
+typedef struct {
+  float max;        /* largest logit (exact input value) */
+  int32_t argmax;   /* lowest index attaining it */
+  double lse;       /* log sum_v exp(l_v / T); 0 when T == 0 */
+  float cut;        /* top-p cut logit (-inf when top-p is off; max when T == 0) */
+  double kept_lse;  /* log sum_{l_v >= cut} exp(l_v / T); lse when off; 0 when T == 0 */
+  double margin;    /* top-p decision margin (+inf when off) */
+} orc_row_stats_t;
+
+/* statistics of one row of V values; T >= 0, top_p in (0, 1] (>= 1: off) */
+void orc_row_stats(const void* row, int32_t dtype, int32_t V, double T, double top_p,
+                   orc_row_stats_t* out);
+/* nrows rows at rows + k*ld, temperature T[req[k]], top_p[req[k]] (top_p NULL: off) */
+void orc_row_stats_batch(const void* rows, int32_t dtype, int64_t ld, int32_t V, int32_t nrows,
+                         const int32_t* req, const float* T, const float* top_p,
+                         orc_row_stats_t* out);
+
+/* argmax (lowest index on ties) of nrows rows */
+void orc_argmax_rows(const void* rows, int32_t dtype, int64_t ld, int32_t V, int32_t nrows,
+                     int32_t* out);
+
+/* ---- one verification step ------------------------------------------- */
+#define ORC_Q_DENSE 0   /* independent draft: q_i = softmax(d_i / T) */
+#define ORC_Q_MIXTURE 1 /* latent mixture of K branches [DBLast] */
+
+typedef struct {
+  int32_t R, b, V, K;
+  int32_t dtype;            /* ORC_F32 / ORC_BF16 for all logit buffers */
+  /* target rows: request r uses rows tgt_row0[r] + j, j = 0..L[r] (L[r]+1 rows) */
+  const void* tgt; int64_t tgt_ld; const int64_t* tgt_row0;
+  const int32_t* L;         /* verified positions per request, 0 <= L <= b */
+  const float* T;           /* [R] temperature (0 = greedy) */
+  const float* top_p;       /* [R] or NULL (off) */
+  const int32_t* x;         /* [R*b] draft tokens */
+  int32_t q_mode;
+  /* dense draft: position i (0-based) of r at row draft_row0[r] + i */
+  const void* draft; int64_t draft_ld; const int64_t* draft_row0;
+  /* mixture: branch z at position i of r at row comp_row0[r] + z*b + i */
+  const void* comp; int64_t comp_ld; const int64_t* comp_row0;
+  const float* mix;         /* [R*K] mixing logits, q(z|y) = softmax */
+  double branch_T;          /* 0: greedy branches; > 0: soft branches softmax(c/branch_T) */
+  uint64_t seed;
+} orc_step_in_t;
+
+typedef struct {
+  int32_t* n_acc;      /* [R] */
+  int32_t* token;      /* [R] residual or bonus token */
+  int32_t* is_bonus;   /* [R] */
+  double* sample_margin; /* [R] */
+  double* u_res;       /* [R] uniform used for the sample */
+  /* per position (R*b), written for i < L[r]; entries past the first
+     rejection are still evaluated (as if that position were reached) */
+  double* u_acc;       /* [R*b] */
+  double* p_x;         /* [R*b] p_i(x_i) */
+  double* q_x;         /* [R*b] q_i(x_i | x_<i) */
+  double* acc_margin;  /* [R*b] */
+  /* mixture only (may be NULL): branch tokens [R*K*b] (greedy) and
+     posterior weights before position i, [R*b*K] */
+  int32_t* branch_tok;
+  double* post_w;
+} orc_step_out_t;
+
+/* Returns 0, or a nonzero code for malformed input. */
+int orc_step(const orc_step_in_t* in, const orc_step_out_t* out);
+
+int orc_num_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
