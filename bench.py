@@ -1,0 +1,228 @@
+"""Benchmark: verified draft positions per second on one MI355X.
+
+Workload (the full combined verification step at the largest shape):
+concurrency 32, block 16, Qwen3 vocabulary V = 151936, bf16 target logits,
+K = 8 latent-mixture draft with greedy branches, DVL budget 256 (half of
+32 x 16) from Beta(8, 2) survival estimates, T = 1.0, top-p 0.95, residual
+and bonus sampling, Philox seeds advancing per step.  Synthetic seeded data
+(synth.config(5)).
+
+A timed step is the whole verification path on inputs resident in HBM:
+dvl_alloc_pack -> sv_topp_threshold -> sv_mixture_q -> sv_accept ->
+sv_residual_sample.  The target forward is outside the path; its output for
+each step (the packed rows for that step's allocation) is prepared before the
+timed region in a buffer of its own, as the target model would have written it.
+
+Prints one JSON line.  `roofline` is for the dominant kernel (the mixture
+argmax over the component rows), timed live with HIP events on the stream the
+kernels run on; `cpu_baseline` is the CPU oracle on a bounded sample of the
+same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the CPU-oracle sample")
+    ap.add_argument("--no-cpu", action="store_true")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    p = os.path.join(ROOT, "draft_verification_sv_amd", "csrc", "sv_mix.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(kernel: str):
+    """HBM traffic per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        rec = json.load(open(p)).get(kernel)
+    except (ValueError, AttributeError):
+        return None
+    if not rec or rec.get("source_sha") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this path runs on a single GPU)",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import draft_verification_sv_amd as sv
+    import synth
+    from draft_verification_sv_amd.step import pack_rows_device, row_pitch, to_device_rows
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    S = args.steps
+    t_gen = time.time()
+    w = synth.config(5, steps=S)
+    R, b, V, K, B = w.R, w.b, w.V, w.K, w.budget
+    print(f"[bench] data generated in {time.time() - t_gen:.1f}s: {w.name}", file=sys.stderr, flush=True)
+    ld = row_pitch(V, "bf16")
+    max_pos = min(B, R * b)
+    max_rows = max_pos + R
+    dt = sv.SV_BF16
+    ws, nb = sv.make_workspace(R, b, K, V, dev)
+
+    full = to_device_rows(w.tgt, ld, dev)            # [R*(b+1), ld]: target rows for every position
+    comp = to_device_rows(w.comp, ld, dev)           # [R*K*b, ld]
+    mix = torch.from_numpy(w.mix.reshape(-1)).to(dev)
+    a_all = torch.from_numpy(w.a.reshape(S, R * b)).to(dev)
+    x_all = torch.from_numpy(w.x.reshape(S, R * b)).to(dev)
+    seeds = torch.from_numpy(w.seeds.view(np.int64)).to(dev)
+    T = torch.from_numpy(w.T).to(dev)
+    top_p = torch.from_numpy(w.top_p).to(dev)
+    budget = torch.tensor([B], dtype=torch.int32, device=dev)
+
+    i32, f32, f64 = torch.int32, torch.float32, torch.float64
+    z = lambda n, t: torch.zeros(n, dtype=t, device=dev)  # noqa: E731
+    s_sc, L, pos_off, tgt_off = z(R * b, f32), z(R, i32), z(R + 1, i32), z(R + 1, i32)
+    row_max, row_arg, row_lse, row_cut, row_kept = z(max_rows, f32), z(max_rows, i32), z(max_rows, f64), \
+        z(max_rows, f32), z(max_rows, f64)
+    branch_tok, post_w, q_at = z(R * K * b, i32), z(R * b * K, f64), z(R * b, f64)
+    n_acc, token, is_bonus = z(R, i32), z(R, i32), z(R, i32)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+
+    # ---- the target forward's output for every step, prepared before timing
+    t_prep = time.time()
+    packed = torch.empty((S, max_rows, ld), dtype=torch.bfloat16, device=dev)
+    L_host = np.zeros((S, R), np.int32)
+    for s in range(S):
+        sv.dvl_alloc_pack(a_all[s], R, b, budget, s_sc, L, pos_off, tgt_off, ws, nb, sp)
+        L_host[s] = L.cpu().numpy()
+        pack_rows_device(full, L_host[s], b + 1, packed[s])
+    torch.cuda.synchronize()
+    print(f"[bench] packed target rows for {S} steps in {time.time() - t_prep:.1f}s", file=sys.stderr, flush=True)
+    positions = L_host.sum(axis=1)  # verified positions per step
+
+    def step(s, ev=None):
+        sv.dvl_alloc_pack(a_all[s], R, b, budget, s_sc, L, pos_off, tgt_off, ws, nb, sp)
+        sv.sv_topp_threshold(packed[s], dt, ld, V, tgt_off, 0, R, max_rows, T, top_p, row_max, row_arg, row_lse,
+                             row_cut, row_kept, ws, nb, sp)
+        if ev is not None:
+            ev[0].record(stream)
+        sv.sv_mixture_q(comp, dt, ld, V, K, b, mix, pos_off, R, max_pos, x_all[s], branch_tok, post_w, q_at, ws, nb,
+                        sp)
+        if ev is not None:
+            ev[1].record(stream)
+        sv.sv_accept(packed[s], dt, ld, V, tgt_off, pos_off, R, b, T, row_arg, row_cut, row_kept, x_all[s],
+                     sv.SV_Q_MIXTURE, None, dt, 0, None, None, q_at, seeds[s:s + 1], n_acc, None, None, None, ws, nb,
+                     sp)
+        sv.sv_residual_sample(packed[s], dt, ld, V, tgt_off, pos_off, R, b, T, row_arg, row_cut, row_kept,
+                              sv.SV_Q_MIXTURE, None, dt, 0, None, None, K, branch_tok, post_w, seeds[s:s + 1], n_acc,
+                              token, is_bonus, ws, nb, sp)
+
+    for k in range(args.warmup):
+        step(k % S)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(S):
+        step(s)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+    status = sv.sv_get_status(ws, sp)
+    if status:
+        print(f"[bench] device status {sv.decode_status(status)}", file=sys.stderr, flush=True)
+
+    # ---- dominant kernel, timed with HIP events on the kernels' stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(S)]
+    for s in range(S):
+        step(s, evs[s])
+    torch.cuda.synchronize()
+    mix_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    row_bytes = V * 2
+    mix_bytes = float(np.mean(positions)) * K * row_bytes  # algorithmic: every verified position's K rows once
+    achieved = mix_bytes / (mix_ms * 1e-3) / 1e9
+    # step-aggregate algorithmic bytes: target rows, component rows, one sampled row per request
+    step_bytes = (positions + R) * row_bytes + positions * K * row_bytes + R * row_bytes
+    ms_per_step = elapsed / S * 1e3
+    value = float(positions.sum()) / elapsed
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(w, args.cpu_seconds)
+
+    traffic = load_traffic("k_mixture")
+    out = {
+        "metric": "verified draft positions/sec at V=151936, conc 32; % of peak HBM GB/s",
+        "value": round(value, 1),
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": S,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Zipfian logits, Beta(8,2) survival estimates)",
+        "config": {"workload": "conc32 block16 V151936 bf16, K8 greedy-branch mixture, DVL budget 256, "
+                               "T1.0 top-p0.95, residual+bonus, seeds advancing per step",
+                   "requests": R, "block": b, "vocab": V, "K": K, "budget": B},
+        "step_gbps": round(float(np.mean(step_bytes)) / (ms_per_step * 1e-3) / 1e9, 1),
+        "step_frac_of_peak": round(float(np.mean(step_bytes)) / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "roofline": {"kernel": "k_mixture (sv_mixture_q)", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": traffic, "avg_launch_us": round(mix_ms * 1e3, 2),
+                     "algorithmic_bytes_per_launch": mix_bytes},
+        "cpu_baseline": cpu,
+        "device_status": status,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(w, seconds: float):
+    """The CPU oracle as it stands, on a bounded sample of the same workload:
+    whole steps (DVL, then the step: target statistics with top-p, mixture
+    argmax and posterior, acceptance, residual/bonus) until `seconds` pass."""
+    import numpy as np
+
+    import oracle
+
+    R, b, V, K = w.R, w.b, w.V, w.K
+    tgt = w.tgt.reshape(R * (b + 1), V)
+    comp = w.comp.reshape(R * K * b, V)
+    t0 = time.perf_counter()
+    pos = n = 0
+    while n < w.steps:
+        dv = oracle.dvl(w.a[n], w.budget)
+        oracle.step(tgt=tgt, tgt_row0=np.arange(R) * (b + 1), L=dv["L"], T=w.T, x=w.x[n], seed=int(w.seeds[n]),
+                    top_p=w.top_p, comp=comp, comp_row0=np.arange(R) * K * b, mix=w.mix)
+        pos += int(dv["L"].sum())
+        n += 1
+        if time.perf_counter() - t0 > seconds:
+            break
+    el = time.perf_counter() - t0
+    return {"value": round(pos / el, 2), "unit": "positions/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{n} whole steps of the same workload ({pos} verified positions) in {el:.1f}s"}
+
+
+if __name__ == "__main__":
+    main()

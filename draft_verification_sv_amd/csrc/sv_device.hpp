@@ -1,0 +1,277 @@
+// sv_device.hpp -- device helpers shared by the libsv kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sv.h"
+
+namespace sv {
+
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------------ Philox4x32-10
+// Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3"
+// (SC'11): ten rounds; each round multiplies words 0 and 2 by two odd 32-bit
+// constants, mixes the high halves with words 1, 3 and the key, and the key
+// advances by two Weyl increments between rounds.
+struct U4 {
+  uint32_t x, y, z, w;
+};
+
+__host__ __device__ __forceinline__ U4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                                     uint32_t k0, uint32_t k1) {
+  constexpr uint32_t kMulA = 0xD2511F53u, kMulB = 0xCD9E8D57u;
+  constexpr uint32_t kWeylA = 0x9E3779B9u, kWeylB = 0xBB67AE85u;
+#pragma unroll
+  for (int round = 0; round < 10; ++round) {
+    const uint64_t pa = static_cast<uint64_t>(kMulA) * c0;  // v_mul_hi_u32 / v_mul_lo_u32 on the GPU
+    const uint64_t pb = static_cast<uint64_t>(kMulB) * c2;
+    const uint32_t hiA = static_cast<uint32_t>(pa >> 32), loA = static_cast<uint32_t>(pa);
+    const uint32_t hiB = static_cast<uint32_t>(pb >> 32), loB = static_cast<uint32_t>(pb);
+    const uint32_t n0 = hiB ^ c1 ^ k0;
+    const uint32_t n2 = hiA ^ c3 ^ k1;
+    c0 = n0;
+    c1 = loB;
+    c2 = n2;
+    c3 = loA;
+    k0 += kWeylA;
+    k1 += kWeylB;
+  }
+  return U4{c0, c1, c2, c3};
+}
+
+// Words at counter (pos, req, 0, 0) under key = 64-bit seed.
+__device__ __forceinline__ U4 philox_at(uint64_t seed, uint32_t pos, uint32_t req) {
+  return philox4x32_10(pos, req, 0u, 0u, static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32));
+}
+
+// 24-bit uniform on {0, 2^-24, ..., 1 - 2^-24}; exact in float and double.
+__device__ __forceinline__ double u24(uint32_t w) { return static_cast<double>(w >> 8) * (1.0 / 16777216.0); }
+
+// ------------------------------------------------------------------ values
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+template <int DT>
+__device__ __forceinline__ float load_val(const void* base, int64_t idx) {
+  if constexpr (DT == SV_BF16) {
+    return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(base)[idx]) << 16);
+  } else {
+    return static_cast<const float*>(base)[idx];
+  }
+}
+
+__device__ __forceinline__ float load_val_rt(const void* base, int dtype, int64_t idx) {
+  return dtype == SV_BF16 ? load_val<SV_BF16>(base, idx) : load_val<SV_F32>(base, idx);
+}
+
+// Streaming 16-byte load (the data is read once).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load16_stream(const uint4* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return uint4{v.x, v.y, v.z, v.w};
+}
+
+// ------------------------------------------------------------------ wave reductions
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint64_t t = __shfl_xor(v, o, kWave);
+    v = t > v ? t : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ int wave_min_i32(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const int t = __shfl_xor(v, o, kWave);
+    v = t < v ? t : v;
+  }
+  return v;
+}
+
+// inclusive scan over the wave, lane order
+__device__ __forceinline__ double wave_incl_scan_f64(double v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const double t = __shfl_up(v, o, kWave);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int wave_incl_scan_i32(int v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int t = __shfl_up(v, o, kWave);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+// ------------------------------------------------------------------ block reductions
+// All threads of the block must call these.  `scratch` holds >= NT/64 items.
+template <int NT>
+__device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t* scratch) {
+  constexpr int NW = NT / kWave;
+  v = wave_max_u64(v);
+  const int w = threadIdx.x / kWave;
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) scratch[w] = v;
+  __syncthreads();
+  uint64_t r = scratch[0];
+#pragma unroll
+  for (int k = 1; k < NW; ++k) r = scratch[k] > r ? scratch[k] : r;
+  return r;
+}
+
+template <int NT>
+__device__ __forceinline__ double block_sum_f64(double v, double* scratch) {
+  constexpr int NW = NT / kWave;
+  v = wave_sum_f64(v);
+  const int w = threadIdx.x / kWave;
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) scratch[w] = v;
+  __syncthreads();
+  double r = 0.0;
+#pragma unroll
+  for (int k = 0; k < NW; ++k) r += scratch[k];  // fixed order: deterministic
+  return r;
+}
+
+template <int NT>
+__device__ __forceinline__ int block_min_i32(int v, int* scratch) {
+  constexpr int NW = NT / kWave;
+  v = wave_min_i32(v);
+  const int w = threadIdx.x / kWave;
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) scratch[w] = v;
+  __syncthreads();
+  int r = scratch[0];
+#pragma unroll
+  for (int k = 1; k < NW; ++k) r = scratch[k] < r ? scratch[k] : r;
+  return r;
+}
+
+// Exclusive scan in thread order; also returns the block total.
+template <int NT>
+__device__ __forceinline__ double block_excl_scan_f64(double v, double* scratch, double* total) {
+  constexpr int NW = NT / kWave;
+  const double inc = wave_incl_scan_f64(v);
+  const int w = threadIdx.x / kWave;
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == kWave - 1) scratch[w] = inc;
+  __syncthreads();
+  double base = 0.0, tot = 0.0;
+#pragma unroll
+  for (int k = 0; k < NW; ++k) {
+    if (k < w) base += scratch[k];
+    tot += scratch[k];
+  }
+  *total = tot;
+  return base + inc - v;
+}
+
+template <int NT>
+__device__ __forceinline__ int block_excl_scan_i32(int v, int* scratch, int* total) {
+  constexpr int NW = NT / kWave;
+  const int inc = wave_incl_scan_i32(v);
+  const int w = threadIdx.x / kWave;
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == kWave - 1) scratch[w] = inc;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int k = 0; k < NW; ++k) {
+    if (k < w) base += scratch[k];
+    tot += scratch[k];
+  }
+  *total = tot;
+  return base + inc - v;
+}
+
+// ------------------------------------------------------------------ ragged offsets
+// Request r with off[r] <= p < off[r+1]; -1 if none (malformed offsets).
+// All threads of the block must call this; `slot` is one shared int.
+template <int NT>
+__device__ __forceinline__ int find_request(const int32_t* off, int R, int p, int* slot) {
+  if (threadIdx.x == 0) *slot = -1;
+  __syncthreads();
+  for (int r = threadIdx.x; r < R; r += NT) {
+    if (off[r] <= p && p < off[r + 1]) *slot = r;
+  }
+  __syncthreads();
+  return *slot;
+}
+
+// ------------------------------------------------------------------ status
+__device__ __forceinline__ void raise_status(uint32_t* status, uint32_t bits) {
+  __hip_atomic_fetch_or(status, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ------------------------------------------------------------------ cross-block hand-off
+// Writer side: make this thread's global writes visible at device scope, then
+// count in.  Returns true in exactly one thread of the last block to arrive.
+__device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected) {
+  __threadfence();
+  const uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+  if (prev + 1u == expected) {
+    __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
+    return true;
+  }
+  return false;
+}
+
+template <typename T>
+__device__ __forceinline__ T load_acquire_relaxed(const T* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ------------------------------------------------------------------ workspace layout
+// [status 256 B][counters: 2*R u32][residual partials: R*S_res*4 doubles][mixture partials: R*b*K*S_mix u64]
+struct WsLayout {
+  size_t status, counters, res_part, mix_part, total;
+};
+
+__host__ __device__ inline int mix_chunks(int V, int dtype) {
+  const int per_vec = dtype == SV_BF16 ? 8 : 4;
+  const int nvec = V / per_vec;
+  const int target = 256 * 16;  // vectors per chunk: 16 per thread
+  int s = (nvec + target - 1) / target;
+  return s < 1 ? 1 : s;
+}
+
+__host__ __device__ inline int res_chunks(int V) {
+  const int nvec = V / 8;
+  const int target = 256 * 4;
+  int s = (nvec + target - 1) / target;
+  if (s < 1) s = 1;
+  if (s > 64) s = 64;
+  return s;
+}
+
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+__host__ __device__ inline WsLayout ws_layout(int R, int b, int K, int V) {
+  WsLayout l;
+  l.status = 0;
+  l.counters = 256;
+  l.res_part = l.counters + align256(sizeof(uint32_t) * 2 * static_cast<size_t>(R));
+  // mixture chunks: take the larger of the two dtypes' counts so one layout serves both
+  const int smix = mix_chunks(V, SV_F32) > mix_chunks(V, SV_BF16) ? mix_chunks(V, SV_F32) : mix_chunks(V, SV_BF16);
+  l.mix_part = l.res_part + align256(sizeof(double) * 4 * static_cast<size_t>(R) * res_chunks(V));
+  l.total = l.mix_part + align256(sizeof(uint64_t) * static_cast<size_t>(R) * b * (K > 0 ? K : 0) * smix);
+  return l;
+}
+
+}  // namespace sv

@@ -1,0 +1,149 @@
+// sv_dvl.hip -- dynamic verify-length (DVL) allocation and packing.
+//
+// "DScale: Scaling Block-Diffusion Speculative Decoding with Adaptive
+// Verification", abstract: DVL packs scored prefixes into half the native
+// verification capacity, and fixed-address workspaces carry the changing
+// boundaries through verification and acceptance.  The score of a prefix is
+// its survival probability (the DSpark summary on "Why does throughput
+// collapse under high concurrency?": verification length from prefix survival
+// probabilities): s_{r,i} = a_{r,1} * ... * a_{r,i}, one float rounding per
+// product.  The allocation keeps the B highest scores in the order (s desc, r
+// asc, i asc); with a <= 1 the scores fall along each request, so the choice is
+// prefix-closed and maximises the summed survival (expected accepted length).
+//
+// One block of 1024 threads:
+//   1. per request, the running products (written to s);
+//   2. radix select, 8 bits per pass from the top, of the B-th largest score
+//      (non-negative floats order like their bit patterns), with LDS count
+//      histograms;
+//   3. per request, positions above the threshold plus the first ties in
+//      (r, i) order, via an exclusive scan of the tie counts over requests;
+//   4. exclusive scans of L and L + 1 into pos_off and tgt_off.
+#include "sv_device.hpp"
+#include "sv_host.hpp"
+
+namespace sv {
+
+constexpr int kDvlNT = 1024;
+
+__global__ __launch_bounds__(kDvlNT) void k_dvl(const float* a, int R, int b, const int32_t* budget, float* s,
+                                               int32_t* L, int32_t* pos_off, int32_t* tgt_off, uint32_t* status) {
+  __shared__ uint32_t hist[256];
+  __shared__ int scr[kDvlNT / kWave];
+  __shared__ uint32_t sh_prefix;
+  __shared__ int sh_remaining;
+  const int tid = threadIdx.x;
+  const int n = R * b;
+  int B = *budget;
+  if (B < 0) {
+    if (tid == 0) raise_status(status, SV_ST_BAD_BUDGET);
+    B = 0;
+  }
+  // 1. survival scores
+  bool bad = false;
+  for (int r = tid; r < R; r += kDvlNT) {
+    float run = 1.0f;
+    for (int i = 0; i < b; ++i) {
+      const float av = a[r * b + i];
+      bad |= !(av >= 0.0f && av <= 1.0f);
+      run = run * av;
+      s[r * b + i] = run;
+    }
+  }
+  if (bad) raise_status(status, SV_ST_BAD_SCORE);
+  __syncthreads();  // s is re-read below by other threads of this block
+
+  // 2. threshold: the B-th largest score (rank from the top, ties counted)
+  uint32_t thr = 0;
+  int remaining = 0;  // how many ties at thr are taken
+  const bool all = B >= n, none = B == 0;
+  if (!all && !none) {
+    uint32_t prefix = 0, mask = 0;
+    remaining = B;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      for (int k = tid; k < 256; k += kDvlNT) hist[k] = 0u;
+      __syncthreads();
+      for (int e = tid; e < n; e += kDvlNT) {
+        const uint32_t kk = __float_as_uint(s[e]);
+        if ((kk & mask) == prefix) atomicAdd(&hist[(kk >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (tid == 0) {
+        int cum = 0;
+        for (int d = 255; d >= 0; --d) {
+          const int h = static_cast<int>(hist[d]);
+          if (cum + h >= remaining) {
+            prefix |= static_cast<uint32_t>(d) << shift;
+            remaining -= cum;
+            break;
+          }
+          cum += h;
+        }
+        sh_prefix = prefix;
+        sh_remaining = remaining;
+      }
+      __syncthreads();
+      prefix = sh_prefix;
+      remaining = sh_remaining;
+      mask |= 255u << shift;
+    }
+    thr = prefix;
+  }
+
+  // 3. per-request counts; ties are taken in (r, i) order
+  const int per = (R + kDvlNT - 1) / kDvlNT;
+  const int r0 = tid * per, r1 = min(R, r0 + per);
+  int eq_local = 0;
+  for (int r = r0; r < r1; ++r)
+    for (int i = 0; i < b; ++i) eq_local += (!all && !none && __float_as_uint(s[r * b + i]) == thr) ? 1 : 0;
+  int eq_total;
+  int tie_base = block_excl_scan_i32<kDvlNT>(eq_local, scr, &eq_total);
+  int l_local = 0;
+  for (int r = r0; r < r1; ++r) {
+    int Lr;
+    if (all) {
+      Lr = b;
+    } else if (none) {
+      Lr = 0;
+    } else {
+      int gt = 0, eq = 0;
+      for (int i = 0; i < b; ++i) {
+        const uint32_t kk = __float_as_uint(s[r * b + i]);
+        gt += kk > thr ? 1 : 0;
+        eq += kk == thr ? 1 : 0;
+      }
+      int take = remaining - tie_base;
+      take = take < 0 ? 0 : (take > eq ? eq : take);
+      tie_base += eq;
+      Lr = gt + take;
+    }
+    L[r] = Lr;
+    l_local += Lr;
+  }
+  // 4. offsets
+  int l_total;
+  int off = block_excl_scan_i32<kDvlNT>(l_local, scr, &l_total);
+  for (int r = r0; r < r1; ++r) {
+    pos_off[r] = off;
+    tgt_off[r] = off + r;
+    off += L[r];
+  }
+  if (tid == 0) {
+    pos_off[R] = l_total;
+    tgt_off[R] = l_total + R;
+  }
+}
+
+}  // namespace sv
+
+using namespace sv;
+
+extern "C" int32_t dvl_alloc_pack(const float* a, int32_t R, int32_t b, const int32_t* budget, float* s, int32_t* L,
+                                  int32_t* pos_off, int32_t* tgt_off, void* ws, size_t ws_bytes, void* stream) {
+  if (!a || !budget || !s || !L || !pos_off || !tgt_off || !ws) return SV_ERR_ARG;
+  if (R < 1 || b < 1 || b > 64 || static_cast<long long>(R) * b > (1LL << 24)) return SV_ERR_ARG;
+  if (ws_bytes < 256) return SV_ERR_WORKSPACE;
+  hipLaunchKernelGGL(k_dvl, dim3(1), dim3(kDvlNT), 0, static_cast<hipStream_t>(stream), a, R, b, budget, s, L, pos_off,
+                     tgt_off, status_word(ws));
+  return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
+}

@@ -1,0 +1,247 @@
+/*
+ * sv.h -- C ABI of libsv: batched verification of block-diffusion draft
+ * blocks against target logits on one AMD Instinct MI355X (gfx950).
+ *
+ * Pages the operations come from (cited by title and section):
+ *  [DScale]  "DScale: Scaling Block-Diffusion Speculative Decoding with
+ *            Adaptive Verification" -- abstract: dynamic verify-length (DVL)
+ *            allocation packs scored prefixes into half the native
+ *            verification capacity; fixed-address workspaces carry changing
+ *            boundaries through verification and acceptance.
+ *  [DBLast]  "Pith review of DBLAST: Dependent Block Drafting for Stochastic
+ *            Speculative Decoding" -- "What carries the argument" (latent
+ *            mixture q_dep and the category posterior along the accepted
+ *            prefix), "Assumptions & free parameters" (speculative sampling
+ *            with rejection correction preserves the target distribution),
+ *            "What would settle it" (target sampling at temperature 1.5 with
+ *            top-p 0.95), Referee report minor 5 (Eq. (20), the greedy-branch
+ *            conditional), reference graph [1], [2] (speculative sampling),
+ *            [18] (nucleus sampling).
+ *  [wispaper] "Why does throughput collapse under high concurrency?" --
+ *            verification length tailored from prefix survival probabilities.
+ *
+ * Conventions shared by every call
+ *  - All array arguments are DEVICE pointers unless marked "host".  The caller
+ *    owns every buffer; the library allocates nothing and keeps no state
+ *    besides the caller's workspace.
+ *  - Every per-step value (lengths, offsets, seed, temperature, top-p,
+ *    budget) is read from device memory at launch time, so a captured
+ *    sequence of calls can be replayed with new values at fixed addresses.
+ *    Grids are sized from host-side capacities; work items beyond the
+ *    device-side counts exit at once.
+ *  - `stream` is a hipStream_t.  Calls are asynchronous; outputs are valid in
+ *    stream order.  Two calls that share one workspace must not run
+ *    concurrently.
+ *  - Requests r = 0..R-1, draft block of b positions, vocabulary V.
+ *    L_r = pos_off[r+1] - pos_off[r] is the number of verified positions of
+ *    request r (0 <= L_r <= b).  The target gives L_r + 1 rows per request:
+ *    rows for positions 1..L_r and the bonus row, packed request after
+ *    request at rows tgt_off[r] .. tgt_off[r] + L_r, so tgt_off[r+1] -
+ *    tgt_off[r] = L_r + 1.
+ *  - Logit rows are row-major with a leading dimension `ld` (elements).  The
+ *    base pointer and ld * element size must be multiples of 16 bytes.
+ *  - dtype: SV_F32 (float) or SV_BF16 (bfloat16).
+ *  - Return value: SV_OK, or an SV_ERR_* code for a host-detectable error, in
+ *    which case nothing is launched.  Problems only visible on the device
+ *    (bad temperatures, non-finite logits, malformed offsets, ...) set bits
+ *    of a sticky status word in the workspace; read it with sv_get_status.
+ *    Outputs affected by such a problem are unspecified.
+ */
+#ifndef SV_H
+#define SV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* value types */
+#define SV_F32 0
+#define SV_BF16 1
+
+/* proposal kinds */
+#define SV_Q_DENSE 0   /* independent draft: q_i = softmax(d_i / T_r), one-hot argmax at T_r = 0 */
+#define SV_Q_MIXTURE 1 /* latent mixture of K greedy branches [DBLast] */
+
+/* return codes */
+#define SV_OK 0
+#define SV_ERR_ARG 1       /* null pointer, size out of range, misalignment, unknown dtype/mode */
+#define SV_ERR_WORKSPACE 2 /* workspace smaller than sv_workspace_bytes() asks for */
+#define SV_ERR_LAUNCH 3    /* the HIP runtime refused a launch or copy */
+
+/* device status bits (sticky; OR-ed by the kernels) */
+#define SV_ST_BAD_TEMPERATURE 0x001u /* T_r < 0 or NaN */
+#define SV_ST_BAD_TOP_P 0x002u       /* top_p_r <= 0 or NaN (treated as keeping the top value) */
+#define SV_ST_NONFINITE 0x004u       /* NaN or +-Inf in a logit row that was read */
+#define SV_ST_BAD_SCORE 0x008u       /* DVL survival estimate outside [0, 1] */
+#define SV_ST_BAD_TOKEN 0x010u       /* draft token outside [0, V) */
+#define SV_ST_BAD_OFFSETS 0x020u     /* offsets not an exclusive scan, L_r > b, or over capacity */
+#define SV_ST_EMPTY_POSTERIOR 0x040u /* no mixture branch consistent with the draft prefix (q = 0) */
+#define SV_ST_BAD_BUDGET 0x080u      /* DVL budget < 0 */
+#define SV_ST_BAD_NACC 0x100u        /* n_acc outside [0, L_r] */
+
+/* ---------------------------------------------------------------- workspace */
+
+/* Bytes of workspace needed for problems of up to R requests, block b,
+ * K mixture components (0 if unused) and vocabulary V.  Host-only. */
+int32_t sv_workspace_bytes(int32_t R, int32_t b, int32_t K, int32_t V, size_t* out_bytes);
+
+/* Zero the workspace (once, before first use).  Each call leaves its
+ * counters at zero again, so no per-step clearing is needed. */
+int32_t sv_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/* Copy the status word to *host_out, then synchronise the stream. */
+int32_t sv_get_status(const void* ws, void* stream, uint32_t* host_out);
+
+/* Reset the status word to 0 (asynchronous, a kernel, no memset). */
+int32_t sv_clear_status(void* ws, void* stream);
+
+/* Human-readable text for a return code. */
+const char* sv_status_string(int32_t code);
+
+/* ---------------------------------------------------------------- DVL */
+
+/* dvl_alloc_pack [DScale abstract: DVL allocation; wispaper: prefix survival
+ * probabilities].
+ *   a[R*b]      per-position acceptance estimates in [0, 1] (float)
+ *   budget      device int32 scalar: verification slots B (>= 0)
+ *   s[R*b]      out: survival scores s_{r,i} = fl32(s_{r,i-1} * a_{r,i}),
+ *               s_{r,0} = a_{r,0}, one float rounding per product
+ *   L[R]        out: verified positions per request
+ *   pos_off[R+1], tgt_off[R+1]  out: exclusive scans of L and of L + 1
+ * The chosen positions are the min(B, R*b) best in the order (s desc, r asc,
+ * i asc); with a <= 1 they are prefix-closed per request and maximise the
+ * summed survival score (expected accepted positions).  Requires
+ * R*b <= 2^24, b <= 64.  Uses the workspace's status word only. */
+int32_t dvl_alloc_pack(const float* a, int32_t R, int32_t b, const int32_t* budget, float* s,
+                       int32_t* L, int32_t* pos_off, int32_t* tgt_off, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- row statistics */
+
+/* sv_softmax_stats: per logit row, the largest value, its lowest index and
+ * log sum_v exp(l_v / T_r) (computed in double) [DBLast, "What would settle
+ * it": target sampling at a temperature].
+ *   logits       rows of V values, leading dimension ld (elements)
+ *   row_off[R+1] device: work items p in [row_off[r], row_off[r+1]) belong to
+ *                request r (an exclusive scan, row_off[0] = 0)
+ *   row_stride   host: 0 -> work item p reads logit row p (packed rows);
+ *                > 0 -> it reads row r*row_stride + (p - row_off[r]) (dense
+ *                rows, e.g. a [R, b, ld] drafter output with row_off = pos_off)
+ *   max_rows     host: capacity; row_off[R] <= max_rows
+ *   temperature[R]  T_r >= 0; T_r = 0 is greedy (row_lse is then 0)
+ *   row_max, row_argmax, row_lse  out: [max_rows], indexed by work item
+ * Ties of the maximum go to the lowest index. */
+int32_t sv_softmax_stats(const void* logits, int32_t dtype, int64_t ld, int32_t V,
+                         const int32_t* row_off, int32_t row_stride, int32_t R, int32_t max_rows,
+                         const float* temperature, float* row_max, int32_t* row_argmax,
+                         double* row_lse, void* ws, size_t ws_bytes, void* stream);
+
+/* sv_topp_threshold: everything sv_softmax_stats computes, plus the top-p
+ * (nucleus) cut [DBLast, "What would settle it": top-p 0.95; reference [18]]:
+ *   row_cut       out: the largest logit value t with
+ *                 sum_{l_v >= t} softmax(l / T)_v >= top_p_r; every token with
+ *                 l_v >= t is kept (ties kept).  -inf when top_p_r >= 1
+ *                 (filter off); the row maximum when T_r = 0.
+ *   row_kept_lse  out: log sum_{l_v >= cut} exp(l_v / T_r) (double); equals
+ *                 row_lse when the filter is off; 0 when T_r = 0.
+ * The target probability of token v is then [l_v >= cut] exp(l_v / T -
+ * kept_lse).  top_p may be NULL (off for every request).  Same row mapping as
+ * sv_softmax_stats. */
+int32_t sv_topp_threshold(const void* logits, int32_t dtype, int64_t ld, int32_t V,
+                          const int32_t* row_off, int32_t row_stride, int32_t R, int32_t max_rows,
+                          const float* temperature, const float* top_p, float* row_max,
+                          int32_t* row_argmax, double* row_lse, float* row_cut,
+                          double* row_kept_lse, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- mixture proposal */
+
+/* sv_mixture_q [DBLast, "What carries the argument"; Referee report minor 5,
+ * Eq. (20)]: the latent-mixture proposal with greedy branches.
+ *   comp_logits  [R, K, b, ld] component logits; branch z of request r at
+ *                position i is row (r*K + z)*b + i
+ *   mix_logits[R*K]  q(z | y) = softmax over z (float)
+ *   pos_off[R+1]     verified positions (from dvl_alloc_pack, or i*b)
+ *   max_pos      host: capacity, pos_off[R] <= max_pos
+ *   draft_tok[R*b]   the draft block (the branch the drafter decoded)
+ *   branch_tok[R*K*b]  out: g_i(z) = argmax_v comp[r, z, i, v] (lowest index),
+ *                      written for i < L_r
+ *   post_w[R*b*K]    out: category posterior before position i, given the
+ *                    draft prefix x_<i: w_z = q(z|y) [g_j(z) = x_j for all
+ *                    j < i] / sum of the same over z (double); i < L_r
+ *   q_at_draft[R*b]  out: q(x_i | x_<i) = sum of w_z over z with g_i(z) = x_i
+ *                    (double); 0 and SV_ST_EMPTY_POSTERIOR when no branch is
+ *                    consistent with x_<i; i < L_r
+ * Requires K <= 64, b <= 64.  Uses the workspace's counters and partials. */
+int32_t sv_mixture_q(const void* comp_logits, int32_t dtype, int64_t ld, int32_t V, int32_t K,
+                     int32_t b, const float* mix_logits, const int32_t* pos_off, int32_t R,
+                     int32_t max_pos, const int32_t* draft_tok, int32_t* branch_tok,
+                     double* post_w, double* q_at_draft, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/* ---------------------------------------------------------------- acceptance */
+
+/* sv_accept [DBLast, "Assumptions": speculative sampling with rejection
+ * correction; reference graph [1], [2]]: for each request and position
+ * i = 1..L_r, accept x_i iff u < p_i(x_i) / q_i(x_i | x_<i) (q = 0: accept iff
+ * p > 0); n_acc[r] = (first rejected position) - 1, or L_r.
+ *   u = (w0 >> 8) * 2^-24, w0 = word 0 of Philox4x32-10 at counter
+ *   (i - 1, r, 0, 0) under key (low, high 32 bits of *seed).
+ *   Target: row tgt_off[r] + i - 1 of tgt_logits with its row_argmax /
+ *   row_cut / row_kept_lse (from sv_topp_threshold; p one-hot at the argmax
+ *   when T_r = 0).
+ *   q_mode SV_Q_DENSE: draft_logits [R, b, draft_ld]; draft_lse / draft_argmax
+ *   indexed by pos_off[r] + i - 1 (from sv_softmax_stats with row_off =
+ *   pos_off, row_stride = b); q = exp(d_x / T_r - lse) or one-hot at T_r = 0.
+ *   q_mode SV_Q_MIXTURE: q_at_draft[R*b] from sv_mixture_q.
+ *   Unused mode's pointers may be NULL.
+ *   p_out, q_out (double), u_out (float): optional [R*b] diagnostics.
+ * Requires b <= 64.  Uses the workspace's status word only. */
+int32_t sv_accept(const void* tgt_logits, int32_t dtype, int64_t tgt_ld, int32_t V,
+                  const int32_t* tgt_off, const int32_t* pos_off, int32_t R, int32_t b,
+                  const float* temperature, const int32_t* row_argmax, const float* row_cut,
+                  const double* row_kept_lse, const int32_t* draft_tok, int32_t q_mode,
+                  const void* draft_logits, int32_t draft_dtype, int64_t draft_ld,
+                  const int32_t* draft_argmax, const double* draft_lse,
+                  const double* q_at_draft, const uint64_t* seed, int32_t* n_acc,
+                  double* p_out, double* q_out, float* u_out, void* ws, size_t ws_bytes,
+                  void* stream);
+
+/* ---------------------------------------------------------------- residual / bonus */
+
+/* sv_residual_sample [DBLast, "Assumptions"; reference graph [1], [2]]: one
+ * token per request from slot j = n_acc[r] (0-based):
+ *   n_acc < L_r: residual norm(max(0, p_j - q_j(. | x_<j))) (if it is zero
+ *                everywhere from rounding: p_j);
+ *   n_acc = L_r: bonus sample from p_{L_r + 1} (is_bonus = 1).
+ *   Inverse CDF in vocabulary order: the smallest v whose running weight
+ *   exceeds u * W, u = (w1 >> 8) * 2^-24 from word 1 of Philox at counter
+ *   (j, r, 0, 0); weights and their sums in double.  T_r = 0: the argmax.
+ *   Arguments as sv_accept; in SV_Q_MIXTURE mode K, branch_tok and post_w
+ *   come from sv_mixture_q.
+ *   token[R], is_bonus[R]  out.
+ * Uses the workspace's counters and partials. */
+int32_t sv_residual_sample(const void* tgt_logits, int32_t dtype, int64_t tgt_ld, int32_t V,
+                           const int32_t* tgt_off, const int32_t* pos_off, int32_t R, int32_t b,
+                           const float* temperature, const int32_t* row_argmax,
+                           const float* row_cut, const double* row_kept_lse, int32_t q_mode,
+                           const void* draft_logits, int32_t draft_dtype, int64_t draft_ld,
+                           const int32_t* draft_argmax, const double* draft_lse, int32_t K,
+                           const int32_t* branch_tok, const double* post_w, const uint64_t* seed,
+                           const int32_t* n_acc, int32_t* token, int32_t* is_bonus, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- Philox (test export) */
+
+/* out[(r*n_pos + i)*4 + k] = word k of Philox4x32-10 at counter (i, r, 0, 0)
+ * under key (low, high 32 bits of *seed) (Salmon et al., SC'11; the pages
+ * name no generator). */
+int32_t sv_philox_uniforms(const uint64_t* seed, int32_t R, int32_t n_pos, uint32_t* out,
+                           void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,151 @@
+"""Parity harness: run one verification step through libsv and through the
+oracle on the same seeded inputs, and compare them.
+
+Comparison rule: Philox uniforms, DVL scores/lengths/offsets, argmax indices,
+row maxima and branch tokens exactly; log-sum-exp, kept mass and p, q at the
+draft tokens within 1e-5 relative; accepted lengths, residual and bonus
+tokens exactly, except a mismatch whose oracle decision margin is below 1e-6
+(after a request's first mismatch its later decisions are not compared); such
+mismatches must number fewer than 1e-4 of the verified positions.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+import synth
+
+REL = 1e-5
+MARGIN = 1e-6
+
+
+def gpu_step_runner(w: synth.Workload, device="cuda"):
+    """Upload a workload once and return (VerifyStep, run(s) -> results)."""
+    import torch
+
+    from draft_verification_sv_amd.step import VerifyStep, pack_rows_device, row_pitch, to_device_rows
+
+    R, b, V, K = w.R, w.b, w.V, w.K
+    ld = row_pitch(V, w.dtype)
+    max_pos = min(w.budget, R * b) if w.budget is not None else R * b
+    vs = VerifyStep(R=R, b=b, V=V, dtype=w.dtype, K=K, max_pos=max_pos, device=device, diagnostics=True)
+    full = to_device_rows(w.tgt, ld, device)  # [R*(b+1), ld]
+    packed = torch.empty_like(full)
+    draft = to_device_rows(w.draft, ld, device) if K == 0 else None
+    comp = to_device_rows(w.comp, ld, device) if K > 0 else None
+
+    def run(s: int) -> dict:
+        vs.set_inputs(T=w.T, x=w.x[s], seed=int(w.seeds[s]), top_p=w.top_p, mix=w.mix,
+                      a=None if w.a is None else w.a[s], budget=w.budget)
+        if w.budget is not None:
+            vs.run_dvl()
+            L = vs.L.cpu().numpy()
+        else:
+            vs.set_full_verification()
+            L = np.full(R, b, np.int32)
+        pack_rows_device(full, L, b + 1, packed)
+        vs.run_verify(packed, ld, draft=draft, draft_ld=ld, comp=comp, comp_ld=ld)
+        return vs.results()
+
+    return vs, run
+
+
+def oracle_step(w: synth.Workload, s: int) -> dict:
+    R, b, V, K = w.R, w.b, w.V, w.K
+    if w.budget is not None:
+        dv = oracle.dvl(w.a[s], w.budget)
+    else:
+        L = np.full(R, b, np.int32)
+        dv = {"L": L, "s": None, "pos_off": np.concatenate([[0], np.cumsum(L)]).astype(np.int32),
+              "tgt_off": np.concatenate([[0], np.cumsum(L + 1)]).astype(np.int32)}
+    L = dv["L"]
+    tgt = w.tgt.reshape(R * (b + 1), V)
+    common = dict(tgt=tgt, tgt_row0=np.arange(R) * (b + 1), L=L, T=w.T, x=w.x[s], seed=int(w.seeds[s]),
+                  top_p=w.top_p)
+    if K == 0:
+        out = oracle.step(**common, draft=w.draft.reshape(R * b, V), draft_row0=np.arange(R) * b)
+    else:
+        out = oracle.step(**common, comp=w.comp.reshape(R * K * b, V), comp_row0=np.arange(R) * K * b, mix=w.mix)
+    out["dvl"] = dv
+    # statistics of every target row read in this step, in packed order
+    rows = np.concatenate([r * (b + 1) + np.arange(L[r] + 1) for r in range(R)])
+    req = np.repeat(np.arange(R), L + 1)
+    out["rows"] = oracle.row_stats_batch(tgt[rows], req, w.T, w.top_p)
+    if K == 0:
+        drows = np.concatenate([r * b + np.arange(L[r]) for r in range(R)]).astype(np.int64)
+        dreq = np.repeat(np.arange(R), L)
+        out["drows"] = oracle.row_stats_batch(w.draft.reshape(R * b, V)[drows], dreq, w.T, None)
+    return out
+
+
+def _rel_close(a, b, rel=REL):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    same_inf = (a == b)
+    return same_inf | (np.abs(a - b) <= rel * np.maximum(np.abs(b), 1e-300))
+
+
+def compare_step(w: synth.Workload, g: dict, o: dict, report: dict | None = None) -> dict:
+    """Compare one step; returns counters and raises AssertionError on a violation."""
+    R, b = w.R, w.b
+    rep = report if report is not None else {"positions": 0, "mismatches": 0, "low_margin": [], "cut_diff": 0}
+    dv = o["dvl"]
+    L = dv["L"]
+    # DVL: bit-exact
+    assert np.array_equal(g["L"], L), "DVL lengths differ"
+    assert np.array_equal(g["pos_off"], dv["pos_off"]), "pos_off differs"
+    assert np.array_equal(g["tgt_off"], dv["tgt_off"]), "tgt_off differs"
+    if dv["s"] is not None:
+        assert np.array_equal(g["s"].view(np.uint32), dv["s"].reshape(-1).view(np.uint32)), "DVL scores differ"
+    n_rows = int(dv["tgt_off"][-1])
+    rows = o["rows"]
+    # target row statistics
+    assert np.array_equal(g["row_max"][:n_rows], rows["max"]), "row max differs"
+    assert np.array_equal(g["row_argmax"][:n_rows], rows["argmax"]), "row argmax differs"
+    assert _rel_close(g["row_lse"][:n_rows], rows["lse"]).all(), "row lse differs"
+    cut_eq = g["row_cut"][:n_rows] == rows["cut"]
+    for k in np.nonzero(~cut_eq)[0]:
+        assert rows["margin"][k] < MARGIN, f"top-p cut of packed row {k} differs at margin {rows['margin'][k]}"
+        rep["cut_diff"] += 1
+    assert _rel_close(g["row_kept"][:n_rows][cut_eq], rows["kept_lse"][cut_eq]).all(), "kept lse differs"
+    if w.K == 0:
+        n_pos = int(dv["pos_off"][-1])
+        d = o["drows"]
+        assert np.array_equal(g["d_max"][:n_pos], d["max"]), "draft max differs"
+        assert np.array_equal(g["d_argmax"][:n_pos], d["argmax"]), "draft argmax differs"
+        assert _rel_close(g["d_lse"][:n_pos], d["lse"]).all(), "draft lse differs"
+    else:
+        for r in range(R):
+            Lr = L[r]
+            assert np.array_equal(g["branch_tok"][r, :, :Lr], o["branch_tok"][r, :, :Lr]), f"branch tokens differ (r={r})"
+            assert np.allclose(g["post_w"][r, :Lr], o["post_w"][r, :Lr], rtol=REL, atol=1e-15), f"posterior differs (r={r})"
+            assert _rel_close(g["q_at_draft"][r, :Lr], o["q_x"][r, :Lr]).all(), f"q at draft differs (r={r})"
+    # per-position diagnostics and decisions
+    for r in range(R):
+        Lr = int(L[r])
+        rep["positions"] += Lr
+        if Lr:
+            assert np.array_equal(g["u_acc"][r, :Lr].astype(np.float64), o["u_acc"][r, :Lr]), "uniforms differ"
+            assert _rel_close(g["p_x"][r, :Lr], o["p_x"][r, :Lr]).all(), f"p(x) differs (r={r})"
+            assert _rel_close(g["q_x"][r, :Lr], o["q_x"][r, :Lr]).all(), f"q(x) differs (r={r})"
+        ng, no = int(g["n_acc"][r]), int(o["n_acc"][r])
+        if ng != no:
+            k = min(ng, no)
+            m = o["acc_margin"][r, k]
+            rep["mismatches"] += 1
+            rep["low_margin"].append(("accept", r, k, float(m)))
+            assert m < MARGIN, f"n_acc differs for r={r}: gpu {ng} oracle {no}, margin {m}"
+            continue
+        if int(g["is_bonus"][r]) != int(o["is_bonus"][r]):
+            raise AssertionError(f"bonus flag differs for r={r}")
+        if int(g["token"][r]) != int(o["token"][r]):
+            m = o["sample_margin"][r]
+            rep["mismatches"] += 1
+            rep["low_margin"].append(("sample", r, no, float(m)))
+            assert m < MARGIN, f"token differs for r={r}: gpu {g['token'][r]} oracle {o['token'][r]}, margin {m}"
+    return rep
+
+
+def assert_rate(rep: dict):
+    assert rep["mismatches"] <= 1e-4 * max(rep["positions"], 1), (
+        f"{rep['mismatches']} low-margin mismatches over {rep['positions']} positions")

@@ -1,0 +1,288 @@
+"""GPU parity: libsv (through its C ABI) against the CPU oracle on the same
+seeded inputs.  Needs an MI355X; run with ``-m gpu``."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from harness import assert_rate, compare_step, gpu_step_runner, oracle_step
+
+pytestmark = pytest.mark.gpu
+
+
+def banner(msg):
+    print(f"\n[gpu-case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+
+
+def _sv():
+    import draft_verification_sv_amd as sv
+
+    return sv
+
+
+# ---------------------------------------------------------------- Philox
+@pytest.mark.parametrize("seed", [0, 1, 5, 2**32 + 7, 2**64 - 1])
+def test_philox_words_bitexact(seed):
+    import torch
+
+    sv = _sv()
+    R, n = 33, 17
+    banner(f"sv_philox_uniforms seed={seed} R={R} n={n}")
+    sd = torch.tensor([np.uint64(seed).view(np.int64)], device="cuda")
+    out = torch.zeros(R * n * 4, dtype=torch.int32, device="cuda")
+    sv.sv_philox_uniforms(sd, R, n, out)
+    got = out.cpu().numpy().view(np.uint32).reshape(R, n, 4)
+    assert np.array_equal(got, oracle.uniform_words(seed, R, n))
+
+
+# ---------------------------------------------------------------- DVL
+def _dvl_cases():
+    rng = np.random.default_rng(7)
+    cases = []
+    for R, b in [(1, 1), (3, 5), (32, 16), (7, 64), (300, 16)]:
+        for kind in ("beta", "ties"):
+            if kind == "beta":
+                a = rng.beta(8, 2, size=(R, b)).astype(np.float32)
+            else:
+                a = rng.choice([0.0, 0.5, 0.75, 1.0], size=(R, b)).astype(np.float32)
+            for B in sorted({0, 1, R * b // 2, R * b - 1, R * b, R * b + 5}):
+                if B >= 0:
+                    cases.append((R, b, kind, B, a))
+    return cases
+
+
+@pytest.mark.parametrize("R,b,kind,B,a", _dvl_cases(), ids=lambda v: str(v) if not hasattr(v, "shape") else "a")
+def test_dvl_bitexact(R, b, kind, B, a):
+    import torch
+
+    sv = _sv()
+    banner(f"dvl_alloc_pack R={R} b={b} {kind} B={B}")
+    ws, nb = sv.make_workspace(R, b, 0, 8)
+    d = dict(device="cuda")
+    at = torch.from_numpy(a.reshape(-1)).to(**d)
+    bud = torch.tensor([B], dtype=torch.int32, **d)
+    s = torch.zeros(R * b, dtype=torch.float32, **d)
+    L = torch.zeros(R, dtype=torch.int32, **d)
+    po = torch.zeros(R + 1, dtype=torch.int32, **d)
+    to = torch.zeros(R + 1, dtype=torch.int32, **d)
+    sv.dvl_alloc_pack(at, R, b, bud, s, L, po, to, ws, nb)
+    o = oracle.dvl(a, B)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), o["s"].reshape(-1).view(np.uint32))
+    assert np.array_equal(L.cpu().numpy(), o["L"])
+    assert np.array_equal(po.cpu().numpy(), o["pos_off"])
+    assert np.array_equal(to.cpu().numpy(), o["tgt_off"])
+    assert sv.sv_get_status(ws) == 0
+
+
+# ---------------------------------------------------------------- row statistics
+def _edge_rows(V, rng):
+    base = (3.0 * rng.standard_normal(V)).astype(np.float32)
+    rows = {"normal": base}
+    rows["ties_at_max"] = base.copy()
+    rows["ties_at_max"][[3 % V, (V // 2), V - 1]] = base.max() + 1.0
+    rows["constant"] = np.full(V, -1.25, np.float32)
+    rows["zeros"] = np.zeros(V, np.float32)
+    z = base.copy()
+    z[::5] = 0.0
+    z[1::7] = -0.0
+    rows["with_zeros"] = z
+    t = base.copy()
+    t[::3] = 1e-30
+    rows["tiny"] = t
+    h = base.copy()
+    h[::11] = 3e7
+    rows["huge"] = h
+    rows["wide"] = (40.0 * rng.standard_normal(V)).astype(np.float32)
+    rows["neg_only"] = -np.abs(base) - 0.5
+    return rows
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("V", [1, 7, 1031, 4096, 151936])
+def test_row_stats_edges(dtype, V):
+    import torch
+
+    sv = _sv()
+    from draft_verification_sv_amd.step import row_pitch, to_device_rows
+
+    rng = np.random.default_rng(V)
+    rows = _edge_rows(V, rng)
+    names = list(rows)
+    mat = np.stack([rows[k] for k in names])
+    stored = synth.f32_to_bf16_bits(mat) if dtype == "bf16" else mat
+    settings = [(T, tp) for T in (0.0, 0.5, 1.0, 1.5) for tp in (None, 0.95, 0.5, 1e-3)]
+    R = len(settings)
+    # request k reads all rows with its own (T, top_p): packed rows = R copies
+    allrows = np.concatenate([stored] * R)
+    ld = row_pitch(V, dtype)
+    dev = to_device_rows(allrows, ld)
+    n = len(names)
+    off = torch.arange(R + 1, dtype=torch.int32, device="cuda") * n
+    T = np.array([s[0] for s in settings], np.float32)
+    tp = np.array([1.0 if s[1] is None else s[1] for s in settings], np.float32)
+    banner(f"sv_topp_threshold edges dtype={dtype} V={V} rows={R * n}")
+    ws, nb = sv.make_workspace(R, 16, 0, V)
+    f32, i32, f64 = torch.float32, torch.int32, torch.float64
+    outs = [torch.zeros(R * n, dtype=t, device="cuda") for t in (f32, i32, f64, f32, f64)]
+    sv.sv_topp_threshold(dev, sv.SV_BF16 if dtype == "bf16" else sv.SV_F32, ld, V, off, 0, R, R * n,
+                         torch.from_numpy(T).cuda(), torch.from_numpy(tp).cuda(), *outs, ws, nb)
+    mx, am, lse, cut, kept = [t.cpu().numpy() for t in outs]
+    req = np.repeat(np.arange(R), n)
+    o = oracle.row_stats_batch(allrows, req, T, tp)
+    assert np.array_equal(mx, o["max"])
+    assert np.array_equal(am, o["argmax"])
+    np.testing.assert_allclose(lse, o["lse"], rtol=1e-12, atol=1e-12)
+    ok = cut == o["cut"]
+    assert np.all(ok | (o["margin"] < 1e-6)), list(zip(np.nonzero(~ok)[0], o["margin"][~ok]))
+    np.testing.assert_allclose(kept[ok], o["kept_lse"][ok], rtol=1e-12, atol=1e-12)
+    assert sv.sv_get_status(ws) == 0
+
+
+def test_row_stats_nonfinite_sets_status():
+    import torch
+
+    sv = _sv()
+    from draft_verification_sv_amd.step import to_device_rows
+
+    V = 1024
+    row = np.linspace(-3, 3, V).astype(np.float32)
+    row[17] = np.inf
+    row[99] = np.nan
+    dev = to_device_rows(synth.f32_to_bf16_bits(row[None]), V)
+    ws, nb = sv.make_workspace(1, 16, 0, V)
+    f32, i32, f64 = torch.float32, torch.int32, torch.float64
+    outs = [torch.zeros(1, dtype=t, device="cuda") for t in (f32, i32, f64, f32, f64)]
+    off = torch.tensor([0, 1], dtype=torch.int32, device="cuda")
+    banner("sv_topp_threshold non-finite row")
+    sv.sv_topp_threshold(dev, sv.SV_BF16, V, V, off, 0, 1, 1, torch.ones(1, device="cuda"),
+                         torch.full((1,), 0.9, device="cuda"), *outs, ws, nb)
+    assert sv.sv_get_status(ws) & 0x004
+
+
+def test_host_argument_errors():
+    import torch
+
+    sv = _sv()
+    ws, nb = sv.make_workspace(2, 16, 0, 64)
+    z = torch.zeros(64, device="cuda")
+    with pytest.raises(sv.SvError):  # misaligned row pitch
+        sv.sv_softmax_stats(z, sv.SV_BF16, 63, 60, z, 0, 2, 4, z, z, z, z, ws, nb)
+    with pytest.raises(sv.SvError):  # unknown dtype
+        sv.sv_softmax_stats(z, 7, 64, 60, z, 0, 2, 4, z, z, z, z, ws, nb)
+    with pytest.raises(sv.SvError):  # workspace too small
+        sv.sv_mixture_q(z, sv.SV_BF16, 64, 64, 8, 16, z, z, 2, 32, z, z, z, z, ws, 256)
+
+
+# ---------------------------------------------------------------- whole steps
+SMALL = [
+    (1, dict()),                                   # tiny fp32, T=1 x3 and greedy
+    (2, dict(V=2053, R=4)),                        # independent draft, ragged V
+    (3, dict(V=2053, R=8, steps=3)),               # DVL + independent draft
+    (4, dict(V=4099, R=4)),                        # mixture, T=1.5, top-p
+    (5, dict(V=4099, R=8, steps=4)),               # DVL + mixture + top-p
+    (5, dict(V=64, R=64, steps=3)),                # many requests, tiny vocabulary
+]
+
+
+@pytest.mark.parametrize("c,kw", SMALL, ids=[f"cfg{c}-" + "-".join(f"{k}{v}" for k, v in kw.items()) for c, kw in SMALL])
+def test_config_small(c, kw):
+    w = synth.config(c, **kw)
+    vs, run = gpu_step_runner(w)
+    rep = None
+    for s in range(w.steps):
+        banner(f"{w.name} V={w.V} R={w.R} step={s}")
+        g = run(s)
+        rep = compare_step(w, g, oracle_step(w, s), rep)
+    assert_rate(rep)
+    assert _sv().sv_get_status(vs.ws) == 0
+
+
+@pytest.mark.parametrize("c", [2, 3, 4])
+def test_config_full_size(c):
+    w = synth.config(c)
+    vs, run = gpu_step_runner(w)
+    banner(f"{w.name} full size step 0")
+    g = run(0)
+    rep = compare_step(w, g, oracle_step(w, 0))
+    assert_rate(rep)
+    assert _sv().sv_get_status(vs.ws) == 0
+
+
+def test_config5_full_size_200_steps():
+    """All 200 steps on the GPU; the oracle checks every step's DVL, branch
+    tokens and invariants, and the full decision chain on sampled steps."""
+    steps = int(os.environ.get("SV_CFG5_STEPS", "200"))
+    w = synth.config(5, steps=steps)
+    R, b, K, V = w.R, w.b, w.K, w.V
+    vs, run = gpu_step_runner(w)
+    g_all = oracle.argmax_rows(w.comp.reshape(-1, V)).reshape(R, K, b)
+    sample = set(np.linspace(0, steps - 1, min(steps, 12)).astype(int).tolist())
+    rep = None
+    for s in range(steps):
+        if s % 20 == 0:
+            banner(f"{w.name} step {s}/{steps}")
+        g = run(s)
+        if s in sample:
+            rep = compare_step(w, g, oracle_step(w, s), rep)
+            continue
+        dv = oracle.dvl(w.a[s], w.budget)
+        assert np.array_equal(g["L"], dv["L"]) and np.array_equal(g["tgt_off"], dv["tgt_off"])
+        for r in range(R):
+            Lr = dv["L"][r]
+            assert np.array_equal(g["branch_tok"][r, :, :Lr], g_all[r, :, :Lr])
+        assert np.all((g["n_acc"] >= 0) & (g["n_acc"] <= g["L"]))
+        assert np.array_equal(g["is_bonus"], (g["n_acc"] == g["L"]).astype(np.int32))
+        assert np.all((g["token"] >= 0) & (g["token"] < V))
+    assert_rate(rep)
+    assert _sv().sv_get_status(vs.ws) == 0
+
+
+def test_edge_steps_all_accept_all_reject_empty():
+    """Greedy drafts that match the target argmax (all accepted, bonus), draft
+    tokens outside the nucleus (first position rejected), and requests that
+    DVL gives no slots (L_r = 0: one token from p_1)."""
+    w = synth.config(5, V=1031, R=8, steps=1)
+    R, b, K = w.R, w.b, w.K
+    tv = synth.values(w.tgt)
+    # requests 0-1: greedy target with drafts equal to the target argmax
+    w.T[:2] = 0.0
+    w.x[0, :2] = np.argmax(tv[:2, :b], axis=-1)
+    # make those drafts the greedy branches of every component
+    comp = synth.values(w.comp).copy()
+    for r in range(2):
+        for i in range(b):
+            comp[r, :, i, w.x[0, r, i]] = comp[r, :, i].max() + 1.0
+    w.comp = synth.f32_to_bf16_bits(comp)
+    # request 2: tiny nucleus, draft outside it
+    w.top_p[2] = 1e-6
+    # requests 5-7: scores near zero so DVL starves them
+    w.a[0, 5:] = 1e-3
+    w.budget = 40
+    vs, run = gpu_step_runner(w)
+    banner("edge steps: all-accept / all-reject / empty")
+    g = run(0)
+    o = oracle_step(w, 0)
+    rep = compare_step(w, g, o)
+    assert_rate(rep)
+    assert g["n_acc"][0] == g["L"][0] and g["is_bonus"][0] == 1
+    assert (g["L"][5:] == 0).all()
+
+
+def test_determinism_repeat_runs():
+    w = synth.config(4, V=8191, R=4)
+    vs, run = gpu_step_runner(w)
+    banner("determinism")
+    a = run(0)
+    b = run(0)
+    for k in a:
+        assert np.array_equal(np.asarray(a[k]).view(np.uint8), np.asarray(b[k]).view(np.uint8)), k

@@ -1,0 +1,94 @@
+"""The C-ABI library without a GPU: it loads, exports every function that
+include/sv.h declares (and the binding exposes each under the same name), its
+host-side self-checks pass, and host-detectable argument errors are reported
+before any launch."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def sv():
+    lib_path = os.path.join(ROOT, "draft_verification_sv_amd", "libsv.so")
+    if not os.path.exists(lib_path):
+        from draft_verification_sv_amd import build
+
+        build.build()
+    import draft_verification_sv_amd as m
+
+    return m
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "sv.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ["sv_softmax_stats", "sv_topp_threshold", "sv_mixture_q", "sv_accept", "sv_residual_sample",
+                 "dvl_alloc_pack"]:
+        assert must in names
+
+
+def test_every_declared_symbol_is_exported(sv):
+    lib = C.CDLL(sv.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} not exported by libsv.so"
+        assert callable(getattr(sv, name)), f"binding lacks {name}"
+    assert sorted(sv.EXPORTS) == sorted(declared_functions())
+
+
+def test_host_selftests(sv):
+    assert sv.selftest_host() == {"rows": 0, "philox": 0}
+
+
+def test_workspace_size_grows_with_problem(sv):
+    small = sv.sv_workspace_bytes(4, 16, 0, 1024)
+    big = sv.sv_workspace_bytes(32, 16, 8, 151936)
+    assert 256 <= small < big
+    with pytest.raises(sv.SvError):
+        sv.sv_workspace_bytes(0, 16, 0, 1024)
+    with pytest.raises(sv.SvError):
+        sv.sv_workspace_bytes(4, 65, 0, 1024)
+
+
+def _buf(n, dt=np.float32):
+    a = np.zeros(n + 64, dt)
+    off = (-a.ctypes.data) % 16 // a.itemsize
+    return a[off:off + n]
+
+
+def test_argument_errors_are_reported_before_launch(sv):
+    z = _buf(4096)
+    p = z.ctypes.data
+    ws = _buf(1 << 16, np.uint8)
+    wp, nb = ws.ctypes.data, ws.nbytes
+    L = sv.lib()
+    # row pitch not a 16-byte multiple
+    assert L.sv_softmax_stats(p, sv.SV_BF16, 63, 60, p, 0, 2, 4, p, p, p, p, wp, nb, None) == sv.SV_ERR_ARG
+    # unknown dtype, null pointer, V < 1
+    assert L.sv_softmax_stats(p, 5, 64, 60, p, 0, 2, 4, p, p, p, p, wp, nb, None) == sv.SV_ERR_ARG
+    assert L.sv_softmax_stats(None, 1, 64, 60, p, 0, 2, 4, p, p, p, p, wp, nb, None) == sv.SV_ERR_ARG
+    assert L.sv_softmax_stats(p, 1, 64, 0, p, 0, 2, 4, p, p, p, p, wp, nb, None) == sv.SV_ERR_ARG
+    # top-p call needs its outputs
+    assert L.sv_topp_threshold(p, 1, 64, 60, p, 0, 2, 4, p, p, p, p, p, None, p, wp, nb, None) == sv.SV_ERR_ARG
+    # mixture: K over 64, workspace too small, capacity over R*b
+    assert L.sv_mixture_q(p, 1, 64, 64, 65, 16, p, p, 2, 32, p, p, p, p, wp, nb, None) == sv.SV_ERR_ARG
+    assert L.sv_mixture_q(p, 1, 64, 64, 8, 16, p, p, 2, 32, p, p, p, p, wp, 256, None) == sv.SV_ERR_WORKSPACE
+    assert L.sv_mixture_q(p, 1, 64, 64, 8, 16, p, p, 2, 33, p, p, p, p, wp, nb, None) == sv.SV_ERR_ARG
+    # accept: unknown proposal mode, b over 64
+    args = [p, 1, 64, 64, p, p, 2, 16, p, p, p, p, p]
+    assert L.sv_accept(*args, 9, p, 1, 64, p, p, p, p, p, None, None, None, wp, nb, None) == sv.SV_ERR_ARG
+    args65 = [p, 1, 64, 64, p, p, 2, 65, p, p, p, p, p]
+    assert L.sv_accept(*args65, 1, None, 1, 0, None, None, p, p, p, None, None, None, wp, nb, None) == sv.SV_ERR_ARG
+    # DVL: b over 64, null budget
+    assert L.dvl_alloc_pack(p, 4, 65, p, p, p, p, p, wp, nb, None) == sv.SV_ERR_ARG
+    assert L.dvl_alloc_pack(p, 4, 16, None, p, p, p, p, wp, nb, None) == sv.SV_ERR_ARG
+    assert sv.sv_status_string(sv.SV_ERR_WORKSPACE) == "workspace too small"
