@@ -8,7 +8,8 @@ and bonus sampling, Philox seeds advancing per step.  Synthetic seeded data
 (synth.config(5)).
 
 A timed step is the whole verification path on inputs resident in HBM:
-dvl_alloc_pack -> sv_topp_threshold -> sv_mixture_q -> sv_accept ->
+dvl_alloc_pack, then sv_topp_threshold (target rows, on a second stream) and
+sv_mixture_q (component rows) concurrently, then sv_accept and
 sv_residual_sample.  The target forward is outside the path; its output for
 each step (the packed rows for that step's allocation) is prepared before the
 timed region in a buffer of its own, as the target model would have written it.
@@ -121,16 +122,26 @@ def main():
     print(f"[bench] packed target rows for {S} steps in {time.time() - t_prep:.1f}s", file=sys.stderr, flush=True)
     positions = L_host.sum(axis=1)  # verified positions per step
 
+    side = torch.cuda.Stream(device=dev)  # default priority
+    spx = side.cuda_stream
+    ev_off = torch.cuda.Event()
+    ev_rows = torch.cuda.Event()
+
     def step(s, ev=None):
         sv.dvl_alloc_pack(a_all[s], R, b, budget, s_sc, L, pos_off, tgt_off, ws, nb, sp)
+        # target-row statistics on a second stream, concurrent with the mixture argmax
+        ev_off.record(stream)
+        side.wait_event(ev_off)
         sv.sv_topp_threshold(packed[s], dt, ld, V, tgt_off, 0, R, max_rows, T, top_p, row_max, row_arg, row_lse,
-                             row_cut, row_kept, ws, nb, sp)
+                             row_cut, row_kept, ws, nb, spx)
+        ev_rows.record(side)
         if ev is not None:
             ev[0].record(stream)
         sv.sv_mixture_q(comp, dt, ld, V, K, b, mix, pos_off, R, max_pos, x_all[s], branch_tok, post_w, q_at, ws, nb,
                         sp)
         if ev is not None:
             ev[1].record(stream)
+        stream.wait_event(ev_rows)
         sv.sv_accept(packed[s], dt, ld, V, tgt_off, pos_off, R, b, T, row_arg, row_cut, row_kept, x_all[s],
                      sv.SV_Q_MIXTURE, None, dt, 0, None, None, q_at, seeds[s:s + 1], n_acc, None, None, None, ws, nb,
                      sp)

@@ -219,42 +219,19 @@ __device__ __forceinline__ void raise_status(uint32_t* status, uint32_t bits) {
   __hip_atomic_fetch_or(status, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// ------------------------------------------------------------------ cross-block hand-off
-// Writer side: make this thread's global writes visible at device scope, then
-// count in.  Returns true in exactly one thread of the last block to arrive.
-__device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected) {
-  __threadfence();
-  const uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-  if (prev + 1u == expected) {
-    __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
-    return true;
-  }
-  return false;
-}
-
-template <typename T>
-__device__ __forceinline__ T load_acquire_relaxed(const T* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // ------------------------------------------------------------------ workspace layout
-// [status 256 B][counters: 2*R u32][residual partials: R*S_res*4 doubles][mixture partials: R*b*K*S_mix u64]
+// [status word, 256 B][residual chunk sums: R * S_res * 2 doubles]
+// Cross-block results travel through kernel boundaries (stream order), not
+// through in-kernel fences: a device-scope release on gfx950 writes back the
+// L2, which is far too costly to pay once per block.
 struct WsLayout {
-  size_t status, counters, res_part, mix_part, total;
+  size_t status, res_part, total;
 };
 
-__host__ __device__ inline int mix_chunks(int V, int dtype) {
-  const int per_vec = dtype == SV_BF16 ? 8 : 4;
-  const int nvec = V / per_vec;
-  const int target = 256 * 16;  // vectors per chunk: 16 per thread
-  int s = (nvec + target - 1) / target;
-  return s < 1 ? 1 : s;
-}
-
 __host__ __device__ inline int res_chunks(int V) {
-  const int nvec = V / 8;
-  const int target = 256 * 4;
-  int s = (nvec + target - 1) / target;
+  const int ngroups = (V + 7) / 8;  // 8-value groups
+  const int target = 64 * 4;        // groups per chunk: 4 per lane of one wave
+  int s = (ngroups + target - 1) / target;
   if (s < 1) s = 1;
   if (s > 64) s = 64;
   return s;
@@ -263,14 +240,12 @@ __host__ __device__ inline int res_chunks(int V) {
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 __host__ __device__ inline WsLayout ws_layout(int R, int b, int K, int V) {
+  (void)b;
+  (void)K;
   WsLayout l;
   l.status = 0;
-  l.counters = 256;
-  l.res_part = l.counters + align256(sizeof(uint32_t) * 2 * static_cast<size_t>(R));
-  // mixture chunks: take the larger of the two dtypes' counts so one layout serves both
-  const int smix = mix_chunks(V, SV_F32) > mix_chunks(V, SV_BF16) ? mix_chunks(V, SV_F32) : mix_chunks(V, SV_BF16);
-  l.mix_part = l.res_part + align256(sizeof(double) * 4 * static_cast<size_t>(R) * res_chunks(V));
-  l.total = l.mix_part + align256(sizeof(uint64_t) * static_cast<size_t>(R) * b * (K > 0 ? K : 0) * smix);
+  l.res_part = 256;
+  l.total = l.res_part + align256(sizeof(double) * 2 * static_cast<size_t>(R) * res_chunks(V));
   return l;
 }
 

@@ -11,11 +11,12 @@
 // asc, i asc); with a <= 1 the scores fall along each request, so the choice is
 // prefix-closed and maximises the summed survival (expected accepted length).
 //
-// One block of 1024 threads:
+// One block of 256 threads:
 //   1. per request, the running products (written to s);
 //   2. radix select, 8 bits per pass from the top, of the B-th largest score
 //      (non-negative floats order like their bit patterns), with LDS count
-//      histograms;
+//      histograms; the digit holding the rank is found by a block scan over
+//      the 256 digit counts;
 //   3. per request, positions above the threshold plus the first ties in
 //      (r, i) order, via an exclusive scan of the tie counts over requests;
 //   4. exclusive scans of L and L + 1 into pos_off and tgt_off.
@@ -24,11 +25,14 @@
 
 namespace sv {
 
-constexpr int kDvlNT = 1024;
+constexpr int kDvlNT = 256;
+constexpr int kDvlLds = 8192;  // scores kept in LDS up to this many positions
 
+template <bool kInLds>
 __global__ __launch_bounds__(kDvlNT) void k_dvl(const float* a, int R, int b, const int32_t* budget, float* s,
                                                int32_t* L, int32_t* pos_off, int32_t* tgt_off, uint32_t* status) {
   __shared__ uint32_t hist[256];
+  __shared__ uint32_t skey[kInLds ? kDvlLds : 1];
   __shared__ int scr[kDvlNT / kWave];
   __shared__ uint32_t sh_prefix;
   __shared__ int sh_remaining;
@@ -39,7 +43,7 @@ __global__ __launch_bounds__(kDvlNT) void k_dvl(const float* a, int R, int b, co
     if (tid == 0) raise_status(status, SV_ST_BAD_BUDGET);
     B = 0;
   }
-  // 1. survival scores
+  // 1. survival scores; non-negative floats order like their bit patterns
   bool bad = false;
   for (int r = tid; r < R; r += kDvlNT) {
     float run = 1.0f;
@@ -48,10 +52,15 @@ __global__ __launch_bounds__(kDvlNT) void k_dvl(const float* a, int R, int b, co
       bad |= !(av >= 0.0f && av <= 1.0f);
       run = run * av;
       s[r * b + i] = run;
+      if constexpr (kInLds) skey[r * b + i] = __float_as_uint(run);
     }
   }
   if (bad) raise_status(status, SV_ST_BAD_SCORE);
-  __syncthreads();  // s is re-read below by other threads of this block
+  __syncthreads();  // scores are re-read below by other threads of this block
+  auto key = [&](int e) -> uint32_t {
+    if constexpr (kInLds) return skey[e];
+    else return __float_as_uint(s[e]);
+  };
 
   // 2. threshold: the B-th largest score (rank from the top, ties counted)
   uint32_t thr = 0;
@@ -64,23 +73,18 @@ __global__ __launch_bounds__(kDvlNT) void k_dvl(const float* a, int R, int b, co
       for (int k = tid; k < 256; k += kDvlNT) hist[k] = 0u;
       __syncthreads();
       for (int e = tid; e < n; e += kDvlNT) {
-        const uint32_t kk = __float_as_uint(s[e]);
+        const uint32_t kk = key(e);
         if ((kk & mask) == prefix) atomicAdd(&hist[(kk >> shift) & 255u], 1u);
       }
       __syncthreads();
-      if (tid == 0) {
-        int cum = 0;
-        for (int d = 255; d >= 0; --d) {
-          const int h = static_cast<int>(hist[d]);
-          if (cum + h >= remaining) {
-            prefix |= static_cast<uint32_t>(d) << shift;
-            remaining -= cum;
-            break;
-          }
-          cum += h;
-        }
-        sh_prefix = prefix;
-        sh_remaining = remaining;
+      // digits from the top: thread t holds digit 255 - t; the crossing digit
+      // is the one whose exclusive count from the top is < remaining <= inclusive
+      const int h = tid < 256 ? static_cast<int>(hist[255 - tid]) : 0;
+      int tot;
+      const int excl = block_excl_scan_i32<kDvlNT>(h, scr, &tot);
+      if (tid < 256 && excl < remaining && remaining <= excl + h) {
+        sh_prefix = prefix | (static_cast<uint32_t>(255 - tid) << shift);
+        sh_remaining = remaining - excl;
       }
       __syncthreads();
       prefix = sh_prefix;
@@ -94,8 +98,9 @@ __global__ __launch_bounds__(kDvlNT) void k_dvl(const float* a, int R, int b, co
   const int per = (R + kDvlNT - 1) / kDvlNT;
   const int r0 = tid * per, r1 = min(R, r0 + per);
   int eq_local = 0;
-  for (int r = r0; r < r1; ++r)
-    for (int i = 0; i < b; ++i) eq_local += (!all && !none && __float_as_uint(s[r * b + i]) == thr) ? 1 : 0;
+  if (!all && !none)
+    for (int r = r0; r < r1; ++r)
+      for (int i = 0; i < b; ++i) eq_local += key(r * b + i) == thr ? 1 : 0;
   int eq_total;
   int tie_base = block_excl_scan_i32<kDvlNT>(eq_local, scr, &eq_total);
   int l_local = 0;
@@ -108,7 +113,7 @@ __global__ __launch_bounds__(kDvlNT) void k_dvl(const float* a, int R, int b, co
     } else {
       int gt = 0, eq = 0;
       for (int i = 0; i < b; ++i) {
-        const uint32_t kk = __float_as_uint(s[r * b + i]);
+        const uint32_t kk = key(r * b + i);
         gt += kk > thr ? 1 : 0;
         eq += kk == thr ? 1 : 0;
       }
@@ -143,7 +148,12 @@ extern "C" int32_t dvl_alloc_pack(const float* a, int32_t R, int32_t b, const in
   if (!a || !budget || !s || !L || !pos_off || !tgt_off || !ws) return SV_ERR_ARG;
   if (R < 1 || b < 1 || b > 64 || static_cast<long long>(R) * b > (1LL << 24)) return SV_ERR_ARG;
   if (ws_bytes < 256) return SV_ERR_WORKSPACE;
-  hipLaunchKernelGGL(k_dvl, dim3(1), dim3(kDvlNT), 0, static_cast<hipStream_t>(stream), a, R, b, budget, s, L, pos_off,
-                     tgt_off, status_word(ws));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (R * b <= kDvlLds)
+    hipLaunchKernelGGL(k_dvl<true>, dim3(1), dim3(kDvlNT), 0, st, a, R, b, budget, s, L, pos_off, tgt_off,
+                       status_word(ws));
+  else
+    hipLaunchKernelGGL(k_dvl<false>, dim3(1), dim3(kDvlNT), 0, st, a, R, b, budget, s, L, pos_off, tgt_off,
+                       status_word(ws));
   return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
 }

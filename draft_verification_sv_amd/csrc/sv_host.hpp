@@ -18,8 +18,4 @@ inline bool rows_aligned(const void* base, int32_t dtype, int64_t ld) {
 
 inline uint32_t* status_word(void* ws) { return reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + 0); }
 
-inline uint32_t* counters(void* ws, size_t off) {
-  return reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + off);
-}
-
 }  // namespace sv

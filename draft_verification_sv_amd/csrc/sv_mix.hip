@@ -10,13 +10,14 @@
 //   w_z = q(z|y) [g_j(z) = x_j, j < i] / sum over z of the same,
 //   q(x_i | x_<i) = sum of w_z over z with g_i(z) = x_i.
 //
-// Work split: the K * L_r component rows of every request are cut into S
-// chunks; one 256-thread block streams one chunk with 128-bit loads and
-// reduces (max value, lowest index) in registers, then in the wave and the
-// block.  Each block stores its chunk result and counts in on the request's
-// counter; the last block of a request merges the chunk results in fixed order
-// and runs the posterior recursion over the positions with one lane per
-// category (K <= 64), in double.
+// k_mix_argmax: one 256-thread block per component row (position, category)
+// streams the row once with 128-bit non-temporal loads, two batches of four
+// 16-byte loads in flight per thread (double-buffered; 49 VGPRs keeps eight
+// waves per SIMD, so every row of a step is resident at once), keeps the maximum of every 8-value
+// vector and the winning vector, and reduces (value, lowest index) over the
+// wave and the block.  One block per row needs no cross-block merge.
+// k_mix_post: one wave per request runs the posterior recursion over the
+// positions with one lane per category (K <= 64), in double.
 #include <math.h>
 
 #include "sv_device.hpp"
@@ -25,6 +26,7 @@
 namespace sv {
 
 constexpr int kMixNT = 256;
+constexpr int kMixBatch = 4;  // 16-byte loads per thread per batch (x2 in flight)
 
 struct MixArgs {
   const void* comp;
@@ -37,10 +39,6 @@ struct MixArgs {
   int32_t* branch_tok;
   double* post_w;
   double* q;
-  uint32_t* counters;  // [R]
-  uint64_t* part;      // [max_pos * K * S]
-  int S;               // chunks per row
-  int CV;              // 16-byte vectors per chunk
   uint32_t* status;
 };
 
@@ -51,77 +49,52 @@ __device__ __forceinline__ uint32_t fkey(float f) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-__device__ __forceinline__ float max8(float a0, float a1, float a2, float a3, float a4, float a5, float a6, float a7) {
-  return fmaxf(fmaxf(fmaxf(a0, a1), fmaxf(a2, a3)), fmaxf(fmaxf(a4, a5), fmaxf(a6, a7)));
+template <int DT>
+__device__ __forceinline__ float vec_max(const uint4& d) {
+  if constexpr (DT == SV_BF16) {
+    return fmaxf(fmaxf(fmaxf(bf16_lo(d.x), bf16_hi(d.x)), fmaxf(bf16_lo(d.y), bf16_hi(d.y))),
+                 fmaxf(fmaxf(bf16_lo(d.z), bf16_hi(d.z)), fmaxf(bf16_lo(d.w), bf16_hi(d.w))));
+  } else {
+    return fmaxf(fmaxf(__uint_as_float(d.x), __uint_as_float(d.y)), fmaxf(__uint_as_float(d.z), __uint_as_float(d.w)));
+  }
 }
 
-template <int DT>
-__global__ __launch_bounds__(kMixNT) void k_mixture(MixArgs a) {
-  __shared__ uint64_t red[kMixNT / kWave];
-  __shared__ int s_req;
-  __shared__ int s_last;
-  const int tid = threadIdx.x;
-  const int blk = blockIdx.x;
-  const int c = blk % a.S;
-  const int z = (blk / a.S) % a.K;
-  const int p = blk / (a.S * a.K);
-  const int total = a.pos_off[a.R];
-  if (blk == 0 && tid == 0 && (a.pos_off[0] != 0 || total > a.max_pos || total < 0))
-    raise_status(a.status, SV_ST_BAD_OFFSETS);
-  if (p >= total) return;
-  const int r = find_request<kMixNT>(a.pos_off, a.R, p, &s_req);
-  if (r < 0) {
-    if (tid == 0) raise_status(a.status, SV_ST_BAD_OFFSETS);
-    return;
-  }
-  const int i = p - a.pos_off[r];
-  const int Lr = a.pos_off[r + 1] - a.pos_off[r];
-  if (Lr > a.b) {
-    if (tid == 0) raise_status(a.status, SV_ST_BAD_OFFSETS);
-    return;
-  }
-  const int64_t row = (static_cast<int64_t>(r) * a.K + z) * a.b + i;
-  constexpr int PER = DT == SV_BF16 ? 8 : 4;  // elements per 16-byte vector
-  const size_t esz = DT == SV_BF16 ? 2 : 4;
-  const char* rowp = static_cast<const char*>(a.comp) + static_cast<size_t>(row) * static_cast<size_t>(a.ld) * esz;
-  const uint4* vp = reinterpret_cast<const uint4*>(rowp);
-  const int nvec = a.V / PER;
-  const int v0 = c * a.CV;
-  const int v1 = min(nvec, v0 + a.CV);
-
-  float best = -INFINITY;
+// Streams vectors [v0, v1) of a row with stride NT per thread; returns the
+// thread's best (value, element index) with the lowest index among ties, or
+// index -1 if it saw no vector.
+template <int DT, int NT>
+__device__ __forceinline__ void stream_argmax(const uint4* vp, int v0, int v1, float& best, int& bidx) {
+  constexpr int PER = DT == SV_BF16 ? 8 : 4;
+  best = -INFINITY;
   int bvi = -1;
   uint4 bv = {0, 0, 0, 0};
-  auto vmax = [](const uint4& d) -> float {
-    if constexpr (DT == SV_BF16) {
-      return max8(bf16_lo(d.x), bf16_hi(d.x), bf16_lo(d.y), bf16_hi(d.y), bf16_lo(d.z), bf16_hi(d.z), bf16_lo(d.w),
-                  bf16_hi(d.w));
-    } else {
-      return fmaxf(fmaxf(__uint_as_float(d.x), __uint_as_float(d.y)), fmaxf(__uint_as_float(d.z), __uint_as_float(d.w)));
+  int v = v0 + static_cast<int>(threadIdx.x);
+  uint4 cur[kMixBatch];
+#pragma unroll
+  for (int k = 0; k < kMixBatch; ++k)
+    if (v + k * NT < v1) cur[k] = load16_stream(vp + v + k * NT);
+  while (v < v1) {
+    const int vn = v + kMixBatch * NT;
+    uint4 nxt[kMixBatch];
+#pragma unroll
+    for (int k = 0; k < kMixBatch; ++k)
+      if (vn + k * NT < v1) nxt[k] = load16_stream(vp + vn + k * NT);
+#pragma unroll
+    for (int k = 0; k < kMixBatch; ++k) {
+      if (v + k * NT < v1) {
+        const float m = vec_max<DT>(cur[k]);
+        if (m > best) {
+          best = m;
+          bvi = v + k * NT;
+          bv = cur[k];
+        }
+      }
     }
-  };
-  int v = v0 + tid;
-  for (; v + 3 * kMixNT < v1; v += 4 * kMixNT) {
-    const uint4 d0 = load16_stream(vp + v);
-    const uint4 d1 = load16_stream(vp + v + kMixNT);
-    const uint4 d2 = load16_stream(vp + v + 2 * kMixNT);
-    const uint4 d3 = load16_stream(vp + v + 3 * kMixNT);
-    float m;
-    m = vmax(d0);
-    if (m > best) { best = m; bvi = v; bv = d0; }
-    m = vmax(d1);
-    if (m > best) { best = m; bvi = v + kMixNT; bv = d1; }
-    m = vmax(d2);
-    if (m > best) { best = m; bvi = v + 2 * kMixNT; bv = d2; }
-    m = vmax(d3);
-    if (m > best) { best = m; bvi = v + 3 * kMixNT; bv = d3; }
+#pragma unroll
+    for (int k = 0; k < kMixBatch; ++k) cur[k] = nxt[k];
+    v = vn;
   }
-  for (; v < v1; v += kMixNT) {
-    const uint4 d0 = load16_stream(vp + v);
-    const float m = vmax(d0);
-    if (m > best) { best = m; bvi = v; bv = d0; }
-  }
-  int bidx = -1;
+  bidx = -1;
   if (bvi >= 0) {
     float e[PER];
     if constexpr (DT == SV_BF16) {
@@ -136,55 +109,82 @@ __global__ __launch_bounds__(kMixNT) void k_mixture(MixArgs a) {
       if (e[q] == best) k = q;
     bidx = bvi * PER + k;
   }
-  if (c == a.S - 1) {  // elements past the last full vector
-    const int e = nvec * PER + tid;
-    if (e < a.V) {
-      const float f = load_val<DT>(rowp, e);
-      if (f > best || bidx < 0) {
-        best = f;
-        bidx = e;
-      }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kMixNT) void k_mix_argmax(MixArgs a) {
+  __shared__ uint64_t red[kMixNT / kWave];
+  __shared__ int s_req;
+  const int tid = threadIdx.x;
+  const int z = blockIdx.x % a.K;
+  const int p = blockIdx.x / a.K;
+  const int total = a.pos_off[a.R];
+  if (blockIdx.x == 0 && tid == 0 && (a.pos_off[0] != 0 || total > a.max_pos || total < 0))
+    raise_status(a.status, SV_ST_BAD_OFFSETS);
+  if (p >= total) return;
+  const int r = find_request<kMixNT>(a.pos_off, a.R, p, &s_req);
+  if (r < 0) {
+    if (tid == 0) raise_status(a.status, SV_ST_BAD_OFFSETS);
+    return;
+  }
+  const int i = p - a.pos_off[r];
+  if (i >= a.b) {
+    if (tid == 0) raise_status(a.status, SV_ST_BAD_OFFSETS);
+    return;
+  }
+  constexpr int PER = DT == SV_BF16 ? 8 : 4;
+  const size_t esz = DT == SV_BF16 ? 2 : 4;
+  const int64_t row = (static_cast<int64_t>(r) * a.K + z) * a.b + i;
+  const char* rowp = static_cast<const char*>(a.comp) + static_cast<size_t>(row) * static_cast<size_t>(a.ld) * esz;
+  const int nvec = a.V / PER;
+  float best;
+  int bidx;
+  stream_argmax<DT, kMixNT>(reinterpret_cast<const uint4*>(rowp), 0, nvec, best, bidx);
+  const int e = nvec * PER + tid;  // elements past the last full vector
+  if (e < a.V) {
+    const float f = load_val<DT>(rowp, e);
+    if (f > best || bidx < 0) {
+      best = f;
+      bidx = e;
     }
   }
   uint64_t packed = bidx >= 0 ? (static_cast<uint64_t>(fkey(best)) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(bidx)) : 0;
   packed = block_max_u64<kMixNT>(packed, red);
-  if (tid == 0) {
-    a.part[(static_cast<size_t>(p) * a.K + z) * a.S + c] = packed;
-    s_last = arrive_last(&a.counters[r], static_cast<uint32_t>(Lr) * a.K * a.S) ? 1 : 0;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  if (tid >= kWave) return;
+  if (tid == 0)
+    a.branch_tok[(static_cast<size_t>(r) * a.K + z) * a.b + i] =
+        packed ? static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(packed)) : 0;
+}
 
-  // ---- last block of request r: branch tokens and the posterior recursion
-  const int lane = tid;
+__global__ __launch_bounds__(kWave) void k_mix_post(MixArgs a) {
+  __shared__ int gtab[64 * 64];  // branch tokens of this request, [z][i]
+  __shared__ int xtab[64];
+  const int r = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int base = a.pos_off[r];
+  const int Lr = a.pos_off[r + 1] - base;
+  if (Lr < 0 || Lr > a.b || a.pos_off[a.R] > a.max_pos) return;  // reported by k_mix_argmax
+  // all loads first: the recursion below then runs out of LDS and registers
+  for (int k = lane; k < a.K * Lr; k += kWave) {
+    const int zz = k / Lr, ii = k % Lr;
+    gtab[zz * 64 + ii] = a.branch_tok[(static_cast<size_t>(r) * a.K + zz) * a.b + ii];
+  }
+  if (lane < Lr) xtab[lane] = a.x[static_cast<size_t>(r) * a.b + lane];
   const bool act = lane < a.K;
   const float ml = act ? a.mix[static_cast<size_t>(r) * a.K + lane] : -INFINITY;
+  __syncthreads();
   float mmax = ml;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, o, kWave));
   const double e = act ? exp(static_cast<double>(ml) - static_cast<double>(mmax)) : 0.0;
   const double pi = e / wave_sum_f64(e);  // q(z | y)
   bool consistent = act;
-  const int base = a.pos_off[r];
   for (int ii = 0; ii < Lr; ++ii) {
-    int g = 0;
-    if (act) {
-      uint64_t best_p = 0;
-      const uint64_t* pp = a.part + (static_cast<size_t>(base + ii) * a.K + lane) * a.S;
-      for (int cc = 0; cc < a.S; ++cc) {
-        const uint64_t t = load_acquire_relaxed(pp + cc);
-        best_p = t > best_p ? t : best_p;
-      }
-      g = best_p ? static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(best_p)) : 0;
-      a.branch_tok[(static_cast<size_t>(r) * a.K + lane) * a.b + ii] = g;
-    }
+    const int g = act ? gtab[lane * 64 + ii] : -1;
     const double w = consistent ? pi : 0.0;
     const double sw = wave_sum_f64(w);
     const double post = sw > 0.0 ? w / sw : 0.0;
     if (act) a.post_w[(static_cast<size_t>(r) * a.b + ii) * a.K + lane] = post;
-    const int xi = a.x[static_cast<size_t>(r) * a.b + ii];
+    const int xi = xtab[ii];
     const double qsum = wave_sum_f64(act && g == xi ? post : 0.0);
     if (lane == 0) {
       a.q[static_cast<size_t>(r) * a.b + ii] = qsum;
@@ -208,24 +208,19 @@ extern "C" int32_t sv_mixture_q(const void* comp_logits, int32_t dtype, int64_t 
   if (R < 1 || V < 1 || K < 1 || K > 64 || b < 1 || b > 64 || ld < V || max_pos < 0) return SV_ERR_ARG;
   if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_ARG;
   if (!rows_aligned(comp_logits, dtype, ld)) return SV_ERR_ARG;
-  if (max_pos > R * b) return SV_ERR_ARG;
-  const WsLayout l = ws_layout(R, b, K, V);
-  if (ws_bytes < l.total) return SV_ERR_WORKSPACE;
+  if (static_cast<long long>(max_pos) > static_cast<long long>(R) * b) return SV_ERR_ARG;
+  if (ws_bytes < ws_layout(R, b, K, V).total) return SV_ERR_WORKSPACE;
   if (max_pos == 0) return SV_OK;
-  const int per = dtype == SV_BF16 ? 8 : 4;
-  const int nvec = V / per;
-  const int S = mix_chunks(V, dtype);
-  int CV = (nvec + S - 1) / S;
-  if (CV < 1) CV = 1;
   MixArgs a{comp_logits, ld, V, K, b, mix_logits, pos_off, R, max_pos, draft_tok, branch_tok, post_w, q_at_draft,
-            counters(ws, l.counters), reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + l.mix_part), S, CV,
             status_word(ws)};
-  const long long grid = static_cast<long long>(max_pos) * K * S;
+  const long long grid = static_cast<long long>(max_pos) * K;
   if (grid > 0x7FFFFFFFLL) return SV_ERR_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == SV_BF16)
-    hipLaunchKernelGGL(k_mixture<SV_BF16>, dim3(static_cast<unsigned>(grid)), dim3(kMixNT), 0, s, a);
+    hipLaunchKernelGGL(k_mix_argmax<SV_BF16>, dim3(static_cast<unsigned>(grid)), dim3(kMixNT), 0, s, a);
   else
-    hipLaunchKernelGGL(k_mixture<SV_F32>, dim3(static_cast<unsigned>(grid)), dim3(kMixNT), 0, s, a);
+    hipLaunchKernelGGL(k_mix_argmax<SV_F32>, dim3(static_cast<unsigned>(grid)), dim3(kMixNT), 0, s, a);
+  if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
+  hipLaunchKernelGGL(k_mix_post, dim3(R), dim3(kWave), 0, s, a);
   return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
 }

@@ -27,7 +27,8 @@
 
 namespace sv {
 
-constexpr int kRowNT = 512;
+constexpr int kRowNT = 1024;
+constexpr int kRowBatch = 8;  // 16-byte loads in flight per thread (double-buffered)
 constexpr uint32_t kExpLo = 103u << 7;  // |v| >= 2^-24: biased exponent 103
 constexpr int kSide = 6144;             // 48 exponents x 128 mantissas
 constexpr int kNBins = 2 * kSide + 2;   // [0] negative special, [1..6144] negative values,
@@ -237,28 +238,32 @@ __global__ __launch_bounds__(kRowNT) void k_row_stats(RowArgs a) {
     int bvec = -1;
     uint4 bbins = {0, 0, 0, 0};
     int v = tid;
-    for (; v + 3 * kRowNT < nvec; v += 4 * kRowNT) {
-      const uint4 d0 = load16_stream(vp + v);
-      const uint4 d1 = load16_stream(vp + v + kRowNT);
-      const uint4 d2 = load16_stream(vp + v + 2 * kRowNT);
-      const uint4 d3 = load16_stream(vp + v + 3 * kRowNT);
-      uint4 bb;
-      uint32_t vm;
-      count_vec(hist, d0, bb, vm);
-      if (vm > best) { best = vm; bvec = v; bbins = bb; }
-      count_vec(hist, d1, bb, vm);
-      if (vm > best) { best = vm; bvec = v + kRowNT; bbins = bb; }
-      count_vec(hist, d2, bb, vm);
-      if (vm > best) { best = vm; bvec = v + 2 * kRowNT; bbins = bb; }
-      count_vec(hist, d3, bb, vm);
-      if (vm > best) { best = vm; bvec = v + 3 * kRowNT; bbins = bb; }
-    }
-    for (; v < nvec; v += kRowNT) {
-      const uint4 d0 = load16_stream(vp + v);
-      uint4 bb;
-      uint32_t vm;
-      count_vec(hist, d0, bb, vm);
-      if (vm > best) { best = vm; bvec = v; bbins = bb; }
+    uint4 cur[kRowBatch];
+#pragma unroll
+    for (int k = 0; k < kRowBatch; ++k)
+      if (v + k * kRowNT < nvec) cur[k] = load16_stream(vp + v + k * kRowNT);
+    while (v < nvec) {
+      const int vn = v + kRowBatch * kRowNT;
+      uint4 nxt[kRowBatch];
+#pragma unroll
+      for (int k = 0; k < kRowBatch; ++k)
+        if (vn + k * kRowNT < nvec) nxt[k] = load16_stream(vp + vn + k * kRowNT);
+#pragma unroll
+      for (int k = 0; k < kRowBatch; ++k) {
+        if (v + k * kRowNT < nvec) {
+          uint4 bb;
+          uint32_t vm;
+          count_vec(hist, cur[k], bb, vm);
+          if (vm > best) {
+            best = vm;
+            bvec = v + k * kRowNT;
+            bbins = bb;
+          }
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kRowBatch; ++k) cur[k] = nxt[k];
+      v = vn;
     }
     int bidx = -1;
     if (bvec >= 0) {

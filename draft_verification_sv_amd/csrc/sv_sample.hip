@@ -11,12 +11,13 @@
 // k_accept: one wave per request, one lane per position (b <= 64); p and q at
 // the draft token are gathered and compared in double; a ballot over the
 // rejecting lanes gives the first rejection.
-// k_residual: the sampled row of each request is cut into S chunks.  Pass 1:
-// each block forms the weights of its chunk in double and sums them.  The last
-// block of the request (counter hand-off) picks the chunk holding u * W from
-// the chunk sums in fixed order, then scans that chunk in tiles of 256 x 8
-// elements with an LDS-staged block prefix scan to find the first index whose
-// running weight exceeds u * W.
+// The sampled row of each request is cut into S <= 64 chunks.  k_res_sums: one
+// wave per chunk forms the weights of its chunk in double and stores their sum
+// (and the sum of p).  k_res_pick (after a kernel boundary): one wave per
+// request scans the chunk sums (one per lane) to find the chunk holding u * W,
+// then walks that chunk 512 values at a time: per-lane sums of 8 consecutive
+// weights, a shuffle scan across the wave, and a ballot for the first lane
+// whose running weight exceeds u * W.
 #include <math.h>
 
 #include "sv_device.hpp"
@@ -55,8 +56,7 @@ struct SampleArgs {
   double* p_out;
   double* q_out;
   float* u_out;
-  uint32_t* counters;  // [R] (residual)
-  double* part;        // [R * S * 4] (residual)
+  double* part;        // [R * S * 2] chunk sums (residual)
   int S;               // chunks per row (residual)
   int CG;              // 8-element groups per chunk (residual)
   uint32_t* status;
@@ -128,7 +128,11 @@ __global__ __launch_bounds__(kWave) void k_accept(SampleArgs a) {
 }
 
 // ------------------------------------------------------------------ residual / bonus
-constexpr int kResNT = 256;
+// One wave per block.  A chunk is a run of 8-value groups; lane l takes groups
+// l, l + 64, l + 128, ... so every load instruction of the wave reads 1 KiB of
+// consecutive logits, and 64 consecutive groups form a "row" of 512 values that
+// the wave scans with shuffles.
+constexpr int kResChunks = 64;
 
 // 8 consecutive values starting at element 8g (elements >= V read as -inf)
 __device__ __forceinline__ void load8(const char* rowp, int dtype, int g, int V, float out[8]) {
@@ -150,29 +154,77 @@ __device__ __forceinline__ void load8(const char* rowp, int dtype, int g, int V,
   }
 }
 
-struct ResShared {
-  double red[kResNT / kWave];
-  int redi[kResNT / kWave];
-  int tok[64];
-  double qv[64];
-  int nt;
-  int req_ok;
-  int last;
-  double wc[64];  // chunk sums used by the draw
-  int use_p;
-  int cstar;
-  double base;
-  double t;
+// What one request's draw needs; filled by res_setup.
+struct ResCtx {
+  int j, trow;
+  bool bonus;
+  double Td, kept, dlse;
+  float cut;
+  const char* trowp;
+  const char* drowp;
+  int nq;        // mixture: branch entries at slot j (K, with their posterior mass)
+  int qtok[64];  // kept in LDS
+  double qw[64];
 };
 
+// Returns false when the request needs no scan (T = 0: the draw is the argmax,
+// written here by the reporting kernel).
 template <bool kDense>
-__device__ __forceinline__ void weights8(const SampleArgs& a, const ResShared& sh, const char* trowp, const char* drowp,
-                                         int g, bool use_p, float cut, double Td, double kept, double dlse, double p8[8],
+__device__ __forceinline__ bool res_setup(const SampleArgs& a, int r, bool report, ResCtx& c) {
+  const int lane = threadIdx.x;
+  const int pb = a.pos_off[r];
+  const int Lr = a.pos_off[r + 1] - pb;
+  const int tb = a.tgt_off[r];
+  if (!(Lr >= 0 && Lr <= a.b && a.tgt_off[r + 1] - tb == Lr + 1)) {
+    if (report && lane == 0) raise_status(a.status, SV_ST_BAD_OFFSETS);
+    return false;
+  }
+  int n = a.n_acc_in[r];
+  if (n < 0 || n > Lr) {
+    if (report && lane == 0) raise_status(a.status, SV_ST_BAD_NACC);
+    n = n < 0 ? 0 : Lr;
+  }
+  c.j = n;  // 0-based slot of the draw
+  c.bonus = n == Lr;
+  c.trow = tb + n;
+  const float T = a.T[r];
+  if (T == 0.0f) {  // p is one-hot at the argmax, and so is the residual
+    if (report && lane == 0) {
+      a.token[r] = a.row_argmax[c.trow];
+      a.is_bonus[r] = c.bonus ? 1 : 0;
+    }
+    return false;
+  }
+  c.Td = static_cast<double>(T);
+  c.cut = a.row_cut[c.trow];
+  c.kept = a.row_kept[c.trow];
+  c.trowp = row_ptr(a.tgt, a.dtype, c.trow, a.tgt_ld);
+  c.drowp = nullptr;
+  c.dlse = 0.0;
+  c.nq = 0;
+  if (kDense && !c.bonus) {
+    c.drowp = row_ptr(a.draft, a.ddtype, static_cast<int64_t>(r) * a.b + n, a.draft_ld);
+    c.dlse = a.dlse[pb + n];
+  }
+  if (!kDense && !c.bonus) {  // branch tokens at slot j with their posterior mass
+    if (lane < a.K) {
+      c.qtok[lane] = a.branch_tok[(static_cast<size_t>(r) * a.K + lane) * a.b + n];
+      c.qw[lane] = a.post_w[(static_cast<size_t>(r) * a.b + n) * a.K + lane];
+    }
+    c.nq = a.K;
+  }
+  __syncthreads();  // one wave: orders the LDS table before use
+  return true;
+}
+
+// p (target, with top-p) and the draw weight w of 8 values of group g
+template <bool kDense>
+__device__ __forceinline__ void weights8(const SampleArgs& a, const ResCtx& c, int g, bool use_p, double p8[8],
                                          double w8[8]) {
   float l[8];
-  load8(trowp, a.dtype, g, a.V, l);
+  load8(c.trowp, a.dtype, g, a.V, l);
 #pragma unroll
-  for (int k = 0; k < 8; ++k) p8[k] = p_of(l[k], cut, Td, kept);
+  for (int k = 0; k < 8; ++k) p8[k] = p_of(l[k], c.cut, c.Td, c.kept);
   if (use_p) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) w8[k] = p8[k];
@@ -180,185 +232,125 @@ __device__ __forceinline__ void weights8(const SampleArgs& a, const ResShared& s
   }
   if constexpr (kDense) {
     float d[8];
-    load8(drowp, a.ddtype, g, a.V, d);
+    load8(c.drowp, a.ddtype, g, a.V, d);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const double q = exp(static_cast<double>(d[k]) / Td - dlse);
+      const double q = exp(static_cast<double>(d[k]) / c.Td - c.dlse);
       const double t = p8[k] - q;
       w8[k] = t > 0.0 ? t : 0.0;
     }
   } else {
+    const int v0 = g * 8;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      w8[k] = p8[k];
-      const int v = g * 8 + k;
-      for (int t = 0; t < sh.nt; ++t)
-        if (sh.tok[t] == v) {
-          const double d = p8[k] - sh.qv[t];
-          w8[k] = d > 0.0 ? d : 0.0;
-        }
+    for (int k = 0; k < 8; ++k) w8[k] = p8[k];
+    for (int t = 0; t < c.nq; ++t) {  // q(v | x_<j) = sum of the posterior over branches at v
+      const int dv = c.qtok[t] - v0;
+      if (dv >= 0 && dv < 8) {
+        double q = 0.0;
+        for (int t2 = 0; t2 < c.nq; ++t2)
+          if (c.qtok[t2] == c.qtok[t]) q += c.qw[t2];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (k == dv) {
+            const double d = p8[k] - q;
+            w8[k] = d > 0.0 ? d : 0.0;
+          }
+      }
     }
   }
 }
 
 template <bool kDense>
-__global__ __launch_bounds__(kResNT) void k_residual(SampleArgs a) {
-  __shared__ ResShared sh;
-  const int tid = threadIdx.x;
+__global__ __launch_bounds__(kWave) void k_res_sums(SampleArgs a) {
+  __shared__ ResCtx c;
+  const int lane = threadIdx.x;
   const int r = blockIdx.x / a.S;
-  const int c = blockIdx.x % a.S;
-  const int pb = a.pos_off[r];
-  const int Lr = a.pos_off[r + 1] - pb;
-  const int tb = a.tgt_off[r];
-  if (!(Lr >= 0 && Lr <= a.b && a.tgt_off[r + 1] - tb == Lr + 1)) {
-    if (tid == 0 && c == 0) raise_status(a.status, SV_ST_BAD_OFFSETS);
-    return;
-  }
-  int n = a.n_acc_in[r];
-  if (n < 0 || n > Lr) {
-    if (tid == 0 && c == 0) raise_status(a.status, SV_ST_BAD_NACC);
-    n = n < 0 ? 0 : Lr;
-  }
-  const int j = n;  // 0-based slot of the draw
-  const bool bonus = n == Lr;
-  const int trow = tb + j;
-  const float T = a.T[r];
-  if (T == 0.0f) {  // p is one-hot at the argmax, and so is the residual
-    if (c == 0 && tid == 0) {
-      a.token[r] = a.row_argmax[trow];
-      a.is_bonus[r] = bonus ? 1 : 0;
-    }
-    return;
-  }
-  const double Td = static_cast<double>(T);
-  const float cut = a.row_cut[trow];
-  const double kept = a.row_kept[trow];
-  const char* trowp = row_ptr(a.tgt, a.dtype, trow, a.tgt_ld);
-  const char* drowp = nullptr;
-  double dlse = 0.0;
-  if (kDense && !bonus) {
-    drowp = row_ptr(a.draft, a.ddtype, static_cast<int64_t>(r) * a.b + j, a.draft_ld);
-    dlse = a.dlse[pb + j];
-  }
-  if (tid == 0) {
-    sh.nt = 0;
-    if (!kDense && !bonus) {  // distinct branch tokens at slot j with their mixture mass
-      for (int zz = 0; zz < a.K; ++zz) {
-        const double w = a.post_w[(static_cast<size_t>(r) * a.b + j) * a.K + zz];
-        if (!(w > 0.0)) continue;
-        const int t = a.branch_tok[(static_cast<size_t>(r) * a.K + zz) * a.b + j];
-        int slot = -1;
-        for (int s2 = 0; s2 < sh.nt; ++s2)
-          if (sh.tok[s2] == t) slot = s2;
-        if (slot < 0) {
-          slot = sh.nt++;
-          sh.tok[slot] = t;
-          sh.qv[slot] = 0.0;
-        }
-        sh.qv[slot] += w;
-      }
-    }
-  }
-  __syncthreads();
-
-  // ---- pass 1: chunk sums of p and of the residual weights
+  const int ch = blockIdx.x % a.S;
+  if (!res_setup<kDense>(a, r, false, c)) return;
   const int NG = (a.V + 7) / 8;
-  const int g0 = c * a.CG;
+  const int g0 = ch * a.CG;
   const int g1 = min(NG, g0 + a.CG);
   double sp = 0.0, sw = 0.0;
-  for (int g = g0 + tid; g < g1; g += kResNT) {
+  for (int g = g0 + lane; g < g1; g += kWave) {
     double p8[8], w8[8];
-    weights8<kDense>(a, sh, trowp, drowp, g, bonus, cut, Td, kept, dlse, p8, w8);
+    weights8<kDense>(a, c, g, c.bonus, p8, w8);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       sp += p8[k];
       sw += w8[k];
     }
   }
-  sp = block_sum_f64<kResNT>(sp, sh.red);
-  sw = block_sum_f64<kResNT>(sw, sh.red);
-  if (tid == 0) {
-    double* pp = a.part + (static_cast<size_t>(r) * a.S + c) * 4;
+  sp = wave_sum_f64(sp);
+  sw = wave_sum_f64(sw);
+  if (lane == 0) {
+    double* pp = a.part + (static_cast<size_t>(r) * a.S + ch) * 2;
     pp[0] = sw;
     pp[1] = sp;
-    sh.last = arrive_last(&a.counters[r], static_cast<uint32_t>(a.S)) ? 1 : 0;
   }
-  __syncthreads();
-  if (!sh.last) return;
-  __threadfence();
+}
 
-  // ---- last block: pick the chunk, then scan it
-  const uint64_t seed = *a.seed;
-  const double u = u24(philox_at(seed, static_cast<uint32_t>(j), static_cast<uint32_t>(r)).y);
-  if (tid == 0) {
-    double W = 0.0;
-    for (int cc = 0; cc < a.S; ++cc) W += load_acquire_relaxed(a.part + (static_cast<size_t>(r) * a.S + cc) * 4);
-    const bool use_p = bonus || !(W > 0.0);  // an all-zero residual (rounding) falls back to p
-    W = 0.0;
-    for (int cc = 0; cc < a.S; ++cc) {
-      sh.wc[cc] = load_acquire_relaxed(a.part + (static_cast<size_t>(r) * a.S + cc) * 4 + (use_p ? 1 : 0));
-      W += sh.wc[cc];
-    }
-    const double t = u * W;
-    double run = 0.0, base = 0.0;
-    int cstar = a.S - 1;
-    for (int cc = 0; cc < a.S; ++cc) {
-      const double nxt = run + sh.wc[cc];
-      base = run;
-      if (nxt > t) {
-        cstar = cc;
-        break;
-      }
-      run = nxt;
-    }
-    sh.use_p = use_p ? 1 : 0;
-    sh.cstar = cstar;
-    sh.base = base;
-    sh.t = t;
-  }
-  __syncthreads();
-  const bool use_p = sh.use_p != 0;
-  const int cstar = sh.cstar;
-  double run = sh.base;
-  const double t = sh.t;
+template <bool kDense>
+__global__ __launch_bounds__(kWave) void k_res_pick(SampleArgs a) {
+  __shared__ ResCtx c;
+  const int lane = threadIdx.x;
+  const int r = blockIdx.x;
+  if (!res_setup<kDense>(a, r, true, c)) return;
+  const double u = u24(philox_at(*a.seed, static_cast<uint32_t>(c.j), static_cast<uint32_t>(r)).y);
+  // chunk sums, one per lane, in chunk order
+  const double* pp = a.part + static_cast<size_t>(r) * a.S * 2;
+  const double cw = lane < a.S ? pp[lane * 2] : 0.0;
+  const bool use_p = c.bonus || !(wave_sum_f64(cw) > 0.0);  // an all-zero residual (rounding) falls back to p
+  const double wc = lane < a.S ? pp[lane * 2 + (use_p ? 1 : 0)] : 0.0;
+  const double incl = wave_incl_scan_f64(wc);
+  const double W = __shfl(incl, kWave - 1, kWave);
+  const double t = u * W;
+  const uint64_t over = __ballot(lane < a.S && incl > t);
+  const int cstar = over ? __ffsll(static_cast<long long>(over)) - 1 : a.S - 1;
+  double run = __shfl(incl - wc, cstar, kWave);  // weight before chunk cstar
+  // scan chunk cstar, 64 groups (512 values) at a time
+  const int NG = (a.V + 7) / 8;
   const int h0 = cstar * a.CG;
   const int h1 = min(NG, h0 + a.CG);
-  int found = 0x7FFFFFFF;
-  int lastpos = -1;
-  for (int gb = h0; gb < h1; gb += kResNT) {
-    const int g = gb + tid;
+  int found = -1, lastpos = -1;
+  for (int gb = h0; gb < h1; gb += kWave) {
+    const int g = gb + lane;
     double p8[8], w8[8];
     double loc = 0.0;
     if (g < h1) {
-      weights8<kDense>(a, sh, trowp, drowp, g, use_p, cut, Td, kept, dlse, p8, w8);
+      weights8<kDense>(a, c, g, use_p, p8, w8);
 #pragma unroll
       for (int k = 0; k < 8; ++k) loc += w8[k];
     }
-    double tile_tot;
-    const double excl = block_excl_scan_f64<kResNT>(loc, sh.red, &tile_tot);
+    const double inc = wave_incl_scan_f64(loc);
+    int mine = -1;
     if (g < h1) {
-      double acc = run + excl;
+      double acc = run + (inc - loc);
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         if (w8[k] > 0.0) lastpos = g * 8 + k;
         acc += w8[k];
-        if (acc > t && found == 0x7FFFFFFF) found = g * 8 + k;
+        if (acc > t && mine < 0) mine = g * 8 + k;
       }
     }
-    const int fmin = block_min_i32<kResNT>(found, sh.redi);
-    if (fmin != 0x7FFFFFFF) {
-      found = fmin;
+    const uint64_t hit = __ballot(mine >= 0);
+    if (hit) {
+      found = __shfl(mine, __ffsll(static_cast<long long>(hit)) - 1, kWave);
       break;
     }
-    run += tile_tot;
+    run += __shfl(inc, kWave - 1, kWave);
   }
-  if (found == 0x7FFFFFFF) {  // rounding: the last positive weight of the chunk
-    found = -block_min_i32<kResNT>(-lastpos, sh.redi);
-    if (found < 0) found = 0;
+  if (found < 0) {  // rounding: the last positive weight of the chunk
+    int lp = lastpos;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const int q = __shfl_xor(lp, o, kWave);
+      lp = q > lp ? q : lp;
+    }
+    found = lp < 0 ? 0 : lp;
   }
-  if (tid == 0) {
+  if (lane == 0) {
     a.token[r] = found;
-    a.is_bonus[r] = bonus ? 1 : 0;
+    a.is_bonus[r] = c.bonus ? 1 : 0;
   }
 }
 
@@ -422,9 +414,9 @@ extern "C" int32_t sv_residual_sample(const void* tgt_logits, int32_t dtype, int
   if (!n_acc || !token || !is_bonus) return SV_ERR_ARG;
   if (q_mode == SV_Q_MIXTURE && (K < 1 || K > 64 || !branch_tok || !post_w)) return SV_ERR_ARG;
   const WsLayout l = ws_layout(R, b, q_mode == SV_Q_MIXTURE ? K : 0, V);
-  if (ws_bytes < l.res_part + sizeof(double) * 4 * static_cast<size_t>(R) * res_chunks(V)) return SV_ERR_WORKSPACE;
-  const int S = res_chunks(V);
+  if (ws_bytes < l.total) return SV_ERR_WORKSPACE;
   const int NG = (V + 7) / 8;
+  const int S = res_chunks(V);
   const int CG = (NG + S - 1) / S;
   SampleArgs a{};
   a.tgt = tgt_logits; a.dtype = dtype; a.tgt_ld = tgt_ld; a.V = V; a.tgt_off = tgt_off; a.pos_off = pos_off;
@@ -432,14 +424,18 @@ extern "C" int32_t sv_residual_sample(const void* tgt_logits, int32_t dtype, int
   a.q_mode = q_mode; a.draft = draft_logits; a.ddtype = draft_dtype; a.draft_ld = draft_ld; a.dargmax = draft_argmax;
   a.dlse = draft_lse; a.K = K; a.branch_tok = branch_tok; a.post_w = post_w; a.seed = seed; a.n_acc_in = n_acc;
   a.token = token; a.is_bonus = is_bonus; a.status = status_word(ws);
-  a.counters = counters(ws, l.counters) + R;
   a.part = reinterpret_cast<double*>(static_cast<char*>(ws) + l.res_part);
   a.S = S;
   a.CG = CG;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (q_mode == SV_Q_DENSE)
-    hipLaunchKernelGGL(k_residual<true>, dim3(R * S), dim3(kResNT), 0, s, a);
-  else
-    hipLaunchKernelGGL(k_residual<false>, dim3(R * S), dim3(kResNT), 0, s, a);
+  if (q_mode == SV_Q_DENSE) {
+    hipLaunchKernelGGL(k_res_sums<true>, dim3(R * S), dim3(kWave), 0, s, a);
+    if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
+    hipLaunchKernelGGL(k_res_pick<true>, dim3(R), dim3(kWave), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(k_res_sums<false>, dim3(R * S), dim3(kWave), 0, s, a);
+    if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
+    hipLaunchKernelGGL(k_res_pick<false>, dim3(R), dim3(kWave), 0, s, a);
+  }
   return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
 }

@@ -142,10 +142,23 @@ class VerifyStep:
                            None if dense else self.post_w, self.seed, self.n_acc, self.token, self.is_bonus,
                            self.ws, self.ws_bytes, stream)
 
-    def run_verify(self, tgt, tgt_ld, *, draft=None, draft_ld=0, comp=None, comp_ld=0, stream=None):
-        self.run_rows(tgt, tgt_ld, stream)
-        self.run_proposal(draft=draft, draft_ld=draft_ld, comp=comp, comp_ld=comp_ld, stream=stream)
-        self.run_accept(tgt, tgt_ld, draft=draft, draft_ld=draft_ld, stream=stream)
+    def run_verify(self, tgt, tgt_ld, *, draft=None, draft_ld=0, comp=None, comp_ld=0, side_stream=None):
+        """The verification calls on torch's current stream.  With `side_stream`,
+        the target-row statistics run there, concurrently with the proposal."""
+        if side_stream is None:
+            self.run_rows(tgt, tgt_ld)
+            self.run_proposal(draft=draft, draft_ld=draft_ld, comp=comp, comp_ld=comp_ld)
+        else:
+            main = torch.cuda.current_stream()
+            ev = torch.cuda.Event()
+            ev.record(main)
+            side_stream.wait_event(ev)
+            self.run_rows(tgt, tgt_ld, side_stream)
+            done = torch.cuda.Event()
+            done.record(side_stream)
+            self.run_proposal(draft=draft, draft_ld=draft_ld, comp=comp, comp_ld=comp_ld)
+            main.wait_event(done)
+        self.run_accept(tgt, tgt_ld, draft=draft, draft_ld=draft_ld)
 
     # ---------------------------------------------------------------- read-back (tests)
     def results(self) -> dict:

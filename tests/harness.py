@@ -19,7 +19,7 @@ REL = 1e-5
 MARGIN = 1e-6
 
 
-def gpu_step_runner(w: synth.Workload, device="cuda"):
+def gpu_step_runner(w: synth.Workload, device="cuda", two_streams: bool = False):
     """Upload a workload once and return (VerifyStep, run(s) -> results)."""
     import torch
 
@@ -33,6 +33,7 @@ def gpu_step_runner(w: synth.Workload, device="cuda"):
     packed = torch.empty_like(full)
     draft = to_device_rows(w.draft, ld, device) if K == 0 else None
     comp = to_device_rows(w.comp, ld, device) if K > 0 else None
+    side = torch.cuda.Stream() if two_streams else None
 
     def run(s: int) -> dict:
         vs.set_inputs(T=w.T, x=w.x[s], seed=int(w.seeds[s]), top_p=w.top_p, mix=w.mix,
@@ -44,7 +45,7 @@ def gpu_step_runner(w: synth.Workload, device="cuda"):
             vs.set_full_verification()
             L = np.full(R, b, np.int32)
         pack_rows_device(full, L, b + 1, packed)
-        vs.run_verify(packed, ld, draft=draft, draft_ld=ld, comp=comp, comp_ld=ld)
+        vs.run_verify(packed, ld, draft=draft, draft_ld=ld, comp=comp, comp_ld=ld, side_stream=side)
         return vs.results()
 
     return vs, run

@@ -278,6 +278,18 @@ def test_edge_steps_all_accept_all_reject_empty():
     assert (g["L"][5:] == 0).all()
 
 
+@pytest.mark.parametrize("c", [3, 5])
+def test_two_stream_step_matches_oracle(c):
+    """Target-row statistics on a second stream, concurrent with the proposal."""
+    w = synth.config(c, V=4099, R=16, steps=3)
+    vs, run = gpu_step_runner(w, two_streams=True)
+    rep = None
+    for s in range(w.steps):
+        banner(f"two streams {w.name} step {s}")
+        rep = compare_step(w, run(s), oracle_step(w, s), rep)
+    assert_rate(rep)
+
+
 def test_determinism_repeat_runs():
     w = synth.config(4, V=8191, R=4)
     vs, run = gpu_step_runner(w)
