@@ -8,14 +8,14 @@ and bonus sampling, Philox seeds advancing per step.  Synthetic seeded data
 (synth.config(5)).
 
 A timed step is the whole verification path on inputs resident in HBM:
-dvl_alloc_pack, then sv_topp_threshold (target rows, on a second stream) and
-sv_mixture_q (component rows) concurrently, then sv_accept and
-sv_residual_sample.  The target forward is outside the path; its output for
+dvl_alloc_pack, sv_verify_rows (target-row statistics with top-p and the
+mixture proposal in one launch), sv_accept, sv_residual_sample.  The target forward is outside the path; its output for
 each step (the packed rows for that step's allocation) is prepared before the
 timed region in a buffer of its own, as the target model would have written it.
 
-Prints one JSON line.  `roofline` is for the dominant kernel (the mixture
-argmax over the component rows), timed live with HIP events on the stream the
+Prints one JSON line.  `roofline` is for the dominant launch (sv_verify_rows:
+target-row statistics and the branch argmax over the component rows in one
+kernel, plus the posterior), timed live with HIP events on the stream the
 kernels run on; `cpu_baseline` is the CPU oracle on a bounded sample of the
 same workload.
 """
@@ -45,8 +45,10 @@ def parse():
 
 
 def kernel_source_hash() -> str:
-    p = os.path.join(ROOT, "draft_verification_sv_amd", "csrc", "sv_mix.hip")
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in ("sv_mix.hip", "sv_rows_dev.hpp", "sv_device.hpp"):
+        h.update(open(os.path.join(ROOT, "draft_verification_sv_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(kernel: str):
@@ -122,26 +124,17 @@ def main():
     print(f"[bench] packed target rows for {S} steps in {time.time() - t_prep:.1f}s", file=sys.stderr, flush=True)
     positions = L_host.sum(axis=1)  # verified positions per step
 
-    side = torch.cuda.Stream(device=dev)  # default priority
-    spx = side.cuda_stream
-    ev_off = torch.cuda.Event()
-    ev_rows = torch.cuda.Event()
-
     def step(s, ev=None):
         sv.dvl_alloc_pack(a_all[s], R, b, budget, s_sc, L, pos_off, tgt_off, ws, nb, sp)
-        # target-row statistics on a second stream, concurrent with the mixture argmax
-        ev_off.record(stream)
-        side.wait_event(ev_off)
-        sv.sv_topp_threshold(packed[s], dt, ld, V, tgt_off, 0, R, max_rows, T, top_p, row_max, row_arg, row_lse,
-                             row_cut, row_kept, ws, nb, spx)
-        ev_rows.record(side)
         if ev is not None:
             ev[0].record(stream)
-        sv.sv_mixture_q(comp, dt, ld, V, K, b, mix, pos_off, R, max_pos, x_all[s], branch_tok, post_w, q_at, ws, nb,
-                        sp)
+        # target rows (statistics, top-p) and component rows (branch argmax) in one launch,
+        # then the category posterior
+        sv.sv_verify_rows(packed[s], dt, ld, V, tgt_off, R, max_rows, T, top_p, row_max, row_arg, row_lse, row_cut,
+                          row_kept, comp, ld, K, b, mix, pos_off, max_pos, x_all[s], branch_tok, post_w, q_at, ws, nb,
+                          sp)
         if ev is not None:
             ev[1].record(stream)
-        stream.wait_event(ev_rows)
         sv.sv_accept(packed[s], dt, ld, V, tgt_off, pos_off, R, b, T, row_arg, row_cut, row_kept, x_all[s],
                      sv.SV_Q_MIXTURE, None, dt, 0, None, None, q_at, seeds[s:s + 1], n_acc, None, None, None, ws, nb,
                      sp)
@@ -169,7 +162,9 @@ def main():
     torch.cuda.synchronize()
     mix_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
     row_bytes = V * 2
-    mix_bytes = float(np.mean(positions)) * K * row_bytes  # algorithmic: every verified position's K rows once
+    # algorithmic bytes of the dominant launch: every target row (L_r + 1 per request)
+    # and every verified position's K component rows, each read once
+    mix_bytes = float(np.mean((positions + R) * row_bytes + positions * K * row_bytes))
     achieved = mix_bytes / (mix_ms * 1e-3) / 1e9
     # step-aggregate algorithmic bytes: target rows, component rows, one sampled row per request
     step_bytes = (positions + R) * row_bytes + positions * K * row_bytes + R * row_bytes
@@ -180,7 +175,7 @@ def main():
     if not args.no_cpu:
         cpu = cpu_baseline(w, args.cpu_seconds)
 
-    traffic = load_traffic("k_mixture")
+    traffic = load_traffic("k_rows_mix")
     out = {
         "metric": "verified draft positions/sec at V=151936, conc 32; % of peak HBM GB/s",
         "value": round(value, 1),
@@ -199,7 +194,7 @@ def main():
                    "requests": R, "block": b, "vocab": V, "K": K, "budget": B},
         "step_gbps": round(float(np.mean(step_bytes)) / (ms_per_step * 1e-3) / 1e9, 1),
         "step_frac_of_peak": round(float(np.mean(step_bytes)) / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-        "roofline": {"kernel": "k_mixture (sv_mixture_q)", "bound": "hbm", "achieved": round(achieved, 1),
+        "roofline": {"kernel": "k_rows_mix + k_mix_post (sv_verify_rows)", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": traffic, "avg_launch_us": round(mix_ms * 1e3, 2),
                      "algorithmic_bytes_per_launch": mix_bytes},

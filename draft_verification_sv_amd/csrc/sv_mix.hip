@@ -22,6 +22,7 @@
 
 #include "sv_device.hpp"
 #include "sv_host.hpp"
+#include "sv_rows_dev.hpp"
 
 namespace sv {
 
@@ -111,18 +112,17 @@ __device__ __forceinline__ void stream_argmax(const uint4* vp, int v0, int v1, f
   }
 }
 
-template <int DT>
-__global__ __launch_bounds__(kMixNT) void k_mix_argmax(MixArgs a) {
-  __shared__ uint64_t red[kMixNT / kWave];
-  __shared__ int s_req;
+// argmax of component row m = p*K + z (position p, category z) by one block
+template <int DT, int NT>
+__device__ __forceinline__ void mix_block(const MixArgs& a, int m, uint64_t* red, int* s_req) {
   const int tid = threadIdx.x;
-  const int z = blockIdx.x % a.K;
-  const int p = blockIdx.x / a.K;
+  const int z = m % a.K;
+  const int p = m / a.K;
   const int total = a.pos_off[a.R];
-  if (blockIdx.x == 0 && tid == 0 && (a.pos_off[0] != 0 || total > a.max_pos || total < 0))
+  if (m == 0 && tid == 0 && (a.pos_off[0] != 0 || total > a.max_pos || total < 0))
     raise_status(a.status, SV_ST_BAD_OFFSETS);
   if (p >= total) return;
-  const int r = find_request<kMixNT>(a.pos_off, a.R, p, &s_req);
+  const int r = find_request<NT>(a.pos_off, a.R, p, s_req);
   if (r < 0) {
     if (tid == 0) raise_status(a.status, SV_ST_BAD_OFFSETS);
     return;
@@ -139,9 +139,8 @@ __global__ __launch_bounds__(kMixNT) void k_mix_argmax(MixArgs a) {
   const int nvec = a.V / PER;
   float best;
   int bidx;
-  stream_argmax<DT, kMixNT>(reinterpret_cast<const uint4*>(rowp), 0, nvec, best, bidx);
-  const int e = nvec * PER + tid;  // elements past the last full vector
-  if (e < a.V) {
+  stream_argmax<DT, NT>(reinterpret_cast<const uint4*>(rowp), 0, nvec, best, bidx);
+  for (int e = nvec * PER + tid; e < a.V; e += NT) {  // elements past the last full vector
     const float f = load_val<DT>(rowp, e);
     if (f > best || bidx < 0) {
       best = f;
@@ -149,10 +148,41 @@ __global__ __launch_bounds__(kMixNT) void k_mix_argmax(MixArgs a) {
     }
   }
   uint64_t packed = bidx >= 0 ? (static_cast<uint64_t>(fkey(best)) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(bidx)) : 0;
-  packed = block_max_u64<kMixNT>(packed, red);
+  packed = block_max_u64<NT>(packed, red);
   if (tid == 0)
     a.branch_tok[(static_cast<size_t>(r) * a.K + z) * a.b + i] =
         packed ? static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(packed)) : 0;
+}
+
+template <int DT>
+__global__ __launch_bounds__(kMixNT) void k_mix_argmax(MixArgs a) {
+  __shared__ uint64_t red[kMixNT / kWave];
+  __shared__ int s_req;
+  mix_block<DT, kMixNT>(a, blockIdx.x, red, &s_req);
+}
+
+// One launch for the target rows and the component rows of a step: blocks
+// [0, n_row_blocks) take target rows (statistics and top-p cut), the rest take
+// component rows (branch argmax).  Lower block numbers are dispatched first,
+// so the target rows, which carry more work per byte, start at once on every
+// CU and share it with the component streaming.
+constexpr int kFusedNT = 256;
+constexpr int kFusedBatch = 4;
+
+template <int DT>
+__global__ __launch_bounds__(kFusedNT) void k_rows_mix(RowArgs ra, MixArgs ma, int n_row_blocks) {
+  __shared__ RowShared<kFusedNT> sh;
+  __shared__ uint32_t hist[DT == SV_BF16 ? kHistWords : 1];
+  const int blk = blockIdx.x;
+  if (blk < n_row_blocks) {
+    const int total = ra.row_off[ra.R];
+    if (blk == 0 && threadIdx.x == 0 && (ra.row_off[0] != 0 || total > ra.max_rows || total < 0))
+      raise_status(ra.status, SV_ST_BAD_OFFSETS);
+    if (blk >= total) return;
+    row_block<DT, kFusedNT, kFusedBatch>(ra, blk, hist, sh);
+  } else {
+    mix_block<DT, kFusedNT>(ma, blk - n_row_blocks, sh.red_u64, &sh.req);
+  }
 }
 
 __global__ __launch_bounds__(kWave) void k_mix_post(MixArgs a) {
@@ -199,16 +229,26 @@ __global__ __launch_bounds__(kWave) void k_mix_post(MixArgs a) {
 
 using namespace sv;
 
+static bool mix_args_ok(const void* comp_logits, int32_t dtype, int64_t ld, int32_t V, int32_t K, int32_t b,
+                        const float* mix_logits, const int32_t* pos_off, int32_t R, int32_t max_pos,
+                        const int32_t* draft_tok, int32_t* branch_tok, double* post_w, double* q_at_draft, void* ws) {
+  if (!comp_logits || !mix_logits || !pos_off || !draft_tok || !branch_tok || !post_w || !q_at_draft || !ws)
+    return false;
+  if (R < 1 || V < 1 || K < 1 || K > 64 || b < 1 || b > 64 || ld < V || max_pos < 0) return false;
+  if (dtype != SV_F32 && dtype != SV_BF16) return false;
+  if (!rows_aligned(comp_logits, dtype, ld)) return false;
+  if (static_cast<long long>(max_pos) > static_cast<long long>(R) * b) return false;
+  if (static_cast<long long>(max_pos) * K > 0x3FFFFFFFLL) return false;
+  return true;
+}
+
 extern "C" int32_t sv_mixture_q(const void* comp_logits, int32_t dtype, int64_t ld, int32_t V, int32_t K, int32_t b,
                                 const float* mix_logits, const int32_t* pos_off, int32_t R, int32_t max_pos,
                                 const int32_t* draft_tok, int32_t* branch_tok, double* post_w, double* q_at_draft,
                                 void* ws, size_t ws_bytes, void* stream) {
-  if (!comp_logits || !mix_logits || !pos_off || !draft_tok || !branch_tok || !post_w || !q_at_draft || !ws)
+  if (!mix_args_ok(comp_logits, dtype, ld, V, K, b, mix_logits, pos_off, R, max_pos, draft_tok, branch_tok, post_w,
+                   q_at_draft, ws))
     return SV_ERR_ARG;
-  if (R < 1 || V < 1 || K < 1 || K > 64 || b < 1 || b > 64 || ld < V || max_pos < 0) return SV_ERR_ARG;
-  if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_ARG;
-  if (!rows_aligned(comp_logits, dtype, ld)) return SV_ERR_ARG;
-  if (static_cast<long long>(max_pos) > static_cast<long long>(R) * b) return SV_ERR_ARG;
   if (ws_bytes < ws_layout(R, b, K, V).total) return SV_ERR_WORKSPACE;
   if (max_pos == 0) return SV_OK;
   MixArgs a{comp_logits, ld, V, K, b, mix_logits, pos_off, R, max_pos, draft_tok, branch_tok, post_w, q_at_draft,
@@ -222,5 +262,38 @@ extern "C" int32_t sv_mixture_q(const void* comp_logits, int32_t dtype, int64_t 
     hipLaunchKernelGGL(k_mix_argmax<SV_F32>, dim3(static_cast<unsigned>(grid)), dim3(kMixNT), 0, s, a);
   if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
   hipLaunchKernelGGL(k_mix_post, dim3(R), dim3(kWave), 0, s, a);
+  return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
+}
+
+extern "C" int32_t sv_verify_rows(const void* tgt_logits, int32_t dtype, int64_t tgt_ld, int32_t V,
+                                  const int32_t* tgt_off, int32_t R, int32_t max_rows, const float* temperature,
+                                  const float* top_p, float* row_max, int32_t* row_argmax, double* row_lse,
+                                  float* row_cut, double* row_kept_lse, const void* comp_logits, int64_t comp_ld,
+                                  int32_t K, int32_t b, const float* mix_logits, const int32_t* pos_off,
+                                  int32_t max_pos, const int32_t* draft_tok, int32_t* branch_tok, double* post_w,
+                                  double* q_at_draft, void* ws, size_t ws_bytes, void* stream) {
+  if (!tgt_logits || !tgt_off || !temperature || !row_max || !row_argmax || !row_lse || !row_cut || !row_kept_lse)
+    return SV_ERR_ARG;
+  if (max_rows < 0 || tgt_ld < V || !rows_aligned(tgt_logits, dtype, tgt_ld)) return SV_ERR_ARG;
+  if (!mix_args_ok(comp_logits, dtype, comp_ld, V, K, b, mix_logits, pos_off, R, max_pos, draft_tok, branch_tok,
+                   post_w, q_at_draft, ws))
+    return SV_ERR_ARG;
+  if (max_rows > 0x3FFFFFFF) return SV_ERR_ARG;
+  if (ws_bytes < ws_layout(R, b, K, V).total) return SV_ERR_WORKSPACE;
+  RowArgs ra{tgt_logits, tgt_ld, V, tgt_off, 0, R, max_rows, temperature, top_p, row_max, row_argmax, row_lse,
+             row_cut, row_kept_lse, status_word(ws)};
+  MixArgs ma{comp_logits, comp_ld, V, K, b, mix_logits, pos_off, R, max_pos, draft_tok, branch_tok, post_w,
+             q_at_draft, status_word(ws)};
+  const unsigned grid = static_cast<unsigned>(max_rows) + static_cast<unsigned>(max_pos) * static_cast<unsigned>(K);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (grid > 0) {
+    if (dtype == SV_BF16)
+      hipLaunchKernelGGL(k_rows_mix<SV_BF16>, dim3(grid), dim3(kFusedNT), 0, s, ra, ma, max_rows);
+    else
+      hipLaunchKernelGGL(k_rows_mix<SV_F32>, dim3(grid), dim3(kFusedNT), 0, s, ra, ma, max_rows);
+    if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
+  }
+  if (max_pos == 0) return SV_OK;
+  hipLaunchKernelGGL(k_mix_post, dim3(R), dim3(kWave), 0, s, ma);
   return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
 }

@@ -1,0 +1,400 @@
+// sv_rows_dev.hpp -- block-level device code for per-row statistics: maximum,
+// argmax, log-sum-exp at temperature T and the top-p (nucleus) cut.
+//
+// Sampling filter: temperature softmax with top-p ("Pith review of DBLAST",
+// "What would settle it": target sampling at T = 1.5, top-p 0.95; nucleus
+// sampling is its reference [18]).
+//
+// bf16 rows, one pass over HBM.  A bf16 logit takes one of 65536 values and
+// every token with the same value has the same probability, so the exact count
+// of tokens per value determines the maximum, sum_v exp(l_v/T) and the top-p
+// cut (the first value, from the top, at which the cumulative mass reaches
+// top_p).  The counts go into an LDS histogram with one bin per bf16 value of
+// magnitude in [2^-24, 2^24) (48 binades x 128 mantissas per sign = 12288
+// bins), two 16-bit counters per 32-bit word (24 KiB).  Integer counts are
+// exact and order-independent, so the result is deterministic.  A 16-bit
+// counter can wrap only if one value holds >= 65536 tokens; then the counts no
+// longer sum to V, which is checked.  The masses count * exp(v/T - m/T) are
+// formed once per non-empty bin in double: one wave takes 64 consecutive bins
+// (one per lane), so the exp work is spread evenly; the row totals are scanned
+// to find the 64-bin row holding the top_p crossing, and one wave rescans that
+// row.  Rows holding a value outside the histogram range (zero, |l| < 2^-24,
+// |l| >= 2^24, NaN, Inf), or a wrapped counter, take the generic path instead.
+//
+// Generic path (fp32 rows, or those bf16 rows): max and argmax, then sum
+// exp(l/T - m/T) in double, then the cut by bisection over the monotone 32-bit
+// key of the values (at most 32 passes over the row, which stays in cache).
+#pragma once
+
+#include <math.h>
+
+#include "sv_device.hpp"
+
+namespace sv {
+
+constexpr uint32_t kExpLo = 103u << 7;     // |v| >= 2^-24: biased exponent 103
+constexpr int kSide = 6144;                // 48 exponents x 128 mantissas
+constexpr int kNBins = 2 * kSide + 2;      // [0] negative special, [1..6144] negative values,
+                                           // [6145..12288] positive values, [12289] positive special
+constexpr int kHistWords = kNBins / 2;     // two 16-bit counters per word
+constexpr int kMassRows = 2 * kSide / 64;  // 64-bin rows of the in-range bins
+
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+typedef int16_t i16x2 __attribute__((ext_vector_type(2)));
+
+// Histogram bins of the two bf16 values packed in w (low half = lower index).
+// Bins ascend with the value; out-of-range magnitudes land in the two special
+// bins 0 (negative) and 12289 (positive).
+__host__ __device__ inline uint32_t bins_of_pair(uint32_t w) {
+  const u16x2 h = __builtin_bit_cast(u16x2, w);
+  const u16x2 mag = h & (u16x2)(0x7FFF);
+  const u16x2 t = mag - (u16x2)(kExpLo);  // wraps to large values below the range
+  const u16x2 tc = __builtin_elementwise_min(t, (u16x2)(kSide));
+  const u16x2 neg = __builtin_bit_cast(u16x2, __builtin_bit_cast(i16x2, h) >> 15);  // 0xFFFF if negative
+  const u16x2 bin = (tc ^ neg) + (u16x2)(kSide + 1);  // negative: 6144 - tc, positive: 6145 + tc
+  return __builtin_bit_cast(uint32_t, bin);
+}
+
+__host__ __device__ inline uint32_t bin_of(uint32_t h16) { return bins_of_pair(h16) & 0xFFFFu; }
+
+// Exact value of an in-range bin (1..12288).
+__host__ __device__ inline float bin_value(int bin) {
+  uint32_t h;
+  if (bin <= kSide)
+    h = 0x8000u | static_cast<uint32_t>(kSide - bin + static_cast<int>(kExpLo));
+  else
+    h = static_cast<uint32_t>(bin - (kSide + 1) + static_cast<int>(kExpLo));
+  uint32_t bits = h << 16;
+  float f;
+  __builtin_memcpy(&f, &bits, 4);
+  return f;
+}
+
+// Order-preserving 32-bit key of a float (-0 folded onto +0 so equal values share a key).
+__host__ __device__ inline uint32_t mono_key(float f) {
+  f = f + 0.0f;
+  uint32_t b;
+  __builtin_memcpy(&b, &f, 4);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__host__ __device__ inline float key_value(uint32_t k) {
+  const uint32_t b = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  float f;
+  __builtin_memcpy(&f, &b, 4);
+  return f;
+}
+
+struct RowArgs {
+  const void* logits;
+  int64_t ld;
+  int V;
+  const int32_t* row_off;
+  int row_stride;
+  int R;
+  int max_rows;
+  const float* T;
+  const float* top_p;  // NULL: filter off
+  float* row_max;
+  int32_t* row_argmax;
+  double* row_lse;
+  float* row_cut;        // NULL when only statistics are wanted
+  double* row_kept_lse;  // NULL when only statistics are wanted
+  uint32_t* status;
+};
+
+template <int NT>
+struct RowShared {
+  uint64_t red_u64[NT / kWave];
+  double red_f64[NT / kWave];
+  int red_i32[NT / kWave];
+  double rowtot[kMassRows];
+  int req;
+  int cut_d;
+  double F;
+};
+
+__device__ inline void write_row(const RowArgs& a, int p, float mx, int am, double lse, float cut, double kept) {
+  a.row_max[p] = mx;
+  a.row_argmax[p] = am;
+  a.row_lse[p] = lse;
+  if (a.row_cut) a.row_cut[p] = cut;
+  if (a.row_kept_lse) a.row_kept_lse[p] = kept;
+}
+
+__device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin) {
+  atomicAdd(&hist[bin >> 1], 1u << ((bin & 1u) << 4));
+}
+
+__device__ __forceinline__ uint32_t hist_get(const uint32_t* hist, int bin) {
+  return (hist[bin >> 1] >> ((bin & 1) << 4)) & 0xFFFFu;
+}
+
+// ------------------------------------------------------------------ generic path
+template <int DT, int NT>
+__device__ void row_generic(const RowArgs& a, const void* rowp, int p, float T, float tp, bool topp_on,
+                            RowShared<NT>& sh) {
+  const int tid = threadIdx.x;
+  const int V = a.V;
+  float best = -INFINITY;
+  int bidx = -1;
+  bool nonfinite = false;
+  for (int v = tid; v < V; v += NT) {
+    const float f = load_val<DT>(rowp, v);
+    nonfinite |= !isfinite(f);
+    if (f > best) {
+      best = f;
+      bidx = v;
+    }
+  }
+  if (nonfinite) raise_status(a.status, SV_ST_NONFINITE);
+  uint64_t packed = bidx >= 0 ? (static_cast<uint64_t>(mono_key(best)) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(bidx)) : 0;
+  packed = block_max_u64<NT>(packed, sh.red_u64);
+  const float m = packed ? key_value(static_cast<uint32_t>(packed >> 32)) : -INFINITY;
+  const int am = packed ? static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(packed)) : 0;
+  if (T == 0.0f) {
+    if (tid == 0) write_row(a, p, m, am, 0.0, m, 0.0);
+    return;
+  }
+  const double Td = static_cast<double>(T);
+  const double M = static_cast<double>(m) / Td;
+  double part = 0.0;
+  for (int v = tid; v < V; v += NT) part += exp(static_cast<double>(load_val<DT>(rowp, v)) / Td - M);
+  const double Z = block_sum_f64<NT>(part, sh.red_f64);
+  const double lse = M + log(Z);
+  if (!topp_on) {
+    if (tid == 0) write_row(a, p, m, am, lse, -INFINITY, lse);
+    return;
+  }
+  const double target = static_cast<double>(tp) * Z;
+  // largest key k with F(k) = sum_{key(l) >= k} exp(l/T - M) >= target
+  uint64_t lo = 0, hi = static_cast<uint64_t>(mono_key(m)) + 1;
+  double F_lo = Z;
+  while (hi - lo > 1) {
+    const uint64_t mid = (lo + hi) >> 1;
+    double s = 0.0;
+    for (int v = tid; v < V; v += NT) {
+      const float f = load_val<DT>(rowp, v);
+      if (mono_key(f) >= mid) s += exp(static_cast<double>(f) / Td - M);
+    }
+    const double F = block_sum_f64<NT>(s, sh.red_f64);
+    if (F >= target) {
+      lo = mid;
+      F_lo = F;
+    } else {
+      hi = mid;
+    }
+  }
+  if (tid == 0) write_row(a, p, m, am, lse, key_value(static_cast<uint32_t>(lo)), M + log(F_lo));
+}
+
+// ------------------------------------------------------------------ bf16 one-pass path
+__device__ __forceinline__ void count_vec(uint32_t* hist, const uint4& d, uint4& bb, uint32_t& vmax) {
+  bb.x = bins_of_pair(d.x);
+  bb.y = bins_of_pair(d.y);
+  bb.z = bins_of_pair(d.z);
+  bb.w = bins_of_pair(d.w);
+  hist_add(hist, bb.x & 0xFFFFu);
+  hist_add(hist, bb.x >> 16);
+  hist_add(hist, bb.y & 0xFFFFu);
+  hist_add(hist, bb.y >> 16);
+  hist_add(hist, bb.z & 0xFFFFu);
+  hist_add(hist, bb.z >> 16);
+  hist_add(hist, bb.w & 0xFFFFu);
+  hist_add(hist, bb.w >> 16);
+  const u16x2 m2 = __builtin_elementwise_max(
+      __builtin_elementwise_max(__builtin_bit_cast(u16x2, bb.x), __builtin_bit_cast(u16x2, bb.y)),
+      __builtin_elementwise_max(__builtin_bit_cast(u16x2, bb.z), __builtin_bit_cast(u16x2, bb.w)));
+  vmax = m2.x > m2.y ? m2.x : m2.y;
+}
+
+// Mass of in-range bin number d in descending order (d = 0 is bin 12288).
+__device__ __forceinline__ double bin_mass(const uint32_t* hist, int d, double Td, double M) {
+  const int bin = 2 * kSide - d;
+  const uint32_t c = hist_get(hist, bin);
+  return c ? static_cast<double>(c) * exp(static_cast<double>(bin_value(bin)) / Td - M) : 0.0;
+}
+
+// Statistics of row p (work item p of the request found from row_off), by one
+// block of NT threads.  `hist` holds kHistWords words of LDS (bf16 rows only).
+template <int DT, int NT, int BATCH>
+__device__ void row_block(const RowArgs& a, int p, uint32_t* hist, RowShared<NT>& sh) {
+  const int tid = threadIdx.x;
+  const int r = find_request<NT>(a.row_off, a.R, p, &sh.req);
+  if (r < 0) {
+    if (tid == 0) raise_status(a.status, SV_ST_BAD_OFFSETS);
+    return;
+  }
+  const int j = p - a.row_off[r];
+  if (a.row_stride > 0 && j >= a.row_stride) {
+    if (tid == 0) raise_status(a.status, SV_ST_BAD_OFFSETS);
+    return;
+  }
+  const int64_t row = a.row_stride > 0 ? static_cast<int64_t>(r) * a.row_stride + j : static_cast<int64_t>(p);
+  const size_t esz = DT == SV_BF16 ? 2 : 4;
+  const void* rowp = static_cast<const char*>(a.logits) + static_cast<size_t>(row) * static_cast<size_t>(a.ld) * esz;
+  const float T = a.T[r];
+  float tp = a.top_p ? a.top_p[r] : 1.0f;
+  if (tid == 0 && !(T >= 0.0f)) raise_status(a.status, SV_ST_BAD_TEMPERATURE);
+  const bool want_cut = a.row_cut != nullptr;
+  const bool topp_on = want_cut && a.top_p != nullptr && !(tp >= 1.0f);
+  if (topp_on && !(tp > 0.0f)) {
+    if (tid == 0) raise_status(a.status, SV_ST_BAD_TOP_P);
+    tp = 1e-30f;  // keeps the top value only
+  }
+
+  if constexpr (DT == SV_BF16) {
+    for (int k = tid; k < kHistWords; k += NT) hist[k] = 0u;
+    __syncthreads();
+    const uint16_t* rp = static_cast<const uint16_t*>(rowp);
+    const uint4* vp = reinterpret_cast<const uint4*>(rp);
+    const int nvec = a.V >> 3;
+    uint32_t best = 0;
+    int bvec = -1;
+    uint4 bbins = {0, 0, 0, 0};
+    int v = tid;
+    uint4 cur[BATCH];
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k)
+      if (v + k * NT < nvec) cur[k] = load16_stream(vp + v + k * NT);
+    while (v < nvec) {
+      const int vn = v + BATCH * NT;
+      uint4 nxt[BATCH];
+#pragma unroll
+      for (int k = 0; k < BATCH; ++k)
+        if (vn + k * NT < nvec) nxt[k] = load16_stream(vp + vn + k * NT);
+#pragma unroll
+      for (int k = 0; k < BATCH; ++k) {
+        if (v + k * NT < nvec) {
+          uint4 bb;
+          uint32_t vm;
+          count_vec(hist, cur[k], bb, vm);
+          if (vm > best) {
+            best = vm;
+            bvec = v + k * NT;
+            bbins = bb;
+          }
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < BATCH; ++k) cur[k] = nxt[k];
+      v = vn;
+    }
+    int bidx = -1;
+    if (bvec >= 0) {
+      const uint32_t h[8] = {bbins.x & 0xFFFFu, bbins.x >> 16, bbins.y & 0xFFFFu, bbins.y >> 16,
+                             bbins.z & 0xFFFFu, bbins.z >> 16, bbins.w & 0xFFFFu, bbins.w >> 16};
+      int k = 7;
+#pragma unroll
+      for (int q = 7; q >= 0; --q)
+        if (h[q] == best) k = q;
+      bidx = bvec * 8 + k;
+    }
+    for (int e = (nvec << 3) + tid; e < a.V; e += NT) {  // elements past the last full vector
+      const uint32_t bn = bin_of(rp[e]);
+      hist_add(hist, bn);
+      if (bn > best || bidx < 0) {
+        best = bn;
+        bidx = e;
+      }
+    }
+    uint64_t packed = bidx >= 0 ? (static_cast<uint64_t>(best) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(bidx)) : 0;
+    packed = block_max_u64<NT>(packed, sh.red_u64);  // its barriers also complete the histogram
+    int csum = 0;
+    for (int k = tid; k < kHistWords; k += NT) csum += static_cast<int>((hist[k] & 0xFFFFu) + (hist[k] >> 16));
+    int ctot;
+    (void)block_excl_scan_i32<NT>(csum, sh.red_i32, &ctot);
+    const uint32_t special = hist_get(hist, 0) + hist_get(hist, kNBins - 1);
+    if (special == 0u && ctot == a.V) {
+      const int mbin = static_cast<int>(packed >> 32);
+      const int am = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(packed));
+      const float m = bin_value(mbin);
+      if (T == 0.0f) {
+        if (tid == 0) write_row(a, p, m, am, 0.0, m, 0.0);
+        return;
+      }
+      const double Td = static_cast<double>(T);
+      const double M = static_cast<double>(m) / Td;
+      // masses: wave w takes 64-bin rows w, w + NW, ...; one bin per lane
+      constexpr int NW = NT / kWave;
+      const int lane = tid & (kWave - 1), wv = tid / kWave;
+      for (int rr = wv; rr < kMassRows; rr += NW) {
+        const double tot = wave_sum_f64(bin_mass(hist, rr * kWave + lane, Td, M));
+        if (lane == 0) sh.rowtot[rr] = tot;
+      }
+      __syncthreads();
+      if (wv != 0) return;
+      // wave 0: scan the row totals (3 per lane, in descending order), then the crossing row
+      constexpr int RPL = kMassRows / kWave;
+      static_assert(RPL * kWave == kMassRows, "row totals must split evenly over a wave");
+      double rt[RPL];
+      double loc = 0.0;
+#pragma unroll
+      for (int k = 0; k < RPL; ++k) {
+        rt[k] = sh.rowtot[lane * RPL + k];
+        loc += rt[k];
+      }
+      const double inc = wave_incl_scan_f64(loc);
+      const double Z = __shfl(inc, kWave - 1, kWave);
+      const double lse = M + log(Z);
+      if (!topp_on) {
+        if (lane == 0) write_row(a, p, m, am, lse, -INFINITY, lse);
+        return;
+      }
+      const double target = static_cast<double>(tp) * Z;
+      const uint64_t over = __ballot(inc >= target);
+      if (!over) {  // rounding kept the cumulative mass below target: keep every token
+        int low = -1;
+        for (int d = lane; d < 2 * kSide; d += kWave)
+          if (hist_get(hist, 2 * kSide - d)) low = d;
+        for (int o = 32; o > 0; o >>= 1) {
+          const int q = __shfl_xor(low, o, kWave);
+          low = q > low ? q : low;
+        }
+        if (lane == 0) write_row(a, p, m, am, lse, bin_value(2 * kSide - low), lse);
+        return;
+      }
+      const int cl = __ffsll(static_cast<long long>(over)) - 1;
+      // within lane cl's rows, the first whose running total reaches target
+      // (its last row if rounding keeps them all below)
+      int crow = 0;
+      double cbase = 0.0;
+      if (lane == cl) {
+        double run = inc - loc;
+        for (int k = 0; k < RPL; ++k) {
+          if (run + rt[k] >= target || k == RPL - 1) {
+            crow = cl * RPL + k;
+            cbase = run;
+            break;
+          }
+          run += rt[k];
+        }
+      }
+      crow = __shfl(crow, cl, kWave);
+      cbase = __shfl(cbase, cl, kWave);
+      const double mass = bin_mass(hist, crow * kWave + lane, Td, M);
+      const double inc2 = cbase + wave_incl_scan_f64(mass);
+      const uint64_t hit = __ballot(inc2 >= target);
+      int cut_d;
+      double F;
+      if (hit) {
+        const int hl = __ffsll(static_cast<long long>(hit)) - 1;
+        cut_d = crow * kWave + hl;
+        F = __shfl(inc2, hl, kWave);
+      } else {  // rounding: the last non-empty bin of the row
+        const uint64_t ne = __ballot(mass > 0.0 || hist_get(hist, 2 * kSide - (crow * kWave + lane)) != 0u);
+        const int hl = ne ? 63 - __clzll(static_cast<long long>(ne)) : kWave - 1;
+        cut_d = crow * kWave + hl;
+        F = __shfl(inc2, kWave - 1, kWave);
+      }
+      if (lane == 0) write_row(a, p, m, am, lse, bin_value(2 * kSide - cut_d), M + log(F));
+      return;
+    }
+    // a value outside the histogram range, or a wrapped counter: exact generic path
+    row_generic<SV_BF16, NT>(a, rowp, p, T, tp, topp_on, sh);
+  } else {
+    row_generic<SV_F32, NT>(a, rowp, p, T, tp, topp_on, sh);
+  }
+}
+
+}  // namespace sv

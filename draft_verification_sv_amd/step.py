@@ -19,7 +19,7 @@ import numpy as np
 import torch
 
 from . import (SV_BF16, SV_F32, SV_Q_DENSE, SV_Q_MIXTURE, dvl_alloc_pack, make_workspace, sv_accept, sv_mixture_q,
-               sv_residual_sample, sv_softmax_stats, sv_topp_threshold)
+               sv_residual_sample, sv_softmax_stats, sv_topp_threshold, sv_verify_rows)
 
 
 def row_pitch(V: int, dtype: str) -> int:
@@ -142,10 +142,22 @@ class VerifyStep:
                            None if dense else self.post_w, self.seed, self.n_acc, self.token, self.is_bonus,
                            self.ws, self.ws_bytes, stream)
 
-    def run_verify(self, tgt, tgt_ld, *, draft=None, draft_ld=0, comp=None, comp_ld=0, side_stream=None):
+    def run_rows_fused(self, tgt, tgt_ld, comp, comp_ld, stream=None):
+        """Target rows and component rows in one launch (mixture proposal)."""
+        sv_verify_rows(tgt, self.dt, tgt_ld, self.V, self.tgt_off, self.R, self.max_rows, self.T,
+                       self.top_p if self.use_topp else None, self.row_max, self.row_argmax, self.row_lse,
+                       self.row_cut, self.row_kept, comp, comp_ld, self.K, self.b, self.mix, self.pos_off,
+                       self.max_pos, self.x, self.branch_tok, self.post_w, self.q_at_draft, self.ws, self.ws_bytes,
+                       stream)
+
+    def run_verify(self, tgt, tgt_ld, *, draft=None, draft_ld=0, comp=None, comp_ld=0, side_stream=None,
+                   fused=False):
         """The verification calls on torch's current stream.  With `side_stream`,
-        the target-row statistics run there, concurrently with the proposal."""
-        if side_stream is None:
+        the target-row statistics run there, concurrently with the proposal;
+        with `fused` (mixture only) they share one launch with it."""
+        if fused:
+            self.run_rows_fused(tgt, tgt_ld, comp, comp_ld)
+        elif side_stream is None:
             self.run_rows(tgt, tgt_ld)
             self.run_proposal(draft=draft, draft_ld=draft_ld, comp=comp, comp_ld=comp_ld)
         else:

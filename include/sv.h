@@ -30,8 +30,9 @@
  *    Grids are sized from host-side capacities; work items beyond the
  *    device-side counts exit at once.
  *  - `stream` is a hipStream_t.  Calls are asynchronous; outputs are valid in
- *    stream order.  Two calls that share one workspace must not run
- *    concurrently.
+ *    stream order.  The workspace holds a status word (updated with atomics,
+ *    so calls on different streams may share it) and the residual chunk sums
+ *    (two sv_residual_sample calls that share a workspace must not overlap).
  *  - Requests r = 0..R-1, draft block of b positions, vocabulary V.
  *    L_r = pos_off[r+1] - pos_off[r] is the number of verified positions of
  *    request r (0 <= L_r <= b).  The target gives L_r + 1 rows per request:
@@ -88,8 +89,7 @@ extern "C" {
  * K mixture components (0 if unused) and vocabulary V.  Host-only. */
 int32_t sv_workspace_bytes(int32_t R, int32_t b, int32_t K, int32_t V, size_t* out_bytes);
 
-/* Zero the workspace (once, before first use).  Each call leaves its
- * counters at zero again, so no per-step clearing is needed. */
+/* Zero the workspace (once, before first use; a fill kernel). */
 int32_t sv_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
 /* Copy the status word to *host_out, then synchronise the stream. */
@@ -174,12 +174,27 @@ int32_t sv_topp_threshold(const void* logits, int32_t dtype, int64_t ld, int32_t
  *   q_at_draft[R*b]  out: q(x_i | x_<i) = sum of w_z over z with g_i(z) = x_i
  *                    (double); 0 and SV_ST_EMPTY_POSTERIOR when no branch is
  *                    consistent with x_<i; i < L_r
- * Requires K <= 64, b <= 64.  Uses the workspace's counters and partials. */
+ * Two launches: one block per component row (argmax), then one wave per
+ * request (posterior).  Requires K <= 64, b <= 64.  Uses the status word only. */
 int32_t sv_mixture_q(const void* comp_logits, int32_t dtype, int64_t ld, int32_t V, int32_t K,
                      int32_t b, const float* mix_logits, const int32_t* pos_off, int32_t R,
                      int32_t max_pos, const int32_t* draft_tok, int32_t* branch_tok,
                      double* post_w, double* q_at_draft, void* ws, size_t ws_bytes,
                      void* stream);
+
+/* sv_verify_rows: sv_topp_threshold over the packed target rows (row_off =
+ * tgt_off, row_stride 0) and sv_mixture_q over the component rows, in one
+ * launch whose blocks take target rows first and component rows after, so the
+ * two read streams share every compute unit; then the posterior recursion.
+ * Arguments and outputs as in those two calls (shared dtype).  Same method and
+ * pages as sv_topp_threshold and sv_mixture_q; uses the status word only. */
+int32_t sv_verify_rows(const void* tgt_logits, int32_t dtype, int64_t tgt_ld, int32_t V,
+                       const int32_t* tgt_off, int32_t R, int32_t max_rows, const float* temperature,
+                       const float* top_p, float* row_max, int32_t* row_argmax, double* row_lse,
+                       float* row_cut, double* row_kept_lse, const void* comp_logits, int64_t comp_ld,
+                       int32_t K, int32_t b, const float* mix_logits, const int32_t* pos_off,
+                       int32_t max_pos, const int32_t* draft_tok, int32_t* branch_tok, double* post_w,
+                       double* q_at_draft, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------- acceptance */
 
@@ -222,7 +237,7 @@ int32_t sv_accept(const void* tgt_logits, int32_t dtype, int64_t tgt_ld, int32_t
  *   Arguments as sv_accept; in SV_Q_MIXTURE mode K, branch_tok and post_w
  *   come from sv_mixture_q.
  *   token[R], is_bonus[R]  out.
- * Uses the workspace's counters and partials. */
+ * Two launches (chunk sums, then the draw); uses the workspace's chunk sums. */
 int32_t sv_residual_sample(const void* tgt_logits, int32_t dtype, int64_t tgt_ld, int32_t V,
                            const int32_t* tgt_off, const int32_t* pos_off, int32_t R, int32_t b,
                            const float* temperature, const int32_t* row_argmax,

@@ -19,7 +19,7 @@ REL = 1e-5
 MARGIN = 1e-6
 
 
-def gpu_step_runner(w: synth.Workload, device="cuda", two_streams: bool = False):
+def gpu_step_runner(w: synth.Workload, device="cuda", two_streams: bool = False, fused: bool = False):
     """Upload a workload once and return (VerifyStep, run(s) -> results)."""
     import torch
 
@@ -45,7 +45,7 @@ def gpu_step_runner(w: synth.Workload, device="cuda", two_streams: bool = False)
             vs.set_full_verification()
             L = np.full(R, b, np.int32)
         pack_rows_device(full, L, b + 1, packed)
-        vs.run_verify(packed, ld, draft=draft, draft_ld=ld, comp=comp, comp_ld=ld, side_stream=side)
+        vs.run_verify(packed, ld, draft=draft, draft_ld=ld, comp=comp, comp_ld=ld, side_stream=side, fused=fused)
         return vs.results()
 
     return vs, run

@@ -290,6 +290,23 @@ def test_two_stream_step_matches_oracle(c):
     assert_rate(rep)
 
 
+FUSED = [(4, dict(V=4099, R=4)), (5, dict(V=4099, R=8, steps=4)), (5, dict(V=1031, R=48, steps=2)),
+         (4, dict()), (5, dict(steps=6))]
+
+
+@pytest.mark.parametrize("c,kw", FUSED, ids=[f"cfg{c}-" + "-".join(f"{k}{v}" for k, v in kw.items()) for c, kw in FUSED])
+def test_fused_rows_mixture_matches_oracle(c, kw):
+    """sv_verify_rows: target rows and component rows in one launch."""
+    w = synth.config(c, **kw)
+    vs, run = gpu_step_runner(w, fused=True)
+    rep = None
+    for s in range(w.steps):
+        banner(f"fused {w.name} V={w.V} R={w.R} step {s}")
+        rep = compare_step(w, run(s), oracle_step(w, s), rep)
+    assert_rate(rep)
+    assert _sv().sv_get_status(vs.ws) == 0
+
+
 def test_determinism_repeat_runs():
     w = synth.config(4, V=8191, R=4)
     vs, run = gpu_step_runner(w)
