@@ -9,14 +9,14 @@ and bonus sampling, Philox seeds advancing per step.  Synthetic seeded data
 
 A timed step is the whole verification path on inputs resident in HBM:
 dvl_alloc_pack, sv_verify_rows (target-row statistics with top-p and the
-mixture proposal in one launch), sv_accept, sv_residual_sample.  The target forward is outside the path; its output for
+branch argmax over the component rows, one launch), sv_accept_sample
+(category posterior, acceptance, residual / bonus draw).  The target forward is outside the path; its output for
 each step (the packed rows for that step's allocation) is prepared before the
 timed region in a buffer of its own, as the target model would have written it.
 
-Prints one JSON line.  `roofline` is for the dominant launch (sv_verify_rows:
-target-row statistics and the branch argmax over the component rows in one
-kernel, plus the posterior), timed live with HIP events on the stream the
-kernels run on; `cpu_baseline` is the CPU oracle on a bounded sample of the
+Prints one JSON line.  `roofline` is for the dominant kernel (k_rows_mix of
+sv_verify_rows: target-row statistics and the branch argmax over the component
+rows), timed live with HIP events on the stream the kernels run on; `cpu_baseline` is the CPU oracle on a bounded sample of the
 same workload.
 """
 from __future__ import annotations
@@ -128,19 +128,15 @@ def main():
         sv.dvl_alloc_pack(a_all[s], R, b, budget, s_sc, L, pos_off, tgt_off, ws, nb, sp)
         if ev is not None:
             ev[0].record(stream)
-        # target rows (statistics, top-p) and component rows (branch argmax) in one launch,
-        # then the category posterior
+        # target rows (statistics, top-p) and component rows (branch argmax) in one launch
         sv.sv_verify_rows(packed[s], dt, ld, V, tgt_off, R, max_rows, T, top_p, row_max, row_arg, row_lse, row_cut,
-                          row_kept, comp, ld, K, b, mix, pos_off, max_pos, x_all[s], branch_tok, post_w, q_at, ws, nb,
-                          sp)
+                          row_kept, comp, ld, K, b, pos_off, max_pos, branch_tok, ws, nb, sp)
         if ev is not None:
             ev[1].record(stream)
-        sv.sv_accept(packed[s], dt, ld, V, tgt_off, pos_off, R, b, T, row_arg, row_cut, row_kept, x_all[s],
-                     sv.SV_Q_MIXTURE, None, dt, 0, None, None, q_at, seeds[s:s + 1], n_acc, None, None, None, ws, nb,
-                     sp)
-        sv.sv_residual_sample(packed[s], dt, ld, V, tgt_off, pos_off, R, b, T, row_arg, row_cut, row_kept,
-                              sv.SV_Q_MIXTURE, None, dt, 0, None, None, K, branch_tok, post_w, seeds[s:s + 1], n_acc,
-                              token, is_bonus, ws, nb, sp)
+        # category posterior, acceptance, residual / bonus draw
+        sv.sv_accept_sample(packed[s], dt, ld, V, tgt_off, pos_off, R, b, T, row_arg, row_cut, row_kept, x_all[s],
+                            sv.SV_Q_MIXTURE, None, dt, 0, None, None, K, mix, branch_tok, post_w, q_at,
+                            seeds[s:s + 1], n_acc, token, is_bonus, None, None, None, ws, nb, sp)
 
     for k in range(args.warmup):
         step(k % S)
@@ -194,7 +190,7 @@ def main():
                    "requests": R, "block": b, "vocab": V, "K": K, "budget": B},
         "step_gbps": round(float(np.mean(step_bytes)) / (ms_per_step * 1e-3) / 1e9, 1),
         "step_frac_of_peak": round(float(np.mean(step_bytes)) / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-        "roofline": {"kernel": "k_rows_mix + k_mix_post (sv_verify_rows)", "bound": "hbm", "achieved": round(achieved, 1),
+        "roofline": {"kernel": "k_rows_mix (sv_verify_rows)", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": traffic, "avg_launch_us": round(mix_ms * 1e3, 2),
                      "algorithmic_bytes_per_launch": mix_bytes},

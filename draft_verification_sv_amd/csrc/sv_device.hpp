@@ -230,7 +230,7 @@ struct WsLayout {
 
 __host__ __device__ inline int res_chunks(int V) {
   const int ngroups = (V + 7) / 8;  // 8-value groups
-  const int target = 64 * 4;        // groups per chunk: 4 per lane of one wave
+  const int target = 256 * 4;       // groups per chunk: 4 per thread of a 256-thread block
   int s = (ngroups + target - 1) / target;
   if (s < 1) s = 1;
   if (s > 64) s = 64;

@@ -17,8 +17,9 @@
 //      (non-negative floats order like their bit patterns), with LDS count
 //      histograms; the digit holding the rank is found by a block scan over
 //      the 256 digit counts;
-//   3. per request, positions above the threshold plus the first ties in
-//      (r, i) order, via an exclusive scan of the tie counts over requests;
+//   3. per position, taken if above the threshold or a tie of rank below
+//      the remainder in (r, i) order (an exclusive scan of tie counts gives the
+//      ranks); L_r counted with integer LDS atomics;
 //   4. exclusive scans of L and L + 1 into pos_off and tgt_off.
 #include "sv_device.hpp"
 #include "sv_host.hpp"
@@ -29,11 +30,14 @@ constexpr int kDvlNT = 256;
 constexpr int kDvlLds = 8192;  // scores kept in LDS up to this many positions
 
 template <bool kInLds>
-__global__ __launch_bounds__(kDvlNT) void k_dvl(const float* a, int R, int b, const int32_t* budget, float* s,
-                                               int32_t* L, int32_t* pos_off, int32_t* tgt_off, uint32_t* status) {
+__global__ __launch_bounds__(kDvlNT) void k_dvl(const float* __restrict__ a, int R, int b,
+                                               const int32_t* __restrict__ budget, float* __restrict__ s,
+                                               int32_t* __restrict__ L, int32_t* __restrict__ pos_off,
+                                               int32_t* __restrict__ tgt_off, uint32_t* status) {
   __shared__ uint32_t hist[256];
   __shared__ uint32_t skey[kInLds ? kDvlLds : 1];
   __shared__ int scr[kDvlNT / kWave];
+  __shared__ int lcount[kInLds ? kDvlLds : 1];
   __shared__ uint32_t sh_prefix;
   __shared__ int sh_remaining;
   const int tid = threadIdx.x;
@@ -43,16 +47,36 @@ __global__ __launch_bounds__(kDvlNT) void k_dvl(const float* a, int R, int b, co
     if (tid == 0) raise_status(status, SV_ST_BAD_BUDGET);
     B = 0;
   }
-  // 1. survival scores; non-negative floats order like their bit patterns
+  // 1. survival scores; non-negative floats order like their bit patterns.
+  // The estimates are read in one coalesced pass (into LDS when they fit)
+  // before any score is written, so no load waits behind a store.
   bool bad = false;
-  for (int r = tid; r < R; r += kDvlNT) {
-    float run = 1.0f;
-    for (int i = 0; i < b; ++i) {
-      const float av = a[r * b + i];
+  if constexpr (kInLds) {
+    for (int e = tid; e < n; e += kDvlNT) {
+      const float av = a[e];
       bad |= !(av >= 0.0f && av <= 1.0f);
-      run = run * av;
-      s[r * b + i] = run;
-      if constexpr (kInLds) skey[r * b + i] = __float_as_uint(run);
+      skey[e] = __float_as_uint(av);
+    }
+    __syncthreads();
+    for (int r = tid; r < R; r += kDvlNT) {
+      float run = 1.0f;
+      for (int i = 0; i < b; ++i) {
+        run = run * __uint_as_float(skey[r * b + i]);
+        skey[r * b + i] = __float_as_uint(run);
+      }
+    }
+    __syncthreads();
+    for (int e = tid; e < n; e += kDvlNT) s[e] = __uint_as_float(skey[e]);
+  } else {
+    for (int r = tid; r < R; r += kDvlNT) L[r] = 0;
+    for (int r = tid; r < R; r += kDvlNT) {
+      float run = 1.0f;
+      for (int i = 0; i < b; ++i) {
+        const float av = a[r * b + i];
+        bad |= !(av >= 0.0f && av <= 1.0f);
+        run = run * av;
+        s[r * b + i] = run;
+      }
     }
   }
   if (bad) raise_status(status, SV_ST_BAD_SCORE);
@@ -94,44 +118,54 @@ __global__ __launch_bounds__(kDvlNT) void k_dvl(const float* a, int R, int b, co
     thr = prefix;
   }
 
-  // 3. per-request counts; ties are taken in (r, i) order
-  const int per = (R + kDvlNT - 1) / kDvlNT;
-  const int r0 = tid * per, r1 = min(R, r0 + per);
+  // 3. element-parallel choice: above the threshold, or a tie whose rank in
+  // (r, i) order is below `remaining`; lengths counted with LDS atomics.
+  // Thread t owns the consecutive elements [t*pe, (t+1)*pe).
+  if constexpr (kInLds)
+    for (int r = tid; r < R; r += kDvlNT) lcount[r] = 0;
+  const int pe = (n + kDvlNT - 1) / kDvlNT;
+  const int e0 = tid * pe, e1 = min(n, e0 + pe);
   int eq_local = 0;
   if (!all && !none)
-    for (int r = r0; r < r1; ++r)
-      for (int i = 0; i < b; ++i) eq_local += key(r * b + i) == thr ? 1 : 0;
+    for (int e = e0; e < e1; ++e) eq_local += key(e) == thr ? 1 : 0;
   int eq_total;
-  int tie_base = block_excl_scan_i32<kDvlNT>(eq_local, scr, &eq_total);
-  int l_local = 0;
-  for (int r = r0; r < r1; ++r) {
-    int Lr;
+  int tie_rank = block_excl_scan_i32<kDvlNT>(eq_local, scr, &eq_total);  // also orders lcount's zeroing
+  for (int e = e0; e < e1; ++e) {
+    bool take;
     if (all) {
-      Lr = b;
+      take = true;
     } else if (none) {
-      Lr = 0;
+      take = false;
     } else {
-      int gt = 0, eq = 0;
-      for (int i = 0; i < b; ++i) {
-        const uint32_t kk = key(r * b + i);
-        gt += kk > thr ? 1 : 0;
-        eq += kk == thr ? 1 : 0;
-      }
-      int take = remaining - tie_base;
-      take = take < 0 ? 0 : (take > eq ? eq : take);
-      tie_base += eq;
-      Lr = gt + take;
+      const uint32_t kk = key(e);
+      take = kk > thr || (kk == thr && tie_rank < remaining);
+      tie_rank += kk == thr ? 1 : 0;
     }
-    L[r] = Lr;
-    l_local += Lr;
+    if (take) {
+      if constexpr (kInLds)
+        atomicAdd(&lcount[e / b], 1);
+      else
+        atomicAdd(&L[e / b], 1);
+    }
   }
-  // 4. offsets
+  __syncthreads();
+  // 4. lengths and offsets: thread t owns the consecutive requests [t*pr, (t+1)*pr)
+  const int pr = (R + kDvlNT - 1) / kDvlNT;
+  const int r0 = tid * pr, r1 = min(R, r0 + pr);
+  int l_local = 0;
+  auto length = [&](int r) -> int {
+    if constexpr (kInLds) return lcount[r];
+    else return __hip_atomic_load(&L[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  for (int r = r0; r < r1; ++r) l_local += length(r);
   int l_total;
   int off = block_excl_scan_i32<kDvlNT>(l_local, scr, &l_total);
   for (int r = r0; r < r1; ++r) {
+    const int Lr = length(r);
+    if constexpr (kInLds) L[r] = Lr;
     pos_off[r] = off;
     tgt_off[r] = off + r;
-    off += L[r];
+    off += Lr;
   }
   if (tid == 0) {
     pos_off[R] = l_total;

@@ -269,31 +269,28 @@ extern "C" int32_t sv_verify_rows(const void* tgt_logits, int32_t dtype, int64_t
                                   const int32_t* tgt_off, int32_t R, int32_t max_rows, const float* temperature,
                                   const float* top_p, float* row_max, int32_t* row_argmax, double* row_lse,
                                   float* row_cut, double* row_kept_lse, const void* comp_logits, int64_t comp_ld,
-                                  int32_t K, int32_t b, const float* mix_logits, const int32_t* pos_off,
-                                  int32_t max_pos, const int32_t* draft_tok, int32_t* branch_tok, double* post_w,
-                                  double* q_at_draft, void* ws, size_t ws_bytes, void* stream) {
+                                  int32_t K, int32_t b, const int32_t* pos_off, int32_t max_pos, int32_t* branch_tok,
+                                  void* ws, size_t ws_bytes, void* stream) {
   if (!tgt_logits || !tgt_off || !temperature || !row_max || !row_argmax || !row_lse || !row_cut || !row_kept_lse)
     return SV_ERR_ARG;
-  if (max_rows < 0 || tgt_ld < V || !rows_aligned(tgt_logits, dtype, tgt_ld)) return SV_ERR_ARG;
-  if (!mix_args_ok(comp_logits, dtype, comp_ld, V, K, b, mix_logits, pos_off, R, max_pos, draft_tok, branch_tok,
-                   post_w, q_at_draft, ws))
+  if (!comp_logits || !pos_off || !branch_tok || !ws) return SV_ERR_ARG;
+  if (R < 1 || V < 1 || K < 1 || K > 64 || b < 1 || b > 64 || max_rows < 0 || max_pos < 0) return SV_ERR_ARG;
+  if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_ARG;
+  if (tgt_ld < V || comp_ld < V || !rows_aligned(tgt_logits, dtype, tgt_ld) || !rows_aligned(comp_logits, dtype, comp_ld))
     return SV_ERR_ARG;
-  if (max_rows > 0x3FFFFFFF) return SV_ERR_ARG;
-  if (ws_bytes < ws_layout(R, b, K, V).total) return SV_ERR_WORKSPACE;
+  if (static_cast<long long>(max_pos) > static_cast<long long>(R) * b) return SV_ERR_ARG;
+  if (static_cast<long long>(max_rows) + static_cast<long long>(max_pos) * K > 0x7FFFFFFFLL) return SV_ERR_ARG;
+  if (ws_bytes < 256) return SV_ERR_WORKSPACE;
   RowArgs ra{tgt_logits, tgt_ld, V, tgt_off, 0, R, max_rows, temperature, top_p, row_max, row_argmax, row_lse,
              row_cut, row_kept_lse, status_word(ws)};
-  MixArgs ma{comp_logits, comp_ld, V, K, b, mix_logits, pos_off, R, max_pos, draft_tok, branch_tok, post_w,
-             q_at_draft, status_word(ws)};
+  MixArgs ma{comp_logits, comp_ld, V, K, b, nullptr, pos_off, R, max_pos, nullptr, branch_tok, nullptr, nullptr,
+             status_word(ws)};
   const unsigned grid = static_cast<unsigned>(max_rows) + static_cast<unsigned>(max_pos) * static_cast<unsigned>(K);
+  if (grid == 0) return SV_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (grid > 0) {
-    if (dtype == SV_BF16)
-      hipLaunchKernelGGL(k_rows_mix<SV_BF16>, dim3(grid), dim3(kFusedNT), 0, s, ra, ma, max_rows);
-    else
-      hipLaunchKernelGGL(k_rows_mix<SV_F32>, dim3(grid), dim3(kFusedNT), 0, s, ra, ma, max_rows);
-    if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
-  }
-  if (max_pos == 0) return SV_OK;
-  hipLaunchKernelGGL(k_mix_post, dim3(R), dim3(kWave), 0, s, ma);
+  if (dtype == SV_BF16)
+    hipLaunchKernelGGL(k_rows_mix<SV_BF16>, dim3(grid), dim3(kFusedNT), 0, s, ra, ma, max_rows);
+  else
+    hipLaunchKernelGGL(k_rows_mix<SV_F32>, dim3(grid), dim3(kFusedNT), 0, s, ra, ma, max_rows);
   return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
 }

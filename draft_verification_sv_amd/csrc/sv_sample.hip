@@ -8,22 +8,33 @@
 // is drawn from p_{L_r + 1}.  Uniforms come from Philox4x32-10 at counter
 // (position, request, 0, 0): word 0 for the test, word 1 for the draw.
 //
-// k_accept: one wave per request, one lane per position (b <= 64); p and q at
-// the draft token are gathered and compared in double; a ballot over the
-// rejecting lanes gives the first rejection.
-// The sampled row of each request is cut into S <= 64 chunks.  k_res_sums: one
-// wave per chunk forms the weights of its chunk in double and stores their sum
-// (and the sum of p).  k_res_pick (after a kernel boundary): one wave per
-// request scans the chunk sums (one per lane) to find the chunk holding u * W,
-// then walks that chunk 512 values at a time: per-lane sums of 8 consecutive
-// weights, a shuffle scan across the wave, and a ballot for the first lane
+// Acceptance: one wave per request, one lane per position (b <= 64); p and q at
+// the draft token are formed in double; a ballot over the rejecting lanes gives
+// the first rejection.
+//
+// Draw: the sampled row is cut into S <= 64 chunks of up to 1024 8-value groups.
+// Chunk sums: one 256-thread block per chunk loads its groups at once and adds
+// their weights in double.  With a top-p cut,
+// tokens below the cut have weight 0, so each wave first compacts the values
+// at or above the cut into LDS and evaluates exp only for those.  Pick (after a
+// kernel boundary): one block per request; its first wave scans the chunk sums
+// (one per lane) to find the chunk holding u * W, then the block walks that
+// chunk 8192 values at a time: per-thread sums of 32 consecutive weights, an
+// LDS-staged exclusive block scan, and a block minimum over the first index
 // whose running weight exceeds u * W.
+//
+// The fused tail (sv_accept_sample) runs the category posterior, the
+// acceptance tests and the chunk sums in one grid: every chunk block
+// recomputes its request's posterior and acceptance (at most 64 positions, a
+// few KB of gathers) so that no block waits for another.
 #include <math.h>
 
 #include "sv_device.hpp"
 #include "sv_host.hpp"
 
 namespace sv {
+
+constexpr int kSumNT = 256;  // threads of a chunk-sum block
 
 struct SampleArgs {
   const void* tgt;
@@ -44,10 +55,12 @@ struct SampleArgs {
   int64_t draft_ld;
   const int32_t* dargmax;
   const double* dlse;
-  const double* qx;  // accept, mixture mode
-  int K;             // residual, mixture mode
+  const double* qx;  // q at the draft tokens (mixture, standalone acceptance)
+  int K;
+  const float* mix;  // mixing logits (fused tail)
   const int32_t* branch_tok;
-  const double* post_w;
+  double* post_w;      // read by the draw; written by the fused tail
+  double* q_at_draft;  // written by the fused tail
   const uint64_t* seed;
   const int32_t* n_acc_in;
   int32_t* n_acc;
@@ -56,9 +69,9 @@ struct SampleArgs {
   double* p_out;
   double* q_out;
   float* u_out;
-  double* part;        // [R * S * 2] chunk sums (residual)
-  int S;               // chunks per row (residual)
-  int CG;              // 8-element groups per chunk (residual)
+  double* part;  // [R * S * 2] chunk sums
+  int S;         // chunks per row
+  int CG;        // 8-value groups per chunk
   uint32_t* status;
 };
 
@@ -66,73 +79,10 @@ __device__ __forceinline__ const char* row_ptr(const void* base, int dtype, int6
   return static_cast<const char*>(base) + static_cast<size_t>(row) * static_cast<size_t>(ld) * (dtype == SV_BF16 ? 2 : 4);
 }
 
-// target probability of token v: [l >= cut] exp(l / T - kept_lse), T > 0
-__device__ __forceinline__ double p_of(float l, float cut, double Td, double kept) {
-  return l >= cut ? exp(static_cast<double>(l) / Td - kept) : 0.0;
+// target probability of a token with logit l: [l >= cut] exp(l / T - kept_lse), T > 0
+__device__ __forceinline__ double p_of(float l, float cut, double invT, double kept) {
+  return l >= cut ? exp(static_cast<double>(l) * invT - kept) : 0.0;
 }
-
-// ------------------------------------------------------------------ acceptance
-__global__ __launch_bounds__(kWave) void k_accept(SampleArgs a) {
-  const int r = blockIdx.x;
-  const int i = threadIdx.x;
-  const int pb = a.pos_off[r];
-  const int Lr = a.pos_off[r + 1] - pb;
-  const int tb = a.tgt_off[r];
-  const bool offs_ok = Lr >= 0 && Lr <= a.b && a.tgt_off[r + 1] - tb == Lr + 1;
-  if (!offs_ok) {
-    if (i == 0) {
-      raise_status(a.status, SV_ST_BAD_OFFSETS);
-      a.n_acc[r] = 0;
-    }
-    return;
-  }
-  const uint64_t seed = *a.seed;
-  const float T = a.T[r];
-  bool reject = false;
-  if (i < Lr) {
-    const int xv = a.x[static_cast<size_t>(r) * a.b + i];
-    const bool tok_ok = xv >= 0 && xv < a.V;
-    if (!tok_ok) raise_status(a.status, SV_ST_BAD_TOKEN);
-    const int trow = tb + i;
-    double p = 0.0, q = 0.0;
-    if (tok_ok) {
-      if (T == 0.0f) {
-        p = xv == a.row_argmax[trow] ? 1.0 : 0.0;
-      } else {
-        const float l = load_val_rt(row_ptr(a.tgt, a.dtype, trow, a.tgt_ld), a.dtype, xv);
-        p = p_of(l, a.row_cut[trow], static_cast<double>(T), a.row_kept[trow]);
-      }
-      if (a.q_mode == SV_Q_MIXTURE) {
-        q = a.qx[static_cast<size_t>(r) * a.b + i];
-      } else {
-        const int pos = pb + i;
-        if (T == 0.0f) {
-          q = xv == a.dargmax[pos] ? 1.0 : 0.0;
-        } else {
-          const float d = load_val_rt(row_ptr(a.draft, a.ddtype, static_cast<int64_t>(r) * a.b + i, a.draft_ld), a.ddtype, xv);
-          q = exp(static_cast<double>(d) / static_cast<double>(T) - a.dlse[pos]);
-        }
-      }
-    }
-    const U4 w = philox_at(seed, static_cast<uint32_t>(i), static_cast<uint32_t>(r));
-    const double u = u24(w.x);
-    const bool accept = q > 0.0 ? (u < p / q) : (p > 0.0);
-    reject = !accept;
-    const size_t k = static_cast<size_t>(r) * a.b + i;
-    if (a.p_out) a.p_out[k] = p;
-    if (a.q_out) a.q_out[k] = q;
-    if (a.u_out) a.u_out[k] = static_cast<float>(u);
-  }
-  const uint64_t mask = __ballot(reject);
-  if (i == 0) a.n_acc[r] = mask ? (__ffsll(static_cast<long long>(mask)) - 1) : Lr;
-}
-
-// ------------------------------------------------------------------ residual / bonus
-// One wave per block.  A chunk is a run of 8-value groups; lane l takes groups
-// l, l + 64, l + 128, ... so every load instruction of the wave reads 1 KiB of
-// consecutive logits, and 64 consecutive groups form a "row" of 512 values that
-// the wave scans with shuffles.
-constexpr int kResChunks = 64;
 
 // 8 consecutive values starting at element 8g (elements >= V read as -inf)
 __device__ __forceinline__ void load8(const char* rowp, int dtype, int g, int V, float out[8]) {
@@ -154,78 +104,189 @@ __device__ __forceinline__ void load8(const char* rowp, int dtype, int g, int V,
   }
 }
 
-// What one request's draw needs; filled by res_setup.
-struct ResCtx {
+// Offsets of request r are an exclusive scan with L_r <= b and L_r + 1 target rows.
+__device__ __forceinline__ bool request_ok(const SampleArgs& a, int r, int& pb, int& Lr, int& tb) {
+  pb = a.pos_off[r];
+  Lr = a.pos_off[r + 1] - pb;
+  tb = a.tgt_off[r];
+  return Lr >= 0 && Lr <= a.b && a.tgt_off[r + 1] - tb == Lr + 1;
+}
+
+// ------------------------------------------------------------------ posterior (one wave)
+// Lane z < K: f_z = the first position where branch z disagrees with the draft
+// (L_r if none).  Branch z is consistent with x_<i iff f_z >= i, and then
+// matches x_i iff f_z > i, so
+//   w_z^(i) = q(z|y) [f_z >= i] / sum_z' q(z'|y) [f_z' >= i],
+//   q(x_i | x_<i) = sum_z w_z^(i) [f_z > i].
+// The request's branch tokens and draft tokens, staged in LDS by the whole block
+// (one load per thread) so that the recursion below reads no global memory.
+struct ReqTables {
+  int g[64 * 64];  // [z][i], z < K, i < L_r
+  int x[64];
+};
+
+__device__ __forceinline__ void stage_tables(const SampleArgs& a, int r, int Lr, ReqTables& t) {
+  for (int k = threadIdx.x; k < a.K * Lr; k += blockDim.x) {
+    const int z = k / Lr, i = k % Lr;
+    t.g[z * 64 + i] = a.branch_tok[(static_cast<size_t>(r) * a.K + z) * a.b + i];
+  }
+  for (int k = threadIdx.x; k < Lr; k += blockDim.x) t.x[k] = a.x[static_cast<size_t>(r) * a.b + k];
+}
+
+__device__ __forceinline__ void branch_agreement(const SampleArgs& a, int r, int Lr, const ReqTables& t, double& pi,
+                                                 int& f) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const bool act = lane < a.K;
+  const float ml = act ? a.mix[static_cast<size_t>(r) * a.K + lane] : -INFINITY;
+  f = Lr;
+  if (act)
+    for (int i = Lr - 1; i >= 0; --i)
+      if (t.g[lane * 64 + i] != t.x[i]) f = i;
+  float mmax = ml;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, o, kWave));
+  const double e = act ? exp(static_cast<double>(ml) - static_cast<double>(mmax)) : 0.0;
+  pi = e / wave_sum_f64(e);  // q(z | y)
+}
+
+// Fills qx[i] for i < L_r; with write_out also post_w, q_at_draft and the status.
+__device__ __forceinline__ void posterior_wave(const SampleArgs& a, int r, int Lr, const ReqTables& t, bool write_out,
+                                               double* qx, double& pi, int& f) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const bool act = lane < a.K;
+  branch_agreement(a, r, Lr, t, pi, f);
+  for (int i = 0; i < Lr; ++i) {
+    const double w = act && f >= i ? pi : 0.0;
+    const double sw = wave_sum_f64(w);
+    const double post = sw > 0.0 ? w / sw : 0.0;
+    const double q = wave_sum_f64(f > i ? post : 0.0);
+    if (lane == 0) {
+      qx[i] = q;
+      if (write_out) {
+        a.q_at_draft[static_cast<size_t>(r) * a.b + i] = q;
+        if (!(sw > 0.0)) raise_status(a.status, SV_ST_EMPTY_POSTERIOR);
+      }
+    }
+    if (write_out && act) a.post_w[(static_cast<size_t>(r) * a.b + i) * a.K + lane] = post;
+  }
+}
+
+// ------------------------------------------------------------------ acceptance (one wave)
+// Lane i < L_r tests position i + 1 (1-based).  q comes from qx (mixture) or
+// from the dense draft row.  Returns n_acc on every lane.
+__device__ __forceinline__ int accept_wave(const SampleArgs& a, int r, int pb, int Lr, int tb, const double* qx,
+                                           bool report) {
+  const int i = threadIdx.x & (kWave - 1);
+  const uint64_t seed = *a.seed;
+  const float T = a.T[r];
+  const double invT = 1.0 / static_cast<double>(T);
+  bool reject = false;
+  if (i < Lr) {
+    const int xv = a.x[static_cast<size_t>(r) * a.b + i];
+    const bool tok_ok = xv >= 0 && xv < a.V;
+    if (report && !tok_ok) raise_status(a.status, SV_ST_BAD_TOKEN);
+    const int trow = tb + i;
+    double p = 0.0, q = 0.0;
+    if (tok_ok) {
+      if (T == 0.0f) {
+        p = xv == a.row_argmax[trow] ? 1.0 : 0.0;
+      } else {
+        const float l = load_val_rt(row_ptr(a.tgt, a.dtype, trow, a.tgt_ld), a.dtype, xv);
+        p = p_of(l, a.row_cut[trow], invT, a.row_kept[trow]);
+      }
+      if (a.q_mode == SV_Q_MIXTURE) {
+        q = qx[i];
+      } else {
+        const int pos = pb + i;
+        if (T == 0.0f) {
+          q = xv == a.dargmax[pos] ? 1.0 : 0.0;
+        } else {
+          const float d = load_val_rt(row_ptr(a.draft, a.ddtype, static_cast<int64_t>(r) * a.b + i, a.draft_ld),
+                                      a.ddtype, xv);
+          q = exp(static_cast<double>(d) * invT - a.dlse[pos]);
+        }
+      }
+    }
+    const double u = u24(philox_at(seed, static_cast<uint32_t>(i), static_cast<uint32_t>(r)).x);
+    const bool accept = q > 0.0 ? (u < p / q) : (p > 0.0);
+    reject = !accept;
+    if (report) {
+      const size_t k = static_cast<size_t>(r) * a.b + i;
+      if (a.p_out) a.p_out[k] = p;
+      if (a.q_out) a.q_out[k] = q;
+      if (a.u_out) a.u_out[k] = static_cast<float>(u);
+    }
+  }
+  const uint64_t mask = __ballot(reject);
+  return mask ? (__ffsll(static_cast<long long>(mask)) - 1) : Lr;
+}
+
+__global__ __launch_bounds__(kWave) void k_accept(SampleArgs a) {
+  const int r = blockIdx.x;
+  int pb, Lr, tb;
+  if (!request_ok(a, r, pb, Lr, tb)) {
+    if (threadIdx.x == 0) {
+      raise_status(a.status, SV_ST_BAD_OFFSETS);
+      a.n_acc[r] = 0;
+    }
+    return;
+  }
+  const double* qx = a.q_mode == SV_Q_MIXTURE ? a.qx + static_cast<size_t>(r) * a.b : nullptr;
+  const int n = accept_wave(a, r, pb, Lr, tb, qx, true);
+  if (threadIdx.x == 0) a.n_acc[r] = n;
+}
+
+// ------------------------------------------------------------------ the draw
+// What one request's draw needs.
+struct DrawCtx {
   int j, trow;
   bool bonus;
-  double Td, kept, dlse;
+  double invT, kept, dlse;
   float cut;
   const char* trowp;
   const char* drowp;
-  int nq;        // mixture: branch entries at slot j (K, with their posterior mass)
-  int qtok[64];  // kept in LDS
+  int nq;  // mixture: branch entries at slot j with their posterior mass
+  int qtok[64];
   double qw[64];
 };
 
-// Returns false when the request needs no scan (T = 0: the draw is the argmax,
-// written here by the reporting kernel).
+// Scalars of the draw context of request r at slot j (thread 0 of the block).
 template <bool kDense>
-__device__ __forceinline__ bool res_setup(const SampleArgs& a, int r, bool report, ResCtx& c) {
-  const int lane = threadIdx.x;
-  const int pb = a.pos_off[r];
-  const int Lr = a.pos_off[r + 1] - pb;
-  const int tb = a.tgt_off[r];
-  if (!(Lr >= 0 && Lr <= a.b && a.tgt_off[r + 1] - tb == Lr + 1)) {
-    if (report && lane == 0) raise_status(a.status, SV_ST_BAD_OFFSETS);
-    return false;
-  }
-  int n = a.n_acc_in[r];
-  if (n < 0 || n > Lr) {
-    if (report && lane == 0) raise_status(a.status, SV_ST_BAD_NACC);
-    n = n < 0 ? 0 : Lr;
-  }
-  c.j = n;  // 0-based slot of the draw
-  c.bonus = n == Lr;
-  c.trow = tb + n;
-  const float T = a.T[r];
-  if (T == 0.0f) {  // p is one-hot at the argmax, and so is the residual
-    if (report && lane == 0) {
-      a.token[r] = a.row_argmax[c.trow];
-      a.is_bonus[r] = c.bonus ? 1 : 0;
-    }
-    return false;
-  }
-  c.Td = static_cast<double>(T);
-  c.cut = a.row_cut[c.trow];
-  c.kept = a.row_kept[c.trow];
-  c.trowp = row_ptr(a.tgt, a.dtype, c.trow, a.tgt_ld);
+__device__ __forceinline__ void draw_scalars(const SampleArgs& a, int r, int pb, int Lr, int tb, int j, DrawCtx& c) {
+  c.j = j;
+  c.bonus = j == Lr;
+  c.trow = tb + j;
+  c.invT = 1.0 / static_cast<double>(a.T[r]);
+  c.cut = a.row_cut[tb + j];
+  c.kept = a.row_kept[tb + j];
+  c.trowp = row_ptr(a.tgt, a.dtype, tb + j, a.tgt_ld);
   c.drowp = nullptr;
   c.dlse = 0.0;
   c.nq = 0;
-  if (kDense && !c.bonus) {
-    c.drowp = row_ptr(a.draft, a.ddtype, static_cast<int64_t>(r) * a.b + n, a.draft_ld);
-    c.dlse = a.dlse[pb + n];
+  if (kDense && j < Lr) {
+    c.drowp = row_ptr(a.draft, a.ddtype, static_cast<int64_t>(r) * a.b + j, a.draft_ld);
+    c.dlse = a.dlse[pb + j];
   }
-  if (!kDense && !c.bonus) {  // branch tokens at slot j with their posterior mass
-    if (lane < a.K) {
-      c.qtok[lane] = a.branch_tok[(static_cast<size_t>(r) * a.K + lane) * a.b + n];
-      c.qw[lane] = a.post_w[(static_cast<size_t>(r) * a.b + n) * a.K + lane];
-    }
-    c.nq = a.K;
-  }
-  __syncthreads();  // one wave: orders the LDS table before use
-  return true;
+  if (!kDense && j < Lr) c.nq = a.K;
 }
 
-// p (target, with top-p) and the draw weight w of 8 values of group g
+// q(v | x_<j) of the mixture at token v: the posterior mass of the branches at v
+__device__ __forceinline__ double mix_q(const DrawCtx& c, int v) {
+  double q = 0.0;
+  for (int t = 0; t < c.nq; ++t)
+    if (c.qtok[t] == v) q += c.qw[t];
+  return q;
+}
+
+// p and the draw weight of the 8 values of group g, in vocabulary order
 template <bool kDense>
-__device__ __forceinline__ void weights8(const SampleArgs& a, const ResCtx& c, int g, bool use_p, double p8[8],
+__device__ __forceinline__ void weights8(const SampleArgs& a, const DrawCtx& c, int g, bool use_p, double p8[8],
                                          double w8[8]) {
   float l[8];
   load8(c.trowp, a.dtype, g, a.V, l);
 #pragma unroll
-  for (int k = 0; k < 8; ++k) p8[k] = p_of(l[k], c.cut, c.Td, c.kept);
-  if (use_p) {
+  for (int k = 0; k < 8; ++k) p8[k] = p_of(l[k], c.cut, c.invT, c.kept);
+  if (use_p || c.bonus) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) w8[k] = p8[k];
     return;
@@ -235,7 +296,7 @@ __device__ __forceinline__ void weights8(const SampleArgs& a, const ResCtx& c, i
     load8(c.drowp, a.ddtype, g, a.V, d);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const double q = exp(static_cast<double>(d[k]) / c.Td - c.dlse);
+      const double q = exp(static_cast<double>(d[k]) * c.invT - c.dlse);
       const double t = p8[k] - q;
       w8[k] = t > 0.0 ? t : 0.0;
     }
@@ -243,12 +304,10 @@ __device__ __forceinline__ void weights8(const SampleArgs& a, const ResCtx& c, i
     const int v0 = g * 8;
 #pragma unroll
     for (int k = 0; k < 8; ++k) w8[k] = p8[k];
-    for (int t = 0; t < c.nq; ++t) {  // q(v | x_<j) = sum of the posterior over branches at v
+    for (int t = 0; t < c.nq; ++t) {
       const int dv = c.qtok[t] - v0;
       if (dv >= 0 && dv < 8) {
-        double q = 0.0;
-        for (int t2 = 0; t2 < c.nq; ++t2)
-          if (c.qtok[t2] == c.qtok[t]) q += c.qw[t2];
+        const double q = mix_q(c, c.qtok[t]);
 #pragma unroll
         for (int k = 0; k < 8; ++k)
           if (k == dv) {
@@ -260,97 +319,288 @@ __device__ __forceinline__ void weights8(const SampleArgs& a, const ResCtx& c, i
   }
 }
 
+struct SumShared {
+  double red[kSumNT / kWave];
+  float st[kSumNT / kWave][512];  // per-wave staging of the values at or above the cut
+  float sd[kSumNT / kWave][512];  // the matching draft values (dense residual)
+};
+
+// Chunk ch of the draw row: sum of p and of the draw weight, in double, to part.
+// Each thread prefetches its (up to) 4 groups of a 1024-group super-tile before
+// any arithmetic.  The mixture's sparse corrections (branch tokens) are added
+// by thread 0.
 template <bool kDense>
-__global__ __launch_bounds__(kWave) void k_res_sums(SampleArgs a) {
-  __shared__ ResCtx c;
-  const int lane = threadIdx.x;
-  const int r = blockIdx.x / a.S;
-  const int ch = blockIdx.x % a.S;
-  if (!res_setup<kDense>(a, r, false, c)) return;
+__device__ void chunk_sums(const SampleArgs& a, const DrawCtx& c, int r, int ch, SumShared& sh) {
+  constexpr int TILES = 4;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wv = tid / kWave;
   const int NG = (a.V + 7) / 8;
   const int g0 = ch * a.CG;
   const int g1 = min(NG, g0 + a.CG);
+  const bool dense_res = kDense && !c.bonus;
+  const bool cut_on = c.cut > -INFINITY;
   double sp = 0.0, sw = 0.0;
-  for (int g = g0 + lane; g < g1; g += kWave) {
-    double p8[8], w8[8];
-    weights8<kDense>(a, c, g, c.bonus, p8, w8);
+  for (int sb = g0; sb < g1; sb += TILES * kSumNT) {
+    float l[TILES][8], d[TILES][8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      sp += p8[k];
-      sw += w8[k];
+    for (int k = 0; k < TILES; ++k) {
+      const int g = sb + k * kSumNT + tid;
+      if (g < g1) {
+        load8(c.trowp, a.dtype, g, a.V, l[k]);
+        if (dense_res) load8(c.drowp, a.ddtype, g, a.V, d[k]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) l[k][q] = -INFINITY;
+      }
+    }
+    if (!cut_on) {
+#pragma unroll
+      for (int k = 0; k < TILES; ++k) {
+        if (sb + k * kSumNT + tid >= g1) continue;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const double p = exp(static_cast<double>(l[k][q]) * c.invT - c.kept);
+          sp += p;
+          if (dense_res) {
+            const double t = p - exp(static_cast<double>(d[k][q]) * c.invT - c.dlse);
+            sw += t > 0.0 ? t : 0.0;
+          } else {
+            sw += p;
+          }
+        }
+      }
+    } else {
+      // top-p: only values at or above the cut carry weight; compact them per wave
+#pragma unroll
+      for (int k = 0; k < TILES; ++k) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) m |= (l[k][q] >= c.cut ? 1u : 0u) << q;
+        const int cnt = __popc(m);
+        const int inc = wave_incl_scan_i32(cnt);
+        const int tot = __shfl(inc, kWave - 1, kWave);
+        int o = inc - cnt;
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if (m & (1u << q)) {
+            sh.st[wv][o] = l[k][q];
+            if (dense_res) sh.sd[wv][o] = d[k][q];
+            ++o;
+          }
+        __syncthreads();
+        for (int e = lane; e < tot; e += kWave) {
+          const double p = exp(static_cast<double>(sh.st[wv][e]) * c.invT - c.kept);
+          sp += p;
+          if (dense_res) {
+            const double t = p - exp(static_cast<double>(sh.sd[wv][e]) * c.invT - c.dlse);
+            sw += t > 0.0 ? t : 0.0;
+          } else {
+            sw += p;
+          }
+        }
+        __syncthreads();
+      }
     }
   }
-  sp = wave_sum_f64(sp);
-  sw = wave_sum_f64(sw);
-  if (lane == 0) {
+  sp = block_sum_f64<kSumNT>(sp, sh.red);
+  sw = block_sum_f64<kSumNT>(sw, sh.red);
+  if (tid == 0) {
+    if (!kDense && !c.bonus) {  // branch tokens: weight max(0, p - q) instead of p
+      const int v0 = g0 * 8, v1 = min(a.V, g1 * 8);
+      for (int t = 0; t < c.nq; ++t) {
+        const int v = c.qtok[t];
+        bool first = true;
+        for (int t2 = 0; t2 < t; ++t2)
+          if (c.qtok[t2] == v) first = false;
+        if (!first || v < v0 || v >= v1) continue;
+        const double p = p_of(load_val_rt(c.trowp, a.dtype, v), c.cut, c.invT, c.kept);
+        const double dq = p - mix_q(c, v);
+        sw += (dq > 0.0 ? dq : 0.0) - p;
+      }
+    }
     double* pp = a.part + (static_cast<size_t>(r) * a.S + ch) * 2;
     pp[0] = sw;
     pp[1] = sp;
   }
 }
 
+struct TailShared {
+  DrawCtx c;
+  SumShared s;
+  ReqTables t;
+  double qx[64];
+  int n;
+};
+
+// Standalone chunk sums (sv_residual_sample): n_acc is an input.
 template <bool kDense>
-__global__ __launch_bounds__(kWave) void k_res_pick(SampleArgs a) {
-  __shared__ ResCtx c;
-  const int lane = threadIdx.x;
-  const int r = blockIdx.x;
-  if (!res_setup<kDense>(a, r, true, c)) return;
-  const double u = u24(philox_at(*a.seed, static_cast<uint32_t>(c.j), static_cast<uint32_t>(r)).y);
-  // chunk sums, one per lane, in chunk order
-  const double* pp = a.part + static_cast<size_t>(r) * a.S * 2;
-  const double cw = lane < a.S ? pp[lane * 2] : 0.0;
-  const bool use_p = c.bonus || !(wave_sum_f64(cw) > 0.0);  // an all-zero residual (rounding) falls back to p
-  const double wc = lane < a.S ? pp[lane * 2 + (use_p ? 1 : 0)] : 0.0;
-  const double incl = wave_incl_scan_f64(wc);
-  const double W = __shfl(incl, kWave - 1, kWave);
-  const double t = u * W;
-  const uint64_t over = __ballot(lane < a.S && incl > t);
-  const int cstar = over ? __ffsll(static_cast<long long>(over)) - 1 : a.S - 1;
-  double run = __shfl(incl - wc, cstar, kWave);  // weight before chunk cstar
-  // scan chunk cstar, 64 groups (512 values) at a time
-  const int NG = (a.V + 7) / 8;
-  const int h0 = cstar * a.CG;
-  const int h1 = min(NG, h0 + a.CG);
-  int found = -1, lastpos = -1;
-  for (int gb = h0; gb < h1; gb += kWave) {
-    const int g = gb + lane;
-    double p8[8], w8[8];
-    double loc = 0.0;
-    if (g < h1) {
-      weights8<kDense>(a, c, g, use_p, p8, w8);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) loc += w8[k];
+__global__ __launch_bounds__(kSumNT) void k_res_sums(SampleArgs a) {
+  __shared__ TailShared sh;
+  const int r = blockIdx.x / a.S, ch = blockIdx.x % a.S;
+  const int tid = threadIdx.x;
+  int pb, Lr, tb;
+  if (!request_ok(a, r, pb, Lr, tb)) return;
+  if (a.T[r] == 0.0f) return;  // the draw is the argmax
+  int n = a.n_acc_in[r];
+  n = n < 0 ? 0 : (n > Lr ? Lr : n);
+  if (tid == 0) draw_scalars<kDense>(a, r, pb, Lr, tb, n, sh.c);
+  if (!kDense && n < Lr && tid < a.K) {
+    sh.c.qtok[tid] = a.branch_tok[(static_cast<size_t>(r) * a.K + tid) * a.b + n];
+    sh.c.qw[tid] = a.post_w[(static_cast<size_t>(r) * a.b + n) * a.K + tid];
+  }
+  __syncthreads();
+  chunk_sums<kDense>(a, sh.c, r, ch, sh.s);
+}
+
+// Fused tail: posterior (mixture), acceptance, then the chunk sums of the draw.
+template <bool kDense>
+__global__ __launch_bounds__(kSumNT) void k_tail_sums(SampleArgs a) {
+  __shared__ TailShared sh;
+  const int r = blockIdx.x / a.S, ch = blockIdx.x % a.S;
+  const int tid = threadIdx.x;
+  int pb, Lr, tb;
+  if (!request_ok(a, r, pb, Lr, tb)) {
+    if (ch == 0 && tid == 0) {
+      raise_status(a.status, SV_ST_BAD_OFFSETS);
+      a.n_acc[r] = 0;
     }
-    const double inc = wave_incl_scan_f64(loc);
-    int mine = -1;
-    if (g < h1) {
-      double acc = run + (inc - loc);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        if (w8[k] > 0.0) lastpos = g * 8 + k;
-        acc += w8[k];
-        if (acc > t && mine < 0) mine = g * 8 + k;
+    return;
+  }
+  const bool report = ch == 0;
+  if (!kDense) {
+    stage_tables(a, r, Lr, sh.t);
+    __syncthreads();
+  }
+  if (tid < kWave) {
+    double pi = 0.0;
+    int f = 0;
+    if (!kDense) posterior_wave(a, r, Lr, sh.t, report, sh.qx, pi, f);
+    const int n = accept_wave(a, r, pb, Lr, tb, sh.qx, report);
+    if (tid == 0) {
+      sh.n = n;
+      if (report) a.n_acc[r] = n;
+      if (a.T[r] != 0.0f) draw_scalars<kDense>(a, r, pb, Lr, tb, n, sh.c);
+    }
+    if (!kDense && n < Lr) {
+      // branch tokens and posterior mass at the draw slot (as posterior_wave formed them)
+      const bool act = tid < a.K;
+      const double w = act && f >= n ? pi : 0.0;
+      const double sw = wave_sum_f64(w);
+      if (act) {
+        sh.c.qw[tid] = sw > 0.0 ? w / sw : 0.0;
+        sh.c.qtok[tid] = sh.t.g[tid * 64 + n];
       }
     }
-    const uint64_t hit = __ballot(mine >= 0);
-    if (hit) {
-      found = __shfl(mine, __ffsll(static_cast<long long>(hit)) - 1, kWave);
+  }
+  __syncthreads();
+  if (a.T[r] == 0.0f) return;  // the draw is the argmax (taken by the pick kernel)
+  chunk_sums<kDense>(a, sh.c, r, ch, sh.s);
+}
+
+// The draw: one 256-thread block per request, after the chunk sums.
+template <bool kDense>
+__global__ __launch_bounds__(kSumNT) void k_res_pick(SampleArgs a) {
+  __shared__ DrawCtx c;
+  __shared__ double red[kSumNT / kWave];
+  __shared__ int redi[kSumNT / kWave];
+  __shared__ int s_cstar, s_use_p;
+  __shared__ double s_base, s_t;
+  const int tid = threadIdx.x;
+  const int r = blockIdx.x;
+  int pb, Lr, tb;
+  if (!request_ok(a, r, pb, Lr, tb)) {
+    if (tid == 0) raise_status(a.status, SV_ST_BAD_OFFSETS);
+    return;
+  }
+  int n = a.n_acc_in[r];
+  if (n < 0 || n > Lr) {
+    if (tid == 0) raise_status(a.status, SV_ST_BAD_NACC);
+    n = n < 0 ? 0 : Lr;
+  }
+  if (a.T[r] == 0.0f) {  // p is one-hot at the argmax, and so is the residual
+    if (tid == 0) {
+      a.token[r] = a.row_argmax[tb + n];
+      a.is_bonus[r] = n == Lr ? 1 : 0;
+    }
+    return;
+  }
+  if (tid == 0) draw_scalars<kDense>(a, r, pb, Lr, tb, n, c);
+  if (!kDense && n < Lr && tid < a.K) {
+    c.qtok[tid] = a.branch_tok[(static_cast<size_t>(r) * a.K + tid) * a.b + n];
+    c.qw[tid] = a.post_w[(static_cast<size_t>(r) * a.b + n) * a.K + tid];
+  }
+  if (tid < kWave) {  // wave 0: the chunk holding u * W, from the chunk sums (one per lane)
+    const int lane = tid;
+    const double u = u24(philox_at(*a.seed, static_cast<uint32_t>(n), static_cast<uint32_t>(r)).y);
+    const double* pp = a.part + static_cast<size_t>(r) * a.S * 2;
+    const double cw = lane < a.S ? pp[lane * 2] : 0.0;
+    const bool use_p = n == Lr || !(wave_sum_f64(cw) > 0.0);  // an all-zero residual (rounding) falls back to p
+    const double wc = lane < a.S ? pp[lane * 2 + (use_p ? 1 : 0)] : 0.0;
+    const double incl = wave_incl_scan_f64(wc);
+    const double W = __shfl(incl, kWave - 1, kWave);
+    const double t = u * W;
+    const uint64_t over = __ballot(lane < a.S && incl > t);
+    const int cstar = over ? __ffsll(static_cast<long long>(over)) - 1 : a.S - 1;
+    const double base = __shfl(incl - wc, cstar, kWave);  // weight before chunk cstar
+    if (lane == 0) {
+      s_cstar = cstar;
+      s_use_p = use_p ? 1 : 0;
+      s_base = base;
+      s_t = t;
+    }
+  }
+  __syncthreads();
+  const bool use_p = s_use_p != 0;
+  const double t = s_t;
+  // walk chunk cstar: thread tid takes GPT consecutive groups (loaded at once),
+  // an exclusive block scan of the per-thread sums finds the thread holding t
+  constexpr int GPT = 4;
+  const int NG = (a.V + 7) / 8;
+  const int h0 = s_cstar * a.CG;
+  const int h1 = min(NG, h0 + a.CG);
+  double run = s_base;
+  int found = 0x7FFFFFFF, lastpos = -1;
+  for (int sb = h0; sb < h1; sb += GPT * kSumNT) {
+    const int gs = sb + tid * GPT;
+    double w[GPT][8];
+    double loc = 0.0;
+#pragma unroll
+    for (int k = 0; k < GPT; ++k) {
+      double p8[8];
+      if (gs + k < h1) {
+        weights8<kDense>(a, c, gs + k, use_p, p8, w[k]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) w[k][q] = 0.0;
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) loc += w[k][q];
+    }
+    double tile;
+    const double excl = block_excl_scan_f64<kSumNT>(loc, red, &tile);
+    double acc = run + excl;
+#pragma unroll
+    for (int k = 0; k < GPT; ++k)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (w[k][q] > 0.0) lastpos = (gs + k) * 8 + q;
+        acc += w[k][q];
+        if (acc > t && found == 0x7FFFFFFF) found = (gs + k) * 8 + q;
+      }
+    const int fmin = block_min_i32<kSumNT>(found, redi);
+    if (fmin != 0x7FFFFFFF) {
+      found = fmin;
       break;
     }
-    run += __shfl(inc, kWave - 1, kWave);
+    run += tile;
   }
-  if (found < 0) {  // rounding: the last positive weight of the chunk
-    int lp = lastpos;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const int q = __shfl_xor(lp, o, kWave);
-      lp = q > lp ? q : lp;
-    }
-    found = lp < 0 ? 0 : lp;
+  if (found == 0x7FFFFFFF) {  // rounding: the last positive weight of the chunk
+    found = -block_min_i32<kSumNT>(-lastpos, redi);
+    if (found < 0) found = 0;
   }
-  if (lane == 0) {
+  if (tid == 0) {
     a.token[r] = found;
-    a.is_bonus[r] = c.bonus ? 1 : 0;
+    a.is_bonus[r] = n == Lr ? 1 : 0;
   }
 }
 
@@ -378,6 +628,23 @@ static bool sample_args_ok(const void* tgt_logits, int32_t dtype, int64_t tgt_ld
   return true;
 }
 
+static SampleArgs sample_args(const void* tgt_logits, int32_t dtype, int64_t tgt_ld, int32_t V, const int32_t* tgt_off,
+                              const int32_t* pos_off, int32_t R, int32_t b, const float* temperature,
+                              const int32_t* row_argmax, const float* row_cut, const double* row_kept_lse,
+                              int32_t q_mode, const void* draft_logits, int32_t draft_dtype, int64_t draft_ld,
+                              const int32_t* draft_argmax, const double* draft_lse, const uint64_t* seed, void* ws) {
+  SampleArgs a{};
+  a.tgt = tgt_logits; a.dtype = dtype; a.tgt_ld = tgt_ld; a.V = V; a.tgt_off = tgt_off; a.pos_off = pos_off;
+  a.R = R; a.b = b; a.T = temperature; a.row_argmax = row_argmax; a.row_cut = row_cut; a.row_kept = row_kept_lse;
+  a.q_mode = q_mode; a.draft = draft_logits; a.ddtype = draft_dtype; a.draft_ld = draft_ld;
+  a.dargmax = draft_argmax; a.dlse = draft_lse; a.seed = seed; a.status = status_word(ws);
+  const WsLayout l = ws_layout(R, b, 0, V);
+  a.part = reinterpret_cast<double*>(static_cast<char*>(ws) + l.res_part);
+  a.S = res_chunks(V);
+  a.CG = ((V + 7) / 8 + a.S - 1) / a.S;
+  return a;
+}
+
 extern "C" int32_t sv_accept(const void* tgt_logits, int32_t dtype, int64_t tgt_ld, int32_t V, const int32_t* tgt_off,
                              const int32_t* pos_off, int32_t R, int32_t b, const float* temperature,
                              const int32_t* row_argmax, const float* row_cut, const double* row_kept_lse,
@@ -390,12 +657,10 @@ extern "C" int32_t sv_accept(const void* tgt_logits, int32_t dtype, int64_t tgt_
     return SV_ERR_ARG;
   if (!draft_tok || !n_acc || (q_mode == SV_Q_MIXTURE && !q_at_draft)) return SV_ERR_ARG;
   if (ws_bytes < 256) return SV_ERR_WORKSPACE;
-  SampleArgs a{};
-  a.tgt = tgt_logits; a.dtype = dtype; a.tgt_ld = tgt_ld; a.V = V; a.tgt_off = tgt_off; a.pos_off = pos_off;
-  a.R = R; a.b = b; a.T = temperature; a.row_argmax = row_argmax; a.row_cut = row_cut; a.row_kept = row_kept_lse;
-  a.x = draft_tok; a.q_mode = q_mode; a.draft = draft_logits; a.ddtype = draft_dtype; a.draft_ld = draft_ld;
-  a.dargmax = draft_argmax; a.dlse = draft_lse; a.qx = q_at_draft; a.seed = seed; a.n_acc = n_acc;
-  a.p_out = p_out; a.q_out = q_out; a.u_out = u_out; a.status = status_word(ws);
+  SampleArgs a = sample_args(tgt_logits, dtype, tgt_ld, V, tgt_off, pos_off, R, b, temperature, row_argmax, row_cut,
+                             row_kept_lse, q_mode, draft_logits, draft_dtype, draft_ld, draft_argmax, draft_lse, seed,
+                             ws);
+  a.x = draft_tok; a.qx = q_at_draft; a.n_acc = n_acc; a.p_out = p_out; a.q_out = q_out; a.u_out = u_out;
   hipLaunchKernelGGL(k_accept, dim3(R), dim3(kWave), 0, static_cast<hipStream_t>(stream), a);
   return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
 }
@@ -413,29 +678,57 @@ extern "C" int32_t sv_residual_sample(const void* tgt_logits, int32_t dtype, int
     return SV_ERR_ARG;
   if (!n_acc || !token || !is_bonus) return SV_ERR_ARG;
   if (q_mode == SV_Q_MIXTURE && (K < 1 || K > 64 || !branch_tok || !post_w)) return SV_ERR_ARG;
-  const WsLayout l = ws_layout(R, b, q_mode == SV_Q_MIXTURE ? K : 0, V);
-  if (ws_bytes < l.total) return SV_ERR_WORKSPACE;
-  const int NG = (V + 7) / 8;
-  const int S = res_chunks(V);
-  const int CG = (NG + S - 1) / S;
-  SampleArgs a{};
-  a.tgt = tgt_logits; a.dtype = dtype; a.tgt_ld = tgt_ld; a.V = V; a.tgt_off = tgt_off; a.pos_off = pos_off;
-  a.R = R; a.b = b; a.T = temperature; a.row_argmax = row_argmax; a.row_cut = row_cut; a.row_kept = row_kept_lse;
-  a.q_mode = q_mode; a.draft = draft_logits; a.ddtype = draft_dtype; a.draft_ld = draft_ld; a.dargmax = draft_argmax;
-  a.dlse = draft_lse; a.K = K; a.branch_tok = branch_tok; a.post_w = post_w; a.seed = seed; a.n_acc_in = n_acc;
-  a.token = token; a.is_bonus = is_bonus; a.status = status_word(ws);
-  a.part = reinterpret_cast<double*>(static_cast<char*>(ws) + l.res_part);
-  a.S = S;
-  a.CG = CG;
+  if (ws_bytes < ws_layout(R, b, q_mode == SV_Q_MIXTURE ? K : 0, V).total) return SV_ERR_WORKSPACE;
+  SampleArgs a = sample_args(tgt_logits, dtype, tgt_ld, V, tgt_off, pos_off, R, b, temperature, row_argmax, row_cut,
+                             row_kept_lse, q_mode, draft_logits, draft_dtype, draft_ld, draft_argmax, draft_lse, seed,
+                             ws);
+  a.K = q_mode == SV_Q_MIXTURE ? K : 0; a.branch_tok = branch_tok; a.post_w = const_cast<double*>(post_w);
+  a.n_acc_in = n_acc; a.token = token; a.is_bonus = is_bonus;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (q_mode == SV_Q_DENSE) {
-    hipLaunchKernelGGL(k_res_sums<true>, dim3(R * S), dim3(kWave), 0, s, a);
+    hipLaunchKernelGGL(k_res_sums<true>, dim3(R * a.S), dim3(kSumNT), 0, s, a);
     if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
-    hipLaunchKernelGGL(k_res_pick<true>, dim3(R), dim3(kWave), 0, s, a);
+    hipLaunchKernelGGL(k_res_pick<true>, dim3(R), dim3(kSumNT), 0, s, a);
   } else {
-    hipLaunchKernelGGL(k_res_sums<false>, dim3(R * S), dim3(kWave), 0, s, a);
+    hipLaunchKernelGGL(k_res_sums<false>, dim3(R * a.S), dim3(kSumNT), 0, s, a);
     if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
-    hipLaunchKernelGGL(k_res_pick<false>, dim3(R), dim3(kWave), 0, s, a);
+    hipLaunchKernelGGL(k_res_pick<false>, dim3(R), dim3(kSumNT), 0, s, a);
+  }
+  return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
+}
+
+extern "C" int32_t sv_accept_sample(const void* tgt_logits, int32_t dtype, int64_t tgt_ld, int32_t V,
+                                    const int32_t* tgt_off, const int32_t* pos_off, int32_t R, int32_t b,
+                                    const float* temperature, const int32_t* row_argmax, const float* row_cut,
+                                    const double* row_kept_lse, const int32_t* draft_tok, int32_t q_mode,
+                                    const void* draft_logits, int32_t draft_dtype, int64_t draft_ld,
+                                    const int32_t* draft_argmax, const double* draft_lse, int32_t K,
+                                    const float* mix_logits, const int32_t* branch_tok, double* post_w,
+                                    double* q_at_draft, const uint64_t* seed, int32_t* n_acc, int32_t* token,
+                                    int32_t* is_bonus, double* p_out, double* q_out, float* u_out, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  if (!sample_args_ok(tgt_logits, dtype, tgt_ld, V, tgt_off, pos_off, R, b, temperature, row_argmax, row_cut,
+                      row_kept_lse, q_mode, draft_logits, draft_dtype, draft_ld, draft_argmax, draft_lse, seed, ws))
+    return SV_ERR_ARG;
+  if (!draft_tok || !n_acc || !token || !is_bonus) return SV_ERR_ARG;
+  if (q_mode == SV_Q_MIXTURE && (K < 1 || K > 64 || !mix_logits || !branch_tok || !post_w || !q_at_draft))
+    return SV_ERR_ARG;
+  if (ws_bytes < ws_layout(R, b, q_mode == SV_Q_MIXTURE ? K : 0, V).total) return SV_ERR_WORKSPACE;
+  SampleArgs a = sample_args(tgt_logits, dtype, tgt_ld, V, tgt_off, pos_off, R, b, temperature, row_argmax, row_cut,
+                             row_kept_lse, q_mode, draft_logits, draft_dtype, draft_ld, draft_argmax, draft_lse, seed,
+                             ws);
+  a.x = draft_tok; a.K = q_mode == SV_Q_MIXTURE ? K : 0; a.mix = mix_logits; a.branch_tok = branch_tok;
+  a.post_w = post_w; a.q_at_draft = q_at_draft; a.n_acc = n_acc; a.n_acc_in = n_acc; a.token = token;
+  a.is_bonus = is_bonus; a.p_out = p_out; a.q_out = q_out; a.u_out = u_out;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (q_mode == SV_Q_DENSE) {
+    hipLaunchKernelGGL(k_tail_sums<true>, dim3(R * a.S), dim3(kSumNT), 0, s, a);
+    if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
+    hipLaunchKernelGGL(k_res_pick<true>, dim3(R), dim3(kSumNT), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(k_tail_sums<false>, dim3(R * a.S), dim3(kSumNT), 0, s, a);
+    if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
+    hipLaunchKernelGGL(k_res_pick<false>, dim3(R), dim3(kSumNT), 0, s, a);
   }
   return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
 }

@@ -19,7 +19,7 @@ import numpy as np
 import torch
 
 from . import (SV_BF16, SV_F32, SV_Q_DENSE, SV_Q_MIXTURE, dvl_alloc_pack, make_workspace, sv_accept, sv_mixture_q,
-               sv_residual_sample, sv_softmax_stats, sv_topp_threshold, sv_verify_rows)
+               sv_accept_sample, sv_residual_sample, sv_softmax_stats, sv_topp_threshold, sv_verify_rows)
 
 
 def row_pitch(V: int, dtype: str) -> int:
@@ -143,21 +143,38 @@ class VerifyStep:
                            self.ws, self.ws_bytes, stream)
 
     def run_rows_fused(self, tgt, tgt_ld, comp, comp_ld, stream=None):
-        """Target rows and component rows in one launch (mixture proposal)."""
+        """Target rows and component rows (branch argmax) in one launch."""
         sv_verify_rows(tgt, self.dt, tgt_ld, self.V, self.tgt_off, self.R, self.max_rows, self.T,
                        self.top_p if self.use_topp else None, self.row_max, self.row_argmax, self.row_lse,
-                       self.row_cut, self.row_kept, comp, comp_ld, self.K, self.b, self.mix, self.pos_off,
-                       self.max_pos, self.x, self.branch_tok, self.post_w, self.q_at_draft, self.ws, self.ws_bytes,
-                       stream)
+                       self.row_cut, self.row_kept, comp, comp_ld, self.K, self.b, self.pos_off, self.max_pos,
+                       self.branch_tok, self.ws, self.ws_bytes, stream)
+
+    def run_accept_sample(self, tgt, tgt_ld, *, draft=None, draft_ld=0, stream=None):
+        """Posterior (mixture), acceptance and the draw: two launches."""
+        dense = self.q_mode == SV_Q_DENSE
+        sv_accept_sample(tgt, self.dt, tgt_ld, self.V, self.tgt_off, self.pos_off, self.R, self.b, self.T,
+                         self.row_argmax, self.row_cut, self.row_kept, self.x, self.q_mode,
+                         draft if dense else None, self.dt, draft_ld if dense else 0,
+                         self.d_argmax if dense else None, self.d_lse if dense else None, self.K,
+                         None if dense else self.mix, None if dense else self.branch_tok,
+                         None if dense else self.post_w, None if dense else self.q_at_draft, self.seed, self.n_acc,
+                         self.token, self.is_bonus, self.p_out, self.q_out, self.u_out, self.ws, self.ws_bytes,
+                         stream)
 
     def run_verify(self, tgt, tgt_ld, *, draft=None, draft_ld=0, comp=None, comp_ld=0, side_stream=None,
                    fused=False):
         """The verification calls on torch's current stream.  With `side_stream`,
-        the target-row statistics run there, concurrently with the proposal;
-        with `fused` (mixture only) they share one launch with it."""
+        the target-row statistics run there, concurrently with the proposal.
+        With `fused`: sv_verify_rows (mixture) and sv_accept_sample."""
         if fused:
-            self.run_rows_fused(tgt, tgt_ld, comp, comp_ld)
-        elif side_stream is None:
+            if self.q_mode == SV_Q_DENSE:
+                self.run_rows(tgt, tgt_ld)
+                self.run_proposal(draft=draft, draft_ld=draft_ld)
+            else:
+                self.run_rows_fused(tgt, tgt_ld, comp, comp_ld)
+            self.run_accept_sample(tgt, tgt_ld, draft=draft, draft_ld=draft_ld)
+            return
+        if side_stream is None:
             self.run_rows(tgt, tgt_ld)
             self.run_proposal(draft=draft, draft_ld=draft_ld, comp=comp, comp_ld=comp_ld)
         else:

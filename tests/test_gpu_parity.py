@@ -49,7 +49,7 @@ def test_philox_words_bitexact(seed):
 def _dvl_cases():
     rng = np.random.default_rng(7)
     cases = []
-    for R, b in [(1, 1), (3, 5), (32, 16), (7, 64), (300, 16)]:
+    for R, b in [(1, 1), (3, 5), (32, 16), (7, 64), (300, 16), (600, 16)]:
         for kind in ("beta", "ties"):
             if kind == "beta":
                 a = rng.beta(8, 2, size=(R, b)).astype(np.float32)
@@ -290,13 +290,14 @@ def test_two_stream_step_matches_oracle(c):
     assert_rate(rep)
 
 
-FUSED = [(4, dict(V=4099, R=4)), (5, dict(V=4099, R=8, steps=4)), (5, dict(V=1031, R=48, steps=2)),
-         (4, dict()), (5, dict(steps=6))]
+FUSED = [(1, dict()), (2, dict(V=2053, R=4)), (3, dict(V=2053, R=8, steps=3)),
+         (4, dict(V=4099, R=4)), (5, dict(V=4099, R=8, steps=4)), (5, dict(V=1031, R=48, steps=2)),
+         (2, dict()), (3, dict()), (4, dict()), (5, dict(steps=6))]
 
 
 @pytest.mark.parametrize("c,kw", FUSED, ids=[f"cfg{c}-" + "-".join(f"{k}{v}" for k, v in kw.items()) for c, kw in FUSED])
 def test_fused_rows_mixture_matches_oracle(c, kw):
-    """sv_verify_rows: target rows and component rows in one launch."""
+    """The fused path: sv_verify_rows (mixture) and sv_accept_sample."""
     w = synth.config(c, **kw)
     vs, run = gpu_step_runner(w, fused=True)
     rep = None
