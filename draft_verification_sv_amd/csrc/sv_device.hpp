@@ -219,23 +219,40 @@ __device__ __forceinline__ void raise_status(uint32_t* status, uint32_t bits) {
   __hip_atomic_fetch_or(status, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ------------------------------------------------------------------ the draw's row layout
+// The row a request draws from is cut into sub-chunks of 64 8-value groups
+// (512 values, one group per lane of a wave); one block of the sums kernel
+// (kSumNT threads) covers a chunk of kSubPerWave sub-chunks per wave.
+constexpr int kSumNT = 256;
+constexpr int kSubG = 64;
+constexpr int kSubPerWave = 4;
+constexpr int kChunkSubs = kSubPerWave * (kSumNT / kWave);  // 16 sub-chunks, 1024 groups
+
+__host__ __device__ inline int groups_of(int V) { return (V + 7) / 8; }
+__host__ __device__ inline int sub_chunks(int V) { return (groups_of(V) + kSubG - 1) / kSubG; }
+__host__ __device__ inline int res_chunks(int V) { return (sub_chunks(V) + kChunkSubs - 1) / kChunkSubs; }
+
+// What the draw of one request needs: written by the first chunk block of the
+// sums kernel, read by the pick kernel.
+enum : int32_t { kDrawResidual = 0, kDrawP = 1, kDrawGreedy = 2, kDrawNone = 3 };
+struct DrawRec {
+  int32_t mode, n, bonus, token;  // token: the argmax when greedy
+  int32_t ncorr, pad0;
+  int64_t trow, drow;  // target row of the draw; dense draft row (residual)
+  float cut, pad1;
+  double invT, kept, dlse;
+  int32_t ctok[64];  // mixture residual: the distinct branch tokens at the slot
+  double cw[64];     // and their draw weight max(0, p - q)
+};
+
 // ------------------------------------------------------------------ workspace layout
-// [status word, 256 B][residual chunk sums: R * S_res * 2 doubles]
+// [status word, 256 B][draw records, R][sub-chunk sums, R * NSUB * 2 doubles]
 // Cross-block results travel through kernel boundaries (stream order), not
 // through in-kernel fences: a device-scope release on gfx950 writes back the
 // L2, which is far too costly to pay once per block.
 struct WsLayout {
-  size_t status, res_part, total;
+  size_t status, rec, sub, total;
 };
-
-__host__ __device__ inline int res_chunks(int V) {
-  const int ngroups = (V + 7) / 8;  // 8-value groups
-  const int target = 256 * 4;       // groups per chunk: 4 per thread of a 256-thread block
-  int s = (ngroups + target - 1) / target;
-  if (s < 1) s = 1;
-  if (s > 64) s = 64;
-  return s;
-}
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
@@ -244,8 +261,9 @@ __host__ __device__ inline WsLayout ws_layout(int R, int b, int K, int V) {
   (void)K;
   WsLayout l;
   l.status = 0;
-  l.res_part = 256;
-  l.total = l.res_part + align256(sizeof(double) * 2 * static_cast<size_t>(R) * res_chunks(V));
+  l.rec = 256;
+  l.sub = l.rec + align256(sizeof(DrawRec) * static_cast<size_t>(R));
+  l.total = l.sub + align256(sizeof(double) * 2 * static_cast<size_t>(R) * sub_chunks(V));
   return l;
 }
 

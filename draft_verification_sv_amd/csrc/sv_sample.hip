@@ -8,33 +8,32 @@
 // is drawn from p_{L_r + 1}.  Uniforms come from Philox4x32-10 at counter
 // (position, request, 0, 0): word 0 for the test, word 1 for the draw.
 //
-// Acceptance: one wave per request, one lane per position (b <= 64); p and q at
-// the draft token are formed in double; a ballot over the rejecting lanes gives
-// the first rejection.
+// Two launches per step, both built as short chains of independent loads:
 //
-// Draw: the sampled row is cut into S <= 64 chunks of up to 1024 8-value groups.
-// Chunk sums: one 256-thread block per chunk loads its groups at once and adds
-// their weights in double.  With a top-p cut,
-// tokens below the cut have weight 0, so each wave first compacts the values
-// at or above the cut into LDS and evaluates exp only for those.  Pick (after a
-// kernel boundary): one block per request; its first wave scans the chunk sums
-// (one per lane) to find the chunk holding u * W, then the block walks that
-// chunk 8192 values at a time: per-thread sums of 32 consecutive weights, an
-// LDS-staged exclusive block scan, and a block minimum over the first index
-// whose running weight exceeds u * W.
+// Sums (one 256-thread block per (request, chunk of 1024 8-value groups)):
+//   A. the request's offsets, temperature, seed, draft tokens, mixing logits
+//      and branch tokens, each by its own thread;
+//   B. the row statistics of the L_r + 1 candidate rows, the target (and
+//      dense draft) logits at the draft tokens, and the target logits at every
+//      branch token, each by its own thread;
+//   C. one wave: the category posterior in closed form, the acceptance tests,
+//      the first rejection n, and the draw context of slot n;
+//   D. the chunk of the drawn row: each wave sums p and the draw weight over
+//      its 512-value sub-chunks (values below the top-p cut are compacted
+//      away first) and writes one pair of doubles per sub-chunk.
+// Every chunk block recomputes A-C (at most 64 positions, a few KB of
+// gathers), so that no block waits for another; the first one writes the
+// acceptance outputs and the draw record.
 //
-// The fused tail (sv_accept_sample) runs the category posterior, the
-// acceptance tests and the chunk sums in one grid: every chunk block
-// recomputes its request's posterior and acceptance (at most 64 positions, a
-// few KB of gathers) so that no block waits for another.
+// Pick (one block per request): a block scan over the request's sub-chunk
+// sums finds the sub-chunk holding u * W; one wave then re-forms its 512
+// weights and scans them.
 #include <math.h>
 
 #include "sv_device.hpp"
 #include "sv_host.hpp"
 
 namespace sv {
-
-constexpr int kSumNT = 256;  // threads of a chunk-sum block
 
 struct SampleArgs {
   const void* tgt;
@@ -59,7 +58,7 @@ struct SampleArgs {
   int K;
   const float* mix;  // mixing logits (fused tail)
   const int32_t* branch_tok;
-  double* post_w;      // read by the draw; written by the fused tail
+  double* post_w;      // read by the standalone draw; written by the fused tail
   double* q_at_draft;  // written by the fused tail
   const uint64_t* seed;
   const int32_t* n_acc_in;
@@ -69,9 +68,10 @@ struct SampleArgs {
   double* p_out;
   double* q_out;
   float* u_out;
-  double* part;  // [R * S * 2] chunk sums
+  DrawRec* rec;  // [R] draw records
+  double* sub;   // [R * NSUB * 2] sub-chunk sums {draw weight, p}
+  int NSUB;      // sub-chunks per row
   int S;         // chunks per row
-  int CG;        // 8-value groups per chunk
   uint32_t* status;
 };
 
@@ -112,70 +112,10 @@ __device__ __forceinline__ bool request_ok(const SampleArgs& a, int r, int& pb, 
   return Lr >= 0 && Lr <= a.b && a.tgt_off[r + 1] - tb == Lr + 1;
 }
 
-// ------------------------------------------------------------------ posterior (one wave)
-// Lane z < K: f_z = the first position where branch z disagrees with the draft
-// (L_r if none).  Branch z is consistent with x_<i iff f_z >= i, and then
-// matches x_i iff f_z > i, so
-//   w_z^(i) = q(z|y) [f_z >= i] / sum_z' q(z'|y) [f_z' >= i],
-//   q(x_i | x_<i) = sum_z w_z^(i) [f_z > i].
-// The request's branch tokens and draft tokens, staged in LDS by the whole block
-// (one load per thread) so that the recursion below reads no global memory.
-struct ReqTables {
-  int g[64 * 64];  // [z][i], z < K, i < L_r
-  int x[64];
-};
-
-__device__ __forceinline__ void stage_tables(const SampleArgs& a, int r, int Lr, ReqTables& t) {
-  for (int k = threadIdx.x; k < a.K * Lr; k += blockDim.x) {
-    const int z = k / Lr, i = k % Lr;
-    t.g[z * 64 + i] = a.branch_tok[(static_cast<size_t>(r) * a.K + z) * a.b + i];
-  }
-  for (int k = threadIdx.x; k < Lr; k += blockDim.x) t.x[k] = a.x[static_cast<size_t>(r) * a.b + k];
-}
-
-__device__ __forceinline__ void branch_agreement(const SampleArgs& a, int r, int Lr, const ReqTables& t, double& pi,
-                                                 int& f) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const bool act = lane < a.K;
-  const float ml = act ? a.mix[static_cast<size_t>(r) * a.K + lane] : -INFINITY;
-  f = Lr;
-  if (act)
-    for (int i = Lr - 1; i >= 0; --i)
-      if (t.g[lane * 64 + i] != t.x[i]) f = i;
-  float mmax = ml;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, o, kWave));
-  const double e = act ? exp(static_cast<double>(ml) - static_cast<double>(mmax)) : 0.0;
-  pi = e / wave_sum_f64(e);  // q(z | y)
-}
-
-// Fills qx[i] for i < L_r; with write_out also post_w, q_at_draft and the status.
-__device__ __forceinline__ void posterior_wave(const SampleArgs& a, int r, int Lr, const ReqTables& t, bool write_out,
-                                               double* qx, double& pi, int& f) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const bool act = lane < a.K;
-  branch_agreement(a, r, Lr, t, pi, f);
-  for (int i = 0; i < Lr; ++i) {
-    const double w = act && f >= i ? pi : 0.0;
-    const double sw = wave_sum_f64(w);
-    const double post = sw > 0.0 ? w / sw : 0.0;
-    const double q = wave_sum_f64(f > i ? post : 0.0);
-    if (lane == 0) {
-      qx[i] = q;
-      if (write_out) {
-        a.q_at_draft[static_cast<size_t>(r) * a.b + i] = q;
-        if (!(sw > 0.0)) raise_status(a.status, SV_ST_EMPTY_POSTERIOR);
-      }
-    }
-    if (write_out && act) a.post_w[(static_cast<size_t>(r) * a.b + i) * a.K + lane] = post;
-  }
-}
-
-// ------------------------------------------------------------------ acceptance (one wave)
-// Lane i < L_r tests position i + 1 (1-based).  q comes from qx (mixture) or
-// from the dense draft row.  Returns n_acc on every lane.
-__device__ __forceinline__ int accept_wave(const SampleArgs& a, int r, int pb, int Lr, int tb, const double* qx,
-                                           bool report) {
+// ------------------------------------------------------------------ standalone acceptance (one wave)
+// Lane i < L_r tests position i + 1 (1-based).  q comes from the given
+// q_at_draft (mixture) or from the dense draft row.  Returns n_acc on every lane.
+__device__ __forceinline__ int accept_wave(const SampleArgs& a, int r, int pb, int Lr, int tb, const double* qx) {
   const int i = threadIdx.x & (kWave - 1);
   const uint64_t seed = *a.seed;
   const float T = a.T[r];
@@ -184,7 +124,7 @@ __device__ __forceinline__ int accept_wave(const SampleArgs& a, int r, int pb, i
   if (i < Lr) {
     const int xv = a.x[static_cast<size_t>(r) * a.b + i];
     const bool tok_ok = xv >= 0 && xv < a.V;
-    if (report && !tok_ok) raise_status(a.status, SV_ST_BAD_TOKEN);
+    if (!tok_ok) raise_status(a.status, SV_ST_BAD_TOKEN);
     const int trow = tb + i;
     double p = 0.0, q = 0.0;
     if (tok_ok) {
@@ -210,12 +150,10 @@ __device__ __forceinline__ int accept_wave(const SampleArgs& a, int r, int pb, i
     const double u = u24(philox_at(seed, static_cast<uint32_t>(i), static_cast<uint32_t>(r)).x);
     const bool accept = q > 0.0 ? (u < p / q) : (p > 0.0);
     reject = !accept;
-    if (report) {
-      const size_t k = static_cast<size_t>(r) * a.b + i;
-      if (a.p_out) a.p_out[k] = p;
-      if (a.q_out) a.q_out[k] = q;
-      if (a.u_out) a.u_out[k] = static_cast<float>(u);
-    }
+    const size_t k = static_cast<size_t>(r) * a.b + i;
+    if (a.p_out) a.p_out[k] = p;
+    if (a.q_out) a.q_out[k] = q;
+    if (a.u_out) a.u_out[k] = static_cast<float>(u);
   }
   const uint64_t mask = __ballot(reject);
   return mask ? (__ffsll(static_cast<long long>(mask)) - 1) : Lr;
@@ -232,375 +170,526 @@ __global__ __launch_bounds__(kWave) void k_accept(SampleArgs a) {
     return;
   }
   const double* qx = a.q_mode == SV_Q_MIXTURE ? a.qx + static_cast<size_t>(r) * a.b : nullptr;
-  const int n = accept_wave(a, r, pb, Lr, tb, qx, true);
+  const int n = accept_wave(a, r, pb, Lr, tb, qx);
   if (threadIdx.x == 0) a.n_acc[r] = n;
 }
 
 // ------------------------------------------------------------------ the draw
-// What one request's draw needs.
+// What the chunk blocks of one request share (built by wave 0).
 struct DrawCtx {
-  int j, trow;
-  bool bonus;
-  double invT, kept, dlse;
+  int mode, n, bonus, token, ncorr;
   float cut;
-  const char* trowp;
-  const char* drowp;
-  int nq;  // mixture: branch entries at slot j with their posterior mass
-  int qtok[64];
-  double qw[64];
+  double invT, kept, dlse;
+  int64_t trow, drow;
+  int ctok[64];
+  double cp[64];  // p at ctok
+  double cw[64];  // draw weight at ctok
 };
 
-// Scalars of the draw context of request r at slot j (thread 0 of the block).
-template <bool kDense>
-__device__ __forceinline__ void draw_scalars(const SampleArgs& a, int r, int pb, int Lr, int tb, int j, DrawCtx& c) {
-  c.j = j;
-  c.bonus = j == Lr;
-  c.trow = tb + j;
-  c.invT = 1.0 / static_cast<double>(a.T[r]);
-  c.cut = a.row_cut[tb + j];
-  c.kept = a.row_kept[tb + j];
-  c.trowp = row_ptr(a.tgt, a.dtype, tb + j, a.tgt_ld);
-  c.drowp = nullptr;
-  c.dlse = 0.0;
-  c.nq = 0;
-  if (kDense && j < Lr) {
-    c.drowp = row_ptr(a.draft, a.ddtype, static_cast<int64_t>(r) * a.b + j, a.draft_ld);
-    c.dlse = a.dlse[pb + j];
-  }
-  if (!kDense && j < Lr) c.nq = a.K;
-}
+struct TailShared {
+  // A. request header and tables
+  int pb, pe, tb, te, nin;
+  float T;
+  uint64_t seed;
+  int x[64];
+  float mix[64];
+  // B. statistics of the candidate rows tb + i (i <= L_r) and values at the draft tokens
+  float rc[65];
+  double rk[65];
+  int ra[65];
+  float lx[64], dx[64];
+  double dl[64];
+  int da[64];
+  // C. posterior and draw context
+  double pi[64], A[64];
+  int f[64];
+  int tv[64];
+  double tw[64];
+  DrawCtx c;
+  // D. per-wave staging of the values at or above the cut
+  float st[kSumNT / kWave][kSubG * 8];
+  float sd[kSumNT / kWave][kSubG * 8];
+};
 
-// q(v | x_<j) of the mixture at token v: the posterior mass of the branches at v
-__device__ __forceinline__ double mix_q(const DrawCtx& c, int v) {
+// Mixture residual at the draw slot (wave 0): lane z < K holds branch z (whether
+// it is consistent with the accepted prefix, its token v, its posterior weight
+// w and the target logit at v).  q(v) is the summed weight of the branches with
+// token v; the draw weight at v is max(0, p(v) - q(v)); every other token keeps
+// p.  The distinct tokens go to c.ctok in lane order.
+__device__ __forceinline__ void build_corrections(TailShared& sh, int K, bool act, int v, double w, float lv) {
+  const int lane = threadIdx.x & (kWave - 1);
+  sh.tv[lane] = act ? v : -1;
+  sh.tw[lane] = act ? w : 0.0;
+  __syncwarp();
+  bool first = act;
   double q = 0.0;
-  for (int t = 0; t < c.nq; ++t)
-    if (c.qtok[t] == v) q += c.qw[t];
-  return q;
+  for (int z = 0; z < K; ++z) {
+    const int vz = sh.tv[z];
+    if (act && vz == v) {
+      q += sh.tw[z];
+      if (z < lane) first = false;
+    }
+  }
+  const uint64_t fm = __ballot(first);
+  if (first) {
+    const int idx = __popcll(fm & ((1ull << lane) - 1ull));
+    const double p = p_of(lv, sh.c.cut, sh.c.invT, sh.c.kept);
+    const double d = p - q;
+    sh.c.ctok[idx] = v;
+    sh.c.cp[idx] = p;
+    sh.c.cw[idx] = d > 0.0 ? d : 0.0;
+  }
+  if (lane == 0) sh.c.ncorr = __popcll(fm);
 }
 
-// p and the draw weight of the 8 values of group g, in vocabulary order
-template <bool kDense>
-__device__ __forceinline__ void weights8(const SampleArgs& a, const DrawCtx& c, int g, bool use_p, double p8[8],
-                                         double w8[8]) {
-  float l[8];
-  load8(c.trowp, a.dtype, g, a.V, l);
-#pragma unroll
-  for (int k = 0; k < 8; ++k) p8[k] = p_of(l[k], c.cut, c.invT, c.kept);
-  if (use_p || c.bonus) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) w8[k] = p8[k];
-    return;
+// The first chunk block's copy of the context for the pick kernel (wave 0).
+__device__ __forceinline__ void write_record(const SampleArgs& a, int r, const DrawCtx& c) {
+  const int lane = threadIdx.x & (kWave - 1);
+  DrawRec& d = a.rec[r];
+  if (lane == 0) {
+    d.mode = c.mode; d.n = c.n; d.bonus = c.bonus; d.token = c.token; d.ncorr = c.ncorr;
+    d.trow = c.trow; d.drow = c.drow; d.cut = c.cut; d.invT = c.invT; d.kept = c.kept; d.dlse = c.dlse;
   }
-  if constexpr (kDense) {
-    float d[8];
-    load8(c.drowp, a.ddtype, g, a.V, d);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const double q = exp(static_cast<double>(d[k]) * c.invT - c.dlse);
-      const double t = p8[k] - q;
-      w8[k] = t > 0.0 ? t : 0.0;
-    }
-  } else {
-    const int v0 = g * 8;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) w8[k] = p8[k];
-    for (int t = 0; t < c.nq; ++t) {
-      const int dv = c.qtok[t] - v0;
-      if (dv >= 0 && dv < 8) {
-        const double q = mix_q(c, c.qtok[t]);
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-          if (k == dv) {
-            const double d = p8[k] - q;
-            w8[k] = d > 0.0 ? d : 0.0;
-          }
-      }
-    }
+  if (lane < c.ncorr) {
+    d.ctok[lane] = c.ctok[lane];
+    d.cw[lane] = c.cw[lane];
   }
 }
 
-struct SumShared {
-  double red[kSumNT / kWave];
-  float st[kSumNT / kWave][512];  // per-wave staging of the values at or above the cut
-  float sd[kSumNT / kWave][512];  // the matching draft values (dense residual)
-};
-
-// Chunk ch of the draw row: sum of p and of the draw weight, in double, to part.
-// Each thread prefetches its (up to) 4 groups of a 1024-group super-tile before
-// any arithmetic.  The mixture's sparse corrections (branch tokens) are added
-// by thread 0.
+// D. Sums of p and of the draw weight over the sub-chunks of chunk ch of the
+// drawn row; wave wv takes sub-chunks ch*16 + k*4 + wv, k < 4, one 8-value
+// group per lane, all loaded before any arithmetic.
 template <bool kDense>
-__device__ void chunk_sums(const SampleArgs& a, const DrawCtx& c, int r, int ch, SumShared& sh) {
-  constexpr int TILES = 4;
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1), wv = tid / kWave;
-  const int NG = (a.V + 7) / 8;
-  const int g0 = ch * a.CG;
-  const int g1 = min(NG, g0 + a.CG);
-  const bool dense_res = kDense && !c.bonus;
+__device__ __forceinline__ void sub_sums(const SampleArgs& a, const DrawCtx& c, int r, int ch, float* st, float* sd) {
+  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+  const int NG = groups_of(a.V);
+  const bool dense_res = kDense && c.mode == kDrawResidual;
+  const bool mix_res = !kDense && c.mode == kDrawResidual;
   const bool cut_on = c.cut > -INFINITY;
-  double sp = 0.0, sw = 0.0;
-  for (int sb = g0; sb < g1; sb += TILES * kSumNT) {
-    float l[TILES][8], d[TILES][8];
+  const char* trowp = row_ptr(a.tgt, a.dtype, c.trow, a.tgt_ld);
+  const char* drowp = dense_res ? row_ptr(a.draft, a.ddtype, c.drow, a.draft_ld) : nullptr;
+  const int sub0 = ch * kChunkSubs + wv;
+  float l[kSubPerWave][8], d[kSubPerWave][8];
 #pragma unroll
-    for (int k = 0; k < TILES; ++k) {
-      const int g = sb + k * kSumNT + tid;
-      if (g < g1) {
-        load8(c.trowp, a.dtype, g, a.V, l[k]);
-        if (dense_res) load8(c.drowp, a.ddtype, g, a.V, d[k]);
-      } else {
+  for (int k = 0; k < kSubPerWave; ++k) {
+    const int g = (sub0 + k * (kSumNT / kWave)) * kSubG + lane;
+    if (g < NG) {
+      load8(trowp, a.dtype, g, a.V, l[k]);
+      if (dense_res) load8(drowp, a.ddtype, g, a.V, d[k]);
+    } else {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) l[k][q] = -INFINITY;
-      }
+      for (int q = 0; q < 8; ++q) l[k][q] = -INFINITY;
     }
+  }
+#pragma unroll
+  for (int k = 0; k < kSubPerWave; ++k) {
+    const int sub = sub0 + k * (kSumNT / kWave);
+    if (sub >= a.NSUB) break;  // wave-uniform
+    double sp = 0.0, sw = 0.0;
     if (!cut_on) {
 #pragma unroll
-      for (int k = 0; k < TILES; ++k) {
-        if (sb + k * kSumNT + tid >= g1) continue;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const double p = exp(static_cast<double>(l[k][q]) * c.invT - c.kept);
-          sp += p;
-          if (dense_res) {
-            const double t = p - exp(static_cast<double>(d[k][q]) * c.invT - c.dlse);
-            sw += t > 0.0 ? t : 0.0;
-          } else {
-            sw += p;
-          }
+      for (int q = 0; q < 8; ++q) {
+        const double p = exp(static_cast<double>(l[k][q]) * c.invT - c.kept);
+        sp += p;
+        if (dense_res) {
+          const double t = p - exp(static_cast<double>(d[k][q]) * c.invT - c.dlse);
+          sw += t > 0.0 ? t : 0.0;
         }
       }
     } else {
-      // top-p: only values at or above the cut carry weight; compact them per wave
+      // only values at or above the cut carry weight: compact them first
+      uint32_t m = 0;
 #pragma unroll
-      for (int k = 0; k < TILES; ++k) {
-        uint32_t m = 0;
+      for (int q = 0; q < 8; ++q) m |= (l[k][q] >= c.cut ? 1u : 0u) << q;
+      const int cnt = __popc(m);
+      const int inc = wave_incl_scan_i32(cnt);
+      const int tot = __shfl(inc, kWave - 1, kWave);
+      int o = inc - cnt;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) m |= (l[k][q] >= c.cut ? 1u : 0u) << q;
-        const int cnt = __popc(m);
-        const int inc = wave_incl_scan_i32(cnt);
-        const int tot = __shfl(inc, kWave - 1, kWave);
-        int o = inc - cnt;
+      for (int q = 0; q < 8; ++q)
+        if (m & (1u << q)) {
+          st[o] = l[k][q];
+          if (dense_res) sd[o] = d[k][q];
+          ++o;
+        }
+      __syncwarp();
+      for (int e = lane; e < tot; e += kWave) {
+        const double p = exp(static_cast<double>(st[e]) * c.invT - c.kept);
+        sp += p;
+        if (dense_res) {
+          const double t = p - exp(static_cast<double>(sd[e]) * c.invT - c.dlse);
+          sw += t > 0.0 ? t : 0.0;
+        }
+      }
+      __syncwarp();  // the staging area is rewritten by the next sub-chunk
+    }
+    sp = wave_sum_f64(sp);
+    if (dense_res) sw = wave_sum_f64(sw);
+    if (lane == 0) {
+      if (!dense_res) sw = sp;
+      if (mix_res) {  // branch tokens: weight max(0, p - q) instead of p
+        const int v0 = sub * kSubG * 8;
+        for (int t = 0; t < c.ncorr; ++t) {
+          const int v = c.ctok[t];
+          if (v >= v0 && v < v0 + kSubG * 8) sw += c.cw[t] - c.cp[t];
+        }
+      }
+      double* pp = a.sub + (static_cast<size_t>(r) * a.NSUB + sub) * 2;
+      pp[0] = sw;
+      pp[1] = sp;
+    }
+  }
+}
+
+// The fused tail (kAccept: posterior, acceptance and the draw's sums) or the
+// standalone draw's sums (n from n_acc_in, posterior weights from post_w).
+template <bool kDense, bool kAccept>
+__global__ __launch_bounds__(kSumNT) void k_draw_sums(SampleArgs a) {
+  __shared__ TailShared sh;
+  extern __shared__ int dyn[];  // mixture: branch tokens [K][b], then target logits at them [K][b]
+  int* g = dyn;
+  float* gl = reinterpret_cast<float*>(dyn + a.K * a.b);
+  const int r = blockIdx.x / a.S, ch = blockIdx.x % a.S;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const bool report = ch == 0;
+  const int K = kDense ? 0 : a.K, b = a.b;
+  DrawCtx& c = sh.c;
+
+  // A. independent loads
+  if (tid == 0) {
+    sh.pb = a.pos_off[r];
+    sh.pe = a.pos_off[r + 1];
+    sh.tb = a.tgt_off[r];
+    sh.te = a.tgt_off[r + 1];
+    sh.T = a.T[r];
+    sh.seed = *a.seed;
+    sh.nin = kAccept ? 0 : a.n_acc_in[r];
+  }
+  if (kAccept) {
+    for (int i = tid; i < b; i += kSumNT) sh.x[i] = a.x[static_cast<size_t>(r) * b + i];
+    if (!kDense) {
+      for (int z = tid; z < K; z += kSumNT) sh.mix[z] = a.mix[static_cast<size_t>(r) * K + z];
+      for (int k = tid; k < K * b; k += kSumNT) g[k] = a.branch_tok[static_cast<size_t>(r) * K * b + k];
+    }
+  }
+  __syncthreads();
+  const int pb = sh.pb, tb = sh.tb, Lr = sh.pe - sh.pb;
+  if (!(Lr >= 0 && Lr <= b && sh.te - tb == Lr + 1)) {
+    if (report && tid == 0) {
+      raise_status(a.status, SV_ST_BAD_OFFSETS);
+      if (kAccept) a.n_acc[r] = 0;
+      a.rec[r].mode = kDrawNone;
+    }
+    return;
+  }
+  const bool greedy = sh.T == 0.0f;
+  const double invT = 1.0 / static_cast<double>(sh.T);
+
+  if (kAccept) {
+    // B. row statistics of the candidate rows, values at the draft and branch tokens
+    for (int i = tid; i <= Lr; i += kSumNT) {
+      sh.rc[i] = a.row_cut[tb + i];
+      sh.rk[i] = a.row_kept[tb + i];
+      sh.ra[i] = a.row_argmax[tb + i];
+    }
+    for (int i = tid; i < Lr; i += kSumNT) {
+      const int xv = sh.x[i];
+      const bool ok = xv >= 0 && xv < a.V;
+      sh.lx[i] = ok ? load_val_rt(row_ptr(a.tgt, a.dtype, tb + i, a.tgt_ld), a.dtype, xv) : -INFINITY;
+      if (kDense) {
+        sh.dx[i] = ok ? load_val_rt(row_ptr(a.draft, a.ddtype, static_cast<int64_t>(r) * b + i, a.draft_ld),
+                                    a.ddtype, xv)
+                      : -INFINITY;
+        sh.dl[i] = a.dlse[pb + i];
+        sh.da[i] = a.dargmax[pb + i];
+      }
+    }
+    if (!kDense)
+      for (int k = tid; k < K * Lr; k += kSumNT) {
+        const int z = k / Lr, i = k - z * Lr;
+        const int v = g[z * b + i];
+        gl[z * b + i] = v >= 0 && v < a.V ? load_val_rt(row_ptr(a.tgt, a.dtype, tb + i, a.tgt_ld), a.dtype, v)
+                                          : -INFINITY;
+      }
+    __syncthreads();
+
+    // C. posterior, acceptance, draw context (wave 0)
+    if (tid < kWave) {
+      double q = 0.0;
+      if (!kDense) {
+        // Lane z < K: pi_z = q(z | y) and f_z = the first position where branch z
+        // leaves the draft (L_r if none).  With A(i) = sum_z pi_z [f_z >= i]:
+        // w_z^(i) = pi_z [f_z >= i] / A(i) and q(x_i | x_<i) = A(i + 1) / A(i).
+        const bool act = lane < K;
+        const float ml = act ? sh.mix[lane] : -INFINITY;
+        float mmax = ml;
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
-          if (m & (1u << q)) {
-            sh.st[wv][o] = l[k][q];
-            if (dense_res) sh.sd[wv][o] = d[k][q];
-            ++o;
-          }
-        __syncthreads();
-        for (int e = lane; e < tot; e += kWave) {
-          const double p = exp(static_cast<double>(sh.st[wv][e]) * c.invT - c.kept);
-          sp += p;
-          if (dense_res) {
-            const double t = p - exp(static_cast<double>(sh.sd[wv][e]) * c.invT - c.dlse);
-            sw += t > 0.0 ? t : 0.0;
-          } else {
-            sw += p;
+        for (int o = 32; o > 0; o >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, o, kWave));
+        const double e = act ? exp(static_cast<double>(ml) - static_cast<double>(mmax)) : 0.0;
+        const double pi = e / wave_sum_f64(e);
+        int f = Lr;
+        if (act)
+          for (int i = Lr - 1; i >= 0; --i)
+            if (g[lane * b + i] != sh.x[i]) f = i;
+        sh.pi[lane] = pi;
+        sh.f[lane] = act ? f : -1;
+        __syncwarp();
+        double Ai = 0.0, Ai1 = 0.0;
+        for (int z = 0; z < K; ++z) {
+          const double pz = sh.pi[z];
+          const int fz = sh.f[z];
+          Ai += fz >= lane ? pz : 0.0;
+          Ai1 += fz > lane ? pz : 0.0;
+        }
+        sh.A[lane] = Ai;
+        if (lane < Lr) {
+          q = Ai > 0.0 ? Ai1 / Ai : 0.0;
+          if (report) {
+            a.q_at_draft[static_cast<size_t>(r) * b + lane] = q;
+            if (!(Ai > 0.0)) raise_status(a.status, SV_ST_EMPTY_POSTERIOR);
+            double* pw = a.post_w + (static_cast<size_t>(r) * b + lane) * K;
+            for (int z = 0; z < K; ++z) pw[z] = Ai > 0.0 && sh.f[z] >= lane ? sh.pi[z] / Ai : 0.0;
           }
         }
-        __syncthreads();
       }
-    }
-  }
-  sp = block_sum_f64<kSumNT>(sp, sh.red);
-  sw = block_sum_f64<kSumNT>(sw, sh.red);
-  if (tid == 0) {
-    if (!kDense && !c.bonus) {  // branch tokens: weight max(0, p - q) instead of p
-      const int v0 = g0 * 8, v1 = min(a.V, g1 * 8);
-      for (int t = 0; t < c.nq; ++t) {
-        const int v = c.qtok[t];
-        bool first = true;
-        for (int t2 = 0; t2 < t; ++t2)
-          if (c.qtok[t2] == v) first = false;
-        if (!first || v < v0 || v >= v1) continue;
-        const double p = p_of(load_val_rt(c.trowp, a.dtype, v), c.cut, c.invT, c.kept);
-        const double dq = p - mix_q(c, v);
-        sw += (dq > 0.0 ? dq : 0.0) - p;
+      bool reject = false;
+      if (lane < Lr) {
+        const int xv = sh.x[lane];
+        const bool ok = xv >= 0 && xv < a.V;
+        if (report && !ok) raise_status(a.status, SV_ST_BAD_TOKEN);
+        double p = 0.0;
+        if (ok) {
+          p = greedy ? (xv == sh.ra[lane] ? 1.0 : 0.0) : p_of(sh.lx[lane], sh.rc[lane], invT, sh.rk[lane]);
+          if (kDense)
+            q = greedy ? (xv == sh.da[lane] ? 1.0 : 0.0)
+                       : exp(static_cast<double>(sh.dx[lane]) * invT - sh.dl[lane]);
+        } else {
+          q = 0.0;
+        }
+        const double u = u24(philox_at(sh.seed, static_cast<uint32_t>(lane), static_cast<uint32_t>(r)).x);
+        reject = !(q > 0.0 ? u < p / q : p > 0.0);
+        if (report) {
+          const size_t k = static_cast<size_t>(r) * b + lane;
+          if (a.p_out) a.p_out[k] = p;
+          if (a.q_out) a.q_out[k] = q;
+          if (a.u_out) a.u_out[k] = static_cast<float>(u);
+        }
       }
+      const uint64_t mask = __ballot(reject);
+      const int n = mask ? __ffsll(static_cast<long long>(mask)) - 1 : Lr;
+      if (report && lane == 0) a.n_acc[r] = n;
+      if (lane == 0) {
+        c.n = n;
+        c.bonus = n == Lr ? 1 : 0;
+        c.mode = greedy ? kDrawGreedy : (n == Lr ? kDrawP : kDrawResidual);
+        c.token = sh.ra[n];
+        c.cut = sh.rc[n];
+        c.kept = sh.rk[n];
+        c.invT = invT;
+        c.dlse = kDense && n < Lr ? sh.dl[n] : 0.0;
+        c.trow = tb + n;
+        c.drow = static_cast<int64_t>(r) * b + n;
+        c.ncorr = 0;
+      }
+      __syncwarp();
+      if (!kDense && !greedy && n < Lr) {
+        const bool act = lane < K && sh.f[lane] >= n;
+        build_corrections(sh, K, act, act ? g[lane * b + n] : -1, act ? sh.pi[lane] / sh.A[n] : 0.0,
+                          act ? gl[lane * b + n] : -INFINITY);
+      }
+      __syncwarp();
+      if (report) write_record(a, r, c);
     }
-    double* pp = a.part + (static_cast<size_t>(r) * a.S + ch) * 2;
-    pp[0] = sw;
-    pp[1] = sp;
-  }
-}
-
-struct TailShared {
-  DrawCtx c;
-  SumShared s;
-  ReqTables t;
-  double qx[64];
-  int n;
-};
-
-// Standalone chunk sums (sv_residual_sample): n_acc is an input.
-template <bool kDense>
-__global__ __launch_bounds__(kSumNT) void k_res_sums(SampleArgs a) {
-  __shared__ TailShared sh;
-  const int r = blockIdx.x / a.S, ch = blockIdx.x % a.S;
-  const int tid = threadIdx.x;
-  int pb, Lr, tb;
-  if (!request_ok(a, r, pb, Lr, tb)) return;
-  if (a.T[r] == 0.0f) return;  // the draw is the argmax
-  int n = a.n_acc_in[r];
-  n = n < 0 ? 0 : (n > Lr ? Lr : n);
-  if (tid == 0) draw_scalars<kDense>(a, r, pb, Lr, tb, n, sh.c);
-  if (!kDense && n < Lr && tid < a.K) {
-    sh.c.qtok[tid] = a.branch_tok[(static_cast<size_t>(r) * a.K + tid) * a.b + n];
-    sh.c.qw[tid] = a.post_w[(static_cast<size_t>(r) * a.b + n) * a.K + tid];
-  }
-  __syncthreads();
-  chunk_sums<kDense>(a, sh.c, r, ch, sh.s);
-}
-
-// Fused tail: posterior (mixture), acceptance, then the chunk sums of the draw.
-template <bool kDense>
-__global__ __launch_bounds__(kSumNT) void k_tail_sums(SampleArgs a) {
-  __shared__ TailShared sh;
-  const int r = blockIdx.x / a.S, ch = blockIdx.x % a.S;
-  const int tid = threadIdx.x;
-  int pb, Lr, tb;
-  if (!request_ok(a, r, pb, Lr, tb)) {
-    if (ch == 0 && tid == 0) {
-      raise_status(a.status, SV_ST_BAD_OFFSETS);
-      a.n_acc[r] = 0;
+  } else {
+    // standalone draw: n given; branch tokens and posterior weights at slot n given
+    int n = sh.nin;
+    if (n < 0 || n > Lr) {
+      if (report && tid == 0) raise_status(a.status, SV_ST_BAD_NACC);
+      n = n < 0 ? 0 : Lr;
     }
-    return;
-  }
-  const bool report = ch == 0;
-  if (!kDense) {
-    stage_tables(a, r, Lr, sh.t);
-    __syncthreads();
-  }
-  if (tid < kWave) {
-    double pi = 0.0;
-    int f = 0;
-    if (!kDense) posterior_wave(a, r, Lr, sh.t, report, sh.qx, pi, f);
-    const int n = accept_wave(a, r, pb, Lr, tb, sh.qx, report);
+    const bool mres = !kDense && !greedy && n < Lr;
     if (tid == 0) {
-      sh.n = n;
-      if (report) a.n_acc[r] = n;
-      if (a.T[r] != 0.0f) draw_scalars<kDense>(a, r, pb, Lr, tb, n, sh.c);
+      c.n = n;
+      c.bonus = n == Lr ? 1 : 0;
+      c.mode = greedy ? kDrawGreedy : (n == Lr ? kDrawP : kDrawResidual);
+      c.token = a.row_argmax[tb + n];
+      c.cut = a.row_cut[tb + n];
+      c.kept = a.row_kept[tb + n];
+      c.invT = invT;
+      c.dlse = kDense && n < Lr ? a.dlse[pb + n] : 0.0;
+      c.trow = tb + n;
+      c.drow = static_cast<int64_t>(r) * b + n;
+      c.ncorr = 0;
     }
-    if (!kDense && n < Lr) {
-      // branch tokens and posterior mass at the draw slot (as posterior_wave formed them)
-      const bool act = tid < a.K;
-      const double w = act && f >= n ? pi : 0.0;
-      const double sw = wave_sum_f64(w);
-      if (act) {
-        sh.c.qw[tid] = sw > 0.0 ? w / sw : 0.0;
-        sh.c.qtok[tid] = sh.t.g[tid * 64 + n];
+    if (mres && tid < K) {
+      sh.tv[tid] = a.branch_tok[(static_cast<size_t>(r) * K + tid) * b + n];
+      sh.tw[tid] = a.post_w[(static_cast<size_t>(r) * b + n) * K + tid];
+    }
+    __syncthreads();
+    if (tid < kWave) {
+      if (mres) {
+        const bool in = lane < K;
+        const int v = in ? sh.tv[lane] : -1;
+        const double w = in ? sh.tw[lane] : 0.0;
+        const bool act = in && w > 0.0 && v >= 0 && v < a.V;
+        const float lv = act ? load_val_rt(row_ptr(a.tgt, a.dtype, tb + n, a.tgt_ld), a.dtype, v) : -INFINITY;
+        __syncwarp();
+        build_corrections(sh, K, act, v, w, lv);
       }
+      __syncwarp();
+      if (report) write_record(a, r, c);
     }
   }
   __syncthreads();
-  if (a.T[r] == 0.0f) return;  // the draw is the argmax (taken by the pick kernel)
-  chunk_sums<kDense>(a, sh.c, r, ch, sh.s);
+  if (c.mode == kDrawGreedy) return;  // the draw is the argmax (taken by the pick kernel)
+  const int wv = tid / kWave;
+  sub_sums<kDense>(a, c, r, ch, sh.st[wv], sh.sd[wv]);
 }
 
-// The draw: one 256-thread block per request, after the chunk sums.
+// The draw: one block per request, after the sums.
 template <bool kDense>
-__global__ __launch_bounds__(kSumNT) void k_res_pick(SampleArgs a) {
-  __shared__ DrawCtx c;
+__global__ __launch_bounds__(kSumNT) void k_pick(SampleArgs a) {
   __shared__ double red[kSumNT / kWave];
   __shared__ int redi[kSumNT / kWave];
-  __shared__ int s_cstar, s_use_p;
-  __shared__ double s_base, s_t;
-  const int tid = threadIdx.x;
-  const int r = blockIdx.x;
-  int pb, Lr, tb;
-  if (!request_ok(a, r, pb, Lr, tb)) {
-    if (tid == 0) raise_status(a.status, SV_ST_BAD_OFFSETS);
-    return;
+  __shared__ int s_sub;
+  __shared__ double s_base;
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1);
+  const DrawRec& rec = a.rec[r];
+  const int mode = rec.mode, n = rec.n, bonus = rec.bonus;
+  const uint64_t seed = *a.seed;
+  // this thread's sub-chunks, and the branch corrections (wave 0), loaded at once
+  const int NSUB = a.NSUB;
+  const int spt = (NSUB + kSumNT - 1) / kSumNT;
+  const int s0 = min(NSUB, tid * spt), s1 = min(NSUB, s0 + spt);
+  const double* subp = a.sub + static_cast<size_t>(r) * NSUB * 2;
+  double lw = 0.0, lp = 0.0;
+  for (int s = s0; s < s1; ++s) {
+    lw += subp[2 * s];
+    lp += subp[2 * s + 1];
   }
-  int n = a.n_acc_in[r];
-  if (n < 0 || n > Lr) {
-    if (tid == 0) raise_status(a.status, SV_ST_BAD_NACC);
-    n = n < 0 ? 0 : Lr;
+  int ctok = -1;
+  double cw = 0.0;
+  if (!kDense && tid < kWave) {
+    ctok = rec.ctok[lane];
+    cw = rec.cw[lane];
   }
-  if (a.T[r] == 0.0f) {  // p is one-hot at the argmax, and so is the residual
+  if (mode == kDrawNone) return;  // malformed offsets (reported by the sums kernel)
+  if (mode == kDrawGreedy) {      // p is one-hot at the argmax, and so is the residual
     if (tid == 0) {
-      a.token[r] = a.row_argmax[tb + n];
-      a.is_bonus[r] = n == Lr ? 1 : 0;
+      a.token[r] = rec.token;
+      a.is_bonus[r] = bonus;
     }
     return;
   }
-  if (tid == 0) draw_scalars<kDense>(a, r, pb, Lr, tb, n, c);
-  if (!kDense && n < Lr && tid < a.K) {
-    c.qtok[tid] = a.branch_tok[(static_cast<size_t>(r) * a.K + tid) * a.b + n];
-    c.qw[tid] = a.post_w[(static_cast<size_t>(r) * a.b + n) * a.K + tid];
+  bool use_p = mode == kDrawP;
+  double W;
+  double excl = block_excl_scan_f64<kSumNT>(use_p ? lp : lw, red, &W);
+  if (!use_p && !(W > 0.0)) {  // an all-zero residual (rounding) falls back to p
+    use_p = true;
+    excl = block_excl_scan_f64<kSumNT>(lp, red, &W);
   }
-  if (tid < kWave) {  // wave 0: the chunk holding u * W, from the chunk sums (one per lane)
-    const int lane = tid;
-    const double u = u24(philox_at(*a.seed, static_cast<uint32_t>(n), static_cast<uint32_t>(r)).y);
-    const double* pp = a.part + static_cast<size_t>(r) * a.S * 2;
-    const double cw = lane < a.S ? pp[lane * 2] : 0.0;
-    const bool use_p = n == Lr || !(wave_sum_f64(cw) > 0.0);  // an all-zero residual (rounding) falls back to p
-    const double wc = lane < a.S ? pp[lane * 2 + (use_p ? 1 : 0)] : 0.0;
-    const double incl = wave_incl_scan_f64(wc);
-    const double W = __shfl(incl, kWave - 1, kWave);
-    const double t = u * W;
-    const uint64_t over = __ballot(lane < a.S && incl > t);
-    const int cstar = over ? __ffsll(static_cast<long long>(over)) - 1 : a.S - 1;
-    const double base = __shfl(incl - wc, cstar, kWave);  // weight before chunk cstar
-    if (lane == 0) {
-      s_cstar = cstar;
-      s_use_p = use_p ? 1 : 0;
-      s_base = base;
-      s_t = t;
+  const double t = u24(philox_at(seed, static_cast<uint32_t>(n), static_cast<uint32_t>(r)).y) * W;
+  // the first sub-chunk whose running weight exceeds t
+  int found = 0x7FFFFFFF, last = -1;
+  double fbase = 0.0, lbase = 0.0, run = excl;
+  for (int s = s0; s < s1; ++s) {
+    const double ws = subp[2 * s + (use_p ? 1 : 0)];
+    if (ws > 0.0) {
+      last = s;
+      lbase = run;
+    }
+    if (run + ws > t) {
+      found = s;
+      fbase = run;
+      break;
+    }
+    run += ws;
+  }
+  const int fmin = block_min_i32<kSumNT>(found, redi);
+  if (fmin != 0x7FFFFFFF) {
+    if (found == fmin) {
+      s_sub = fmin;
+      s_base = fbase;
+    }
+  } else {  // rounding: the last sub-chunk with positive weight
+    const int lmax = -block_min_i32<kSumNT>(-last, redi);
+    if (lmax >= 0 && last == lmax) {
+      s_sub = lmax;
+      s_base = lbase;
+    } else if (lmax < 0 && tid == 0) {
+      s_sub = 0;
+      s_base = 0.0;
     }
   }
   __syncthreads();
-  const bool use_p = s_use_p != 0;
-  const double t = s_t;
-  // walk chunk cstar: thread tid takes GPT consecutive groups (loaded at once),
-  // an exclusive block scan of the per-thread sums finds the thread holding t
-  constexpr int GPT = 4;
-  const int NG = (a.V + 7) / 8;
-  const int h0 = s_cstar * a.CG;
-  const int h1 = min(NG, h0 + a.CG);
-  double run = s_base;
-  int found = 0x7FFFFFFF, lastpos = -1;
-  for (int sb = h0; sb < h1; sb += GPT * kSumNT) {
-    const int gs = sb + tid * GPT;
-    double w[GPT][8];
-    double loc = 0.0;
-#pragma unroll
-    for (int k = 0; k < GPT; ++k) {
-      double p8[8];
-      if (gs + k < h1) {
-        weights8<kDense>(a, c, gs + k, use_p, p8, w[k]);
-      } else {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) w[k][q] = 0.0;
-      }
-#pragma unroll
-      for (int q = 0; q < 8; ++q) loc += w[k][q];
+  if (tid >= kWave) return;
+  // wave 0 walks the sub-chunk: lane = 8-value group
+  const int sub = s_sub;
+  const double base = s_base;
+  const int g = sub * kSubG + lane;
+  const bool in = g < groups_of(a.V);
+  const bool dense_res = kDense && !use_p;
+  double w8[8];
+  {
+    float l[8], d[8];
+    if (in) {
+      load8(row_ptr(a.tgt, a.dtype, rec.trow, a.tgt_ld), a.dtype, g, a.V, l);
+      if (dense_res) load8(row_ptr(a.draft, a.ddtype, rec.drow, a.draft_ld), a.ddtype, g, a.V, d);
     }
-    double tile;
-    const double excl = block_excl_scan_f64<kSumNT>(loc, red, &tile);
-    double acc = run + excl;
+    const float cut = rec.cut;
+    const double invT = rec.invT, kept = rec.kept, dlse = rec.dlse;
 #pragma unroll
-    for (int k = 0; k < GPT; ++k)
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        if (w[k][q] > 0.0) lastpos = (gs + k) * 8 + q;
-        acc += w[k][q];
-        if (acc > t && found == 0x7FFFFFFF) found = (gs + k) * 8 + q;
+    for (int q = 0; q < 8; ++q) {
+      double w = 0.0;
+      if (in && g * 8 + q < a.V) {
+        w = p_of(l[q], cut, invT, kept);
+        if (dense_res) {
+          const double t2 = w - exp(static_cast<double>(d[q]) * invT - dlse);
+          w = t2 > 0.0 ? t2 : 0.0;
+        }
       }
-    const int fmin = block_min_i32<kSumNT>(found, redi);
-    if (fmin != 0x7FFFFFFF) {
-      found = fmin;
-      break;
+      w8[q] = w;
     }
-    run += tile;
   }
-  if (found == 0x7FFFFFFF) {  // rounding: the last positive weight of the chunk
-    found = -block_min_i32<kSumNT>(-lastpos, redi);
-    if (found < 0) found = 0;
+  if (!kDense && !use_p) {
+    const int nc = rec.ncorr;
+    for (int t2 = 0; t2 < nc; ++t2) {
+      const int v = __shfl(ctok, t2, kWave);
+      const double wv = __shfl(cw, t2, kWave);
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (v == g * 8 + q) w8[q] = wv;
+    }
   }
-  if (tid == 0) {
-    a.token[r] = found;
-    a.is_bonus[r] = n == Lr ? 1 : 0;
+  double lsum = 0.0;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) lsum += w8[q];
+  const double incl = wave_incl_scan_f64(lsum);
+  const uint64_t over = __ballot(in && base + incl > t);
+  int lastpos = -1;
+#pragma unroll
+  for (int q = 0; q < 8; ++q)
+    if (w8[q] > 0.0) lastpos = g * 8 + q;
+  int tok;
+  if (over) {
+    const int L = __ffsll(static_cast<long long>(over)) - 1;
+    int pick = -1;
+    double acc = base + incl - lsum;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      acc += w8[q];
+      if (acc > t && pick < 0 && w8[q] > 0.0) pick = g * 8 + q;
+    }
+    if (pick < 0) pick = lastpos;
+    tok = __shfl(pick, L, kWave);
+    if (tok < 0) tok = -wave_min_i32(-lastpos);
+  } else {  // rounding: the last positive weight of the sub-chunk
+    tok = -wave_min_i32(-lastpos);
+  }
+  if (tok < 0) tok = sub * kSubG * 8;
+  if (lane == 0) {
+    a.token[r] = tok;
+    a.is_bonus[r] = bonus;
   }
 }
 
@@ -639,10 +728,21 @@ static SampleArgs sample_args(const void* tgt_logits, int32_t dtype, int64_t tgt
   a.q_mode = q_mode; a.draft = draft_logits; a.ddtype = draft_dtype; a.draft_ld = draft_ld;
   a.dargmax = draft_argmax; a.dlse = draft_lse; a.seed = seed; a.status = status_word(ws);
   const WsLayout l = ws_layout(R, b, 0, V);
-  a.part = reinterpret_cast<double*>(static_cast<char*>(ws) + l.res_part);
+  a.rec = reinterpret_cast<DrawRec*>(static_cast<char*>(ws) + l.rec);
+  a.sub = reinterpret_cast<double*>(static_cast<char*>(ws) + l.sub);
+  a.NSUB = sub_chunks(V);
   a.S = res_chunks(V);
-  a.CG = ((V + 7) / 8 + a.S - 1) / a.S;
   return a;
+}
+
+// sums grid, then the pick; dynamic LDS holds the mixture's branch tables
+template <bool kDense, bool kAccept>
+static int32_t launch_draw(const SampleArgs& a, hipStream_t s) {
+  const size_t dyn = kDense ? 0 : sizeof(int) * 2 * static_cast<size_t>(a.K) * a.b;
+  hipLaunchKernelGGL((k_draw_sums<kDense, kAccept>), dim3(a.R * a.S), dim3(kSumNT), dyn, s, a);
+  if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
+  hipLaunchKernelGGL(k_pick<kDense>, dim3(a.R), dim3(kSumNT), 0, s, a);
+  return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
 }
 
 extern "C" int32_t sv_accept(const void* tgt_logits, int32_t dtype, int64_t tgt_ld, int32_t V, const int32_t* tgt_off,
@@ -685,16 +785,7 @@ extern "C" int32_t sv_residual_sample(const void* tgt_logits, int32_t dtype, int
   a.K = q_mode == SV_Q_MIXTURE ? K : 0; a.branch_tok = branch_tok; a.post_w = const_cast<double*>(post_w);
   a.n_acc_in = n_acc; a.token = token; a.is_bonus = is_bonus;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (q_mode == SV_Q_DENSE) {
-    hipLaunchKernelGGL(k_res_sums<true>, dim3(R * a.S), dim3(kSumNT), 0, s, a);
-    if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
-    hipLaunchKernelGGL(k_res_pick<true>, dim3(R), dim3(kSumNT), 0, s, a);
-  } else {
-    hipLaunchKernelGGL(k_res_sums<false>, dim3(R * a.S), dim3(kSumNT), 0, s, a);
-    if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
-    hipLaunchKernelGGL(k_res_pick<false>, dim3(R), dim3(kSumNT), 0, s, a);
-  }
-  return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
+  return q_mode == SV_Q_DENSE ? launch_draw<true, false>(a, s) : launch_draw<false, false>(a, s);
 }
 
 extern "C" int32_t sv_accept_sample(const void* tgt_logits, int32_t dtype, int64_t tgt_ld, int32_t V,
@@ -721,14 +812,5 @@ extern "C" int32_t sv_accept_sample(const void* tgt_logits, int32_t dtype, int64
   a.post_w = post_w; a.q_at_draft = q_at_draft; a.n_acc = n_acc; a.n_acc_in = n_acc; a.token = token;
   a.is_bonus = is_bonus; a.p_out = p_out; a.q_out = q_out; a.u_out = u_out;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (q_mode == SV_Q_DENSE) {
-    hipLaunchKernelGGL(k_tail_sums<true>, dim3(R * a.S), dim3(kSumNT), 0, s, a);
-    if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
-    hipLaunchKernelGGL(k_res_pick<true>, dim3(R), dim3(kSumNT), 0, s, a);
-  } else {
-    hipLaunchKernelGGL(k_tail_sums<false>, dim3(R * a.S), dim3(kSumNT), 0, s, a);
-    if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
-    hipLaunchKernelGGL(k_res_pick<false>, dim3(R), dim3(kSumNT), 0, s, a);
-  }
-  return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
+  return q_mode == SV_Q_DENSE ? launch_draw<true, true>(a, s) : launch_draw<false, true>(a, s);
 }
