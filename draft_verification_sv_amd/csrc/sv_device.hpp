@@ -74,49 +74,96 @@ __device__ __forceinline__ uint4 load16_stream(const uint4* p) {
 }
 
 // ------------------------------------------------------------------ wave reductions
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const uint64_t t = __shfl_xor(v, o, kWave);
-    v = t > v ? t : v;
-  }
-  return v;
+// Cross-lane steps use DPP (quad permutes, row mirrors and row shifts inside
+// 16-lane rows) and v_readlane for the four row results, so no step takes an
+// LDS round trip.  Every caller runs them with all 64 lanes of the wave active;
+// the `lane` argument of the broadcasts is wave-uniform.
+namespace dpp {
+constexpr int kXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kHalfMirror = 0x141;  // lane i <- 7 - i within each 8 lanes
+constexpr int kMirror = 0x140;      // lane i <- 15 - i within each row
+constexpr int kShr1 = 0x111, kShr2 = 0x112, kShr4 = 0x114, kShr8 = 0x118;  // row_shr:n (0 shifted in)
+}  // namespace dpp
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(dpp_i32<CTRL>(__float_as_int(v)));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  return __hiloint2double(dpp_i32<CTRL>(__double2hiint(v)), dpp_i32<CTRL>(__double2loint(v)));
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = static_cast<uint32_t>(dpp_i32<CTRL>(static_cast<int>(static_cast<uint32_t>(v))));
+  const uint32_t hi = static_cast<uint32_t>(dpp_i32<CTRL>(static_cast<int>(static_cast<uint32_t>(v >> 32))));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+__device__ __forceinline__ int bcast_i32(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
+__device__ __forceinline__ float bcast_f32(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+__device__ __forceinline__ double bcast_f64(double v, int lane) {
+  return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), lane),
+                          __builtin_amdgcn_readlane(__double2loint(v), lane));
+}
+__device__ __forceinline__ uint64_t bcast_u64(uint64_t v, int lane) {
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)), lane));
+  const uint32_t hi =
+      static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v >> 32)), lane));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
-__device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
+// Butterfly inside each row (every lane of a row ends with the row's result:
+// each step combines the same two operands in either order), then the four
+// row results in a fixed order.  Identical in every lane.
+#define SV_WAVE_REDUCE(T, SUF, OP)                                                  \
+  v = OP(v, dpp_##SUF<dpp::kXor1>(v));                                              \
+  v = OP(v, dpp_##SUF<dpp::kXor2>(v));                                              \
+  v = OP(v, dpp_##SUF<dpp::kHalfMirror>(v));                                        \
+  v = OP(v, dpp_##SUF<dpp::kMirror>(v));                                            \
+  return OP(OP(bcast_##SUF(v, 0), bcast_##SUF(v, 16)), OP(bcast_##SUF(v, 32), bcast_##SUF(v, 48)))
 
-__device__ __forceinline__ int wave_min_i32(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const int t = __shfl_xor(v, o, kWave);
-    v = t < v ? t : v;
-  }
-  return v;
-}
+__device__ __forceinline__ double sv_add_f64(double a, double b) { return a + b; }
+__device__ __forceinline__ uint64_t sv_max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+__device__ __forceinline__ int sv_min_i32(int a, int b) { return a < b ? a : b; }
+__device__ __forceinline__ int sv_max_i32(int a, int b) { return a > b ? a : b; }
 
-// inclusive scan over the wave, lane order
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) { SV_WAVE_REDUCE(uint64_t, u64, sv_max_u64); }
+__device__ __forceinline__ double wave_sum_f64(double v) { SV_WAVE_REDUCE(double, f64, sv_add_f64); }
+__device__ __forceinline__ int wave_min_i32(int v) { SV_WAVE_REDUCE(int, i32, sv_min_i32); }
+__device__ __forceinline__ int wave_max_i32(int v) { SV_WAVE_REDUCE(int, i32, sv_max_i32); }
+__device__ __forceinline__ float wave_max_f32(float v) { SV_WAVE_REDUCE(float, f32, fmaxf); }
+#undef SV_WAVE_REDUCE
+
+// Inclusive scan over the wave in lane order: shifts by 1, 2, 4, 8 inside each
+// row, then the totals of the rows before.
 __device__ __forceinline__ double wave_incl_scan_f64(double v) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const double t = __shfl_up(v, o, kWave);
-    if (lane >= o) v += t;
-  }
-  return v;
+  const int row = (threadIdx.x & (kWave - 1)) >> 4;
+  v += dpp_f64<dpp::kShr1>(v);
+  v += dpp_f64<dpp::kShr2>(v);
+  v += dpp_f64<dpp::kShr4>(v);
+  v += dpp_f64<dpp::kShr8>(v);
+  const double r0 = bcast_f64(v, 15), r1 = bcast_f64(v, 31), r2 = bcast_f64(v, 47);
+  const double r01 = r0 + r1;
+  const double off = row == 0 ? 0.0 : row == 1 ? r0 : row == 2 ? r01 : r01 + r2;
+  return off + v;
 }
 
 __device__ __forceinline__ int wave_incl_scan_i32(int v) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int t = __shfl_up(v, o, kWave);
-    if (lane >= o) v += t;
-  }
-  return v;
+  const int row = (threadIdx.x & (kWave - 1)) >> 4;
+  v += dpp_i32<dpp::kShr1>(v);
+  v += dpp_i32<dpp::kShr2>(v);
+  v += dpp_i32<dpp::kShr4>(v);
+  v += dpp_i32<dpp::kShr8>(v);
+  const int r0 = bcast_i32(v, 15), r1 = bcast_i32(v, 31), r2 = bcast_i32(v, 47);
+  const int off = row == 0 ? 0 : row == 1 ? r0 : row == 2 ? r0 + r1 : r0 + r1 + r2;
+  return off + v;
 }
 
 // ------------------------------------------------------------------ block reductions

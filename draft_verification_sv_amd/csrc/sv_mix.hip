@@ -203,8 +203,7 @@ __global__ __launch_bounds__(kWave) void k_mix_post(MixArgs a) {
   const float ml = act ? a.mix[static_cast<size_t>(r) * a.K + lane] : -INFINITY;
   __syncthreads();
   float mmax = ml;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, o, kWave));
+mmax = wave_max_f32(mmax);
   const double e = act ? exp(static_cast<double>(ml) - static_cast<double>(mmax)) : 0.0;
   const double pi = e / wave_sum_f64(e);  // q(z | y)
   bool consistent = act;

@@ -335,7 +335,7 @@ __device__ void row_block(const RowArgs& a, int p, uint32_t* hist, RowShared<NT>
         loc += rt[k];
       }
       const double inc = wave_incl_scan_f64(loc);
-      const double Z = __shfl(inc, kWave - 1, kWave);
+      const double Z = bcast_f64(inc, kWave - 1);
       const double lse = M + log(Z);
       if (!topp_on) {
         if (lane == 0) write_row(a, p, m, am, lse, -INFINITY, lse);
@@ -347,10 +347,7 @@ __device__ void row_block(const RowArgs& a, int p, uint32_t* hist, RowShared<NT>
         int low = -1;
         for (int d = lane; d < 2 * kSide; d += kWave)
           if (hist_get(hist, 2 * kSide - d)) low = d;
-        for (int o = 32; o > 0; o >>= 1) {
-          const int q = __shfl_xor(low, o, kWave);
-          low = q > low ? q : low;
-        }
+        low = wave_max_i32(low);
         if (lane == 0) write_row(a, p, m, am, lse, bin_value(2 * kSide - low), lse);
         return;
       }
@@ -370,8 +367,8 @@ __device__ void row_block(const RowArgs& a, int p, uint32_t* hist, RowShared<NT>
           run += rt[k];
         }
       }
-      crow = __shfl(crow, cl, kWave);
-      cbase = __shfl(cbase, cl, kWave);
+      crow = bcast_i32(crow, cl);
+      cbase = bcast_f64(cbase, cl);
       const double mass = bin_mass(hist, crow * kWave + lane, Td, M);
       const double inc2 = cbase + wave_incl_scan_f64(mass);
       const uint64_t hit = __ballot(inc2 >= target);
@@ -380,12 +377,12 @@ __device__ void row_block(const RowArgs& a, int p, uint32_t* hist, RowShared<NT>
       if (hit) {
         const int hl = __ffsll(static_cast<long long>(hit)) - 1;
         cut_d = crow * kWave + hl;
-        F = __shfl(inc2, hl, kWave);
+        F = bcast_f64(inc2, hl);
       } else {  // rounding: the last non-empty bin of the row
         const uint64_t ne = __ballot(mass > 0.0 || hist_get(hist, 2 * kSide - (crow * kWave + lane)) != 0u);
         const int hl = ne ? 63 - __clzll(static_cast<long long>(ne)) : kWave - 1;
         cut_d = crow * kWave + hl;
-        F = __shfl(inc2, kWave - 1, kWave);
+        F = bcast_f64(inc2, kWave - 1);
       }
       if (lane == 0) write_row(a, p, m, am, lse, bin_value(2 * kSide - cut_d), M + log(F));
       return;

@@ -19,15 +19,15 @@
 //   C. one wave: the category posterior in closed form, the acceptance tests,
 //      the first rejection n, and the draw context of slot n;
 //   D. the chunk of the drawn row: each wave sums p and the draw weight over
-//      its 512-value sub-chunks (values below the top-p cut are compacted
-//      away first) and writes one pair of doubles per sub-chunk.
+//      its 512-value sub-chunks (exp only over the values at or above the
+//      top-p cut, packed first) and writes one pair of doubles per sub-chunk.
 // Every chunk block recomputes A-C (at most 64 positions, a few KB of
 // gathers), so that no block waits for another; the first one writes the
 // acceptance outputs and the draw record.
 //
-// Pick (one block per request): a block scan over the request's sub-chunk
-// sums finds the sub-chunk holding u * W; one wave then re-forms its 512
-// weights and scans them.
+// Pick (one wave per request): a wave scan over the request's sub-chunk sums
+// finds the sub-chunk holding u * W; the wave then re-forms its 512 weights
+// and scans them.
 #include <math.h>
 
 #include "sv_device.hpp"
@@ -193,20 +193,20 @@ struct TailShared {
   uint64_t seed;
   int x[64];
   float mix[64];
-  // B. statistics of the candidate rows tb + i (i <= L_r) and values at the draft tokens
+  // B. statistics of the candidate rows tb + i (i <= L_r), values at the draft
+  // tokens, and f_z (the first position where branch z leaves the draft)
   float rc[65];
   double rk[65];
   int ra[65];
   float lx[64], dx[64];
   double dl[64];
   int da[64];
-  // C. posterior and draw context
-  double pi[64], A[64];
   int f[64];
+  // standalone draw: branch tokens and posterior weights at the slot
   int tv[64];
   double tw[64];
   DrawCtx c;
-  // D. per-wave staging of the values at or above the cut
+  // D. per-wave lists of the values at or above the cut (and their draft values)
   float st[kSumNT / kWave][kSubG * 8];
   float sd[kSumNT / kWave][kSubG * 8];
 };
@@ -216,30 +216,30 @@ struct TailShared {
 // w and the target logit at v).  q(v) is the summed weight of the branches with
 // token v; the draw weight at v is max(0, p(v) - q(v)); every other token keeps
 // p.  The distinct tokens go to c.ctok in lane order.
-__device__ __forceinline__ void build_corrections(TailShared& sh, int K, bool act, int v, double w, float lv) {
+__device__ __forceinline__ void build_corrections(DrawCtx& c, int K, bool act, int v, double w, float lv) {
   const int lane = threadIdx.x & (kWave - 1);
-  sh.tv[lane] = act ? v : -1;
-  sh.tw[lane] = act ? w : 0.0;
-  __syncwarp();
+  const int va = act ? v : -1;
+  const double wa = act ? w : 0.0;
   bool first = act;
   double q = 0.0;
   for (int z = 0; z < K; ++z) {
-    const int vz = sh.tv[z];
+    const int vz = bcast_i32(va, z);
+    const double wz = bcast_f64(wa, z);
     if (act && vz == v) {
-      q += sh.tw[z];
+      q += wz;
       if (z < lane) first = false;
     }
   }
   const uint64_t fm = __ballot(first);
   if (first) {
     const int idx = __popcll(fm & ((1ull << lane) - 1ull));
-    const double p = p_of(lv, sh.c.cut, sh.c.invT, sh.c.kept);
+    const double p = p_of(lv, c.cut, c.invT, c.kept);
     const double d = p - q;
-    sh.c.ctok[idx] = v;
-    sh.c.cp[idx] = p;
-    sh.c.cw[idx] = d > 0.0 ? d : 0.0;
+    c.ctok[idx] = v;
+    c.cp[idx] = p;
+    c.cw[idx] = d > 0.0 ? d : 0.0;
   }
-  if (lane == 0) sh.c.ncorr = __popcll(fm);
+  if (lane == 0) c.ncorr = __popcll(fm);
 }
 
 // The first chunk block's copy of the context for the pick kernel (wave 0).
@@ -258,14 +258,16 @@ __device__ __forceinline__ void write_record(const SampleArgs& a, int r, const D
 
 // D. Sums of p and of the draw weight over the sub-chunks of chunk ch of the
 // drawn row; wave wv takes sub-chunks ch*16 + k*4 + wv, k < 4, one 8-value
-// group per lane, all loaded before any arithmetic.
+// group per lane, all loaded before any arithmetic.  Only values at or above
+// the top-p cut carry weight, so each sub-chunk's such values are first packed
+// densely into the wave's LDS list (a ballot per value slot gives each lane its
+// position) and exp runs over the packed list only.
 template <bool kDense>
 __device__ __forceinline__ void sub_sums(const SampleArgs& a, const DrawCtx& c, int r, int ch, float* st, float* sd) {
   const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
   const int NG = groups_of(a.V);
   const bool dense_res = kDense && c.mode == kDrawResidual;
   const bool mix_res = !kDense && c.mode == kDrawResidual;
-  const bool cut_on = c.cut > -INFINITY;
   const char* trowp = row_ptr(a.tgt, a.dtype, c.trow, a.tgt_ld);
   const char* drowp = dense_res ? row_ptr(a.draft, a.ddtype, c.drow, a.draft_ld) : nullptr;
   const int sub0 = ch * kChunkSubs + wv;
@@ -285,44 +287,30 @@ __device__ __forceinline__ void sub_sums(const SampleArgs& a, const DrawCtx& c, 
   for (int k = 0; k < kSubPerWave; ++k) {
     const int sub = sub0 + k * (kSumNT / kWave);
     if (sub >= a.NSUB) break;  // wave-uniform
-    double sp = 0.0, sw = 0.0;
-    if (!cut_on) {
+    int tot = 0;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const double p = exp(static_cast<double>(l[k][q]) * c.invT - c.kept);
-        sp += p;
-        if (dense_res) {
-          const double t = p - exp(static_cast<double>(d[k][q]) * c.invT - c.dlse);
-          sw += t > 0.0 ? t : 0.0;
-        }
+    for (int q = 0; q < 8; ++q) {
+      const bool keep = l[k][q] >= c.cut;  // -inf padding fails unless the cut is -inf (then it weighs 0)
+      const uint64_t m = __ballot(keep);
+      if (keep) {
+        const int o = tot + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+        st[o] = l[k][q];
+        if (dense_res) sd[o] = d[k][q];
       }
-    } else {
-      // only values at or above the cut carry weight: compact them first
-      uint32_t m = 0;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) m |= (l[k][q] >= c.cut ? 1u : 0u) << q;
-      const int cnt = __popc(m);
-      const int inc = wave_incl_scan_i32(cnt);
-      const int tot = __shfl(inc, kWave - 1, kWave);
-      int o = inc - cnt;
-#pragma unroll
-      for (int q = 0; q < 8; ++q)
-        if (m & (1u << q)) {
-          st[o] = l[k][q];
-          if (dense_res) sd[o] = d[k][q];
-          ++o;
-        }
-      __syncwarp();
-      for (int e = lane; e < tot; e += kWave) {
-        const double p = exp(static_cast<double>(st[e]) * c.invT - c.kept);
-        sp += p;
-        if (dense_res) {
-          const double t = p - exp(static_cast<double>(sd[e]) * c.invT - c.dlse);
-          sw += t > 0.0 ? t : 0.0;
-        }
-      }
-      __syncwarp();  // the staging area is rewritten by the next sub-chunk
+      tot += __popcll(m);
     }
+    __syncwarp();
+    double sp = 0.0, sw = 0.0;
+    for (int e = lane; e < tot; e += kWave) {
+      const double p = exp(static_cast<double>(st[e]) * c.invT - c.kept);
+      sp += p;
+      if (dense_res) {
+        const double t = p - exp(static_cast<double>(sd[e]) * c.invT - c.dlse);
+        sw += t > 0.0 ? t : 0.0;
+      }
+    }
+    __syncwarp();  // the list is rewritten by the next sub-chunk
     sp = wave_sum_f64(sp);
     if (dense_res) sw = wave_sum_f64(sw);
     if (lane == 0) {
@@ -365,6 +353,7 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums(SampleArgs a) {
     sh.seed = *a.seed;
     sh.nin = kAccept ? 0 : a.n_acc_in[r];
   }
+  if (tid < kWave) sh.f[tid] = 0x7FFFFFFF;
   if (kAccept) {
     for (int i = tid; i < b; i += kSumNT) sh.x[i] = a.x[static_cast<size_t>(r) * b + i];
     if (!kDense) {
@@ -386,7 +375,8 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums(SampleArgs a) {
   const double invT = 1.0 / static_cast<double>(sh.T);
 
   if (kAccept) {
-    // B. row statistics of the candidate rows, values at the draft and branch tokens
+    // B. row statistics of the candidate rows, values at the draft and branch
+    // tokens; f_z = the first position where branch z leaves the draft
     for (int i = tid; i <= Lr; i += kSumNT) {
       sh.rc[i] = a.row_cut[tb + i];
       sh.rk[i] = a.row_kept[tb + i];
@@ -408,65 +398,64 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums(SampleArgs a) {
       for (int k = tid; k < K * Lr; k += kSumNT) {
         const int z = k / Lr, i = k - z * Lr;
         const int v = g[z * b + i];
+        if (v != sh.x[i]) atomicMin(&sh.f[z], i);
         gl[z * b + i] = v >= 0 && v < a.V ? load_val_rt(row_ptr(a.tgt, a.dtype, tb + i, a.tgt_ld), a.dtype, v)
                                           : -INFINITY;
       }
     __syncthreads();
 
-    // C. posterior, acceptance, draw context (wave 0)
+    // C. acceptance, posterior and draw context (wave 0; lane i < L_r tests
+    // position i + 1)
     if (tid < kWave) {
-      double q = 0.0;
+      const bool pos = lane < Lr;
+      const int xv = pos ? sh.x[lane] : -1;
+      const bool ok = xv >= 0 && xv < a.V;
+      if (report && pos && !ok) raise_status(a.status, SV_ST_BAD_TOKEN);
+      double p = 0.0, q = 0.0;
+      if (ok) {
+        p = greedy ? (xv == sh.ra[lane] ? 1.0 : 0.0) : p_of(sh.lx[lane], sh.rc[lane], invT, sh.rk[lane]);
+        if (kDense)
+          q = greedy ? (xv == sh.da[lane] ? 1.0 : 0.0) : exp(static_cast<double>(sh.dx[lane]) * invT - sh.dl[lane]);
+      }
+      const double u = u24(philox_at(sh.seed, static_cast<uint32_t>(lane), static_cast<uint32_t>(r)).x);
+      double pi = 0.0, A = 0.0;  // lane z: pi_z; lane i: A(i)
+      int f = -1;
       if (!kDense) {
-        // Lane z < K: pi_z = q(z | y) and f_z = the first position where branch z
-        // leaves the draft (L_r if none).  With A(i) = sum_z pi_z [f_z >= i]:
-        // w_z^(i) = pi_z [f_z >= i] / A(i) and q(x_i | x_<i) = A(i + 1) / A(i).
+        // Lane z < K: pi_z = q(z | y), f_z as above (L_r if none).  With
+        // A(i) = sum_z pi_z [f_z >= i]: w_z^(i) = pi_z [f_z >= i] / A(i) and
+        // q(x_i | x_<i) = A(i + 1) / A(i).
         const bool act = lane < K;
         const float ml = act ? sh.mix[lane] : -INFINITY;
-        float mmax = ml;
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, o, kWave));
+        const float mmax = wave_max_f32(ml);
         const double e = act ? exp(static_cast<double>(ml) - static_cast<double>(mmax)) : 0.0;
-        const double pi = e / wave_sum_f64(e);
-        int f = Lr;
-        if (act)
-          for (int i = Lr - 1; i >= 0; --i)
-            if (g[lane * b + i] != sh.x[i]) f = i;
-        sh.pi[lane] = pi;
-        sh.f[lane] = act ? f : -1;
-        __syncwarp();
+        pi = e / wave_sum_f64(e);
+        f = act ? min(sh.f[lane], Lr) : -1;
         double Ai = 0.0, Ai1 = 0.0;
         for (int z = 0; z < K; ++z) {
-          const double pz = sh.pi[z];
-          const int fz = sh.f[z];
+          const double pz = bcast_f64(pi, z);
+          const int fz = bcast_i32(f, z);
           Ai += fz >= lane ? pz : 0.0;
           Ai1 += fz > lane ? pz : 0.0;
         }
-        sh.A[lane] = Ai;
-        if (lane < Lr) {
-          q = Ai > 0.0 ? Ai1 / Ai : 0.0;
+        if (pos) {
+          if (ok) q = Ai > 0.0 ? Ai1 / Ai : 0.0;
           if (report) {
-            a.q_at_draft[static_cast<size_t>(r) * b + lane] = q;
+            a.q_at_draft[static_cast<size_t>(r) * b + lane] = Ai > 0.0 ? Ai1 / Ai : 0.0;
             if (!(Ai > 0.0)) raise_status(a.status, SV_ST_EMPTY_POSTERIOR);
-            double* pw = a.post_w + (static_cast<size_t>(r) * b + lane) * K;
-            for (int z = 0; z < K; ++z) pw[z] = Ai > 0.0 && sh.f[z] >= lane ? sh.pi[z] / Ai : 0.0;
           }
         }
+        if (report) {  // post_w[i][z], lane i < L_r
+          double* pw = a.post_w + static_cast<size_t>(r) * b * K;
+          for (int z = 0; z < K; ++z) {
+            const double pz = bcast_f64(pi, z);
+            const int fz = bcast_i32(f, z);
+            if (pos) pw[lane * K + z] = Ai > 0.0 && fz >= lane ? pz / Ai : 0.0;
+          }
+        }
+        A = Ai;
       }
       bool reject = false;
-      if (lane < Lr) {
-        const int xv = sh.x[lane];
-        const bool ok = xv >= 0 && xv < a.V;
-        if (report && !ok) raise_status(a.status, SV_ST_BAD_TOKEN);
-        double p = 0.0;
-        if (ok) {
-          p = greedy ? (xv == sh.ra[lane] ? 1.0 : 0.0) : p_of(sh.lx[lane], sh.rc[lane], invT, sh.rk[lane]);
-          if (kDense)
-            q = greedy ? (xv == sh.da[lane] ? 1.0 : 0.0)
-                       : exp(static_cast<double>(sh.dx[lane]) * invT - sh.dl[lane]);
-        } else {
-          q = 0.0;
-        }
-        const double u = u24(philox_at(sh.seed, static_cast<uint32_t>(lane), static_cast<uint32_t>(r)).x);
+      if (pos) {
         reject = !(q > 0.0 ? u < p / q : p > 0.0);
         if (report) {
           const size_t k = static_cast<size_t>(r) * b + lane;
@@ -493,8 +482,9 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums(SampleArgs a) {
       }
       __syncwarp();
       if (!kDense && !greedy && n < Lr) {
-        const bool act = lane < K && sh.f[lane] >= n;
-        build_corrections(sh, K, act, act ? g[lane * b + n] : -1, act ? sh.pi[lane] / sh.A[n] : 0.0,
+        const double An = bcast_f64(A, n);
+        const bool act = lane < K && f >= n;
+        build_corrections(c, K, act, act ? g[lane * b + n] : -1, act ? pi / An : 0.0,
                           act ? gl[lane * b + n] : -INFINITY);
       }
       __syncwarp();
@@ -533,8 +523,7 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums(SampleArgs a) {
         const double w = in ? sh.tw[lane] : 0.0;
         const bool act = in && w > 0.0 && v >= 0 && v < a.V;
         const float lv = act ? load_val_rt(row_ptr(a.tgt, a.dtype, tb + n, a.tgt_ld), a.dtype, v) : -INFINITY;
-        __syncwarp();
-        build_corrections(sh, K, act, v, w, lv);
+        build_corrections(c, K, act, v, w, lv);
       }
       __syncwarp();
       if (report) write_record(a, r, c);
@@ -546,86 +535,114 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums(SampleArgs a) {
   sub_sums<kDense>(a, c, r, ch, sh.st[wv], sh.sd[wv]);
 }
 
-// The draw: one block per request, after the sums.
+// The draw: one wave per request, after the sums.  Lane l holds the sub-chunk
+// sums [l*spt, (l+1)*spt); a wave scan finds the sub-chunk holding t = u * W,
+// then the lanes take its 64 groups and a second scan finds the token.
+constexpr int kPickCache = 8;  // sub-chunk sums kept in registers per lane
+
 template <bool kDense>
-__global__ __launch_bounds__(kSumNT) void k_pick(SampleArgs a) {
-  __shared__ double red[kSumNT / kWave];
-  __shared__ int redi[kSumNT / kWave];
-  __shared__ int s_sub;
-  __shared__ double s_base;
-  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1);
+__global__ __launch_bounds__(kWave) void k_pick(SampleArgs a) {
+  const int r = blockIdx.x, lane = threadIdx.x;
   const DrawRec& rec = a.rec[r];
   const int mode = rec.mode, n = rec.n, bonus = rec.bonus;
   const uint64_t seed = *a.seed;
-  // this thread's sub-chunks, and the branch corrections (wave 0), loaded at once
   const int NSUB = a.NSUB;
-  const int spt = (NSUB + kSumNT - 1) / kSumNT;
-  const int s0 = min(NSUB, tid * spt), s1 = min(NSUB, s0 + spt);
+  const int spt = (NSUB + kWave - 1) / kWave;
+  const int s0 = min(NSUB, lane * spt), s1 = min(NSUB, s0 + spt);
   const double* subp = a.sub + static_cast<size_t>(r) * NSUB * 2;
+  // every load of this round is independent of the others
+  double cw_[kPickCache], cp_[kPickCache];
   double lw = 0.0, lp = 0.0;
-  for (int s = s0; s < s1; ++s) {
+#pragma unroll
+  for (int k = 0; k < kPickCache; ++k) {
+    const int s = s0 + k;
+    cw_[k] = s < s1 ? subp[2 * s] : 0.0;
+    cp_[k] = s < s1 ? subp[2 * s + 1] : 0.0;
+  }
+#pragma unroll
+  for (int k = 0; k < kPickCache; ++k) {
+    lw += cw_[k];
+    lp += cp_[k];
+  }
+  for (int s = s0 + kPickCache; s < s1; ++s) {
     lw += subp[2 * s];
     lp += subp[2 * s + 1];
   }
-  int ctok = -1;
-  double cw = 0.0;
-  if (!kDense && tid < kWave) {
-    ctok = rec.ctok[lane];
-    cw = rec.cw[lane];
-  }
+  const int ctok = kDense ? -1 : rec.ctok[lane];
+  const double cwt = kDense ? 0.0 : rec.cw[lane];
   if (mode == kDrawNone) return;  // malformed offsets (reported by the sums kernel)
   if (mode == kDrawGreedy) {      // p is one-hot at the argmax, and so is the residual
-    if (tid == 0) {
+    if (lane == 0) {
       a.token[r] = rec.token;
       a.is_bonus[r] = bonus;
     }
     return;
   }
   bool use_p = mode == kDrawP;
-  double W;
-  double excl = block_excl_scan_f64<kSumNT>(use_p ? lp : lw, red, &W);
+  double incl = wave_incl_scan_f64(use_p ? lp : lw);
+  double W = bcast_f64(incl, kWave - 1);
   if (!use_p && !(W > 0.0)) {  // an all-zero residual (rounding) falls back to p
     use_p = true;
-    excl = block_excl_scan_f64<kSumNT>(lp, red, &W);
+    incl = wave_incl_scan_f64(lp);
+    W = bcast_f64(incl, kWave - 1);
   }
+  const double loc = use_p ? lp : lw;
   const double t = u24(philox_at(seed, static_cast<uint32_t>(n), static_cast<uint32_t>(r)).y) * W;
-  // the first sub-chunk whose running weight exceeds t
-  int found = 0x7FFFFFFF, last = -1;
-  double fbase = 0.0, lbase = 0.0, run = excl;
-  for (int s = s0; s < s1; ++s) {
-    const double ws = subp[2 * s + (use_p ? 1 : 0)];
-    if (ws > 0.0) {
-      last = s;
-      lbase = run;
+  // this lane's sub-chunks from running weight run0: the first whose running
+  // weight exceeds t (first_over), or the last with positive weight
+  auto search = [&](double run0, bool first_over, int& found, double& fb) {
+    double run = run0;
+#pragma unroll
+    for (int k = 0; k < kPickCache; ++k) {
+      const int s = s0 + k;
+      const double ws = use_p ? cp_[k] : cw_[k];
+      if (s < s1) {
+        if (first_over ? (found < 0 && run + ws > t) : ws > 0.0) {
+          found = s;
+          fb = run;
+        }
+        run += ws;
+      }
     }
-    if (run + ws > t) {
-      found = s;
-      fbase = run;
-      break;
+    for (int s = s0 + kPickCache; s < s1; ++s) {
+      const double ws = subp[2 * s + (use_p ? 1 : 0)];
+      if (first_over ? (found < 0 && run + ws > t) : ws > 0.0) {
+        found = s;
+        fb = run;
+      }
+      run += ws;
     }
-    run += ws;
+  };
+  int sub = -1;
+  double base = 0.0;
+  const uint64_t over = __ballot(incl > t);
+  if (over) {
+    const int L = __ffsll(static_cast<long long>(over)) - 1;
+    int found = -1;
+    double fb = 0.0;
+    if (lane == L) {
+      search(incl - loc, true, found, fb);
+      if (found < 0) search(incl - loc, false, found, fb);  // rounding inside the lane
+    }
+    sub = bcast_i32(found, L);
+    base = bcast_f64(fb, L);
   }
-  const int fmin = block_min_i32<kSumNT>(found, redi);
-  if (fmin != 0x7FFFFFFF) {
-    if (found == fmin) {
-      s_sub = fmin;
-      s_base = fbase;
-    }
-  } else {  // rounding: the last sub-chunk with positive weight
-    const int lmax = -block_min_i32<kSumNT>(-last, redi);
-    if (lmax >= 0 && last == lmax) {
-      s_sub = lmax;
-      s_base = lbase;
-    } else if (lmax < 0 && tid == 0) {
-      s_sub = 0;
-      s_base = 0.0;
+  if (sub < 0) {  // rounding: the last sub-chunk with positive weight
+    int last = -1;
+    double lb = 0.0;
+    search(incl - loc, false, last, lb);
+    const int lmax = wave_max_i32(last);
+    if (lmax >= 0) {
+      const uint64_t who = __ballot(last == lmax);
+      const int L = __ffsll(static_cast<long long>(who)) - 1;
+      sub = lmax;
+      base = bcast_f64(lb, L);
+    } else {
+      sub = 0;
+      base = 0.0;
     }
   }
-  __syncthreads();
-  if (tid >= kWave) return;
-  // wave 0 walks the sub-chunk: lane = 8-value group
-  const int sub = s_sub;
-  const double base = s_base;
+  // the sub-chunk: lane = 8-value group
   const int g = sub * kSubG + lane;
   const bool in = g < groups_of(a.V);
   const bool dense_res = kDense && !use_p;
@@ -654,8 +671,8 @@ __global__ __launch_bounds__(kSumNT) void k_pick(SampleArgs a) {
   if (!kDense && !use_p) {
     const int nc = rec.ncorr;
     for (int t2 = 0; t2 < nc; ++t2) {
-      const int v = __shfl(ctok, t2, kWave);
-      const double wv = __shfl(cw, t2, kWave);
+      const int v = bcast_i32(ctok, t2);
+      const double wv = bcast_f64(cwt, t2);
 #pragma unroll
       for (int q = 0; q < 8; ++q)
         if (v == g * 8 + q) w8[q] = wv;
@@ -664,27 +681,27 @@ __global__ __launch_bounds__(kSumNT) void k_pick(SampleArgs a) {
   double lsum = 0.0;
 #pragma unroll
   for (int q = 0; q < 8; ++q) lsum += w8[q];
-  const double incl = wave_incl_scan_f64(lsum);
-  const uint64_t over = __ballot(in && base + incl > t);
+  const double inc2 = wave_incl_scan_f64(lsum);
+  const uint64_t hit = __ballot(in && base + inc2 > t);
   int lastpos = -1;
 #pragma unroll
   for (int q = 0; q < 8; ++q)
     if (w8[q] > 0.0) lastpos = g * 8 + q;
   int tok;
-  if (over) {
-    const int L = __ffsll(static_cast<long long>(over)) - 1;
+  if (hit) {
+    const int L = __ffsll(static_cast<long long>(hit)) - 1;
     int pick = -1;
-    double acc = base + incl - lsum;
+    double acc = base + inc2 - lsum;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       acc += w8[q];
       if (acc > t && pick < 0 && w8[q] > 0.0) pick = g * 8 + q;
     }
     if (pick < 0) pick = lastpos;
-    tok = __shfl(pick, L, kWave);
-    if (tok < 0) tok = -wave_min_i32(-lastpos);
+    tok = bcast_i32(pick, L);
+    if (tok < 0) tok = wave_max_i32(lastpos);
   } else {  // rounding: the last positive weight of the sub-chunk
-    tok = -wave_min_i32(-lastpos);
+    tok = wave_max_i32(lastpos);
   }
   if (tok < 0) tok = sub * kSubG * 8;
   if (lane == 0) {
@@ -741,7 +758,7 @@ static int32_t launch_draw(const SampleArgs& a, hipStream_t s) {
   const size_t dyn = kDense ? 0 : sizeof(int) * 2 * static_cast<size_t>(a.K) * a.b;
   hipLaunchKernelGGL((k_draw_sums<kDense, kAccept>), dim3(a.R * a.S), dim3(kSumNT), dyn, s, a);
   if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
-  hipLaunchKernelGGL(k_pick<kDense>, dim3(a.R), dim3(kSumNT), 0, s, a);
+  hipLaunchKernelGGL(k_pick<kDense>, dim3(a.R), dim3(kWave), 0, s, a);
   return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
 }
 
