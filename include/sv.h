@@ -31,8 +31,10 @@
  *    device-side counts exit at once.
  *  - `stream` is a hipStream_t.  Calls are asynchronous; outputs are valid in
  *    stream order.  The workspace holds a status word (updated with atomics,
- *    so calls on different streams may share it) and the residual chunk sums
- *    (two sv_residual_sample calls that share a workspace must not overlap).
+ *    so calls on different streams may share it), one draw record per
+ *    request and the draw's sums per 512-value sub-chunk of the drawn row
+ *    (two draws -- sv_residual_sample or sv_accept_sample -- that share a
+ *    workspace must not overlap).  Only the status word outlives a call.
  *  - Requests r = 0..R-1, draft block of b positions, vocabulary V.
  *    L_r = pos_off[r+1] - pos_off[r] is the number of verified positions of
  *    request r (0 <= L_r <= b).  The target gives L_r + 1 rows per request:
@@ -237,7 +239,8 @@ int32_t sv_accept(const void* tgt_logits, int32_t dtype, int64_t tgt_ld, int32_t
  *   Arguments as sv_accept; in SV_Q_MIXTURE mode K, branch_tok and post_w
  *   come from sv_mixture_q.
  *   token[R], is_bonus[R]  out.
- * Two launches (chunk sums, then the draw); uses the workspace's chunk sums. */
+ * Two launches (sums of the drawn row per 512-value sub-chunk, then the draw);
+ * uses the workspace's draw records and sub-chunk sums. */
 int32_t sv_residual_sample(const void* tgt_logits, int32_t dtype, int64_t tgt_ld, int32_t V,
                            const int32_t* tgt_off, const int32_t* pos_off, int32_t R, int32_t b,
                            const float* temperature, const int32_t* row_argmax,
@@ -256,7 +259,7 @@ int32_t sv_residual_sample(const void* tgt_logits, int32_t dtype, int64_t tgt_ld
  * block of the draw recomputes its request's posterior and acceptance, so no
  * block waits for another.  SV_Q_DENSE takes the draft arguments of
  * sv_accept; K, mix_logits, branch_tok, post_w, q_at_draft may then be NULL.
- * Uses the workspace's chunk sums. */
+ * Uses the workspace's draw records and sub-chunk sums. */
 int32_t sv_accept_sample(const void* tgt_logits, int32_t dtype, int64_t tgt_ld, int32_t V,
                          const int32_t* tgt_off, const int32_t* pos_off, int32_t R, int32_t b,
                          const float* temperature, const int32_t* row_argmax, const float* row_cut,
