@@ -84,24 +84,49 @@ __device__ __forceinline__ double p_of(float l, float cut, double invT, double k
   return l >= cut ? exp(static_cast<double>(l) * invT - kept) : 0.0;
 }
 
-// 8 consecutive values starting at element 8g (elements >= V read as -inf)
-__device__ __forceinline__ void load8(const char* rowp, int dtype, int g, int V, float out[8]) {
-  const int e0 = g * 8;
-  if (e0 + 8 <= V) {
-    if (dtype == SV_BF16) {
-      const uint4 d = *reinterpret_cast<const uint4*>(rowp + static_cast<size_t>(e0) * 2);
-      out[0] = bf16_lo(d.x); out[1] = bf16_hi(d.x); out[2] = bf16_lo(d.y); out[3] = bf16_hi(d.y);
-      out[4] = bf16_lo(d.z); out[5] = bf16_hi(d.z); out[6] = bf16_lo(d.w); out[7] = bf16_hi(d.w);
-    } else {
-      const uint4 d0 = *reinterpret_cast<const uint4*>(rowp + static_cast<size_t>(e0) * 4);
-      const uint4 d1 = *reinterpret_cast<const uint4*>(rowp + static_cast<size_t>(e0) * 4 + 16);
-      out[0] = __uint_as_float(d0.x); out[1] = __uint_as_float(d0.y); out[2] = __uint_as_float(d0.z); out[3] = __uint_as_float(d0.w);
-      out[4] = __uint_as_float(d1.x); out[5] = __uint_as_float(d1.y); out[6] = __uint_as_float(d1.z); out[7] = __uint_as_float(d1.w);
-    }
+// The 8 values of group g (elements 8g .. 8g+7) as raw 16-byte words, issued
+// before any of them is used so that all of a thread's loads are in flight
+// together; decode8 converts them and reads elements >= V (and every element
+// of a group that is not `in` the row) as -inf.  Row bases
+// and pitches are 16-byte multiples, so an aligned 16-byte word holding an
+// element below V lies in the same mapped page as that element; the fp32 upper
+// word is read only when it holds one (else the lower word is read twice).
+template <int DT>
+__device__ __forceinline__ void raw8(const char* rowp, int g, int V, uint4& w0, uint4& w1) {
+  if constexpr (DT == SV_BF16) {
+    w0 = *reinterpret_cast<const uint4*>(rowp + static_cast<size_t>(g) * 16);
+    w1 = w0;
   } else {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) out[k] = e0 + k < V ? load_val_rt(rowp, dtype, e0 + k) : -INFINITY;
+    const char* q = rowp + static_cast<size_t>(g) * 32;
+    w0 = *reinterpret_cast<const uint4*>(q);
+    w1 = *reinterpret_cast<const uint4*>(g * 8 + 4 < V ? q + 16 : q);
   }
+}
+
+template <int DT>
+__device__ __forceinline__ void decode8(const uint4& w0, const uint4& w1, int g, int V, bool in, float out[8]) {
+  float v[8];
+  if constexpr (DT == SV_BF16) {
+    v[0] = bf16_lo(w0.x); v[1] = bf16_hi(w0.x); v[2] = bf16_lo(w0.y); v[3] = bf16_hi(w0.y);
+    v[4] = bf16_lo(w0.z); v[5] = bf16_hi(w0.z); v[6] = bf16_lo(w0.w); v[7] = bf16_hi(w0.w);
+  } else {
+    v[0] = __uint_as_float(w0.x); v[1] = __uint_as_float(w0.y); v[2] = __uint_as_float(w0.z); v[3] = __uint_as_float(w0.w);
+    v[4] = __uint_as_float(w1.x); v[5] = __uint_as_float(w1.y); v[6] = __uint_as_float(w1.z); v[7] = __uint_as_float(w1.w);
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) out[k] = in && g * 8 + k < V ? v[k] : -INFINITY;
+}
+
+// One element's raw bits (bf16: the 16-bit pattern; fp32: the word), converted
+// later by raw_f32, so that a load inside a branch needs no wait there.
+template <int DT>
+__device__ __forceinline__ uint32_t raw1(const char* rowp, int idx) {
+  if constexpr (DT == SV_BF16) return reinterpret_cast<const uint16_t*>(rowp)[idx];
+  else return reinterpret_cast<const uint32_t*>(rowp)[idx];
+}
+template <int DT>
+__device__ __forceinline__ float raw_f32(uint32_t w) {
+  return __uint_as_float(DT == SV_BF16 ? w << 16 : w);
 }
 
 // Offsets of request r are an exclusive scan with L_r <= b and L_r + 1 target rows.
@@ -187,28 +212,30 @@ struct DrawCtx {
 };
 
 struct TailShared {
-  // A. request header and tables
-  int pb, pe, tb, te, nin;
-  float T;
-  uint64_t seed;
+  // A. draft tokens and mixing logits
   int x[64];
   float mix[64];
-  // B. statistics of the candidate rows tb + i (i <= L_r), values at the draft
-  // tokens, and f_z (the first position where branch z leaves the draft)
+  // B. statistics of the candidate rows tb + i (i <= L_r); the mixture's
+  // q(z | y) and f_z (the first position where branch z leaves the draft)
   float rc[65];
   double rk[65];
   int ra[65];
-  float lx[64], dx[64];
-  double dl[64];
-  int da[64];
+  double pi[64];
   int f[64];
   // standalone draw: branch tokens and posterior weights at the slot
   int tv[64];
   double tw[64];
   DrawCtx c;
-  // D. per-wave lists of the values at or above the cut (and their draft values)
-  float st[kSumNT / kWave][kSubG * 8];
-  float sd[kSumNT / kWave][kSubG * 8];
+};
+
+// D's per-wave lists of values at or above the cut: kLists sub-chunks are
+// packed before any exp runs, so that their exp chains interleave.  They share
+// the dynamic LDS with the mixture's branch tables, which are dead by then.
+template <bool kDense>
+struct DLists {
+  static constexpr int kLists = kDense ? 2 : 4;                          // sub-chunks packed per pass
+  static constexpr int kPerWave = kLists * kSubG * 8 * (kDense ? 2 : 1);  // floats
+  static constexpr size_t kBytes = sizeof(float) * kPerWave * (kSumNT / kWave);
 };
 
 // Mixture residual at the draw slot (wave 0): lane z < K holds branch z (whether
@@ -220,6 +247,7 @@ __device__ __forceinline__ void build_corrections(DrawCtx& c, int K, bool act, i
   const int lane = threadIdx.x & (kWave - 1);
   const int va = act ? v : -1;
   const double wa = act ? w : 0.0;
+  const double p = act ? p_of(lv, c.cut, c.invT, c.kept) : 0.0;  // independent of the loop below
   bool first = act;
   double q = 0.0;
   for (int z = 0; z < K; ++z) {
@@ -233,7 +261,6 @@ __device__ __forceinline__ void build_corrections(DrawCtx& c, int K, bool act, i
   const uint64_t fm = __ballot(first);
   if (first) {
     const int idx = __popcll(fm & ((1ull << lane) - 1ull));
-    const double p = p_of(lv, c.cut, c.invT, c.kept);
     const double d = p - q;
     c.ctok[idx] = v;
     c.cp[idx] = p;
@@ -256,114 +283,161 @@ __device__ __forceinline__ void write_record(const SampleArgs& a, int r, const D
   }
 }
 
+// A(i) = sum_z pi_z [f_z >= i] and A(i + 1), lane i (pi, f in LDS, K <= 64).
+__device__ __forceinline__ void posterior_mass(const TailShared& sh, int K, int i, double& Ai, double& Ai1) {
+  Ai = 0.0;
+  Ai1 = 0.0;
+#pragma unroll 8
+  for (int z = 0; z < K; ++z) {
+    const double pz = sh.pi[z];
+    const int fz = sh.f[z];
+    Ai += fz >= i ? pz : 0.0;
+    Ai1 += fz > i ? pz : 0.0;
+  }
+}
+
 // D. Sums of p and of the draw weight over the sub-chunks of chunk ch of the
 // drawn row; wave wv takes sub-chunks ch*16 + k*4 + wv, k < 4, one 8-value
 // group per lane, all loaded before any arithmetic.  Only values at or above
-// the top-p cut carry weight, so each sub-chunk's such values are first packed
-// densely into the wave's LDS list (a ballot per value slot gives each lane its
-// position) and exp runs over the packed list only.
-template <bool kDense>
-__device__ __forceinline__ void sub_sums(const SampleArgs& a, const DrawCtx& c, int r, int ch, float* st, float* sd) {
+// the top-p cut carry weight: kLists sub-chunks at a time, each sub-chunk's
+// such values are packed densely into a list (a ballot per value slot gives
+// each lane its position), then exp runs over the lists, interleaved.
+template <int DT, int DDT, bool kDense>
+__device__ __forceinline__ void sub_sums(const SampleArgs& a, const DrawCtx& c, int r, int ch, float* lists) {
+  using DL = DLists<kDense>;
+  constexpr int kL = DL::kLists, kLen = kSubG * 8;
   const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
-  const int NG = groups_of(a.V);
+  const int V = a.V, NG = groups_of(V);
   const bool dense_res = kDense && c.mode == kDrawResidual;
   const bool mix_res = !kDense && c.mode == kDrawResidual;
-  const char* trowp = row_ptr(a.tgt, a.dtype, c.trow, a.tgt_ld);
-  const char* drowp = dense_res ? row_ptr(a.draft, a.ddtype, c.drow, a.draft_ld) : nullptr;
+  const float cut = c.cut;
+  const double invT = c.invT, kept = c.kept, dlse = c.dlse;
+  const char* trowp = row_ptr(a.tgt, DT, c.trow, a.tgt_ld);
+  const char* drowp = kDense ? row_ptr(a.draft, DDT, c.drow, a.draft_ld) : nullptr;
+  float* st = lists + wv * DL::kPerWave;  // kL lists of kLen target values
+  float* sd = st + kL * kLen;             // dense: kL lists of the matching draft values
   const int sub0 = ch * kChunkSubs + wv;
-  float l[kSubPerWave][8], d[kSubPerWave][8];
+  uint4 t0[kSubPerWave], t1[kSubPerWave], d0[kSubPerWave], d1[kSubPerWave];
 #pragma unroll
   for (int k = 0; k < kSubPerWave; ++k) {
-    const int g = (sub0 + k * (kSumNT / kWave)) * kSubG + lane;
-    if (g < NG) {
-      load8(trowp, a.dtype, g, a.V, l[k]);
-      if (dense_res) load8(drowp, a.ddtype, g, a.V, d[k]);
-    } else {
-#pragma unroll
-      for (int q = 0; q < 8; ++q) l[k][q] = -INFINITY;
-    }
+    const int g = min((sub0 + k * (kSumNT / kWave)) * kSubG + lane, NG - 1);
+    raw8<DT>(trowp, g, V, t0[k], t1[k]);
+    if (dense_res) raw8<DDT>(drowp, g, V, d0[k], d1[k]);
   }
+  // corrections of the mixture residual: lane t < ncorr holds branch token t
+  const int ctok = mix_res && lane < c.ncorr ? c.ctok[lane] : -1;
+  const double cdel = mix_res && lane < c.ncorr ? c.cw[lane] - c.cp[lane] : 0.0;
 #pragma unroll
-  for (int k = 0; k < kSubPerWave; ++k) {
-    const int sub = sub0 + k * (kSumNT / kWave);
-    if (sub >= a.NSUB) break;  // wave-uniform
-    int tot = 0;
+  for (int k0 = 0; k0 < kSubPerWave; k0 += kL) {
+    if (sub0 + k0 * (kSumNT / kWave) >= a.NSUB) break;  // wave-uniform
+    int tot[kL];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const bool keep = l[k][q] >= c.cut;  // -inf padding fails unless the cut is -inf (then it weighs 0)
-      const uint64_t m = __ballot(keep);
-      if (keep) {
-        const int o = tot + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+    for (int j = 0; j < kL; ++j) {
+      const int k = k0 + j;
+      const int g = (sub0 + k * (kSumNT / kWave)) * kSubG + lane;
+      float l[8], d[8];
+      decode8<DT>(t0[k], t1[k], g, V, g < NG, l);
+      if (dense_res) decode8<DDT>(d0[k], d1[k], g, V, g < NG, d);
+      int n = 0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const bool keep = l[q] >= cut;  // -inf past V fails unless the cut is -inf (then it weighs 0)
+        const uint64_t m = __ballot(keep);
+        if (keep) {
+          const int o = n + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
                                                       __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
-        st[o] = l[k][q];
-        if (dense_res) sd[o] = d[k][q];
+          st[j * kLen + o] = l[q];
+          if (dense_res) sd[j * kLen + o] = d[q];
+        }
+        n += __popcll(m);
       }
-      tot += __popcll(m);
+      tot[j] = n;
     }
     __syncwarp();
-    double sp = 0.0, sw = 0.0;
-    for (int e = lane; e < tot; e += kWave) {
-      const double p = exp(static_cast<double>(st[e]) * c.invT - c.kept);
-      sp += p;
-      if (dense_res) {
-        const double t = p - exp(static_cast<double>(sd[e]) * c.invT - c.dlse);
-        sw += t > 0.0 ? t : 0.0;
-      }
-    }
-    __syncwarp();  // the list is rewritten by the next sub-chunk
-    sp = wave_sum_f64(sp);
-    if (dense_res) sw = wave_sum_f64(sw);
-    if (lane == 0) {
-      if (!dense_res) sw = sp;
-      if (mix_res) {  // branch tokens: weight max(0, p - q) instead of p
-        const int v0 = sub * kSubG * 8;
-        for (int t = 0; t < c.ncorr; ++t) {
-          const int v = c.ctok[t];
-          if (v >= v0 && v < v0 + kSubG * 8) sw += c.cw[t] - c.cp[t];
+    int mx = 0;
+#pragma unroll
+    for (int j = 0; j < kL; ++j) mx = max(mx, tot[j]);
+    double sp[kL], sw[kL];
+#pragma unroll
+    for (int j = 0; j < kL; ++j) sp[j] = sw[j] = 0.0;
+    for (int e = lane; e < mx; e += kWave) {
+#pragma unroll
+      for (int j = 0; j < kL; ++j) {  // independent chains; entries past a list's end weigh 0
+        const bool in = e < tot[j];
+        const double p = exp(static_cast<double>(in ? st[j * kLen + e] : -INFINITY) * invT - kept);
+        sp[j] += in ? p : 0.0;
+        if (dense_res) {
+          const double t = p - exp(static_cast<double>(in ? sd[j * kLen + e] : -INFINITY) * invT - dlse);
+          sw[j] += in && t > 0.0 ? t : 0.0;
         }
       }
-      double* pp = a.sub + (static_cast<size_t>(r) * a.NSUB + sub) * 2;
-      pp[0] = sw;
-      pp[1] = sp;
+    }
+    __syncwarp();  // the lists are rewritten by the next pass
+#pragma unroll
+    for (int j = 0; j < kL; ++j) {
+      const int sub = sub0 + (k0 + j) * (kSumNT / kWave);
+      if (sub >= a.NSUB) break;  // wave-uniform
+      double tp = wave_sum_f64(sp[j]);
+      double tw = dense_res ? wave_sum_f64(sw[j]) : tp;
+      if (mix_res) {  // branch tokens in this sub-chunk: weight max(0, p - q) instead of p
+        const int v0 = sub * kLen;
+        const bool here = ctok >= v0 && ctok < v0 + kLen;
+        if (__ballot(here)) tw += wave_sum_f64(here ? cdel : 0.0);
+      }
+      if (lane == 0) {
+        double* pp = a.sub + (static_cast<size_t>(r) * a.NSUB + sub) * 2;
+        pp[0] = tw;
+        pp[1] = tp;
+      }
     }
   }
 }
 
 // The fused tail (kAccept: posterior, acceptance and the draw's sums) or the
 // standalone draw's sums (n from n_acc_in, posterior weights from post_w).
-template <bool kDense, bool kAccept>
+// DT / DDT: target / dense-draft logit types.
+template <int DT, int DDT, bool kDense, bool kAccept>
 __global__ __launch_bounds__(kSumNT) void k_draw_sums(SampleArgs a) {
   __shared__ TailShared sh;
-  extern __shared__ int dyn[];  // mixture: branch tokens [K][b], then target logits at them [K][b]
+  // dynamic LDS: the mixture's branch tokens [K][b] and target logits at them
+  // [K][b] through phase C, then D's lists
+  extern __shared__ int dyn[];
   int* g = dyn;
   float* gl = reinterpret_cast<float*>(dyn + a.K * a.b);
   const int r = blockIdx.x / a.S, ch = blockIdx.x % a.S;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
   const bool report = ch == 0;
-  const int K = kDense ? 0 : a.K, b = a.b;
+  const int K = kDense ? 0 : a.K, b = a.b, V = a.V;
   DrawCtx& c = sh.c;
 
-  // A. independent loads
-  if (tid == 0) {
-    sh.pb = a.pos_off[r];
-    sh.pe = a.pos_off[r + 1];
-    sh.tb = a.tgt_off[r];
-    sh.te = a.tgt_off[r + 1];
-    sh.T = a.T[r];
-    sh.seed = *a.seed;
-    sh.nin = kAccept ? 0 : a.n_acc_in[r];
+  // A. the request header (uniform: scalar loads) and the draft tokens, mixing
+  // logits and branch tokens (one per thread, clamped in-bounds), all issued
+  // before any is used; the offsets are checked after the barrier
+  const int pb = a.pos_off[r], pe = a.pos_off[r + 1], tb = a.tgt_off[r], te = a.tgt_off[r + 1];
+  const float T = a.T[r];
+  const int nin = kAccept ? 0 : a.n_acc_in[r];
+  int x0 = 0, g0 = 0;
+  float m0 = 0.0f;
+  if (kAccept) {
+    x0 = a.x[static_cast<size_t>(r) * b + min(tid, b - 1)];
+    if (!kDense) {
+      m0 = a.mix[static_cast<size_t>(r) * K + min(tid, K - 1)];
+      g0 = a.branch_tok[static_cast<size_t>(r) * K * b + min(tid, K * b - 1)];
+    }
   }
+  asm volatile("" ::: "memory");  // the compiler keeps every load above ahead of what follows
   if (tid < kWave) sh.f[tid] = 0x7FFFFFFF;
   if (kAccept) {
-    for (int i = tid; i < b; i += kSumNT) sh.x[i] = a.x[static_cast<size_t>(r) * b + i];
+    if (tid < b) sh.x[tid] = x0;
     if (!kDense) {
-      for (int z = tid; z < K; z += kSumNT) sh.mix[z] = a.mix[static_cast<size_t>(r) * K + z];
-      for (int k = tid; k < K * b; k += kSumNT) g[k] = a.branch_tok[static_cast<size_t>(r) * K * b + k];
+      if (tid < K) sh.mix[tid] = m0;
+      if (tid < K * b) g[tid] = g0;
+      for (int k = tid + kSumNT; k < K * b; k += kSumNT) g[k] = a.branch_tok[static_cast<size_t>(r) * K * b + k];
     }
   }
   __syncthreads();
-  const int pb = sh.pb, tb = sh.tb, Lr = sh.pe - sh.pb;
-  if (!(Lr >= 0 && Lr <= b && sh.te - tb == Lr + 1)) {
+  const int Lr = pe - pb;
+  if (!(Lr >= 0 && Lr <= b && te - tb == Lr + 1)) {
     if (report && tid == 0) {
       raise_status(a.status, SV_ST_BAD_OFFSETS);
       if (kAccept) a.n_acc[r] = 0;
@@ -371,88 +445,90 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums(SampleArgs a) {
     }
     return;
   }
-  const bool greedy = sh.T == 0.0f;
-  const double invT = 1.0 / static_cast<double>(sh.T);
+  const bool greedy = T == 0.0f;
+  const double invT = 1.0 / static_cast<double>(T);
 
   if (kAccept) {
     // B. row statistics of the candidate rows, values at the draft and branch
-    // tokens; f_z = the first position where branch z leaves the draft
-    for (int i = tid; i <= Lr; i += kSumNT) {
-      sh.rc[i] = a.row_cut[tb + i];
-      sh.rk[i] = a.row_kept[tb + i];
-      sh.ra[i] = a.row_argmax[tb + i];
+    // tokens (clamped in-bounds, all issued together); f_z by LDS atomicMin.
+    // Thread i (< L_r) keeps p(x_i), the dense q(x_i) and u_i in registers for
+    // phase C; wave 1 forms q(z | y).
+    const int is = min(tid, Lr);
+    const float rc0 = a.row_cut[tb + is];
+    const double rk0 = a.row_kept[tb + is];
+    const int ra0 = a.row_argmax[tb + is];
+    const int il = min(tid, Lr > 0 ? Lr - 1 : 0);
+    const int xl = sh.x[il];
+    const bool xok = xl >= 0 && xl < V;
+    const int xc = xok ? xl : 0;
+    const uint32_t lx0 = raw1<DT>(row_ptr(a.tgt, DT, tb + il, a.tgt_ld), xc);
+    uint32_t dx0 = 0;
+    double dl0 = 0.0;
+    int da0 = 0;
+    if (kDense && Lr > 0) {
+      dx0 = raw1<DDT>(row_ptr(a.draft, DDT, static_cast<int64_t>(r) * b + il, a.draft_ld), xc);
+      dl0 = a.dlse[pb + il];
+      da0 = a.dargmax[pb + il];
     }
-    for (int i = tid; i < Lr; i += kSumNT) {
-      const int xv = sh.x[i];
-      const bool ok = xv >= 0 && xv < a.V;
-      sh.lx[i] = ok ? load_val_rt(row_ptr(a.tgt, a.dtype, tb + i, a.tgt_ld), a.dtype, xv) : -INFINITY;
-      if (kDense) {
-        sh.dx[i] = ok ? load_val_rt(row_ptr(a.draft, a.ddtype, static_cast<int64_t>(r) * b + i, a.draft_ld),
-                                    a.ddtype, xv)
-                      : -INFINITY;
-        sh.dl[i] = a.dlse[pb + i];
-        sh.da[i] = a.dargmax[pb + i];
-      }
+    const int KL = K * Lr, Lq = Lr > 0 ? Lr : 1;
+    int gz = 0, gi = 0;
+    bool gok = false;
+    uint32_t gl0 = 0;
+    if (!kDense) {  // clamped in-bounds also when K * L_r = 0
+      const int k = min(tid, KL > 0 ? KL - 1 : 0);
+      gz = k / Lq;
+      gi = k - gz * Lq;
+      const int v = g[gz * b + gi];
+      gok = v >= 0 && v < V;
+      gl0 = raw1<DT>(row_ptr(a.tgt, DT, tb + gi, a.tgt_ld), gok ? v : 0);
+      if (tid < KL && v != sh.x[gi]) atomicMin(&sh.f[gz], gi);
     }
-    if (!kDense)
-      for (int k = tid; k < K * Lr; k += kSumNT) {
+    const uint64_t seed = *a.seed;  // last: it is moved to scalar registers at once
+    asm volatile("" ::: "memory");  // every load above is issued before the stores below
+    if (tid <= Lr) {
+      sh.rc[tid] = rc0;
+      sh.rk[tid] = rk0;
+      sh.ra[tid] = ra0;
+    }
+    if (!kDense) {
+      if (tid < KL) gl[gz * b + gi] = gok ? raw_f32<DT>(gl0) : -INFINITY;
+      for (int k = tid + kSumNT; k < KL; k += kSumNT) {  // K * L_r > kSumNT only
         const int z = k / Lr, i = k - z * Lr;
         const int v = g[z * b + i];
+        const bool ok = v >= 0 && v < V;
         if (v != sh.x[i]) atomicMin(&sh.f[z], i);
-        gl[z * b + i] = v >= 0 && v < a.V ? load_val_rt(row_ptr(a.tgt, a.dtype, tb + i, a.tgt_ld), a.dtype, v)
-                                          : -INFINITY;
+        gl[z * b + i] = ok ? load_val<DT>(row_ptr(a.tgt, DT, tb + i, a.tgt_ld), v) : -INFINITY;
       }
-    __syncthreads();
-
-    // C. acceptance, posterior and draw context (wave 0; lane i < L_r tests
-    // position i + 1)
-    if (tid < kWave) {
-      const bool pos = lane < Lr;
-      const int xv = pos ? sh.x[lane] : -1;
-      const bool ok = xv >= 0 && xv < a.V;
-      if (report && pos && !ok) raise_status(a.status, SV_ST_BAD_TOKEN);
-      double p = 0.0, q = 0.0;
-      if (ok) {
-        p = greedy ? (xv == sh.ra[lane] ? 1.0 : 0.0) : p_of(sh.lx[lane], sh.rc[lane], invT, sh.rk[lane]);
-        if (kDense)
-          q = greedy ? (xv == sh.da[lane] ? 1.0 : 0.0) : exp(static_cast<double>(sh.dx[lane]) * invT - sh.dl[lane]);
-      }
-      const double u = u24(philox_at(sh.seed, static_cast<uint32_t>(lane), static_cast<uint32_t>(r)).x);
-      double pi = 0.0, A = 0.0;  // lane z: pi_z; lane i: A(i)
-      int f = -1;
-      if (!kDense) {
-        // Lane z < K: pi_z = q(z | y), f_z as above (L_r if none).  With
-        // A(i) = sum_z pi_z [f_z >= i]: w_z^(i) = pi_z [f_z >= i] / A(i) and
-        // q(x_i | x_<i) = A(i + 1) / A(i).
+      if (wv == 1) {  // q(z | y) = softmax of the mixing logits
         const bool act = lane < K;
         const float ml = act ? sh.mix[lane] : -INFINITY;
         const float mmax = wave_max_f32(ml);
         const double e = act ? exp(static_cast<double>(ml) - static_cast<double>(mmax)) : 0.0;
-        pi = e / wave_sum_f64(e);
-        f = act ? min(sh.f[lane], Lr) : -1;
-        double Ai = 0.0, Ai1 = 0.0;
-        for (int z = 0; z < K; ++z) {
-          const double pz = bcast_f64(pi, z);
-          const int fz = bcast_i32(f, z);
-          Ai += fz >= lane ? pz : 0.0;
-          Ai1 += fz > lane ? pz : 0.0;
-        }
-        if (pos) {
-          if (ok) q = Ai > 0.0 ? Ai1 / Ai : 0.0;
-          if (report) {
-            a.q_at_draft[static_cast<size_t>(r) * b + lane] = Ai > 0.0 ? Ai1 / Ai : 0.0;
-            if (!(Ai > 0.0)) raise_status(a.status, SV_ST_EMPTY_POSTERIOR);
-          }
-        }
-        if (report) {  // post_w[i][z], lane i < L_r
-          double* pw = a.post_w + static_cast<size_t>(r) * b * K;
-          for (int z = 0; z < K; ++z) {
-            const double pz = bcast_f64(pi, z);
-            const int fz = bcast_i32(f, z);
-            if (pos) pw[lane * K + z] = Ai > 0.0 && fz >= lane ? pz / Ai : 0.0;
-          }
-        }
-        A = Ai;
+        sh.pi[lane] = e / wave_sum_f64(e);
+      }
+    }
+    // lane i < L_r of wave 0: p(x_i), the dense q(x_i), u_i (word 0)
+    const bool pos = tid < Lr;
+    double p = 0.0, qd = 0.0, u = 0.0;
+    if (tid < kWave) {
+      u = u24(philox_at(seed, static_cast<uint32_t>(lane), static_cast<uint32_t>(r)).x);
+      if (pos && xok) {
+        p = greedy ? (xl == ra0 ? 1.0 : 0.0) : p_of(raw_f32<DT>(lx0), rc0, invT, rk0);
+        if (kDense) qd = greedy ? (xl == da0 ? 1.0 : 0.0) : exp(static_cast<double>(raw_f32<DDT>(dx0)) * invT - dl0);
+      }
+      if (report && pos && !xok) raise_status(a.status, SV_ST_BAD_TOKEN);
+    }
+    __syncthreads();
+
+    // C. acceptance and the draw context (wave 0); posterior outputs (wave 1 of
+    // the reporting block)
+    if (tid < kWave) {
+      double q = qd, A = 0.0;  // lane i: q(x_i | x_<i), A(i)
+      if (!kDense) {
+        // w_z^(i) = pi_z [f_z >= i] / A(i), q(x_i | x_<i) = A(i + 1) / A(i)
+        double Ai1;
+        posterior_mass(sh, K, lane, A, Ai1);
+        q = pos && xok && A > 0.0 ? Ai1 / A : 0.0;
       }
       bool reject = false;
       if (pos) {
@@ -467,6 +543,7 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums(SampleArgs a) {
       const uint64_t mask = __ballot(reject);
       const int n = mask ? __ffsll(static_cast<long long>(mask)) - 1 : Lr;
       if (report && lane == 0) a.n_acc[r] = n;
+      const double dln = kDense ? bcast_f64(dl0, n < Lr ? n : 0) : 0.0;  // lane n loaded slot n's lse
       if (lane == 0) {
         c.n = n;
         c.bonus = n == Lr ? 1 : 0;
@@ -475,7 +552,7 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums(SampleArgs a) {
         c.cut = sh.rc[n];
         c.kept = sh.rk[n];
         c.invT = invT;
-        c.dlse = kDense && n < Lr ? sh.dl[n] : 0.0;
+        c.dlse = kDense && n < Lr ? dln : 0.0;
         c.trow = tb + n;
         c.drow = static_cast<int64_t>(r) * b + n;
         c.ncorr = 0;
@@ -483,16 +560,27 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums(SampleArgs a) {
       __syncwarp();
       if (!kDense && !greedy && n < Lr) {
         const double An = bcast_f64(A, n);
+        const int f = lane < K ? min(sh.f[lane], Lr) : -1;
         const bool act = lane < K && f >= n;
-        build_corrections(c, K, act, act ? g[lane * b + n] : -1, act ? pi / An : 0.0,
+        build_corrections(c, K, act, act ? g[lane * b + n] : -1, act ? sh.pi[lane] / An : 0.0,
                           act ? gl[lane * b + n] : -INFINITY);
       }
       __syncwarp();
       if (report) write_record(a, r, c);
+    } else if (!kDense && report && wv == 1) {
+      // post_w[i][z] and q_at_draft[i], lane i < L_r
+      double Ai, Ai1;
+      posterior_mass(sh, K, lane, Ai, Ai1);
+      if (lane < Lr) {
+        a.q_at_draft[static_cast<size_t>(r) * b + lane] = Ai > 0.0 ? Ai1 / Ai : 0.0;
+        if (!(Ai > 0.0)) raise_status(a.status, SV_ST_EMPTY_POSTERIOR);
+        double* pw = a.post_w + (static_cast<size_t>(r) * b + lane) * K;
+        for (int z = 0; z < K; ++z) pw[z] = Ai > 0.0 && min(sh.f[z], Lr) >= lane ? sh.pi[z] / Ai : 0.0;
+      }
     }
   } else {
     // standalone draw: n given; branch tokens and posterior weights at slot n given
-    int n = sh.nin;
+    int n = nin;
     if (n < 0 || n > Lr) {
       if (report && tid == 0) raise_status(a.status, SV_ST_BAD_NACC);
       n = n < 0 ? 0 : Lr;
@@ -521,18 +609,17 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums(SampleArgs a) {
         const bool in = lane < K;
         const int v = in ? sh.tv[lane] : -1;
         const double w = in ? sh.tw[lane] : 0.0;
-        const bool act = in && w > 0.0 && v >= 0 && v < a.V;
-        const float lv = act ? load_val_rt(row_ptr(a.tgt, a.dtype, tb + n, a.tgt_ld), a.dtype, v) : -INFINITY;
+        const bool act = in && w > 0.0 && v >= 0 && v < V;
+        const float lv = act ? load_val<DT>(row_ptr(a.tgt, DT, tb + n, a.tgt_ld), v) : -INFINITY;
         build_corrections(c, K, act, v, w, lv);
       }
       __syncwarp();
       if (report) write_record(a, r, c);
     }
   }
-  __syncthreads();
+  __syncthreads();  // also ends every use of the branch tables, which D's lists overwrite
   if (c.mode == kDrawGreedy) return;  // the draw is the argmax (taken by the pick kernel)
-  const int wv = tid / kWave;
-  sub_sums<kDense>(a, c, r, ch, sh.st[wv], sh.sd[wv]);
+  sub_sums<DT, DDT, kDense>(a, c, r, ch, reinterpret_cast<float*>(dyn));
 }
 
 // The draw: one wave per request, after the sums.  Lane l holds the sub-chunk
@@ -540,40 +627,49 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums(SampleArgs a) {
 // then the lanes take its 64 groups and a second scan finds the token.
 constexpr int kPickCache = 8;  // sub-chunk sums kept in registers per lane
 
-template <bool kDense>
+template <int DT, int DDT, bool kDense>
 __global__ __launch_bounds__(kWave) void k_pick(SampleArgs a) {
   const int r = blockIdx.x, lane = threadIdx.x;
   const DrawRec& rec = a.rec[r];
-  const int mode = rec.mode, n = rec.n, bonus = rec.bonus;
+  const int mode = rec.mode, n = rec.n, bonus = rec.bonus, rtok = rec.token, nc = kDense ? 0 : rec.ncorr;
+  const int64_t trow = rec.trow, drow = rec.drow;
+  const float cut = rec.cut;
+  const double invT = rec.invT, kept = rec.kept, dlse = rec.dlse;
   const uint64_t seed = *a.seed;
-  const int NSUB = a.NSUB;
+  const int V = a.V, NSUB = a.NSUB;
   const int spt = (NSUB + kWave - 1) / kWave;
   const int s0 = min(NSUB, lane * spt), s1 = min(NSUB, s0 + spt);
   const double* subp = a.sub + static_cast<size_t>(r) * NSUB * 2;
-  // every load of this round is independent of the others
+  // this round's loads (clamped in-bounds) are all issued before any is used
   double cw_[kPickCache], cp_[kPickCache];
-  double lw = 0.0, lp = 0.0;
 #pragma unroll
   for (int k = 0; k < kPickCache; ++k) {
-    const int s = s0 + k;
-    cw_[k] = s < s1 ? subp[2 * s] : 0.0;
-    cp_[k] = s < s1 ? subp[2 * s + 1] : 0.0;
-  }
-#pragma unroll
-  for (int k = 0; k < kPickCache; ++k) {
-    lw += cw_[k];
-    lp += cp_[k];
-  }
-  for (int s = s0 + kPickCache; s < s1; ++s) {
-    lw += subp[2 * s];
-    lp += subp[2 * s + 1];
+    const int s = min(s0 + k, NSUB - 1);
+    cw_[k] = subp[2 * s];
+    cp_[k] = subp[2 * s + 1];
   }
   const int ctok = kDense ? -1 : rec.ctok[lane];
   const double cwt = kDense ? 0.0 : rec.cw[lane];
+  asm volatile("" ::: "memory");  // every load above is issued before any is used
+  double lw = 0.0, lp = 0.0;
+#pragma unroll
+  for (int k = 0; k < kPickCache; ++k) {
+    if (s0 + k < s1) {
+      lw += cw_[k];
+      lp += cp_[k];
+    } else {
+      cw_[k] = 0.0;
+      cp_[k] = 0.0;
+    }
+  }
+  for (int s = s0 + kPickCache; s < s1; ++s) {  // more than kPickCache sub-chunks per lane
+    lw += subp[2 * s];
+    lp += subp[2 * s + 1];
+  }
   if (mode == kDrawNone) return;  // malformed offsets (reported by the sums kernel)
   if (mode == kDrawGreedy) {      // p is one-hot at the argmax, and so is the residual
     if (lane == 0) {
-      a.token[r] = rec.token;
+      a.token[r] = rtok;
       a.is_bonus[r] = bonus;
     }
     return;
@@ -643,33 +739,28 @@ __global__ __launch_bounds__(kWave) void k_pick(SampleArgs a) {
     }
   }
   // the sub-chunk: lane = 8-value group
+  const int NG = groups_of(V);
   const int g = sub * kSubG + lane;
-  const bool in = g < groups_of(a.V);
+  const int gc = min(g, NG - 1);
   const bool dense_res = kDense && !use_p;
+  uint4 t0, t1, d0, d1;
+  raw8<DT>(row_ptr(a.tgt, DT, trow, a.tgt_ld), gc, V, t0, t1);
+  if (dense_res) raw8<DDT>(row_ptr(a.draft, DDT, drow, a.draft_ld), gc, V, d0, d1);
+  float l[8], d[8];
+  decode8<DT>(t0, t1, g, V, g < NG, l);
+  if (dense_res) decode8<DDT>(d0, d1, g, V, g < NG, d);
   double w8[8];
-  {
-    float l[8], d[8];
-    if (in) {
-      load8(row_ptr(a.tgt, a.dtype, rec.trow, a.tgt_ld), a.dtype, g, a.V, l);
-      if (dense_res) load8(row_ptr(a.draft, a.ddtype, rec.drow, a.draft_ld), a.ddtype, g, a.V, d);
-    }
-    const float cut = rec.cut;
-    const double invT = rec.invT, kept = rec.kept, dlse = rec.dlse;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      double w = 0.0;
-      if (in && g * 8 + q < a.V) {
-        w = p_of(l[q], cut, invT, kept);
-        if (dense_res) {
-          const double t2 = w - exp(static_cast<double>(d[q]) * invT - dlse);
-          w = t2 > 0.0 ? t2 : 0.0;
-        }
-      }
-      w8[q] = w;
+  for (int q = 0; q < 8; ++q) {
+    double w = p_of(l[q], cut, invT, kept);  // 0 past V (value -inf) unless the cut is -inf
+    if (!(l[q] > -INFINITY)) w = 0.0;
+    if (dense_res) {
+      const double t2 = w - exp(static_cast<double>(d[q]) * invT - dlse);
+      w = t2 > 0.0 ? t2 : 0.0;
     }
+    w8[q] = w;
   }
   if (!kDense && !use_p) {
-    const int nc = rec.ncorr;
     for (int t2 = 0; t2 < nc; ++t2) {
       const int v = bcast_i32(ctok, t2);
       const double wv = bcast_f64(cwt, t2);
@@ -682,7 +773,7 @@ __global__ __launch_bounds__(kWave) void k_pick(SampleArgs a) {
 #pragma unroll
   for (int q = 0; q < 8; ++q) lsum += w8[q];
   const double inc2 = wave_incl_scan_f64(lsum);
-  const uint64_t hit = __ballot(in && base + inc2 > t);
+  const uint64_t hit = __ballot(g < NG && base + inc2 > t);
   int lastpos = -1;
 #pragma unroll
   for (int q = 0; q < 8; ++q)
@@ -753,13 +844,24 @@ static SampleArgs sample_args(const void* tgt_logits, int32_t dtype, int64_t tgt
 }
 
 // sums grid, then the pick; dynamic LDS holds the mixture's branch tables
-template <bool kDense, bool kAccept>
-static int32_t launch_draw(const SampleArgs& a, hipStream_t s) {
-  const size_t dyn = kDense ? 0 : sizeof(int) * 2 * static_cast<size_t>(a.K) * a.b;
-  hipLaunchKernelGGL((k_draw_sums<kDense, kAccept>), dim3(a.R * a.S), dim3(kSumNT), dyn, s, a);
+template <int DT, int DDT, bool kDense, bool kAccept>
+static int32_t launch_draw_t(const SampleArgs& a, hipStream_t s) {
+  const size_t tables = kDense ? 0 : sizeof(int) * 2 * static_cast<size_t>(a.K) * a.b;
+  const size_t dyn = tables > DLists<kDense>::kBytes ? tables : DLists<kDense>::kBytes;
+  hipLaunchKernelGGL((k_draw_sums<DT, DDT, kDense, kAccept>), dim3(a.R * a.S), dim3(kSumNT), dyn, s, a);
   if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
-  hipLaunchKernelGGL(k_pick<kDense>, dim3(a.R), dim3(kWave), 0, s, a);
+  hipLaunchKernelGGL((k_pick<DT, DDT, kDense>), dim3(a.R), dim3(kWave), 0, s, a);
   return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
+}
+
+template <bool kAccept>
+static int32_t launch_draw(const SampleArgs& a, hipStream_t s) {
+  const bool bf = a.dtype == SV_BF16, dbf = a.ddtype == SV_BF16;
+  if (a.q_mode == SV_Q_MIXTURE)
+    return bf ? launch_draw_t<SV_BF16, SV_BF16, false, kAccept>(a, s) : launch_draw_t<SV_F32, SV_F32, false, kAccept>(a, s);
+  if (bf)
+    return dbf ? launch_draw_t<SV_BF16, SV_BF16, true, kAccept>(a, s) : launch_draw_t<SV_BF16, SV_F32, true, kAccept>(a, s);
+  return dbf ? launch_draw_t<SV_F32, SV_BF16, true, kAccept>(a, s) : launch_draw_t<SV_F32, SV_F32, true, kAccept>(a, s);
 }
 
 extern "C" int32_t sv_accept(const void* tgt_logits, int32_t dtype, int64_t tgt_ld, int32_t V, const int32_t* tgt_off,
@@ -801,8 +903,7 @@ extern "C" int32_t sv_residual_sample(const void* tgt_logits, int32_t dtype, int
                              ws);
   a.K = q_mode == SV_Q_MIXTURE ? K : 0; a.branch_tok = branch_tok; a.post_w = const_cast<double*>(post_w);
   a.n_acc_in = n_acc; a.token = token; a.is_bonus = is_bonus;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  return q_mode == SV_Q_DENSE ? launch_draw<true, false>(a, s) : launch_draw<false, false>(a, s);
+  return launch_draw<false>(a, static_cast<hipStream_t>(stream));
 }
 
 extern "C" int32_t sv_accept_sample(const void* tgt_logits, int32_t dtype, int64_t tgt_ld, int32_t V,
@@ -828,6 +929,5 @@ extern "C" int32_t sv_accept_sample(const void* tgt_logits, int32_t dtype, int64
   a.x = draft_tok; a.K = q_mode == SV_Q_MIXTURE ? K : 0; a.mix = mix_logits; a.branch_tok = branch_tok;
   a.post_w = post_w; a.q_at_draft = q_at_draft; a.n_acc = n_acc; a.n_acc_in = n_acc; a.token = token;
   a.is_bonus = is_bonus; a.p_out = p_out; a.q_out = q_out; a.u_out = u_out;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  return q_mode == SV_Q_DENSE ? launch_draw<true, true>(a, s) : launch_draw<false, true>(a, s);
+  return launch_draw<true>(a, static_cast<hipStream_t>(stream));
 }
