@@ -209,7 +209,7 @@ def main():
             ev[0].record(stream)
         # target rows (statistics, top-p) and component rows (branch argmax) in one launch
         sv.sv_verify_rows(packed[s], dt, ld, V, tgt_off, R, max_rows, T, top_p, row_max, row_arg, row_lse, row_cut,
-                          row_kept, comp, ld, K, b, pos_off, max_pos, branch_tok, ws, nb, sp)
+                          row_kept, comp, ld, K, b, pos_off, max_pos, ws, nb, sp)
         if ev is not None:
             ev[1].record(stream)
         # category posterior, acceptance, residual / bonus draw

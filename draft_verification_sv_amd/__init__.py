@@ -66,7 +66,7 @@ _SIGS = {
                            _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "sv_philox_uniforms": [_vp, _i32, _i32, _vp, _vp],
     "sv_verify_rows": [_vp, _i32, _i64, _i32, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32,
-                       _i32, _vp, _i32, _vp, _vp, _sz, _vp],
+                       _i32, _vp, _i32, _vp, _sz, _vp],
     "sv_accept_sample": [_vp, _i32, _i64, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i64,
                          _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
 }
@@ -174,12 +174,12 @@ def sv_mixture_q(comp_logits, dtype, ld, V, K, b, mix_logits, pos_off, R, max_po
 
 
 def sv_verify_rows(tgt_logits, dtype, tgt_ld, V, tgt_off, R, max_rows, temperature, top_p, row_max, row_argmax,
-                   row_lse, row_cut, row_kept_lse, comp_logits, comp_ld, K, b, pos_off, max_pos, branch_tok, ws,
-                   ws_bytes, stream=None):
+                   row_lse, row_cut, row_kept_lse, comp_logits, comp_ld, K, b, pos_off, max_pos, ws, ws_bytes,
+                   stream=None):
     _check(_lib.sv_verify_rows(_p(tgt_logits), dtype, tgt_ld, V, _p(tgt_off), R, max_rows, _p(temperature),
                                _p(top_p), _p(row_max), _p(row_argmax), _p(row_lse), _p(row_cut), _p(row_kept_lse),
-                               _p(comp_logits), comp_ld, K, b, _p(pos_off), max_pos, _p(branch_tok), _p(ws),
-                               ws_bytes, _stream(stream)), "sv_verify_rows")
+                               _p(comp_logits), comp_ld, K, b, _p(pos_off), max_pos, _p(ws), ws_bytes,
+                               _stream(stream)), "sv_verify_rows")
 
 
 def sv_accept_sample(tgt_logits, dtype, tgt_ld, V, tgt_off, pos_off, R, b, temperature, row_argmax, row_cut,

@@ -292,25 +292,37 @@ struct DrawRec {
   double cw[64];     // and their draw weight max(0, p - q)
 };
 
+// ------------------------------------------------------------------ branch argmax parts
+// In the fused rows launch each component row is streamed by kMixParts blocks
+// (contiguous quarters of its 16-byte vectors); each writes its partial
+// argmax as a packed key (order key of the value above the complemented
+// index, 0 if it saw nothing) to its own workspace slot, and the draw's first
+// load round takes the largest key of the parts.
+constexpr int kMixParts = 4;
+
+__device__ __host__ inline uint32_t argmax_token(uint64_t key) {
+  return key ? 0xFFFFFFFFu - static_cast<uint32_t>(key) : 0u;
+}
+
 // ------------------------------------------------------------------ workspace layout
 // [status word, 256 B][draw records, R][sub-chunk sums, R * NSUB * 2 doubles]
+// [branch argmax parts, R * K * b * kMixParts keys]
 // Cross-block results travel through kernel boundaries (stream order), not
 // through in-kernel fences: a device-scope release on gfx950 writes back the
 // L2, which is far too costly to pay once per block.
 struct WsLayout {
-  size_t status, rec, sub, total;
+  size_t status, rec, sub, bkey, total;
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 __host__ __device__ inline WsLayout ws_layout(int R, int b, int K, int V) {
-  (void)b;
-  (void)K;
   WsLayout l;
   l.status = 0;
   l.rec = 256;
   l.sub = l.rec + align256(sizeof(DrawRec) * static_cast<size_t>(R));
-  l.total = l.sub + align256(sizeof(double) * 2 * static_cast<size_t>(R) * sub_chunks(V));
+  l.bkey = l.sub + align256(sizeof(double) * 2 * static_cast<size_t>(R) * sub_chunks(V));
+  l.total = l.bkey + align256(sizeof(uint64_t) * static_cast<size_t>(R) * K * b * kMixParts);
   return l;
 }
 

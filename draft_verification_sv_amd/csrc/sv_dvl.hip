@@ -14,17 +14,23 @@
 // One block of 256 threads:
 //   1. per request, the running products (written to s);
 //   2. radix select, 8 bits per pass from the top, of the B-th largest score
-//      (non-negative floats order like their bit patterns), with LDS count
-//      histograms; the digit holding the rank is found by a block scan over
-//      the 256 digit counts;
-//   3. per position, taken if above the threshold or a tie of rank below
-//      the remainder in (r, i) order (an exclusive scan of tie counts gives the
-//      ranks); L_r counted with integer LDS atomics;
+//      (score bits with -0 read as +0: non-negative floats order like their
+//      bit patterns), with LDS count histograms; the digit holding the rank is
+//      found by a block scan over the 256 digit counts; then a position is
+//      taken if above the threshold or a tie of rank below the remainder in
+//      (r, i) order (an exclusive scan of tie counts);
+//   3. L_r counted with integer atomics;
 //   4. exclusive scans of L and L + 1 into pos_off and tgt_off.
 #include "sv_device.hpp"
 #include "sv_host.hpp"
 
 namespace sv {
+
+// order key of a non-negative score: its bits, with -0 read as +0
+__device__ __forceinline__ uint32_t score_key(float v) {
+  const uint32_t k = __float_as_uint(v);
+  return k == 0x80000000u ? 0u : k;
+}
 
 constexpr int kDvlNT = 256;
 constexpr int kDvlLds = 8192;  // scores kept in LDS up to this many positions
@@ -47,9 +53,9 @@ __global__ __launch_bounds__(kDvlNT) void k_dvl(const float* __restrict__ a, int
     if (tid == 0) raise_status(status, SV_ST_BAD_BUDGET);
     B = 0;
   }
-  // 1. survival scores; non-negative floats order like their bit patterns.
-  // The estimates are read in one coalesced pass (into LDS when they fit)
-  // before any score is written, so no load waits behind a store.
+  // 1. survival scores.  The estimates are read in one coalesced pass (into
+  // LDS when they fit) before any score is written, so no load waits behind a
+  // store.
   bool bad = false;
   if constexpr (kInLds) {
     for (int e = tid; e < n; e += kDvlNT) {
@@ -57,6 +63,7 @@ __global__ __launch_bounds__(kDvlNT) void k_dvl(const float* __restrict__ a, int
       bad |= !(av >= 0.0f && av <= 1.0f);
       skey[e] = __float_as_uint(av);
     }
+    for (int r = tid; r < R; r += kDvlNT) lcount[r] = 0;
     __syncthreads();
     for (int r = tid; r < R; r += kDvlNT) {
       float run = 1.0f;
@@ -66,7 +73,11 @@ __global__ __launch_bounds__(kDvlNT) void k_dvl(const float* __restrict__ a, int
       }
     }
     __syncthreads();
-    for (int e = tid; e < n; e += kDvlNT) s[e] = __uint_as_float(skey[e]);
+    for (int e = tid; e < n; e += kDvlNT) {
+      const float sv = __uint_as_float(skey[e]);
+      s[e] = sv;
+      skey[e] = score_key(sv);
+    }
   } else {
     for (int r = tid; r < R; r += kDvlNT) L[r] = 0;
     for (int r = tid; r < R; r += kDvlNT) {
@@ -81,71 +92,70 @@ __global__ __launch_bounds__(kDvlNT) void k_dvl(const float* __restrict__ a, int
   }
   if (bad) raise_status(status, SV_ST_BAD_SCORE);
   __syncthreads();  // scores are re-read below by other threads of this block
-  auto key = [&](int e) -> uint32_t {
-    if constexpr (kInLds) return skey[e];
-    else return __float_as_uint(s[e]);
-  };
-
-  // 2. threshold: the B-th largest score (rank from the top, ties counted)
-  uint32_t thr = 0;
-  int remaining = 0;  // how many ties at thr are taken
   const bool all = B >= n, none = B == 0;
-  if (!all && !none) {
-    uint32_t prefix = 0, mask = 0;
-    remaining = B;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int k = tid; k < 256; k += kDvlNT) hist[k] = 0u;
-      __syncthreads();
-      for (int e = tid; e < n; e += kDvlNT) {
-        const uint32_t kk = key(e);
-        if ((kk & mask) == prefix) atomicAdd(&hist[(kk >> shift) & 255u], 1u);
-      }
-      __syncthreads();
-      // digits from the top: thread t holds digit 255 - t; the crossing digit
-      // is the one whose exclusive count from the top is < remaining <= inclusive
-      const int h = tid < 256 ? static_cast<int>(hist[255 - tid]) : 0;
-      int tot;
-      const int excl = block_excl_scan_i32<kDvlNT>(h, scr, &tot);
-      if (tid < 256 && excl < remaining && remaining <= excl + h) {
-        sh_prefix = prefix | (static_cast<uint32_t>(255 - tid) << shift);
-        sh_remaining = remaining - excl;
-      }
-      __syncthreads();
-      prefix = sh_prefix;
-      remaining = sh_remaining;
-      mask |= 255u << shift;
-    }
-    thr = prefix;
-  }
 
-  // 3. element-parallel choice: above the threshold, or a tie whose rank in
-  // (r, i) order is below `remaining`; lengths counted with LDS atomics.
-  // Thread t owns the consecutive elements [t*pe, (t+1)*pe).
-  if constexpr (kInLds)
-    for (int r = tid; r < R; r += kDvlNT) lcount[r] = 0;
-  const int pe = (n + kDvlNT - 1) / kDvlNT;
-  const int e0 = tid * pe, e1 = min(n, e0 + pe);
-  int eq_local = 0;
-  if (!all && !none)
-    for (int e = e0; e < e1; ++e) eq_local += key(e) == thr ? 1 : 0;
-  int eq_total;
-  int tie_rank = block_excl_scan_i32<kDvlNT>(eq_local, scr, &eq_total);  // also orders lcount's zeroing
-  for (int e = e0; e < e1; ++e) {
-    bool take;
-    if (all) {
-      take = true;
-    } else if (none) {
-      take = false;
-    } else {
-      const uint32_t kk = key(e);
-      take = kk > thr || (kk == thr && tie_rank < remaining);
-      tie_rank += kk == thr ? 1 : 0;
+  {
+    auto key = [&](int e) -> uint32_t {
+      if constexpr (kInLds) return skey[e];
+      else return score_key(s[e]);
+    };
+    // 2. threshold: the B-th largest score (rank from the top, ties counted)
+    uint32_t thr = 0;
+    int remaining = 0;  // how many ties at thr are taken
+    if (!all && !none) {
+      uint32_t prefix = 0, mask = 0;
+      remaining = B;
+      for (int shift = 24; shift >= 0; shift -= 8) {
+        for (int k = tid; k < 256; k += kDvlNT) hist[k] = 0u;
+        __syncthreads();
+        for (int e = tid; e < n; e += kDvlNT) {
+          const uint32_t kk = key(e);
+          if ((kk & mask) == prefix) atomicAdd(&hist[(kk >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        // digits from the top: thread t holds digit 255 - t; the crossing digit
+        // is the one whose exclusive count from the top is < remaining <= inclusive
+        const int h = tid < 256 ? static_cast<int>(hist[255 - tid]) : 0;
+        int tot;
+        const int excl = block_excl_scan_i32<kDvlNT>(h, scr, &tot);
+        if (tid < 256 && excl < remaining && remaining <= excl + h) {
+          sh_prefix = prefix | (static_cast<uint32_t>(255 - tid) << shift);
+          sh_remaining = remaining - excl;
+        }
+        __syncthreads();
+        prefix = sh_prefix;
+        remaining = sh_remaining;
+        mask |= 255u << shift;
+      }
+      thr = prefix;
     }
-    if (take) {
-      if constexpr (kInLds)
-        atomicAdd(&lcount[e / b], 1);
-      else
-        atomicAdd(&L[e / b], 1);
+    // 3. element-parallel choice: above the threshold, or a tie whose rank in
+    // (r, i) order is below `remaining`; lengths counted with atomics.
+    // Thread t owns the consecutive elements [t*pe, (t+1)*pe).
+    const int pe = (n + kDvlNT - 1) / kDvlNT;
+    const int e0 = tid * pe, e1 = min(n, e0 + pe);
+    int eq_local = 0;
+    if (!all && !none)
+      for (int e = e0; e < e1; ++e) eq_local += key(e) == thr ? 1 : 0;
+    int eq_total;
+    int tie_rank = block_excl_scan_i32<kDvlNT>(eq_local, scr, &eq_total);
+    for (int e = e0; e < e1; ++e) {
+      bool take;
+      if (all) {
+        take = true;
+      } else if (none) {
+        take = false;
+      } else {
+        const uint32_t kk = key(e);
+        take = kk > thr || (kk == thr && tie_rank < remaining);
+        tie_rank += kk == thr ? 1 : 0;
+      }
+      if (take) {
+        if constexpr (kInLds)
+          atomicAdd(&lcount[e / b], 1);
+        else
+          atomicAdd(&L[e / b], 1);
+      }
     }
   }
   __syncthreads();

@@ -37,7 +37,9 @@ struct MixArgs {
   const int32_t* pos_off;
   int R, max_pos;
   const int32_t* x;
-  int32_t* branch_tok;
+  int32_t* branch_tok;  // the argmax (one block per row), or
+  uint64_t* bkey;       // the partial argmax keys of `parts` blocks per row
+  int parts;
   double* post_w;
   double* q;
   uint32_t* status;
@@ -112,9 +114,10 @@ __device__ __forceinline__ void stream_argmax(const uint4* vp, int v0, int v1, f
   }
 }
 
-// argmax of component row m = p*K + z (position p, category z) by one block
+// argmax of part `part` (of a.parts) of component row m = p*K + z (position p,
+// category z) by one block
 template <int DT, int NT>
-__device__ __forceinline__ void mix_block(const MixArgs& a, int m, uint64_t* red, int* s_req) {
+__device__ __forceinline__ void mix_block(const MixArgs& a, int m, int part, uint64_t* red, int* s_req) {
   const int tid = threadIdx.x;
   const int z = m % a.K;
   const int p = m / a.K;
@@ -137,35 +140,45 @@ __device__ __forceinline__ void mix_block(const MixArgs& a, int m, uint64_t* red
   const int64_t row = (static_cast<int64_t>(r) * a.K + z) * a.b + i;
   const char* rowp = static_cast<const char*>(a.comp) + static_cast<size_t>(row) * static_cast<size_t>(a.ld) * esz;
   const int nvec = a.V / PER;
+  const int v0 = static_cast<int>(static_cast<int64_t>(nvec) * part / a.parts);
+  const int v1 = static_cast<int>(static_cast<int64_t>(nvec) * (part + 1) / a.parts);
   float best;
   int bidx;
-  stream_argmax<DT, NT>(reinterpret_cast<const uint4*>(rowp), 0, nvec, best, bidx);
-  for (int e = nvec * PER + tid; e < a.V; e += NT) {  // elements past the last full vector
-    const float f = load_val<DT>(rowp, e);
-    if (f > best || bidx < 0) {
-      best = f;
-      bidx = e;
+  stream_argmax<DT, NT>(reinterpret_cast<const uint4*>(rowp), v0, v1, best, bidx);
+  if (part == a.parts - 1)
+    for (int e = nvec * PER + tid; e < a.V; e += NT) {  // elements past the last full vector
+      const float f = load_val<DT>(rowp, e);
+      if (f > best || bidx < 0) {
+        best = f;
+        bidx = e;
+      }
     }
-  }
   uint64_t packed = bidx >= 0 ? (static_cast<uint64_t>(fkey(best)) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(bidx)) : 0;
   packed = block_max_u64<NT>(packed, red);
-  if (tid == 0)
-    a.branch_tok[(static_cast<size_t>(r) * a.K + z) * a.b + i] =
-        packed ? static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(packed)) : 0;
+  if (tid == 0) {
+    const size_t slot = (static_cast<size_t>(r) * a.K + z) * a.b + i;
+    if (a.bkey)
+      a.bkey[slot * a.parts + part] = packed;
+    else
+      a.branch_tok[slot] = static_cast<int>(argmax_token(packed));
+  }
 }
 
 template <int DT>
 __global__ __launch_bounds__(kMixNT) void k_mix_argmax(MixArgs a) {
   __shared__ uint64_t red[kMixNT / kWave];
   __shared__ int s_req;
-  mix_block<DT, kMixNT>(a, blockIdx.x, red, &s_req);
+  mix_block<DT, kMixNT>(a, blockIdx.x, 0, red, &s_req);
 }
 
 // One launch for the target rows and the component rows of a step: blocks
 // [0, n_row_blocks) take target rows (statistics and top-p cut), the rest take
-// component rows (branch argmax).  Lower block numbers are dispatched first,
-// so the target rows, which carry more work per byte, start at once on every
-// CU and share it with the component streaming.
+// one kMixParts-th of a component row each (partial branch argmax).  Lower
+// block numbers are dispatched first, so the target rows, which carry more work
+// per byte, start at once on every CU and share it with the component
+// streaming.  The launch has more blocks than fit at once; short component
+// blocks keep the last round short (cfg5: 107 us with 4 parts per row against
+// 110 us with whole rows).
 constexpr int kFusedNT = 256;
 constexpr int kFusedBatch = 4;
 
@@ -181,7 +194,8 @@ __global__ __launch_bounds__(kFusedNT) void k_rows_mix(RowArgs ra, MixArgs ma, i
     if (blk >= total) return;
     row_block<DT, kFusedNT, kFusedBatch>(ra, blk, hist, sh);
   } else {
-    mix_block<DT, kFusedNT>(ma, blk - n_row_blocks, sh.red_u64, &sh.req);
+    const int u = blk - n_row_blocks;
+    mix_block<DT, kFusedNT>(ma, u / kMixParts, u % kMixParts, sh.red_u64, &sh.req);
   }
 }
 
@@ -202,8 +216,7 @@ __global__ __launch_bounds__(kWave) void k_mix_post(MixArgs a) {
   const bool act = lane < a.K;
   const float ml = act ? a.mix[static_cast<size_t>(r) * a.K + lane] : -INFINITY;
   __syncthreads();
-  float mmax = ml;
-mmax = wave_max_f32(mmax);
+  const float mmax = wave_max_f32(ml);
   const double e = act ? exp(static_cast<double>(ml) - static_cast<double>(mmax)) : 0.0;
   const double pi = e / wave_sum_f64(e);  // q(z | y)
   bool consistent = act;
@@ -250,8 +263,8 @@ extern "C" int32_t sv_mixture_q(const void* comp_logits, int32_t dtype, int64_t 
     return SV_ERR_ARG;
   if (ws_bytes < ws_layout(R, b, K, V).total) return SV_ERR_WORKSPACE;
   if (max_pos == 0) return SV_OK;
-  MixArgs a{comp_logits, ld, V, K, b, mix_logits, pos_off, R, max_pos, draft_tok, branch_tok, post_w, q_at_draft,
-            status_word(ws)};
+  MixArgs a{comp_logits, ld, V, K, b, mix_logits, pos_off, R, max_pos, draft_tok, branch_tok, nullptr, 1,
+            post_w, q_at_draft, status_word(ws)};
   const long long grid = static_cast<long long>(max_pos) * K;
   if (grid > 0x7FFFFFFFLL) return SV_ERR_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -268,23 +281,27 @@ extern "C" int32_t sv_verify_rows(const void* tgt_logits, int32_t dtype, int64_t
                                   const int32_t* tgt_off, int32_t R, int32_t max_rows, const float* temperature,
                                   const float* top_p, float* row_max, int32_t* row_argmax, double* row_lse,
                                   float* row_cut, double* row_kept_lse, const void* comp_logits, int64_t comp_ld,
-                                  int32_t K, int32_t b, const int32_t* pos_off, int32_t max_pos, int32_t* branch_tok,
-                                  void* ws, size_t ws_bytes, void* stream) {
+                                  int32_t K, int32_t b, const int32_t* pos_off, int32_t max_pos, void* ws,
+                                  size_t ws_bytes, void* stream) {
   if (!tgt_logits || !tgt_off || !temperature || !row_max || !row_argmax || !row_lse || !row_cut || !row_kept_lse)
     return SV_ERR_ARG;
-  if (!comp_logits || !pos_off || !branch_tok || !ws) return SV_ERR_ARG;
+  if (!comp_logits || !pos_off || !ws) return SV_ERR_ARG;
   if (R < 1 || V < 1 || K < 1 || K > 64 || b < 1 || b > 64 || max_rows < 0 || max_pos < 0) return SV_ERR_ARG;
   if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_ARG;
   if (tgt_ld < V || comp_ld < V || !rows_aligned(tgt_logits, dtype, tgt_ld) || !rows_aligned(comp_logits, dtype, comp_ld))
     return SV_ERR_ARG;
   if (static_cast<long long>(max_pos) > static_cast<long long>(R) * b) return SV_ERR_ARG;
-  if (static_cast<long long>(max_rows) + static_cast<long long>(max_pos) * K > 0x7FFFFFFFLL) return SV_ERR_ARG;
-  if (ws_bytes < 256) return SV_ERR_WORKSPACE;
+  if (static_cast<long long>(max_rows) + static_cast<long long>(max_pos) * K * kMixParts > 0x7FFFFFFFLL)
+    return SV_ERR_ARG;
+  const WsLayout l = ws_layout(R, b, K, V);
+  if (ws_bytes < l.total) return SV_ERR_WORKSPACE;
   RowArgs ra{tgt_logits, tgt_ld, V, tgt_off, 0, R, max_rows, temperature, top_p, row_max, row_argmax, row_lse,
              row_cut, row_kept_lse, status_word(ws)};
-  MixArgs ma{comp_logits, comp_ld, V, K, b, nullptr, pos_off, R, max_pos, nullptr, branch_tok, nullptr, nullptr,
+  MixArgs ma{comp_logits, comp_ld, V, K, b, nullptr, pos_off, R, max_pos, nullptr, nullptr,
+             reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + l.bkey), kMixParts, nullptr, nullptr,
              status_word(ws)};
-  const unsigned grid = static_cast<unsigned>(max_rows) + static_cast<unsigned>(max_pos) * static_cast<unsigned>(K);
+  const unsigned mix_blocks = static_cast<unsigned>(max_pos) * static_cast<unsigned>(K) * kMixParts;
+  const unsigned grid = static_cast<unsigned>(max_rows) + mix_blocks;
   if (grid == 0) return SV_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == SV_BF16)

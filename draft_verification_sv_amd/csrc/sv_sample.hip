@@ -57,7 +57,9 @@ struct SampleArgs {
   const double* qx;  // q at the draft tokens (mixture, standalone acceptance)
   int K;
   const float* mix;  // mixing logits (fused tail)
-  const int32_t* branch_tok;
+  const int32_t* branch_tok;  // standalone draw: the branch argmax
+  const uint64_t* bkey;       // fused tail: the partial argmax keys of the rows launch
+  int32_t* branch_out;        // fused tail: the branch argmax, written for i < L_r
   double* post_w;      // read by the standalone draw; written by the fused tail
   double* q_at_draft;  // written by the fused tail
   const uint64_t* seed;
@@ -416,23 +418,39 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums(SampleArgs a) {
   const int pb = a.pos_off[r], pe = a.pos_off[r + 1], tb = a.tgt_off[r], te = a.tgt_off[r + 1];
   const float T = a.T[r];
   const int nin = kAccept ? 0 : a.n_acc_in[r];
-  int x0 = 0, g0 = 0;
+  int x0 = 0;
   float m0 = 0.0f;
+  uint64_t k0[kMixParts];  // the parts of branch (z, i) = thread t: the argmax is the largest key
+#pragma unroll
+  for (int q = 0; q < kMixParts; ++q) k0[q] = 0;
+  const uint64_t* kr = a.bkey + static_cast<size_t>(r) * K * b * kMixParts;
   if (kAccept) {
     x0 = a.x[static_cast<size_t>(r) * b + min(tid, b - 1)];
     if (!kDense) {
       m0 = a.mix[static_cast<size_t>(r) * K + min(tid, K - 1)];
-      g0 = a.branch_tok[static_cast<size_t>(r) * K * b + min(tid, K * b - 1)];
+#pragma unroll
+      for (int q = 0; q < kMixParts; ++q) k0[q] = kr[static_cast<size_t>(min(tid, K * b - 1)) * kMixParts + q];
     }
   }
   asm volatile("" ::: "memory");  // the compiler keeps every load above ahead of what follows
+  auto merged = [&](const uint64_t* ks) -> int {
+    uint64_t m = 0;
+#pragma unroll
+    for (int q = 0; q < kMixParts; ++q) m = ks[q] > m ? ks[q] : m;
+    return static_cast<int>(argmax_token(m));
+  };
   if (tid < kWave) sh.f[tid] = 0x7FFFFFFF;
   if (kAccept) {
     if (tid < b) sh.x[tid] = x0;
     if (!kDense) {
       if (tid < K) sh.mix[tid] = m0;
-      if (tid < K * b) g[tid] = g0;
-      for (int k = tid + kSumNT; k < K * b; k += kSumNT) g[k] = a.branch_tok[static_cast<size_t>(r) * K * b + k];
+      if (tid < K * b) g[tid] = merged(k0);
+      for (int k = tid + kSumNT; k < K * b; k += kSumNT) {  // K * b > kSumNT only
+        uint64_t ks[kMixParts];
+#pragma unroll
+        for (int q = 0; q < kMixParts; ++q) ks[q] = kr[static_cast<size_t>(k) * kMixParts + q];
+        g[k] = merged(ks);
+      }
     }
   }
   __syncthreads();
@@ -485,6 +503,9 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums(SampleArgs a) {
     }
     const uint64_t seed = *a.seed;  // last: it is moved to scalar registers at once
     asm volatile("" ::: "memory");  // every load above is issued before the stores below
+    if (!kDense && report)  // the merged branch argmax, i < L_r
+      for (int k = tid; k < K * b; k += kSumNT)
+        if (k % b < Lr) a.branch_out[static_cast<size_t>(r) * K * b + k] = g[k];
     if (tid <= Lr) {
       sh.rc[tid] = rc0;
       sh.rk[tid] = rk0;
@@ -912,7 +933,7 @@ extern "C" int32_t sv_accept_sample(const void* tgt_logits, int32_t dtype, int64
                                     const double* row_kept_lse, const int32_t* draft_tok, int32_t q_mode,
                                     const void* draft_logits, int32_t draft_dtype, int64_t draft_ld,
                                     const int32_t* draft_argmax, const double* draft_lse, int32_t K,
-                                    const float* mix_logits, const int32_t* branch_tok, double* post_w,
+                                    const float* mix_logits, int32_t* branch_tok, double* post_w,
                                     double* q_at_draft, const uint64_t* seed, int32_t* n_acc, int32_t* token,
                                     int32_t* is_bonus, double* p_out, double* q_out, float* u_out, void* ws,
                                     size_t ws_bytes, void* stream) {
@@ -926,7 +947,8 @@ extern "C" int32_t sv_accept_sample(const void* tgt_logits, int32_t dtype, int64
   SampleArgs a = sample_args(tgt_logits, dtype, tgt_ld, V, tgt_off, pos_off, R, b, temperature, row_argmax, row_cut,
                              row_kept_lse, q_mode, draft_logits, draft_dtype, draft_ld, draft_argmax, draft_lse, seed,
                              ws);
-  a.x = draft_tok; a.K = q_mode == SV_Q_MIXTURE ? K : 0; a.mix = mix_logits; a.branch_tok = branch_tok;
+  a.x = draft_tok; a.K = q_mode == SV_Q_MIXTURE ? K : 0; a.mix = mix_logits; a.branch_out = branch_tok;
+  a.bkey = reinterpret_cast<const uint64_t*>(static_cast<char*>(ws) + ws_layout(R, b, a.K, V).bkey);
   a.post_w = post_w; a.q_at_draft = q_at_draft; a.n_acc = n_acc; a.n_acc_in = n_acc; a.token = token;
   a.is_bonus = is_bonus; a.p_out = p_out; a.q_out = q_out; a.u_out = u_out;
   return launch_draw<true>(a, static_cast<hipStream_t>(stream));

@@ -143,11 +143,12 @@ class VerifyStep:
                            self.ws, self.ws_bytes, stream)
 
     def run_rows_fused(self, tgt, tgt_ld, comp, comp_ld, stream=None):
-        """Target rows and component rows (branch argmax) in one launch."""
+        """Target rows and component rows (partial branch argmax, merged by
+        sv_accept_sample) in one launch."""
         sv_verify_rows(tgt, self.dt, tgt_ld, self.V, self.tgt_off, self.R, self.max_rows, self.T,
                        self.top_p if self.use_topp else None, self.row_max, self.row_argmax, self.row_lse,
                        self.row_cut, self.row_kept, comp, comp_ld, self.K, self.b, self.pos_off, self.max_pos,
-                       self.branch_tok, self.ws, self.ws_bytes, stream)
+                       self.ws, self.ws_bytes, stream)
 
     def run_accept_sample(self, tgt, tgt_ld, *, draft=None, draft_ld=0, stream=None):
         """Posterior (mixture), acceptance and the draw: two launches."""

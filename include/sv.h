@@ -186,17 +186,21 @@ int32_t sv_mixture_q(const void* comp_logits, int32_t dtype, int64_t ld, int32_t
 
 /* sv_verify_rows: sv_topp_threshold over the packed target rows (row_off =
  * tgt_off, row_stride 0) and the branch argmax of sv_mixture_q over the
- * component rows (branch_tok[R*K*b] for i < L_r), in ONE launch: its blocks
- * take target rows first and component rows after, so the two read streams
- * share every compute unit.  The category posterior is left to
- * sv_accept_sample.  Arguments as in those two calls (one dtype).  Same method
- * and pages as sv_topp_threshold and sv_mixture_q; uses the status word only. */
+ * component rows, in ONE launch: its blocks take target rows first and
+ * component rows after, so the two read streams share every compute unit.
+ * Each component row is streamed by 4 blocks (contiguous quarters); each
+ * leaves its partial argmax in the workspace, and sv_accept_sample merges the
+ * parts into branch_tok and forms the category posterior.  Arguments as in
+ * those two calls (one dtype).  Same method and pages as sv_topp_threshold and
+ * sv_mixture_q.  Uses the status word and the workspace's branch argmax
+ * parts: call sv_accept_sample on the same workspace before the next
+ * sv_verify_rows. */
 int32_t sv_verify_rows(const void* tgt_logits, int32_t dtype, int64_t tgt_ld, int32_t V,
                        const int32_t* tgt_off, int32_t R, int32_t max_rows, const float* temperature,
                        const float* top_p, float* row_max, int32_t* row_argmax, double* row_lse,
                        float* row_cut, double* row_kept_lse, const void* comp_logits, int64_t comp_ld,
-                       int32_t K, int32_t b, const int32_t* pos_off, int32_t max_pos, int32_t* branch_tok,
-                       void* ws, size_t ws_bytes, void* stream);
+                       int32_t K, int32_t b, const int32_t* pos_off, int32_t max_pos, void* ws,
+                       size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------- acceptance */
 
@@ -252,21 +256,23 @@ int32_t sv_residual_sample(const void* tgt_logits, int32_t dtype, int64_t tgt_ld
                            size_t ws_bytes, void* stream);
 
 /* sv_accept_sample: the rest of a step in two launches -- for SV_Q_MIXTURE the
- * category posterior of sv_mixture_q (from branch_tok, mix_logits[R*K] and the
- * draft tokens; writes post_w and q_at_draft), then sv_accept and
- * sv_residual_sample (n_acc, token, is_bonus; optional p_out, q_out, u_out as
- * in sv_accept).  Same method and pages as those three calls.  Every chunk
- * block of the draw recomputes its request's posterior and acceptance, so no
- * block waits for another.  SV_Q_DENSE takes the draft arguments of
- * sv_accept; K, mix_logits, branch_tok, post_w, q_at_draft may then be NULL.
- * Uses the workspace's draw records and sub-chunk sums. */
+ * branch argmax (merged from the parts sv_verify_rows left in the workspace;
+ * branch_tok[R*K*b] out, written for i < L_r) and the category posterior of
+ * sv_mixture_q (from mix_logits[R*K] and the draft tokens; writes post_w and
+ * q_at_draft), then sv_accept and sv_residual_sample (n_acc, token, is_bonus;
+ * optional p_out, q_out, u_out as in sv_accept).  Same method and pages as
+ * those calls.  Every chunk block of the draw recomputes its request's
+ * posterior and acceptance, so no block waits for another.  SV_Q_DENSE takes
+ * the draft arguments of sv_accept; K, mix_logits, branch_tok, post_w,
+ * q_at_draft may then be NULL.  Uses the workspace's draw records and sub-chunk
+ * sums. */
 int32_t sv_accept_sample(const void* tgt_logits, int32_t dtype, int64_t tgt_ld, int32_t V,
                          const int32_t* tgt_off, const int32_t* pos_off, int32_t R, int32_t b,
                          const float* temperature, const int32_t* row_argmax, const float* row_cut,
                          const double* row_kept_lse, const int32_t* draft_tok, int32_t q_mode,
                          const void* draft_logits, int32_t draft_dtype, int64_t draft_ld,
                          const int32_t* draft_argmax, const double* draft_lse, int32_t K,
-                         const float* mix_logits, const int32_t* branch_tok, double* post_w,
+                         const float* mix_logits, int32_t* branch_tok, double* post_w,
                          double* q_at_draft, const uint64_t* seed, int32_t* n_acc, int32_t* token,
                          int32_t* is_bonus, double* p_out, double* q_out, float* u_out, void* ws,
                          size_t ws_bytes, void* stream);

@@ -49,12 +49,15 @@ def test_philox_words_bitexact(seed):
 def _dvl_cases():
     rng = np.random.default_rng(7)
     cases = []
-    for R, b in [(1, 1), (3, 5), (32, 16), (7, 64), (300, 16), (600, 16)]:
-        for kind in ("beta", "ties"):
+    # R*b up to 8192 keeps the scores in LDS, beyond that in global memory
+    for R, b in [(1, 1), (3, 5), (32, 16), (7, 64), (64, 16), (65, 16), (300, 16), (600, 16)]:
+        for kind in ("beta", "ties", "signed_zeros"):
             if kind == "beta":
                 a = rng.beta(8, 2, size=(R, b)).astype(np.float32)
-            else:
+            elif kind == "ties":
                 a = rng.choice([0.0, 0.5, 0.75, 1.0], size=(R, b)).astype(np.float32)
+            else:  # -0 orders as 0: ties broken by (r, i)
+                a = rng.choice([0.0, -0.0, 0.5, 1.0], size=(R, b)).astype(np.float32)
             for B in sorted({0, 1, R * b // 2, R * b - 1, R * b, R * b + 5}):
                 if B >= 0:
                     cases.append((R, b, kind, B, a))
