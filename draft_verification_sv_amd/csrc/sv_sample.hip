@@ -115,8 +115,21 @@ __device__ __forceinline__ void decode8(const uint4& w0, const uint4& w1, int g,
     v[0] = __uint_as_float(w0.x); v[1] = __uint_as_float(w0.y); v[2] = __uint_as_float(w0.z); v[3] = __uint_as_float(w0.w);
     v[4] = __uint_as_float(w1.x); v[5] = __uint_as_float(w1.y); v[6] = __uint_as_float(w1.z); v[7] = __uint_as_float(w1.w);
   }
+  const int valid = in ? min(max(V - g * 8, 0), 8) : 0;  // elements of the group below V
 #pragma unroll
-  for (int k = 0; k < 8; ++k) out[k] = in && g * 8 + k < V ? v[k] : -INFINITY;
+  for (int k = 0; k < 8; ++k) out[k] = k < valid ? v[k] : -INFINITY;
+}
+
+// The 8 values of a group from its raw words, unmasked.
+template <int DT>
+__device__ __forceinline__ void unpack8(const uint4& w0, const uint4& w1, float v[8]) {
+  if constexpr (DT == SV_BF16) {
+    v[0] = bf16_lo(w0.x); v[1] = bf16_hi(w0.x); v[2] = bf16_lo(w0.y); v[3] = bf16_hi(w0.y);
+    v[4] = bf16_lo(w0.z); v[5] = bf16_hi(w0.z); v[6] = bf16_lo(w0.w); v[7] = bf16_hi(w0.w);
+  } else {
+    v[0] = __uint_as_float(w0.x); v[1] = __uint_as_float(w0.y); v[2] = __uint_as_float(w0.z); v[3] = __uint_as_float(w0.w);
+    v[4] = __uint_as_float(w1.x); v[5] = __uint_as_float(w1.y); v[6] = __uint_as_float(w1.z); v[7] = __uint_as_float(w1.w);
+  }
 }
 
 // One element's raw bits (bf16: the 16-bit pattern; fp32: the word), converted
@@ -230,26 +243,28 @@ struct TailShared {
   DrawCtx c;
 };
 
-// D's per-wave lists of values at or above the cut: kLists sub-chunks are
-// packed before any exp runs, so that their exp chains interleave.  They share
-// the dynamic LDS with the mixture's branch tables, which are dead by then.
+// D's per-wave lists of values at or above the cut: the kLists sub-chunks of
+// a pass are packed one after another into one list (then one dummy slot per
+// lane), so that exp runs over the pass's kept values with no idle slots.  The
+// lists share the dynamic LDS with the mixture's branch tables, which are dead
+// by then.
 template <bool kDense>
 struct DLists {
   static constexpr int kLists = kDense ? 2 : 4;                          // sub-chunks packed per pass
-  static constexpr int kPerWave = kLists * kSubG * 8 * (kDense ? 2 : 1);  // floats
+  static constexpr int kCap = kLists * kSubG * 8;                        // values of a pass
+  static constexpr int kPerWave = (kCap + kWave) * (kDense ? 2 : 1);     // floats
   static constexpr size_t kBytes = sizeof(float) * kPerWave * (kSumNT / kWave);
 };
 
 // Mixture residual at the draw slot (wave 0): lane z < K holds branch z (whether
 // it is consistent with the accepted prefix, its token v, its posterior weight
-// w and the target logit at v).  q(v) is the summed weight of the branches with
-// token v; the draw weight at v is max(0, p(v) - q(v)); every other token keeps
-// p.  The distinct tokens go to c.ctok in lane order.
-__device__ __forceinline__ void build_corrections(DrawCtx& c, int K, bool act, int v, double w, float lv) {
+// w and the target probability p at v).  q(v) is the summed weight of the
+// branches with token v; the draw weight at v is max(0, p(v) - q(v)); every
+// other token keeps p.  The distinct tokens go to c.ctok in lane order.
+__device__ __forceinline__ void build_corrections(DrawCtx& c, int K, bool act, int v, double w, double p) {
   const int lane = threadIdx.x & (kWave - 1);
   const int va = act ? v : -1;
   const double wa = act ? w : 0.0;
-  const double p = act ? p_of(lv, c.cut, c.invT, c.kept) : 0.0;  // independent of the loop below
   bool first = act;
   double q = 0.0;
   for (int z = 0; z < K; ++z) {
@@ -302,8 +317,9 @@ __device__ __forceinline__ void posterior_mass(const TailShared& sh, int K, int 
 // drawn row; wave wv takes sub-chunks ch*16 + k*4 + wv, k < 4, one 8-value
 // group per lane, all loaded before any arithmetic.  Only values at or above
 // the top-p cut carry weight: kLists sub-chunks at a time, each sub-chunk's
-// such values are packed densely into a list (a ballot per value slot gives
-// each lane its position), then exp runs over the lists, interleaved.
+// such values are packed densely into a list (positions from a wave scan of the
+// per-lane counts; the other values go to the lane's dummy slot, so no store
+// branches), then exp runs over the lists, interleaved.
 template <int DT, int DDT, bool kDense>
 __device__ __forceinline__ void sub_sums(const SampleArgs& a, const DrawCtx& c, int r, int ch, float* lists) {
   using DL = DLists<kDense>;
@@ -316,8 +332,8 @@ __device__ __forceinline__ void sub_sums(const SampleArgs& a, const DrawCtx& c, 
   const double invT = c.invT, kept = c.kept, dlse = c.dlse;
   const char* trowp = row_ptr(a.tgt, DT, c.trow, a.tgt_ld);
   const char* drowp = kDense ? row_ptr(a.draft, DDT, c.drow, a.draft_ld) : nullptr;
-  float* st = lists + wv * DL::kPerWave;  // kL lists of kLen target values
-  float* sd = st + kL * kLen;             // dense: kL lists of the matching draft values
+  float* st = lists + wv * DL::kPerWave;  // the pass's kept target values, then lane dummies
+  float* sd = st + DL::kCap + kWave;      // dense: the matching draft values
   const int sub0 = ch * kChunkSubs + wv;
   uint4 t0[kSubPerWave], t1[kSubPerWave], d0[kSubPerWave], d1[kSubPerWave];
 #pragma unroll
@@ -332,49 +348,54 @@ __device__ __forceinline__ void sub_sums(const SampleArgs& a, const DrawCtx& c, 
 #pragma unroll
   for (int k0 = 0; k0 < kSubPerWave; k0 += kL) {
     if (sub0 + k0 * (kSumNT / kWave) >= a.NSUB) break;  // wave-uniform
-    int tot[kL];
+    // pack: segment j holds sub-chunk k0 + j's kept values, in vocabulary order
+    int seg[kL + 1];
+    seg[0] = 0;
 #pragma unroll
     for (int j = 0; j < kL; ++j) {
       const int k = k0 + j;
       const int g = (sub0 + k * (kSumNT / kWave)) * kSubG + lane;
+      const int valid = g < NG ? min(V - g * 8, 8) : 0;
       float l[8], d[8];
-      decode8<DT>(t0[k], t1[k], g, V, g < NG, l);
-      if (dense_res) decode8<DDT>(d0[k], d1[k], g, V, g < NG, d);
-      int n = 0;
+      unpack8<DT>(t0[k], t1[k], l);
+      if (dense_res) unpack8<DDT>(d0[k], d1[k], d);
+      if (valid < 8)  // the row's last group, or past its end: those values are dropped
+#pragma unroll
+        for (int q = 0; q < 8; ++q) l[q] = q < valid ? l[q] : -INFINITY;
+      int cnt = 0;  // -inf fails the test unless the cut is -inf (then it weighs 0)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) cnt += l[q] >= cut ? 1 : 0;
+      const int inc = wave_incl_scan_i32(cnt);
+      int o = seg[j] + inc - cnt;
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
-        const bool keep = l[q] >= cut;  // -inf past V fails unless the cut is -inf (then it weighs 0)
-        const uint64_t m = __ballot(keep);
-        if (keep) {
-          const int o = n + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
-                                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
-          st[j * kLen + o] = l[q];
-          if (dense_res) sd[j * kLen + o] = d[q];
-        }
-        n += __popcll(m);
+        const bool keep = l[q] >= cut;
+        const int at = keep ? o : DL::kCap + lane;
+        st[at] = l[q];
+        if (dense_res) sd[at] = d[q];
+        o += keep ? 1 : 0;
       }
-      tot[j] = n;
+      seg[j + 1] = seg[j] + bcast_i32(inc, kWave - 1);
     }
     __syncwarp();
-    int mx = 0;
-#pragma unroll
-    for (int j = 0; j < kL; ++j) mx = max(mx, tot[j]);
     double sp[kL], sw[kL];
 #pragma unroll
     for (int j = 0; j < kL; ++j) sp[j] = sw[j] = 0.0;
-    for (int e = lane; e < mx; e += kWave) {
+    for (int e = lane; e < seg[kL]; e += kWave) {
+      const double p = exp(static_cast<double>(st[e]) * invT - kept);
+      double t = 0.0;
+      if (dense_res) {
+        t = p - exp(static_cast<double>(sd[e]) * invT - dlse);
+        t = t > 0.0 ? t : 0.0;
+      }
 #pragma unroll
-      for (int j = 0; j < kL; ++j) {  // independent chains; entries past a list's end weigh 0
-        const bool in = e < tot[j];
-        const double p = exp(static_cast<double>(in ? st[j * kLen + e] : -INFINITY) * invT - kept);
-        sp[j] += in ? p : 0.0;
-        if (dense_res) {
-          const double t = p - exp(static_cast<double>(in ? sd[j * kLen + e] : -INFINITY) * invT - dlse);
-          sw[j] += in && t > 0.0 ? t : 0.0;
-        }
+      for (int j = 0; j < kL; ++j) {  // the segment holding e
+        const bool here = e >= seg[j] && e < seg[j + 1];
+        sp[j] += here ? p : 0.0;
+        if (dense_res) sw[j] += here ? t : 0.0;
       }
     }
-    __syncwarp();  // the lists are rewritten by the next pass
+    __syncwarp();  // the list is rewritten by the next pass
 #pragma unroll
     for (int j = 0; j < kL; ++j) {
       const int sub = sub0 + (k0 + j) * (kSumNT / kWave);
@@ -401,11 +422,11 @@ __device__ __forceinline__ void sub_sums(const SampleArgs& a, const DrawCtx& c, 
 template <int DT, int DDT, bool kDense, bool kAccept>
 __global__ __launch_bounds__(kSumNT) void k_draw_sums(SampleArgs a) {
   __shared__ TailShared sh;
-  // dynamic LDS: the mixture's branch tokens [K][b] and target logits at them
-  // [K][b] through phase C, then D's lists
-  extern __shared__ int dyn[];
+  // dynamic LDS: the mixture's branch tokens [K][b] and the target
+  // probabilities at them [K][b] (double) through phase C, then D's lists
+  extern __shared__ __align__(16) int dyn[];
   int* g = dyn;
-  float* gl = reinterpret_cast<float*>(dyn + a.K * a.b);
+  double* gp = reinterpret_cast<double*>(dyn + ((a.K * a.b + 1) & ~1));
   const int r = blockIdx.x / a.S, ch = blockIdx.x % a.S;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
   const bool report = ch == 0;
@@ -492,6 +513,8 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums(SampleArgs a) {
     int gz = 0, gi = 0;
     bool gok = false;
     uint32_t gl0 = 0;
+    float grc = 0.0f;
+    double grk = 0.0;
     if (!kDense) {  // clamped in-bounds also when K * L_r = 0
       const int k = min(tid, KL > 0 ? KL - 1 : 0);
       gz = k / Lq;
@@ -499,6 +522,8 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums(SampleArgs a) {
       const int v = g[gz * b + gi];
       gok = v >= 0 && v < V;
       gl0 = raw1<DT>(row_ptr(a.tgt, DT, tb + gi, a.tgt_ld), gok ? v : 0);
+      grc = a.row_cut[tb + gi];  // the row's statistics again, for p at this branch token
+      grk = a.row_kept[tb + gi];
       if (tid < KL && v != sh.x[gi]) atomicMin(&sh.f[gz], gi);
     }
     const uint64_t seed = *a.seed;  // last: it is moved to scalar registers at once
@@ -512,13 +537,17 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums(SampleArgs a) {
       sh.ra[tid] = ra0;
     }
     if (!kDense) {
-      if (tid < KL) gl[gz * b + gi] = gok ? raw_f32<DT>(gl0) : -INFINITY;
+      // p at every branch token of every candidate slot (used at the draw slot)
+      if (tid < KL && !greedy) gp[gz * b + gi] = gok ? p_of(raw_f32<DT>(gl0), grc, invT, grk) : 0.0;
       for (int k = tid + kSumNT; k < KL; k += kSumNT) {  // K * L_r > kSumNT only
         const int z = k / Lr, i = k - z * Lr;
         const int v = g[z * b + i];
         const bool ok = v >= 0 && v < V;
         if (v != sh.x[i]) atomicMin(&sh.f[z], i);
-        gl[z * b + i] = ok ? load_val<DT>(row_ptr(a.tgt, DT, tb + i, a.tgt_ld), v) : -INFINITY;
+        if (!greedy)
+          gp[z * b + i] = ok ? p_of(load_val<DT>(row_ptr(a.tgt, DT, tb + i, a.tgt_ld), v), a.row_cut[tb + i], invT,
+                                    a.row_kept[tb + i])
+                             : 0.0;
       }
       if (wv == 1) {  // q(z | y) = softmax of the mixing logits
         const bool act = lane < K;
@@ -584,7 +613,7 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums(SampleArgs a) {
         const int f = lane < K ? min(sh.f[lane], Lr) : -1;
         const bool act = lane < K && f >= n;
         build_corrections(c, K, act, act ? g[lane * b + n] : -1, act ? sh.pi[lane] / An : 0.0,
-                          act ? gl[lane * b + n] : -INFINITY);
+                          act ? gp[lane * b + n] : 0.0);
       }
       __syncwarp();
       if (report) write_record(a, r, c);
@@ -632,7 +661,7 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums(SampleArgs a) {
         const double w = in ? sh.tw[lane] : 0.0;
         const bool act = in && w > 0.0 && v >= 0 && v < V;
         const float lv = act ? load_val<DT>(row_ptr(a.tgt, DT, tb + n, a.tgt_ld), v) : -INFINITY;
-        build_corrections(c, K, act, v, w, lv);
+        build_corrections(c, K, act, v, w, act ? p_of(lv, c.cut, c.invT, c.kept) : 0.0);
       }
       __syncwarp();
       if (report) write_record(a, r, c);
@@ -867,7 +896,8 @@ static SampleArgs sample_args(const void* tgt_logits, int32_t dtype, int64_t tgt
 // sums grid, then the pick; dynamic LDS holds the mixture's branch tables
 template <int DT, int DDT, bool kDense, bool kAccept>
 static int32_t launch_draw_t(const SampleArgs& a, hipStream_t s) {
-  const size_t tables = kDense ? 0 : sizeof(int) * 2 * static_cast<size_t>(a.K) * a.b;
+  const size_t kb = static_cast<size_t>(a.K) * a.b;
+  const size_t tables = kDense ? 0 : sizeof(int) * ((kb + 1) & ~static_cast<size_t>(1)) + sizeof(double) * kb;
   const size_t dyn = tables > DLists<kDense>::kBytes ? tables : DLists<kDense>::kBytes;
   hipLaunchKernelGGL((k_draw_sums<DT, DDT, kDense, kAccept>), dim3(a.R * a.S), dim3(kSumNT), dyn, s, a);
   if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
