@@ -218,3 +218,41 @@ def pack_rows_device(full: torch.Tensor, L: np.ndarray, rows_per_req: int, out: 
     n = len(idx)
     torch.index_select(full, 0, torch.from_numpy(idx).to(full.device), out=out[:n])
     return out
+
+
+def pack_rows_by_offsets(full: torch.Tensor, tgt_off: torch.Tensor, rows_per_req: int, out: torch.Tensor,
+                         slots: torch.Tensor) -> torch.Tensor:
+    """Device-side stand-in for the target forward over the packed slots (not
+    part of verification): slot k of `out` receives row r*rows_per_req + j of
+    `full`, where r is the request whose range [tgt_off[r], tgt_off[r+1])
+    holds k and j = k - tgt_off[r].  The offsets are read on the device only,
+    so the copy can sit in a captured graph behind dvl_alloc_pack; slots past
+    tgt_off[R] receive a copy of the last request's last row and are never
+    read.  `slots` is arange(out.shape[0]) as int32 on the device."""
+    R = tgt_off.numel() - 1
+    r = torch.searchsorted(tgt_off[1:], slots, right=True).clamp_(max=R - 1)
+    j = (slots.long() - tgt_off[r].long()).clamp_(0, rows_per_req - 1)
+    torch.index_select(full, 0, r * rows_per_req + j, out=out)
+    return out
+
+
+def capture_graph(fn, warmup: int = 1) -> torch.cuda.CUDAGraph:
+    """Record the launches `fn` makes on torch's current stream into a HIP graph.
+    `fn` is run `warmup` times eagerly on a side stream first (torch's own lazy
+    set-up must not happen under capture).  Every libsv call takes its per-step
+    values (seed, budget, offsets, lengths, temperatures, top-p, tokens) from
+    device memory, so one graph serves every step whose inputs are written to
+    the same addresses before `replay()`.  The graph records raw addresses:
+    `fn` (and so every buffer its closure holds) is kept alive as
+    `graph.recorded_fn` for as long as the graph is."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(warmup):
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    g.recorded_fn = fn
+    return g

@@ -51,6 +51,50 @@ def gpu_step_runner(w: synth.Workload, device="cuda", two_streams: bool = False,
     return vs, run
 
 
+def gpu_graph_runner(w: synth.Workload, device="cuda"):
+    """The whole step captured once as a HIP graph over fixed-address buffers:
+    dvl_alloc_pack (with a budget), a device-side packing of the target rows
+    by the new offsets (the target forward's stand-in), and the fused
+    verification calls.  Returns (VerifyStep, graph, run(s) -> results), where
+    run(s) writes step s's inputs to the fixed addresses eagerly and replays."""
+    import torch
+
+    from draft_verification_sv_amd.step import (VerifyStep, capture_graph, pack_rows_by_offsets, row_pitch,
+                                                to_device_rows)
+
+    R, b, V, K = w.R, w.b, w.V, w.K
+    ld = row_pitch(V, w.dtype)
+    max_pos = min(w.budget, R * b) if w.budget is not None else R * b
+    vs = VerifyStep(R=R, b=b, V=V, dtype=w.dtype, K=K, max_pos=max_pos, device=device, diagnostics=True)
+    full = to_device_rows(w.tgt, ld, device)
+    packed = torch.empty((vs.max_rows, ld), dtype=full.dtype, device=device)
+    slots = torch.arange(vs.max_rows, dtype=torch.int32, device=device)
+    draft = to_device_rows(w.draft, ld, device) if K == 0 else None
+    comp = to_device_rows(w.comp, ld, device) if K > 0 else None
+
+    def set_step(s: int):
+        vs.set_inputs(T=w.T, x=w.x[s], seed=int(w.seeds[s]), top_p=w.top_p, mix=w.mix,
+                      a=None if w.a is None else w.a[s], budget=w.budget)
+        if w.budget is None:
+            vs.set_full_verification()
+
+    def body():
+        if w.budget is not None:
+            vs.run_dvl()
+        pack_rows_by_offsets(full, vs.tgt_off, b + 1, packed, slots)
+        vs.run_verify(packed, ld, draft=draft, draft_ld=ld, comp=comp, comp_ld=ld, fused=True)
+
+    set_step(0)
+    graph = capture_graph(body)
+
+    def run(s: int) -> dict:
+        set_step(s)
+        graph.replay()
+        return vs.results()
+
+    return vs, graph, run
+
+
 def oracle_step(w: synth.Workload, s: int) -> dict:
     R, b, V, K = w.R, w.b, w.V, w.K
     if w.budget is not None:

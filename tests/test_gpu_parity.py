@@ -7,7 +7,7 @@ import pytest
 
 import oracle
 import synth
-from harness import assert_rate, compare_step, gpu_step_runner, oracle_step
+from harness import assert_rate, compare_step, gpu_graph_runner, gpu_step_runner, oracle_step
 
 pytestmark = pytest.mark.gpu
 
@@ -319,3 +319,85 @@ def test_determinism_repeat_runs():
     b = run(0)
     for k in a:
         assert np.array_equal(np.asarray(a[k]).view(np.uint8), np.asarray(b[k]).view(np.uint8)), k
+
+
+# ---------------------------------------------------------------- whole step in a HIP graph
+GRAPH = [(3, dict(V=2053, R=8, steps=4)), (5, dict(V=4099, R=8, steps=4)), (4, dict(V=4099, R=4, steps=2)),
+         (2, dict(V=2053, R=4, steps=2)), (5, dict(steps=4))]
+
+
+def _same_bits(a: dict, b: dict):
+    """Bitwise equality over the entries a step defines (positions i < L_r,
+    packed rows below tgt_off[R], draft rows below pos_off[R]); the rest keep
+    whatever earlier steps left there."""
+    L = a["L"]
+    assert np.array_equal(L, b["L"]), "L"
+    n_rows, n_pos = int(a["tgt_off"][-1]), int(a["pos_off"][-1])
+    pos_mask = np.arange(a["u_acc"].shape[1])[None, :] < L[:, None]
+    for k in a:
+        x, y = np.asarray(a[k]), np.asarray(b[k])
+        if k.startswith("row_"):
+            x, y = x[:n_rows], y[:n_rows]
+        elif k.startswith("d_"):
+            x, y = x[:n_pos], y[:n_pos]
+        elif k in ("p_x", "q_x", "u_acc", "q_at_draft"):
+            x, y = x[pos_mask], y[pos_mask]
+        elif k == "post_w":
+            x, y = x[pos_mask], y[pos_mask]
+        elif k == "branch_tok":
+            x, y = x.transpose(0, 2, 1)[pos_mask], y.transpose(0, 2, 1)[pos_mask]
+        assert np.array_equal(x.view(np.uint8), y.view(np.uint8)), k
+
+
+@pytest.mark.parametrize("c,kw", GRAPH, ids=[f"cfg{c}-" + "-".join(f"{k}{v}" for k, v in kw.items()) for c, kw in GRAPH])
+def test_graph_replay_matches_eager_and_oracle(c, kw):
+    """One captured graph (DVL, device-side packing by the new offsets, the
+    verification calls) replayed for several steps whose inputs are written to
+    the same addresses: every replay equals the eager run bit for bit and
+    passes the oracle comparison, with unrelated eager work and
+    synchronisations between replays."""
+    import torch
+
+    w = synth.config(c, **kw)
+    banner(f"graph capture {w.name} V={w.V} R={w.R}")
+    _, _, run_graph = gpu_graph_runner(w)
+    _, run_eager = gpu_step_runner(w, fused=True)
+    order = [s % w.steps for s in (1, 0, 2, 3, 1)]
+    rep = None
+    lengths = set()
+    for s in order:
+        banner(f"graph replay {w.name} step {s}")
+        g = run_graph(s)
+        noise = torch.randn(1 << 20, device="cuda")
+        float((noise * noise).sum())
+        torch.cuda.synchronize()
+        _same_bits(g, run_eager(s))
+        rep = compare_step(w, g, oracle_step(w, s), rep)
+        lengths.add(tuple(g["L"].tolist()))
+    assert_rate(rep)
+    if w.budget is not None and w.steps > 1:
+        assert len(lengths) > 1, "the steps should change the DVL boundaries"
+
+
+@pytest.mark.parametrize("c,kw", [(5, dict(V=4099, R=8, steps=3)), (3, dict(V=2053, R=16, steps=2)), (5, dict(steps=2))],
+                         ids=["cfg5-small", "cfg3-small", "cfg5-full"])
+def test_graph_replay_budget_changes(c, kw):
+    """The verification budget sits at a fixed device address: one graph
+    captured at budget B (its capacity) replays at other budgets, down to 0
+    (every request then emits one token from its first target row), without
+    recapture; each replay matches the eager run and the oracle."""
+    w = synth.config(c, **kw)
+    B = w.budget
+    banner(f"graph budgets {w.name} V={w.V} R={w.R} capacity {B}")
+    _, _, run_graph = gpu_graph_runner(w)
+    _, run_eager = gpu_step_runner(w, fused=True)
+    rep = None
+    for k, budget in enumerate([B // 2, 0, B, 1, B - 3, w.R]):
+        s = k % w.steps
+        w.budget = budget
+        banner(f"graph replay {w.name} step {s} budget {budget}")
+        g = run_graph(s)
+        _same_bits(g, run_eager(s))
+        assert int(g["pos_off"][-1]) == min(budget, w.R * w.b)
+        rep = compare_step(w, g, oracle_step(w, s), rep)
+    assert_rate(rep)
