@@ -5,7 +5,9 @@ concurrency 32, block 16, Qwen3 vocabulary V = 151936, bf16 target logits,
 K = 8 latent-mixture draft with greedy branches, DVL budget 256 (half of
 32 x 16) from Beta(8, 2) survival estimates, T = 1.0, top-p 0.95, residual
 and bonus sampling, Philox seeds advancing per step.  Synthetic seeded data
-(synth.config(5)).
+(synth.config(5)).  With --branch-T T_b > 0 the same workload runs with the
+soft-branch drafter (each branch softmax(c / T_b)), a variant measured
+beside the headline line.
 
 A timed step is the whole verification path on inputs resident in HBM:
 dvl_alloc_pack, sv_verify_rows (target-row statistics with top-p and the
@@ -41,6 +43,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the CPU-oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--branch-T", type=float, default=0.0,
+                    help="soft-branch mixture: the drafter samples each branch from softmax(c / T_b) and "
+                         "verification uses those branch distributions (0: greedy branches, the default)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before the steps, one elementwise kernel that reads and writes MIB MiB: "
                          "the known-size reference that scales the HBM counters")
@@ -153,7 +158,9 @@ def main():
     torch.cuda.set_device(dev)
     S = args.steps
     t_gen = time.time()
-    w = synth.config(5, steps=S)
+    bT = args.branch_T
+    soft = bT > 0
+    w = synth.config(5, steps=S, branch_T=bT)
     R, b, V, K, B = w.R, w.b, w.V, w.K, w.budget
     print(f"[bench] data generated in {time.time() - t_gen:.1f}s: {w.name}", file=sys.stderr, flush=True)
     ld = row_pitch(V, "bf16")
@@ -171,6 +178,7 @@ def main():
     T = torch.from_numpy(w.T).to(dev)
     top_p = torch.from_numpy(w.top_p).to(dev)
     budget = torch.tensor([B], dtype=torch.int32, device=dev)
+    branch_T = torch.full((R,), bT, dtype=torch.float32, device=dev) if soft else None
 
     i32, f32, f64 = torch.int32, torch.float32, torch.float64
     z = lambda n, t: torch.zeros(n, dtype=t, device=dev)  # noqa: E731
@@ -209,12 +217,13 @@ def main():
             ev[0].record(stream)
         # target rows (statistics, top-p) and component rows (branch argmax) in one launch
         sv.sv_verify_rows(packed[s], dt, ld, V, tgt_off, R, max_rows, T, top_p, row_max, row_arg, row_lse, row_cut,
-                          row_kept, comp, ld, K, b, pos_off, max_pos, ws, nb, sp)
+                          row_kept, comp, ld, K, b, pos_off, max_pos, branch_T, ws, nb, sp)
         if ev is not None:
             ev[1].record(stream)
         # category posterior, acceptance, residual / bonus draw
         sv.sv_accept_sample(packed[s], dt, ld, V, tgt_off, pos_off, R, b, T, row_arg, row_cut, row_kept, x_all[s],
-                            sv.SV_Q_MIXTURE, None, dt, 0, None, None, K, mix, branch_tok, post_w, q_at,
+                            sv.SV_Q_MIXTURE, None, dt, 0, None, None, K, mix, comp if soft else None,
+                            ld if soft else 0, branch_T, branch_tok, post_w, q_at,
                             seeds[s:s + 1], n_acc, token, is_bonus, None, None, None, ws, nb, sp)
 
     for k in range(args.warmup):
@@ -232,17 +241,23 @@ def main():
 
     # ---- dominant kernel, timed with HIP events on the kernels' stream
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(S)]
+    nacc_hist = torch.zeros((S, R), dtype=torch.int32, device=dev)  # per-step accepted lengths (untimed pass)
     for s in range(S):
         step(s, evs[s])
+        nacc_hist[s].copy_(n_acc)
     torch.cuda.synchronize()
+    rejected = (nacc_hist.cpu().numpy() < L_host).sum(axis=1)  # requests drawing a residual, per step
     mix_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
     row_bytes = V * 2
     # algorithmic bytes of the dominant launch: every target row (L_r + 1 per request)
     # and every verified position's K component rows, each read once
     mix_bytes = float(np.mean((positions + R) * row_bytes + positions * K * row_bytes))
     achieved = mix_bytes / (mix_ms * 1e-3) / 1e9
-    # step-aggregate algorithmic bytes: target rows, component rows, one sampled row per request
+    # step-aggregate algorithmic bytes: target rows, component rows, one sampled row per request (soft
+    # branches: a residual also reads the K branch rows of its slot)
     step_bytes = (positions + R) * row_bytes + positions * K * row_bytes + R * row_bytes
+    if soft:
+        step_bytes = step_bytes + rejected * K * row_bytes
     ms_per_step = elapsed / S * 1e3
     value = float(positions.sum()) / elapsed
 
@@ -250,7 +265,8 @@ def main():
     if not args.no_cpu:
         cpu = cpu_baseline(w, args.cpu_seconds)
 
-    traffic = load_traffic(ROWS_KERNEL)
+    traffic = None if soft else load_traffic(ROWS_KERNEL)
+    mixture = f"K8 soft-branch mixture T_b {bT:g}" if soft else "K8 greedy-branch mixture"
     out = {
         "metric": "verified draft positions/sec at V=151936, conc 32; % of peak HBM GB/s",
         "value": round(value, 1),
@@ -264,12 +280,13 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded Zipfian logits, Beta(8,2) survival estimates)",
-        "config": {"workload": "conc32 block16 V151936 bf16, K8 greedy-branch mixture, DVL budget 256, "
+        "config": {"workload": f"conc32 block16 V151936 bf16, {mixture}, DVL budget 256, "
                                "T1.0 top-p0.95, residual+bonus, seeds advancing per step",
-                   "requests": R, "block": b, "vocab": V, "K": K, "budget": B},
+                   "requests": R, "block": b, "vocab": V, "K": K, "budget": B,
+                   **({"branch_T": bT} if soft else {})},
         "step_gbps": round(float(np.mean(step_bytes)) / (ms_per_step * 1e-3) / 1e9, 1),
         "step_frac_of_peak": round(float(np.mean(step_bytes)) / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-        "roofline": {"kernel": "k_rows_mix (sv_verify_rows)", "bound": "hbm", "achieved": round(achieved, 1),
+        "roofline": {"kernel": "k_rows_mix (sv_verify_rows" + (", soft branches)" if soft else ")"), "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": traffic, "avg_launch_us": round(mix_ms * 1e3, 2),
                      "algorithmic_bytes_per_launch": mix_bytes},
@@ -295,7 +312,7 @@ def cpu_baseline(w, seconds: float):
     while n < w.steps:
         dv = oracle.dvl(w.a[n], w.budget)
         oracle.step(tgt=tgt, tgt_row0=np.arange(R) * (b + 1), L=dv["L"], T=w.T, x=w.x[n], seed=int(w.seeds[n]),
-                    top_p=w.top_p, comp=comp, comp_row0=np.arange(R) * K * b, mix=w.mix)
+                    top_p=w.top_p, comp=comp, comp_row0=np.arange(R) * K * b, mix=w.mix, branch_T=w.branch_T)
         pos += int(dv["L"].sum())
         n += 1
         if time.perf_counter() - t0 > seconds:

@@ -66,9 +66,10 @@ _SIGS = {
                            _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "sv_philox_uniforms": [_vp, _i32, _i32, _vp, _vp],
     "sv_verify_rows": [_vp, _i32, _i64, _i32, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32,
-                       _i32, _vp, _i32, _vp, _sz, _vp],
+                       _i32, _vp, _i32, _vp, _vp, _sz, _vp],
     "sv_accept_sample": [_vp, _i32, _i64, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i64,
-                         _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+                         _vp, _vp, _i32, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                         _vp, _sz, _vp],
 }
 for _name, _args in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -174,24 +175,24 @@ def sv_mixture_q(comp_logits, dtype, ld, V, K, b, mix_logits, pos_off, R, max_po
 
 
 def sv_verify_rows(tgt_logits, dtype, tgt_ld, V, tgt_off, R, max_rows, temperature, top_p, row_max, row_argmax,
-                   row_lse, row_cut, row_kept_lse, comp_logits, comp_ld, K, b, pos_off, max_pos, ws, ws_bytes,
-                   stream=None):
+                   row_lse, row_cut, row_kept_lse, comp_logits, comp_ld, K, b, pos_off, max_pos, branch_T, ws,
+                   ws_bytes, stream=None):
     _check(_lib.sv_verify_rows(_p(tgt_logits), dtype, tgt_ld, V, _p(tgt_off), R, max_rows, _p(temperature),
                                _p(top_p), _p(row_max), _p(row_argmax), _p(row_lse), _p(row_cut), _p(row_kept_lse),
-                               _p(comp_logits), comp_ld, K, b, _p(pos_off), max_pos, _p(ws), ws_bytes,
+                               _p(comp_logits), comp_ld, K, b, _p(pos_off), max_pos, _p(branch_T), _p(ws), ws_bytes,
                                _stream(stream)), "sv_verify_rows")
 
 
 def sv_accept_sample(tgt_logits, dtype, tgt_ld, V, tgt_off, pos_off, R, b, temperature, row_argmax, row_cut,
                      row_kept_lse, draft_tok, q_mode, draft_logits, draft_dtype, draft_ld, draft_argmax, draft_lse, K,
-                     mix_logits, branch_tok, post_w, q_at_draft, seed, n_acc, token, is_bonus, p_out, q_out, u_out,
-                     ws, ws_bytes, stream=None):
+                     mix_logits, comp_logits, comp_ld, branch_T, branch_tok, post_w, q_at_draft, seed, n_acc, token,
+                     is_bonus, p_out, q_out, u_out, ws, ws_bytes, stream=None):
     _check(_lib.sv_accept_sample(_p(tgt_logits), dtype, tgt_ld, V, _p(tgt_off), _p(pos_off), R, b, _p(temperature),
                                  _p(row_argmax), _p(row_cut), _p(row_kept_lse), _p(draft_tok), q_mode,
                                  _p(draft_logits), draft_dtype, draft_ld, _p(draft_argmax), _p(draft_lse), K,
-                                 _p(mix_logits), _p(branch_tok), _p(post_w), _p(q_at_draft), _p(seed), _p(n_acc),
-                                 _p(token), _p(is_bonus), _p(p_out), _p(q_out), _p(u_out), _p(ws), ws_bytes,
-                                 _stream(stream)), "sv_accept_sample")
+                                 _p(mix_logits), _p(comp_logits), comp_ld, _p(branch_T), _p(branch_tok), _p(post_w),
+                                 _p(q_at_draft), _p(seed), _p(n_acc), _p(token), _p(is_bonus), _p(p_out), _p(q_out),
+                                 _p(u_out), _p(ws), ws_bytes, _stream(stream)), "sv_accept_sample")
 
 
 def sv_accept(tgt_logits, dtype, tgt_ld, V, tgt_off, pos_off, R, b, temperature, row_argmax, row_cut, row_kept_lse,

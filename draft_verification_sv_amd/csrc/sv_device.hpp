@@ -281,15 +281,20 @@ __host__ __device__ inline int res_chunks(int V) { return (sub_chunks(V) + kChun
 
 // What the draw of one request needs: written by the first chunk block of the
 // sums kernel, read by the pick kernel.
-enum : int32_t { kDrawResidual = 0, kDrawP = 1, kDrawGreedy = 2, kDrawNone = 3 };
+// kDrawResidual: norm(max(0, p - q)) with q a dense draft row or the point
+// masses of greedy branches (corrections at their tokens); kDrawSoft: q the
+// posterior-weighted sum of K soft branch rows; kDrawP: p (bonus, or T = 0
+// fallback); kDrawGreedy: the argmax; kDrawNone: malformed offsets.
+enum : int32_t { kDrawResidual = 0, kDrawP = 1, kDrawGreedy = 2, kDrawNone = 3, kDrawSoft = 4 };
 struct DrawRec {
   int32_t mode, n, bonus, token;  // token: the argmax when greedy
   int32_t ncorr, pad0;
-  int64_t trow, drow;  // target row of the draw; dense draft row (residual)
+  int64_t trow, drow;  // target row of the draw; dense draft row, or branch 0's row (soft)
   float cut, pad1;
   double invT, kept, dlse;
-  int32_t ctok[64];  // mixture residual: the distinct branch tokens at the slot
-  double cw[64];     // and their draw weight max(0, p - q)
+  double invTb;      // soft branches: 1 / T_b
+  int32_t ctok[64];  // greedy-branch residual: the distinct branch tokens at the slot
+  double cw[64];     // and their draw weight max(0, p - q); soft: lse_z - log w_z per branch z
 };
 
 // ------------------------------------------------------------------ branch argmax parts
@@ -307,11 +312,12 @@ __device__ __host__ inline uint32_t argmax_token(uint64_t key) {
 // ------------------------------------------------------------------ workspace layout
 // [status word, 256 B][draw records, R][sub-chunk sums, R * NSUB * 2 doubles]
 // [branch argmax parts, R * K * b * kMixParts keys]
+// [soft branch rows, R * K * b each: lse (double), argmax (int32), max (float)]
 // Cross-block results travel through kernel boundaries (stream order), not
 // through in-kernel fences: a device-scope release on gfx950 writes back the
 // L2, which is far too costly to pay once per block.
 struct WsLayout {
-  size_t status, rec, sub, bkey, total;
+  size_t status, rec, sub, bkey, blse, barg, bmax, total;
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -322,7 +328,11 @@ __host__ __device__ inline WsLayout ws_layout(int R, int b, int K, int V) {
   l.rec = 256;
   l.sub = l.rec + align256(sizeof(DrawRec) * static_cast<size_t>(R));
   l.bkey = l.sub + align256(sizeof(double) * 2 * static_cast<size_t>(R) * sub_chunks(V));
-  l.total = l.bkey + align256(sizeof(uint64_t) * static_cast<size_t>(R) * K * b * kMixParts);
+  const size_t kb = static_cast<size_t>(R) * K * b;
+  l.blse = l.bkey + align256(sizeof(uint64_t) * kb * kMixParts);
+  l.barg = l.blse + align256(sizeof(double) * kb);
+  l.bmax = l.barg + align256(sizeof(int32_t) * kb);
+  l.total = l.bmax + align256(sizeof(float) * kb);
   return l;
 }
 

@@ -1,4 +1,5 @@
-// sv_mix.hip -- latent-mixture proposal with greedy branches.
+// sv_mix.hip -- latent-mixture proposal: branch statistics and the category
+// posterior.
 //
 // "Pith review of DBLAST", "What carries the argument": the block proposal is
 // q_dep(x_1:b | y) = sum_z q(z|y) prod_i q_i(x_i | y, z); at inference a
@@ -18,6 +19,12 @@
 // wave and the block.  One block per row needs no cross-block merge.
 // k_mix_post: one wave per request runs the posterior recursion over the
 // positions with one lane per category (K <= 64), in double.
+//
+// Soft branches (same review, "What carries the argument": each branch is a
+// distribution q_i(. | y, z); here softmax(c / T_b)): the fused rows launch
+// gives every component row one block that forms lse(c / T_b), argmax and
+// maximum with the target rows' exact-histogram code; the draw kernels form
+// the posterior from them (sv_sample.hip).
 #include <math.h>
 
 #include "sv_device.hpp"
@@ -43,6 +50,10 @@ struct MixArgs {
   double* post_w;
   double* q;
   uint32_t* status;
+  const float* branch_T;  // soft branches: temperature per request (device), else NULL
+  double* blse;           // soft branches: lse of c / T_b per component row [R*K*b]
+  int32_t* barg;          // soft branches: argmax per component row
+  float* bmax;            // soft branches: maximum per component row
 };
 
 // Order-preserving key of a float with -0 folded onto +0.
@@ -164,6 +175,45 @@ __device__ __forceinline__ void mix_block(const MixArgs& a, int m, int part, uin
   }
 }
 
+// Soft branches: statistics of component row m = p*K + z (position p, category
+// z) at its request's branch temperature T_b, by one block, with the target
+// rows' code: lse of c / T_b, argmax and maximum (T_b = 0: argmax and maximum).
+template <int DT, int NT, int BATCH>
+__device__ __forceinline__ void soft_block(const MixArgs& a, int m, uint32_t* hist, RowShared<NT>& sh) {
+  const int tid = threadIdx.x;
+  const int z = m % a.K;
+  const int p = m / a.K;
+  const int total = a.pos_off[a.R];
+  if (m == 0 && tid == 0 && (a.pos_off[0] != 0 || total > a.max_pos || total < 0))
+    raise_status(a.status, SV_ST_BAD_OFFSETS);
+  if (p >= total) return;
+  const int r = find_request<NT>(a.pos_off, a.R, p, &sh.req);
+  if (r < 0) {
+    if (tid == 0) raise_status(a.status, SV_ST_BAD_OFFSETS);
+    return;
+  }
+  const int i = p - a.pos_off[r];
+  if (i >= a.b) {
+    if (tid == 0) raise_status(a.status, SV_ST_BAD_OFFSETS);
+    return;
+  }
+  const size_t esz = DT == SV_BF16 ? 2 : 4;
+  const int64_t row = (static_cast<int64_t>(r) * a.K + z) * a.b + i;
+  const char* rowp = static_cast<const char*>(a.comp) + static_cast<size_t>(row) * static_cast<size_t>(a.ld) * esz;
+  const float Tb = a.branch_T[r];
+  if (tid == 0 && !(Tb >= 0.0f)) raise_status(a.status, SV_ST_BAD_TEMPERATURE);
+  RowArgs ca{};
+  ca.logits = a.comp;
+  ca.ld = a.ld;
+  ca.V = a.V;
+  ca.R = a.R;
+  ca.row_max = a.bmax;
+  ca.row_argmax = a.barg;
+  ca.row_lse = a.blse;
+  ca.status = a.status;
+  row_stats_at<DT, NT, BATCH>(ca, rowp, static_cast<int>(row), Tb, 1.0f, false, hist, sh);
+}
+
 template <int DT>
 __global__ __launch_bounds__(kMixNT) void k_mix_argmax(MixArgs a) {
   __shared__ uint64_t red[kMixNT / kWave];
@@ -182,7 +232,7 @@ __global__ __launch_bounds__(kMixNT) void k_mix_argmax(MixArgs a) {
 constexpr int kFusedNT = 256;
 constexpr int kFusedBatch = 4;
 
-template <int DT>
+template <int DT, bool kSoft>
 __global__ __launch_bounds__(kFusedNT) void k_rows_mix(RowArgs ra, MixArgs ma, int n_row_blocks) {
   __shared__ RowShared<kFusedNT> sh;
   __shared__ uint32_t hist[DT == SV_BF16 ? kHistWords : 1];
@@ -195,7 +245,10 @@ __global__ __launch_bounds__(kFusedNT) void k_rows_mix(RowArgs ra, MixArgs ma, i
     row_block<DT, kFusedNT, kFusedBatch>(ra, blk, hist, sh);
   } else {
     const int u = blk - n_row_blocks;
-    mix_block<DT, kFusedNT>(ma, u / kMixParts, u % kMixParts, sh.red_u64, &sh.req);
+    if constexpr (kSoft)
+      soft_block<DT, kFusedNT, kFusedBatch>(ma, u, hist, sh);
+    else
+      mix_block<DT, kFusedNT>(ma, u / kMixParts, u % kMixParts, sh.red_u64, &sh.req);
   }
 }
 
@@ -281,8 +334,8 @@ extern "C" int32_t sv_verify_rows(const void* tgt_logits, int32_t dtype, int64_t
                                   const int32_t* tgt_off, int32_t R, int32_t max_rows, const float* temperature,
                                   const float* top_p, float* row_max, int32_t* row_argmax, double* row_lse,
                                   float* row_cut, double* row_kept_lse, const void* comp_logits, int64_t comp_ld,
-                                  int32_t K, int32_t b, const int32_t* pos_off, int32_t max_pos, void* ws,
-                                  size_t ws_bytes, void* stream) {
+                                  int32_t K, int32_t b, const int32_t* pos_off, int32_t max_pos,
+                                  const float* branch_T, void* ws, size_t ws_bytes, void* stream) {
   if (!tgt_logits || !tgt_off || !temperature || !row_max || !row_argmax || !row_lse || !row_cut || !row_kept_lse)
     return SV_ERR_ARG;
   if (!comp_logits || !pos_off || !ws) return SV_ERR_ARG;
@@ -300,13 +353,28 @@ extern "C" int32_t sv_verify_rows(const void* tgt_logits, int32_t dtype, int64_t
   MixArgs ma{comp_logits, comp_ld, V, K, b, nullptr, pos_off, R, max_pos, nullptr, nullptr,
              reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + l.bkey), kMixParts, nullptr, nullptr,
              status_word(ws)};
-  const unsigned mix_blocks = static_cast<unsigned>(max_pos) * static_cast<unsigned>(K) * kMixParts;
+  const bool soft = branch_T != nullptr;
+  if (soft) {
+    ma.branch_T = branch_T;
+    ma.blse = reinterpret_cast<double*>(static_cast<char*>(ws) + l.blse);
+    ma.barg = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + l.barg);
+    ma.bmax = reinterpret_cast<float*>(static_cast<char*>(ws) + l.bmax);
+  }
+  // greedy branches: kMixParts blocks per component row; soft: one
+  const unsigned mix_blocks = static_cast<unsigned>(max_pos) * static_cast<unsigned>(K) * (soft ? 1u : kMixParts);
   const unsigned grid = static_cast<unsigned>(max_rows) + mix_blocks;
   if (grid == 0) return SV_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (dtype == SV_BF16)
-    hipLaunchKernelGGL(k_rows_mix<SV_BF16>, dim3(grid), dim3(kFusedNT), 0, s, ra, ma, max_rows);
-  else
-    hipLaunchKernelGGL(k_rows_mix<SV_F32>, dim3(grid), dim3(kFusedNT), 0, s, ra, ma, max_rows);
+  if (dtype == SV_BF16) {
+    if (soft)
+      hipLaunchKernelGGL((k_rows_mix<SV_BF16, true>), dim3(grid), dim3(kFusedNT), 0, s, ra, ma, max_rows);
+    else
+      hipLaunchKernelGGL((k_rows_mix<SV_BF16, false>), dim3(grid), dim3(kFusedNT), 0, s, ra, ma, max_rows);
+  } else {
+    if (soft)
+      hipLaunchKernelGGL((k_rows_mix<SV_F32, true>), dim3(grid), dim3(kFusedNT), 0, s, ra, ma, max_rows);
+    else
+      hipLaunchKernelGGL((k_rows_mix<SV_F32, false>), dim3(grid), dim3(kFusedNT), 0, s, ra, ma, max_rows);
+  }
   return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
 }

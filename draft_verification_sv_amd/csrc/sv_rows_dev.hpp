@@ -215,6 +215,10 @@ __device__ __forceinline__ double bin_mass(const uint32_t* hist, int d, double T
   return c ? static_cast<double>(c) * exp(static_cast<double>(bin_value(bin)) / Td - M) : 0.0;
 }
 
+template <int DT, int NT, int BATCH>
+__device__ __forceinline__ void row_stats_at(const RowArgs& a, const void* rowp, int p, float T, float tp, bool topp_on,
+                             uint32_t* hist, RowShared<NT>& sh);
+
 // Statistics of row p (work item p of the request found from row_off), by one
 // block of NT threads.  `hist` holds kHistWords words of LDS (bf16 rows only).
 template <int DT, int NT, int BATCH>
@@ -242,7 +246,15 @@ __device__ void row_block(const RowArgs& a, int p, uint32_t* hist, RowShared<NT>
     if (tid == 0) raise_status(a.status, SV_ST_BAD_TOP_P);
     tp = 1e-30f;  // keeps the top value only
   }
+  row_stats_at<DT, NT, BATCH>(a, rowp, p, T, tp, topp_on, hist, sh);
+}
 
+// Statistics of the row at `rowp` at temperature T (top-p cut when topp_on),
+// written to output slot p of a's arrays, by one block of NT threads.
+template <int DT, int NT, int BATCH>
+__device__ __forceinline__ void row_stats_at(const RowArgs& a, const void* rowp, int p, float T, float tp, bool topp_on,
+                             uint32_t* hist, RowShared<NT>& sh) {
+  const int tid = threadIdx.x;
   if constexpr (DT == SV_BF16) {
     for (int k = tid; k < kHistWords; k += NT) hist[k] = 0u;
     __syncthreads();

@@ -75,6 +75,11 @@ struct SampleArgs {
   int NSUB;      // sub-chunks per row
   int S;         // chunks per row
   uint32_t* status;
+  const void* comp;        // soft branches: component rows [R*K*b, comp_ld], target dtype
+  int64_t comp_ld;
+  const float* branch_T;   // soft branches: T_b per request
+  const double* blse;      // soft branches: lse(c / T_b) per component row (rows launch)
+  const int32_t* barg;     // soft branches: argmax per component row (rows launch)
 };
 
 __device__ __forceinline__ const char* row_ptr(const void* base, int dtype, int64_t row, int64_t ld) {
@@ -219,7 +224,7 @@ __global__ __launch_bounds__(kWave) void k_accept(SampleArgs a) {
 struct DrawCtx {
   int mode, n, bonus, token, ncorr;
   float cut;
-  double invT, kept, dlse;
+  double invT, kept, dlse, invTb;
   int64_t trow, drow;
   int ctok[64];
   double cp[64];  // p at ctok
@@ -293,6 +298,7 @@ __device__ __forceinline__ void write_record(const SampleArgs& a, int r, const D
   if (lane == 0) {
     d.mode = c.mode; d.n = c.n; d.bonus = c.bonus; d.token = c.token; d.ncorr = c.ncorr;
     d.trow = c.trow; d.drow = c.drow; d.cut = c.cut; d.invT = c.invT; d.kept = c.kept; d.dlse = c.dlse;
+    d.invTb = c.invTb;
   }
   if (lane < c.ncorr) {
     d.ctok[lane] = c.ctok[lane];
@@ -606,6 +612,7 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums(SampleArgs a) {
         c.trow = tb + n;
         c.drow = static_cast<int64_t>(r) * b + n;
         c.ncorr = 0;
+        c.invTb = 0.0;
       }
       __syncwarp();
       if (!kDense && !greedy && n < Lr) {
@@ -648,6 +655,7 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums(SampleArgs a) {
       c.trow = tb + n;
       c.drow = static_cast<int64_t>(r) * b + n;
       c.ncorr = 0;
+      c.invTb = 0.0;
     }
     if (mres && tid < K) {
       sh.tv[tid] = a.branch_tok[(static_cast<size_t>(r) * K + tid) * b + n];
@@ -672,12 +680,290 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums(SampleArgs a) {
   sub_sums<DT, DDT, kDense>(a, c, r, ch, reinterpret_cast<float*>(dyn));
 }
 
+// ------------------------------------------------------------------ soft branches
+// Branch z's distribution at position i is softmax(c_{z,i} / T_b) ("Pith review
+// of DBLAST", "What carries the argument": q_dep = sum_z q(z|y) prod_i
+// q_i(x_i | y, z)).  By Bayes' rule on the mixture the category posterior
+// before position i is proportional to q(z|y) prod_{j<i} q_j(x_j | z), carried
+// in logs and normalised per position; q(x_i | x_<i) = sum_z w_z q_i(x_i | z).
+// A rejection at j draws from norm(max(0, p_j - sum_z w_z q_j(. | z))), which
+// reads the K branch rows of slot j next to the target row.  A request with
+// T_b = 0 keeps point-mass branches at each row's argmax (the greedy residual).
+
+// p and the soft-residual weight of the 8 values of group g of the drawn row:
+// max(0, p(v) - sum_z exp(c_z(v) / T_b - off_z)), off_z = lse_z - log w_z
+// (+inf where w_z = 0); the branch sum is formed only where p(v) > 0.  Branch
+// z's row is crow0 + z * cstride bytes.
+template <int DT>
+__device__ __forceinline__ void soft_group(const SampleArgs& a, const char* trowp, const char* crow0, size_t cstride,
+                                           const double* off, int g, float cut, double invT, double kept,
+                                           double invTb, double p8[8], double w8[8]) {
+  const int V = a.V, NG = groups_of(V), K = a.K;
+  const int gc = min(g, NG - 1);
+  uint4 t0, t1;
+  raw8<DT>(trowp, gc, V, t0, t1);
+  float l[8];
+  decode8<DT>(t0, t1, g, V, g < NG, l);
+  double q8[8];
+  bool any = false;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    p8[q] = l[q] > -INFINITY ? p_of(l[q], cut, invT, kept) : 0.0;
+    q8[q] = 0.0;
+    any |= p8[q] > 0.0;
+  }
+  if (any) {
+    for (int z0 = 0; z0 < K; z0 += 4) {  // four branch rows' loads in flight at a time
+      uint4 c0[4], c1[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) raw8<DT>(crow0 + cstride * min(z0 + j, K - 1), gc, V, c0[j], c1[j]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const double o = off[min(z0 + j, K - 1)];
+        if (z0 + j < K && o < INFINITY) {
+          float cv[8];
+          unpack8<DT>(c0[j], c1[j], cv);
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            if (p8[q] > 0.0) q8[q] += exp(static_cast<double>(cv[q]) * invTb - o);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const double t = p8[q] - q8[q];
+    w8[q] = t > 0.0 ? t : 0.0;
+  }
+}
+
+// D (soft residual): sums of p and of the draw weight over the sub-chunks of
+// chunk ch, one group per lane, one sub-chunk at a time per wave.
+template <int DT>
+__device__ __forceinline__ void sub_sums_soft(const SampleArgs& a, const DrawCtx& c, int r, int ch) {
+  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+  const char* trowp = row_ptr(a.tgt, DT, c.trow, a.tgt_ld);
+  const char* crow0 = row_ptr(a.comp, DT, c.drow, a.comp_ld);
+  const size_t cstride = static_cast<size_t>(a.b) * static_cast<size_t>(a.comp_ld) * (DT == SV_BF16 ? 2 : 4);
+  const int sub0 = ch * kChunkSubs + wv;
+  for (int k = 0; k < kSubPerWave; ++k) {
+    const int sub = sub0 + k * (kSumNT / kWave);
+    if (sub >= a.NSUB) break;  // wave-uniform
+    double p8[8], w8[8];
+    soft_group<DT>(a, trowp, crow0, cstride, c.cw, sub * kSubG + lane, c.cut, c.invT, c.kept, c.invTb, p8, w8);
+    double sp = 0.0, sw = 0.0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      sp += p8[q];
+      sw += w8[q];
+    }
+    const double tp = wave_sum_f64(sp), tw = wave_sum_f64(sw);
+    if (lane == 0) {
+      double* pp = a.sub + (static_cast<size_t>(r) * a.NSUB + sub) * 2;
+      pp[0] = tw;
+      pp[1] = tp;
+    }
+  }
+}
+
+// Dynamic LDS of the soft tail: branch argmax [K][b] (int), log q_i(x_i | z)
+// [K][b] and the unnormalised log posterior [b + 1][K] (double); D's lists
+// reuse it.
+constexpr long long kSoftMaxKb = 2048;  // K * b bound of the soft tail (its tables stay below 48 KB)
+
+__host__ __device__ inline size_t soft_tables_bytes(int K, int b) {
+  const size_t kb = static_cast<size_t>(K) * b;
+  return sizeof(int) * ((kb + 1) & ~static_cast<size_t>(1)) + sizeof(double) * kb +
+         sizeof(double) * static_cast<size_t>(b + 1) * K;
+}
+
+// The fused tail with soft branches (one block per (request, chunk)): A and B
+// load the header, the draft tokens, the mixing logits, the branch argmax and
+// lse of the rows launch and every branch's logit at the draft tokens; C (wave
+// 0) runs the posterior and the acceptance tests; D sums the drawn row.
+template <int DT>
+__global__ __launch_bounds__(kSumNT) void k_draw_sums_soft(SampleArgs a) {
+  __shared__ TailShared sh;
+  extern __shared__ __align__(16) int dyn[];
+  const int K = a.K, b = a.b, V = a.V, kb = K * b;
+  int* g = dyn;
+  double* lq = reinterpret_cast<double*>(dyn + ((kb + 1) & ~1));
+  double* S = lq + kb;
+  const int r = blockIdx.x / a.S, ch = blockIdx.x % a.S;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+  const bool report = ch == 0;
+  DrawCtx& c = sh.c;
+  const size_t bbase = static_cast<size_t>(r) * kb;  // component row (r, z, i) = bbase + z * b + i
+
+  // A. header, draft tokens, mixing logits, branch argmax
+  const int pb = a.pos_off[r], pe = a.pos_off[r + 1], tb = a.tgt_off[r], te = a.tgt_off[r + 1];
+  const float T = a.T[r], Tb = a.branch_T[r];
+  const int x0 = a.x[static_cast<size_t>(r) * b + min(tid, b - 1)];
+  const float m0 = a.mix[static_cast<size_t>(r) * K + min(tid, K - 1)];
+  for (int k = tid; k < kb; k += kSumNT) g[k] = a.barg[bbase + k];
+  if (tid < b) sh.x[tid] = x0;
+  if (tid < K) sh.mix[tid] = m0;
+  __syncthreads();
+  const int Lr = pe - pb;
+  if (!(Lr >= 0 && Lr <= b && te - tb == Lr + 1)) {
+    if (report && tid == 0) {
+      raise_status(a.status, SV_ST_BAD_OFFSETS);
+      a.n_acc[r] = 0;
+      a.rec[r].mode = kDrawNone;
+    }
+    return;
+  }
+  const bool greedy = T == 0.0f, softb = Tb > 0.0f;
+  const double invT = 1.0 / static_cast<double>(T), Tbd = static_cast<double>(Tb);
+
+  // B. candidate rows' statistics; log q_i(x_i | z) for i < L_r; log q(z | y)
+  const int is = min(tid, Lr);
+  const float rc0 = a.row_cut[tb + is];
+  const double rk0 = a.row_kept[tb + is];
+  const int ra0 = a.row_argmax[tb + is];
+  if (tid <= Lr) {
+    sh.rc[tid] = rc0;
+    sh.rk[tid] = rk0;
+    sh.ra[tid] = ra0;
+  }
+  for (int k = tid; k < K * Lr; k += kSumNT) {
+    const int z = k / Lr, i = k - z * Lr;
+    const int xv = sh.x[i];
+    double v = -INFINITY;
+    if (xv >= 0 && xv < V) {
+      const size_t row = bbase + static_cast<size_t>(z) * b + i;
+      if (softb)
+        v = static_cast<double>(load_val<DT>(row_ptr(a.comp, DT, static_cast<int64_t>(row), a.comp_ld), xv)) / Tbd -
+            a.blse[row];
+      else
+        v = g[z * b + i] == xv ? 0.0 : -INFINITY;
+    }
+    lq[z * b + i] = v;
+  }
+  if (wv == 1) {  // log q(z | y), q(z | y) = softmax of the mixing logits
+    const bool act = lane < K;
+    const float ml = act ? sh.mix[lane] : -INFINITY;
+    const float mmax = wave_max_f32(ml);
+    const double e = act ? exp(static_cast<double>(ml) - static_cast<double>(mmax)) : 0.0;
+    const double lsum = log(wave_sum_f64(e));
+    sh.pi[lane] = act ? (static_cast<double>(ml) - static_cast<double>(mmax)) - lsum : -INFINITY;
+  }
+  const uint64_t seed = *a.seed;
+  double p = 0.0, u = 0.0;
+  bool xok = true;
+  if (tid < kWave) {  // lane i < L_r: p(x_i) and u_i (word 0)
+    u = u24(philox_at(seed, static_cast<uint32_t>(lane), static_cast<uint32_t>(r)).x);
+    if (lane < Lr) {
+      const int xv = sh.x[lane];
+      xok = xv >= 0 && xv < V;
+      if (xok)
+        p = greedy ? (xv == ra0 ? 1.0 : 0.0)
+                   : p_of(load_val<DT>(row_ptr(a.tgt, DT, tb + lane, a.tgt_ld), xv), rc0, invT, rk0);
+      else if (report)
+        raise_status(a.status, SV_ST_BAD_TOKEN);
+    }
+  }
+  __syncthreads();
+  // running log posterior, in position order: lane z of wave 0
+  if (tid < K) {
+    double run = sh.pi[tid];
+    S[tid] = run;
+    for (int i = 0; i < Lr; ++i) {
+      run += lq[tid * b + i];
+      S[(i + 1) * K + tid] = run;
+    }
+  }
+  if (report && wv >= 1)  // the branch argmax, i < L_r
+    for (int k = tid - kWave; k < kb; k += kSumNT - kWave)
+      if (k % b < Lr) a.branch_out[bbase + k] = g[k];
+  __syncthreads();
+
+  // C. acceptance and the draw context (wave 0)
+  if (tid < kWave) {
+    // lane i: w_z^(i) = exp(S_iz - M) / sum, q(x_i | x_<i) = sum_z w_z exp(lq_zi)
+    const int il = min(lane, Lr);
+    const double* Si = S + static_cast<size_t>(il) * K;
+    double M = -INFINITY;
+    for (int z = 0; z < K; ++z) M = fmax(M, Si[z]);
+    double tot = 0.0;
+    if (M > -INFINITY)
+      for (int z = 0; z < K; ++z) tot += exp(Si[z] - M);
+    double q = 0.0;
+    if (lane < Lr && M > -INFINITY) {
+      for (int z = 0; z < K; ++z) {
+        const double w = exp(Si[z] - M) / tot;
+        const double l = lq[z * b + lane];
+        if (w != 0.0 && l > -INFINITY) q += w * exp(l);
+      }
+    }
+    if (lane < Lr && !xok) q = 0.0;
+    const bool pos = lane < Lr;
+    bool reject = false;
+    if (pos) {
+      reject = !(q > 0.0 ? u < p / q : p > 0.0);
+      if (report) {
+        const size_t k = static_cast<size_t>(r) * b + lane;
+        if (a.p_out) a.p_out[k] = p;
+        if (a.q_out) a.q_out[k] = q;
+        if (a.u_out) a.u_out[k] = static_cast<float>(u);
+        a.q_at_draft[k] = q;
+        double* pw = a.post_w + k * K;
+        for (int z = 0; z < K; ++z) pw[z] = M > -INFINITY ? exp(Si[z] - M) / tot : 0.0;
+        if (!(M > -INFINITY)) raise_status(a.status, SV_ST_EMPTY_POSTERIOR);
+      }
+    }
+    const uint64_t mask = __ballot(reject);
+    const int n = mask ? __ffsll(static_cast<long long>(mask)) - 1 : Lr;
+    if (report && lane == 0) a.n_acc[r] = n;
+    const bool res = !greedy && n < Lr;
+    if (lane == 0) {
+      c.n = n;
+      c.bonus = n == Lr ? 1 : 0;
+      c.mode = greedy ? kDrawGreedy : (n == Lr ? kDrawP : (softb ? kDrawSoft : kDrawResidual));
+      c.token = sh.ra[n];
+      c.cut = sh.rc[n];
+      c.kept = sh.rk[n];
+      c.invT = invT;
+      c.dlse = 0.0;
+      c.invTb = softb ? 1.0 / Tbd : 0.0;
+      c.trow = tb + n;
+      c.drow = static_cast<int64_t>(bbase) + n;  // branch 0's row at slot n; branch z: + z * b
+      c.ncorr = 0;
+    }
+    if (res && lane == n)  // the posterior at the draw slot, one weight per branch
+      for (int z = 0; z < K; ++z) sh.tw[z] = M > -INFINITY ? exp(Si[z] - M) / tot : 0.0;
+    __syncwarp();
+    if (res) {
+      const bool in = lane < K;
+      const double w = in ? sh.tw[lane] : 0.0;
+      if (softb) {
+        const double bl = in ? a.blse[bbase + static_cast<size_t>(lane) * b + n] : 0.0;
+        if (in) c.cw[lane] = w > 0.0 ? bl - log(w) : INFINITY;
+        if (lane == 0) c.ncorr = K;
+      } else {
+        const int v = in ? g[lane * b + n] : -1;
+        const bool act = in && w > 0.0 && v >= 0 && v < V;
+        const float lv = act ? load_val<DT>(row_ptr(a.tgt, DT, tb + n, a.tgt_ld), v) : -INFINITY;
+        build_corrections(c, K, act, v, w, act ? p_of(lv, sh.rc[n], invT, sh.rk[n]) : 0.0);
+      }
+    }
+    __syncwarp();
+    if (report) write_record(a, r, c);
+  }
+  __syncthreads();  // also ends every use of the tables, which D's lists overwrite
+  if (c.mode == kDrawGreedy) return;
+  if (c.mode == kDrawSoft)
+    sub_sums_soft<DT>(a, c, r, ch);
+  else
+    sub_sums<DT, DT, false>(a, c, r, ch, reinterpret_cast<float*>(dyn));
+}
+
 // The draw: one wave per request, after the sums.  Lane l holds the sub-chunk
 // sums [l*spt, (l+1)*spt); a wave scan finds the sub-chunk holding t = u * W,
 // then the lanes take its 64 groups and a second scan finds the token.
 constexpr int kPickCache = 8;  // sub-chunk sums kept in registers per lane
 
-template <int DT, int DDT, bool kDense>
+template <int DT, int DDT, bool kDense, bool kSoft>
 __global__ __launch_bounds__(kWave) void k_pick(SampleArgs a) {
   const int r = blockIdx.x, lane = threadIdx.x;
   const DrawRec& rec = a.rec[r];
@@ -791,32 +1077,46 @@ __global__ __launch_bounds__(kWave) void k_pick(SampleArgs a) {
   // the sub-chunk: lane = 8-value group
   const int NG = groups_of(V);
   const int g = sub * kSubG + lane;
-  const int gc = min(g, NG - 1);
-  const bool dense_res = kDense && !use_p;
-  uint4 t0, t1, d0, d1;
-  raw8<DT>(row_ptr(a.tgt, DT, trow, a.tgt_ld), gc, V, t0, t1);
-  if (dense_res) raw8<DDT>(row_ptr(a.draft, DDT, drow, a.draft_ld), gc, V, d0, d1);
-  float l[8], d[8];
-  decode8<DT>(t0, t1, g, V, g < NG, l);
-  if (dense_res) decode8<DDT>(d0, d1, g, V, g < NG, d);
   double w8[8];
+  bool formed = false;
+  if constexpr (kSoft) {
+    if (mode == kDrawSoft) {  // the same weights as the sums kernel formed
+      double p8[8], s8[8];
+      const size_t cstride = static_cast<size_t>(a.b) * static_cast<size_t>(a.comp_ld) * (DT == SV_BF16 ? 2 : 4);
+      soft_group<DT>(a, row_ptr(a.tgt, DT, trow, a.tgt_ld), row_ptr(a.comp, DT, drow, a.comp_ld), cstride, rec.cw, g,
+                     cut, invT, kept, rec.invTb, p8, s8);
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    double w = p_of(l[q], cut, invT, kept);  // 0 past V (value -inf) unless the cut is -inf
-    if (!(l[q] > -INFINITY)) w = 0.0;
-    if (dense_res) {
-      const double t2 = w - exp(static_cast<double>(d[q]) * invT - dlse);
-      w = t2 > 0.0 ? t2 : 0.0;
+      for (int q = 0; q < 8; ++q) w8[q] = use_p ? p8[q] : s8[q];
+      formed = true;
     }
-    w8[q] = w;
   }
-  if (!kDense && !use_p) {
-    for (int t2 = 0; t2 < nc; ++t2) {
-      const int v = bcast_i32(ctok, t2);
-      const double wv = bcast_f64(cwt, t2);
+  if (!formed) {
+    const int gc = min(g, NG - 1);
+    const bool dense_res = kDense && !use_p;
+    uint4 t0, t1, d0, d1;
+    raw8<DT>(row_ptr(a.tgt, DT, trow, a.tgt_ld), gc, V, t0, t1);
+    if (dense_res) raw8<DDT>(row_ptr(a.draft, DDT, drow, a.draft_ld), gc, V, d0, d1);
+    float l[8], d[8];
+    decode8<DT>(t0, t1, g, V, g < NG, l);
+    if (dense_res) decode8<DDT>(d0, d1, g, V, g < NG, d);
 #pragma unroll
-      for (int q = 0; q < 8; ++q)
-        if (v == g * 8 + q) w8[q] = wv;
+    for (int q = 0; q < 8; ++q) {
+      double w = p_of(l[q], cut, invT, kept);  // 0 past V (value -inf) unless the cut is -inf
+      if (!(l[q] > -INFINITY)) w = 0.0;
+      if (dense_res) {
+        const double t2 = w - exp(static_cast<double>(d[q]) * invT - dlse);
+        w = t2 > 0.0 ? t2 : 0.0;
+      }
+      w8[q] = w;
+    }
+    if (!kDense && !use_p) {
+      for (int t2 = 0; t2 < nc; ++t2) {
+        const int v = bcast_i32(ctok, t2);
+        const double wv = bcast_f64(cwt, t2);
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if (v == g * 8 + q) w8[q] = wv;
+      }
     }
   }
   double lsum = 0.0;
@@ -901,7 +1201,18 @@ static int32_t launch_draw_t(const SampleArgs& a, hipStream_t s) {
   const size_t dyn = tables > DLists<kDense>::kBytes ? tables : DLists<kDense>::kBytes;
   hipLaunchKernelGGL((k_draw_sums<DT, DDT, kDense, kAccept>), dim3(a.R * a.S), dim3(kSumNT), dyn, s, a);
   if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
-  hipLaunchKernelGGL((k_pick<DT, DDT, kDense>), dim3(a.R), dim3(kWave), 0, s, a);
+  hipLaunchKernelGGL((k_pick<DT, DDT, kDense, false>), dim3(a.R), dim3(kWave), 0, s, a);
+  return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
+}
+
+// soft branches: the soft tail, then the pick
+template <int DT>
+static int32_t launch_draw_soft(const SampleArgs& a, hipStream_t s) {
+  const size_t tables = soft_tables_bytes(a.K, a.b);
+  const size_t dyn = tables > DLists<false>::kBytes ? tables : DLists<false>::kBytes;
+  hipLaunchKernelGGL((k_draw_sums_soft<DT>), dim3(a.R * a.S), dim3(kSumNT), dyn, s, a);
+  if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
+  hipLaunchKernelGGL((k_pick<DT, DT, false, true>), dim3(a.R), dim3(kWave), 0, s, a);
   return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
 }
 
@@ -963,7 +1274,8 @@ extern "C" int32_t sv_accept_sample(const void* tgt_logits, int32_t dtype, int64
                                     const double* row_kept_lse, const int32_t* draft_tok, int32_t q_mode,
                                     const void* draft_logits, int32_t draft_dtype, int64_t draft_ld,
                                     const int32_t* draft_argmax, const double* draft_lse, int32_t K,
-                                    const float* mix_logits, int32_t* branch_tok, double* post_w,
+                                    const float* mix_logits, const void* comp_logits, int64_t comp_ld,
+                                    const float* branch_T, int32_t* branch_tok, double* post_w,
                                     double* q_at_draft, const uint64_t* seed, int32_t* n_acc, int32_t* token,
                                     int32_t* is_bonus, double* p_out, double* q_out, float* u_out, void* ws,
                                     size_t ws_bytes, void* stream) {
@@ -973,13 +1285,27 @@ extern "C" int32_t sv_accept_sample(const void* tgt_logits, int32_t dtype, int64
   if (!draft_tok || !n_acc || !token || !is_bonus) return SV_ERR_ARG;
   if (q_mode == SV_Q_MIXTURE && (K < 1 || K > 64 || !mix_logits || !branch_tok || !post_w || !q_at_draft))
     return SV_ERR_ARG;
-  if (ws_bytes < ws_layout(R, b, q_mode == SV_Q_MIXTURE ? K : 0, V).total) return SV_ERR_WORKSPACE;
+  const bool soft = branch_T != nullptr;
+  if (soft) {
+    if (q_mode != SV_Q_MIXTURE || !comp_logits || comp_ld < V || !rows_aligned(comp_logits, dtype, comp_ld))
+      return SV_ERR_ARG;
+    if (static_cast<long long>(K) * b > kSoftMaxKb) return SV_ERR_ARG;
+  }
+  const WsLayout l = ws_layout(R, b, q_mode == SV_Q_MIXTURE ? K : 0, V);
+  if (ws_bytes < l.total) return SV_ERR_WORKSPACE;
   SampleArgs a = sample_args(tgt_logits, dtype, tgt_ld, V, tgt_off, pos_off, R, b, temperature, row_argmax, row_cut,
                              row_kept_lse, q_mode, draft_logits, draft_dtype, draft_ld, draft_argmax, draft_lse, seed,
                              ws);
   a.x = draft_tok; a.K = q_mode == SV_Q_MIXTURE ? K : 0; a.mix = mix_logits; a.branch_out = branch_tok;
-  a.bkey = reinterpret_cast<const uint64_t*>(static_cast<char*>(ws) + ws_layout(R, b, a.K, V).bkey);
+  a.bkey = reinterpret_cast<const uint64_t*>(static_cast<char*>(ws) + l.bkey);
   a.post_w = post_w; a.q_at_draft = q_at_draft; a.n_acc = n_acc; a.n_acc_in = n_acc; a.token = token;
   a.is_bonus = is_bonus; a.p_out = p_out; a.q_out = q_out; a.u_out = u_out;
+  if (soft) {
+    a.comp = comp_logits; a.comp_ld = comp_ld; a.branch_T = branch_T;
+    a.blse = reinterpret_cast<const double*>(static_cast<char*>(ws) + l.blse);
+    a.barg = reinterpret_cast<const int32_t*>(static_cast<char*>(ws) + l.barg);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    return dtype == SV_BF16 ? launch_draw_soft<SV_BF16>(a, st) : launch_draw_soft<SV_F32>(a, st);
+  }
   return launch_draw<true>(a, static_cast<hipStream_t>(stream));
 }

@@ -44,7 +44,7 @@ def to_device_rows(arr: np.ndarray, ld: int, device="cuda", pad_bits: int | None
 
 class VerifyStep:
     def __init__(self, *, R: int, b: int, V: int, dtype: str, K: int = 0, max_pos: int | None = None,
-                 device="cuda", diagnostics: bool = False):
+                 device="cuda", diagnostics: bool = False, soft_branches: bool = False):
         self.R, self.b, self.V, self.K = R, b, V, K
         self.dtype = dtype
         self.dt = SV_BF16 if dtype == "bf16" else SV_F32
@@ -80,6 +80,9 @@ class VerifyStep:
         self.post_w = torch.zeros(R * b * kk, dtype=f64, **d)
         self.q_at_draft = torch.zeros(R * b, dtype=f64, **d)
         self.mix = torch.zeros(R * kk, dtype=f32, **d)
+        # soft branches: the branch temperature T_b per request (0 keeps that request's branches greedy)
+        self.soft = soft_branches
+        self.branch_T = torch.zeros(R, dtype=f32, **d) if soft_branches else None
         self.n_acc = torch.zeros(R, dtype=i32, **d)
         self.token = torch.zeros(R, dtype=i32, **d)
         self.is_bonus = torch.zeros(R, dtype=i32, **d)
@@ -89,7 +92,8 @@ class VerifyStep:
         self.u_out = torch.zeros(R * b, dtype=f32, **d) if diagnostics else None
 
     # ---------------------------------------------------------------- per-step inputs (host -> fixed addresses)
-    def set_inputs(self, *, T, x, seed: int, top_p=None, mix=None, a=None, budget: int | None = None):
+    def set_inputs(self, *, T, x, seed: int, top_p=None, mix=None, a=None, budget: int | None = None,
+                   branch_T=None):
         self.T.copy_(torch.as_tensor(np.asarray(T, np.float32)))
         self.top_p.copy_(torch.as_tensor(np.ones(self.R, np.float32) if top_p is None else np.asarray(top_p, np.float32)))
         self.use_topp = top_p is not None
@@ -101,6 +105,9 @@ class VerifyStep:
             self.a.copy_(torch.as_tensor(np.asarray(a, np.float32).reshape(-1)))
         if budget is not None:
             self.budget.fill_(int(budget))
+        if branch_T is not None:
+            assert self.soft, "branch temperatures need soft_branches=True"
+            self.branch_T.copy_(torch.as_tensor(np.broadcast_to(np.asarray(branch_T, np.float32), (self.R,)).copy()))
 
     def set_full_verification(self):
         """Offsets for L_r = b (no DVL): the exclusive scans of b and b + 1."""
@@ -148,16 +155,18 @@ class VerifyStep:
         sv_verify_rows(tgt, self.dt, tgt_ld, self.V, self.tgt_off, self.R, self.max_rows, self.T,
                        self.top_p if self.use_topp else None, self.row_max, self.row_argmax, self.row_lse,
                        self.row_cut, self.row_kept, comp, comp_ld, self.K, self.b, self.pos_off, self.max_pos,
-                       self.ws, self.ws_bytes, stream)
+                       self.branch_T, self.ws, self.ws_bytes, stream)
 
-    def run_accept_sample(self, tgt, tgt_ld, *, draft=None, draft_ld=0, stream=None):
-        """Posterior (mixture), acceptance and the draw: two launches."""
+    def run_accept_sample(self, tgt, tgt_ld, *, draft=None, draft_ld=0, comp=None, comp_ld=0, stream=None):
+        """Posterior (mixture), acceptance and the draw: two launches.  Soft
+        branches read the component rows again (`comp`)."""
         dense = self.q_mode == SV_Q_DENSE
         sv_accept_sample(tgt, self.dt, tgt_ld, self.V, self.tgt_off, self.pos_off, self.R, self.b, self.T,
                          self.row_argmax, self.row_cut, self.row_kept, self.x, self.q_mode,
                          draft if dense else None, self.dt, draft_ld if dense else 0,
                          self.d_argmax if dense else None, self.d_lse if dense else None, self.K,
-                         None if dense else self.mix, None if dense else self.branch_tok,
+                         None if dense else self.mix, comp if self.soft else None, comp_ld if self.soft else 0,
+                         self.branch_T, None if dense else self.branch_tok,
                          None if dense else self.post_w, None if dense else self.q_at_draft, self.seed, self.n_acc,
                          self.token, self.is_bonus, self.p_out, self.q_out, self.u_out, self.ws, self.ws_bytes,
                          stream)
@@ -173,8 +182,10 @@ class VerifyStep:
                 self.run_proposal(draft=draft, draft_ld=draft_ld)
             else:
                 self.run_rows_fused(tgt, tgt_ld, comp, comp_ld)
-            self.run_accept_sample(tgt, tgt_ld, draft=draft, draft_ld=draft_ld)
+            self.run_accept_sample(tgt, tgt_ld, draft=draft, draft_ld=draft_ld, comp=comp, comp_ld=comp_ld)
             return
+        if self.soft:
+            raise ValueError("soft branches run on the fused calls (fused=True)")
         if side_stream is None:
             self.run_rows(tgt, tgt_ld)
             self.run_proposal(draft=draft, draft_ld=draft_ld, comp=comp, comp_ld=comp_ld)

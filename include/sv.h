@@ -192,15 +192,24 @@ int32_t sv_mixture_q(const void* comp_logits, int32_t dtype, int64_t ld, int32_t
  * leaves its partial argmax in the workspace, and sv_accept_sample merges the
  * parts into branch_tok and forms the category posterior.  Arguments as in
  * those two calls (one dtype).  Same method and pages as sv_topp_threshold and
- * sv_mixture_q.  Uses the status word and the workspace's branch argmax
- * parts: call sv_accept_sample on the same workspace before the next
- * sv_verify_rows. */
+ * sv_mixture_q.
+ *   branch_T[R]  soft branches [DBLast, "What carries the argument": each
+ *                branch is a distribution q_i(. | y, z)], here
+ *                softmax(c / T_b,r) (float, device): each component row is
+ *                streamed by one block that forms its argmax, maximum and
+ *                log sum_v exp(c_v / T_b,r) (double, exact bf16 histogram as
+ *                for target rows); T_b,r = 0 keeps point-mass branches at the
+ *                argmax for that request.  NULL: greedy branches for every
+ *                request (the four-block partial argmax above).  Pass the
+ *                same branch_T to the following sv_accept_sample.
+ * Uses the status word and the workspace's branch results: call
+ * sv_accept_sample on the same workspace before the next sv_verify_rows. */
 int32_t sv_verify_rows(const void* tgt_logits, int32_t dtype, int64_t tgt_ld, int32_t V,
                        const int32_t* tgt_off, int32_t R, int32_t max_rows, const float* temperature,
                        const float* top_p, float* row_max, int32_t* row_argmax, double* row_lse,
                        float* row_cut, double* row_kept_lse, const void* comp_logits, int64_t comp_ld,
-                       int32_t K, int32_t b, const int32_t* pos_off, int32_t max_pos, void* ws,
-                       size_t ws_bytes, void* stream);
+                       int32_t K, int32_t b, const int32_t* pos_off, int32_t max_pos,
+                       const float* branch_T, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------- acceptance */
 
@@ -264,15 +273,26 @@ int32_t sv_residual_sample(const void* tgt_logits, int32_t dtype, int64_t tgt_ld
  * those calls.  Every chunk block of the draw recomputes its request's
  * posterior and acceptance, so no block waits for another.  SV_Q_DENSE takes
  * the draft arguments of sv_accept; K, mix_logits, branch_tok, post_w,
- * q_at_draft may then be NULL.  Uses the workspace's draw records and sub-chunk
- * sums. */
+ * q_at_draft may then be NULL.
+ *   branch_T[R], comp_logits, comp_ld  soft branches (NULL: greedy; then
+ *                comp_logits may be NULL): the branch statistics come from the
+ *                preceding sv_verify_rows with the same branch_T.  The
+ *                posterior before position i is proportional to
+ *                q(z | y) prod_{j<i} softmax(c_{z,j} / T_b)(x_j) (logs, double);
+ *                q(x_i | x_<i) = sum_z w_z softmax(c_{z,i} / T_b)(x_i); the
+ *                residual at a rejection j is norm(max(0, p_j - sum_z w_z
+ *                softmax(c_{z,j} / T_b))), formed over the K branch rows of
+ *                slot j (weights in double).  branch_tok gets each row's
+ *                argmax.  Requires K * b <= 2048 and comp_logits in dtype.
+ * Uses the workspace's draw records and sub-chunk sums. */
 int32_t sv_accept_sample(const void* tgt_logits, int32_t dtype, int64_t tgt_ld, int32_t V,
                          const int32_t* tgt_off, const int32_t* pos_off, int32_t R, int32_t b,
                          const float* temperature, const int32_t* row_argmax, const float* row_cut,
                          const double* row_kept_lse, const int32_t* draft_tok, int32_t q_mode,
                          const void* draft_logits, int32_t draft_dtype, int64_t draft_ld,
                          const int32_t* draft_argmax, const double* draft_lse, int32_t K,
-                         const float* mix_logits, int32_t* branch_tok, double* post_w,
+                         const float* mix_logits, const void* comp_logits, int64_t comp_ld,
+                         const float* branch_T, int32_t* branch_tok, double* post_w,
                          double* q_at_draft, const uint64_t* seed, int32_t* n_acc, int32_t* token,
                          int32_t* is_bonus, double* p_out, double* q_out, float* u_out, void* ws,
                          size_t ws_bytes, void* stream);

@@ -17,7 +17,9 @@ datasets and models are not used):
   * latent mixture (DBLast review, "What carries the argument"): K component
     rows per position = the target row's Zipfian base + N(0, 1.5^2); mixing
     logits N(0, 1); the drafter samples z ~ softmax(mixing logits)
-    (Gumbel-max) and decodes branch z greedily (argmax of the stored values).
+    (Gumbel-max) and decodes branch z greedily (argmax of the stored values),
+    or, with a branch temperature T_b > 0, samples every position of branch z
+    from softmax(c / T_b) (Gumbel-max).
   * survival estimates a ~ Beta(8, 2) per position for DVL.
 All randomness comes from numpy Generators seeded from SeedSequence(seed);
 work is split per request with spawned child sequences, so the output does
@@ -73,6 +75,7 @@ class Workload:
     x: np.ndarray               # [S, R, b] draft tokens per step
     seeds: np.ndarray           # [S] uint64 verification seeds
     branch_tok: Optional[np.ndarray] = None  # [R, K, b] drafter's greedy branch tokens
+    branch_T: float = 0.0       # mixture branches: 0 greedy; > 0 sampled from softmax(c / branch_T)
 
     @property
     def steps(self) -> int:
@@ -108,9 +111,11 @@ def _gumbel_argmax(rng, logits: np.ndarray, T: float) -> np.ndarray:
 def make(name: str, *, R: int, b: int = 16, V: int = QWEN3_VOCAB, K: int = 0, dtype: str = "bf16",
          target: str = "zipf", draft_sigma: float = 1.0, comp_sigma: float = 1.5,
          T=1.0, top_p: Optional[float] = None, budget: Optional[int] = None, steps: int = 1,
-         seed: int = 1000, vseed: int = 1, threads: Optional[int] = None) -> Workload:
+         seed: int = 1000, vseed: int = 1, threads: Optional[int] = None, branch_T: float = 0.0) -> Workload:
     """Draw one workload.  ``target`` is "zipf" (Zipfian base + N(0,1)) or
-    "normal2" (N(0, 2^2)); ``K`` > 0 selects the latent-mixture drafter."""
+    "normal2" (N(0, 2^2)); ``K`` > 0 selects the latent-mixture drafter, whose
+    branches decode greedily (``branch_T`` = 0) or sample from
+    softmax(c / branch_T)."""
     threads = threads or _default_threads()
     ss = np.random.SeedSequence(seed)
     kids = ss.spawn(R + 1)
@@ -166,16 +171,25 @@ def make(name: str, *, R: int, b: int = 16, V: int = QWEN3_VOCAB, K: int = 0, dt
         x = np.empty((steps, R, b), np.int32)
         for s in range(steps):
             zs = _gumbel_argmax(rng, mix, 1.0)
-            x[s] = branch_tok[np.arange(R), zs]
+            if branch_T == 0.0:
+                x[s] = branch_tok[np.arange(R), zs]
+            else:  # the drafter samples every position of the chosen branch
+                for r in range(R):
+                    x[s, r] = _gumbel_argmax(rng, values(comp[r, zs[r]]), branch_T)
     tp = None if top_p is None else np.full(R, top_p, np.float32)
     return Workload(name=name, R=R, b=b, V=V, K=K, dtype=dtype, tgt=tgt, draft=draft, comp=comp, mix=mix,
-                    T=Tr, top_p=tp, budget=budget, a=a, x=x, seeds=seeds, branch_tok=branch_tok)
+                    T=Tr, top_p=tp, budget=budget, a=a, x=x, seeds=seeds, branch_tok=branch_tok,
+                    branch_T=float(branch_T))
 
 
 # ------------------------------------------------------------ the five workloads
 def config(c: int, *, V: Optional[int] = None, R: Optional[int] = None, steps: Optional[int] = None,
-           threads: Optional[int] = None) -> Workload:
-    """Workload c = 1..5 (sizes may be shrunk for quick parity cases)."""
+           threads: Optional[int] = None, branch_T: float = 0.0) -> Workload:
+    """Workload c = 1..5 (sizes may be shrunk for quick parity cases).  For the
+    mixture workloads (4, 5) ``branch_T`` > 0 gives the soft-branch drafter."""
+    if branch_T and c not in (4, 5):
+        raise ValueError("branch_T applies to the mixture workloads 4 and 5")
+    soft = f"-softTb{branch_T:g}" if branch_T else ""
     if c == 1:
         R_ = R or 4
         T = np.ones(R_, np.float32)
@@ -190,13 +204,13 @@ def config(c: int, *, V: Optional[int] = None, R: Optional[int] = None, steps: O
         return make("cfg3-conc32-dvl-indep", R=R_, V=V or QWEN3_VOCAB, T=1.0, budget=R_ * 16 // 2,
                     seed=1003, vseed=3, steps=steps or 1, threads=threads)
     if c == 4:
-        return make("cfg4-conc16-mix8-T1.5-topp", R=R or 16, V=V or QWEN3_VOCAB, K=8, T=1.5, top_p=0.95,
-                    seed=1004, vseed=4, steps=steps or 1, threads=threads)
+        return make("cfg4-conc16-mix8-T1.5-topp" + soft, R=R or 16, V=V or QWEN3_VOCAB, K=8, T=1.5, top_p=0.95,
+                    seed=1004, vseed=4, steps=steps or 1, threads=threads, branch_T=branch_T)
     if c == 5:
         R_ = R or 32
-        return make("cfg5-conc32-dvl-mix8-topp", R=R_, V=V or QWEN3_VOCAB, K=8, T=1.0, top_p=0.95,
+        return make("cfg5-conc32-dvl-mix8-topp" + soft, R=R_, V=V or QWEN3_VOCAB, K=8, T=1.0, top_p=0.95,
                     budget=R_ * 16 // 2, seed=1005, vseed=5, steps=200 if steps is None else steps,
-                    threads=threads)
+                    threads=threads, branch_T=branch_T)
     raise ValueError(c)
 
 

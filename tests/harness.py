@@ -28,7 +28,11 @@ def gpu_step_runner(w: synth.Workload, device="cuda", two_streams: bool = False,
     R, b, V, K = w.R, w.b, w.V, w.K
     ld = row_pitch(V, w.dtype)
     max_pos = min(w.budget, R * b) if w.budget is not None else R * b
-    vs = VerifyStep(R=R, b=b, V=V, dtype=w.dtype, K=K, max_pos=max_pos, device=device, diagnostics=True)
+    soft = bool(np.any(np.asarray(w.branch_T) > 0))
+    if soft:
+        fused = True  # soft branches run on the fused calls
+    vs = VerifyStep(R=R, b=b, V=V, dtype=w.dtype, K=K, max_pos=max_pos, device=device, diagnostics=True,
+                    soft_branches=soft)
     full = to_device_rows(w.tgt, ld, device)  # [R*(b+1), ld]
     packed = torch.empty_like(full)
     draft = to_device_rows(w.draft, ld, device) if K == 0 else None
@@ -37,7 +41,8 @@ def gpu_step_runner(w: synth.Workload, device="cuda", two_streams: bool = False,
 
     def run(s: int) -> dict:
         vs.set_inputs(T=w.T, x=w.x[s], seed=int(w.seeds[s]), top_p=w.top_p, mix=w.mix,
-                      a=None if w.a is None else w.a[s], budget=w.budget)
+                      a=None if w.a is None else w.a[s], budget=w.budget,
+                      branch_T=w.branch_T if soft else None)
         if w.budget is not None:
             vs.run_dvl()
             L = vs.L.cpu().numpy()
@@ -65,7 +70,9 @@ def gpu_graph_runner(w: synth.Workload, device="cuda"):
     R, b, V, K = w.R, w.b, w.V, w.K
     ld = row_pitch(V, w.dtype)
     max_pos = min(w.budget, R * b) if w.budget is not None else R * b
-    vs = VerifyStep(R=R, b=b, V=V, dtype=w.dtype, K=K, max_pos=max_pos, device=device, diagnostics=True)
+    soft = bool(np.any(np.asarray(w.branch_T) > 0))
+    vs = VerifyStep(R=R, b=b, V=V, dtype=w.dtype, K=K, max_pos=max_pos, device=device, diagnostics=True,
+                    soft_branches=soft)
     full = to_device_rows(w.tgt, ld, device)
     packed = torch.empty((vs.max_rows, ld), dtype=full.dtype, device=device)
     slots = torch.arange(vs.max_rows, dtype=torch.int32, device=device)
@@ -74,7 +81,8 @@ def gpu_graph_runner(w: synth.Workload, device="cuda"):
 
     def set_step(s: int):
         vs.set_inputs(T=w.T, x=w.x[s], seed=int(w.seeds[s]), top_p=w.top_p, mix=w.mix,
-                      a=None if w.a is None else w.a[s], budget=w.budget)
+                      a=None if w.a is None else w.a[s], budget=w.budget,
+                      branch_T=w.branch_T if soft else None)
         if w.budget is None:
             vs.set_full_verification()
 
@@ -110,7 +118,12 @@ def oracle_step(w: synth.Workload, s: int) -> dict:
     if K == 0:
         out = oracle.step(**common, draft=w.draft.reshape(R * b, V), draft_row0=np.arange(R) * b)
     else:
-        out = oracle.step(**common, comp=w.comp.reshape(R * K * b, V), comp_row0=np.arange(R) * K * b, mix=w.mix)
+        # the oracle takes one branch temperature; requests are independent, so a
+        # per-request T_b is one oracle run per distinct value, merged by request
+        bT = np.broadcast_to(np.asarray(w.branch_T, np.float64), (R,))
+        runs = {float(t): oracle.step(**common, comp=w.comp.reshape(R * K * b, V), comp_row0=np.arange(R) * K * b,
+                                      mix=w.mix, branch_T=float(t)) for t in np.unique(bT)}
+        out = {k: np.stack([runs[float(bT[r])][k][r] for r in range(R)]) for k in runs[float(bT[0])]}
     out["dvl"] = dv
     # statistics of every target row read in this step, in packed order
     rows = np.concatenate([r * (b + 1) + np.arange(L[r] + 1) for r in range(R)])

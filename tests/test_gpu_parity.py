@@ -323,7 +323,7 @@ def test_determinism_repeat_runs():
 
 # ---------------------------------------------------------------- whole step in a HIP graph
 GRAPH = [(3, dict(V=2053, R=8, steps=4)), (5, dict(V=4099, R=8, steps=4)), (4, dict(V=4099, R=4, steps=2)),
-         (2, dict(V=2053, R=4, steps=2)), (5, dict(steps=4))]
+         (2, dict(V=2053, R=4, steps=2)), (5, dict(steps=4)), (5, dict(V=4099, R=8, steps=3, branch_T=1.0))]
 
 
 def _same_bits(a: dict, b: dict):
@@ -401,3 +401,42 @@ def test_graph_replay_budget_changes(c, kw):
         assert int(g["pos_off"][-1]) == min(budget, w.R * w.b)
         rep = compare_step(w, g, oracle_step(w, s), rep)
     assert_rate(rep)
+
+
+# ---------------------------------------------------------------- soft branches
+SOFT = [(4, dict(V=4099, R=4, branch_T=1.0)), (5, dict(V=4099, R=8, steps=3, branch_T=0.7)),
+        (5, dict(V=1031, R=16, steps=2, branch_T=2.0)), (4, dict(V=64, R=8, steps=2, branch_T=0.3)),
+        (4, dict(branch_T=1.0)), (5, dict(steps=3, branch_T=1.0))]
+
+
+@pytest.mark.parametrize("c,kw", SOFT, ids=[f"cfg{c}-" + "-".join(f"{k}{v}" for k, v in kw.items()) for c, kw in SOFT])
+def test_soft_branches_match_oracle(c, kw):
+    """Soft-branch mixture (each branch softmax(c / T_b), drafts sampled from
+    it): branch argmax, posterior, q at the drafts, decisions and the dense
+    K-row residual against the oracle."""
+    w = synth.config(c, **kw)
+    vs, run = gpu_step_runner(w)
+    rep = None
+    for s in range(w.steps):
+        banner(f"soft {w.name} V={w.V} R={w.R} step {s}")
+        rep = compare_step(w, run(s), oracle_step(w, s), rep)
+    assert_rate(rep)
+    assert _sv().sv_get_status(vs.ws) == 0
+
+
+def test_soft_branches_per_request_temperatures():
+    """T_b per request, some 0 (point-mass branches, drafts from greedy
+    branches) and some soft, in one step."""
+    w = synth.config(5, V=4099, R=8, steps=3, branch_T=1.0)
+    tb = np.array([1.0, 0.0, 0.5, 0.0, 2.0, 1.5, 0.0, 0.25], np.float32)
+    w.branch_T = tb
+    for s in range(w.steps):
+        for r in np.nonzero(tb == 0)[0]:
+            w.x[s, r] = w.branch_tok[r, (s + r) % w.K]
+    vs, run = gpu_step_runner(w)
+    rep = None
+    for s in range(w.steps):
+        banner(f"soft per-request T_b step {s}")
+        rep = compare_step(w, run(s), oracle_step(w, s), rep)
+    assert_rate(rep)
+    assert _sv().sv_get_status(vs.ws) == 0
