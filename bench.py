@@ -204,7 +204,7 @@ def main():
     packed = torch.empty((S, max_rows, ld), dtype=torch.bfloat16, device=dev)
     L_host = np.zeros((S, R), np.int32)
     for s in range(S):
-        sv.dvl_alloc_pack(a_all[s], R, b, budget, s_sc, L, pos_off, tgt_off, ws, nb, sp)
+        sv.dvl_alloc_pack(a_all[s], R, b, None, budget, s_sc, L, pos_off, tgt_off, ws, nb, sp)
         L_host[s] = L.cpu().numpy()
         pack_rows_device(full, L_host[s], b + 1, packed[s])
     torch.cuda.synchronize()
@@ -212,7 +212,7 @@ def main():
     positions = L_host.sum(axis=1)  # verified positions per step
 
     def step(s, ev=None):
-        sv.dvl_alloc_pack(a_all[s], R, b, budget, s_sc, L, pos_off, tgt_off, ws, nb, sp)
+        sv.dvl_alloc_pack(a_all[s], R, b, None, budget, s_sc, L, pos_off, tgt_off, ws, nb, sp)
         if ev is not None:
             ev[0].record(stream)
         # target rows (statistics, top-p) and component rows (branch argmax) in one launch

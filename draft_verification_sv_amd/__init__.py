@@ -27,7 +27,7 @@ SV_ERR_LAUNCH = 3
 STATUS_BITS = {
     0x001: "BAD_TEMPERATURE", 0x002: "BAD_TOP_P", 0x004: "NONFINITE", 0x008: "BAD_SCORE",
     0x010: "BAD_TOKEN", 0x020: "BAD_OFFSETS", 0x040: "EMPTY_POSTERIOR", 0x080: "BAD_BUDGET",
-    0x100: "BAD_NACC",
+    0x100: "BAD_NACC", 0x200: "BAD_BLOCK",
 }
 
 EXPORTS = [
@@ -55,7 +55,7 @@ _SIGS = {
     "sv_workspace_init": [_vp, _sz, _vp],
     "sv_get_status": [_vp, _vp, C.POINTER(C.c_uint32)],
     "sv_clear_status": [_vp, _vp],
-    "dvl_alloc_pack": [_vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+    "dvl_alloc_pack": [_vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "sv_softmax_stats": [_vp, _i32, _i64, _i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "sv_topp_threshold": [_vp, _i32, _i64, _i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                           _sz, _vp],
@@ -148,9 +148,9 @@ def make_workspace(R: int, b: int, K: int, V: int, device="cuda"):
 
 
 # ---------------------------------------------------------------- entry points
-def dvl_alloc_pack(a, R, b, budget, s, L, pos_off, tgt_off, ws, ws_bytes, stream=None):
-    _check(_lib.dvl_alloc_pack(_p(a), R, b, _p(budget), _p(s), _p(L), _p(pos_off), _p(tgt_off), _p(ws), ws_bytes,
-                               _stream(stream)), "dvl_alloc_pack")
+def dvl_alloc_pack(a, R, b, block_len, budget, s, L, pos_off, tgt_off, ws, ws_bytes, stream=None):
+    _check(_lib.dvl_alloc_pack(_p(a), R, b, _p(block_len), _p(budget), _p(s), _p(L), _p(pos_off), _p(tgt_off),
+                               _p(ws), ws_bytes, _stream(stream)), "dvl_alloc_pack")
 
 
 def sv_softmax_stats(logits, dtype, ld, V, row_off, row_stride, R, max_rows, temperature, row_max, row_argmax,

@@ -11,6 +11,16 @@
 // asc, i asc); with a <= 1 the scores fall along each request, so the choice is
 // prefix-closed and maximises the summed survival (expected accepted length).
 //
+// Per-request block length ("Why does throughput collapse under high
+// concurrency?", section "How does draft quality decay with block length and
+// sampling temperature?": BlockPilot finds the best block size varies per
+// request): with block_len, request r drafted only its
+// first b_r positions; the others are not candidates and get s = 0.  The
+// selection key of a candidate is its score key + 1 and that of any other
+// position 0, and the budget is capped at sum_r b_r, so the threshold is >= 1
+// and never admits a non-candidate.  Without block_len every key is shifted
+// alike and the result is unchanged.
+//
 // One block of 256 threads:
 //   1. per request, the running products (written to s);
 //   2. radix select, 8 bits per pass from the top, of the B-th largest score
@@ -35,8 +45,14 @@ __device__ __forceinline__ uint32_t score_key(float v) {
 constexpr int kDvlNT = 256;
 constexpr int kDvlLds = 8192;  // scores kept in LDS up to this many positions
 
+// b_r of request r: block_len[r] clamped to [0, b] (b without block_len)
+__device__ __forceinline__ int block_of(const int32_t* block_len, int r, int b) {
+  return block_len ? min(max(block_len[r], 0), b) : b;
+}
+
 template <bool kInLds>
 __global__ __launch_bounds__(kDvlNT) void k_dvl(const float* __restrict__ a, int R, int b,
+                                               const int32_t* __restrict__ block_len,
                                                const int32_t* __restrict__ budget, float* __restrict__ s,
                                                int32_t* __restrict__ L, int32_t* __restrict__ pos_off,
                                                int32_t* __restrict__ tgt_off, uint32_t* status) {
@@ -53,6 +69,20 @@ __global__ __launch_bounds__(kDvlNT) void k_dvl(const float* __restrict__ a, int
     if (tid == 0) raise_status(status, SV_ST_BAD_BUDGET);
     B = 0;
   }
+  // candidates: sum_r b_r
+  int n_cand = n;
+  if (block_len) {
+    const int pr0 = (R + kDvlNT - 1) / kDvlNT;
+    int c = 0;
+    bool bad_bl = false;
+    for (int r = tid * pr0; r < min(R, (tid + 1) * pr0); ++r) {
+      const int v = block_len[r];
+      bad_bl |= v < 0 || v > b;
+      c += min(max(v, 0), b);
+    }
+    if (bad_bl) raise_status(status, SV_ST_BAD_BLOCK);
+    (void)block_excl_scan_i32<kDvlNT>(c, scr, &n_cand);
+  }
   // 1. survival scores.  The estimates are read in one coalesced pass (into
   // LDS when they fit) before any score is written, so no load waits behind a
   // store.
@@ -60,44 +90,48 @@ __global__ __launch_bounds__(kDvlNT) void k_dvl(const float* __restrict__ a, int
   if constexpr (kInLds) {
     for (int e = tid; e < n; e += kDvlNT) {
       const float av = a[e];
-      bad |= !(av >= 0.0f && av <= 1.0f);
+      bad |= (e % b) < block_of(block_len, e / b, b) && !(av >= 0.0f && av <= 1.0f);
       skey[e] = __float_as_uint(av);
     }
     for (int r = tid; r < R; r += kDvlNT) lcount[r] = 0;
     __syncthreads();
     for (int r = tid; r < R; r += kDvlNT) {
+      const int br = block_of(block_len, r, b);
       float run = 1.0f;
       for (int i = 0; i < b; ++i) {
         run = run * __uint_as_float(skey[r * b + i]);
-        skey[r * b + i] = __float_as_uint(run);
+        skey[r * b + i] = i < br ? __float_as_uint(run) : 0xFFFFFFFFu;  // marks a position past b_r
       }
     }
     __syncthreads();
     for (int e = tid; e < n; e += kDvlNT) {
-      const float sv = __uint_as_float(skey[e]);
+      const bool cand = skey[e] != 0xFFFFFFFFu;
+      const float sv = cand ? __uint_as_float(skey[e]) : 0.0f;
       s[e] = sv;
-      skey[e] = score_key(sv);
+      skey[e] = cand ? score_key(sv) + 1u : 0u;
     }
   } else {
     for (int r = tid; r < R; r += kDvlNT) L[r] = 0;
     for (int r = tid; r < R; r += kDvlNT) {
+      const int br = block_of(block_len, r, b);
       float run = 1.0f;
       for (int i = 0; i < b; ++i) {
         const float av = a[r * b + i];
-        bad |= !(av >= 0.0f && av <= 1.0f);
+        bad |= i < br && !(av >= 0.0f && av <= 1.0f);
         run = run * av;
-        s[r * b + i] = run;
+        s[r * b + i] = i < br ? run : 0.0f;
       }
     }
   }
   if (bad) raise_status(status, SV_ST_BAD_SCORE);
   __syncthreads();  // scores are re-read below by other threads of this block
-  const bool all = B >= n, none = B == 0;
+  const bool all = B >= n_cand, none = B == 0;
 
   {
+    // selection key: score key + 1 for a candidate, 0 past b_r
     auto key = [&](int e) -> uint32_t {
       if constexpr (kInLds) return skey[e];
-      else return score_key(s[e]);
+      else return (e % b) < block_of(block_len, e / b, b) ? score_key(s[e]) + 1u : 0u;
     };
     // 2. threshold: the B-th largest score (rank from the top, ties counted)
     uint32_t thr = 0;
@@ -142,7 +176,7 @@ __global__ __launch_bounds__(kDvlNT) void k_dvl(const float* __restrict__ a, int
     for (int e = e0; e < e1; ++e) {
       bool take;
       if (all) {
-        take = true;
+        take = key(e) != 0u;
       } else if (none) {
         take = false;
       } else {
@@ -187,17 +221,18 @@ __global__ __launch_bounds__(kDvlNT) void k_dvl(const float* __restrict__ a, int
 
 using namespace sv;
 
-extern "C" int32_t dvl_alloc_pack(const float* a, int32_t R, int32_t b, const int32_t* budget, float* s, int32_t* L,
-                                  int32_t* pos_off, int32_t* tgt_off, void* ws, size_t ws_bytes, void* stream) {
+extern "C" int32_t dvl_alloc_pack(const float* a, int32_t R, int32_t b, const int32_t* block_len,
+                                  const int32_t* budget, float* s, int32_t* L, int32_t* pos_off, int32_t* tgt_off,
+                                  void* ws, size_t ws_bytes, void* stream) {
   if (!a || !budget || !s || !L || !pos_off || !tgt_off || !ws) return SV_ERR_ARG;
   if (R < 1 || b < 1 || b > 64 || static_cast<long long>(R) * b > (1LL << 24)) return SV_ERR_ARG;
   if (ws_bytes < 256) return SV_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (R * b <= kDvlLds)
-    hipLaunchKernelGGL(k_dvl<true>, dim3(1), dim3(kDvlNT), 0, st, a, R, b, budget, s, L, pos_off, tgt_off,
-                       status_word(ws));
+    hipLaunchKernelGGL(k_dvl<true>, dim3(1), dim3(kDvlNT), 0, st, a, R, b, block_len, budget, s, L, pos_off,
+                       tgt_off, status_word(ws));
   else
-    hipLaunchKernelGGL(k_dvl<false>, dim3(1), dim3(kDvlNT), 0, st, a, R, b, budget, s, L, pos_off, tgt_off,
-                       status_word(ws));
+    hipLaunchKernelGGL(k_dvl<false>, dim3(1), dim3(kDvlNT), 0, st, a, R, b, block_len, budget, s, L, pos_off,
+                       tgt_off, status_word(ws));
   return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
 }

@@ -44,7 +44,7 @@ def to_device_rows(arr: np.ndarray, ld: int, device="cuda", pad_bits: int | None
 
 class VerifyStep:
     def __init__(self, *, R: int, b: int, V: int, dtype: str, K: int = 0, max_pos: int | None = None,
-                 device="cuda", diagnostics: bool = False, soft_branches: bool = False):
+                 device="cuda", diagnostics: bool = False, soft_branches: bool = False, ragged: bool = False):
         self.R, self.b, self.V, self.K = R, b, V, K
         self.dtype = dtype
         self.dt = SV_BF16 if dtype == "bf16" else SV_F32
@@ -58,6 +58,9 @@ class VerifyStep:
         self.seed = torch.zeros(1, dtype=torch.int64, **d)
         self.budget = torch.zeros(1, dtype=i32, **d)
         self.a = torch.zeros(R * b, dtype=f32, **d)
+        # per-request block length b_r <= b (None: every request drafted b positions)
+        self.block_len = torch.full((R,), b, dtype=i32, **d) if ragged else None
+        self._block_len_host = np.full(R, b, np.int32)
         self.s = torch.zeros(R * b, dtype=f32, **d)
         self.L = torch.zeros(R, dtype=i32, **d)
         self.pos_off = torch.zeros(R + 1, dtype=i32, **d)
@@ -93,7 +96,7 @@ class VerifyStep:
 
     # ---------------------------------------------------------------- per-step inputs (host -> fixed addresses)
     def set_inputs(self, *, T, x, seed: int, top_p=None, mix=None, a=None, budget: int | None = None,
-                   branch_T=None):
+                   branch_T=None, block_len=None):
         self.T.copy_(torch.as_tensor(np.asarray(T, np.float32)))
         self.top_p.copy_(torch.as_tensor(np.ones(self.R, np.float32) if top_p is None else np.asarray(top_p, np.float32)))
         self.use_topp = top_p is not None
@@ -105,21 +108,25 @@ class VerifyStep:
             self.a.copy_(torch.as_tensor(np.asarray(a, np.float32).reshape(-1)))
         if budget is not None:
             self.budget.fill_(int(budget))
+        if block_len is not None:
+            assert self.block_len is not None, "block lengths need ragged=True"
+            self._block_len_host = np.asarray(block_len, np.int32).reshape(self.R).copy()
+            self.block_len.copy_(torch.as_tensor(self._block_len_host))
         if branch_T is not None:
             assert self.soft, "branch temperatures need soft_branches=True"
             self.branch_T.copy_(torch.as_tensor(np.broadcast_to(np.asarray(branch_T, np.float32), (self.R,)).copy()))
 
     def set_full_verification(self):
-        """Offsets for L_r = b (no DVL): the exclusive scans of b and b + 1."""
-        R, b = self.R, self.b
-        self.L.fill_(b)
-        self.pos_off.copy_(torch.arange(R + 1, dtype=torch.int32) * b)
-        self.tgt_off.copy_(torch.arange(R + 1, dtype=torch.int32) * (b + 1))
+        """Offsets for L_r = b_r (no DVL): the exclusive scans of b_r and b_r + 1."""
+        L = self._block_len_host
+        self.L.copy_(torch.as_tensor(L))
+        self.pos_off.copy_(torch.as_tensor(np.concatenate([[0], np.cumsum(L)]).astype(np.int32)))
+        self.tgt_off.copy_(torch.as_tensor(np.concatenate([[0], np.cumsum(L + 1)]).astype(np.int32)))
 
     # ---------------------------------------------------------------- the calls
     def run_dvl(self, stream=None):
-        dvl_alloc_pack(self.a, self.R, self.b, self.budget, self.s, self.L, self.pos_off, self.tgt_off, self.ws,
-                       self.ws_bytes, stream)
+        dvl_alloc_pack(self.a, self.R, self.b, self.block_len, self.budget, self.s, self.L, self.pos_off,
+                       self.tgt_off, self.ws, self.ws_bytes, stream)
 
     def run_rows(self, tgt, tgt_ld, stream=None):
         sv_topp_threshold(tgt, self.dt, tgt_ld, self.V, self.tgt_off, 0, self.R, self.max_rows, self.T,

@@ -84,6 +84,7 @@ extern "C" {
 #define SV_ST_EMPTY_POSTERIOR 0x040u /* no mixture branch consistent with the draft prefix (q = 0) */
 #define SV_ST_BAD_BUDGET 0x080u      /* DVL budget < 0 */
 #define SV_ST_BAD_NACC 0x100u        /* n_acc outside [0, L_r] */
+#define SV_ST_BAD_BLOCK 0x200u       /* DVL block length outside [0, b] (clamped) */
 
 /* ---------------------------------------------------------------- workspace */
 
@@ -108,18 +109,27 @@ const char* sv_status_string(int32_t code);
 /* dvl_alloc_pack [DScale abstract: DVL allocation; wispaper: prefix survival
  * probabilities].
  *   a[R*b]      per-position acceptance estimates in [0, 1] (float)
+ *   block_len[R]  optional (NULL: b for every request): request r drafted
+ *               only its first b_r positions (0 <= b_r <= b; others clamped,
+ *               SV_ST_BAD_BLOCK) [wispaper, section "How does draft quality
+ *               decay with block length and sampling temperature?": BlockPilot's
+ *               block size varies per request]; positions i >= b_r are never
+ *               chosen and their estimates are ignored (not checked)
  *   budget      device int32 scalar: verification slots B (>= 0)
  *   s[R*b]      out: survival scores s_{r,i} = fl32(s_{r,i-1} * a_{r,i}),
- *               s_{r,0} = a_{r,0}, one float rounding per product
- *   L[R]        out: verified positions per request
+ *               s_{r,0} = a_{r,0}, one float rounding per product; 0 for
+ *               i >= b_r
+ *   L[R]        out: verified positions per request (L_r <= b_r)
  *   pos_off[R+1], tgt_off[R+1]  out: exclusive scans of L and of L + 1
- * The chosen positions are the min(B, R*b) best in the order (s desc, r asc,
- * i asc); with a <= 1 they are prefix-closed per request and maximise the
- * summed survival score (expected accepted positions).  Requires
- * R*b <= 2^24, b <= 64.  Uses the workspace's status word only. */
-int32_t dvl_alloc_pack(const float* a, int32_t R, int32_t b, const int32_t* budget, float* s,
-                       int32_t* L, int32_t* pos_off, int32_t* tgt_off, void* ws,
-                       size_t ws_bytes, void* stream);
+ * The chosen positions are the min(B, sum_r b_r) best drafted positions in the
+ * order (s desc, r asc, i asc); with a <= 1 they are prefix-closed per
+ * request and maximise the summed survival score (expected accepted
+ * positions).  With B >= sum_r b_r every drafted position is verified (L_r =
+ * b_r).  Requires R*b <= 2^24, b <= 64.  Uses the workspace's status word
+ * only. */
+int32_t dvl_alloc_pack(const float* a, int32_t R, int32_t b, const int32_t* block_len,
+                       const int32_t* budget, float* s, int32_t* L, int32_t* pos_off,
+                       int32_t* tgt_off, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------- row statistics */
 

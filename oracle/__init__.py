@@ -88,6 +88,8 @@ def _declare(L):
     L.orc_uniform_words.restype = None
     L.orc_dvl.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp]
     L.orc_dvl.restype = C.c_int
+    L.orc_dvl_ragged.argtypes = [vp, i32, i32, vp, i32, vp, vp, vp, vp]
+    L.orc_dvl_ragged.restype = C.c_int
     L.orc_dvl_objective.argtypes = [vp, vp, i32, i32]
     L.orc_dvl_objective.restype = dbl
     L.orc_row_stats.argtypes = [vp, i32, i32, dbl, dbl, vp]
@@ -142,14 +144,20 @@ def uniform_words(seed: int, R: int, n_pos: int) -> np.ndarray:
 
 
 # ---------------------------------------------------------------- DVL
-def dvl(a, budget: int) -> dict:
+def dvl(a, budget: int, block_len=None) -> dict:
+    """DVL allocation of survival estimates a [R, b] under `budget`; with
+    `block_len` [R], request r drafted only its first block_len[r] positions."""
     a = _c(a, np.float32)
     R, b = a.shape
     s = np.zeros((R, b), np.float32)
     Lr = np.zeros(R, np.int32)
     pos_off = np.zeros(R + 1, np.int32)
     tgt_off = np.zeros(R + 1, np.int32)
-    bad = lib().orc_dvl(_ptr(a), R, b, int(budget), _ptr(s), _ptr(Lr), _ptr(pos_off), _ptr(tgt_off))
+    bl = None if block_len is None else _c(block_len, np.int32)
+    bad = lib().orc_dvl_ragged(_ptr(a), R, b, _ptr(bl), int(budget), _ptr(s), _ptr(Lr), _ptr(pos_off),
+                               _ptr(tgt_off))
+    if bad == 2:
+        raise ValueError("block_len outside [0, b]")
     return {"s": s, "L": Lr, "pos_off": pos_off, "tgt_off": tgt_off, "bad": int(bad)}
 
 

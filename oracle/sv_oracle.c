@@ -119,27 +119,47 @@ static int orc_dvl_cmp(const void* pa, const void* pb) {
   return 0;
 }
 
-int orc_dvl(const float* a, int32_t R, int32_t b, int32_t budget, float* s, int32_t* L,
-            int32_t* pos_off, int32_t* tgt_off) {
+/* Per-request block length ["Why does throughput collapse under high         */
+/* concurrency?", section "How does draft quality decay with block length and */
+/* sampling temperature?": BlockPilot finds the best block size varies from   */
+/* request to request]: request r drafts b_r <= b                             */
+/* positions; positions i >= b_r were not drafted, are never candidates and   */
+/* get score 0.  block_len NULL: b_r = b.  Returns 2 if some b_r lies outside */
+/* [0, b] (nothing written).                                                  */
+int orc_dvl_ragged(const float* a, int32_t R, int32_t b, const int32_t* block_len, int32_t budget, float* s,
+                   int32_t* L, int32_t* pos_off, int32_t* tgt_off) {
   int bad = 0;
-  size_t n = (size_t)R * (size_t)b;
-  for (size_t k = 0; k < n; ++k)
-    if (!(a[k] >= 0.0f && a[k] <= 1.0f)) bad = 1;
+  if (block_len)
+    for (int32_t r = 0; r < R; ++r)
+      if (block_len[r] < 0 || block_len[r] > b) return 2;
+  size_t n = 0; /* candidates */
   for (int32_t r = 0; r < R; ++r) {
+    const int32_t br = block_len ? block_len[r] : b;
     float run = 1.0f;
     for (int32_t i = 0; i < b; ++i) {
-      float prod = run * a[(size_t)r * b + i]; /* one float rounding per step */
+      if (i >= br) {
+        s[(size_t)r * b + i] = 0.0f;
+        continue;
+      }
+      const float av = a[(size_t)r * b + i];
+      if (!(av >= 0.0f && av <= 1.0f)) bad = 1;
+      float prod = run * av; /* one float rounding per step */
       s[(size_t)r * b + i] = prod;
       run = prod;
     }
+    n += (size_t)br;
   }
   orc_dvl_item* items = (orc_dvl_item*)malloc(sizeof(orc_dvl_item) * (n ? n : 1));
-  for (int32_t r = 0; r < R; ++r)
-    for (int32_t i = 0; i < b; ++i) {
-      items[(size_t)r * b + i].s = s[(size_t)r * b + i];
-      items[(size_t)r * b + i].r = r;
-      items[(size_t)r * b + i].i = i;
+  size_t k0 = 0;
+  for (int32_t r = 0; r < R; ++r) {
+    const int32_t br = block_len ? block_len[r] : b;
+    for (int32_t i = 0; i < br; ++i) {
+      items[k0].s = s[(size_t)r * b + i];
+      items[k0].r = r;
+      items[k0].i = i;
+      ++k0;
     }
+  }
   qsort(items, n, sizeof(orc_dvl_item), orc_dvl_cmp);
   size_t take = budget <= 0 ? 0 : ((size_t)budget < n ? (size_t)budget : n);
   for (int32_t r = 0; r < R; ++r) L[r] = 0;
@@ -152,6 +172,11 @@ int orc_dvl(const float* a, int32_t R, int32_t b, int32_t budget, float* s, int3
     tgt_off[r + 1] = tgt_off[r] + L[r] + 1;
   }
   return bad;
+}
+
+int orc_dvl(const float* a, int32_t R, int32_t b, int32_t budget, float* s, int32_t* L,
+            int32_t* pos_off, int32_t* tgt_off) {
+  return orc_dvl_ragged(a, R, b, NULL, budget, s, L, pos_off, tgt_off);
 }
 
 double orc_dvl_objective(const float* s, const int32_t* L, int32_t R, int32_t b) {

@@ -64,6 +64,13 @@ void orc_uniform_words(uint64_t seed, int32_t R, int32_t n_pos, uint32_t* out);
  * an input lies outside [0, 1] (outputs still written). */
 int orc_dvl(const float* a, int32_t R, int32_t b, int32_t budget,
             float* s, int32_t* L, int32_t* pos_off, int32_t* tgt_off);
+/* The same with a block length b_r per request (block_len[R], NULL = b):
+ * only positions i < b_r are candidates; s[r*b+i] = 0 for i >= b_r; the
+ * budget is capped at sum_r b_r.  Returns 2 (nothing written) if some b_r
+ * lies outside [0, b]; else as orc_dvl (estimates of undrafted positions are
+ * not checked). */
+int orc_dvl_ragged(const float* a, int32_t R, int32_t b, const int32_t* block_len, int32_t budget,
+                   float* s, int32_t* L, int32_t* pos_off, int32_t* tgt_off);
 /* objective sum_r sum_{i<L_r} s[r*b+i] in double */
 double orc_dvl_objective(const float* s, const int32_t* L, int32_t R, int32_t b);
 

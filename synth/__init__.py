@@ -76,6 +76,7 @@ class Workload:
     seeds: np.ndarray           # [S] uint64 verification seeds
     branch_tok: Optional[np.ndarray] = None  # [R, K, b] drafter's greedy branch tokens
     branch_T: float = 0.0       # mixture branches: 0 greedy; > 0 sampled from softmax(c / branch_T)
+    block_len: Optional[np.ndarray] = None  # [R] drafted positions per request (None: b for every request)
 
     @property
     def steps(self) -> int:
@@ -184,11 +185,22 @@ def make(name: str, *, R: int, b: int = 16, V: int = QWEN3_VOCAB, K: int = 0, dt
 
 # ------------------------------------------------------------ the five workloads
 def config(c: int, *, V: Optional[int] = None, R: Optional[int] = None, steps: Optional[int] = None,
-           threads: Optional[int] = None, branch_T: float = 0.0) -> Workload:
+           threads: Optional[int] = None, branch_T: float = 0.0, ragged: bool = False) -> Workload:
     """Workload c = 1..5 (sizes may be shrunk for quick parity cases).  For the
-    mixture workloads (4, 5) ``branch_T`` > 0 gives the soft-branch drafter."""
+    mixture workloads (4, 5) ``branch_T`` > 0 gives the soft-branch drafter.
+    ``ragged`` gives every request its own block length b_r, uniform on
+    0..b (seeded), of which only the first b_r drafted positions count."""
     if branch_T and c not in (4, 5):
         raise ValueError("branch_T applies to the mixture workloads 4 and 5")
+    w = _config(c, V=V, R=R, steps=steps, threads=threads, branch_T=branch_T)
+    if ragged:
+        rng = np.random.default_rng(np.random.SeedSequence([2000 + c, w.R]))
+        w.block_len = rng.integers(0, w.b + 1, size=w.R).astype(np.int32)
+        w.name += "-ragged"
+    return w
+
+
+def _config(c: int, *, V, R, steps, threads, branch_T) -> Workload:
     soft = f"-softTb{branch_T:g}" if branch_T else ""
     if c == 1:
         R_ = R or 4

@@ -32,7 +32,7 @@ def gpu_step_runner(w: synth.Workload, device="cuda", two_streams: bool = False,
     if soft:
         fused = True  # soft branches run on the fused calls
     vs = VerifyStep(R=R, b=b, V=V, dtype=w.dtype, K=K, max_pos=max_pos, device=device, diagnostics=True,
-                    soft_branches=soft)
+                    soft_branches=soft, ragged=w.block_len is not None)
     full = to_device_rows(w.tgt, ld, device)  # [R*(b+1), ld]
     packed = torch.empty_like(full)
     draft = to_device_rows(w.draft, ld, device) if K == 0 else None
@@ -42,13 +42,13 @@ def gpu_step_runner(w: synth.Workload, device="cuda", two_streams: bool = False,
     def run(s: int) -> dict:
         vs.set_inputs(T=w.T, x=w.x[s], seed=int(w.seeds[s]), top_p=w.top_p, mix=w.mix,
                       a=None if w.a is None else w.a[s], budget=w.budget,
-                      branch_T=w.branch_T if soft else None)
+                      branch_T=w.branch_T if soft else None, block_len=w.block_len)
         if w.budget is not None:
             vs.run_dvl()
             L = vs.L.cpu().numpy()
         else:
             vs.set_full_verification()
-            L = np.full(R, b, np.int32)
+            L = np.full(R, b, np.int32) if w.block_len is None else w.block_len.copy()
         pack_rows_device(full, L, b + 1, packed)
         vs.run_verify(packed, ld, draft=draft, draft_ld=ld, comp=comp, comp_ld=ld, side_stream=side, fused=fused)
         return vs.results()
@@ -72,7 +72,7 @@ def gpu_graph_runner(w: synth.Workload, device="cuda"):
     max_pos = min(w.budget, R * b) if w.budget is not None else R * b
     soft = bool(np.any(np.asarray(w.branch_T) > 0))
     vs = VerifyStep(R=R, b=b, V=V, dtype=w.dtype, K=K, max_pos=max_pos, device=device, diagnostics=True,
-                    soft_branches=soft)
+                    soft_branches=soft, ragged=w.block_len is not None)
     full = to_device_rows(w.tgt, ld, device)
     packed = torch.empty((vs.max_rows, ld), dtype=full.dtype, device=device)
     slots = torch.arange(vs.max_rows, dtype=torch.int32, device=device)
@@ -82,7 +82,7 @@ def gpu_graph_runner(w: synth.Workload, device="cuda"):
     def set_step(s: int):
         vs.set_inputs(T=w.T, x=w.x[s], seed=int(w.seeds[s]), top_p=w.top_p, mix=w.mix,
                       a=None if w.a is None else w.a[s], budget=w.budget,
-                      branch_T=w.branch_T if soft else None)
+                      branch_T=w.branch_T if soft else None, block_len=w.block_len)
         if w.budget is None:
             vs.set_full_verification()
 
@@ -106,9 +106,9 @@ def gpu_graph_runner(w: synth.Workload, device="cuda"):
 def oracle_step(w: synth.Workload, s: int) -> dict:
     R, b, V, K = w.R, w.b, w.V, w.K
     if w.budget is not None:
-        dv = oracle.dvl(w.a[s], w.budget)
+        dv = oracle.dvl(w.a[s], w.budget, block_len=w.block_len)
     else:
-        L = np.full(R, b, np.int32)
+        L = np.full(R, b, np.int32) if w.block_len is None else w.block_len.astype(np.int32)
         dv = {"L": L, "s": None, "pos_off": np.concatenate([[0], np.cumsum(L)]).astype(np.int32),
               "tgt_off": np.concatenate([[0], np.cumsum(L + 1)]).astype(np.int32)}
     L = dv["L"]

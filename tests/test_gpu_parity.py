@@ -78,8 +78,56 @@ def test_dvl_bitexact(R, b, kind, B, a):
     L = torch.zeros(R, dtype=torch.int32, **d)
     po = torch.zeros(R + 1, dtype=torch.int32, **d)
     to = torch.zeros(R + 1, dtype=torch.int32, **d)
-    sv.dvl_alloc_pack(at, R, b, bud, s, L, po, to, ws, nb)
+    sv.dvl_alloc_pack(at, R, b, None, bud, s, L, po, to, ws, nb)
     o = oracle.dvl(a, B)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), o["s"].reshape(-1).view(np.uint32))
+    assert np.array_equal(L.cpu().numpy(), o["L"])
+    assert np.array_equal(po.cpu().numpy(), o["pos_off"])
+    assert np.array_equal(to.cpu().numpy(), o["tgt_off"])
+    assert sv.sv_get_status(ws) == 0
+
+
+def _dvl_ragged_cases():
+    rng = np.random.default_rng(8)
+    cases = []
+    for R, b in [(1, 1), (3, 5), (32, 16), (7, 64), (64, 16), (600, 16)]:
+        for pattern in ("random", "zeros_and_full", "all_zero"):
+            if pattern == "random":
+                bl = rng.integers(0, b + 1, size=R)
+            elif pattern == "zeros_and_full":
+                bl = np.where(rng.random(R) < 0.5, 0, b)
+            else:
+                bl = np.zeros(R)
+            bl = bl.astype(np.int32)
+            kind = "ties" if R % 2 else "beta"
+            a = (rng.choice([0.0, 0.5, 0.75, 1.0], size=(R, b)) if kind == "ties"
+                 else rng.beta(8, 2, size=(R, b))).astype(np.float32)
+            n = int(bl.sum())
+            for B in sorted({0, 1, n // 2, max(n - 1, 0), n, n + 3, R * b}):
+                cases.append((R, b, pattern, B, a, bl))
+    return cases
+
+
+@pytest.mark.parametrize("R,b,pattern,B,a,bl", _dvl_ragged_cases(),
+                         ids=lambda v: str(v) if not hasattr(v, "shape") else "arr")
+def test_dvl_ragged_block_lengths_bitexact(R, b, pattern, B, a, bl):
+    """Per-request block length b_r: only the first b_r positions of request r
+    are candidates (scores past b_r are 0); bit-exact against the oracle."""
+    import torch
+
+    sv = _sv()
+    banner(f"dvl_alloc_pack ragged R={R} b={b} {pattern} B={B}")
+    ws, nb = sv.make_workspace(R, b, 0, 8)
+    d = dict(device="cuda")
+    at = torch.from_numpy(a.reshape(-1)).to(**d)
+    blt = torch.from_numpy(bl).to(**d)
+    bud = torch.tensor([B], dtype=torch.int32, **d)
+    s = torch.full((R * b,), 7.0, dtype=torch.float32, **d)
+    L = torch.zeros(R, dtype=torch.int32, **d)
+    po = torch.zeros(R + 1, dtype=torch.int32, **d)
+    to = torch.zeros(R + 1, dtype=torch.int32, **d)
+    sv.dvl_alloc_pack(at, R, b, blt, bud, s, L, po, to, ws, nb)
+    o = oracle.dvl(a, B, block_len=bl)
     assert np.array_equal(s.cpu().numpy().view(np.uint32), o["s"].reshape(-1).view(np.uint32))
     assert np.array_equal(L.cpu().numpy(), o["L"])
     assert np.array_equal(po.cpu().numpy(), o["pos_off"])
@@ -440,3 +488,45 @@ def test_soft_branches_per_request_temperatures():
         rep = compare_step(w, run(s), oracle_step(w, s), rep)
     assert_rate(rep)
     assert _sv().sv_get_status(vs.ws) == 0
+
+
+# ---------------------------------------------------------------- per-request block length
+RAGGED = [(3, dict(V=2053, R=8, steps=3)), (5, dict(V=4099, R=8, steps=3)), (4, dict(V=4099, R=6)),
+          (2, dict(V=2053, R=6)), (1, dict()), (5, dict(steps=2)), (5, dict(V=4099, R=8, steps=2, branch_T=1.0))]
+
+
+@pytest.mark.parametrize("c,kw", RAGGED, ids=[f"cfg{c}-" + "-".join(f"{k}{v}" for k, v in kw.items()) for c, kw in RAGGED])
+def test_ragged_block_lengths_match_oracle(c, kw):
+    """Every request drafted its own number b_r of positions (some 0): DVL
+    chooses among drafted positions only, or all b_r are verified without a
+    budget; the whole step against the oracle."""
+    w = synth.config(c, ragged=True, **kw)
+    vs, run = gpu_step_runner(w, fused=True)
+    rep = None
+    for s in range(w.steps):
+        banner(f"ragged {w.name} V={w.V} R={w.R} b_r={w.block_len.tolist()} step {s}")
+        g = run(s)
+        assert (g["L"] <= w.block_len).all()
+        rep = compare_step(w, g, oracle_step(w, s), rep)
+    assert_rate(rep)
+    assert _sv().sv_get_status(vs.ws) == 0
+
+
+def test_graph_replay_block_lengths_change():
+    """Block lengths, like the budget, sit at fixed addresses: one captured
+    graph replays with new b_r per step."""
+    w = synth.config(5, V=4099, R=8, steps=3, ragged=True)
+    _, _, run_graph = gpu_graph_runner(w)
+    _, run_eager = gpu_step_runner(w, fused=True)
+    rng = np.random.default_rng(17)
+    rep = None
+    for k in range(5):
+        s = k % w.steps
+        w.block_len = rng.integers(0, w.b + 1, size=w.R).astype(np.int32)
+        if k == 1:
+            w.block_len[:] = 0
+        banner(f"graph replay ragged step {s} b_r={w.block_len.tolist()}")
+        g = run_graph(s)
+        _same_bits(g, run_eager(s))
+        rep = compare_step(w, g, oracle_step(w, s), rep)
+    assert_rate(rep)

@@ -89,6 +89,6 @@ def test_argument_errors_are_reported_before_launch(sv):
     args65 = [p, 1, 64, 64, p, p, 2, 65, p, p, p, p, p]
     assert L.sv_accept(*args65, 1, None, 1, 0, None, None, p, p, p, None, None, None, wp, nb, None) == sv.SV_ERR_ARG
     # DVL: b over 64, null budget
-    assert L.dvl_alloc_pack(p, 4, 65, p, p, p, p, p, wp, nb, None) == sv.SV_ERR_ARG
-    assert L.dvl_alloc_pack(p, 4, 16, None, p, p, p, p, wp, nb, None) == sv.SV_ERR_ARG
+    assert L.dvl_alloc_pack(p, 4, 65, None, p, p, p, p, p, wp, nb, None) == sv.SV_ERR_ARG
+    assert L.dvl_alloc_pack(p, 4, 16, None, None, p, p, p, p, wp, nb, None) == sv.SV_ERR_ARG
     assert sv.sv_status_string(sv.SV_ERR_WORKSPACE) == "workspace too small"

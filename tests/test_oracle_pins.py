@@ -379,6 +379,65 @@ def test_dvl_brute_force_optimum():
             np.testing.assert_array_equal(o["tgt_off"], np.concatenate([[0], np.cumsum(o["L"] + 1)]))
 
 
+def _brute_dvl_ragged(s, bl, B):
+    R, b = s.shape
+    pref = np.concatenate([np.zeros((R, 1)), np.cumsum(s.astype(np.float64), axis=1)], axis=1)
+    best, arg, count = -1.0, None, 0
+    for L in itertools.product(*[range(int(x) + 1) for x in bl]):
+        if sum(L) > B:
+            continue
+        obj = sum(pref[r, L[r]] for r in range(R))
+        if obj > best + 1e-15:
+            best, arg, count = obj, L, 1
+        elif abs(obj - best) <= 1e-15:
+            count += 1
+    return best, np.array(arg), count
+
+
+def test_dvl_ragged_block_lengths_brute_force():
+    """Per-request block length ("Why does throughput collapse under high
+    concurrency?", section "How does draft quality decay with block length and
+    sampling temperature?": BlockPilot's block size varies per request): request r drafted b_r positions; the allocation
+    over its prefixes of length <= b_r is checked against exhaustive search."""
+    rng = np.random.default_rng(43)
+    for trial in range(150):
+        R, b = int(rng.integers(1, 5)), int(rng.integers(1, 6))
+        bl = rng.integers(0, b + 1, size=R).astype(np.int32)
+        if trial % 3 == 0:
+            a = rng.choice([0.0, 0.25, 0.5, 1.0], size=(R, b)).astype(np.float32)
+        else:
+            a = rng.beta(8, 2, size=(R, b)).astype(np.float32)
+        n = int(bl.sum())
+        for B in range(0, n + 2):
+            o = oracle.dvl(a, B, block_len=bl)
+            assert o["bad"] == 0
+            for r in range(R):
+                np.testing.assert_array_equal(o["s"][r, :bl[r]], np.cumprod(a[r, :bl[r]], dtype=np.float32))
+                assert (o["s"][r, bl[r]:] == 0).all()
+            assert (o["L"] <= bl).all() and o["L"].sum() == min(B, n)
+            best, arg, count = _brute_dvl_ragged(o["s"], bl, B)
+            assert oracle.dvl_objective(o["s"], o["L"]) == pytest.approx(best, abs=1e-12)
+            if count == 1:
+                np.testing.assert_array_equal(o["L"], arg)
+            np.testing.assert_array_equal(o["pos_off"], np.concatenate([[0], np.cumsum(o["L"])]))
+            np.testing.assert_array_equal(o["tgt_off"], np.concatenate([[0], np.cumsum(o["L"] + 1)]))
+
+
+def test_dvl_ragged_special_cases():
+    a = np.full((4, 16), 0.9, np.float32)
+    full = np.full(4, 16, np.int32)
+    for B in (0, 7, 33, 64):
+        u, g = oracle.dvl(a, B), oracle.dvl(a, B, block_len=full)
+        for k in ("s", "L", "pos_off", "tgt_off"):
+            np.testing.assert_array_equal(u[k], g[k])
+    bl = np.array([16, 0, 5, 9], np.int32)
+    assert list(oracle.dvl(a, 1000, block_len=bl)["L"]) == [16, 0, 5, 9]   # budget above sum b_r
+    assert list(oracle.dvl(a, 12, block_len=bl)["L"]) == [4, 0, 4, 4]     # equal scores: even split
+    assert list(oracle.dvl(a, 19, block_len=bl)["L"]) == [7, 0, 5, 7]     # request 2 is exhausted
+    with pytest.raises(ValueError):
+        oracle.dvl(a, 10, block_len=np.array([17, 0, 0, 0], np.int32))
+
+
 def test_dvl_special_cases():
     a = np.full((4, 16), 0.9, np.float32)
     assert list(oracle.dvl(a, 64)["L"]) == [16] * 4          # full capacity
