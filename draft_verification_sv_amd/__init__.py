@@ -41,6 +41,13 @@ class SvError(RuntimeError):
     pass
 
 
+# torch first: its libraries load the HIP runtime it ships (by the name
+# libamdhip64.so), and libsv, loaded after it, binds to that same runtime by
+# soname.  Loaded the other way round, libsv would pull in the system runtime
+# and torch a second one beside it, and torch's streams would be foreign to
+# libsv's launches.
+import torch  # noqa: E402,F401
+
 if not os.path.exists(LIB_PATH):
     raise ImportError(
         f"libsv.so not found at {LIB_PATH}; build it with `python -m draft_verification_sv_amd.build` "

@@ -92,3 +92,20 @@ def test_argument_errors_are_reported_before_launch(sv):
     assert L.dvl_alloc_pack(p, 4, 65, None, p, p, p, p, p, wp, nb, None) == sv.SV_ERR_ARG
     assert L.dvl_alloc_pack(p, 4, 16, None, None, p, p, p, p, wp, nb, None) == sv.SV_ERR_ARG
     assert sv.sv_status_string(sv.SV_ERR_WORKSPACE) == "workspace too small"
+
+
+def test_one_hip_runtime_when_the_package_is_imported_first():
+    """Importing the package before torch must not load a second HIP runtime
+    beside the one torch ships (libsv's launches would then go to streams of
+    the other runtime and fail)."""
+    import ast
+    import subprocess
+    import sys
+
+    code = ("import draft_verification_sv_amd, torch\n"
+            "print(sorted({l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}))\n")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300,
+                         cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert out.returncode == 0, out.stderr
+    paths = ast.literal_eval(out.stdout.strip().splitlines()[-1])
+    assert len(paths) == 1, paths
