@@ -112,11 +112,13 @@ def _gumbel_argmax(rng, logits: np.ndarray, T: float) -> np.ndarray:
 def make(name: str, *, R: int, b: int = 16, V: int = QWEN3_VOCAB, K: int = 0, dtype: str = "bf16",
          target: str = "zipf", draft_sigma: float = 1.0, comp_sigma: float = 1.5,
          T=1.0, top_p: Optional[float] = None, budget: Optional[int] = None, steps: int = 1,
-         seed: int = 1000, vseed: int = 1, threads: Optional[int] = None, branch_T: float = 0.0) -> Workload:
+         seed: int = 1000, vseed: int = 1, threads: Optional[int] = None, branch_T: float = 0.0,
+         cat_T: float = 1.0) -> Workload:
     """Draw one workload.  ``target`` is "zipf" (Zipfian base + N(0,1)) or
     "normal2" (N(0, 2^2)); ``K`` > 0 selects the latent-mixture drafter, whose
     branches decode greedily (``branch_T`` = 0) or sample from
-    softmax(c / branch_T)."""
+    softmax(c / branch_T); its category is drawn from softmax(mix / cat_T)
+    (``cat_T`` = 0: the argmax category)."""
     threads = threads or _default_threads()
     ss = np.random.SeedSequence(seed)
     kids = ss.spawn(R + 1)
@@ -171,7 +173,7 @@ def make(name: str, *, R: int, b: int = 16, V: int = QWEN3_VOCAB, K: int = 0, dt
         )
         x = np.empty((steps, R, b), np.int32)
         for s in range(steps):
-            zs = _gumbel_argmax(rng, mix, 1.0)
+            zs = _gumbel_argmax(rng, mix, cat_T)
             if branch_T == 0.0:
                 x[s] = branch_tok[np.arange(R), zs]
             else:  # the drafter samples every position of the chosen branch

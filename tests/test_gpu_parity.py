@@ -530,3 +530,23 @@ def test_graph_replay_block_lengths_change():
         _same_bits(g, run_eager(s))
         rep = compare_step(w, g, oracle_step(w, s), rep)
     assert_rate(rep)
+
+
+# ---------------------------------------------------------------- temperature / category-temperature sweep
+def test_sweep_points_match_oracle():
+    """The sweep's steps (K = 1 and K = 8 greedy branches, category temperature
+    ZT applied to the mixing logits, ZT = 0 giving -inf logits off the argmax
+    category, target temperatures 0 to 2) against the oracle."""
+    from draft_verification_sv_amd import sweep
+
+    temps = (0.0, 1.0, 2.0)
+    rep = None
+    for K, ZT in ((1, 0.0), (8, 0.0), (8, 0.6), (8, 1.4)):
+        w = sweep.workload(K, ZT, V=1031, R=8, steps=2)
+        banner(f"sweep K={K} ZT={ZT}")
+        res = sweep.verify_steps(w, temps)
+        for T in temps:
+            w.T = np.full(w.R, T, np.float32)
+            for s in range(w.steps):
+                rep = compare_step(w, res[T][s], oracle_step(w, s), rep)
+    assert_rate(rep)
