@@ -212,7 +212,9 @@ __device__ __forceinline__ void count_vec(uint32_t* hist, const uint4& d, uint4&
 __device__ __forceinline__ double bin_mass(const uint32_t* hist, int d, double Td, double M) {
   const int bin = 2 * kSide - d;
   const uint32_t c = hist_get(hist, bin);
-  return c ? static_cast<double>(c) * exp(static_cast<double>(bin_value(bin)) / Td - M) : 0.0;
+  double m = 0.0;
+  if (c) m = static_cast<double>(c) * exp(static_cast<double>(bin_value(bin)) / Td - M);
+  return m;
 }
 
 template <int DT, int NT, int BATCH>
@@ -331,7 +333,10 @@ __device__ __forceinline__ void row_stats_at(const RowArgs& a, const void* rowp,
       constexpr int NW = NT / kWave;
       const int lane = tid & (kWave - 1), wv = tid / kWave;
       for (int rr = wv; rr < kMassRows; rr += NW) {
-        const double tot = wave_sum_f64(bin_mass(hist, rr * kWave + lane, Td, M));
+        // a 64-bin row with no token (most rows outside the values' binades) skips the exp
+        const double tot = __ballot(hist_get(hist, 2 * kSide - (rr * kWave + lane)) != 0u)
+                               ? wave_sum_f64(bin_mass(hist, rr * kWave + lane, Td, M))
+                               : 0.0;
         if (lane == 0) sh.rowtot[rr] = tot;
       }
       __syncthreads();

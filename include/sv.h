@@ -207,8 +207,9 @@ int32_t sv_mixture_q(const void* comp_logits, int32_t dtype, int64_t ld, int32_t
  *                branch is a distribution q_i(. | y, z)], here
  *                softmax(c / T_b,r) (float, device): each component row is
  *                streamed by one block that forms its argmax, maximum and
- *                log sum_v exp(c_v / T_b,r) (double, exact bf16 histogram as
- *                for target rows); T_b,r = 0 keeps point-mass branches at the
+ *                log sum_v exp(c_v / T_b,r) (fp32 exponentials and partial
+ *                sums, double across vectors and threads; fp32 rows: double
+ *                throughout); T_b,r = 0 keeps point-mass branches at the
  *                argmax for that request.  NULL: greedy branches for every
  *                request (the four-block partial argmax above).  Pass the
  *                same branch_T to the following sv_accept_sample.
