@@ -698,35 +698,36 @@ template <int DT>
 __device__ __forceinline__ void soft_group(const SampleArgs& a, const char* trowp, const char* crow0, size_t cstride,
                                            const double* off, int g, float cut, double invT, double kept,
                                            double invTb, double p8[8], double w8[8]) {
+  constexpr int kB = 8;  // branch rows whose 16-byte words are in flight together
   const int V = a.V, NG = groups_of(V), K = a.K;
   const int gc = min(g, NG - 1);
-  uint4 t0, t1;
+  uint4 t0, t1, c0[kB], c1[kB];
   raw8<DT>(trowp, gc, V, t0, t1);
+#pragma unroll
+  for (int j = 0; j < kB; ++j) raw8<DT>(crow0 + cstride * min(j, K - 1), gc, V, c0[j], c1[j]);
+  asm volatile("" ::: "memory");  // every load above is issued before any is used
   float l[8];
   decode8<DT>(t0, t1, g, V, g < NG, l);
   double q8[8];
-  bool any = false;
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
     p8[q] = l[q] > -INFINITY ? p_of(l[q], cut, invT, kept) : 0.0;
     q8[q] = 0.0;
-    any |= p8[q] > 0.0;
   }
-  if (any) {
-    for (int z0 = 0; z0 < K; z0 += 4) {  // four branch rows' loads in flight at a time
-      uint4 c0[4], c1[4];
+  for (int z0 = 0; z0 < K; z0 += kB) {
+    if (z0 > 0) {  // K > 8 only
 #pragma unroll
-      for (int j = 0; j < 4; ++j) raw8<DT>(crow0 + cstride * min(z0 + j, K - 1), gc, V, c0[j], c1[j]);
+      for (int j = 0; j < kB; ++j) raw8<DT>(crow0 + cstride * min(z0 + j, K - 1), gc, V, c0[j], c1[j]);
+    }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const double o = off[min(z0 + j, K - 1)];
-        if (z0 + j < K && o < INFINITY) {
-          float cv[8];
-          unpack8<DT>(c0[j], c1[j], cv);
+    for (int j = 0; j < kB; ++j) {
+      const double o = off[min(z0 + j, K - 1)];
+      if (z0 + j < K && o < INFINITY) {
+        float cv[8];
+        unpack8<DT>(c0[j], c1[j], cv);
 #pragma unroll
-          for (int q = 0; q < 8; ++q)
-            if (p8[q] > 0.0) q8[q] += exp(static_cast<double>(cv[q]) * invTb - o);
-        }
+        for (int q = 0; q < 8; ++q)
+          if (p8[q] > 0.0) q8[q] += exp(static_cast<double>(cv[q]) * invTb - o);
       }
     }
   }
@@ -737,32 +738,27 @@ __device__ __forceinline__ void soft_group(const SampleArgs& a, const char* trow
   }
 }
 
-// D (soft residual): sums of p and of the draw weight over the sub-chunks of
-// chunk ch, one group per lane, one sub-chunk at a time per wave.
+// D (soft residual): sums of p and of the draw weight over sub-chunk `sub`
+// (one group per lane) by one wave.
 template <int DT>
-__device__ __forceinline__ void sub_sums_soft(const SampleArgs& a, const DrawCtx& c, int r, int ch) {
-  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+__device__ __forceinline__ void sub_sum_soft(const SampleArgs& a, const DrawCtx& c, int r, int sub) {
+  const int lane = threadIdx.x & (kWave - 1);
   const char* trowp = row_ptr(a.tgt, DT, c.trow, a.tgt_ld);
   const char* crow0 = row_ptr(a.comp, DT, c.drow, a.comp_ld);
   const size_t cstride = static_cast<size_t>(a.b) * static_cast<size_t>(a.comp_ld) * (DT == SV_BF16 ? 2 : 4);
-  const int sub0 = ch * kChunkSubs + wv;
-  for (int k = 0; k < kSubPerWave; ++k) {
-    const int sub = sub0 + k * (kSumNT / kWave);
-    if (sub >= a.NSUB) break;  // wave-uniform
-    double p8[8], w8[8];
-    soft_group<DT>(a, trowp, crow0, cstride, c.cw, sub * kSubG + lane, c.cut, c.invT, c.kept, c.invTb, p8, w8);
-    double sp = 0.0, sw = 0.0;
+  double p8[8], w8[8];
+  soft_group<DT>(a, trowp, crow0, cstride, c.cw, sub * kSubG + lane, c.cut, c.invT, c.kept, c.invTb, p8, w8);
+  double sp = 0.0, sw = 0.0;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      sp += p8[q];
-      sw += w8[q];
-    }
-    const double tp = wave_sum_f64(sp), tw = wave_sum_f64(sw);
-    if (lane == 0) {
-      double* pp = a.sub + (static_cast<size_t>(r) * a.NSUB + sub) * 2;
-      pp[0] = tw;
-      pp[1] = tp;
-    }
+  for (int q = 0; q < 8; ++q) {
+    sp += p8[q];
+    sw += w8[q];
+  }
+  const double tp = wave_sum_f64(sp), tw = wave_sum_f64(sw);
+  if (lane == 0) {
+    double* pp = a.sub + (static_cast<size_t>(r) * a.NSUB + sub) * 2;
+    pp[0] = tw;
+    pp[1] = tp;
   }
 }
 
@@ -777,10 +773,17 @@ __host__ __device__ inline size_t soft_tables_bytes(int K, int b) {
          sizeof(double) * static_cast<size_t>(b + 1) * K;
 }
 
-// The fused tail with soft branches (one block per (request, chunk)): A and B
-// load the header, the draft tokens, the mixing logits, the branch argmax and
-// lse of the rows launch and every branch's logit at the draft tokens; C (wave
-// 0) runs the posterior and the acceptance tests; D sums the drawn row.
+// Blocks per request of the soft tail: one sub-chunk per wave, so that the K
+// branch exponentials per value spread over four times the blocks of the
+// greedy tail (whose chunks are kChunkSubs sub-chunks).
+__host__ __device__ inline int soft_chunks(int V) { return (sub_chunks(V) + kSumNT / kWave - 1) / (kSumNT / kWave); }
+
+// The fused tail with soft branches (one block per (request, soft chunk)): A
+// and B load the header, the draft tokens, the mixing logits, the branch
+// argmax and lse of the rows launch and every branch's logit at the draft
+// tokens; C (wave 0) runs the posterior and the acceptance tests; D sums the
+// drawn row: for a soft residual each wave sums one sub-chunk; a p or greedy-
+// branch draw takes the greedy tail's chunks (every fourth block).
 template <int DT>
 __global__ __launch_bounds__(kSumNT) void k_draw_sums_soft(SampleArgs a) {
   __shared__ TailShared sh;
@@ -789,7 +792,8 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums_soft(SampleArgs a) {
   int* g = dyn;
   double* lq = reinterpret_cast<double*>(dyn + ((kb + 1) & ~1));
   double* S = lq + kb;
-  const int r = blockIdx.x / a.S, ch = blockIdx.x % a.S;
+  const int S4 = soft_chunks(V);
+  const int r = blockIdx.x / S4, ch = blockIdx.x % S4;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
   const bool report = ch == 0;
   DrawCtx& c = sh.c;
@@ -952,10 +956,13 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums_soft(SampleArgs a) {
   }
   __syncthreads();  // also ends every use of the tables, which D's lists overwrite
   if (c.mode == kDrawGreedy) return;
-  if (c.mode == kDrawSoft)
-    sub_sums_soft<DT>(a, c, r, ch);
-  else
-    sub_sums<DT, DT, false>(a, c, r, ch, reinterpret_cast<float*>(dyn));
+  constexpr int kPer = kSumNT / kWave;  // sub-chunks of a soft chunk
+  if (c.mode == kDrawSoft) {
+    const int sub = ch * kPer + wv;
+    if (sub < a.NSUB) sub_sum_soft<DT>(a, c, r, sub);
+  } else if (ch % (kChunkSubs / kPer) == 0) {
+    sub_sums<DT, DT, false>(a, c, r, ch / (kChunkSubs / kPer), reinterpret_cast<float*>(dyn));
+  }
 }
 
 // The draw: one wave per request, after the sums.  Lane l holds the sub-chunk
@@ -1210,7 +1217,7 @@ template <int DT>
 static int32_t launch_draw_soft(const SampleArgs& a, hipStream_t s) {
   const size_t tables = soft_tables_bytes(a.K, a.b);
   const size_t dyn = tables > DLists<false>::kBytes ? tables : DLists<false>::kBytes;
-  hipLaunchKernelGGL((k_draw_sums_soft<DT>), dim3(a.R * a.S), dim3(kSumNT), dyn, s, a);
+  hipLaunchKernelGGL((k_draw_sums_soft<DT>), dim3(a.R * soft_chunks(a.V)), dim3(kSumNT), dyn, s, a);
   if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
   hipLaunchKernelGGL((k_pick<DT, DT, false, true>), dim3(a.R), dim3(kWave), 0, s, a);
   return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
