@@ -33,7 +33,7 @@ STATUS_BITS = {
 EXPORTS = [
     "sv_workspace_bytes", "sv_workspace_init", "sv_get_status", "sv_clear_status", "sv_status_string",
     "dvl_alloc_pack", "sv_softmax_stats", "sv_topp_threshold", "sv_mixture_q", "sv_accept",
-    "sv_residual_sample", "sv_philox_uniforms", "sv_verify_rows", "sv_accept_sample",
+    "sv_residual_sample", "sv_philox_uniforms", "sv_verify_rows", "sv_accept_sample", "sv_selftest_exp",
 ]
 
 
@@ -50,7 +50,7 @@ import torch  # noqa: E402,F401
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"libsv.so not found at {LIB_PATH}; build it with `python -m draft_verification_sv_amd.build` "
+        f"libsv.so not found at {LIB_PATH}; build it with `python draft_verification_sv_amd/build.py` "
         "(there is no CPU fallback)"
     )
 
@@ -72,6 +72,7 @@ _SIGS = {
     "sv_residual_sample": [_vp, _i32, _i64, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i64,
                            _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "sv_philox_uniforms": [_vp, _i32, _i32, _vp, _vp],
+    "sv_selftest_exp": [_vp, _vp, _i32, _vp],
     "sv_verify_rows": [_vp, _i32, _i64, _i32, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32,
                        _i32, _vp, _i32, _vp, _vp, _sz, _vp],
     "sv_accept_sample": [_vp, _i32, _i64, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i64,
@@ -220,6 +221,10 @@ def sv_residual_sample(tgt_logits, dtype, tgt_ld, V, tgt_off, pos_off, R, b, tem
                                    _p(draft_logits), draft_dtype, draft_ld, _p(draft_argmax), _p(draft_lse), K,
                                    _p(branch_tok), _p(post_w), _p(seed), _p(n_acc), _p(token), _p(is_bonus), _p(ws),
                                    ws_bytes, _stream(stream)), "sv_residual_sample")
+
+
+def sv_selftest_exp(x, out, n, stream=None):
+    _check(_lib.sv_selftest_exp(_p(x), _p(out), n, _stream(stream)), "sv_selftest_exp")
 
 
 def sv_philox_uniforms(seed, R, n_pos, out, stream=None):

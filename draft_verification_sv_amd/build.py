@@ -1,4 +1,7 @@
-"""Build libsv.so (HIP, gfx950) in the package directory."""
+"""Build libsv.so (HIP, gfx950) in the package directory.
+
+Run as a script (`python draft_verification_sv_amd/build.py`) or load it by
+path: importing the package first would load the library being replaced."""
 from __future__ import annotations
 
 import glob

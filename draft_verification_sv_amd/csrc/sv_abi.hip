@@ -22,9 +22,23 @@ __global__ void k_philox(const uint64_t* seed, int R, int n_pos, uint32_t* out) 
   o[3] = w.w;
 }
 
+__global__ void k_exp_selftest(const double* x, double* out, int n) {
+  __shared__ double tab[kExpTab];
+  exp_table_init(tab);
+  __syncthreads();
+  const int k = blockIdx.x * blockDim.x + threadIdx.x;
+  if (k < n) out[k] = exp_tab(x[k], tab);
+}
+
 }  // namespace sv
 
 using namespace sv;
+
+extern "C" int32_t sv_selftest_exp(const double* x, double* out, int32_t n, void* stream) {
+  if (!x || !out || n < 1) return SV_ERR_ARG;
+  hipLaunchKernelGGL(k_exp_selftest, dim3((n + 255) / 256), dim3(256), 0, static_cast<hipStream_t>(stream), x, out, n);
+  return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
+}
 
 extern "C" int32_t sv_workspace_bytes(int32_t R, int32_t b, int32_t K, int32_t V, size_t* out_bytes) {
   if (!out_bytes || R < 1 || b < 1 || b > 64 || K < 0 || K > 64 || V < 1) return SV_ERR_ARG;

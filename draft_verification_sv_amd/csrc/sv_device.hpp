@@ -266,6 +266,43 @@ __device__ __forceinline__ void raise_status(uint32_t* status, uint32_t bits) {
   __hip_atomic_fetch_or(status, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ------------------------------------------------------------------ exp in double
+// exp(x) by Tang's table method (P. T. P. Tang, "Table-driven implementation
+// of the exponential function in IEEE floating-point arithmetic", ACM TOMS 15,
+// 1989): x = (64 k + j) ln2/64 + r with |r| <= ln2/128, so that
+// exp(x) = 2^k 2^(j/64) e^r; e^r by its Taylor polynomial of degree 5 (the
+// first omitted term is below 4e-17 relative), 2^(j/64) from a 64-entry table
+// in LDS (exp_table_init), 2^k by ldexp, which rounds once and underflows
+// gradually.  ln2/64 is split into a 36-bit head (k times it is exact for
+// |k| < 2^17) and the rounded remainder.  Meant for the arguments of the
+// probabilities (x <= 0 up to rounding); x < -746 gives 0 and NaN stays NaN.
+constexpr int kExpTab = 64;
+
+// tab[t] = 2^(t/64), by threads 0..63 of the block; the caller's next barrier
+// publishes it.
+__device__ __forceinline__ void exp_table_init(double* tab) {
+  const int t = threadIdx.x;
+  if (t < kExpTab) tab[t] = exp2(static_cast<double>(t) / kExpTab);
+}
+
+__device__ __forceinline__ double exp_tab(double x, const double* tab) {
+  constexpr double kInvStep = 0x1.71547652b82fep+6;    // 64 / ln 2
+  constexpr double kStepHi = 0x1.62e42fefa0000p-7;     // ln 2 / 64, 36 significant bits
+  constexpr double kStepLo = 0x1.cf79abc9e3b3ap-46;    // ln 2 / 64 - kStepHi
+  const double xc = x > -746.0 ? x : -746.0;           // NaN and -inf handled at the end
+  const double kd = __builtin_rint(xc * kInvStep);
+  const int k = static_cast<int>(kd);
+  double r = fma(-kd, kStepHi, xc);
+  r = fma(-kd, kStepLo, r);
+  double p = fma(r, 1.0 / 120.0, 1.0 / 24.0);
+  p = fma(p, r, 1.0 / 6.0);
+  p = fma(p, r, 0.5);
+  p = fma(p, r, 1.0);
+  p = fma(p, r, 1.0);
+  const double y = ldexp(tab[k & (kExpTab - 1)] * p, k >> 6);
+  return x > -746.0 ? y : (x != x ? x : 0.0);
+}
+
 // ------------------------------------------------------------------ the draw's row layout
 // The row a request draws from is cut into sub-chunks of 64 8-value groups
 // (512 values, one group per lane of a wave); one block of the sums kernel

@@ -345,6 +345,7 @@ __global__ __launch_bounds__(kFusedNT) void k_rows_mix(RowArgs ra, MixArgs ma, i
     if (blk == 0 && threadIdx.x == 0 && (ra.row_off[0] != 0 || total > ra.max_rows || total < 0))
       raise_status(ra.status, SV_ST_BAD_OFFSETS);
     if (blk >= total) return;
+    exp_table_init(sh.etab);  // published by row_block's first barrier
     row_block<DT, kFusedNT, kFusedBatch>(ra, blk, hist, sh);
   } else {
     const int u = blk - n_row_blocks;

@@ -17,6 +17,7 @@ __global__ __launch_bounds__(kRowNT) void k_row_stats(RowArgs a) {
   if (p == 0 && threadIdx.x == 0 && (a.row_off[0] != 0 || total > a.max_rows || total < 0))
     raise_status(a.status, SV_ST_BAD_OFFSETS);
   if (p >= total) return;
+  exp_table_init(sh.etab);  // published by row_block's first barrier
   row_block<DT, kRowNT, kRowBatch>(a, p, hist, sh);
 }
 

@@ -109,6 +109,7 @@ struct RowShared {
   double red_f64[NT / kWave];
   int red_i32[NT / kWave];
   double rowtot[kMassRows];
+  double etab[kExpTab];  // the exponential's table (exp_table_init at the kernel's start)
   int req;
   int cut_d;
   double F;
@@ -209,11 +210,11 @@ __device__ __forceinline__ void count_vec(uint32_t* hist, const uint4& d, uint4&
 }
 
 // Mass of in-range bin number d in descending order (d = 0 is bin 12288).
-__device__ __forceinline__ double bin_mass(const uint32_t* hist, int d, double Td, double M) {
+__device__ __forceinline__ double bin_mass(const uint32_t* hist, int d, double Td, double M, const double* tab) {
   const int bin = 2 * kSide - d;
   const uint32_t c = hist_get(hist, bin);
   double m = 0.0;
-  if (c) m = static_cast<double>(c) * exp(static_cast<double>(bin_value(bin)) / Td - M);
+  if (c) m = static_cast<double>(c) * exp_tab(static_cast<double>(bin_value(bin)) / Td - M, tab);
   return m;
 }
 
@@ -335,7 +336,7 @@ __device__ __forceinline__ void row_stats_at(const RowArgs& a, const void* rowp,
       for (int rr = wv; rr < kMassRows; rr += NW) {
         // a 64-bin row with no token (most rows outside the values' binades) skips the exp
         const double tot = __ballot(hist_get(hist, 2 * kSide - (rr * kWave + lane)) != 0u)
-                               ? wave_sum_f64(bin_mass(hist, rr * kWave + lane, Td, M))
+                               ? wave_sum_f64(bin_mass(hist, rr * kWave + lane, Td, M, sh.etab))
                                : 0.0;
         if (lane == 0) sh.rowtot[rr] = tot;
       }
@@ -386,7 +387,7 @@ __device__ __forceinline__ void row_stats_at(const RowArgs& a, const void* rowp,
       }
       crow = bcast_i32(crow, cl);
       cbase = bcast_f64(cbase, cl);
-      const double mass = bin_mass(hist, crow * kWave + lane, Td, M);
+      const double mass = bin_mass(hist, crow * kWave + lane, Td, M, sh.etab);
       const double inc2 = cbase + wave_incl_scan_f64(mass);
       const uint64_t hit = __ballot(inc2 >= target);
       int cut_d;

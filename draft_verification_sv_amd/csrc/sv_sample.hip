@@ -87,8 +87,9 @@ __device__ __forceinline__ const char* row_ptr(const void* base, int dtype, int6
 }
 
 // target probability of a token with logit l: [l >= cut] exp(l / T - kept_lse), T > 0
-__device__ __forceinline__ double p_of(float l, float cut, double invT, double kept) {
-  return l >= cut ? exp(static_cast<double>(l) * invT - kept) : 0.0;
+// (tab: the exponential's table, exp_table_init)
+__device__ __forceinline__ double p_of(float l, float cut, double invT, double kept, const double* tab) {
+  return l >= cut ? exp_tab(static_cast<double>(l) * invT - kept, tab) : 0.0;
 }
 
 // The 8 values of group g (elements 8g .. 8g+7) as raw 16-byte words, issued
@@ -160,7 +161,8 @@ __device__ __forceinline__ bool request_ok(const SampleArgs& a, int r, int& pb, 
 // ------------------------------------------------------------------ standalone acceptance (one wave)
 // Lane i < L_r tests position i + 1 (1-based).  q comes from the given
 // q_at_draft (mixture) or from the dense draft row.  Returns n_acc on every lane.
-__device__ __forceinline__ int accept_wave(const SampleArgs& a, int r, int pb, int Lr, int tb, const double* qx) {
+__device__ __forceinline__ int accept_wave(const SampleArgs& a, int r, int pb, int Lr, int tb, const double* qx,
+                                           const double* tab) {
   const int i = threadIdx.x & (kWave - 1);
   const uint64_t seed = *a.seed;
   const float T = a.T[r];
@@ -177,7 +179,7 @@ __device__ __forceinline__ int accept_wave(const SampleArgs& a, int r, int pb, i
         p = xv == a.row_argmax[trow] ? 1.0 : 0.0;
       } else {
         const float l = load_val_rt(row_ptr(a.tgt, a.dtype, trow, a.tgt_ld), a.dtype, xv);
-        p = p_of(l, a.row_cut[trow], invT, a.row_kept[trow]);
+        p = p_of(l, a.row_cut[trow], invT, a.row_kept[trow], tab);
       }
       if (a.q_mode == SV_Q_MIXTURE) {
         q = qx[i];
@@ -188,7 +190,7 @@ __device__ __forceinline__ int accept_wave(const SampleArgs& a, int r, int pb, i
         } else {
           const float d = load_val_rt(row_ptr(a.draft, a.ddtype, static_cast<int64_t>(r) * a.b + i, a.draft_ld),
                                       a.ddtype, xv);
-          q = exp(static_cast<double>(d) * invT - a.dlse[pos]);
+          q = exp_tab(static_cast<double>(d) * invT - a.dlse[pos], tab);
         }
       }
     }
@@ -205,6 +207,9 @@ __device__ __forceinline__ int accept_wave(const SampleArgs& a, int r, int pb, i
 }
 
 __global__ __launch_bounds__(kWave) void k_accept(SampleArgs a) {
+  __shared__ double etab[kExpTab];
+  exp_table_init(etab);
+  __syncthreads();
   const int r = blockIdx.x;
   int pb, Lr, tb;
   if (!request_ok(a, r, pb, Lr, tb)) {
@@ -215,7 +220,7 @@ __global__ __launch_bounds__(kWave) void k_accept(SampleArgs a) {
     return;
   }
   const double* qx = a.q_mode == SV_Q_MIXTURE ? a.qx + static_cast<size_t>(r) * a.b : nullptr;
-  const int n = accept_wave(a, r, pb, Lr, tb, qx);
+  const int n = accept_wave(a, r, pb, Lr, tb, qx, etab);
   if (threadIdx.x == 0) a.n_acc[r] = n;
 }
 
@@ -245,6 +250,7 @@ struct TailShared {
   // standalone draw: branch tokens and posterior weights at the slot
   int tv[64];
   double tw[64];
+  double etab[kExpTab];  // the exponential's table
   DrawCtx c;
 };
 
@@ -327,7 +333,8 @@ __device__ __forceinline__ void posterior_mass(const TailShared& sh, int K, int 
 // per-lane counts; the other values go to the lane's dummy slot, so no store
 // branches), then exp runs over the lists, interleaved.
 template <int DT, int DDT, bool kDense>
-__device__ __forceinline__ void sub_sums(const SampleArgs& a, const DrawCtx& c, int r, int ch, float* lists) {
+__device__ __forceinline__ void sub_sums(const SampleArgs& a, const DrawCtx& c, int r, int ch, float* lists,
+                                         const double* tab) {
   using DL = DLists<kDense>;
   constexpr int kL = DL::kLists, kLen = kSubG * 8;
   const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
@@ -388,10 +395,10 @@ __device__ __forceinline__ void sub_sums(const SampleArgs& a, const DrawCtx& c, 
 #pragma unroll
     for (int j = 0; j < kL; ++j) sp[j] = sw[j] = 0.0;
     for (int e = lane; e < seg[kL]; e += kWave) {
-      const double p = exp(static_cast<double>(st[e]) * invT - kept);
+      const double p = exp_tab(static_cast<double>(st[e]) * invT - kept, tab);
       double t = 0.0;
       if (dense_res) {
-        t = p - exp(static_cast<double>(sd[e]) * invT - dlse);
+        t = p - exp_tab(static_cast<double>(sd[e]) * invT - dlse, tab);
         t = t > 0.0 ? t : 0.0;
       }
 #pragma unroll
@@ -460,6 +467,7 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums(SampleArgs a) {
     }
   }
   asm volatile("" ::: "memory");  // the compiler keeps every load above ahead of what follows
+  exp_table_init(sh.etab);
   auto merged = [&](const uint64_t* ks) -> int {
     uint64_t m = 0;
 #pragma unroll
@@ -544,7 +552,7 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums(SampleArgs a) {
     }
     if (!kDense) {
       // p at every branch token of every candidate slot (used at the draw slot)
-      if (tid < KL && !greedy) gp[gz * b + gi] = gok ? p_of(raw_f32<DT>(gl0), grc, invT, grk) : 0.0;
+      if (tid < KL && !greedy) gp[gz * b + gi] = gok ? p_of(raw_f32<DT>(gl0), grc, invT, grk, sh.etab) : 0.0;
       for (int k = tid + kSumNT; k < KL; k += kSumNT) {  // K * L_r > kSumNT only
         const int z = k / Lr, i = k - z * Lr;
         const int v = g[z * b + i];
@@ -552,7 +560,7 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums(SampleArgs a) {
         if (v != sh.x[i]) atomicMin(&sh.f[z], i);
         if (!greedy)
           gp[z * b + i] = ok ? p_of(load_val<DT>(row_ptr(a.tgt, DT, tb + i, a.tgt_ld), v), a.row_cut[tb + i], invT,
-                                    a.row_kept[tb + i])
+                                    a.row_kept[tb + i], sh.etab)
                              : 0.0;
       }
       if (wv == 1) {  // q(z | y) = softmax of the mixing logits
@@ -569,8 +577,9 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums(SampleArgs a) {
     if (tid < kWave) {
       u = u24(philox_at(seed, static_cast<uint32_t>(lane), static_cast<uint32_t>(r)).x);
       if (pos && xok) {
-        p = greedy ? (xl == ra0 ? 1.0 : 0.0) : p_of(raw_f32<DT>(lx0), rc0, invT, rk0);
-        if (kDense) qd = greedy ? (xl == da0 ? 1.0 : 0.0) : exp(static_cast<double>(raw_f32<DDT>(dx0)) * invT - dl0);
+        p = greedy ? (xl == ra0 ? 1.0 : 0.0) : p_of(raw_f32<DT>(lx0), rc0, invT, rk0, sh.etab);
+        if (kDense)
+          qd = greedy ? (xl == da0 ? 1.0 : 0.0) : exp_tab(static_cast<double>(raw_f32<DDT>(dx0)) * invT - dl0, sh.etab);
       }
       if (report && pos && !xok) raise_status(a.status, SV_ST_BAD_TOKEN);
     }
@@ -669,7 +678,7 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums(SampleArgs a) {
         const double w = in ? sh.tw[lane] : 0.0;
         const bool act = in && w > 0.0 && v >= 0 && v < V;
         const float lv = act ? load_val<DT>(row_ptr(a.tgt, DT, tb + n, a.tgt_ld), v) : -INFINITY;
-        build_corrections(c, K, act, v, w, act ? p_of(lv, c.cut, c.invT, c.kept) : 0.0);
+        build_corrections(c, K, act, v, w, act ? p_of(lv, c.cut, c.invT, c.kept, sh.etab) : 0.0);
       }
       __syncwarp();
       if (report) write_record(a, r, c);
@@ -677,7 +686,7 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums(SampleArgs a) {
   }
   __syncthreads();  // also ends every use of the branch tables, which D's lists overwrite
   if (c.mode == kDrawGreedy) return;  // the draw is the argmax (taken by the pick kernel)
-  sub_sums<DT, DDT, kDense>(a, c, r, ch, reinterpret_cast<float*>(dyn));
+  sub_sums<DT, DDT, kDense>(a, c, r, ch, reinterpret_cast<float*>(dyn), sh.etab);
 }
 
 // ------------------------------------------------------------------ soft branches
@@ -697,7 +706,7 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums(SampleArgs a) {
 template <int DT>
 __device__ __forceinline__ void soft_group(const SampleArgs& a, const char* trowp, const char* crow0, size_t cstride,
                                            const double* off, int g, float cut, double invT, double kept,
-                                           double invTb, double p8[8], double w8[8]) {
+                                           double invTb, const double* tab, double p8[8], double w8[8]) {
   constexpr int kB = 8;  // branch rows whose 16-byte words are in flight together
   const int V = a.V, NG = groups_of(V), K = a.K;
   const int gc = min(g, NG - 1);
@@ -711,7 +720,7 @@ __device__ __forceinline__ void soft_group(const SampleArgs& a, const char* trow
   double q8[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
-    p8[q] = l[q] > -INFINITY ? p_of(l[q], cut, invT, kept) : 0.0;
+    p8[q] = l[q] > -INFINITY ? p_of(l[q], cut, invT, kept, tab) : 0.0;
     q8[q] = 0.0;
   }
   for (int z0 = 0; z0 < K; z0 += kB) {
@@ -727,7 +736,7 @@ __device__ __forceinline__ void soft_group(const SampleArgs& a, const char* trow
         unpack8<DT>(c0[j], c1[j], cv);
 #pragma unroll
         for (int q = 0; q < 8; ++q)
-          if (p8[q] > 0.0) q8[q] += exp(static_cast<double>(cv[q]) * invTb - o);
+          if (p8[q] > 0.0) q8[q] += exp_tab(static_cast<double>(cv[q]) * invTb - o, tab);
       }
     }
   }
@@ -741,13 +750,13 @@ __device__ __forceinline__ void soft_group(const SampleArgs& a, const char* trow
 // D (soft residual): sums of p and of the draw weight over sub-chunk `sub`
 // (one group per lane) by one wave.
 template <int DT>
-__device__ __forceinline__ void sub_sum_soft(const SampleArgs& a, const DrawCtx& c, int r, int sub) {
+__device__ __forceinline__ void sub_sum_soft(const SampleArgs& a, const DrawCtx& c, int r, int sub, const double* tab) {
   const int lane = threadIdx.x & (kWave - 1);
   const char* trowp = row_ptr(a.tgt, DT, c.trow, a.tgt_ld);
   const char* crow0 = row_ptr(a.comp, DT, c.drow, a.comp_ld);
   const size_t cstride = static_cast<size_t>(a.b) * static_cast<size_t>(a.comp_ld) * (DT == SV_BF16 ? 2 : 4);
   double p8[8], w8[8];
-  soft_group<DT>(a, trowp, crow0, cstride, c.cw, sub * kSubG + lane, c.cut, c.invT, c.kept, c.invTb, p8, w8);
+  soft_group<DT>(a, trowp, crow0, cstride, c.cw, sub * kSubG + lane, c.cut, c.invT, c.kept, c.invTb, tab, p8, w8);
   double sp = 0.0, sw = 0.0;
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
@@ -805,6 +814,7 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums_soft(SampleArgs a) {
   const int x0 = a.x[static_cast<size_t>(r) * b + min(tid, b - 1)];
   const float m0 = a.mix[static_cast<size_t>(r) * K + min(tid, K - 1)];
   for (int k = tid; k < kb; k += kSumNT) g[k] = a.barg[bbase + k];
+  exp_table_init(sh.etab);
   if (tid < b) sh.x[tid] = x0;
   if (tid < K) sh.mix[tid] = m0;
   __syncthreads();
@@ -862,7 +872,7 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums_soft(SampleArgs a) {
       xok = xv >= 0 && xv < V;
       if (xok)
         p = greedy ? (xv == ra0 ? 1.0 : 0.0)
-                   : p_of(load_val<DT>(row_ptr(a.tgt, DT, tb + lane, a.tgt_ld), xv), rc0, invT, rk0);
+                   : p_of(load_val<DT>(row_ptr(a.tgt, DT, tb + lane, a.tgt_ld), xv), rc0, invT, rk0, sh.etab);
       else if (report)
         raise_status(a.status, SV_ST_BAD_TOKEN);
     }
@@ -948,7 +958,7 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums_soft(SampleArgs a) {
         const int v = in ? g[lane * b + n] : -1;
         const bool act = in && w > 0.0 && v >= 0 && v < V;
         const float lv = act ? load_val<DT>(row_ptr(a.tgt, DT, tb + n, a.tgt_ld), v) : -INFINITY;
-        build_corrections(c, K, act, v, w, act ? p_of(lv, sh.rc[n], invT, sh.rk[n]) : 0.0);
+        build_corrections(c, K, act, v, w, act ? p_of(lv, sh.rc[n], invT, sh.rk[n], sh.etab) : 0.0);
       }
     }
     __syncwarp();
@@ -959,9 +969,9 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums_soft(SampleArgs a) {
   constexpr int kPer = kSumNT / kWave;  // sub-chunks of a soft chunk
   if (c.mode == kDrawSoft) {
     const int sub = ch * kPer + wv;
-    if (sub < a.NSUB) sub_sum_soft<DT>(a, c, r, sub);
+    if (sub < a.NSUB) sub_sum_soft<DT>(a, c, r, sub, sh.etab);
   } else if (ch % (kChunkSubs / kPer) == 0) {
-    sub_sums<DT, DT, false>(a, c, r, ch / (kChunkSubs / kPer), reinterpret_cast<float*>(dyn));
+    sub_sums<DT, DT, false>(a, c, r, ch / (kChunkSubs / kPer), reinterpret_cast<float*>(dyn), sh.etab);
   }
 }
 
@@ -994,6 +1004,9 @@ __global__ __launch_bounds__(kWave) void k_pick(SampleArgs a) {
   const int ctok = kDense ? -1 : rec.ctok[lane];
   const double cwt = kDense ? 0.0 : rec.cw[lane];
   asm volatile("" ::: "memory");  // every load above is issued before any is used
+  __shared__ double etab[kExpTab];
+  exp_table_init(etab);
+  __syncthreads();
   double lw = 0.0, lp = 0.0;
 #pragma unroll
   for (int k = 0; k < kPickCache; ++k) {
@@ -1091,7 +1104,7 @@ __global__ __launch_bounds__(kWave) void k_pick(SampleArgs a) {
       double p8[8], s8[8];
       const size_t cstride = static_cast<size_t>(a.b) * static_cast<size_t>(a.comp_ld) * (DT == SV_BF16 ? 2 : 4);
       soft_group<DT>(a, row_ptr(a.tgt, DT, trow, a.tgt_ld), row_ptr(a.comp, DT, drow, a.comp_ld), cstride, rec.cw, g,
-                     cut, invT, kept, rec.invTb, p8, s8);
+                     cut, invT, kept, rec.invTb, etab, p8, s8);
 #pragma unroll
       for (int q = 0; q < 8; ++q) w8[q] = use_p ? p8[q] : s8[q];
       formed = true;
@@ -1108,10 +1121,10 @@ __global__ __launch_bounds__(kWave) void k_pick(SampleArgs a) {
     if (dense_res) decode8<DDT>(d0, d1, g, V, g < NG, d);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      double w = p_of(l[q], cut, invT, kept);  // 0 past V (value -inf) unless the cut is -inf
+      double w = p_of(l[q], cut, invT, kept, etab);  // 0 past V (value -inf) unless the cut is -inf
       if (!(l[q] > -INFINITY)) w = 0.0;
       if (dense_res) {
-        const double t2 = w - exp(static_cast<double>(d[q]) * invT - dlse);
+        const double t2 = w - exp_tab(static_cast<double>(d[q]) * invT - dlse, etab);
         w = t2 > 0.0 ? t2 : 0.0;
       }
       w8[q] = w;

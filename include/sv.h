@@ -316,6 +316,11 @@ int32_t sv_accept_sample(const void* tgt_logits, int32_t dtype, int64_t tgt_ld, 
 int32_t sv_philox_uniforms(const uint64_t* seed, int32_t R, int32_t n_pos, uint32_t* out,
                            void* stream);
 
+/* Test export: out[k] = exp(x[k]) by the library's table-driven double
+ * exponential (the one its probability and draw-weight kernels use; Tang's
+ * method, ACM TOMS 1989), for checking its error against the host's exp. */
+int32_t sv_selftest_exp(const double* x, double* out, int32_t n, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

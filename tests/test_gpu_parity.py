@@ -550,3 +550,39 @@ def test_sweep_points_match_oracle():
             for s in range(w.steps):
                 rep = compare_step(w, res[T][s], oracle_step(w, s), rep)
     assert_rate(rep)
+
+
+# ---------------------------------------------------------------- the library's double exponential
+def test_table_exp_error_against_host_exp():
+    """exp_tab (Tang's table method) over the probabilities' argument range
+    [-746, 0] and a little above 0: within 3 ulp of the host's exp for normal
+    results, 2 units of the smallest subnormal below them; exp(0) = 1,
+    exp(-inf) = 0, NaN stays NaN, arguments below -746 give 0."""
+    import torch
+
+    sv = _sv()
+    rng = np.random.default_rng(23)
+    xs = np.concatenate([
+        -np.linspace(0.0, 746.0, 400001), rng.uniform(-40.0, 0.0, 200000), -rng.uniform(0, 1e-6, 1000),
+        -(2.0 ** -np.arange(1, 1075, dtype=np.float64)), rng.uniform(0.0, 1e-3, 1000),
+        np.array([0.0, -0.0, -708.39, -708.4, -744.4, -745.13, -745.14, -745.2, -746.0, -746.5, -1e5, -np.inf]),
+    ])
+    banner(f"exp_tab on {xs.size} arguments")
+    xt = torch.from_numpy(xs).cuda()
+    out = torch.empty_like(xt)
+    sv.sv_selftest_exp(xt, out, xs.size)
+    got = out.cpu().numpy()
+    ref = np.exp(xs)
+    normal = ref >= np.finfo(np.float64).tiny
+    ulps = np.abs(got[normal] - ref[normal]) / np.spacing(ref[normal])
+    assert ulps.max() <= 3.0, f"max {ulps.max()} ulp at x = {xs[normal][np.argmax(ulps)]}"
+    sub = ~normal
+    assert np.all(np.abs(got[sub] - ref[sub]) <= 2 * 2.0 ** -1074)
+    assert got[xs == 0.0].tolist() == [1.0] * int((xs == 0.0).sum())
+    assert got[np.isneginf(xs)].tolist() == [0.0]
+    assert np.all(got[xs < -746.0] == 0.0)
+    nan = torch.tensor([np.nan], dtype=torch.float64).cuda()
+    o1 = torch.empty_like(nan)
+    sv.sv_selftest_exp(nan, o1, 1)
+    assert np.isnan(o1.cpu().numpy()[0])
+    print(f"\n[exp_tab] max error {ulps.max():.2f} ulp, mean {ulps.mean():.3f} ulp", flush=True)

@@ -16,12 +16,39 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def sv():
     lib_path = os.path.join(ROOT, "draft_verification_sv_amd", "libsv.so")
     if not os.path.exists(lib_path):
-        from draft_verification_sv_amd import build
-
-        build.build()
+        _load_build_script().build()
     import draft_verification_sv_amd as m
 
     return m
+
+
+def _load_build_script():
+    import importlib.util
+
+    spec = importlib.util.spec_from_file_location("sv_build", os.path.join(ROOT, "draft_verification_sv_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_build_script_loads_without_the_package():
+    """The build step must not import the package (which loads the library
+    being rebuilt, absent on a fresh checkout)."""
+    import subprocess
+    import sys
+
+    code = ("import importlib.util, os, sys\n"
+            "spec = importlib.util.spec_from_file_location('b', os.path.join('draft_verification_sv_amd', 'build.py'))\n"
+            "m = importlib.util.module_from_spec(spec); spec.loader.exec_module(m)\n"
+            "cmd = m.command('x.so')\n"
+            "assert cmd[0] == 'hipcc' and any(a.startswith('--offload-arch=gfx950') for a in cmd)\n"
+            "assert 'draft_verification_sv_amd' not in sys.modules and 'torch' not in sys.modules\n"
+            "print('ok')\n")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert out.returncode == 0 and out.stdout.strip() == "ok", out.stderr
+    src = open(os.path.join(ROOT, "__graft_entry__.py")).read()
+    body = src[src.index("def build()"):src.index("def smoke()")]
+    assert body.index("spec_from_file_location") < body.index("import draft_verification_sv_amd")
 
 
 def declared_functions():
