@@ -23,10 +23,11 @@
 //
 // One block of 256 threads:
 //   1. per request, the running products (written to s);
-//   2. radix select, 8 bits per pass from the top, of the B-th largest score
-//      (score bits with -0 read as +0: non-negative floats order like their
-//      bit patterns), with LDS count histograms; the digit holding the rank is
-//      found by a block scan over the 256 digit counts; then a position is
+//   2. radix select, 10 bits per pass from the top (three passes: selection
+//      keys are below 2^30), of the B-th largest score (score bits with -0
+//      read as +0: non-negative floats order like their bit patterns), with
+//      LDS count histograms; the digit holding the rank is
+//      found by a block scan over the 1024 digit counts; then a position is
 //      taken if above the threshold or a tie of rank below the remainder in
 //      (r, i) order (an exclusive scan of tie counts);
 //   3. L_r counted with integer atomics;
@@ -42,6 +43,14 @@ __device__ __forceinline__ uint32_t score_key(float v) {
   return k == 0x80000000u ? 0u : k;
 }
 
+// selection key of a drafted position: score key + 1, with keys above that
+// of 1.0 (only from estimates outside [0, 1], which raise a status bit) held
+// at it, so that every key is below 2^30
+__device__ __forceinline__ uint32_t select_key(float v) { return min(score_key(v), 0x3F800000u) + 1u; }
+
+constexpr int kDigitBits = 10;            // three radix passes cover the 30 key bits
+constexpr int kBins = 1 << kDigitBits;
+
 constexpr int kDvlNT = 256;
 constexpr int kDvlLds = 8192;  // scores kept in LDS up to this many positions
 
@@ -56,7 +65,7 @@ __global__ __launch_bounds__(kDvlNT) void k_dvl(const float* __restrict__ a, int
                                                const int32_t* __restrict__ budget, float* __restrict__ s,
                                                int32_t* __restrict__ L, int32_t* __restrict__ pos_off,
                                                int32_t* __restrict__ tgt_off, uint32_t* status) {
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t hist[kBins];
   __shared__ uint32_t skey[kInLds ? kDvlLds : 1];
   __shared__ int scr[kDvlNT / kWave];
   __shared__ int lcount[kInLds ? kDvlLds : 1];
@@ -88,19 +97,19 @@ __global__ __launch_bounds__(kDvlNT) void k_dvl(const float* __restrict__ a, int
   // store.
   bool bad = false;
   if constexpr (kInLds) {
-    for (int e = tid; e < n; e += kDvlNT) {
-      const float av = a[e];
-      bad |= (e % b) < block_of(block_len, e / b, b) && !(av >= 0.0f && av <= 1.0f);
-      skey[e] = __float_as_uint(av);
-    }
+    for (int e = tid; e < n; e += kDvlNT) skey[e] = __float_as_uint(a[e]);
     for (int r = tid; r < R; r += kDvlNT) lcount[r] = 0;
     __syncthreads();
+    // per request: the running products in place, the estimates checked;
+    // positions past b_r marked (no score has these bits)
     for (int r = tid; r < R; r += kDvlNT) {
       const int br = block_of(block_len, r, b);
       float run = 1.0f;
       for (int i = 0; i < b; ++i) {
-        run = run * __uint_as_float(skey[r * b + i]);
-        skey[r * b + i] = i < br ? __float_as_uint(run) : 0xFFFFFFFFu;  // marks a position past b_r
+        const float av = __uint_as_float(skey[r * b + i]);
+        bad |= i < br && !(av >= 0.0f && av <= 1.0f);
+        run = run * av;
+        skey[r * b + i] = i < br ? __float_as_uint(run) : 0xFFFFFFFFu;
       }
     }
     __syncthreads();
@@ -108,7 +117,7 @@ __global__ __launch_bounds__(kDvlNT) void k_dvl(const float* __restrict__ a, int
       const bool cand = skey[e] != 0xFFFFFFFFu;
       const float sv = cand ? __uint_as_float(skey[e]) : 0.0f;
       s[e] = sv;
-      skey[e] = cand ? score_key(sv) + 1u : 0u;
+      skey[e] = cand ? select_key(sv) : 0u;
     }
   } else {
     for (int r = tid; r < R; r += kDvlNT) L[r] = 0;
@@ -131,7 +140,7 @@ __global__ __launch_bounds__(kDvlNT) void k_dvl(const float* __restrict__ a, int
     // selection key: score key + 1 for a candidate, 0 past b_r
     auto key = [&](int e) -> uint32_t {
       if constexpr (kInLds) return skey[e];
-      else return (e % b) < block_of(block_len, e / b, b) ? score_key(s[e]) + 1u : 0u;
+      else return (e % b) < block_of(block_len, e / b, b) ? select_key(s[e]) : 0u;
     };
     // 2. threshold: the B-th largest score (rank from the top, ties counted)
     uint32_t thr = 0;
@@ -139,27 +148,42 @@ __global__ __launch_bounds__(kDvlNT) void k_dvl(const float* __restrict__ a, int
     if (!all && !none) {
       uint32_t prefix = 0, mask = 0;
       remaining = B;
-      for (int shift = 24; shift >= 0; shift -= 8) {
-        for (int k = tid; k < 256; k += kDvlNT) hist[k] = 0u;
+      constexpr int kPerThread = kBins / kDvlNT;
+      static_assert(kPerThread * kDvlNT == kBins, "digits must split evenly over the block");
+      for (int shift = 2 * kDigitBits; shift >= 0; shift -= kDigitBits) {
+        for (int k = tid; k < kBins; k += kDvlNT) hist[k] = 0u;
         __syncthreads();
         for (int e = tid; e < n; e += kDvlNT) {
           const uint32_t kk = key(e);
-          if ((kk & mask) == prefix) atomicAdd(&hist[(kk >> shift) & 255u], 1u);
+          if ((kk & mask) == prefix) atomicAdd(&hist[(kk >> shift) & (kBins - 1)], 1u);
         }
         __syncthreads();
-        // digits from the top: thread t holds digit 255 - t; the crossing digit
-        // is the one whose exclusive count from the top is < remaining <= inclusive
-        const int h = tid < 256 ? static_cast<int>(hist[255 - tid]) : 0;
+        // digits from the top: thread t holds digits kBins-1 - (t*kPerThread + j);
+        // the crossing digit is the one whose exclusive count from the top is
+        // < remaining <= inclusive
+        int h[kPerThread], hs = 0;
+#pragma unroll
+        for (int j = 0; j < kPerThread; ++j) {
+          h[j] = static_cast<int>(hist[kBins - 1 - (tid * kPerThread + j)]);
+          hs += h[j];
+        }
         int tot;
-        const int excl = block_excl_scan_i32<kDvlNT>(h, scr, &tot);
-        if (tid < 256 && excl < remaining && remaining <= excl + h) {
-          sh_prefix = prefix | (static_cast<uint32_t>(255 - tid) << shift);
-          sh_remaining = remaining - excl;
+        const int excl = block_excl_scan_i32<kDvlNT>(hs, scr, &tot);
+        if (excl < remaining && remaining <= excl + hs) {
+          int run = excl;
+#pragma unroll
+          for (int j = 0; j < kPerThread; ++j) {
+            if (run < remaining && remaining <= run + h[j]) {
+              sh_prefix = prefix | (static_cast<uint32_t>(kBins - 1 - (tid * kPerThread + j)) << shift);
+              sh_remaining = remaining - run;
+            }
+            run += h[j];
+          }
         }
         __syncthreads();
         prefix = sh_prefix;
         remaining = sh_remaining;
-        mask |= 255u << shift;
+        mask |= static_cast<uint32_t>(kBins - 1) << shift;
       }
       thr = prefix;
     }
