@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the CPU-oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--config", type=int, default=5, choices=(3, 5),
+                    help="5: conc 32 K=8 mixture with top-p and DVL (the headline workload); 3: conc 32 dense "
+                         "independent draft with DVL, no top-p")
     ap.add_argument("--branch-T", type=float, default=0.0,
                     help="soft-branch mixture: the drafter samples each branch from softmax(c / T_b) and "
                          "verification uses those branch distributions (0: greedy branches, the default)")
@@ -160,7 +163,10 @@ def main():
     t_gen = time.time()
     bT = args.branch_T
     soft = bT > 0
-    w = synth.config(5, steps=S, branch_T=bT)
+    dense = args.config == 3
+    if dense and soft:
+        raise SystemExit("--branch-T applies to the mixture workload (--config 5)")
+    w = synth.config(args.config, steps=S, branch_T=bT)
     R, b, V, K, B = w.R, w.b, w.V, w.K, w.budget
     print(f"[bench] data generated in {time.time() - t_gen:.1f}s: {w.name}", file=sys.stderr, flush=True)
     ld = row_pitch(V, "bf16")
@@ -170,13 +176,14 @@ def main():
     ws, nb = sv.make_workspace(R, b, K, V, dev)
 
     full = to_device_rows(w.tgt, ld, dev)            # [R*(b+1), ld]: target rows for every position
-    comp = to_device_rows(w.comp, ld, dev)           # [R*K*b, ld]
-    mix = torch.from_numpy(w.mix.reshape(-1)).to(dev)
+    comp = None if dense else to_device_rows(w.comp, ld, dev)    # [R*K*b, ld]
+    draft = to_device_rows(w.draft, ld, dev) if dense else None  # [R*b, ld]
+    mix = None if dense else torch.from_numpy(w.mix.reshape(-1)).to(dev)
     a_all = torch.from_numpy(w.a.reshape(S, R * b)).to(dev)
     x_all = torch.from_numpy(w.x.reshape(S, R * b)).to(dev)
     seeds = torch.from_numpy(w.seeds.view(np.int64)).to(dev)
     T = torch.from_numpy(w.T).to(dev)
-    top_p = torch.from_numpy(w.top_p).to(dev)
+    top_p = None if w.top_p is None else torch.from_numpy(w.top_p).to(dev)
     budget = torch.tensor([B], dtype=torch.int32, device=dev)
     branch_T = torch.full((R,), bT, dtype=torch.float32, device=dev) if soft else None
 
@@ -185,7 +192,8 @@ def main():
     s_sc, L, pos_off, tgt_off = z(R * b, f32), z(R, i32), z(R + 1, i32), z(R + 1, i32)
     row_max, row_arg, row_lse, row_cut, row_kept = z(max_rows, f32), z(max_rows, i32), z(max_rows, f64), \
         z(max_rows, f32), z(max_rows, f64)
-    branch_tok, post_w, q_at = z(R * K * b, i32), z(R * b * K, f64), z(R * b, f64)
+    branch_tok, post_w, q_at = z(max(R * K * b, 1), i32), z(max(R * b * K, 1), f64), z(R * b, f64)
+    d_max, d_arg, d_lse = z(max_pos, f32), z(max_pos, i32), z(max_pos, f64)
     n_acc, token, is_bonus = z(R, i32), z(R, i32), z(R, i32)
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
@@ -211,7 +219,24 @@ def main():
     print(f"[bench] packed target rows for {S} steps in {time.time() - t_prep:.1f}s", file=sys.stderr, flush=True)
     positions = L_host.sum(axis=1)  # verified positions per step
 
+    def step_dense(s, ev=None):
+        sv.dvl_alloc_pack(a_all[s], R, b, None, budget, s_sc, L, pos_off, tgt_off, ws, nb, sp)
+        if ev is not None:
+            ev[0].record(stream)
+        # target-row and draft-row statistics in one launch
+        sv.sv_verify_rows_dense(packed[s], dt, ld, V, tgt_off, R, max_rows, T, top_p, row_max, row_arg, row_lse,
+                                row_cut, row_kept, draft, dt, ld, b, pos_off, max_pos, d_max, d_arg, d_lse, ws, nb,
+                                sp)
+        if ev is not None:
+            ev[1].record(stream)
+        # acceptance, residual / bonus draw
+        sv.sv_accept_sample(packed[s], dt, ld, V, tgt_off, pos_off, R, b, T, row_arg, row_cut, row_kept, x_all[s],
+                            sv.SV_Q_DENSE, draft, dt, ld, d_arg, d_lse, 0, None, None, 0, None, None, None, None,
+                            seeds[s:s + 1], n_acc, token, is_bonus, None, None, None, ws, nb, sp)
+
     def step(s, ev=None):
+        if dense:
+            return step_dense(s, ev)
         sv.dvl_alloc_pack(a_all[s], R, b, None, budget, s_sc, L, pos_off, tgt_off, ws, nb, sp)
         if ev is not None:
             ev[0].record(stream)
@@ -249,15 +274,18 @@ def main():
     rejected = (nacc_hist.cpu().numpy() < L_host).sum(axis=1)  # requests drawing a residual, per step
     mix_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
     row_bytes = V * 2
-    # algorithmic bytes of the dominant launch: every target row (L_r + 1 per request)
-    # and every verified position's K component rows, each read once
-    mix_bytes = float(np.mean((positions + R) * row_bytes + positions * K * row_bytes))
+    # algorithmic bytes of the timed statistics launch(es): every target row (L_r + 1 per request) and
+    # every verified position's K component rows (dense: its draft row), each read once
+    per_pos = 1 if dense else K
+    mix_bytes = float(np.mean((positions + R) * row_bytes + positions * per_pos * row_bytes))
     achieved = mix_bytes / (mix_ms * 1e-3) / 1e9
-    # step-aggregate algorithmic bytes: target rows, component rows, one sampled row per request (soft
-    # branches: a residual also reads the K branch rows of its slot)
-    step_bytes = (positions + R) * row_bytes + positions * K * row_bytes + R * row_bytes
+    # step-aggregate algorithmic bytes: target rows, component (draft) rows, one sampled row per request
+    # (dense draft or soft branches: a residual also reads the draft row, or the K branch rows, of its slot)
+    step_bytes = (positions + R) * row_bytes + positions * per_pos * row_bytes + R * row_bytes
     if soft:
         step_bytes = step_bytes + rejected * K * row_bytes
+    if dense:
+        step_bytes = step_bytes + rejected * row_bytes
     ms_per_step = elapsed / S * 1e3
     value = float(positions.sum()) / elapsed
 
@@ -265,8 +293,16 @@ def main():
     if not args.no_cpu:
         cpu = cpu_baseline(w, args.cpu_seconds)
 
-    traffic = None if soft else load_traffic(ROWS_KERNEL)
+    traffic = None if (soft or dense) else load_traffic(ROWS_KERNEL)
     mixture = f"K8 soft-branch mixture T_b {bT:g}" if soft else "K8 greedy-branch mixture"
+    if dense:
+        workload = ("conc32 block16 V151936 bf16, independent (dense) draft, DVL budget 256, T1.0, no top-p, "
+                    "residual+bonus, seeds advancing per step")
+        kernel = "k_rows_dense (sv_verify_rows_dense: target rows + draft rows)"
+    else:
+        workload = (f"conc32 block16 V151936 bf16, {mixture}, DVL budget 256, T1.0 top-p0.95, residual+bonus, "
+                    "seeds advancing per step")
+        kernel = "k_rows_mix (sv_verify_rows" + (", soft branches)" if soft else ")")
     out = {
         "metric": "verified draft positions/sec at V=151936, conc 32; % of peak HBM GB/s",
         "value": round(value, 1),
@@ -280,13 +316,12 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded Zipfian logits, Beta(8,2) survival estimates)",
-        "config": {"workload": f"conc32 block16 V151936 bf16, {mixture}, DVL budget 256, "
-                               "T1.0 top-p0.95, residual+bonus, seeds advancing per step",
+        "config": {"workload": workload,
                    "requests": R, "block": b, "vocab": V, "K": K, "budget": B,
                    **({"branch_T": bT} if soft else {})},
         "step_gbps": round(float(np.mean(step_bytes)) / (ms_per_step * 1e-3) / 1e9, 1),
         "step_frac_of_peak": round(float(np.mean(step_bytes)) / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-        "roofline": {"kernel": "k_rows_mix (sv_verify_rows" + (", soft branches)" if soft else ")"), "bound": "hbm", "achieved": round(achieved, 1),
+        "roofline": {"kernel": kernel, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": traffic, "avg_launch_us": round(mix_ms * 1e3, 2),
                      "algorithmic_bytes_per_launch": mix_bytes},
@@ -306,13 +341,14 @@ def cpu_baseline(w, seconds: float):
 
     R, b, V, K = w.R, w.b, w.V, w.K
     tgt = w.tgt.reshape(R * (b + 1), V)
-    comp = w.comp.reshape(R * K * b, V)
+    prop = dict(comp=w.comp.reshape(R * K * b, V), comp_row0=np.arange(R) * K * b, mix=w.mix, branch_T=w.branch_T) \
+        if K > 0 else dict(draft=w.draft.reshape(R * b, V), draft_row0=np.arange(R) * b)
     t0 = time.perf_counter()
     pos = n = 0
     while n < w.steps:
         dv = oracle.dvl(w.a[n], w.budget)
         oracle.step(tgt=tgt, tgt_row0=np.arange(R) * (b + 1), L=dv["L"], T=w.T, x=w.x[n], seed=int(w.seeds[n]),
-                    top_p=w.top_p, comp=comp, comp_row0=np.arange(R) * K * b, mix=w.mix, branch_T=w.branch_T)
+                    top_p=w.top_p, **prop)
         pos += int(dv["L"].sum())
         n += 1
         if time.perf_counter() - t0 > seconds:

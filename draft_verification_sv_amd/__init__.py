@@ -33,7 +33,8 @@ STATUS_BITS = {
 EXPORTS = [
     "sv_workspace_bytes", "sv_workspace_init", "sv_get_status", "sv_clear_status", "sv_status_string",
     "dvl_alloc_pack", "sv_softmax_stats", "sv_topp_threshold", "sv_mixture_q", "sv_accept",
-    "sv_residual_sample", "sv_philox_uniforms", "sv_verify_rows", "sv_accept_sample", "sv_selftest_exp",
+    "sv_residual_sample", "sv_philox_uniforms", "sv_verify_rows", "sv_verify_rows_dense", "sv_accept_sample",
+    "sv_selftest_exp",
 ]
 
 
@@ -73,6 +74,8 @@ _SIGS = {
                            _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "sv_philox_uniforms": [_vp, _i32, _i32, _vp, _vp],
     "sv_selftest_exp": [_vp, _vp, _i32, _vp],
+    "sv_verify_rows_dense": [_vp, _i32, _i64, _i32, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
+                             _i64, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _sz, _vp],
     "sv_verify_rows": [_vp, _i32, _i64, _i32, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32,
                        _i32, _vp, _i32, _vp, _vp, _sz, _vp],
     "sv_accept_sample": [_vp, _i32, _i64, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i64,
@@ -189,6 +192,16 @@ def sv_verify_rows(tgt_logits, dtype, tgt_ld, V, tgt_off, R, max_rows, temperatu
                                _p(top_p), _p(row_max), _p(row_argmax), _p(row_lse), _p(row_cut), _p(row_kept_lse),
                                _p(comp_logits), comp_ld, K, b, _p(pos_off), max_pos, _p(branch_T), _p(ws), ws_bytes,
                                _stream(stream)), "sv_verify_rows")
+
+
+def sv_verify_rows_dense(tgt_logits, dtype, tgt_ld, V, tgt_off, R, max_rows, temperature, top_p, row_max,
+                         row_argmax, row_lse, row_cut, row_kept_lse, draft_logits, draft_dtype, draft_ld, b, pos_off,
+                         max_pos, draft_max, draft_argmax, draft_lse, ws, ws_bytes, stream=None):
+    _check(_lib.sv_verify_rows_dense(_p(tgt_logits), dtype, tgt_ld, V, _p(tgt_off), R, max_rows, _p(temperature),
+                                     _p(top_p), _p(row_max), _p(row_argmax), _p(row_lse), _p(row_cut),
+                                     _p(row_kept_lse), _p(draft_logits), draft_dtype, draft_ld, b, _p(pos_off),
+                                     max_pos, _p(draft_max), _p(draft_argmax), _p(draft_lse), _p(ws), ws_bytes,
+                                     _stream(stream)), "sv_verify_rows_dense")
 
 
 def sv_accept_sample(tgt_logits, dtype, tgt_ld, V, tgt_off, pos_off, R, b, temperature, row_argmax, row_cut,

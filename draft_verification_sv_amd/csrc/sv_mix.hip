@@ -23,7 +23,7 @@
 // Soft branches (same review, "What carries the argument": each branch is a
 // distribution q_i(. | y, z); here softmax(c / T_b)): the fused rows launch
 // gives every component row one block that forms lse(c / T_b), argmax and
-// maximum in one streaming pass (soft_row_bf16); the draw kernels form the
+// maximum in one streaming pass (stream_row_bf16); the draw kernels form the
 // posterior from them (sv_sample.hip).
 #include <math.h>
 
@@ -83,16 +83,20 @@ __device__ __forceinline__ void stream_argmax(const uint4* vp, int v0, int v1, f
   int bvi = -1;
   uint4 bv = {0, 0, 0, 0};
   int v = v0 + static_cast<int>(threadIdx.x);
+  // loads are unconditional, their indices clamped to the range's last vector
+  // (re-read, unused), so that no branch makes the compiler wait for the batch
+  // in flight before using the one before it
+  const int last = v1 - 1;
   uint4 cur[kMixBatch];
+  if (v1 > v0) {
 #pragma unroll
-  for (int k = 0; k < kMixBatch; ++k)
-    if (v + k * NT < v1) cur[k] = load16_stream(vp + v + k * NT);
+    for (int k = 0; k < kMixBatch; ++k) cur[k] = load16_stream(vp + min(v + k * NT, last));
+  }
   while (v < v1) {
     const int vn = v + kMixBatch * NT;
     uint4 nxt[kMixBatch];
 #pragma unroll
-    for (int k = 0; k < kMixBatch; ++k)
-      if (vn + k * NT < v1) nxt[k] = load16_stream(vp + vn + k * NT);
+    for (int k = 0; k < kMixBatch; ++k) nxt[k] = load16_stream(vp + min(vn + k * NT, last));
 #pragma unroll
     for (int k = 0; k < kMixBatch; ++k) {
       if (v + k * NT < v1) {
@@ -175,96 +179,10 @@ __device__ __forceinline__ void mix_block(const MixArgs& a, int m, int part, uin
   }
 }
 
-// One bf16 soft-branch row in one pass: argmax (lowest index), maximum and
-// log sum_v exp(c_v / T_b).  Each thread keeps a running maximum m and a sum
-// of exp((c - m) / T_b), rescaled when m grows; the 8 values of a 16-byte
-// vector are exponentiated in fp32 (the hardware exp2 of (c - m) * log2(e) /
-// T_b; a term below 2^-126 of the running maximum may flush to 0, far below
-// the sum's rounding) and summed in fp32, the vector sums in double; the block
-// combines the threads' sums in double.  fp32 accumulation, as for row statistics; no top-p is needed for a
-// branch row, so the exact histogram of the target rows is not used.
-template <int NT>
-__device__ __forceinline__ void soft_row_bf16(const uint4* vp, const uint16_t* rp, int V, float Tb, float& M,
-                                              int& am, double& lse, RowShared<NT>& sh) {
-  const int tid = threadIdx.x;
-  const int nvec = V >> 3;
-  const float c2 = 1.4426950408889634f / Tb;  // log2(e) / T_b
-  float m = -INFINITY;
-  double s = 0.0;
-  int bvi = -1;
-  uint4 bv = {0, 0, 0, 0};
-  auto take = [&](const uint4& d, int vi) {
-    float v[8];
-    v[0] = bf16_lo(d.x); v[1] = bf16_hi(d.x); v[2] = bf16_lo(d.y); v[3] = bf16_hi(d.y);
-    v[4] = bf16_lo(d.z); v[5] = bf16_hi(d.z); v[6] = bf16_lo(d.w); v[7] = bf16_hi(d.w);
-    const float vm = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])), fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
-    if (vm > m) {  // rare after the first vectors: the rescale runs in double
-      s *= exp2((static_cast<double>(m) - static_cast<double>(vm)) * static_cast<double>(c2));  // 0 while m = -inf
-      m = vm;
-      bvi = vi;
-      bv = d;
-    }
-    float acc = 0.0f;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) acc += __builtin_amdgcn_exp2f((v[q] - m) * c2);
-    s += static_cast<double>(acc);
-  };
-  int v = tid;
-  uint4 cur[kMixBatch];
-#pragma unroll
-  for (int k = 0; k < kMixBatch; ++k)
-    if (v + k * NT < nvec) cur[k] = load16_stream(vp + v + k * NT);
-  while (v < nvec) {
-    const int vn = v + kMixBatch * NT;
-    uint4 nxt[kMixBatch];
-#pragma unroll
-    for (int k = 0; k < kMixBatch; ++k)
-      if (vn + k * NT < nvec) nxt[k] = load16_stream(vp + vn + k * NT);
-#pragma unroll
-    for (int k = 0; k < kMixBatch; ++k)
-      if (v + k * NT < nvec) take(cur[k], v + k * NT);
-#pragma unroll
-    for (int k = 0; k < kMixBatch; ++k) cur[k] = nxt[k];
-    v = vn;
-  }
-  int bidx = -1;
-  float best = m;
-  if (bvi >= 0) {
-    const float e[8] = {bf16_lo(bv.x), bf16_hi(bv.x), bf16_lo(bv.y), bf16_hi(bv.y),
-                        bf16_lo(bv.z), bf16_hi(bv.z), bf16_lo(bv.w), bf16_hi(bv.w)};
-    int k = 7;
-#pragma unroll
-    for (int q = 7; q >= 0; --q)
-      if (e[q] == best) k = q;
-    bidx = bvi * 8 + k;
-  }
-  for (int e = (nvec << 3) + tid; e < V; e += NT) {  // elements past the last full vector
-    const float f = __uint_as_float(static_cast<uint32_t>(rp[e]) << 16);
-    if (f > m) {
-      s *= exp2((static_cast<double>(m) - static_cast<double>(f)) * static_cast<double>(c2));
-      m = f;
-    }
-    if (f > best || bidx < 0) {
-      best = f;
-      bidx = e;
-    }
-    s += static_cast<double>(__builtin_amdgcn_exp2f((f - m) * c2));
-  }
-  uint64_t packed = bidx >= 0 ? (static_cast<uint64_t>(fkey(best)) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(bidx)) : 0;
-  packed = block_max_u64<NT>(packed, sh.red_u64);
-  M = packed ? key_value(static_cast<uint32_t>(packed >> 32)) : -INFINITY;
-  am = static_cast<int>(argmax_token(packed));
-  // this thread's sum rescaled to the row maximum, in double (same scale constant as the terms)
-  const double part =
-      m > -INFINITY ? s * exp2((static_cast<double>(m) - static_cast<double>(M)) * static_cast<double>(c2)) : 0.0;
-  const double S = block_sum_f64<NT>(part, sh.red_f64);
-  lse = static_cast<double>(M) / static_cast<double>(Tb) + log(S);
-}
-
 // Soft branches: statistics of component row m = p*K + z (position p, category
 // z) at its request's branch temperature T_b, by one block: lse of c / T_b,
-// argmax and maximum (T_b = 0: argmax and maximum).  bf16 rows stream once
-// (soft_row_bf16); fp32 rows use the target rows' generic code.
+// argmax and maximum (T_b = 0: argmax and maximum), with the row statistics'
+// code without a cut (bf16: one streaming pass; fp32: the generic path).
 template <int DT, int NT, int BATCH>
 __device__ __forceinline__ void soft_block(const MixArgs& a, int m, uint32_t* hist, RowShared<NT>& sh) {
   const int tid = threadIdx.x;
@@ -289,22 +207,6 @@ __device__ __forceinline__ void soft_block(const MixArgs& a, int m, uint32_t* hi
   const char* rowp = static_cast<const char*>(a.comp) + static_cast<size_t>(row) * static_cast<size_t>(a.ld) * esz;
   const float Tb = a.branch_T[r];
   if (tid == 0 && !(Tb >= 0.0f)) raise_status(a.status, SV_ST_BAD_TEMPERATURE);
-  if constexpr (DT == SV_BF16) {
-    if (Tb > 0.0f) {
-      float M;
-      int am;
-      double lse;
-      soft_row_bf16<NT>(reinterpret_cast<const uint4*>(rowp), reinterpret_cast<const uint16_t*>(rowp), a.V, Tb, M,
-                        am, lse, sh);
-      if (tid == 0) {
-        if (!(M < INFINITY) || !(lse < INFINITY)) raise_status(a.status, SV_ST_NONFINITE);
-        a.bmax[row] = M;
-        a.barg[row] = am;
-        a.blse[row] = lse;
-      }
-      return;
-    }
-  }
   RowArgs ca{};
   ca.logits = a.comp;
   ca.ld = a.ld;

@@ -7,18 +7,113 @@ namespace sv {
 
 constexpr int kRowNT = 512;
 constexpr int kRowBatch = 8;  // 16-byte loads per thread per batch (x2 in flight)
+constexpr int kDenseNT = 256;  // sv_verify_rows_dense: kRowParts blocks of 256 per split row
+constexpr int kDenseBatch = 8;
 
+// Row p of a's rows (p < the device-side count), by one block.
 template <int DT>
-__global__ __launch_bounds__(kRowNT) void k_row_stats(RowArgs a) {
-  __shared__ RowShared<kRowNT> sh;
-  __shared__ uint32_t hist[DT == SV_BF16 ? kHistWords : 1];
-  const int p = blockIdx.x;
+__device__ __forceinline__ void stats_block(const RowArgs& a, int p, uint32_t* hist, RowShared<kRowNT>& sh) {
   const int total = a.row_off[a.R];
   if (p == 0 && threadIdx.x == 0 && (a.row_off[0] != 0 || total > a.max_rows || total < 0))
     raise_status(a.status, SV_ST_BAD_OFFSETS);
   if (p >= total) return;
   exp_table_init(sh.etab);  // published by row_block's first barrier
   row_block<DT, kRowNT, kRowBatch>(a, p, hist, sh);
+}
+
+template <int DT>
+__global__ __launch_bounds__(kRowNT) void k_row_stats(RowArgs a) {
+  __shared__ RowShared<kRowNT> sh;
+  __shared__ uint32_t hist[DT == SV_BF16 ? kHistWords : 1];
+  stats_block<DT>(a, blockIdx.x, hist, sh);
+}
+
+// Part `part` of row p of a (sv_verify_rows_dense).  A bf16 row without a
+// top-p cut is streamed as kRowParts blocks, each leaving its partial
+// statistics in parts[p * kRowParts + part]; any other row is done whole by
+// part 0, which marks it unsplit.
+template <int DT, int NT, int BATCH>
+__device__ __forceinline__ void stats_part(const RowArgs& a, int p, int part, RowPart* parts, uint32_t* hist,
+                                           RowShared<NT>& sh) {
+  const int total = a.row_off[a.R];
+  if (p == 0 && part == 0 && threadIdx.x == 0 && (a.row_off[0] != 0 || total > a.max_rows || total < 0))
+    raise_status(a.status, SV_ST_BAD_OFFSETS);
+  if (p >= total) return;
+  exp_table_init(sh.etab);  // published by row_locate's barriers
+  const RowLoc l = row_locate<DT, NT>(a, p, sh);
+  if (!l.ok) return;
+  RowPart* rec = parts + static_cast<size_t>(p) * kRowParts;
+  if (DT != SV_BF16 || l.topp_on) {
+    if (part != 0) return;
+    row_stats_at<DT, NT, BATCH>(a, l.rowp, p, l.T, l.tp, l.topp_on, hist, sh);
+    if (threadIdx.x == 0) rec[0].split = 0;
+    return;
+  }
+  const int nvec = a.V >> 3;
+  const int v0 = static_cast<int>(static_cast<int64_t>(nvec) * part / kRowParts);
+  const int v1 = static_cast<int>(static_cast<int64_t>(nvec) * (part + 1) / kRowParts);
+  const StreamPart sp = stream_part_bf16<NT, BATCH>(static_cast<const uint16_t*>(l.rowp), a.V, v0, v1,
+                                                     part == kRowParts - 1, l.T, a.status, sh);
+  if (threadIdx.x == 0) {
+    RowPart o;
+    o.S = sp.S;
+    o.key = sp.key;
+    o.M = sp.M;
+    o.T = l.T;
+    o.split = 1;
+    o.pad = 0;
+    rec[part] = o;
+  }
+}
+
+// The packed target rows and the dense draft's rows in one grid
+// (sv_verify_rows_dense): kRowParts blocks per row, target rows first, then
+// draft rows.  One launch keeps every compute unit on both read streams, and
+// the parts spread a few hundred rows over the whole chip.
+template <int DT, int DDT>
+__global__ __launch_bounds__(kDenseNT) void k_rows_dense(RowArgs ta, RowArgs da, int n_tgt, RowPart* tparts,
+                                                         RowPart* dparts) {
+  __shared__ RowShared<kDenseNT> sh;
+  __shared__ uint32_t hist[(DT == SV_BF16 || DDT == SV_BF16) ? kHistWords : 1];
+  const int q = blockIdx.x / kRowParts, part = blockIdx.x % kRowParts;
+  if (q < n_tgt)
+    stats_part<DT, kDenseNT, kDenseBatch>(ta, q, part, tparts, hist, sh);
+  else
+    stats_part<DDT, kDenseNT, kDenseBatch>(da, q - n_tgt, part, dparts, hist, sh);
+}
+
+// Merge of the split rows' parts (one thread per row): maximum and argmax key
+// by max, the sums rescaled to the row maximum in double with the parts' own
+// scale constant, lse = M / T + log(S).
+__global__ __launch_bounds__(256) void k_rows_merge(RowArgs ta, RowArgs da, int n_tgt, int n_all, RowPart* tparts,
+                                                    RowPart* dparts) {
+  const int q = blockIdx.x * blockDim.x + threadIdx.x;
+  if (q >= n_all) return;
+  const bool tgt = q < n_tgt;
+  const RowArgs& a = tgt ? ta : da;
+  const int p = tgt ? q : q - n_tgt;
+  const int total = a.row_off[a.R];
+  if (p >= total || total > a.max_rows) return;
+  const RowPart* rec = (tgt ? tparts : dparts) + static_cast<size_t>(p) * kRowParts;
+  if (!rec[0].split) return;
+  float M = -INFINITY;
+  uint64_t key = 0;
+  for (int k = 0; k < kRowParts; ++k) {
+    M = fmaxf(M, rec[k].M);
+    key = rec[k].key > key ? rec[k].key : key;
+  }
+  const float T = rec[0].T;
+  const int am = static_cast<int>(argmax_token(key));
+  if (T == 0.0f) {
+    write_row(a, p, M, am, 0.0, M, 0.0);
+    return;
+  }
+  const double c2 = static_cast<double>(soft_c2(T));
+  double S = 0.0;
+  for (int k = 0; k < kRowParts; ++k)
+    if (rec[k].M > -INFINITY) S += rec[k].S * exp2((static_cast<double>(rec[k].M) - static_cast<double>(M)) * c2);
+  const double lse = static_cast<double>(M) / static_cast<double>(T) + log(S);
+  write_row(a, p, M, am, lse, -INFINITY, lse);
 }
 
 }  // namespace sv
@@ -96,4 +191,53 @@ extern "C" int32_t sv_selftest_rows_host(void) {
     if (key_value(mono_key(probe[k])) != probe[k]) return 8;
   }
   return 0;
+}
+
+extern "C" int32_t sv_verify_rows_dense(const void* tgt_logits, int32_t dtype, int64_t tgt_ld, int32_t V,
+                                        const int32_t* tgt_off, int32_t R, int32_t max_rows,
+                                        const float* temperature, const float* top_p, float* row_max,
+                                        int32_t* row_argmax, double* row_lse, float* row_cut,
+                                        double* row_kept_lse, const void* draft_logits, int32_t draft_dtype,
+                                        int64_t draft_ld, int32_t b, const int32_t* pos_off, int32_t max_pos,
+                                        float* draft_max, int32_t* draft_argmax, double* draft_lse, void* ws,
+                                        size_t ws_bytes, void* stream) {
+  if (!tgt_logits || !tgt_off || !temperature || !row_max || !row_argmax || !row_lse || !row_cut || !row_kept_lse)
+    return SV_ERR_ARG;
+  if (!draft_logits || !pos_off || !draft_max || !draft_argmax || !draft_lse || !ws) return SV_ERR_ARG;
+  if (R < 1 || V < 1 || b < 1 || b > 64 || max_rows < 0 || max_pos < 0 || tgt_ld < V || draft_ld < V)
+    return SV_ERR_ARG;
+  if ((dtype != SV_F32 && dtype != SV_BF16) || (draft_dtype != SV_F32 && draft_dtype != SV_BF16)) return SV_ERR_ARG;
+  if (!rows_aligned(tgt_logits, dtype, tgt_ld) || !rows_aligned(draft_logits, draft_dtype, draft_ld)) return SV_ERR_ARG;
+  if (static_cast<long long>(max_pos) > static_cast<long long>(R) * b) return SV_ERR_ARG;
+  if (static_cast<long long>(max_rows) + max_pos > 0x7FFFFFFFLL) return SV_ERR_ARG;
+  if (max_rows > R * (b + 1)) return SV_ERR_ARG;
+  const WsLayout l = ws_layout(R, b, 0, V);
+  if (ws_bytes < l.total) return SV_ERR_WORKSPACE;
+  const unsigned n_all = static_cast<unsigned>(max_rows) + static_cast<unsigned>(max_pos);
+  if (n_all == 0) return SV_OK;
+  const unsigned grid = n_all * kRowParts;
+  RowPart* tparts = reinterpret_cast<RowPart*>(static_cast<char*>(ws) + l.rpart);
+  RowPart* dparts = tparts + static_cast<size_t>(R) * (b + 1) * kRowParts;
+  RowArgs ta{tgt_logits, tgt_ld, V, tgt_off, 0, R, max_rows, temperature, top_p, row_max, row_argmax, row_lse,
+             row_cut, row_kept_lse, status_word(ws)};
+  RowArgs da{draft_logits, draft_ld, V, pos_off, b, R, max_pos, temperature, nullptr, draft_max, draft_argmax,
+             draft_lse, nullptr, nullptr, status_word(ws)};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool t16 = dtype == SV_BF16, d16 = draft_dtype == SV_BF16;
+  if (t16 && d16)
+    hipLaunchKernelGGL((k_rows_dense<SV_BF16, SV_BF16>), dim3(grid), dim3(kDenseNT), 0, s, ta, da, max_rows, tparts,
+                       dparts);
+  else if (t16)
+    hipLaunchKernelGGL((k_rows_dense<SV_BF16, SV_F32>), dim3(grid), dim3(kDenseNT), 0, s, ta, da, max_rows, tparts,
+                       dparts);
+  else if (d16)
+    hipLaunchKernelGGL((k_rows_dense<SV_F32, SV_BF16>), dim3(grid), dim3(kDenseNT), 0, s, ta, da, max_rows, tparts,
+                       dparts);
+  else
+    hipLaunchKernelGGL((k_rows_dense<SV_F32, SV_F32>), dim3(grid), dim3(kDenseNT), 0, s, ta, da, max_rows, tparts,
+                       dparts);
+  if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
+  hipLaunchKernelGGL(k_rows_merge, dim3((n_all + 255) / 256), dim3(256), 0, s, ta, da, max_rows,
+                     static_cast<int>(n_all), tparts, dparts);
+  return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
 }

@@ -222,34 +222,179 @@ template <int DT, int NT, int BATCH>
 __device__ __forceinline__ void row_stats_at(const RowArgs& a, const void* rowp, int p, float T, float tp, bool topp_on,
                              uint32_t* hist, RowShared<NT>& sh);
 
-// Statistics of row p (work item p of the request found from row_off), by one
-// block of NT threads.  `hist` holds kHistWords words of LDS (bf16 rows only).
-template <int DT, int NT, int BATCH>
-__device__ void row_block(const RowArgs& a, int p, uint32_t* hist, RowShared<NT>& sh) {
+// Where row p (work item p of the request found from row_off) lies and how it
+// is filtered; ok = false if the offsets are malformed (status raised).
+struct RowLoc {
+  bool ok, topp_on;
+  const void* rowp;
+  float T, tp;
+};
+
+template <int DT, int NT>
+__device__ __forceinline__ RowLoc row_locate(const RowArgs& a, int p, RowShared<NT>& sh) {
+  RowLoc l{false, false, nullptr, 0.0f, 1.0f};
   const int tid = threadIdx.x;
   const int r = find_request<NT>(a.row_off, a.R, p, &sh.req);
   if (r < 0) {
     if (tid == 0) raise_status(a.status, SV_ST_BAD_OFFSETS);
-    return;
+    return l;
   }
   const int j = p - a.row_off[r];
   if (a.row_stride > 0 && j >= a.row_stride) {
     if (tid == 0) raise_status(a.status, SV_ST_BAD_OFFSETS);
-    return;
+    return l;
   }
   const int64_t row = a.row_stride > 0 ? static_cast<int64_t>(r) * a.row_stride + j : static_cast<int64_t>(p);
   const size_t esz = DT == SV_BF16 ? 2 : 4;
-  const void* rowp = static_cast<const char*>(a.logits) + static_cast<size_t>(row) * static_cast<size_t>(a.ld) * esz;
-  const float T = a.T[r];
-  float tp = a.top_p ? a.top_p[r] : 1.0f;
-  if (tid == 0 && !(T >= 0.0f)) raise_status(a.status, SV_ST_BAD_TEMPERATURE);
-  const bool want_cut = a.row_cut != nullptr;
-  const bool topp_on = want_cut && a.top_p != nullptr && !(tp >= 1.0f);
-  if (topp_on && !(tp > 0.0f)) {
+  l.rowp = static_cast<const char*>(a.logits) + static_cast<size_t>(row) * static_cast<size_t>(a.ld) * esz;
+  l.T = a.T[r];
+  l.tp = a.top_p ? a.top_p[r] : 1.0f;
+  if (tid == 0 && !(l.T >= 0.0f)) raise_status(a.status, SV_ST_BAD_TEMPERATURE);
+  l.topp_on = a.row_cut != nullptr && a.top_p != nullptr && !(l.tp >= 1.0f);
+  if (l.topp_on && !(l.tp > 0.0f)) {
     if (tid == 0) raise_status(a.status, SV_ST_BAD_TOP_P);
-    tp = 1e-30f;  // keeps the top value only
+    l.tp = 1e-30f;  // keeps the top value only
   }
-  row_stats_at<DT, NT, BATCH>(a, rowp, p, T, tp, topp_on, hist, sh);
+  l.ok = true;
+  return l;
+}
+
+// Statistics of row p (work item p of the request found from row_off), by one
+// block of NT threads.  `hist` holds kHistWords words of LDS (bf16 rows only).
+template <int DT, int NT, int BATCH>
+__device__ void row_block(const RowArgs& a, int p, uint32_t* hist, RowShared<NT>& sh) {
+  const RowLoc l = row_locate<DT, NT>(a, p, sh);
+  if (l.ok) row_stats_at<DT, NT, BATCH>(a, l.rowp, p, l.T, l.tp, l.topp_on, hist, sh);
+}
+
+// ------------------------------------------------------------------ bf16 streaming path (no cut)
+// Maximum, argmax (lowest index) and sum_v exp(l_v / T) of a bf16 row, or of
+// the vectors [v0, v1) of it, in one pass, when no top-p cut is wanted (the
+// histogram's LDS atomics would only cost time).  Each thread keeps a running
+// maximum m and a sum of exp((l - m) / T), rescaled in double when m grows;
+// the 8 values of a 16-byte vector are exponentiated in fp32 (the hardware
+// exp2 of (l - m) * log2(e) / T; a term below 2^-126 of the running maximum
+// may flush to 0, far below the sum's rounding) and summed in fp32, the
+// vector sums in double; the block combines the threads' sums in double
+// (fp32 accumulation, as the row statistics are specified).  Output: the
+// block maximum M, the packed argmax key (order key of the value above the
+// complemented index; 0 if the range is empty) and S = sum exp2((l - M) * c2)
+// with c2 = log2(e) / T, so that lse = M / T + log(S).  T = 0: M and the key
+// only (S = 0).  NaN and +-Inf raise SV_ST_NONFINITE.  `tail`: the elements past
+// the last full vector belong to this range.
+struct StreamPart {
+  float M;
+  uint64_t key;
+  double S;
+};
+
+__device__ __forceinline__ float soft_c2(float T) { return T > 0.0f ? 1.4426950408889634f / T : 0.0f; }
+
+template <int NT, int BATCH>
+__device__ __forceinline__ StreamPart stream_part_bf16(const uint16_t* rp, int V, int v0, int v1, bool tail, float T,
+                                                       uint32_t* status, RowShared<NT>& sh) {
+  const int tid = threadIdx.x;
+  const uint4* vp = reinterpret_cast<const uint4*>(rp);
+  const int nvec = V >> 3;
+  const bool sums = T > 0.0f;
+  const float c2 = soft_c2(T);  // log2(e) / T
+  // The thread's terms are exp2(fma(l, c2, -mc)) with mc = fl(m * c2): the
+  // frame mc changes (exactly, in double) when m grows; the block frame is
+  // M * c2 in double.
+  float m = -INFINITY, mc = -INFINITY, mn = INFINITY;
+  double s = 0.0;
+  int bvi = -1;
+  uint4 bv = {0, 0, 0, 0};
+  auto take = [&](const uint4& d, int vi) {
+    float v[8];
+    v[0] = bf16_lo(d.x); v[1] = bf16_hi(d.x); v[2] = bf16_lo(d.y); v[3] = bf16_hi(d.y);
+    v[4] = bf16_lo(d.z); v[5] = bf16_hi(d.z); v[6] = bf16_lo(d.w); v[7] = bf16_hi(d.w);
+    const float vm = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])), fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
+    mn = fminf(fminf(mn, fminf(v[0], v[1])), fminf(fminf(v[2], v[3]), fminf(v[4], v[5])));
+    mn = fminf(mn, fminf(v[6], v[7]));
+    if (vm > m) {  // rare after the first vectors: the frame change runs in double
+      const float mcn = vm * c2;
+      if (sums) s *= exp2(static_cast<double>(mc) - static_cast<double>(mcn));  // 0 while m = -inf
+      m = vm;
+      mc = mcn;
+      bvi = vi;
+      bv = d;
+    }
+    if (sums) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc += __builtin_amdgcn_exp2f(fmaf(v[q], c2, -mc));
+      s += static_cast<double>(acc);
+    }
+  };
+  int v = v0 + tid;
+  // unconditional loads, indices clamped to the range's last vector (re-read,
+  // unused): no branch makes the compiler wait for the batch in flight
+  const int last = v1 - 1;
+  uint4 cur[BATCH];
+  if (v1 > v0) {
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) cur[k] = load16_stream(vp + min(v + k * NT, last));
+  }
+  while (v < v1) {
+    const int vn = v + BATCH * NT;
+    uint4 nxt[BATCH];
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) nxt[k] = load16_stream(vp + min(vn + k * NT, last));
+    if (v + (BATCH - 1) * NT < v1) {  // a full batch: no range checks
+#pragma unroll
+      for (int k = 0; k < BATCH; ++k) take(cur[k], v + k * NT);
+    } else {
+#pragma unroll
+      for (int k = 0; k < BATCH; ++k)
+        if (v + k * NT < v1) take(cur[k], v + k * NT);
+    }
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) cur[k] = nxt[k];
+    v = vn;
+  }
+  int bidx = -1;
+  float best = m;
+  if (bvi >= 0) {
+    const float e[8] = {bf16_lo(bv.x), bf16_hi(bv.x), bf16_lo(bv.y), bf16_hi(bv.y),
+                        bf16_lo(bv.z), bf16_hi(bv.z), bf16_lo(bv.w), bf16_hi(bv.w)};
+    int k = 7;
+#pragma unroll
+    for (int q = 7; q >= 0; --q)
+      if (e[q] == best) k = q;
+    bidx = bvi * 8 + k;
+  }
+  if (tail) {
+    for (int e = (nvec << 3) + tid; e < V; e += NT) {  // elements past the last full vector
+      const float f = __uint_as_float(static_cast<uint32_t>(rp[e]) << 16);
+      mn = fminf(mn, f);
+      if (f > m) {
+        const float mcn = f * c2;
+        if (sums) s *= exp2(static_cast<double>(mc) - static_cast<double>(mcn));
+        m = f;
+        mc = mcn;
+      }
+      if (f > best || bidx < 0) {
+        best = f;
+        bidx = e;
+      }
+      if (sums) s += static_cast<double>(__builtin_amdgcn_exp2f(fmaf(f, c2, -mc)));
+    }
+  }
+  if (mn == -INFINITY) raise_status(status, SV_ST_NONFINITE);
+  uint64_t packed =
+      bidx >= 0 ? (static_cast<uint64_t>(mono_key(best)) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(bidx)) : 0;
+  StreamPart out;
+  out.key = block_max_u64<NT>(packed, sh.red_u64);
+  out.M = out.key ? key_value(static_cast<uint32_t>(out.key >> 32)) : -INFINITY;
+  out.S = 0.0;
+  if (sums) {  // this thread's sum moved to the block frame M * c2, in double
+    const double part =
+        m > -INFINITY ? s * exp2(static_cast<double>(mc) - static_cast<double>(out.M) * static_cast<double>(c2)) : 0.0;
+    out.S = block_sum_f64<NT>(part, sh.red_f64);
+  }
+  if (tid == 0 && !(out.M < INFINITY && out.S < INFINITY)) raise_status(status, SV_ST_NONFINITE);
+  return out;
 }
 
 // Statistics of the row at `rowp` at temperature T (top-p cut when topp_on),
@@ -259,6 +404,20 @@ __device__ __forceinline__ void row_stats_at(const RowArgs& a, const void* rowp,
                              uint32_t* hist, RowShared<NT>& sh) {
   const int tid = threadIdx.x;
   if constexpr (DT == SV_BF16) {
+    if (!topp_on) {  // no cut wanted: one streaming pass
+      const StreamPart sp =
+          stream_part_bf16<NT, BATCH>(static_cast<const uint16_t*>(rowp), a.V, 0, a.V >> 3, true, T, a.status, sh);
+      if (tid == 0) {
+        const int am = static_cast<int>(argmax_token(sp.key));
+        if (T == 0.0f)
+          write_row(a, p, sp.M, am, 0.0, sp.M, 0.0);
+        else {
+          const double lse = static_cast<double>(sp.M) / static_cast<double>(T) + log(sp.S);
+          write_row(a, p, sp.M, am, lse, -INFINITY, lse);
+        }
+      }
+      return;
+    }
     for (int k = tid; k < kHistWords; k += NT) hist[k] = 0u;
     __syncthreads();
     const uint16_t* rp = static_cast<const uint16_t*>(rowp);
@@ -268,16 +427,17 @@ __device__ __forceinline__ void row_stats_at(const RowArgs& a, const void* rowp,
     int bvec = -1;
     uint4 bbins = {0, 0, 0, 0};
     int v = tid;
+    const int last = nvec - 1;  // unconditional, clamped loads (see stream_row_bf16)
     uint4 cur[BATCH];
+    if (nvec > 0) {
 #pragma unroll
-    for (int k = 0; k < BATCH; ++k)
-      if (v + k * NT < nvec) cur[k] = load16_stream(vp + v + k * NT);
+      for (int k = 0; k < BATCH; ++k) cur[k] = load16_stream(vp + min(v + k * NT, last));
+    }
     while (v < nvec) {
       const int vn = v + BATCH * NT;
       uint4 nxt[BATCH];
 #pragma unroll
-      for (int k = 0; k < BATCH; ++k)
-        if (vn + k * NT < nvec) nxt[k] = load16_stream(vp + vn + k * NT);
+      for (int k = 0; k < BATCH; ++k) nxt[k] = load16_stream(vp + min(vn + k * NT, last));
 #pragma unroll
       for (int k = 0; k < BATCH; ++k) {
         if (v + k * NT < nvec) {

@@ -19,7 +19,8 @@ import numpy as np
 import torch
 
 from . import (SV_BF16, SV_F32, SV_Q_DENSE, SV_Q_MIXTURE, dvl_alloc_pack, make_workspace, sv_accept, sv_mixture_q,
-               sv_accept_sample, sv_residual_sample, sv_softmax_stats, sv_topp_threshold, sv_verify_rows)
+               sv_accept_sample, sv_residual_sample, sv_softmax_stats, sv_topp_threshold, sv_verify_rows,
+               sv_verify_rows_dense)
 
 
 def row_pitch(V: int, dtype: str) -> int:
@@ -164,6 +165,13 @@ class VerifyStep:
                        self.row_cut, self.row_kept, comp, comp_ld, self.K, self.b, self.pos_off, self.max_pos,
                        self.branch_T, self.ws, self.ws_bytes, stream)
 
+    def run_rows_dense(self, tgt, tgt_ld, draft, draft_ld, stream=None):
+        """Target rows and the dense draft's rows in one launch."""
+        sv_verify_rows_dense(tgt, self.dt, tgt_ld, self.V, self.tgt_off, self.R, self.max_rows, self.T,
+                             self.top_p if self.use_topp else None, self.row_max, self.row_argmax, self.row_lse,
+                             self.row_cut, self.row_kept, draft, self.dt, draft_ld, self.b, self.pos_off,
+                             self.max_pos, self.d_max, self.d_argmax, self.d_lse, self.ws, self.ws_bytes, stream)
+
     def run_accept_sample(self, tgt, tgt_ld, *, draft=None, draft_ld=0, comp=None, comp_ld=0, stream=None):
         """Posterior (mixture), acceptance and the draw: two launches.  Soft
         branches read the component rows again (`comp`)."""
@@ -182,11 +190,10 @@ class VerifyStep:
                    fused=False):
         """The verification calls on torch's current stream.  With `side_stream`,
         the target-row statistics run there, concurrently with the proposal.
-        With `fused`: sv_verify_rows (mixture) and sv_accept_sample."""
+        With `fused`: sv_verify_rows (mixture) or sv_verify_rows_dense, then sv_accept_sample."""
         if fused:
             if self.q_mode == SV_Q_DENSE:
-                self.run_rows(tgt, tgt_ld)
-                self.run_proposal(draft=draft, draft_ld=draft_ld)
+                self.run_rows_dense(tgt, tgt_ld, draft, draft_ld)
             else:
                 self.run_rows_fused(tgt, tgt_ld, comp, comp_ld)
             self.run_accept_sample(tgt, tgt_ld, draft=draft, draft_ld=draft_ld, comp=comp, comp_ld=comp_ld)

@@ -222,6 +222,23 @@ int32_t sv_verify_rows(const void* tgt_logits, int32_t dtype, int64_t tgt_ld, in
                        int32_t K, int32_t b, const int32_t* pos_off, int32_t max_pos,
                        const float* branch_T, void* ws, size_t ws_bytes, void* stream);
 
+/* sv_verify_rows_dense: sv_topp_threshold over the packed target rows (row_off
+ * = tgt_off, row_stride 0) and sv_softmax_stats over the dense draft's rows
+ * (row_off = pos_off, row_stride = b: position i of request r is row r*b + i
+ * of draft_logits, at the request's temperature, no top-p), in ONE launch:
+ * its blocks take target rows first and draft rows after, so both read
+ * streams share every compute unit.  Same method and pages as those two calls;
+ * outputs as theirs (draft_max, draft_argmax, draft_lse[max_pos] indexed by
+ * pos_off[r] + i).  draft_dtype may differ from dtype.  Uses the workspace's
+ * status word only. */
+int32_t sv_verify_rows_dense(const void* tgt_logits, int32_t dtype, int64_t tgt_ld, int32_t V,
+                             const int32_t* tgt_off, int32_t R, int32_t max_rows, const float* temperature,
+                             const float* top_p, float* row_max, int32_t* row_argmax, double* row_lse,
+                             float* row_cut, double* row_kept_lse, const void* draft_logits,
+                             int32_t draft_dtype, int64_t draft_ld, int32_t b, const int32_t* pos_off,
+                             int32_t max_pos, float* draft_max, int32_t* draft_argmax, double* draft_lse,
+                             void* ws, size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------- acceptance */
 
 /* sv_accept [DBLast, "Assumptions": speculative sampling with rejection

@@ -192,10 +192,16 @@ def test_row_stats_edges(dtype, V):
     o = oracle.row_stats_batch(allrows, req, T, tp)
     assert np.array_equal(mx, o["max"])
     assert np.array_equal(am, o["argmax"])
-    np.testing.assert_allclose(lse, o["lse"], rtol=1e-12, atol=1e-12)
+    # bf16 rows with top-p off take the streaming pass (fp32 exponentials,
+    # double sums): the 1e-5 relative bar of the row statistics; the exact
+    # histogram (top-p on) and the fp32 generic path agree to 1e-12
+    stream = np.repeat(tp >= 1.0, n) & (dtype == "bf16")
+    np.testing.assert_allclose(lse[~stream], o["lse"][~stream], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse[stream], o["lse"][stream], rtol=1e-5, atol=1e-12)
     ok = cut == o["cut"]
     assert np.all(ok | (o["margin"] < 1e-6)), list(zip(np.nonzero(~ok)[0], o["margin"][~ok]))
-    np.testing.assert_allclose(kept[ok], o["kept_lse"][ok], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(kept[ok & ~stream], o["kept_lse"][ok & ~stream], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(kept[ok & stream], o["kept_lse"][ok & stream], rtol=1e-5, atol=1e-12)
     assert sv.sv_get_status(ws) == 0
 
 
@@ -218,6 +224,14 @@ def test_row_stats_nonfinite_sets_status():
     sv.sv_topp_threshold(dev, sv.SV_BF16, V, V, off, 0, 1, 1, torch.ones(1, device="cuda"),
                          torch.full((1,), 0.9, device="cuda"), *outs, ws, nb)
     assert sv.sv_get_status(ws) & 0x004
+    # the streaming pass (top-p off), with +inf / NaN and with -inf alone
+    ninf = np.linspace(-3, 3, V).astype(np.float32)
+    ninf[500] = -np.inf
+    for r in (row, ninf):
+        d2 = to_device_rows(synth.f32_to_bf16_bits(r[None]), V)
+        ws2, nb2 = sv.make_workspace(1, 16, 0, V)
+        sv.sv_topp_threshold(d2, sv.SV_BF16, V, V, off, 0, 1, 1, torch.ones(1, device="cuda"), None, *outs, ws2, nb2)
+        assert sv.sv_get_status(ws2) & 0x004
 
 
 def test_host_argument_errors():
