@@ -347,12 +347,14 @@ __device__ __host__ inline uint32_t argmax_token(uint64_t key) {
 }
 
 // ------------------------------------------------------------------ split rows
-// sv_verify_rows_dense streams each row without a top-p cut as kRowParts
-// blocks (contiguous parts of its vectors); each leaves its partial statistics
-// in the workspace and a second launch merges them.  Part 0 of every row also
+// sv_verify_rows_dense streams each row without a top-p cut as P blocks
+// (contiguous parts of its vectors; P = kRowParts when a top-p value is given,
+// else up to kDenseMaxParts); each leaves its partial statistics in the
+// workspace and a second launch merges them.  Part 0 of every row also
 // records whether the row was split (rows with a cut, and fp32 rows, are done
 // whole by part 0).
 constexpr int kRowParts = 2;
+constexpr int kDenseMaxParts = 16;
 struct RowPart {
   double S;      // sum over the part of exp2((l - M) * c2), c2 = log2(e) / T in fp32
   uint64_t key;  // packed argmax key of the part (0: empty)
@@ -366,7 +368,7 @@ struct RowPart {
 // [status word, 256 B][draw records, R][sub-chunk sums, R * NSUB * 2 doubles]
 // [branch argmax parts, R * K * b * kMixParts keys]
 // [soft branch rows, R * K * b each: lse (double), argmax (int32), max (float)]
-// [split-row parts, (R * (b + 1) + R * b) * kRowParts RowPart records]
+// [split-row parts, (R * (b + 1) + R * b) * kDenseMaxParts RowPart records]
 // Cross-block results travel through kernel boundaries (stream order), not
 // through in-kernel fences: a device-scope release on gfx950 writes back the
 // L2, which is far too costly to pay once per block.
@@ -387,7 +389,7 @@ __host__ __device__ inline WsLayout ws_layout(int R, int b, int K, int V) {
   l.barg = l.blse + align256(sizeof(double) * kb);
   l.bmax = l.barg + align256(sizeof(int32_t) * kb);
   l.rpart = l.bmax + align256(sizeof(float) * kb);
-  l.total = l.rpart + align256(sizeof(RowPart) * static_cast<size_t>(R) * (2 * b + 1) * kRowParts);
+  l.total = l.rpart + align256(sizeof(RowPart) * static_cast<size_t>(R) * (2 * b + 1) * kDenseMaxParts);
   return l;
 }
 

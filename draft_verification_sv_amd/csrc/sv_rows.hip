@@ -7,8 +7,9 @@ namespace sv {
 
 constexpr int kRowNT = 512;
 constexpr int kRowBatch = 8;  // 16-byte loads per thread per batch (x2 in flight)
-constexpr int kDenseNT = 256;  // sv_verify_rows_dense: kRowParts blocks of 256 per split row
+constexpr int kDenseNT = 256;  // sv_verify_rows_dense: P blocks of 256 per split row
 constexpr int kDenseBatch = 8;
+constexpr int kDensePartVec = 10240;  // vectors per part (160 KiB of bf16) without a cut
 
 // Row p of a's rows (p < the device-side count), by one block.
 template <int DT>
@@ -29,31 +30,33 @@ __global__ __launch_bounds__(kRowNT) void k_row_stats(RowArgs a) {
 }
 
 // Part `part` of row p of a (sv_verify_rows_dense).  A bf16 row without a
-// top-p cut is streamed as kRowParts blocks, each leaving its partial
-// statistics in parts[p * kRowParts + part]; any other row is done whole by
-// part 0, which marks it unsplit.
-template <int DT, int NT, int BATCH>
-__device__ __forceinline__ void stats_part(const RowArgs& a, int p, int part, RowPart* parts, uint32_t* hist,
+// top-p cut is streamed as P blocks, each leaving its partial statistics in
+// parts[p * P + part]; any other row is done whole by part 0, which marks it
+// unsplit.  kCut = false: no row of a has a top-p value (a.top_p is null), so
+// the cut's histogram code, table and LDS are left out.
+template <int DT, int NT, int BATCH, bool kCut>
+__device__ __forceinline__ void stats_part(const RowArgs& a, int p, int part, int P, RowPart* parts, uint32_t* hist,
                                            RowShared<NT>& sh) {
-  const int total = a.row_off[a.R];
-  if (p == 0 && part == 0 && threadIdx.x == 0 && (a.row_off[0] != 0 || total > a.max_rows || total < 0))
+  if (p == 0 && part == 0 && threadIdx.x == 0 && a.row_off[0] != 0) raise_status(a.status, SV_ST_BAD_OFFSETS);
+  if (kCut) exp_table_init(sh.etab);  // published by row_locate_fast's barrier
+  int total = 0;
+  const RowLoc l = row_locate_fast<DT, NT>(a, p, sh, total);
+  if (p == 0 && part == 0 && threadIdx.x == 0 && (total > a.max_rows || total < 0))
     raise_status(a.status, SV_ST_BAD_OFFSETS);
-  if (p >= total) return;
-  exp_table_init(sh.etab);  // published by row_locate's barriers
-  const RowLoc l = row_locate<DT, NT>(a, p, sh);
-  if (!l.ok) return;
-  RowPart* rec = parts + static_cast<size_t>(p) * kRowParts;
-  if (DT != SV_BF16 || l.topp_on) {
+  if (!l.ok || p >= total) return;
+  RowPart* rec = parts + static_cast<size_t>(p) * P;
+  const bool topp_on = kCut && l.topp_on;
+  if (DT != SV_BF16 || topp_on) {
     if (part != 0) return;
-    row_stats_at<DT, NT, BATCH>(a, l.rowp, p, l.T, l.tp, l.topp_on, hist, sh);
+    row_stats_at<DT, NT, BATCH>(a, l.rowp, p, l.T, l.tp, topp_on, hist, sh);
     if (threadIdx.x == 0) rec[0].split = 0;
     return;
   }
   const int nvec = a.V >> 3;
-  const int v0 = static_cast<int>(static_cast<int64_t>(nvec) * part / kRowParts);
-  const int v1 = static_cast<int>(static_cast<int64_t>(nvec) * (part + 1) / kRowParts);
-  const StreamPart sp = stream_part_bf16<NT, BATCH>(static_cast<const uint16_t*>(l.rowp), a.V, v0, v1,
-                                                     part == kRowParts - 1, l.T, a.status, sh);
+  const int v0 = static_cast<int>(static_cast<int64_t>(nvec) * part / P);
+  const int v1 = static_cast<int>(static_cast<int64_t>(nvec) * (part + 1) / P);
+  const StreamPart sp = stream_part_bf16<NT, BATCH>(static_cast<const uint16_t*>(l.rowp), a.V, v0, v1, part == P - 1,
+                                                     l.T, a.status, sh);
   if (threadIdx.x == 0) {
     RowPart o;
     o.S = sp.S;
@@ -67,26 +70,29 @@ __device__ __forceinline__ void stats_part(const RowArgs& a, int p, int part, Ro
 }
 
 // The packed target rows and the dense draft's rows in one grid
-// (sv_verify_rows_dense): kRowParts blocks per row, target rows first, then
-// draft rows.  One launch keeps every compute unit on both read streams, and
-// the parts spread a few hundred rows over the whole chip.
-template <int DT, int DDT>
-__global__ __launch_bounds__(kDenseNT) void k_rows_dense(RowArgs ta, RowArgs da, int n_tgt, RowPart* tparts,
+// (sv_verify_rows_dense): P blocks per row, target rows first, then draft
+// rows; blocks past a row set's device-side count exit after the lookup.
+// Many short blocks let the dispatcher keep every compute unit streaming to
+// the end (a compute unit issues its oldest waves first, so equal shares of
+// long blocks would end at unequal times).  Draft rows never take a cut;
+// kCut is false when no target row can either.
+template <int DT, int DDT, bool kCut>
+__global__ __launch_bounds__(kDenseNT) void k_rows_dense(RowArgs ta, RowArgs da, int n_tgt, int P, RowPart* tparts,
                                                          RowPart* dparts) {
   __shared__ RowShared<kDenseNT> sh;
-  __shared__ uint32_t hist[(DT == SV_BF16 || DDT == SV_BF16) ? kHistWords : 1];
-  const int q = blockIdx.x / kRowParts, part = blockIdx.x % kRowParts;
+  __shared__ uint32_t hist[kCut && DT == SV_BF16 ? kHistWords : 1];
+  const int q = blockIdx.x / P, part = blockIdx.x % P;
   if (q < n_tgt)
-    stats_part<DT, kDenseNT, kDenseBatch>(ta, q, part, tparts, hist, sh);
+    stats_part<DT, kDenseNT, kDenseBatch, kCut>(ta, q, part, P, tparts, hist, sh);
   else
-    stats_part<DDT, kDenseNT, kDenseBatch>(da, q - n_tgt, part, dparts, hist, sh);
+    stats_part<DDT, kDenseNT, kDenseBatch, false>(da, q - n_tgt, part, P, dparts, hist, sh);
 }
 
 // Merge of the split rows' parts (one thread per row): maximum and argmax key
 // by max, the sums rescaled to the row maximum in double with the parts' own
 // scale constant, lse = M / T + log(S).
-__global__ __launch_bounds__(256) void k_rows_merge(RowArgs ta, RowArgs da, int n_tgt, int n_all, RowPart* tparts,
-                                                    RowPart* dparts) {
+__global__ __launch_bounds__(256) void k_rows_merge(RowArgs ta, RowArgs da, int n_tgt, int n_all, int P,
+                                                    RowPart* tparts, RowPart* dparts) {
   const int q = blockIdx.x * blockDim.x + threadIdx.x;
   if (q >= n_all) return;
   const bool tgt = q < n_tgt;
@@ -94,11 +100,11 @@ __global__ __launch_bounds__(256) void k_rows_merge(RowArgs ta, RowArgs da, int 
   const int p = tgt ? q : q - n_tgt;
   const int total = a.row_off[a.R];
   if (p >= total || total > a.max_rows) return;
-  const RowPart* rec = (tgt ? tparts : dparts) + static_cast<size_t>(p) * kRowParts;
+  const RowPart* rec = (tgt ? tparts : dparts) + static_cast<size_t>(p) * P;
   if (!rec[0].split) return;
   float M = -INFINITY;
   uint64_t key = 0;
-  for (int k = 0; k < kRowParts; ++k) {
+  for (int k = 0; k < P; ++k) {
     M = fmaxf(M, rec[k].M);
     key = rec[k].key > key ? rec[k].key : key;
   }
@@ -110,7 +116,7 @@ __global__ __launch_bounds__(256) void k_rows_merge(RowArgs ta, RowArgs da, int 
   }
   const double c2 = static_cast<double>(soft_c2(T));
   double S = 0.0;
-  for (int k = 0; k < kRowParts; ++k)
+  for (int k = 0; k < P; ++k)
     if (rec[k].M > -INFINITY) S += rec[k].S * exp2((static_cast<double>(rec[k].M) - static_cast<double>(M)) * c2);
   const double lse = static_cast<double>(M) / static_cast<double>(T) + log(S);
   write_row(a, p, M, am, lse, -INFINITY, lse);
@@ -193,6 +199,19 @@ extern "C" int32_t sv_selftest_rows_host(void) {
   return 0;
 }
 
+// The cut's histogram (and its LDS, table and registers) only where a top-p value is given.
+template <int DT, int DDT>
+static int32_t launch_dense(const RowArgs& ta, const RowArgs& da, int32_t n_tgt, int P, RowPart* tparts,
+                            RowPart* dparts, unsigned grid, hipStream_t s) {
+  if (ta.top_p)
+    hipLaunchKernelGGL((k_rows_dense<DT, DDT, true>), dim3(grid), dim3(kDenseNT), 0, s, ta, da, n_tgt, P, tparts,
+                       dparts);
+  else
+    hipLaunchKernelGGL((k_rows_dense<DT, DDT, false>), dim3(grid), dim3(kDenseNT), 0, s, ta, da, n_tgt, P, tparts,
+                       dparts);
+  return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
+}
+
 extern "C" int32_t sv_verify_rows_dense(const void* tgt_logits, int32_t dtype, int64_t tgt_ld, int32_t V,
                                         const int32_t* tgt_off, int32_t R, int32_t max_rows,
                                         const float* temperature, const float* top_p, float* row_max,
@@ -215,29 +234,26 @@ extern "C" int32_t sv_verify_rows_dense(const void* tgt_logits, int32_t dtype, i
   if (ws_bytes < l.total) return SV_ERR_WORKSPACE;
   const unsigned n_all = static_cast<unsigned>(max_rows) + static_cast<unsigned>(max_pos);
   if (n_all == 0) return SV_OK;
-  const unsigned grid = n_all * kRowParts;
+  const int nvec = V >> 3;
+  int P = kRowParts;  // parts per split row
+  if (!top_p) P = nvec >= kDensePartVec * kDenseMaxParts ? kDenseMaxParts : (nvec + kDensePartVec - 1) / kDensePartVec;
+  P = P < 1 ? 1 : P;
+  if (static_cast<unsigned long long>(n_all) * P > 0x7FFFFFFFull) return SV_ERR_ARG;
+  const unsigned grid = n_all * static_cast<unsigned>(P);
   RowPart* tparts = reinterpret_cast<RowPart*>(static_cast<char*>(ws) + l.rpart);
-  RowPart* dparts = tparts + static_cast<size_t>(R) * (b + 1) * kRowParts;
+  RowPart* dparts = tparts + static_cast<size_t>(R) * (b + 1) * P;
   RowArgs ta{tgt_logits, tgt_ld, V, tgt_off, 0, R, max_rows, temperature, top_p, row_max, row_argmax, row_lse,
              row_cut, row_kept_lse, status_word(ws)};
   RowArgs da{draft_logits, draft_ld, V, pos_off, b, R, max_pos, temperature, nullptr, draft_max, draft_argmax,
              draft_lse, nullptr, nullptr, status_word(ws)};
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool t16 = dtype == SV_BF16, d16 = draft_dtype == SV_BF16;
-  if (t16 && d16)
-    hipLaunchKernelGGL((k_rows_dense<SV_BF16, SV_BF16>), dim3(grid), dim3(kDenseNT), 0, s, ta, da, max_rows, tparts,
-                       dparts);
-  else if (t16)
-    hipLaunchKernelGGL((k_rows_dense<SV_BF16, SV_F32>), dim3(grid), dim3(kDenseNT), 0, s, ta, da, max_rows, tparts,
-                       dparts);
-  else if (d16)
-    hipLaunchKernelGGL((k_rows_dense<SV_F32, SV_BF16>), dim3(grid), dim3(kDenseNT), 0, s, ta, da, max_rows, tparts,
-                       dparts);
-  else
-    hipLaunchKernelGGL((k_rows_dense<SV_F32, SV_F32>), dim3(grid), dim3(kDenseNT), 0, s, ta, da, max_rows, tparts,
-                       dparts);
-  if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
+  const int32_t st = t16 ? (d16 ? launch_dense<SV_BF16, SV_BF16>(ta, da, max_rows, P, tparts, dparts, grid, s)
+                                : launch_dense<SV_BF16, SV_F32>(ta, da, max_rows, P, tparts, dparts, grid, s))
+                         : (d16 ? launch_dense<SV_F32, SV_BF16>(ta, da, max_rows, P, tparts, dparts, grid, s)
+                                : launch_dense<SV_F32, SV_F32>(ta, da, max_rows, P, tparts, dparts, grid, s));
+  if (st != SV_OK) return st;
   hipLaunchKernelGGL(k_rows_merge, dim3((n_all + 255) / 256), dim3(256), 0, s, ta, da, max_rows,
-                     static_cast<int>(n_all), tparts, dparts);
+                     static_cast<int>(n_all), P, tparts, dparts);
   return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
 }

@@ -358,6 +358,46 @@ __device__ __forceinline__ void sub_sums(const SampleArgs& a, const DrawCtx& c, 
   // corrections of the mixture residual: lane t < ncorr holds branch token t
   const int ctok = mix_res && lane < c.ncorr ? c.ctok[lane] : -1;
   const double cdel = mix_res && lane < c.ncorr ? c.cw[lane] - c.cp[lane] : 0.0;
+  // one sub-chunk's two sums, the branch-token corrections added, by lane 0
+  auto publish = [&](int sub, double sp, double sw) {
+    const double tp = wave_sum_f64(sp);
+    double tw = dense_res ? wave_sum_f64(sw) : tp;
+    if (mix_res) {  // branch tokens in this sub-chunk: weight max(0, p - q) instead of p
+      const int v0 = sub * kLen;
+      const bool here = ctok >= v0 && ctok < v0 + kLen;
+      if (__ballot(here)) tw += wave_sum_f64(here ? cdel : 0.0);
+    }
+    if (lane == 0) {
+      double* pp = a.sub + (static_cast<size_t>(r) * a.NSUB + sub) * 2;
+      pp[0] = tw;
+      pp[1] = tp;
+    }
+  };
+  if (cut == -INFINITY) {  // no cut: every value weighs; sums straight from the registers
+#pragma unroll
+    for (int k = 0; k < kSubPerWave; ++k) {
+      const int sub = sub0 + k * (kSumNT / kWave);
+      if (sub >= a.NSUB) break;  // wave-uniform
+      const int g = sub * kSubG + lane;
+      const int valid = g < NG ? min(V - g * 8, 8) : 0;
+      float l[8], d[8];
+      unpack8<DT>(t0[k], t1[k], l);
+      if (dense_res) unpack8<DDT>(d0[k], d1[k], d);
+      double sp = 0.0, sw = 0.0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const bool keep = q < valid && l[q] >= cut;  // NaN and values past the row weigh 0
+        const double p = exp_tab(keep ? static_cast<double>(l[q]) * invT - kept : -INFINITY, tab);
+        sp += p;
+        if (dense_res) {
+          const double t = p - exp_tab(keep ? static_cast<double>(d[q]) * invT - dlse : -INFINITY, tab);
+          sw += t > 0.0 ? t : 0.0;
+        }
+      }
+      publish(sub, sp, sw);
+    }
+    return;
+  }
 #pragma unroll
   for (int k0 = 0; k0 < kSubPerWave; k0 += kL) {
     if (sub0 + k0 * (kSumNT / kWave) >= a.NSUB) break;  // wave-uniform
@@ -413,18 +453,7 @@ __device__ __forceinline__ void sub_sums(const SampleArgs& a, const DrawCtx& c, 
     for (int j = 0; j < kL; ++j) {
       const int sub = sub0 + (k0 + j) * (kSumNT / kWave);
       if (sub >= a.NSUB) break;  // wave-uniform
-      double tp = wave_sum_f64(sp[j]);
-      double tw = dense_res ? wave_sum_f64(sw[j]) : tp;
-      if (mix_res) {  // branch tokens in this sub-chunk: weight max(0, p - q) instead of p
-        const int v0 = sub * kLen;
-        const bool here = ctok >= v0 && ctok < v0 + kLen;
-        if (__ballot(here)) tw += wave_sum_f64(here ? cdel : 0.0);
-      }
-      if (lane == 0) {
-        double* pp = a.sub + (static_cast<size_t>(r) * a.NSUB + sub) * 2;
-        pp[0] = tw;
-        pp[1] = tp;
-      }
+      publish(sub, sp[j], sw[j]);
     }
   }
 }

@@ -357,7 +357,10 @@ def test_two_stream_step_matches_oracle(c):
 
 FUSED = [(1, dict()), (2, dict(V=2053, R=4)), (3, dict(V=2053, R=8, steps=3)),
          (4, dict(V=4099, R=4)), (5, dict(V=4099, R=8, steps=4)), (5, dict(V=1031, R=48, steps=2)),
-         (2, dict()), (3, dict()), (4, dict()), (5, dict(steps=6))]
+         (2, dict()), (3, dict()), (4, dict()), (5, dict(steps=6)),
+         # tiny rows: more row slices than 8-value vectors (empty slices), a
+         # row shorter than one vector, and a vector plus a ragged tail
+         (3, dict(V=13, R=2, steps=2)), (3, dict(V=7, R=2, steps=2)), (2, dict(V=8, R=1))]
 
 
 @pytest.mark.parametrize("c,kw", FUSED, ids=[f"cfg{c}-" + "-".join(f"{k}{v}" for k, v in kw.items()) for c, kw in FUSED])
@@ -368,6 +371,21 @@ def test_fused_rows_mixture_matches_oracle(c, kw):
     rep = None
     for s in range(w.steps):
         banner(f"fused {w.name} V={w.V} R={w.R} step {s}")
+        rep = compare_step(w, run(s), oracle_step(w, s), rep)
+    assert_rate(rep)
+    assert _sv().sv_get_status(vs.ws) == 0
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_mixture_without_top_p_matches_oracle(fused):
+    """The mixture proposal with no top-p: the draw's sums take every value
+    (no cut) and still apply the branch-token corrections of the residual."""
+    w = synth.config(5, V=4099, R=8, steps=3)
+    w.top_p = None
+    vs, run = gpu_step_runner(w, fused=fused)
+    rep = None
+    for s in range(w.steps):
+        banner(f"mixture without top-p fused={fused} step {s}")
         rep = compare_step(w, run(s), oracle_step(w, s), rep)
     assert_rate(rep)
     assert _sv().sv_get_status(vs.ws) == 0
