@@ -37,13 +37,13 @@ __global__ __launch_bounds__(kRowNT) void k_row_stats(RowArgs a) {
 template <int DT, int NT, int BATCH, bool kCut>
 __device__ __forceinline__ void stats_part(const RowArgs& a, int p, int part, int P, RowPart* parts, uint32_t* hist,
                                            RowShared<NT>& sh) {
-  if (p == 0 && part == 0 && threadIdx.x == 0 && a.row_off[0] != 0) raise_status(a.status, SV_ST_BAD_OFFSETS);
-  if (kCut) exp_table_init(sh.etab);  // published by row_locate_fast's barrier
-  int total = 0;
-  const RowLoc l = row_locate_fast<DT, NT>(a, p, sh, total);
-  if (p == 0 && part == 0 && threadIdx.x == 0 && (total > a.max_rows || total < 0))
+  const int total = a.row_off[a.R];
+  if (p == 0 && part == 0 && threadIdx.x == 0 && (a.row_off[0] != 0 || total > a.max_rows || total < 0))
     raise_status(a.status, SV_ST_BAD_OFFSETS);
-  if (!l.ok || p >= total) return;
+  if (p >= total) return;
+  if (kCut) exp_table_init(sh.etab);  // published by row_locate's barriers
+  const RowLoc l = row_locate<DT, NT>(a, p, sh);
+  if (!l.ok) return;
   RowPart* rec = parts + static_cast<size_t>(p) * P;
   const bool topp_on = kCut && l.topp_on;
   if (DT != SV_BF16 || topp_on) {

@@ -26,7 +26,6 @@
 // key of the values (at most 32 passes over the row, which stays in cache).
 #pragma once
 
-#include <float.h>
 #include <math.h>
 
 #include "sv_device.hpp"
@@ -114,8 +113,6 @@ struct RowShared {
   int req;
   int cut_d;
   double F;
-  float reqT, reqTp;  // row_locate_fast: the request's temperature and top-p value
-  int reqOff;         // and its first row
 };
 
 __device__ inline void write_row(const RowArgs& a, int p, float mx, int am, double lse, float cut, double kept) {
@@ -262,52 +259,6 @@ __device__ __forceinline__ RowLoc row_locate(const RowArgs& a, int p, RowShared<
   return l;
 }
 
-// row_locate with one round trip to memory: each thread loads the offsets,
-// temperature and top-p value of its requests together, and the thread whose
-// request holds row p publishes them; `total` receives row_off[R].  Also the
-// block's first barrier.
-template <int DT, int NT>
-__device__ __forceinline__ RowLoc row_locate_fast(const RowArgs& a, int p, RowShared<NT>& sh, int& total) {
-  RowLoc l{false, false, nullptr, 0.0f, 1.0f};
-  const int tid = threadIdx.x;
-  total = a.row_off[a.R];
-  int mine = 0;
-  for (int r = tid; r < a.R; r += NT) {
-    const int o0 = a.row_off[r], o1 = a.row_off[r + 1];
-    const float T = a.T[r];
-    const float tp = a.top_p ? a.top_p[r] : 1.0f;
-    if (o0 <= p && p < o1) {
-      sh.req = r;
-      sh.reqT = T;
-      sh.reqTp = tp;
-      sh.reqOff = o0;
-      mine = 1;
-    }
-  }
-  if (!__syncthreads_or(mine)) {
-    if (tid == 0 && p < total) raise_status(a.status, SV_ST_BAD_OFFSETS);
-    return l;
-  }
-  const int r = sh.req, j = p - sh.reqOff;
-  if (a.row_stride > 0 && j >= a.row_stride) {
-    if (tid == 0) raise_status(a.status, SV_ST_BAD_OFFSETS);
-    return l;
-  }
-  const int64_t row = a.row_stride > 0 ? static_cast<int64_t>(r) * a.row_stride + j : static_cast<int64_t>(p);
-  const size_t esz = DT == SV_BF16 ? 2 : 4;
-  l.rowp = static_cast<const char*>(a.logits) + static_cast<size_t>(row) * static_cast<size_t>(a.ld) * esz;
-  l.T = sh.reqT;
-  l.tp = sh.reqTp;
-  if (tid == 0 && !(l.T >= 0.0f)) raise_status(a.status, SV_ST_BAD_TEMPERATURE);
-  l.topp_on = a.row_cut != nullptr && a.top_p != nullptr && !(l.tp >= 1.0f);
-  if (l.topp_on && !(l.tp > 0.0f)) {
-    if (tid == 0) raise_status(a.status, SV_ST_BAD_TOP_P);
-    l.tp = 1e-30f;  // keeps the top value only
-  }
-  l.ok = true;
-  return l;
-}
-
 // Statistics of row p (work item p of the request found from row_off), by one
 // block of NT threads.  `hist` holds kHistWords words of LDS (bf16 rows only).
 template <int DT, int NT, int BATCH>
@@ -322,19 +273,15 @@ __device__ void row_block(const RowArgs& a, int p, uint32_t* hist, RowShared<NT>
 // histogram's LDS atomics would only cost time).  Each thread keeps a running
 // maximum m and a sum of exp((l - m) / T), rescaled in double when m grows;
 // the 8 values of a 16-byte vector are exponentiated in fp32 (the hardware
-// exp2 of t = l * c2 - fl(m * c2), c2 = log2(e) / T; a term below 2^-126 of
-// the running maximum may flush to 0, far below the sum's rounding) and summed
-// in fp32, the vector sums in double; the block combines the threads' sums in
-// double (fp32 accumulation, as the row statistics are specified).  A new
-// maximum shows as a t above the frame's own t (the fma is monotone in l and
-// bf16 neighbours differ by far more than its rounding), so the common vector
-// costs an fma, a 3-way max, an exp2 and an add per value; -inf (and negative
-// NaN) bit patterns are caught by a packed 16-bit maximum of the raw words.
-// Output: the block maximum M, the packed argmax key (order key of the value
-// above the complemented index; 0 if the range is empty) and
-// S = sum exp2((l - M) * c2), so that lse = M / T + log(S).  T = 0: M and the
-// key only (S = 0).  NaN and +-Inf raise SV_ST_NONFINITE.  `tail`: the
-// elements past the last full vector belong to this range.
+// exp2 of (l - m) * log2(e) / T; a term below 2^-126 of the running maximum
+// may flush to 0, far below the sum's rounding) and summed in fp32, the
+// vector sums in double; the block combines the threads' sums in double
+// (fp32 accumulation, as the row statistics are specified).  Output: the
+// block maximum M, the packed argmax key (order key of the value above the
+// complemented index; 0 if the range is empty) and S = sum exp2((l - M) * c2)
+// with c2 = log2(e) / T, so that lse = M / T + log(S).  T = 0: M and the key
+// only (S = 0).  NaN and +-Inf raise SV_ST_NONFINITE.  `tail`: the elements past
+// the last full vector belong to this range.
 struct StreamPart {
   float M;
   uint64_t key;
@@ -342,10 +289,6 @@ struct StreamPart {
 };
 
 __device__ __forceinline__ float soft_c2(float T) { return T > 0.0f ? 1.4426950408889634f / T : 0.0f; }
-
-__device__ __forceinline__ float max8(const float v[8]) {
-  return fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])), fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
-}
 
 template <int NT, int BATCH>
 __device__ __forceinline__ StreamPart stream_part_bf16(const uint16_t* rp, int V, int v0, int v1, bool tail, float T,
@@ -355,90 +298,61 @@ __device__ __forceinline__ StreamPart stream_part_bf16(const uint16_t* rp, int V
   const int nvec = V >> 3;
   const bool sums = T > 0.0f;
   const float c2 = soft_c2(T);  // log2(e) / T
-  // The thread's terms are exp2(fma(l, c2, -mc)) with mc = fl(m * c2) (finite
-  // before the first value, so that -inf values give exp2(-inf) = 0); the
-  // frame mc changes, exactly in double, when m grows; tm = fma(m, c2, -mc).
-  float m = -INFINITY, mc = -FLT_MAX, tm = -INFINITY;
+  // The thread's terms are exp2(fma(l, c2, -mc)) with mc = fl(m * c2): the
+  // frame mc changes (exactly, in double) when m grows; the block frame is
+  // M * c2 in double.
+  float m = -INFINITY, mc = -INFINITY, mn = INFINITY;
   double s = 0.0;
   int bvi = -1;
   uint4 bv = {0, 0, 0, 0};
-  u16x2 rmax = {0, 0};  // largest raw half-word: 0xFF80 and above only for -inf or a negative NaN
-  auto raw = [&](const uint4& d) {
-    rmax = __builtin_elementwise_max(rmax, __builtin_bit_cast(u16x2, d.x));
-    rmax = __builtin_elementwise_max(rmax, __builtin_bit_cast(u16x2, d.y));
-    rmax = __builtin_elementwise_max(rmax, __builtin_bit_cast(u16x2, d.z));
-    rmax = __builtin_elementwise_max(rmax, __builtin_bit_cast(u16x2, d.w));
-  };
-  auto unpack = [](const uint4& d, float v[8]) {
+  auto take = [&](const uint4& d, int vi) {
+    float v[8];
     v[0] = bf16_lo(d.x); v[1] = bf16_hi(d.x); v[2] = bf16_lo(d.y); v[3] = bf16_hi(d.y);
     v[4] = bf16_lo(d.z); v[5] = bf16_hi(d.z); v[6] = bf16_lo(d.w); v[7] = bf16_hi(d.w);
-  };
-  auto take_sum = [&](const uint4& d, int vi) {
-    raw(d);
-    float v[8], t[8];
-    unpack(d, v);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) t[q] = fmaf(v[q], c2, -mc);
-    if (max8(t) > tm) {  // a new maximum (rare after the first vectors): frame change in double
-      const float vm = max8(v);
+    const float vm = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])), fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
+    mn = fminf(fminf(mn, fminf(v[0], v[1])), fminf(fminf(v[2], v[3]), fminf(v[4], v[5])));
+    mn = fminf(mn, fminf(v[6], v[7]));
+    if (vm > m) {  // rare after the first vectors: the frame change runs in double
       const float mcn = vm * c2;
-      s *= exp2(static_cast<double>(mc) - static_cast<double>(mcn));
+      if (sums) s *= exp2(static_cast<double>(mc) - static_cast<double>(mcn));  // 0 while m = -inf
       m = vm;
       mc = mcn;
-      tm = fmaf(vm, c2, -mcn);
-      bvi = vi;
-      bv = d;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) t[q] = fmaf(v[q], c2, -mc);
-    }
-    float acc = 0.0f;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) acc += __builtin_amdgcn_exp2f(t[q]);
-    s += static_cast<double>(acc);
-  };
-  auto take_max = [&](const uint4& d, int vi) {  // T = 0: maximum and argmax only
-    raw(d);
-    float v[8];
-    unpack(d, v);
-    const float vm = max8(v);
-    if (vm > m) {
-      m = vm;
       bvi = vi;
       bv = d;
     }
+    if (sums) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc += __builtin_amdgcn_exp2f(fmaf(v[q], c2, -mc));
+      s += static_cast<double>(acc);
+    }
   };
+  int v = v0 + tid;
   // unconditional loads, indices clamped to the range's last vector (re-read,
   // unused): no branch makes the compiler wait for the batch in flight
-  auto run = [&](auto&& take) {
-    int v = v0 + tid;
-    const int last = v1 - 1;
-    uint4 cur[BATCH];
-    if (v1 > v0) {
+  const int last = v1 - 1;
+  uint4 cur[BATCH];
+  if (v1 > v0) {
 #pragma unroll
-      for (int k = 0; k < BATCH; ++k) cur[k] = load16_stream(vp + min(v + k * NT, last));
+    for (int k = 0; k < BATCH; ++k) cur[k] = load16_stream(vp + min(v + k * NT, last));
+  }
+  while (v < v1) {
+    const int vn = v + BATCH * NT;
+    uint4 nxt[BATCH];
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) nxt[k] = load16_stream(vp + min(vn + k * NT, last));
+    if (v + (BATCH - 1) * NT < v1) {  // a full batch: no range checks
+#pragma unroll
+      for (int k = 0; k < BATCH; ++k) take(cur[k], v + k * NT);
+    } else {
+#pragma unroll
+      for (int k = 0; k < BATCH; ++k)
+        if (v + k * NT < v1) take(cur[k], v + k * NT);
     }
-    while (v < v1) {
-      const int vn = v + BATCH * NT;
-      uint4 nxt[BATCH];
 #pragma unroll
-      for (int k = 0; k < BATCH; ++k) nxt[k] = load16_stream(vp + min(vn + k * NT, last));
-      if (v + (BATCH - 1) * NT < v1) {  // a full batch: no range checks
-#pragma unroll
-        for (int k = 0; k < BATCH; ++k) take(cur[k], v + k * NT);
-      } else {
-#pragma unroll
-        for (int k = 0; k < BATCH; ++k)
-          if (v + k * NT < v1) take(cur[k], v + k * NT);
-      }
-#pragma unroll
-      for (int k = 0; k < BATCH; ++k) cur[k] = nxt[k];
-      v = vn;
-    }
-  };
-  if (sums)
-    run(take_sum);
-  else
-    run(take_max);
+    for (int k = 0; k < BATCH; ++k) cur[k] = nxt[k];
+    v = vn;
+  }
   int bidx = -1;
   float best = m;
   if (bvi >= 0) {
@@ -450,11 +364,10 @@ __device__ __forceinline__ StreamPart stream_part_bf16(const uint16_t* rp, int V
       if (e[q] == best) k = q;
     bidx = bvi * 8 + k;
   }
-  bool ninf = rmax.x >= 0xFF80u || rmax.y >= 0xFF80u;
   if (tail) {
     for (int e = (nvec << 3) + tid; e < V; e += NT) {  // elements past the last full vector
-      ninf |= rp[e] >= 0xFF80u;
       const float f = __uint_as_float(static_cast<uint32_t>(rp[e]) << 16);
+      mn = fminf(mn, f);
       if (f > m) {
         const float mcn = f * c2;
         if (sums) s *= exp2(static_cast<double>(mc) - static_cast<double>(mcn));
@@ -468,7 +381,7 @@ __device__ __forceinline__ StreamPart stream_part_bf16(const uint16_t* rp, int V
       if (sums) s += static_cast<double>(__builtin_amdgcn_exp2f(fmaf(f, c2, -mc)));
     }
   }
-  if (ninf) raise_status(status, SV_ST_NONFINITE);
+  if (mn == -INFINITY) raise_status(status, SV_ST_NONFINITE);
   uint64_t packed =
       bidx >= 0 ? (static_cast<uint64_t>(mono_key(best)) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(bidx)) : 0;
   StreamPart out;
