@@ -248,7 +248,7 @@ __global__ __launch_bounds__(kFusedNT) void k_rows_mix(RowArgs ra, MixArgs ma, i
       raise_status(ra.status, SV_ST_BAD_OFFSETS);
     if (blk >= total) return;
     exp_table_init(sh.etab);  // published by row_block's first barrier
-    row_block<DT, kFusedNT, kFusedBatch>(ra, blk, hist, sh);
+    row_block<DT, kFusedNT, kFusedBatch, kSoft>(ra, blk, hist, sh);  // the greedy kernel keeps its register budget
   } else {
     const int u = blk - n_row_blocks;
     if constexpr (kSoft)

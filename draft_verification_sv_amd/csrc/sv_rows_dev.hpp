@@ -218,7 +218,7 @@ __device__ __forceinline__ double bin_mass(const uint32_t* hist, int d, double T
   return m;
 }
 
-template <int DT, int NT, int BATCH>
+template <int DT, int NT, int BATCH, bool kBatchCheck = true>
 __device__ __forceinline__ void row_stats_at(const RowArgs& a, const void* rowp, int p, float T, float tp, bool topp_on,
                              uint32_t* hist, RowShared<NT>& sh);
 
@@ -261,10 +261,10 @@ __device__ __forceinline__ RowLoc row_locate(const RowArgs& a, int p, RowShared<
 
 // Statistics of row p (work item p of the request found from row_off), by one
 // block of NT threads.  `hist` holds kHistWords words of LDS (bf16 rows only).
-template <int DT, int NT, int BATCH>
+template <int DT, int NT, int BATCH, bool kBatchCheck = true>
 __device__ void row_block(const RowArgs& a, int p, uint32_t* hist, RowShared<NT>& sh) {
   const RowLoc l = row_locate<DT, NT>(a, p, sh);
-  if (l.ok) row_stats_at<DT, NT, BATCH>(a, l.rowp, p, l.T, l.tp, l.topp_on, hist, sh);
+  if (l.ok) row_stats_at<DT, NT, BATCH, kBatchCheck>(a, l.rowp, p, l.T, l.tp, l.topp_on, hist, sh);
 }
 
 // ------------------------------------------------------------------ bf16 streaming path (no cut)
@@ -272,6 +272,9 @@ __device__ void row_block(const RowArgs& a, int p, uint32_t* hist, RowShared<NT>
 // the vectors [v0, v1) of it, in one pass, when no top-p cut is wanted (the
 // histogram's LDS atomics would only cost time).  Each thread keeps a running
 // maximum m and a sum of exp((l - m) / T), rescaled in double when m grows;
+// a full batch of BATCH vectors is checked once (its maximum first, then all
+// its exponentials in the frame that maximum sets: one branch per batch, so
+// the exponentials of the batch issue back to back);
 // the 8 values of a 16-byte vector are exponentiated in fp32 (the hardware
 // exp2 of (l - m) * log2(e) / T; a term below 2^-126 of the running maximum
 // may flush to 0, far below the sum's rounding) and summed in fp32, the
@@ -290,7 +293,7 @@ struct StreamPart {
 
 __device__ __forceinline__ float soft_c2(float T) { return T > 0.0f ? 1.4426950408889634f / T : 0.0f; }
 
-template <int NT, int BATCH>
+template <int NT, int BATCH, bool kBatchCheck = true>
 __device__ __forceinline__ StreamPart stream_part_bf16(const uint16_t* rp, int V, int v0, int v1, bool tail, float T,
                                                        uint32_t* status, RowShared<NT>& sh) {
   const int tid = threadIdx.x;
@@ -341,9 +344,51 @@ __device__ __forceinline__ StreamPart stream_part_bf16(const uint16_t* rp, int V
     uint4 nxt[BATCH];
 #pragma unroll
     for (int k = 0; k < BATCH; ++k) nxt[k] = load16_stream(vp + min(vn + k * NT, last));
-    if (v + (BATCH - 1) * NT < v1) {  // a full batch: no range checks
+    if (!kBatchCheck && v + (BATCH - 1) * NT < v1) {  // a full batch, one check per vector (fewer registers)
 #pragma unroll
       for (int k = 0; k < BATCH; ++k) take(cur[k], v + k * NT);
+    } else if (v + (BATCH - 1) * NT < v1) {  // a full batch: one frame check for its vectors
+      float vmx[BATCH];
+#pragma unroll
+      for (int k = 0; k < BATCH; ++k) {
+        const uint4& d = cur[k];
+        float w[8];
+        w[0] = bf16_lo(d.x); w[1] = bf16_hi(d.x); w[2] = bf16_lo(d.y); w[3] = bf16_hi(d.y);
+        w[4] = bf16_lo(d.z); w[5] = bf16_hi(d.z); w[6] = bf16_lo(d.w); w[7] = bf16_hi(d.w);
+        vmx[k] = fmaxf(fmaxf(fmaxf(w[0], w[1]), fmaxf(w[2], w[3])), fmaxf(fmaxf(w[4], w[5]), fmaxf(w[6], w[7])));
+        mn = fminf(fminf(mn, fminf(w[0], w[1])), fminf(fminf(w[2], w[3]), fminf(w[4], w[5])));
+        mn = fminf(mn, fminf(w[6], w[7]));
+      }
+      float bm = vmx[0];
+#pragma unroll
+      for (int k = 1; k < BATCH; ++k) bm = fmaxf(bm, vmx[k]);
+      if (bm > m) {
+        bool found = false;
+#pragma unroll
+        for (int k = 0; k < BATCH; ++k)
+          if (!found && vmx[k] == bm) {
+            found = true;
+            bvi = v + k * NT;
+            bv = cur[k];
+          }
+        const float mcn = bm * c2;
+        if (sums) s *= exp2(static_cast<double>(mc) - static_cast<double>(mcn));
+        m = bm;
+        mc = mcn;
+      }
+      if (sums) {
+#pragma unroll
+        for (int k = 0; k < BATCH; ++k) {
+          const uint4& d = cur[k];
+          float w[8];
+          w[0] = bf16_lo(d.x); w[1] = bf16_hi(d.x); w[2] = bf16_lo(d.y); w[3] = bf16_hi(d.y);
+          w[4] = bf16_lo(d.z); w[5] = bf16_hi(d.z); w[6] = bf16_lo(d.w); w[7] = bf16_hi(d.w);
+          float acc = 0.0f;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) acc += __builtin_amdgcn_exp2f(fmaf(w[q], c2, -mc));
+          s += static_cast<double>(acc);
+        }
+      }
     } else {
 #pragma unroll
       for (int k = 0; k < BATCH; ++k)
@@ -399,14 +444,15 @@ __device__ __forceinline__ StreamPart stream_part_bf16(const uint16_t* rp, int V
 
 // Statistics of the row at `rowp` at temperature T (top-p cut when topp_on),
 // written to output slot p of a's arrays, by one block of NT threads.
-template <int DT, int NT, int BATCH>
+template <int DT, int NT, int BATCH, bool kBatchCheck>
 __device__ __forceinline__ void row_stats_at(const RowArgs& a, const void* rowp, int p, float T, float tp, bool topp_on,
                              uint32_t* hist, RowShared<NT>& sh) {
   const int tid = threadIdx.x;
   if constexpr (DT == SV_BF16) {
     if (!topp_on) {  // no cut wanted: one streaming pass
       const StreamPart sp =
-          stream_part_bf16<NT, BATCH>(static_cast<const uint16_t*>(rowp), a.V, 0, a.V >> 3, true, T, a.status, sh);
+          stream_part_bf16<NT, BATCH, kBatchCheck>(static_cast<const uint16_t*>(rowp), a.V, 0, a.V >> 3, true, T,
+                                                   a.status, sh);
       if (tid == 0) {
         const int am = static_cast<int>(argmax_token(sp.key));
         if (T == 0.0f)
