@@ -309,8 +309,8 @@ __device__ __forceinline__ double exp_tab(double x, const double* tab) {
 // (kSumNT threads) covers a chunk of kSubPerWave sub-chunks per wave.
 constexpr int kSumNT = 256;
 constexpr int kSubG = 64;
-constexpr int kSubPerWave = 4;
-constexpr int kChunkSubs = kSubPerWave * (kSumNT / kWave);  // 16 sub-chunks, 1024 groups
+constexpr int kSubPerWave = 2;
+constexpr int kChunkSubs = kSubPerWave * (kSumNT / kWave);  // 8 sub-chunks, 512 groups (a block per 4096 values)
 
 __host__ __device__ inline int groups_of(int V) { return (V + 7) / 8; }
 __host__ __device__ inline int sub_chunks(int V) { return (groups_of(V) + kSubG - 1) / kSubG; }

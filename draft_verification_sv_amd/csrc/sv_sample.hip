@@ -261,7 +261,7 @@ struct TailShared {
 // by then.
 template <bool kDense>
 struct DLists {
-  static constexpr int kLists = kDense ? 2 : 4;                          // sub-chunks packed per pass
+  static constexpr int kLists = (kDense ? 2 : 4) < kSubPerWave ? (kDense ? 2 : 4) : kSubPerWave;  // sub-chunks per pass
   static constexpr int kCap = kLists * kSubG * 8;                        // values of a pass
   static constexpr int kPerWave = (kCap + kWave) * (kDense ? 2 : 1);     // floats
   static constexpr size_t kBytes = sizeof(float) * kPerWave * (kSumNT / kWave);
@@ -800,6 +800,80 @@ __device__ __forceinline__ void sub_sum_soft(const SampleArgs& a, const DrawCtx&
   }
 }
 
+// D (soft residual, bf16 rows, K <= kSoftB): the same sums over the values of
+// the nucleus only.  The wave stores its 64 target words and the K branch
+// words of the sub-chunk in LDS and packs the positions at or above the cut
+// into a list (wave scan of per-lane counts), so that the K exponentials per
+// value run over kept values with no idle lanes (about a fifth of a sub-chunk
+// at top-p 0.95).  Per value the terms are formed exactly as in soft_group
+// (branches in ascending order), so the pick kernel re-forms the same weights.
+constexpr int kSoftB = 8;  // branch rows per pass of soft_group; the list path takes K <= kSoftB
+struct SoftLists {
+  static constexpr size_t kPerWave = static_cast<size_t>(kSoftB + 1) * kWave * 16 + kSubG * 8 * sizeof(uint16_t);
+  static constexpr size_t kBytes = kPerWave * (kSumNT / kWave);
+};
+
+__device__ __forceinline__ void sub_sum_soft_lists(const SampleArgs& a, const DrawCtx& c, int r, int sub,
+                                                   const double* tab, char* lds) {
+  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+  u32x4_t* words = reinterpret_cast<u32x4_t*>(lds + wv * SoftLists::kPerWave);  // [1 + kSoftB][kWave], target first
+  uint16_t* pos = reinterpret_cast<uint16_t*>(words + (kSoftB + 1) * kWave);
+  const uint16_t* vals = reinterpret_cast<const uint16_t*>(words);  // value i of row j at j * 512 + i
+  const int V = a.V, NG = groups_of(V), K = a.K;
+  const int g = sub * kSubG + lane, gc = min(g, NG - 1);
+  const char* trowp = row_ptr(a.tgt, SV_BF16, c.trow, a.tgt_ld);
+  const char* crow0 = row_ptr(a.comp, SV_BF16, c.drow, a.comp_ld);
+  const size_t cstride = static_cast<size_t>(a.b) * static_cast<size_t>(a.comp_ld) * 2;
+  // 16-byte words as native vectors (kept in registers), all loads issued before any is used
+  const u32x4_t tword = *reinterpret_cast<const u32x4_t*>(trowp + static_cast<size_t>(gc) * 16);
+  u32x4_t cw[kSoftB];
+#pragma unroll
+  for (int j = 0; j < kSoftB; ++j)
+    cw[j] = *reinterpret_cast<const u32x4_t*>(crow0 + cstride * min(j, K - 1) + static_cast<size_t>(gc) * 16);
+  asm volatile("" ::: "memory");
+  words[lane] = tword;
+#pragma unroll
+  for (int j = 0; j < kSoftB; ++j) words[(1 + j) * kWave + lane] = cw[j];  // rows past K repeat row K - 1, unread
+  const uint4 t0 = {tword.x, tword.y, tword.z, tword.w};
+  float l[8];
+  decode8<SV_BF16>(t0, t0, g, V, g < NG, l);  // values past the row read -inf
+  const float cut = c.cut;
+  int cnt = 0;  // p > 0 only at or above the cut; -inf and NaN weigh 0
+#pragma unroll
+  for (int q = 0; q < 8; ++q) cnt += l[q] >= cut && l[q] > -INFINITY ? 1 : 0;
+  const int inc = wave_incl_scan_i32(cnt);
+  const int n = bcast_i32(inc, kWave - 1);
+  int o = inc - cnt;
+#pragma unroll
+  for (int q = 0; q < 8; ++q)
+    if (l[q] >= cut && l[q] > -INFINITY) pos[o++] = static_cast<uint16_t>(lane * 8 + q);
+  __syncwarp();
+  const double invT = c.invT, kept = c.kept, invTb = c.invTb;
+  double sp = 0.0, sw = 0.0;
+  for (int e = lane; e < n; e += kWave) {
+    const int i = pos[e];
+    const double p = exp_tab(static_cast<double>(__uint_as_float(static_cast<uint32_t>(vals[i]) << 16)) * invT - kept, tab);
+    double qv = 0.0;
+#pragma unroll
+    for (int j = 0; j < kSoftB; ++j) {
+      const double off = c.cw[min(j, K - 1)];
+      if (j < K && off < INFINITY)
+        qv += exp_tab(static_cast<double>(__uint_as_float(static_cast<uint32_t>(vals[(1 + j) * kSubG * 8 + i]) << 16)) *
+                          invTb - off,
+                      tab);
+    }
+    const double t = p - qv;
+    sp += p;
+    sw += t > 0.0 ? t : 0.0;
+  }
+  const double tp = wave_sum_f64(sp), tw = wave_sum_f64(sw);
+  if (lane == 0) {
+    double* pp = a.sub + (static_cast<size_t>(r) * a.NSUB + sub) * 2;
+    pp[0] = tw;
+    pp[1] = tp;
+  }
+}
+
 // Dynamic LDS of the soft tail: branch argmax [K][b] (int), log q_i(x_i | z)
 // [K][b] and the unnormalised log posterior [b + 1][K] (double); D's lists
 // reuse it.
@@ -998,7 +1072,12 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums_soft(SampleArgs a) {
   constexpr int kPer = kSumNT / kWave;  // sub-chunks of a soft chunk
   if (c.mode == kDrawSoft) {
     const int sub = ch * kPer + wv;
-    if (sub < a.NSUB) sub_sum_soft<DT>(a, c, r, sub, sh.etab);
+    if (sub < a.NSUB) {
+      if (DT == SV_BF16 && K <= kSoftB)
+        sub_sum_soft_lists(a, c, r, sub, sh.etab, reinterpret_cast<char*>(dyn));
+      else
+        sub_sum_soft<DT>(a, c, r, sub, sh.etab);
+    }
   } else if (ch % (kChunkSubs / kPer) == 0) {
     sub_sums<DT, DT, false>(a, c, r, ch / (kChunkSubs / kPer), reinterpret_cast<float*>(dyn), sh.etab);
   }
@@ -1258,7 +1337,8 @@ static int32_t launch_draw_t(const SampleArgs& a, hipStream_t s) {
 template <int DT>
 static int32_t launch_draw_soft(const SampleArgs& a, hipStream_t s) {
   const size_t tables = soft_tables_bytes(a.K, a.b);
-  const size_t dyn = tables > DLists<false>::kBytes ? tables : DLists<false>::kBytes;
+  size_t dyn = tables > DLists<false>::kBytes ? tables : DLists<false>::kBytes;
+  if (DT == SV_BF16 && a.K <= kSoftB && SoftLists::kBytes > dyn) dyn = SoftLists::kBytes;
   hipLaunchKernelGGL((k_draw_sums_soft<DT>), dim3(a.R * soft_chunks(a.V)), dim3(kSumNT), dyn, s, a);
   if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
   hipLaunchKernelGGL((k_pick<DT, DT, false, true>), dim3(a.R), dim3(kWave), 0, s, a);
