@@ -813,17 +813,19 @@ struct SoftLists {
   static constexpr size_t kBytes = kPerWave * (kSumNT / kWave);
 };
 
-__device__ __forceinline__ void sub_sum_soft_lists(const SampleArgs& a, const DrawCtx& c, int r, int sub,
-                                                   const double* tab, char* lds) {
-  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
-  u32x4_t* words = reinterpret_cast<u32x4_t*>(lds + wv * SoftLists::kPerWave);  // [1 + kSoftB][kWave], target first
+// Calls f(i, p, w) for every value i of sub-chunk `sub` at or above the cut,
+// by one wave (lane-strided over the packed list); `lds` is the wave's
+// SoftLists::kPerWave bytes.
+template <typename F>
+__device__ __forceinline__ void soft_nucleus(const SampleArgs& a, const char* trowp, const char* crow0,
+                                             size_t cstride, const double* off, int sub, float cut, double invT,
+                                             double kept, double invTb, const double* tab, char* lds, F&& f) {
+  const int lane = threadIdx.x & (kWave - 1);
+  u32x4_t* words = reinterpret_cast<u32x4_t*>(lds);  // [1 + kSoftB][kWave], target first
   uint16_t* pos = reinterpret_cast<uint16_t*>(words + (kSoftB + 1) * kWave);
   const uint16_t* vals = reinterpret_cast<const uint16_t*>(words);  // value i of row j at j * 512 + i
   const int V = a.V, NG = groups_of(V), K = a.K;
   const int g = sub * kSubG + lane, gc = min(g, NG - 1);
-  const char* trowp = row_ptr(a.tgt, SV_BF16, c.trow, a.tgt_ld);
-  const char* crow0 = row_ptr(a.comp, SV_BF16, c.drow, a.comp_ld);
-  const size_t cstride = static_cast<size_t>(a.b) * static_cast<size_t>(a.comp_ld) * 2;
   // 16-byte words as native vectors (kept in registers), all loads issued before any is used
   const u32x4_t tword = *reinterpret_cast<const u32x4_t*>(trowp + static_cast<size_t>(gc) * 16);
   u32x4_t cw[kSoftB];
@@ -837,7 +839,6 @@ __device__ __forceinline__ void sub_sum_soft_lists(const SampleArgs& a, const Dr
   const uint4 t0 = {tword.x, tword.y, tword.z, tword.w};
   float l[8];
   decode8<SV_BF16>(t0, t0, g, V, g < NG, l);  // values past the row read -inf
-  const float cut = c.cut;
   int cnt = 0;  // p > 0 only at or above the cut; -inf and NaN weigh 0
 #pragma unroll
   for (int q = 0; q < 8; ++q) cnt += l[q] >= cut && l[q] > -INFINITY ? 1 : 0;
@@ -848,24 +849,34 @@ __device__ __forceinline__ void sub_sum_soft_lists(const SampleArgs& a, const Dr
   for (int q = 0; q < 8; ++q)
     if (l[q] >= cut && l[q] > -INFINITY) pos[o++] = static_cast<uint16_t>(lane * 8 + q);
   __syncwarp();
-  const double invT = c.invT, kept = c.kept, invTb = c.invTb;
-  double sp = 0.0, sw = 0.0;
   for (int e = lane; e < n; e += kWave) {
     const int i = pos[e];
     const double p = exp_tab(static_cast<double>(__uint_as_float(static_cast<uint32_t>(vals[i]) << 16)) * invT - kept, tab);
     double qv = 0.0;
 #pragma unroll
     for (int j = 0; j < kSoftB; ++j) {
-      const double off = c.cw[min(j, K - 1)];
-      if (j < K && off < INFINITY)
+      const double oz = off[min(j, K - 1)];
+      if (j < K && oz < INFINITY)
         qv += exp_tab(static_cast<double>(__uint_as_float(static_cast<uint32_t>(vals[(1 + j) * kSubG * 8 + i]) << 16)) *
-                          invTb - off,
+                          invTb - oz,
                       tab);
     }
     const double t = p - qv;
-    sp += p;
-    sw += t > 0.0 ? t : 0.0;
+    f(i, p, t > 0.0 ? t : 0.0);
   }
+}
+
+__device__ __forceinline__ void sub_sum_soft_lists(const SampleArgs& a, const DrawCtx& c, int r, int sub,
+                                                   const double* tab, char* lds) {
+  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+  const size_t cstride = static_cast<size_t>(a.b) * static_cast<size_t>(a.comp_ld) * 2;
+  double sp = 0.0, sw = 0.0;
+  soft_nucleus(a, row_ptr(a.tgt, SV_BF16, c.trow, a.tgt_ld), row_ptr(a.comp, SV_BF16, c.drow, a.comp_ld), cstride,
+               c.cw, sub, c.cut, c.invT, c.kept, c.invTb, tab, lds + wv * SoftLists::kPerWave,
+               [&](int, double p, double w) {
+                 sp += p;
+                 sw += w;
+               });
   const double tp = wave_sum_f64(sp), tw = wave_sum_f64(sw);
   if (lane == 0) {
     double* pp = a.sub + (static_cast<size_t>(r) * a.NSUB + sub) * 2;
@@ -1113,6 +1124,8 @@ __global__ __launch_bounds__(kWave) void k_pick(SampleArgs a) {
   const double cwt = kDense ? 0.0 : rec.cw[lane];
   asm volatile("" ::: "memory");  // every load above is issued before any is used
   __shared__ double etab[kExpTab];
+  __shared__ __align__(16) char plists[kSoft ? SoftLists::kPerWave : 16];  // soft residual: the nucleus list
+  __shared__ double wsub[kSoft ? kSubG * 8 : 1];                              // and the sub-chunk's weights
   exp_table_init(etab);
   __syncthreads();
   double lw = 0.0, lp = 0.0;
@@ -1208,13 +1221,25 @@ __global__ __launch_bounds__(kWave) void k_pick(SampleArgs a) {
   double w8[8];
   bool formed = false;
   if constexpr (kSoft) {
-    if (mode == kDrawSoft) {  // the same weights as the sums kernel formed
-      double p8[8], s8[8];
+    if (mode == kDrawSoft && !use_p) {  // the same weights as the sums kernel formed
       const size_t cstride = static_cast<size_t>(a.b) * static_cast<size_t>(a.comp_ld) * (DT == SV_BF16 ? 2 : 4);
-      soft_group<DT>(a, row_ptr(a.tgt, DT, trow, a.tgt_ld), row_ptr(a.comp, DT, drow, a.comp_ld), cstride, rec.cw, g,
-                     cut, invT, kept, rec.invTb, etab, p8, s8);
+      const char* trowp = row_ptr(a.tgt, DT, trow, a.tgt_ld);
+      const char* crow0 = row_ptr(a.comp, DT, drow, a.comp_ld);
+      if (DT == SV_BF16 && a.K <= kSoftB) {  // over the nucleus only, as the sums kernel did
 #pragma unroll
-      for (int q = 0; q < 8; ++q) w8[q] = use_p ? p8[q] : s8[q];
+        for (int q = 0; q < 8; ++q) wsub[lane * 8 + q] = 0.0;
+        __syncwarp();
+        soft_nucleus(a, trowp, crow0, cstride, rec.cw, sub, cut, invT, kept, rec.invTb, etab, plists,
+                     [&](int i, double, double w) { wsub[i] = w; });
+        __syncwarp();
+#pragma unroll
+        for (int q = 0; q < 8; ++q) w8[q] = wsub[lane * 8 + q];
+      } else {
+        double p8[8], s8[8];
+        soft_group<DT>(a, trowp, crow0, cstride, rec.cw, g, cut, invT, kept, rec.invTb, etab, p8, s8);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) w8[q] = s8[q];
+      }
       formed = true;
     }
   }

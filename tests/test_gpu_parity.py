@@ -504,6 +504,22 @@ def test_soft_branches_match_oracle(c, kw):
     assert _sv().sv_get_status(vs.ws) == 0
 
 
+@pytest.mark.parametrize("K,top_p", [(3, 0.95), (12, 0.95), (2, None)])
+def test_soft_branches_other_component_counts(K, top_p):
+    """Soft branches with K below the eight branch rows the nucleus-list sums
+    hold (rows past K unused), above them (the per-group sums in passes of
+    eight branches), and without top-p (every value in the nucleus)."""
+    w = synth.make(f"soft-K{K}", R=8, V=4099, K=K, T=1.0, top_p=top_p, budget=64, seed=1200 + K, vseed=7,
+                   steps=2, branch_T=1.0)
+    vs, run = gpu_step_runner(w)
+    rep = None
+    for s in range(w.steps):
+        banner(f"soft K={K} top_p={top_p} step {s}")
+        rep = compare_step(w, run(s), oracle_step(w, s), rep)
+    assert_rate(rep)
+    assert _sv().sv_get_status(vs.ws) == 0
+
+
 def test_soft_branches_per_request_temperatures():
     """T_b per request, some 0 (point-mass branches, drafts from greedy
     branches) and some soft, in one step."""
