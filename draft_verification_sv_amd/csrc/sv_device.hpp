@@ -332,6 +332,7 @@ struct DrawRec {
   double invTb;      // soft branches: 1 / T_b
   int32_t ctok[64];  // greedy-branch residual: the distinct branch tokens at the slot
   double cw[64];     // and their draw weight max(0, p - q); soft: lse_z - log w_z per branch z
+  double cp[64];     // greedy-branch residual: p at those tokens
 };
 
 // ------------------------------------------------------------------ branch argmax parts

@@ -250,6 +250,7 @@ struct TailShared {
   // standalone draw: branch tokens and posterior weights at the slot
   int tv[64];
   double tw[64];
+  double mrow[65];  // soft tail: maximum of each position's log posterior
   double etab[kExpTab];  // the exponential's table
   DrawCtx c;
 };
@@ -309,6 +310,7 @@ __device__ __forceinline__ void write_record(const SampleArgs& a, int r, const D
   if (lane < c.ncorr) {
     d.ctok[lane] = c.ctok[lane];
     d.cw[lane] = c.cw[lane];
+    d.cp[lane] = c.cp[lane];
   }
 }
 
@@ -864,6 +866,7 @@ __device__ __forceinline__ void soft_nucleus(const SampleArgs& a, const char* tr
     const double t = p - qv;
     f(i, p, t > 0.0 ? t : 0.0);
   }
+  __syncwarp();  // the wave's list and words may be rewritten by its next sub-chunk
 }
 
 __device__ __forceinline__ void sub_sum_soft_lists(const SampleArgs& a, const DrawCtx& c, int r, int sub,
@@ -886,39 +889,45 @@ __device__ __forceinline__ void sub_sum_soft_lists(const SampleArgs& a, const Dr
 }
 
 // Dynamic LDS of the soft tail: branch argmax [K][b] (int), log q_i(x_i | z)
-// [K][b] and the unnormalised log posterior [b + 1][K] (double); D's lists
-// reuse it.
-constexpr long long kSoftMaxKb = 2048;  // K * b bound of the soft tail (its tables stay below 48 KB)
+// [K][b], the branch rows' lse [K][b] and the unnormalised log posterior
+// [b + 1][K] (double); D's lists reuse it.
+constexpr long long kSoftMaxKb = 2048;  // K * b bound of the soft tail (its tables stay below 60 KB)
 
 __host__ __device__ inline size_t soft_tables_bytes(int K, int b) {
   const size_t kb = static_cast<size_t>(K) * b;
-  return sizeof(int) * ((kb + 1) & ~static_cast<size_t>(1)) + sizeof(double) * kb +
+  return sizeof(int) * ((kb + 1) & ~static_cast<size_t>(1)) + 2 * sizeof(double) * kb +
          sizeof(double) * static_cast<size_t>(b + 1) * K;
 }
 
-// Blocks per request of the soft tail: one sub-chunk per wave, so that the K
-// branch exponentials per value spread over four times the blocks of the
-// greedy tail (whose chunks are kChunkSubs sub-chunks).
-__host__ __device__ inline int soft_chunks(int V) { return (sub_chunks(V) + kSumNT / kWave - 1) / (kSumNT / kWave); }
+// Blocks per request of the soft tail: kSoftSubs sub-chunks per wave, so that
+// a soft chunk is one chunk of the greedy tail (a p or greedy-branch draw in
+// soft mode then sums that chunk).
+constexpr int kSoftSubs = 2;
+constexpr int kSoftChunk = (kSumNT / kWave) * kSoftSubs;  // sub-chunks of a soft chunk
+static_assert(kSoftChunk == kChunkSubs, "a soft chunk is one greedy chunk");
+__host__ __device__ inline int soft_chunks(int V) { return (sub_chunks(V) + kSoftChunk - 1) / kSoftChunk; }
 
-// The fused tail with soft branches (one block per (request, soft chunk)): A
+// The fused tail with soft branches, first launch (one block per request): A
 // and B load the header, the draft tokens, the mixing logits, the branch
 // argmax and lse of the rows launch and every branch's logit at the draft
-// tokens; C (wave 0) runs the posterior and the acceptance tests; D sums the
-// drawn row: for a soft residual each wave sums one sub-chunk; a p or greedy-
-// branch draw takes the greedy tail's chunks (every fourth block).
+// tokens; C1 forms the posterior's exponentials, one (position, branch) per
+// thread; C (wave 0) runs the acceptance tests and writes the draw record.
+// The sums over the drawn row (k_soft_body) read only that record: with K
+// branch rows per value they are long enough that recomputing A-C in each of
+// their blocks, as the greedy tail does, would hold every block up before its
+// first load.
 template <int DT>
-__global__ __launch_bounds__(kSumNT) void k_draw_sums_soft(SampleArgs a) {
+__global__ __launch_bounds__(kSumNT) void k_soft_head(SampleArgs a) {
   __shared__ TailShared sh;
   extern __shared__ __align__(16) int dyn[];
   const int K = a.K, b = a.b, V = a.V, kb = K * b;
   int* g = dyn;
   double* lq = reinterpret_cast<double*>(dyn + ((kb + 1) & ~1));
-  double* S = lq + kb;
-  const int S4 = soft_chunks(V);
-  const int r = blockIdx.x / S4, ch = blockIdx.x % S4;
+  double* bls = lq + kb;  // lse of branch row (z, i), for the residual's offsets at the draw slot
+  double* S = bls + kb;
+  const int r = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
-  const bool report = ch == 0;
+  const bool report = true;
   DrawCtx& c = sh.c;
   const size_t bbase = static_cast<size_t>(r) * kb;  // component row (r, z, i) = bbase + z * b + i
 
@@ -958,15 +967,17 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums_soft(SampleArgs a) {
     const int z = k / Lr, i = k - z * Lr;
     const int xv = sh.x[i];
     double v = -INFINITY;
+    const size_t row = bbase + static_cast<size_t>(z) * b + i;
+    const double bl = softb ? a.blse[row] : 0.0;
     if (xv >= 0 && xv < V) {
-      const size_t row = bbase + static_cast<size_t>(z) * b + i;
       if (softb)
         v = static_cast<double>(load_val<DT>(row_ptr(a.comp, DT, static_cast<int64_t>(row), a.comp_ld), xv)) / Tbd -
-            a.blse[row];
+            bl;
       else
         v = g[z * b + i] == xv ? 0.0 : -INFINITY;
     }
     lq[z * b + i] = v;
+    bls[z * b + i] = bl;
   }
   if (wv == 1) {  // log q(z | y), q(z | y) = softmax of the mixing logits
     const bool act = lane < K;
@@ -1006,22 +1017,39 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums_soft(SampleArgs a) {
       if (k % b < Lr) a.branch_out[bbase + k] = g[k];
   __syncthreads();
 
+  // C1. the exponentials, one (position, branch) per thread (table method;
+  // arguments <= 0): S becomes exp(S_iz - M_i) and lq becomes q_i(x_i | z)
+  for (int i = tid; i <= Lr; i += kSumNT) {
+    double M = -INFINITY;
+    for (int z = 0; z < K; ++z) M = fmax(M, S[i * K + z]);
+    sh.mrow[i] = M;
+  }
+  __syncthreads();
+  for (int k = tid; k < (Lr + 1) * K; k += kSumNT) {
+    const int i = k / K, z = k - i * K;
+    const double M = sh.mrow[i];
+    S[k] = M > -INFINITY ? exp_tab(S[k] - M, sh.etab) : 0.0;
+    if (i < Lr) {
+      const double l = lq[z * b + i];
+      lq[z * b + i] = l > -INFINITY ? exp_tab(l, sh.etab) : 0.0;
+    }
+  }
+  __syncthreads();
+
   // C. acceptance and the draw context (wave 0)
   if (tid < kWave) {
-    // lane i: w_z^(i) = exp(S_iz - M) / sum, q(x_i | x_<i) = sum_z w_z exp(lq_zi)
+    // lane i: w_z^(i) = exp(S_iz - M) / sum, q(x_i | x_<i) = sum_z w_z q_i(x_i | z)
     const int il = min(lane, Lr);
-    const double* Si = S + static_cast<size_t>(il) * K;
-    double M = -INFINITY;
-    for (int z = 0; z < K; ++z) M = fmax(M, Si[z]);
+    const double* Si = S + static_cast<size_t>(il) * K;  // the exponentials of C1
+    const double M = sh.mrow[il];
     double tot = 0.0;
     if (M > -INFINITY)
-      for (int z = 0; z < K; ++z) tot += exp(Si[z] - M);
+      for (int z = 0; z < K; ++z) tot += Si[z];
     double q = 0.0;
     if (lane < Lr && M > -INFINITY) {
       for (int z = 0; z < K; ++z) {
-        const double w = exp(Si[z] - M) / tot;
-        const double l = lq[z * b + lane];
-        if (w != 0.0 && l > -INFINITY) q += w * exp(l);
+        const double w = Si[z] / tot;
+        if (w != 0.0) q += w * lq[z * b + lane];
       }
     }
     if (lane < Lr && !xok) q = 0.0;
@@ -1036,7 +1064,7 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums_soft(SampleArgs a) {
         if (a.u_out) a.u_out[k] = static_cast<float>(u);
         a.q_at_draft[k] = q;
         double* pw = a.post_w + k * K;
-        for (int z = 0; z < K; ++z) pw[z] = M > -INFINITY ? exp(Si[z] - M) / tot : 0.0;
+        for (int z = 0; z < K; ++z) pw[z] = M > -INFINITY ? Si[z] / tot : 0.0;
         if (!(M > -INFINITY)) raise_status(a.status, SV_ST_EMPTY_POSTERIOR);
       }
     }
@@ -1059,13 +1087,13 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums_soft(SampleArgs a) {
       c.ncorr = 0;
     }
     if (res && lane == n)  // the posterior at the draw slot, one weight per branch
-      for (int z = 0; z < K; ++z) sh.tw[z] = M > -INFINITY ? exp(Si[z] - M) / tot : 0.0;
+      for (int z = 0; z < K; ++z) sh.tw[z] = M > -INFINITY ? Si[z] / tot : 0.0;
     __syncwarp();
     if (res) {
       const bool in = lane < K;
       const double w = in ? sh.tw[lane] : 0.0;
       if (softb) {
-        const double bl = in ? a.blse[bbase + static_cast<size_t>(lane) * b + n] : 0.0;
+        const double bl = in ? bls[lane * b + n] : 0.0;  // n < L_r: stored in B
         if (in) c.cw[lane] = w > 0.0 ? bl - log(w) : INFINITY;
         if (lane == 0) c.ncorr = K;
       } else {
@@ -1078,19 +1106,48 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums_soft(SampleArgs a) {
     __syncwarp();
     if (report) write_record(a, r, c);
   }
-  __syncthreads();  // also ends every use of the tables, which D's lists overwrite
-  if (c.mode == kDrawGreedy) return;
-  constexpr int kPer = kSumNT / kWave;  // sub-chunks of a soft chunk
-  if (c.mode == kDrawSoft) {
-    const int sub = ch * kPer + wv;
-    if (sub < a.NSUB) {
-      if (DT == SV_BF16 && K <= kSoftB)
-        sub_sum_soft_lists(a, c, r, sub, sh.etab, reinterpret_cast<char*>(dyn));
-      else
-        sub_sum_soft<DT>(a, c, r, sub, sh.etab);
+}
+
+// The soft tail's sums over the drawn row (one block per (request, chunk)),
+// from the draw record of k_soft_head: for a soft residual each wave sums
+// kSoftSubs sub-chunks (over the nucleus lists for bf16 rows and K <= kSoftB);
+// a p or greedy-branch draw sums the block's chunk as the greedy tail does.
+template <int DT>
+__global__ __launch_bounds__(kSumNT) void k_soft_body(SampleArgs a) {
+  __shared__ DrawCtx c;
+  __shared__ double etab[kExpTab];
+  extern __shared__ __align__(16) int dyn[];
+  const int S4 = soft_chunks(a.V);
+  const int r = blockIdx.x / S4, ch = blockIdx.x % S4;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+  exp_table_init(etab);
+  if (tid < kWave) {
+    const DrawRec& d = a.rec[r];
+    const int nc = d.ncorr;
+    if (lane == 0) {
+      c.mode = d.mode; c.n = d.n; c.bonus = d.bonus; c.token = d.token; c.ncorr = nc;
+      c.cut = d.cut; c.invT = d.invT; c.kept = d.kept; c.dlse = d.dlse; c.invTb = d.invTb;
+      c.trow = d.trow; c.drow = d.drow;
     }
-  } else if (ch % (kChunkSubs / kPer) == 0) {
-    sub_sums<DT, DT, false>(a, c, r, ch / (kChunkSubs / kPer), reinterpret_cast<float*>(dyn), sh.etab);
+    if (lane < nc) {
+      c.ctok[lane] = d.ctok[lane];
+      c.cw[lane] = d.cw[lane];
+      c.cp[lane] = d.cp[lane];
+    }
+  }
+  __syncthreads();
+  if (c.mode == kDrawGreedy || c.mode == kDrawNone) return;
+  if (c.mode == kDrawSoft) {
+    for (int j = 0; j < kSoftSubs; ++j) {
+      const int sub = ch * kSoftChunk + j * (kSumNT / kWave) + wv;
+      if (sub >= a.NSUB) break;  // wave-uniform
+      if (DT == SV_BF16 && a.K <= kSoftB)
+        sub_sum_soft_lists(a, c, r, sub, etab, reinterpret_cast<char*>(dyn));
+      else
+        sub_sum_soft<DT>(a, c, r, sub, etab);
+    }
+  } else {
+    sub_sums<DT, DT, false>(a, c, r, ch, reinterpret_cast<float*>(dyn), etab);
   }
 }
 
@@ -1361,10 +1418,11 @@ static int32_t launch_draw_t(const SampleArgs& a, hipStream_t s) {
 // soft branches: the soft tail, then the pick
 template <int DT>
 static int32_t launch_draw_soft(const SampleArgs& a, hipStream_t s) {
-  const size_t tables = soft_tables_bytes(a.K, a.b);
-  size_t dyn = tables > DLists<false>::kBytes ? tables : DLists<false>::kBytes;
+  hipLaunchKernelGGL((k_soft_head<DT>), dim3(a.R), dim3(kSumNT), soft_tables_bytes(a.K, a.b), s, a);
+  if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
+  size_t dyn = DLists<false>::kBytes;
   if (DT == SV_BF16 && a.K <= kSoftB && SoftLists::kBytes > dyn) dyn = SoftLists::kBytes;
-  hipLaunchKernelGGL((k_draw_sums_soft<DT>), dim3(a.R * soft_chunks(a.V)), dim3(kSumNT), dyn, s, a);
+  hipLaunchKernelGGL((k_soft_body<DT>), dim3(a.R * soft_chunks(a.V)), dim3(kSumNT), dyn, s, a);
   if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
   hipLaunchKernelGGL((k_pick<DT, DT, false, true>), dim3(a.R), dim3(kWave), 0, s, a);
   return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
