@@ -9,7 +9,7 @@ constexpr int kRowNT = 512;
 constexpr int kRowBatch = 8;  // 16-byte loads per thread per batch (x2 in flight)
 constexpr int kDenseNT = 256;  // sv_verify_rows_dense: P blocks of 256 per split row
 constexpr int kDenseBatch = 4;
-constexpr int kDensePartVec = 10240;  // vectors per part (160 KiB of bf16) without a cut
+constexpr int kDensePartVec = 6400;  // vectors per part (100 KiB of bf16) without a cut
 
 // Row p of a's rows (p < the device-side count), by one block.
 template <int DT>

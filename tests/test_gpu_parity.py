@@ -205,6 +205,52 @@ def test_row_stats_edges(dtype, V):
     assert sv.sv_get_status(ws) == 0
 
 
+@pytest.mark.parametrize("V", [7, 1031, 151936])
+def test_dense_rows_edges(V):
+    """sv_verify_rows_dense without top-p (rows split into parts, streamed in
+    batches with one maximum check per batch): maximum and argmax (lowest index
+    among ties, ties inside a batch, across batches and across parts) exactly,
+    lse to the 1e-5 bar, for target and draft rows at T = 0, 0.5, 1 and 1.5."""
+    import torch
+
+    sv = _sv()
+    from draft_verification_sv_amd.step import row_pitch, to_device_rows
+
+    rng = np.random.default_rng(V + 7)
+    rows = _edge_rows(V, rng)
+    t = rows["normal"].copy()  # the maximum at two positions one batch stride apart, and at the row's end
+    for i in (V // 3, V // 3 + 256 * 8, V - 1):
+        t[i % V] = t.max() + 2.0
+    rows["ties_spread"] = t
+    stored = synth.f32_to_bf16_bits(np.stack(list(rows.values())))
+    n = len(stored)
+    T = np.array([0.0, 0.5, 1.0, 1.5], np.float32)
+    R, b = len(T), n - 1
+    tgt = np.concatenate([stored] * R)  # request r: all n rows as its L_r + 1 = n target rows
+    dft = np.stack([stored[1 + (r + j) % (n - 1)] for r in range(R) for j in range(b)])  # [R * b, V]
+    ld = row_pitch(V, "bf16")
+    dt, dd = to_device_rows(tgt, ld), to_device_rows(dft, ld)
+    d = dict(device="cuda")
+    tgt_off = torch.arange(R + 1, dtype=torch.int32, **d) * n
+    pos_off = torch.arange(R + 1, dtype=torch.int32, **d) * b
+    ws, nb = sv.make_workspace(R, b, 0, V)
+    f32, i32, f64 = torch.float32, torch.int32, torch.float64
+    ro = [torch.zeros(R * n, dtype=x, **d) for x in (f32, i32, f64, f32, f64)]
+    do = [torch.zeros(R * b, dtype=x, **d) for x in (f32, i32, f64)]
+    banner(f"sv_verify_rows_dense edges V={V}")
+    sv.sv_verify_rows_dense(dt, sv.SV_BF16, ld, V, tgt_off, R, R * n, torch.from_numpy(T).cuda(), None, *ro, dd,
+                            sv.SV_BF16, ld, b, pos_off, R * b, *do, ws, nb)
+    torch.cuda.synchronize()
+    for got, rows_, per in ((ro, tgt, n), (do, dft, b)):
+        o = oracle.row_stats_batch(rows_, np.repeat(np.arange(R), per), T)
+        mx, am, lse = [x.cpu().numpy() for x in got[:3]]
+        assert np.array_equal(mx, o["max"])
+        assert np.array_equal(am, o["argmax"])
+        hot = np.repeat(T > 0, per)
+        np.testing.assert_allclose(lse[hot], o["lse"][hot], rtol=1e-5, atol=1e-12)
+    assert sv.sv_get_status(ws) == 0
+
+
 def test_row_stats_nonfinite_sets_status():
     import torch
 
