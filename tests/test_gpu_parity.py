@@ -437,6 +437,42 @@ def test_mixture_without_top_p_matches_oracle(fused):
     assert _sv().sv_get_status(vs.ws) == 0
 
 
+def _random_workloads(seed, n):
+    """Seeded draws over config, vocabulary, request count, soft or greedy
+    branches, per-request block lengths, top-p on or off and the fused or
+    separate calls."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        c = int(rng.choice([1, 2, 3, 4, 5]))
+        V = int(rng.choice([7, 13, 64, 257, 1031, 2053, 4099, 9001, 32768]))
+        R = int(rng.integers(1, 24)) if V <= 10000 else int(rng.integers(2, 12))
+        soft = c in (4, 5) and rng.random() < 0.4
+        bt = float(rng.choice([0.3, 1.0, 2.0])) if soft else 0.0
+        ragged = bool(rng.random() < 0.3)
+        fused = bool(rng.random() < 0.6) or soft
+        topp_off = c in (4, 5) and rng.random() < 0.3
+        out.append((c, V, R, bt, ragged, fused, topp_off))
+    return out
+
+
+@pytest.mark.parametrize("seed", [101, 202, 303])
+def test_random_workloads_match_oracle(seed):
+    """Twenty seeded random small workloads per seed (two steps each) against
+    the oracle, under the usual bar."""
+    for c, V, R, bt, ragged, fused, topp_off in _random_workloads(seed, 20):
+        w = synth.config(c, V=V, R=R, steps=2, branch_T=bt, ragged=ragged)
+        if topp_off:
+            w.top_p = None
+        banner(f"random cfg{c} V={V} R={R} T_b={bt} ragged={ragged} fused={fused} top-p off={topp_off}")
+        vs, run = gpu_step_runner(w, fused=fused)
+        rep = None
+        for s in range(w.steps):
+            rep = compare_step(w, run(s), oracle_step(w, s), rep)
+        assert_rate(rep)
+        assert _sv().sv_get_status(vs.ws) == 0
+
+
 def test_determinism_repeat_runs():
     w = synth.config(4, V=8191, R=4)
     vs, run = gpu_step_runner(w)
