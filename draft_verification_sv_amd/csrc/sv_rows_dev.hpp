@@ -293,6 +293,15 @@ struct StreamPart {
 
 __device__ __forceinline__ float soft_c2(float T) { return T > 0.0f ? 1.4426950408889634f / T : 0.0f; }
 
+// Maximum of three values as the hardware's v_max3_f32 forms it, without the
+// quieting of signalling NaNs that fmaxf adds before each maximum: a NaN
+// value still reaches the sums, which report it.
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 template <int NT, int BATCH, bool kBatchCheck = true>
 __device__ __forceinline__ StreamPart stream_part_bf16(const uint16_t* rp, int V, int v0, int v1, bool tail, float T,
                                                        uint32_t* status, RowShared<NT>& sh) {
@@ -305,6 +314,7 @@ __device__ __forceinline__ StreamPart stream_part_bf16(const uint16_t* rp, int V
   // frame mc changes (exactly, in double) when m grows; the block frame is
   // M * c2 in double.
   float m = -INFINITY, mc = -INFINITY, mn = INFINITY;
+  u16x2 hw = {0, 0};  // largest raw halves of the full batches: -inf (0xFF80) and negative NaNs at or above it
   double s = 0.0;
   int bvi = -1;
   uint4 bv = {0, 0, 0, 0};
@@ -324,9 +334,9 @@ __device__ __forceinline__ StreamPart stream_part_bf16(const uint16_t* rp, int V
       bv = d;
     }
     if (sums) {
-      float acc = 0.0f;
+      float acc = __builtin_amdgcn_exp2f(fmaf(v[0], c2, -mc));
 #pragma unroll
-      for (int q = 0; q < 8; ++q) acc += __builtin_amdgcn_exp2f(fmaf(v[q], c2, -mc));
+      for (int q = 1; q < 8; ++q) acc += __builtin_amdgcn_exp2f(fmaf(v[q], c2, -mc));
       s += static_cast<double>(acc);
     }
   };
@@ -355,13 +365,15 @@ __device__ __forceinline__ StreamPart stream_part_bf16(const uint16_t* rp, int V
         float w[8];
         w[0] = bf16_lo(d.x); w[1] = bf16_hi(d.x); w[2] = bf16_lo(d.y); w[3] = bf16_hi(d.y);
         w[4] = bf16_lo(d.z); w[5] = bf16_hi(d.z); w[6] = bf16_lo(d.w); w[7] = bf16_hi(d.w);
-        vmx[k] = fmaxf(fmaxf(fmaxf(w[0], w[1]), fmaxf(w[2], w[3])), fmaxf(fmaxf(w[4], w[5]), fmaxf(w[6], w[7])));
-        mn = fminf(fminf(mn, fminf(w[0], w[1])), fminf(fminf(w[2], w[3]), fminf(w[4], w[5])));
-        mn = fminf(mn, fminf(w[6], w[7]));
+        vmx[k] = max3_raw(max3_raw(w[0], w[1], w[2]), max3_raw(w[3], w[4], w[5]), max3_raw(w[6], w[7], w[7]));
+        hw = __builtin_elementwise_max(
+            hw, __builtin_elementwise_max(
+                    __builtin_elementwise_max(__builtin_bit_cast(u16x2, d.x), __builtin_bit_cast(u16x2, d.y)),
+                    __builtin_elementwise_max(__builtin_bit_cast(u16x2, d.z), __builtin_bit_cast(u16x2, d.w))));
       }
       float bm = vmx[0];
 #pragma unroll
-      for (int k = 1; k < BATCH; ++k) bm = fmaxf(bm, vmx[k]);
+      for (int k = 1; k < BATCH; k += 2) bm = max3_raw(bm, vmx[k], vmx[k + 1 < BATCH ? k + 1 : k]);
       if (bm > m) {
         bool found = false;
 #pragma unroll
@@ -383,9 +395,9 @@ __device__ __forceinline__ StreamPart stream_part_bf16(const uint16_t* rp, int V
           float w[8];
           w[0] = bf16_lo(d.x); w[1] = bf16_hi(d.x); w[2] = bf16_lo(d.y); w[3] = bf16_hi(d.y);
           w[4] = bf16_lo(d.z); w[5] = bf16_hi(d.z); w[6] = bf16_lo(d.w); w[7] = bf16_hi(d.w);
-          float acc = 0.0f;
+          float acc = __builtin_amdgcn_exp2f(fmaf(w[0], c2, -mc));
 #pragma unroll
-          for (int q = 0; q < 8; ++q) acc += __builtin_amdgcn_exp2f(fmaf(w[q], c2, -mc));
+          for (int q = 1; q < 8; ++q) acc += __builtin_amdgcn_exp2f(fmaf(w[q], c2, -mc));
           s += static_cast<double>(acc);
         }
       }
@@ -426,7 +438,7 @@ __device__ __forceinline__ StreamPart stream_part_bf16(const uint16_t* rp, int V
       if (sums) s += static_cast<double>(__builtin_amdgcn_exp2f(fmaf(f, c2, -mc)));
     }
   }
-  if (mn == -INFINITY) raise_status(status, SV_ST_NONFINITE);
+  if (mn == -INFINITY || hw.x >= 0xFF80u || hw.y >= 0xFF80u) raise_status(status, SV_ST_NONFINITE);
   uint64_t packed =
       bidx >= 0 ? (static_cast<uint64_t>(mono_key(best)) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(bidx)) : 0;
   StreamPart out;

@@ -251,6 +251,88 @@ def test_dense_rows_edges(V):
     assert sv.sv_get_status(ws) == 0
 
 
+DENSE_SHAPES = [  # (V, b, L per request)
+    (8192, 4, [1, 4, 0]),            # short rows, one part each
+    (8200, 2, [0]),                  # one target row, no draft rows
+    (151936, 4, [0, 3]),             # full rows, few
+    (65536, 16, "random40"),         # ragged counts, many rows
+    (8192, 16, "full64"),            # every position verified
+]
+
+
+@pytest.mark.parametrize("V,b,Ls", DENSE_SHAPES,
+                         ids=[f"V{v}-b{b}-{l if isinstance(l, str) else len(l)}" for v, b, l in DENSE_SHAPES])
+def test_dense_rows_shapes(V, b, Ls):
+    """sv_verify_rows_dense without top-p over several row lengths and
+    request mixes: device-side row counts below the capacities, per-request
+    temperatures (0 included), the maximum repeated 1024 and 4096 vectors
+    apart and at the row end (across batches and parts); maximum and argmax
+    exactly, lse to 1e-5; two runs bit-equal; a non-finite value sets the
+    status bit."""
+    import torch
+
+    sv = _sv()
+    from draft_verification_sv_amd.step import row_pitch, to_device_rows
+
+    rng = np.random.default_rng(V * 31 + b)
+    if Ls == "random40":
+        L = rng.integers(0, b + 1, size=40)
+    elif Ls == "full64":
+        L = np.full(64, b)
+    else:
+        L = np.array(Ls)
+    R = len(L)
+    nt, nd = int((L + 1).sum()), int(L.sum())
+    tgt = (3.0 * rng.standard_normal((nt, V))).astype(np.float32)
+    dft = (2.0 * rng.standard_normal((R * b, V))).astype(np.float32)
+    for k in range(0, nt, 3):  # ties at the maximum, 1024 and 4096 vectors apart and at the row end
+        m = tgt[k].max() + 1.0
+        for i in (V // 5, V // 5 + 1024 * 8, V // 5 + 4096 * 8, V - 1):
+            tgt[k, i % V] = m
+    T = np.array([(0.0, 0.5, 1.0, 1.5)[r % 4] for r in range(R)], np.float32)
+    tb, db = synth.f32_to_bf16_bits(tgt), synth.f32_to_bf16_bits(dft)
+    ld = row_pitch(V, "bf16")
+    dt, dd = to_device_rows(tb, ld), to_device_rows(db, ld)
+    d = dict(device="cuda")
+    tgt_off = torch.from_numpy(np.concatenate([[0], np.cumsum(L + 1)]).astype(np.int32)).cuda()
+    pos_off = torch.from_numpy(np.concatenate([[0], np.cumsum(L)]).astype(np.int32)).cuda()
+    ws, nb = sv.make_workspace(R, b, 0, V)
+    f32, i32, f64 = torch.float32, torch.int32, torch.float64
+    cap_t, cap_d = R * (b + 1), R * b
+    runs = []
+    for rep in range(2):
+        ro = [torch.zeros(cap_t, dtype=x, **d) for x in (f32, i32, f64, f32, f64)]
+        do = [torch.zeros(cap_d, dtype=x, **d) for x in (f32, i32, f64)]
+        banner(f"sv_verify_rows_dense V={V} R={R} rows {nt}+{nd} run {rep}")
+        sv.sv_verify_rows_dense(dt, sv.SV_BF16, ld, V, tgt_off, R, cap_t, torch.from_numpy(T).cuda(), None, *ro, dd,
+                                sv.SV_BF16, ld, b, pos_off, cap_d, *do, ws, nb)
+        torch.cuda.synchronize()
+        runs.append([x.cpu().numpy() for x in ro[:3] + do[:3]])
+    for a, c in zip(runs[0], runs[1]):
+        assert a.tobytes() == c.tobytes()
+    mx, am, lse, dmx, dam, dlse = runs[0]
+    o = oracle.row_stats_batch(tb, np.repeat(np.arange(R), L + 1), T)
+    assert np.array_equal(mx[:nt], o["max"]) and np.array_equal(am[:nt], o["argmax"])
+    hot = np.repeat(T > 0, L + 1)
+    np.testing.assert_allclose(lse[:nt][hot], o["lse"][hot], rtol=1e-5, atol=1e-12)
+    drows = np.concatenate([np.arange(r * b, r * b + L[r]) for r in range(R)]).astype(np.int64)
+    o = oracle.row_stats_batch(db[drows], np.repeat(np.arange(R), L), T)
+    assert np.array_equal(dmx[:nd], o["max"]) and np.array_equal(dam[:nd], o["argmax"])
+    hot = np.repeat(T > 0, L)
+    np.testing.assert_allclose(dlse[:nd][hot], o["lse"][hot], rtol=1e-5, atol=1e-12)
+    assert sv.sv_get_status(ws) == 0
+    # a non-finite value in the last target row sets the status bit
+    for bad in (-np.inf, np.nan, np.inf):
+        t2 = tgt.copy()
+        t2[nt - 1, V // 2] = bad
+        d2 = to_device_rows(synth.f32_to_bf16_bits(t2), ld)
+        ws2, nb2 = sv.make_workspace(R, b, 0, V)
+        T2 = torch.ones(R, **d)
+        sv.sv_verify_rows_dense(d2, sv.SV_BF16, ld, V, tgt_off, R, cap_t, T2, None, *ro, dd, sv.SV_BF16, ld, b,
+                                pos_off, cap_d, *do, ws2, nb2)
+        assert sv.sv_get_status(ws2) & 0x004, bad
+
+
 def test_row_stats_nonfinite_sets_status():
     import torch
 
