@@ -259,10 +259,13 @@ struct TailShared {
 // a pass are packed one after another into one list (then one dummy slot per
 // lane), so that exp runs over the pass's kept values with no idle slots.  The
 // lists share the dynamic LDS with the mixture's branch tables, which are dead
-// by then.
+// by then.  Dense proposals keep one sub-chunk per pass (two lists of it, p
+// and q): 18 KiB of lists, so that six blocks fit on a compute unit and a
+// cfg3-sized grid (1216 blocks) is resident at once; two sub-chunks per pass
+// took 34 KiB, four blocks per compute unit and a second round of blocks.
 template <bool kDense>
 struct DLists {
-  static constexpr int kLists = (kDense ? 2 : 4) < kSubPerWave ? (kDense ? 2 : 4) : kSubPerWave;  // sub-chunks per pass
+  static constexpr int kLists = (kDense ? 1 : 4) < kSubPerWave ? (kDense ? 1 : 4) : kSubPerWave;  // sub-chunks per pass
   static constexpr int kCap = kLists * kSubG * 8;                        // values of a pass
   static constexpr int kPerWave = (kCap + kWave) * (kDense ? 2 : 1);     // floats
   static constexpr size_t kBytes = sizeof(float) * kPerWave * (kSumNT / kWave);
