@@ -21,7 +21,7 @@
 // and never admits a non-candidate.  Without block_len every key is shifted
 // alike and the result is unchanged.
 //
-// One block of 256 threads:
+// One block of kDvlNT = 512 threads:
 //   1. per request, the running products (written to s);
 //   2. radix select, 10 bits per pass from the top (three passes: selection
 //      keys are below 2^30), of the B-th largest score (score bits with -0
@@ -51,7 +51,7 @@ __device__ __forceinline__ uint32_t select_key(float v) { return min(score_key(v
 constexpr int kDigitBits = 10;            // three radix passes cover the 30 key bits
 constexpr int kBins = 1 << kDigitBits;
 
-constexpr int kDvlNT = 256;
+constexpr int kDvlNT = 512;  // 8 waves: 5.5 us a call at R = 32, b = 16 against 6.0 (256), 7.2 (128), 6.4 (1024)
 constexpr int kDvlLds = 8192;  // scores kept in LDS up to this many positions
 
 // b_r of request r: block_len[r] clamped to [0, b] (b without block_len)
