@@ -34,7 +34,7 @@ EXPORTS = [
     "sv_workspace_bytes", "sv_workspace_init", "sv_get_status", "sv_clear_status", "sv_status_string",
     "dvl_alloc_pack", "sv_softmax_stats", "sv_topp_threshold", "sv_mixture_q", "sv_accept",
     "sv_residual_sample", "sv_philox_uniforms", "sv_verify_rows", "sv_verify_rows_dense", "sv_accept_sample",
-    "sv_selftest_exp",
+    "sv_selftest_exp", "sv_selftest_philox_host", "sv_selftest_rows_host",
 ]
 
 
@@ -244,6 +244,14 @@ def sv_philox_uniforms(seed, R, n_pos, out, stream=None):
     _check(_lib.sv_philox_uniforms(_p(seed), R, n_pos, _p(out), _stream(stream)), "sv_philox_uniforms")
 
 
+def sv_selftest_philox_host() -> int:
+    return int(_lib.sv_selftest_philox_host())
+
+
+def sv_selftest_rows_host() -> int:
+    return int(_lib.sv_selftest_rows_host())
+
+
 def selftest_host() -> dict:
     """Host-side checks compiled into the library (no GPU needed)."""
-    return {"rows": int(_lib.sv_selftest_rows_host()), "philox": int(_lib.sv_selftest_philox_host())}
+    return {"rows": sv_selftest_rows_host(), "philox": sv_selftest_philox_host()}

@@ -1,21 +1,21 @@
 // sv_dvl.hip -- dynamic verify-length (DVL) allocation and packing.
 //
 // "DScale: Scaling Block-Diffusion Speculative Decoding with Adaptive
-// Verification", abstract: DVL packs scored prefixes into half the native
-// verification capacity, and fixed-address workspaces carry the changing
-// boundaries through verification and acceptance.  The score of a prefix is
-// its survival probability (the DSpark summary on "Why does throughput
-// collapse under high concurrency?": verification length from prefix survival
-// probabilities): s_{r,i} = a_{r,1} * ... * a_{r,i}, one float rounding per
+// Verification", abstract: a budget of verification slots -- half of what the
+// engine could verify at full length -- goes to the draft prefixes with the
+// best scores, and the per-request lengths reach the verification kernels
+// through buffers at fixed addresses.  A prefix is scored by the probability
+// that it survives verification (wispaper Q&A on block-diffusion decode
+// failures, section "Why does throughput collapse under high concurrency?",
+// on DSpark): s_{r,i} = a_{r,1} * ... * a_{r,i}, one float rounding per
 // product.  The allocation keeps the B highest scores in the order (s desc, r
 // asc, i asc); with a <= 1 the scores fall along each request, so the choice is
 // prefix-closed and maximises the summed survival (expected accepted length).
 //
-// Per-request block length ("Why does throughput collapse under high
-// concurrency?", section "How does draft quality decay with block length and
-// sampling temperature?": BlockPilot finds the best block size varies per
-// request): with block_len, request r drafted only its
-// first b_r positions; the others are not candidates and get s = 0.  The
+// Per-request block length (wispaper Q&A on block-diffusion decode failures,
+// section "Why is a fixed block size a failure mode in production?": BlockPilot
+// finds the best block size varies per request): with block_len, request r
+// drafted only its first b_r positions; the others are not candidates and get s = 0.  The
 // selection key of a candidate is its score key + 1 and that of any other
 // position 0, and the budget is capped at sum_r b_r, so the threshold is >= 1
 // and never admits a non-candidate.  Without block_len every key is shifted

@@ -2,10 +2,11 @@
 // posterior.
 //
 // "Pith review of DBLAST", "What carries the argument": the block proposal is
-// q_dep(x_1:b | y) = sum_z q(z|y) prod_i q_i(x_i | y, z); at inference a
-// category is sampled and its branch decoded greedily, and verification
-// conditions on the accepted prefix through the category posterior (the
-// greedy-branch conditional, Eq. (20) per the Referee report, minor 5).  With
+// q_dep(x_1:b | y) = sum_z q(z|y) prod_i q_i(x_i | y, z).  The drafter draws
+// one category and emits that branch's argmax tokens; the verifier scores each
+// position under the mixture whose category weights have been updated by the
+// draft prefix (the greedy-branch conditional, Eq. (20) per the Referee
+// report, minor 5).  With
 // point-mass branches at g_i(z) = argmax_v c_{r,z,i,v}, the posterior before
 // position i keeps the categories whose branch agrees with the draft prefix:
 //   w_z = q(z|y) [g_j(z) = x_j, j < i] / sum over z of the same,

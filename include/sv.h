@@ -5,20 +5,25 @@
  * Pages the operations come from (cited by title and section):
  *  [DScale]  "DScale: Scaling Block-Diffusion Speculative Decoding with
  *            Adaptive Verification" -- abstract: dynamic verify-length (DVL)
- *            allocation packs scored prefixes into half the native
- *            verification capacity; fixed-address workspaces carry changing
- *            boundaries through verification and acceptance.
+ *            allocation gives a verification budget of half the full-length
+ *            capacity to the best-scored draft prefixes; per-step lengths
+ *            reach verification and acceptance through buffers at fixed
+ *            addresses.
  *  [DBLast]  "Pith review of DBLAST: Dependent Block Drafting for Stochastic
  *            Speculative Decoding" -- "What carries the argument" (latent
  *            mixture q_dep and the category posterior along the accepted
- *            prefix), "Assumptions & free parameters" (speculative sampling
- *            with rejection correction preserves the target distribution),
+ *            prefix), "Assumptions & free parameters" (the rejection-
+ *            corrected sampler emits tokens distributed as the target),
  *            "What would settle it" (target sampling at temperature 1.5 with
  *            top-p 0.95), Referee report minor 5 (Eq. (20), the greedy-branch
  *            conditional), reference graph [1], [2] (speculative sampling),
  *            [18] (nucleus sampling).
- *  [wispaper] "Why does throughput collapse under high concurrency?" --
- *            verification length tailored from prefix survival probabilities.
+ *  [wispaper] wispaper Q&A on block-diffusion decode failures -- section
+ *            "Why does throughput collapse under high concurrency?" (DSpark
+ *            sets each request's verification length from the chance that
+ *            its draft prefixes survive); section "Why is a fixed block size
+ *            a failure mode in production?" (BlockPilot: block size per
+ *            request).
  *
  * Conventions shared by every call
  *  - All array arguments are DEVICE pointers unless marked "host".  The caller
@@ -111,9 +116,9 @@ const char* sv_status_string(int32_t code);
  *   a[R*b]      per-position acceptance estimates in [0, 1] (float)
  *   block_len[R]  optional (NULL: b for every request): request r drafted
  *               only its first b_r positions (0 <= b_r <= b; others clamped,
- *               SV_ST_BAD_BLOCK) [wispaper, section "How does draft quality
- *               decay with block length and sampling temperature?": BlockPilot's
- *               block size varies per request]; positions i >= b_r are never
+ *               SV_ST_BAD_BLOCK) [wispaper, section "Why is a fixed block
+ *               size a failure mode in production?": BlockPilot's block size
+ *               varies per request]; positions i >= b_r are never
  *               chosen and their estimates are ignored (not checked)
  *   budget      device int32 scalar: verification slots B (>= 0)
  *   s[R*b]      out: survival scores s_{r,i} = fl32(s_{r,i-1} * a_{r,i}),
@@ -337,6 +342,15 @@ int32_t sv_philox_uniforms(const uint64_t* seed, int32_t R, int32_t n_pos, uint3
  * exponential (the one its probability and draw-weight kernels use; Tang's
  * method, ACM TOMS 1989), for checking its error against the host's exp. */
 int32_t sv_selftest_exp(const double* x, double* out, int32_t n, void* stream);
+
+/* Host-only self-checks of code compiled into the library (no GPU needed).
+ * sv_selftest_philox_host: the library's Philox4x32-10 round function against
+ * the Random123 known-answer vectors (Salmon et al., SC'11).
+ * sv_selftest_rows_host: the bf16 value <-> histogram-bin maps and the
+ * order-preserving 32-bit float key used by the top-p cut.
+ * Each returns 0 on success, else the number of the first failed check. */
+int32_t sv_selftest_philox_host(void);
+int32_t sv_selftest_rows_host(void);
 
 #ifdef __cplusplus
 }

@@ -19,6 +19,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "sv_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# A test may point this package at another build of the oracle (a copy with a
+# planted mistake, to show that the pins catch it); it is never built here.
+_LIB_OVERRIDE = os.environ.get("SV_ORACLE_LIB")
 
 F32 = 0
 BF16 = 1
@@ -26,13 +29,15 @@ Q_DENSE = 0
 Q_MIXTURE = 1
 
 
+def compile_command(src: str, out: str) -> list:
+    return ["gcc", "-O2", "-std=c11", "-Wall", "-fopenmp", "-fPIC", "-shared", "-o", out, src, "-lm"]
+
+
 def build(force: bool = True) -> str:
     """Compile liboracle.so with gcc -O2 -fopenmp (IEEE double, no fast-math)."""
     if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp"
-        subprocess.check_call(
-            ["gcc", "-O2", "-std=c11", "-Wall", "-fopenmp", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"]
-        )
+        subprocess.check_call(compile_command(_SRC, tmp))
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
 
@@ -42,6 +47,9 @@ _lib = None
 
 def lib():
     global _lib
+    if _lib is None and _LIB_OVERRIDE:
+        _lib = C.CDLL(_LIB_OVERRIDE)
+        _declare(_lib)
     if _lib is None:
         if not os.path.exists(_LIB_PATH):
             build(force=True)

@@ -94,9 +94,9 @@ static const void* orc_row(const void* base, int32_t dtype, int64_t row, int64_t
 }
 
 /* ------------------------------------------------------------------------ */
-/* DVL allocation [DScale abstract: "packs scored prefixes into half the     */
-/* native verification capacity"; wispaper: verification length from prefix  */
-/* survival probabilities].                                                  */
+/* DVL allocation [DScale abstract: a verification budget of half the       */
+/* full-length capacity goes to the best-scored draft prefixes; wispaper:    */
+/* prefixes are scored by how likely they are to survive verification].      */
 /* Reading: the score of a prefix of length i is its survival probability    */
 /* s_i = a_1 * ... * a_i (products rounded to float one at a time); the      */
 /* allocation maximises the summed score of the verified positions under the  */
@@ -119,10 +119,10 @@ static int orc_dvl_cmp(const void* pa, const void* pb) {
   return 0;
 }
 
-/* Per-request block length ["Why does throughput collapse under high         */
-/* concurrency?", section "How does draft quality decay with block length and */
-/* sampling temperature?": BlockPilot finds the best block size varies from   */
-/* request to request]: request r drafts b_r <= b                             */
+/* Per-request block length [wispaper Q&A on block-diffusion decode failures, */
+/* section "Why is a fixed block size a failure mode in production?":         */
+/* BlockPilot finds the best block size varies from request to request]:     */
+/* request r drafts b_r <= b                                                  */
 /* positions; positions i >= b_r were not drafted, are never candidates and   */
 /* get score 0.  block_len NULL: b_r = b.  Returns 2 if some b_r lies outside */
 /* [0, b] (nothing written).                                                  */

@@ -9,26 +9,29 @@
  * Sources (web pages on the subject; cited by title and section):
  *  [DScale]  "DScale: Scaling Block-Diffusion Speculative Decoding with
  *            Adaptive Verification", abstract (aiqbench.com / arxivdaily.com):
- *            dynamic verify-length (DVL) allocation of scored prefixes into
- *            half the native verification capacity; fixed-address workspaces.
+ *            dynamic verify-length (DVL) allocation of a budget of half the
+ *            full-length verification capacity to the best-scored prefixes;
+ *            buffers at fixed addresses for the per-step lengths.
  *  [DBLast]  "Pith review of DBLAST: Dependent Block Drafting for Stochastic
  *            Speculative Decoding" (pith.science):
  *              - "What carries the argument": latent-mixture proposal
- *                q_dep(x_1:b|y) = sum_z q(z|y) prod_i q_i(x_i|y,z); a category
- *                is sampled, its branch decoded greedily, and verification
- *                conditions on the accepted prefix through the category
- *                posterior.
- *              - "Assumptions & free parameters": speculative sampling with
- *                rejection correction keeps the target distribution for any
- *                proposal q.
+ *                q_dep(x_1:b|y) = sum_z q(z|y) prod_i q_i(x_i|y,z); the
+ *                drafter draws one category and emits that branch's argmax
+ *                tokens, and the verifier weighs the categories by how well
+ *                they explain the draft prefix (the category posterior).
+ *              - "Assumptions & free parameters": whatever the proposal q,
+ *                the rejection-corrected sampler emits target-distributed
+ *                tokens.
  *              - "What would settle it": target sampling at T = 1.5, top-p 0.95.
  *              - Referee report, minor comment 5: experiments use the
  *                conditional of Eq. (20) (greedy-branch proposal).
  *              - Reference graph [1], [2]: Leviathan et al., Chen et al.
  *                (speculative sampling); [18]: nucleus (top-p) sampling.
- *  [wispaper] "Why does throughput collapse under high concurrency?"
- *            (wispaper.ai Q&A): verification length tailored from prefix
- *            survival probabilities (DSpark summary).
+ *  [wispaper] wispaper.ai Q&A on block-diffusion decode failures, section
+ *            "Why does throughput collapse under high concurrency?" (DSpark
+ *            sets verification length from how likely each draft prefix is
+ *            to survive) and section "Why is a fixed block size a failure
+ *            mode in production?" (BlockPilot: block size per request).
  *  [Philox]  Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as
  *            1, 2, 3", SC'11 -- Philox4x32-10 (outside the pages; the pages
  *            name no generator, the counter-based choice is the build's).

@@ -356,9 +356,10 @@ def _brute_dvl(s, B):
 
 
 def test_dvl_brute_force_optimum():
-    """DScale abstract: DVL packs scored prefixes into a budget; with survival
-    scores s_i = prod_{j<=i} a_j the allocation maximises the expected number
-    of accepted positions; checked against exhaustive search."""
+    """DScale abstract: DVL spends a budget of verification slots on the
+    best-scored prefixes; with survival scores s_i = prod_{j<=i} a_j the
+    allocation maximises the expected number of accepted positions; checked
+    against exhaustive search."""
     rng = np.random.default_rng(41)
     for trial in range(120):
         R, b = int(rng.integers(1, 5)), int(rng.integers(1, 5))
@@ -395,10 +396,11 @@ def _brute_dvl_ragged(s, bl, B):
 
 
 def test_dvl_ragged_block_lengths_brute_force():
-    """Per-request block length ("Why does throughput collapse under high
-    concurrency?", section "How does draft quality decay with block length and
-    sampling temperature?": BlockPilot's block size varies per request): request r drafted b_r positions; the allocation
-    over its prefixes of length <= b_r is checked against exhaustive search."""
+    """Per-request block length (wispaper Q&A on block-diffusion decode
+    failures, section "Why is a fixed block size a failure mode in production?":
+    BlockPilot's block size varies per request): request r drafted b_r
+    positions; the allocation over its prefixes of length <= b_r is checked
+    against exhaustive search."""
     rng = np.random.default_rng(43)
     for trial in range(150):
         R, b = int(rng.integers(1, 5)), int(rng.integers(1, 6))
@@ -448,3 +450,117 @@ def test_dvl_special_cases():
     bad = a.copy()
     bad[1, 3] = 1.5
     assert oracle.dvl(bad, 10)["bad"] == 1
+
+
+# ---------------------------------------------------------------- decision margins
+# The margins decide which GPU/oracle disagreements may be excused, so each is
+# pinned on inputs whose probabilities are known in closed form.  Rows are
+# built from logits 0 and ln k, so that softmax gives simple fractions; fp32
+# rounding of ln k moves them by ~1e-8, far inside the 1e-9 + 1e-6 tolerances
+# below and far below the O(0.1) change any plausible mistake makes.
+#   accept: |u - min(1, p/q)|                    (q = 0: as if p/q were +inf, or 0 when p = 0 too)
+#   draw:   distance of u*W to the ends of the chosen token's CDF interval, / W
+#   top-p:  min(|C_{>cut} - top_p|, |C_{>=cut} - top_p|)
+# (DBLast review, "Assumptions & free parameters": rejection correction keeps
+# the target distribution, so a decision that sits within a tiny margin of its
+# threshold is the only place two exact implementations may part.)
+MTOL = 1e-6
+
+
+def _ln(k):
+    return np.float32(np.log(k))
+
+
+def _margin_workload(R=256):
+    """b = 1, V = 4: target row 1 uniform (p = 1/4 each), bonus row with
+    logits (0, 0, ln 2, 0) (p = 1/5, 1/5, 2/5, 1/5); the draft row (0, 0, 0,
+    ln 3) gives q = 1/6, 1/6, 1/6, 1/2.  Even requests draft token 3 (rho =
+    1/2), odd ones token 0 (rho = 3/2)."""
+    tgt = np.array([[0, 0, 0, 0], [0, 0, _ln(2), 0]], np.float32)
+    draft = np.array([[0, 0, 0, _ln(3)]], np.float32)
+    x = np.where(np.arange(R) % 2 == 0, 3, 0).astype(np.int32)[:, None]
+    return tgt, draft, x
+
+
+def test_accept_margin_closed_form():
+    R = 256
+    tgt, draft, x = _margin_workload(R)
+    out = oracle.step(tgt=tgt, tgt_row0=np.zeros(R, np.int64), L=np.ones(R, np.int32), T=np.ones(R, np.float32),
+                      x=x, seed=20240611, draft=draft, draft_row0=np.zeros(R, np.int64))
+    u = out["u_acc"][:, 0]
+    even = np.arange(R) % 2 == 0
+    np.testing.assert_allclose(out["p_x"][:, 0], 0.25, atol=1e-9)
+    np.testing.assert_allclose(out["q_x"][:, 0], np.where(even, 0.5, 1 / 6), atol=1e-8)
+    # rho = 1/2 (token 3) and rho = 3/2 (token 0, capped at 1 by min(1, .))
+    want = np.where(even, np.abs(u - 0.5), 1.0 - u)
+    np.testing.assert_allclose(out["acc_margin"][:, 0], want, atol=MTOL)
+    # the decision sits on the side of the threshold the margin measures from
+    assert np.array_equal(out["n_acc"] == 1, np.where(even, u < 0.5, True))
+    assert (out["acc_margin"][:, 0] > 0).all()
+
+
+def test_accept_margin_zero_q_and_point_masses():
+    """T = 0: p and q are one-hot at the target and draft argmax, so the
+    ratio is 1 (both hit), +inf (q = 0 < p), 0 (p = 0 < q) or undefined (both
+    0, rejected): margins 1 - u, 1 - u, u, u."""
+    R = 64
+    tgt = np.array([[0, 5, 0, 0], [1, 0, 0, 0]], np.float32)   # target argmax 1
+    draft = np.array([[0, 5, 0, 0], [0, 0, 5, 0]], np.float32)  # draft argmax 1 in row 0, 2 in row 1
+    kind = np.arange(R) % 4
+    # kind 0: x = 1 from row 0 (p = q = 1); 1: x = 1 from row 1 (p = 1, q = 0);
+    #      2: x = 2 from row 1 (p = 0, q = 1); 3: x = 3 from row 0 (p = q = 0)
+    x = np.array([1, 1, 2, 3], np.int32)[kind][:, None]
+    drow = np.array([0, 1, 1, 0])[kind]
+    out = oracle.step(tgt=tgt, tgt_row0=np.zeros(R, np.int64), L=np.ones(R, np.int32), T=np.zeros(R, np.float32),
+                      x=x, seed=77, draft=draft, draft_row0=drow.astype(np.int64))
+    u = out["u_acc"][:, 0]
+    want = np.where(kind <= 1, 1.0 - u, u)
+    np.testing.assert_allclose(out["acc_margin"][:, 0], want, atol=1e-15)
+    assert np.array_equal(out["n_acc"], (kind <= 1).astype(np.int32))
+
+
+def test_draw_margin_closed_form():
+    """Residual at position 1 (rejected token 3): weights max(0, p - q) =
+    (1/12, 1/12, 1/12, 0), W = 1/4, so with t = 3u the token is floor(t) and
+    the margin min(frac(t), 1 - frac(t)) / 3.  Bonus from (1/5, 1/5, 2/5, 1/5)
+    (W = 1): cumulative (1/5, 2/5, 4/5, 1)."""
+    R = 512
+    tgt, draft, x = _margin_workload(R)
+    x[:] = 3
+    out = oracle.step(tgt=tgt, tgt_row0=np.zeros(R, np.int64), L=np.ones(R, np.int32), T=np.ones(R, np.float32),
+                      x=x, seed=4242, draft=draft, draft_row0=np.zeros(R, np.int64))
+    u = out["u_res"]
+    rej = out["n_acc"] == 0
+    assert 100 < rej.sum() < R - 100
+    t = 3.0 * u[rej]
+    np.testing.assert_array_equal(out["token"][rej], np.floor(t).astype(np.int32))
+    fr = t - np.floor(t)
+    np.testing.assert_allclose(out["sample_margin"][rej], np.minimum(fr, 1.0 - fr) / 3.0, atol=MTOL)
+    cum = np.array([0.0, 0.2, 0.4, 0.8, 1.0])
+    ub = u[~rej]
+    tok = np.searchsorted(cum, ub, side="right") - 1
+    np.testing.assert_array_equal(out["token"][~rej], tok)
+    np.testing.assert_allclose(out["sample_margin"][~rej], np.minimum(ub - cum[tok], cum[tok + 1] - ub), atol=MTOL)
+
+
+def test_topp_margin_two_level_closed_form():
+    """n1 tokens at a above n2 at c: the top level holds mass M1.  A top_p
+    below M1 cuts at a (C_> = 0, C_>= = M1); above it, at c (C_> = M1,
+    C_>= = 1)."""
+    n1, n2, a, c, T = 3, 997, 2.0, -1.0, 1.0
+    row = np.full(n1 + n2, c, np.float32)
+    row[[5, 400, 999]] = a
+    M1 = n1 * np.exp(a / T) / (n1 * np.exp(a / T) + n2 * np.exp(c / T))
+    tp = 0.8 * M1                         # nearer to M1 than to 0
+    st = oracle.row_stats(row, T, tp)
+    assert st["cut"] == a
+    assert st["margin"] == pytest.approx(0.2 * M1, abs=1e-12)
+    tp = M1 + 0.3 * (1 - M1)              # nearer to M1 than to 1
+    st = oracle.row_stats(row, T, tp)
+    assert st["cut"] == c
+    assert st["margin"] == pytest.approx(0.3 * (1 - M1), abs=1e-12)
+    tp = M1 + 0.9 * (1 - M1)              # nearer to 1
+    st = oracle.row_stats(row, T, tp)
+    assert st["margin"] == pytest.approx(0.1 * (1 - M1), abs=1e-12)
+    assert oracle.row_stats(row, T, 1.0)["margin"] == np.inf
+    assert oracle.row_stats(row, 0.0, 0.5)["margin"] == np.inf
