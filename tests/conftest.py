@@ -14,3 +14,16 @@ def pytest_configure(config):
 
 def pytest_report_header(config):
     return "draft_verification_sv_amd test-suite"
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    """Counts of the long parity runs (positions compared and disagreements
+    excused by a low oracle margin), shown whatever the verbosity."""
+    try:
+        from harness import PARITY_LOG
+    except ImportError:
+        return
+    if PARITY_LOG:
+        terminalreporter.section("parity against the oracle")
+        for line in PARITY_LOG:
+            terminalreporter.write_line(line)
