@@ -23,6 +23,8 @@ SV_OK = 0
 SV_ERR_ARG = 1
 SV_ERR_WORKSPACE = 2
 SV_ERR_LAUNCH = 3
+SV_ERR_TOO_LARGE = 4
+SV_NOALLOC_SCRATCH_BYTES = 1 << 20
 
 STATUS_BITS = {
     0x001: "BAD_TEMPERATURE", 0x002: "BAD_TOP_P", 0x004: "NONFINITE", 0x008: "BAD_SCORE",
@@ -34,7 +36,7 @@ EXPORTS = [
     "sv_workspace_bytes", "sv_workspace_init", "sv_get_status", "sv_clear_status", "sv_status_string",
     "dvl_alloc_pack", "sv_softmax_stats", "sv_topp_threshold", "sv_mixture_q", "sv_accept",
     "sv_residual_sample", "sv_philox_uniforms", "sv_verify_rows", "sv_verify_rows_dense", "sv_accept_sample",
-    "sv_selftest_exp", "sv_selftest_philox_host", "sv_selftest_rows_host",
+    "sv_selftest_exp", "sv_selftest_philox_host", "sv_selftest_rows_host", "sv_residual_sample_noalloc",
 ]
 
 
@@ -72,6 +74,8 @@ _SIGS = {
                   _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "sv_residual_sample": [_vp, _i32, _i64, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i64,
                            _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+    "sv_residual_sample_noalloc": [_vp, _i32, _i64, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _vp,
+                                   _i32, _i64, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "sv_philox_uniforms": [_vp, _i32, _i32, _vp, _vp],
     "sv_selftest_exp": [_vp, _vp, _i32, _vp],
     "sv_verify_rows_dense": [_vp, _i32, _i64, _i32, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
@@ -115,7 +119,9 @@ def _stream(stream):
 
 def _check(rc: int, name: str):
     if rc != SV_OK:
-        raise SvError(f"{name}: {_lib.sv_status_string(rc).decode()} (code {rc})")
+        err = SvError(f"{name}: {_lib.sv_status_string(rc).decode()} (code {rc})")
+        err.code = rc
+        raise err
 
 
 def sv_status_string(code: int) -> str:
@@ -234,6 +240,16 @@ def sv_residual_sample(tgt_logits, dtype, tgt_ld, V, tgt_off, pos_off, R, b, tem
                                    _p(draft_logits), draft_dtype, draft_ld, _p(draft_argmax), _p(draft_lse), K,
                                    _p(branch_tok), _p(post_w), _p(seed), _p(n_acc), _p(token), _p(is_bonus), _p(ws),
                                    ws_bytes, _stream(stream)), "sv_residual_sample")
+
+
+def sv_residual_sample_noalloc(tgt_logits, dtype, tgt_ld, V, tgt_off, pos_off, R, b, temperature, row_argmax,
+                               row_cut, row_kept_lse, q_mode, draft_logits, draft_dtype, draft_ld, draft_argmax,
+                               draft_lse, K, branch_tok, post_w, seed, n_acc, token, is_bonus, status, stream=None):
+    _check(_lib.sv_residual_sample_noalloc(_p(tgt_logits), dtype, tgt_ld, V, _p(tgt_off), _p(pos_off), R, b,
+                                           _p(temperature), _p(row_argmax), _p(row_cut), _p(row_kept_lse), q_mode,
+                                           _p(draft_logits), draft_dtype, draft_ld, _p(draft_argmax), _p(draft_lse),
+                                           K, _p(branch_tok), _p(post_w), _p(seed), _p(n_acc), _p(token),
+                                           _p(is_bonus), _p(status), _stream(stream)), "sv_residual_sample_noalloc")
 
 
 def sv_selftest_exp(x, out, n, stream=None):

@@ -75,6 +75,8 @@ extern "C" const char* sv_status_string(int32_t code) {
     case SV_ERR_ARG: return "invalid argument (null pointer, size out of range, misalignment, dtype or mode)";
     case SV_ERR_WORKSPACE: return "workspace too small";
     case SV_ERR_LAUNCH: return "HIP launch or copy failed";
+    case SV_ERR_TOO_LARGE:
+      return "problem too large for the fixed scratch of the allocation-free entry point (SV_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status code";
   }
 }

@@ -30,6 +30,8 @@
 // and scans them.
 #include <math.h>
 
+#include <mutex>
+
 #include "sv_device.hpp"
 #include "sv_host.hpp"
 
@@ -1478,6 +1480,65 @@ extern "C" int32_t sv_residual_sample(const void* tgt_logits, int32_t dtype, int
   SampleArgs a = sample_args(tgt_logits, dtype, tgt_ld, V, tgt_off, pos_off, R, b, temperature, row_argmax, row_cut,
                              row_kept_lse, q_mode, draft_logits, draft_dtype, draft_ld, draft_argmax, draft_lse, seed,
                              ws);
+  a.K = q_mode == SV_Q_MIXTURE ? K : 0; a.branch_tok = branch_tok; a.post_w = const_cast<double*>(post_w);
+  a.n_acc_in = n_acc; a.token = token; a.is_bonus = is_bonus;
+  return launch_draw<false>(a, static_cast<hipStream_t>(stream));
+}
+
+// ------------------------------------------------------------------ allocation-free draw
+// sv_residual_sample_noalloc keeps the draw records and sub-chunk sums in this
+// file-scope array instead of a caller workspace.  Host code never passes the
+// array's name to a kernel: its device address is looked up once per device
+// (hipGetSymbolAddress, with that device current) and kept in g_scratch_dev.
+// Nothing in it must start at zero: every call rewrites each record it uses and
+// every sub-chunk sum its pick reads.  Calls that overlap on one GPU share it
+// and race.
+static __device__ __align__(256) unsigned char scratch[SV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (nullptr on failure).
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_dev[dev] = ptr;
+  }
+  return g_scratch_dev[dev];
+}
+}  // namespace
+
+extern "C" int32_t sv_residual_sample_noalloc(const void* tgt_logits, int32_t dtype, int64_t tgt_ld, int32_t V,
+                                              const int32_t* tgt_off, const int32_t* pos_off, int32_t R, int32_t b,
+                                              const float* temperature, const int32_t* row_argmax,
+                                              const float* row_cut, const double* row_kept_lse, int32_t q_mode,
+                                              const void* draft_logits, int32_t draft_dtype, int64_t draft_ld,
+                                              const int32_t* draft_argmax, const double* draft_lse, int32_t K,
+                                              const int32_t* branch_tok, const double* post_w, const uint64_t* seed,
+                                              const int32_t* n_acc, int32_t* token, int32_t* is_bonus,
+                                              uint32_t* status, void* stream) {
+  if (!sample_args_ok(tgt_logits, dtype, tgt_ld, V, tgt_off, pos_off, R, b, temperature, row_argmax, row_cut,
+                      row_kept_lse, q_mode, draft_logits, draft_dtype, draft_ld, draft_argmax, draft_lse, seed, status))
+    return SV_ERR_ARG;
+  if (!n_acc || !token || !is_bonus) return SV_ERR_ARG;
+  if (q_mode == SV_Q_MIXTURE && (K < 1 || K > 64 || !branch_tok || !post_w)) return SV_ERR_ARG;
+  const size_t rec_bytes = align256(sizeof(DrawRec) * static_cast<size_t>(R));
+  const size_t sub_bytes = sizeof(double) * 2 * static_cast<size_t>(R) * static_cast<size_t>(sub_chunks(V));
+  if (rec_bytes + sub_bytes > SV_NOALLOC_SCRATCH_BYTES) return SV_ERR_TOO_LARGE;
+  void* ptr = scratch_on_current_device();
+  if (!ptr) return SV_ERR_LAUNCH;
+  SampleArgs a = sample_args(tgt_logits, dtype, tgt_ld, V, tgt_off, pos_off, R, b, temperature, row_argmax, row_cut,
+                             row_kept_lse, q_mode, draft_logits, draft_dtype, draft_ld, draft_argmax, draft_lse, seed,
+                             ptr);
+  a.status = status;
+  a.rec = reinterpret_cast<DrawRec*>(ptr);
+  a.sub = reinterpret_cast<double*>(static_cast<char*>(ptr) + rec_bytes);
   a.K = q_mode == SV_Q_MIXTURE ? K : 0; a.branch_tok = branch_tok; a.post_w = const_cast<double*>(post_w);
   a.n_acc_in = n_acc; a.token = token; a.is_bonus = is_bonus;
   return launch_draw<false>(a, static_cast<hipStream_t>(stream));

@@ -78,6 +78,7 @@ extern "C" {
 #define SV_ERR_ARG 1       /* null pointer, size out of range, misalignment, unknown dtype/mode */
 #define SV_ERR_WORKSPACE 2 /* workspace smaller than sv_workspace_bytes() asks for */
 #define SV_ERR_LAUNCH 3    /* the HIP runtime refused a launch or copy */
+#define SV_ERR_TOO_LARGE 4 /* problem exceeds SV_NOALLOC_SCRATCH_BYTES (allocation-free entry point) */
 
 /* device status bits (sticky; OR-ed by the kernels) */
 #define SV_ST_BAD_TEMPERATURE 0x001u /* T_r < 0 or NaN */
@@ -296,6 +297,34 @@ int32_t sv_residual_sample(const void* tgt_logits, int32_t dtype, int64_t tgt_ld
                            const int32_t* branch_tok, const double* post_w, const uint64_t* seed,
                            const int32_t* n_acc, int32_t* token, int32_t* is_bonus, void* ws,
                            size_t ws_bytes, void* stream);
+
+/* sv_residual_sample_noalloc: sv_residual_sample for callers that cannot
+ * allocate device memory or hand the library a workspace (code under HIP graph
+ * capture that must not touch the allocator, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments, kernels and results as
+ * sv_residual_sample, except that the workspace is replaced by
+ *   status      device uint32: the status bits (SV_ST_*) are OR-ed into it
+ *               (the caller clears it; it is never reset here)
+ * and that the draw records and sub-chunk sums live in a library-owned,
+ * fixed-size device array of SV_NOALLOC_SCRATCH_BYTES, one copy per GPU,
+ * held until the process ends.  A call needs
+ *   round_up_256(1360 * R) + 16 * R * ceil(ceil(V / 8) / 64)  bytes
+ * of it (e.g. R <= 128 at V = 151936, R <= 64 at V = 262144); larger problems
+ * return SV_ERR_TOO_LARGE before any launch.  The call allocates nothing (no
+ * hipMalloc, hipFree or allocating library routine); its first call on a
+ * device looks up that device's copy of the array, so make the stream's
+ * device current.  Calls that overlap on one GPU (other streams, other host
+ * threads) share the array and race: serialise them. */
+#define SV_NOALLOC_SCRATCH_BYTES (1u << 20)
+int32_t sv_residual_sample_noalloc(const void* tgt_logits, int32_t dtype, int64_t tgt_ld, int32_t V,
+                                   const int32_t* tgt_off, const int32_t* pos_off, int32_t R, int32_t b,
+                                   const float* temperature, const int32_t* row_argmax,
+                                   const float* row_cut, const double* row_kept_lse, int32_t q_mode,
+                                   const void* draft_logits, int32_t draft_dtype, int64_t draft_ld,
+                                   const int32_t* draft_argmax, const double* draft_lse, int32_t K,
+                                   const int32_t* branch_tok, const double* post_w, const uint64_t* seed,
+                                   const int32_t* n_acc, int32_t* token, int32_t* is_bonus,
+                                   uint32_t* status, void* stream);
 
 /* sv_accept_sample: the rest of a step in two launches -- for SV_Q_MIXTURE the
  * branch argmax (merged from the parts sv_verify_rows left in the workspace;
