@@ -74,12 +74,47 @@ __device__ __forceinline__ float vec_max(const uint4& d) {
   }
 }
 
+// Largest magnitude field of a vector's values (sign bits cleared), per 16-bit
+// half for bf16 (two halves) and per word for fp32: a value is +-inf or NaN iff
+// its magnitude reaches the all-ones exponent (0x7F80 / 0x7F800000).
+template <int DT>
+__device__ __forceinline__ uint32_t vec_mag(const uint4& d) {
+  if constexpr (DT == SV_BF16) {
+    constexpr uint32_t m = 0x7FFF7FFFu;
+    return __builtin_bit_cast(
+        uint32_t, __builtin_elementwise_max(
+                      __builtin_elementwise_max(__builtin_bit_cast(u16x2, d.x & m), __builtin_bit_cast(u16x2, d.y & m)),
+                      __builtin_elementwise_max(__builtin_bit_cast(u16x2, d.z & m), __builtin_bit_cast(u16x2, d.w & m))));
+  } else {
+    constexpr uint32_t m = 0x7FFFFFFFu;
+    return max(max(d.x & m, d.y & m), max(d.z & m, d.w & m));
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ uint32_t mag_max(uint32_t a, uint32_t b) {
+  if constexpr (DT == SV_BF16)
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a), __builtin_bit_cast(u16x2, b)));
+  else
+    return max(a, b);
+}
+
+template <int DT>
+__device__ __forceinline__ bool mag_nonfinite(uint32_t m) {
+  if constexpr (DT == SV_BF16)
+    return (m & 0xFFFFu) >= 0x7F80u || (m >> 16) >= 0x7F80u;
+  else
+    return m >= 0x7F800000u;
+}
+
 // Streams vectors [v0, v1) of a row with stride NT per thread; returns the
 // thread's best (value, element index) with the lowest index among ties, or
-// index -1 if it saw no vector.
+// index -1 if it saw no vector, and whether one of its values was +-inf or NaN.
 template <int DT, int NT>
-__device__ __forceinline__ void stream_argmax(const uint4* vp, int v0, int v1, float& best, int& bidx) {
+__device__ __forceinline__ void stream_argmax(const uint4* vp, int v0, int v1, float& best, int& bidx,
+                                              bool& nonfinite) {
   constexpr int PER = DT == SV_BF16 ? 8 : 4;
+  uint32_t mg = 0;
   best = -INFINITY;
   int bvi = -1;
   uint4 bv = {0, 0, 0, 0};
@@ -102,6 +137,7 @@ __device__ __forceinline__ void stream_argmax(const uint4* vp, int v0, int v1, f
     for (int k = 0; k < kMixBatch; ++k) {
       if (v + k * NT < v1) {
         const float m = vec_max<DT>(cur[k]);
+        mg = mag_max<DT>(mg, vec_mag<DT>(cur[k]));
         if (m > best) {
           best = m;
           bvi = v + k * NT;
@@ -128,6 +164,7 @@ __device__ __forceinline__ void stream_argmax(const uint4* vp, int v0, int v1, f
       if (e[q] == best) k = q;
     bidx = bvi * PER + k;
   }
+  nonfinite = mag_nonfinite<DT>(mg);
 }
 
 // argmax of part `part` (of a.parts) of component row m = p*K + z (position p,
@@ -160,15 +197,18 @@ __device__ __forceinline__ void mix_block(const MixArgs& a, int m, int part, uin
   const int v1 = static_cast<int>(static_cast<int64_t>(nvec) * (part + 1) / a.parts);
   float best;
   int bidx;
-  stream_argmax<DT, NT>(reinterpret_cast<const uint4*>(rowp), v0, v1, best, bidx);
+  bool nonfinite;
+  stream_argmax<DT, NT>(reinterpret_cast<const uint4*>(rowp), v0, v1, best, bidx, nonfinite);
   if (part == a.parts - 1)
     for (int e = nvec * PER + tid; e < a.V; e += NT) {  // elements past the last full vector
       const float f = load_val<DT>(rowp, e);
+      nonfinite |= !isfinite(f);
       if (f > best || bidx < 0) {
         best = f;
         bidx = e;
       }
     }
+  if (nonfinite) raise_status(a.status, SV_ST_NONFINITE);
   uint64_t packed = bidx >= 0 ? (static_cast<uint64_t>(fkey(best)) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(bidx)) : 0;
   packed = block_max_u64<NT>(packed, red);
   if (tid == 0) {

@@ -315,6 +315,16 @@ __device__ __forceinline__ StreamPart stream_part_bf16(const uint16_t* rp, int V
   // M * c2 in double.
   float m = -INFINITY, mc = -INFINITY, mn = INFINITY;
   u16x2 hw = {0, 0};  // largest raw halves of the full batches: -inf (0xFF80) and negative NaNs at or above it
+  // T = 0 forms no sums, so NaN cannot show there: the largest magnitude half
+  // (sign bit cleared) of every vector is kept instead; >= 0x7F80 is +-inf or NaN
+  u16x2 hz = {0, 0};
+  const uint32_t kMag = 0x7FFF7FFFu;
+  auto mags = [&](const uint4& d) {
+    hz = __builtin_elementwise_max(
+        hz, __builtin_elementwise_max(
+                __builtin_elementwise_max(__builtin_bit_cast(u16x2, d.x & kMag), __builtin_bit_cast(u16x2, d.y & kMag)),
+                __builtin_elementwise_max(__builtin_bit_cast(u16x2, d.z & kMag), __builtin_bit_cast(u16x2, d.w & kMag))));
+  };
   double s = 0.0;
   int bvi = -1;
   uint4 bv = {0, 0, 0, 0};
@@ -338,6 +348,8 @@ __device__ __forceinline__ StreamPart stream_part_bf16(const uint16_t* rp, int V
 #pragma unroll
       for (int q = 1; q < 8; ++q) acc += __builtin_amdgcn_exp2f(fmaf(v[q], c2, -mc));
       s += static_cast<double>(acc);
+    } else {
+      mags(d);
     }
   };
   int v = v0 + tid;
@@ -400,6 +412,9 @@ __device__ __forceinline__ StreamPart stream_part_bf16(const uint16_t* rp, int V
           for (int q = 1; q < 8; ++q) acc += __builtin_amdgcn_exp2f(fmaf(w[q], c2, -mc));
           s += static_cast<double>(acc);
         }
+      } else {
+#pragma unroll
+        for (int k = 0; k < BATCH; ++k) mags(cur[k]);
       }
     } else {
 #pragma unroll
@@ -424,6 +439,7 @@ __device__ __forceinline__ StreamPart stream_part_bf16(const uint16_t* rp, int V
   if (tail) {
     for (int e = (nvec << 3) + tid; e < V; e += NT) {  // elements past the last full vector
       const float f = __uint_as_float(static_cast<uint32_t>(rp[e]) << 16);
+      if (!(f == f)) hz.x = 0x7FFFu;  // NaN (a tail element; T = 0 forms no sum to show it)
       mn = fminf(mn, f);
       if (f > m) {
         const float mcn = f * c2;
@@ -438,7 +454,8 @@ __device__ __forceinline__ StreamPart stream_part_bf16(const uint16_t* rp, int V
       if (sums) s += static_cast<double>(__builtin_amdgcn_exp2f(fmaf(f, c2, -mc)));
     }
   }
-  if (mn == -INFINITY || hw.x >= 0xFF80u || hw.y >= 0xFF80u) raise_status(status, SV_ST_NONFINITE);
+  if (mn == -INFINITY || hw.x >= 0xFF80u || hw.y >= 0xFF80u || hz.x >= 0x7F80u || hz.y >= 0x7F80u)
+    raise_status(status, SV_ST_NONFINITE);
   uint64_t packed =
       bidx >= 0 ? (static_cast<uint64_t>(mono_key(best)) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(bidx)) : 0;
   StreamPart out;
