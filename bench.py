@@ -1,31 +1,38 @@
 """Benchmark: verified draft positions per second on one MI355X.
 
-Workload (the full combined verification step at the largest shape):
+Default workload (the full combined verification step at the largest shape):
 concurrency 32, block 16, Qwen3 vocabulary V = 151936, bf16 target logits,
 K = 8 latent-mixture draft with greedy branches, DVL budget 256 (half of
 32 x 16) from Beta(8, 2) survival estimates, T = 1.0, top-p 0.95, residual
 and bonus sampling, Philox seeds advancing per step.  Synthetic seeded data
-(synth.config(5)).  With --branch-T T_b > 0 the same workload runs with the
-soft-branch drafter (each branch softmax(c / T_b)), a variant measured
-beside the headline line.
+(synth.config(5)).  --config 1..4 runs the other workloads (1: 4 requests,
+V 1024, fp32, dense draft; 2: conc 8, dense draft, full verification; 3: conc
+32, dense draft, DVL 256; 4: conc 16, K 8 mixture, T 1.5, top-p 0.95, full
+verification).  With --branch-T T_b > 0 the mixture workloads run with the
+soft-branch drafter (each branch softmax(c / T_b)).
 
 A timed step is the whole verification path on inputs resident in HBM:
-dvl_alloc_pack, sv_verify_rows (target-row statistics with top-p and the
-branch argmax over the component rows, one launch), sv_accept_sample
-(category posterior, acceptance, residual / bonus draw).  The target forward is outside the path; its output for
-each step (the packed rows for that step's allocation) is prepared before the
-timed region in a buffer of its own, as the target model would have written it.
+dvl_alloc_pack (workloads with a budget), the rows launch (sv_verify_rows:
+target-row statistics with top-p and the branch argmax over the component
+rows; sv_verify_rows_dense: target and draft rows), sv_accept_sample
+(category posterior, acceptance, residual / bonus draw).  The target forward
+is outside the path; its output for each step (the packed rows for that
+step's allocation) is prepared before the timed region in a buffer of its
+own.  Tensors that every step re-reads (the component or draft rows, and the
+target rows under full verification) are held in several device copies used
+in turn, so that a step never reads what the steps before it left in the
+256 MB Infinity Cache (--copies overrides the count).
 
-Prints one JSON line.  `roofline` is for the dominant kernel (k_rows_mix of
-sv_verify_rows: target-row statistics and the branch argmax over the component
-rows), timed live with HIP events on the stream the kernels run on; `cpu_baseline` is the CPU oracle on a bounded sample of the
-same workload.
+Prints one JSON line.  `roofline` is for the dominant kernel (the rows
+launch), timed live with HIP events on the stream the kernels run on;
+`cpu_baseline` is the CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -34,6 +41,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
+MALL_BYTES = 256 << 20  # Infinity Cache of one MI355X
 
 
 def parse():
@@ -43,44 +51,60 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the CPU-oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--config", type=int, default=5, choices=(3, 5),
-                    help="5: conc 32 K=8 mixture with top-p and DVL (the headline workload); 3: conc 32 dense "
-                         "independent draft with DVL, no top-p")
+    ap.add_argument("--config", type=int, default=5, choices=(1, 2, 3, 4, 5),
+                    help="5: conc 32 K=8 mixture with top-p and DVL (the headline workload); 1-4: the other "
+                         "workloads")
     ap.add_argument("--branch-T", type=float, default=0.0,
                     help="soft-branch mixture: the drafter samples each branch from softmax(c / T_b) and "
                          "verification uses those branch distributions (0: greedy branches, the default)")
+    ap.add_argument("--copies", type=int, default=0,
+                    help="device copies of each re-read tensor, used in turn (0: enough that a step never re-reads "
+                         "what the previous 768 MB of reads left in cache)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before the steps, one elementwise kernel that reads and writes MIB MiB: "
                          "the known-size reference that scales the HBM counters")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="write profiles/traffic.json from two rocprofv3 counter_collection.csv files "
-                         "(FETCH_SIZE run, WRITE_SIZE run, both with --copy-calibration) and exit")
+                    help="write the rows kernel's record in profiles/traffic.json from two rocprofv3 "
+                         "counter_collection.csv files (FETCH_SIZE run, WRITE_SIZE run, both with --copy-calibration "
+                         "and the same --config) and exit")
     return ap.parse_args()
 
 
-def kernel_source_hash() -> str:
+# ---------------------------------------------------------------- HBM traffic records
+def rows_kernel(config: int) -> str:
+    return "k_rows_mix" if config in (4, 5) else "k_rows_dense"
+
+
+KERNEL_SOURCES = {
+    "k_rows_mix": ("sv_mix.hip", "sv_rows_dev.hpp", "sv_device.hpp"),
+    "k_rows_dense": ("sv_rows.hip", "sv_rows_dev.hpp", "sv_device.hpp"),
+}
+
+
+def kernel_source_hash(kernel: str) -> str:
     h = hashlib.sha256()
-    for f in ("sv_mix.hip", "sv_rows_dev.hpp", "sv_device.hpp"):
+    for f in KERNEL_SOURCES[kernel]:
         h.update(open(os.path.join(ROOT, "draft_verification_sv_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel: str):
-    """HBM traffic per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel source; else None."""
+def traffic_key(config: int) -> str:
+    return f"cfg{config}:{rows_kernel(config)}"
+
+
+def load_traffic(config: int):
+    """HBM traffic per launch of the rows kernel from committed rocprofv3 counter
+    runs of this workload, if they were taken on the current kernel source; else None."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
     try:
-        rec = json.load(open(p)).get(kernel)
+        rec = json.load(open(p)).get(traffic_key(config))
     except (ValueError, AttributeError):
         return None
-    if not rec or rec.get("source_sha") != kernel_source_hash():
+    if not rec or rec.get("source_sha") != kernel_source_hash(rows_kernel(config)):
         return None
     return rec.get("bytes_per_launch")
-
-
-ROWS_KERNEL = "k_rows_mix"
 
 
 def _counter_rows(path: str, counter: str):
@@ -99,27 +123,44 @@ def _counter_rows(path: str, counter: str):
     return list(per.values())
 
 
-def summarize_counters(fetch_csv: str, write_csv: str, copy_bytes: int, algorithmic: float):
+def algorithmic_rows_bytes(config: int) -> float:
+    """Algorithmic bytes of one rows launch: every target row (L_r + 1 per request)
+    and every verified position's K component rows (dense: its draft row), each
+    read once.  Workloads with a budget verify exactly `budget` positions (every
+    survival score is positive)."""
+    import synth
+
+    w = synth.config(config, V=8, steps=1)  # the shapes only
+    R, b, K = w.R, w.b, w.K
+    V, esz = 151936 if config != 1 else 1024, 2 if config != 1 else 4
+    pos = w.budget if w.budget is not None else R * b
+    return float((pos + R) * V * esz + pos * max(K, 1) * V * esz)
+
+
+def summarize_counters(config: int, fetch_csv: str, write_csv: str, copy_bytes: int):
     """Per-launch HBM traffic of the rows kernel: FETCH_SIZE and WRITE_SIZE (KiB per
     dispatch), each scaled by what the same counter reads for the calibration kernel
     (torch.neg over copy_bytes: copy_bytes read and copy_bytes written)."""
     import numpy as np
 
+    kernel = rows_kernel(config)
+
     def split(rows):
         copy = [v for n, v in rows if "neg_kernel" in n]
-        kern = [v for n, v in rows if ROWS_KERNEL in n]
+        kern = [v for n, v in rows if kernel in n]
         if not copy or not kern:
-            raise SystemExit(f"counter file lacks the calibration copy or {ROWS_KERNEL}: "
+            raise SystemExit(f"counter file lacks the calibration copy or {kernel}: "
                              f"{sorted(set(n for n, _ in rows))}")
         return max(copy), kern
 
+    algorithmic = algorithmic_rows_bytes(config)
     cf, kf = split(_counter_rows(fetch_csv, "FETCH_SIZE"))
     cw, kw = split(_counter_rows(write_csv, "WRITE_SIZE"))
     known_kib = copy_bytes / 1024.0
     sf, sw = known_kib / cf, known_kib / cw
     fetch_b = float(np.mean(kf)) * 1024.0 * sf
     write_b = float(np.mean(kw)) * 1024.0 * sw
-    rec = {"source_sha": kernel_source_hash(), "bytes_per_launch": round(fetch_b + write_b),
+    rec = {"source_sha": kernel_source_hash(kernel), "bytes_per_launch": round(fetch_b + write_b),
            "fetch_bytes": round(fetch_b), "write_bytes": round(write_b),
            "fetch_kib_raw": float(np.mean(kf)), "write_kib_raw": float(np.mean(kw)),
            "copy_fetch_kib_raw": cf, "copy_write_kib_raw": cw, "copy_bytes": copy_bytes,
@@ -132,19 +173,25 @@ def summarize_counters(fetch_csv: str, write_csv: str, copy_bytes: int, algorith
             allrec = json.load(open(path))
         except ValueError:
             allrec = {}
-    allrec[ROWS_KERNEL] = rec
+    allrec[traffic_key(config)] = rec
     with open(path, "w") as f:
         json.dump(allrec, f, indent=1)
     print(json.dumps(rec, indent=1))
 
 
+# ---------------------------------------------------------------- the benchmark
+def copies_for(per_step_bytes: float, override: int) -> int:
+    """Copies of a tensor of which each step reads per_step_bytes, so that a copy
+    is read again only after 3x the Infinity Cache's size of other reads."""
+    if override > 0:
+        return override
+    return max(1, min(64, math.ceil(3 * MALL_BYTES / max(per_step_bytes, 1.0))))
+
+
 def main():
     args = parse()
     if args.summarize_counters:
-        # cfg5 verifies exactly `budget` positions every step (all survival scores > 0)
-        pos, R, K, V = 256, 32, 8, 151936
-        summarize_counters(*args.summarize_counters, args.copy_calibration << 20,
-                           float((pos + R) * V * 2 + pos * K * V * 2))
+        summarize_counters(args.config, *args.summarize_counters, args.copy_calibration << 20)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this path runs on a single GPU)",
@@ -163,28 +210,35 @@ def main():
     t_gen = time.time()
     bT = args.branch_T
     soft = bT > 0
-    dense = args.config == 3
-    if dense and soft:
-        raise SystemExit("--branch-T applies to the mixture workload (--config 5)")
-    w = synth.config(args.config, steps=S, branch_T=bT)
+    cfg = args.config
+    if soft and cfg not in (4, 5):
+        raise SystemExit("--branch-T applies to the mixture workloads (--config 4 or 5)")
+    w = synth.config(cfg, steps=S, branch_T=bT)
     R, b, V, K, B = w.R, w.b, w.V, w.K, w.budget
+    dense = K == 0
+    dvl = B is not None
     print(f"[bench] data generated in {time.time() - t_gen:.1f}s: {w.name}", file=sys.stderr, flush=True)
-    ld = row_pitch(V, "bf16")
-    max_pos = min(B, R * b)
+    ld = row_pitch(V, w.dtype)
+    esz = 2 if w.dtype == "bf16" else 4
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dt = sv.SV_BF16 if w.dtype == "bf16" else sv.SV_F32
+    max_pos = min(B, R * b) if dvl else R * b
     max_rows = max_pos + R
-    dt = sv.SV_BF16
     ws, nb = sv.make_workspace(R, b, K, V, dev)
+    row_bytes = V * esz
 
-    full = to_device_rows(w.tgt, ld, dev)            # [R*(b+1), ld]: target rows for every position
-    comp = None if dense else to_device_rows(w.comp, ld, dev)    # [R*K*b, ld]
-    draft = to_device_rows(w.draft, ld, dev) if dense else None  # [R*b, ld]
+    # proposal rows, in copies used in turn
+    prop_host = w.draft if dense else w.comp
+    prop_rows_per_step = max_pos * (1 if dense else K)
+    n_prop = copies_for(prop_rows_per_step * row_bytes, args.copies)
+    prop = [to_device_rows(prop_host, ld, dev) for _ in range(n_prop)]
     mix = None if dense else torch.from_numpy(w.mix.reshape(-1)).to(dev)
-    a_all = torch.from_numpy(w.a.reshape(S, R * b)).to(dev)
+    a_all = torch.from_numpy(w.a.reshape(S, R * b)).to(dev) if dvl else None
     x_all = torch.from_numpy(w.x.reshape(S, R * b)).to(dev)
     seeds = torch.from_numpy(w.seeds.view(np.int64)).to(dev)
     T = torch.from_numpy(w.T).to(dev)
     top_p = None if w.top_p is None else torch.from_numpy(w.top_p).to(dev)
-    budget = torch.tensor([B], dtype=torch.int32, device=dev)
+    budget = torch.tensor([B if dvl else 0], dtype=torch.int32, device=dev)
     branch_T = torch.full((R,), bT, dtype=torch.float32, device=dev) if soft else None
 
     i32, f32, f64 = torch.int32, torch.float32, torch.float64
@@ -209,47 +263,54 @@ def main():
 
     # ---- the target forward's output for every step, prepared before timing
     t_prep = time.time()
-    packed = torch.empty((S, max_rows, ld), dtype=torch.bfloat16, device=dev)
+    full = to_device_rows(w.tgt, ld, dev)  # [R*(b+1), ld]: target rows for every position
     L_host = np.zeros((S, R), np.int32)
-    for s in range(S):
-        sv.dvl_alloc_pack(a_all[s], R, b, None, budget, s_sc, L, pos_off, tgt_off, ws, nb, sp)
-        L_host[s] = L.cpu().numpy()
-        pack_rows_device(full, L_host[s], b + 1, packed[s])
+    if dvl:  # each step's packed rows in a buffer of its own
+        packed = torch.empty((S, max_rows, ld), dtype=tdt, device=dev)
+        for s in range(S):
+            sv.dvl_alloc_pack(a_all[s], R, b, None, budget, s_sc, L, pos_off, tgt_off, ws, nb, sp)
+            L_host[s] = L.cpu().numpy()
+            pack_rows_device(full, L_host[s], b + 1, packed[s])
+        del full
+        n_tgt = S
+    else:  # full verification: the same rows every step, in copies used in turn
+        L_host[:] = b
+        n_tgt = copies_for(max_rows * row_bytes, args.copies)
+        packed = [full] + [full.clone() for _ in range(n_tgt - 1)]
+        L.fill_(b)
+        pos_off.copy_(torch.arange(R + 1, dtype=i32, device=dev) * b)
+        tgt_off.copy_(torch.arange(R + 1, dtype=i32, device=dev) * (b + 1))
     torch.cuda.synchronize()
-    print(f"[bench] packed target rows for {S} steps in {time.time() - t_prep:.1f}s", file=sys.stderr, flush=True)
+    print(f"[bench] target rows for {S} steps in {time.time() - t_prep:.1f}s; {n_tgt} target and {n_prop} "
+          f"proposal copies", file=sys.stderr, flush=True)
     positions = L_host.sum(axis=1)  # verified positions per step
 
-    def step_dense(s, ev=None):
-        sv.dvl_alloc_pack(a_all[s], R, b, None, budget, s_sc, L, pos_off, tgt_off, ws, nb, sp)
-        if ev is not None:
-            ev[0].record(stream)
-        # target-row and draft-row statistics in one launch
-        sv.sv_verify_rows_dense(packed[s], dt, ld, V, tgt_off, R, max_rows, T, top_p, row_max, row_arg, row_lse,
-                                row_cut, row_kept, draft, dt, ld, b, pos_off, max_pos, d_max, d_arg, d_lse, ws, nb,
-                                sp)
-        if ev is not None:
-            ev[1].record(stream)
-        # acceptance, residual / bonus draw
-        sv.sv_accept_sample(packed[s], dt, ld, V, tgt_off, pos_off, R, b, T, row_arg, row_cut, row_kept, x_all[s],
-                            sv.SV_Q_DENSE, draft, dt, ld, d_arg, d_lse, 0, None, None, 0, None, None, None, None,
-                            seeds[s:s + 1], n_acc, token, is_bonus, None, None, None, ws, nb, sp)
-
     def step(s, ev=None):
-        if dense:
-            return step_dense(s, ev)
-        sv.dvl_alloc_pack(a_all[s], R, b, None, budget, s_sc, L, pos_off, tgt_off, ws, nb, sp)
+        tg = packed[s % n_tgt]
+        pr = prop[s % n_prop]
+        if dvl:
+            sv.dvl_alloc_pack(a_all[s], R, b, None, budget, s_sc, L, pos_off, tgt_off, ws, nb, sp)
         if ev is not None:
             ev[0].record(stream)
-        # target rows (statistics, top-p) and component rows (branch argmax) in one launch
-        sv.sv_verify_rows(packed[s], dt, ld, V, tgt_off, R, max_rows, T, top_p, row_max, row_arg, row_lse, row_cut,
-                          row_kept, comp, ld, K, b, pos_off, max_pos, branch_T, ws, nb, sp)
+        if dense:  # target-row and draft-row statistics in one launch
+            sv.sv_verify_rows_dense(tg, dt, ld, V, tgt_off, R, max_rows, T, top_p, row_max, row_arg, row_lse,
+                                    row_cut, row_kept, pr, dt, ld, b, pos_off, max_pos, d_max, d_arg, d_lse, ws, nb,
+                                    sp)
+        else:  # target rows (statistics, top-p) and component rows (branch argmax) in one launch
+            sv.sv_verify_rows(tg, dt, ld, V, tgt_off, R, max_rows, T, top_p, row_max, row_arg, row_lse, row_cut,
+                              row_kept, pr, ld, K, b, pos_off, max_pos, branch_T, ws, nb, sp)
         if ev is not None:
             ev[1].record(stream)
-        # category posterior, acceptance, residual / bonus draw
-        sv.sv_accept_sample(packed[s], dt, ld, V, tgt_off, pos_off, R, b, T, row_arg, row_cut, row_kept, x_all[s],
-                            sv.SV_Q_MIXTURE, None, dt, 0, None, None, K, mix, comp if soft else None,
-                            ld if soft else 0, branch_T, branch_tok, post_w, q_at,
-                            seeds[s:s + 1], n_acc, token, is_bonus, None, None, None, ws, nb, sp)
+        # (mixture: category posterior), acceptance, residual / bonus draw
+        if dense:
+            sv.sv_accept_sample(tg, dt, ld, V, tgt_off, pos_off, R, b, T, row_arg, row_cut, row_kept, x_all[s],
+                                sv.SV_Q_DENSE, pr, dt, ld, d_arg, d_lse, 0, None, None, 0, None, None, None, None,
+                                seeds[s:s + 1], n_acc, token, is_bonus, None, None, None, ws, nb, sp)
+        else:
+            sv.sv_accept_sample(tg, dt, ld, V, tgt_off, pos_off, R, b, T, row_arg, row_cut, row_kept, x_all[s],
+                                sv.SV_Q_MIXTURE, None, dt, 0, None, None, K, mix, pr if soft else None,
+                                ld if soft else 0, branch_T, branch_tok, post_w, q_at,
+                                seeds[s:s + 1], n_acc, token, is_bonus, None, None, None, ws, nb, sp)
 
     for k in range(args.warmup):
         step(k % S)
@@ -272,13 +333,12 @@ def main():
         nacc_hist[s].copy_(n_acc)
     torch.cuda.synchronize()
     rejected = (nacc_hist.cpu().numpy() < L_host).sum(axis=1)  # requests drawing a residual, per step
-    mix_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
-    row_bytes = V * 2
-    # algorithmic bytes of the timed statistics launch(es): every target row (L_r + 1 per request) and
-    # every verified position's K component rows (dense: its draft row), each read once
+    rows_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    # algorithmic bytes of the rows launch: every target row (L_r + 1 per request) and every verified
+    # position's K component rows (dense: its draft row), each read once
     per_pos = 1 if dense else K
-    mix_bytes = float(np.mean((positions + R) * row_bytes + positions * per_pos * row_bytes))
-    achieved = mix_bytes / (mix_ms * 1e-3) / 1e9
+    rows_bytes = float(np.mean((positions + R) * row_bytes + positions * per_pos * row_bytes))
+    achieved = rows_bytes / (rows_ms * 1e-3) / 1e9
     # step-aggregate algorithmic bytes: target rows, component (draft) rows, one sampled row per request
     # (dense draft or soft branches: a residual also reads the draft row, or the K branch rows, of its slot)
     step_bytes = (positions + R) * row_bytes + positions * per_pos * row_bytes + R * row_bytes
@@ -293,16 +353,16 @@ def main():
     if not args.no_cpu:
         cpu = cpu_baseline(w, args.cpu_seconds)
 
-    traffic = None if (soft or dense) else load_traffic(ROWS_KERNEL)
-    mixture = f"K8 soft-branch mixture T_b {bT:g}" if soft else "K8 greedy-branch mixture"
-    if dense:
-        workload = ("conc32 block16 V151936 bf16, independent (dense) draft, DVL budget 256, T1.0, no top-p, "
-                    "residual+bonus, seeds advancing per step")
-        kernel = "k_rows_dense (sv_verify_rows_dense: target rows + draft rows)"
-    else:
-        workload = (f"conc32 block16 V151936 bf16, {mixture}, DVL budget 256, T1.0 top-p0.95, residual+bonus, "
-                    "seeds advancing per step")
-        kernel = "k_rows_mix (sv_verify_rows" + (", soft branches)" if soft else ")")
+    traffic = None if soft else load_traffic(cfg)
+    prop_desc = (f"K8 soft-branch mixture T_b {bT:g}" if soft else "K8 greedy-branch mixture") if not dense \
+        else "independent (dense) draft"
+    alloc = f"DVL budget {B}" if dvl else "full verification"
+    tp = f"top-p{w.top_p[0]:g}" if w.top_p is not None else "no top-p"
+    temps = "/".join(f"{t:g}" for t in sorted(set(w.T.tolist())))
+    workload = (f"cfg{cfg}: conc{R} block{b} V{V} {w.dtype}, {prop_desc}, {alloc}, T{temps} {tp}, residual+bonus, "
+                f"seeds advancing per step")
+    kernel = rows_kernel(cfg) + (" (sv_verify_rows" + (", soft branches)" if soft else ")") if not dense
+                                 else " (sv_verify_rows_dense: target rows + draft rows)")
     out = {
         "metric": "verified draft positions/sec at V=151936, conc 32; % of peak HBM GB/s",
         "value": round(value, 1),
@@ -314,17 +374,19 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded Zipfian logits, Beta(8,2) survival estimates)",
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded Zipfian logits, Beta(8,2) survival estimates)" if cfg != 1
+                else "synthetic (seeded N(0, 4) logits)",
         "config": {"workload": workload,
                    "requests": R, "block": b, "vocab": V, "K": K, "budget": B,
+                   "copies": {"target": n_tgt if not dvl else "one per step", "proposal": n_prop},
                    **({"branch_T": bT} if soft else {})},
         "step_gbps": round(float(np.mean(step_bytes)) / (ms_per_step * 1e-3) / 1e9, 1),
         "step_frac_of_peak": round(float(np.mean(step_bytes)) / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
         "roofline": {"kernel": kernel, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
-                     "traffic": traffic, "avg_launch_us": round(mix_ms * 1e3, 2),
-                     "algorithmic_bytes_per_launch": mix_bytes},
+                     "traffic": traffic, "avg_launch_us": round(rows_ms * 1e3, 2),
+                     "algorithmic_bytes_per_launch": rows_bytes},
         "cpu_baseline": cpu,
         "device_status": status,
     }
@@ -333,8 +395,9 @@ def main():
 
 def cpu_baseline(w, seconds: float):
     """The CPU oracle as it stands, on a bounded sample of the same workload:
-    whole steps (DVL, then the step: target statistics with top-p, mixture
-    argmax and posterior, acceptance, residual/bonus) until `seconds` pass."""
+    whole steps (DVL when the workload has a budget, then the step: target
+    statistics with top-p, proposal, acceptance, residual/bonus) on every
+    OpenMP thread until `seconds` pass; then one step on a single thread."""
     import numpy as np
 
     import oracle
@@ -343,19 +406,33 @@ def cpu_baseline(w, seconds: float):
     tgt = w.tgt.reshape(R * (b + 1), V)
     prop = dict(comp=w.comp.reshape(R * K * b, V), comp_row0=np.arange(R) * K * b, mix=w.mix, branch_T=w.branch_T) \
         if K > 0 else dict(draft=w.draft.reshape(R * b, V), draft_row0=np.arange(R) * b)
+
+    def one(n):
+        if w.budget is not None:
+            Lr = oracle.dvl(w.a[n], w.budget)["L"]
+        else:
+            Lr = np.full(R, b, np.int32)
+        oracle.step(tgt=tgt, tgt_row0=np.arange(R) * (b + 1), L=Lr, T=w.T, x=w.x[n], seed=int(w.seeds[n]),
+                    top_p=w.top_p, **prop)
+        return int(Lr.sum())
+
+    threads = oracle.num_threads()
     t0 = time.perf_counter()
     pos = n = 0
     while n < w.steps:
-        dv = oracle.dvl(w.a[n], w.budget)
-        oracle.step(tgt=tgt, tgt_row0=np.arange(R) * (b + 1), L=dv["L"], T=w.T, x=w.x[n], seed=int(w.seeds[n]),
-                    top_p=w.top_p, **prop)
-        pos += int(dv["L"].sum())
+        pos += one(n)
         n += 1
         if time.perf_counter() - t0 > seconds:
             break
     el = time.perf_counter() - t0
-    return {"value": round(pos / el, 2), "unit": "positions/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{n} whole steps of the same workload ({pos} verified positions) in {el:.1f}s"}
+    oracle.set_num_threads(1)
+    t1 = time.perf_counter()
+    one(0)
+    single = time.perf_counter() - t1
+    oracle.set_num_threads(threads)
+    return {"value": round(pos / el, 2), "unit": "positions/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} whole steps of the same workload ({pos} verified positions) in {el:.1f}s",
+            "nproc": os.cpu_count(), "omp_threads": threads, "single_thread_step_s": round(single, 3)}
 
 
 if __name__ == "__main__":

@@ -110,6 +110,8 @@ def _declare(L):
     L.orc_step.restype = C.c_int
     L.orc_num_threads.argtypes = []
     L.orc_num_threads.restype = C.c_int
+    L.orc_set_num_threads.argtypes = [C.c_int]
+    L.orc_set_num_threads.restype = None
 
 
 def _ptr(a):
@@ -130,6 +132,10 @@ def _rows_dtype(rows):
 
 def num_threads() -> int:
     return int(lib().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    lib().orc_set_num_threads(int(n))
 
 
 # ---------------------------------------------------------------- Philox

@@ -27,6 +27,14 @@ int orc_num_threads(void) {
 #endif
 }
 
+void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------------------ */
 /* Philox4x32-10 [Philox]: ten rounds of a 2x(32x32->64) multiply round.   */
 /* Per round, with multipliers M0, M1 and the current key (k0, k1):          */

@@ -144,6 +144,8 @@ typedef struct {
 int orc_step(const orc_step_in_t* in, const orc_step_out_t* out);
 
 int orc_num_threads(void);
+/* threads for the oracle's later parallel loops (OpenMP); n <= 0 is ignored */
+void orc_set_num_threads(int n);
 
 #ifdef __cplusplus
 }
