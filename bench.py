@@ -63,10 +63,13 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before the steps, one elementwise kernel that reads and writes MIB MiB: "
                          "the known-size reference that scales the HBM counters")
-    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="write the rows kernel's record in profiles/traffic.json from two rocprofv3 "
-                         "counter_collection.csv files (FETCH_SIZE run, WRITE_SIZE run, both with --copy-calibration "
-                         "and the same --config) and exit")
+    ap.add_argument("--summarize-db", nargs="+", metavar="DB",
+                    help="print a markdown summary (per-kernel mean duration, or mean counter values) of rocprofv3 "
+                         "result databases (*_results.db) and exit")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH", "WRITE"),
+                    help="write the rows kernel's record in profiles/traffic.json from two rocprofv3 counter "
+                         "outputs (counter_collection.csv or *_results.db: a FETCH_SIZE run, a WRITE_SIZE run, both "
+                         "with --copy-calibration and the same --config) and exit")
     return ap.parse_args()
 
 
@@ -108,10 +111,19 @@ def load_traffic(config: int):
 
 
 def _counter_rows(path: str, counter: str):
-    """(kernel name, value) per dispatch of one counter in a rocprofv3 CSV."""
+    """(kernel name, value) per dispatch of one counter in a rocprofv3 CSV or result database."""
     import csv
 
     per = {}
+    if path.endswith(".db"):
+        import sqlite3
+
+        con = sqlite3.connect(path)
+        for key, name, val in con.execute("select dispatch_id, kernel_name, value from counters_collection "
+                                          "where counter_name = ?", (counter,)):
+            k0 = per.get(key)
+            per[key] = (name, float(val) + (k0[1] if k0 else 0.0))
+        return list(per.values())
     with open(path, newline="") as f:
         for row in csv.DictReader(f):
             if row.get("Counter_Name") != counter:
@@ -188,8 +200,49 @@ def copies_for(per_step_bytes: float, override: int) -> int:
     return max(1, min(64, math.ceil(3 * MALL_BYTES / max(per_step_bytes, 1.0))))
 
 
+def summarize_db(paths):
+    """Markdown tables from rocprofv3 result databases: per kernel, the number of
+    dispatches and mean duration (kernel traces), or the mean of each counter
+    over its dispatches (counter runs)."""
+    import collections
+    import sqlite3
+
+    def short(name):
+        name = name.split("(")[0]
+        return name[5:] if name.startswith("void ") else name
+
+    for path in paths:
+        con = sqlite3.connect(path)
+        views = {r[0] for r in con.execute("select name from sqlite_master where type in ('table', 'view')")}
+        print(f"### {os.path.basename(os.path.dirname(path))}/{os.path.basename(path)}\n")
+        rows = list(con.execute("select dispatch_id, kernel_name, counter_name, value from counters_collection")) \
+            if "counters_collection" in views else []
+        if rows:
+            per = collections.defaultdict(float)  # a counter's instances (per XCD, SE ...) summed per dispatch
+            for did, name, counter, value in rows:
+                per[(did, short(name), counter)] += float(value)
+            acc = collections.defaultdict(lambda: collections.defaultdict(list))
+            for (_, name, counter), value in per.items():
+                acc[name][counter].append(value)
+            counters = sorted({c for k in acc.values() for c in k})
+            print("| kernel | dispatches | " + " | ".join(counters) + " |")
+            print("|---|---|" + "---|" * len(counters))
+            for k in sorted(acc):
+                n = max(len(v) for v in acc[k].values())
+                cells = [f"{sum(acc[k][c]) / len(acc[k][c]):.4g}" if acc[k].get(c) else "" for c in counters]
+                print(f"| {k} | {n} | " + " | ".join(cells) + " |")
+        else:
+            print("| kernel | dispatches | mean us | total us |\n|---|---|---|---|")
+            for name, calls, total, avg, _ in con.execute("select * from top_kernels"):
+                print(f"| {short(name)} | {calls} | {avg:.2f} | {total:.1f} |")
+        print()
+
+
 def main():
     args = parse()
+    if args.summarize_db:
+        summarize_db(args.summarize_db)
+        return
     if args.summarize_counters:
         summarize_counters(args.config, *args.summarize_counters, args.copy_calibration << 20)
         return

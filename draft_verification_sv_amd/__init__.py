@@ -29,7 +29,7 @@ SV_NOALLOC_SCRATCH_BYTES = 1 << 20
 STATUS_BITS = {
     0x001: "BAD_TEMPERATURE", 0x002: "BAD_TOP_P", 0x004: "NONFINITE", 0x008: "BAD_SCORE",
     0x010: "BAD_TOKEN", 0x020: "BAD_OFFSETS", 0x040: "EMPTY_POSTERIOR", 0x080: "BAD_BUDGET",
-    0x100: "BAD_NACC", 0x200: "BAD_BLOCK",
+    0x100: "BAD_NACC", 0x200: "BAD_BLOCK", 0x400: "BAD_TREE",
 }
 
 EXPORTS = [
@@ -37,6 +37,7 @@ EXPORTS = [
     "dvl_alloc_pack", "sv_softmax_stats", "sv_topp_threshold", "sv_mixture_q", "sv_accept",
     "sv_residual_sample", "sv_philox_uniforms", "sv_verify_rows", "sv_verify_rows_dense", "sv_accept_sample",
     "sv_selftest_exp", "sv_selftest_philox_host", "sv_selftest_rows_host", "sv_residual_sample_noalloc",
+    "sv_tree_workspace_bytes", "sv_tree_verify",
 ]
 
 
@@ -77,6 +78,9 @@ _SIGS = {
     "sv_residual_sample_noalloc": [_vp, _i32, _i64, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _vp,
                                    _i32, _i64, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "sv_philox_uniforms": [_vp, _i32, _i32, _vp, _vp],
+    "sv_tree_workspace_bytes": [_i32, _i32, _i32, C.POINTER(C.c_size_t)],
+    "sv_tree_verify": [_vp, _i32, _i64, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32,
+                       _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _sz, _vp],
     "sv_selftest_exp": [_vp, _vp, _i32, _vp],
     "sv_verify_rows_dense": [_vp, _i32, _i64, _i32, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
                              _i64, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _sz, _vp],
@@ -250,6 +254,24 @@ def sv_residual_sample_noalloc(tgt_logits, dtype, tgt_ld, V, tgt_off, pos_off, R
                                            _p(draft_logits), draft_dtype, draft_ld, _p(draft_argmax), _p(draft_lse),
                                            K, _p(branch_tok), _p(post_w), _p(seed), _p(n_acc), _p(token),
                                            _p(is_bonus), _p(status), _stream(stream)), "sv_residual_sample_noalloc")
+
+
+def sv_tree_workspace_bytes(max_nodes, max_kids, V) -> int:
+    out = C.c_size_t(0)
+    _check(_lib.sv_tree_workspace_bytes(max_nodes, max_kids, V, C.byref(out)), "sv_tree_workspace_bytes")
+    return int(out.value)
+
+
+def sv_tree_verify(tgt_logits, dtype, tgt_ld, V, node_off, parent, token, R, b, max_nodes, max_kids, temperature,
+                   row_argmax, row_cut, row_kept_lse, draft_logits, draft_dtype, draft_ld, draft_argmax, draft_lse,
+                   seed, n_acc, path, stop_node, token_out, is_bonus, p_out, q_out, u_out, ws, ws_bytes, tree_ws,
+                   tree_ws_bytes, stream=None):
+    _check(_lib.sv_tree_verify(_p(tgt_logits), dtype, tgt_ld, V, _p(node_off), _p(parent), _p(token), R, b, max_nodes,
+                               max_kids, _p(temperature), _p(row_argmax), _p(row_cut), _p(row_kept_lse),
+                               _p(draft_logits), draft_dtype, draft_ld, _p(draft_argmax), _p(draft_lse), _p(seed),
+                               _p(n_acc), _p(path), _p(stop_node), _p(token_out), _p(is_bonus), _p(p_out), _p(q_out),
+                               _p(u_out), _p(ws), ws_bytes, _p(tree_ws), tree_ws_bytes, _stream(stream)),
+           "sv_tree_verify")
 
 
 def sv_selftest_exp(x, out, n, stream=None):

@@ -33,56 +33,10 @@
 #include <mutex>
 
 #include "sv_device.hpp"
+#include "sv_draw.hpp"
 #include "sv_host.hpp"
 
 namespace sv {
-
-struct SampleArgs {
-  const void* tgt;
-  int dtype;
-  int64_t tgt_ld;
-  int V;
-  const int32_t* tgt_off;
-  const int32_t* pos_off;
-  int R, b;
-  const float* T;
-  const int32_t* row_argmax;
-  const float* row_cut;
-  const double* row_kept;
-  const int32_t* x;
-  int q_mode;
-  const void* draft;
-  int ddtype;
-  int64_t draft_ld;
-  const int32_t* dargmax;
-  const double* dlse;
-  const double* qx;  // q at the draft tokens (mixture, standalone acceptance)
-  int K;
-  const float* mix;  // mixing logits (fused tail)
-  const int32_t* branch_tok;  // standalone draw: the branch argmax
-  const uint64_t* bkey;       // fused tail: the partial argmax keys of the rows launch
-  int32_t* branch_out;        // fused tail: the branch argmax, written for i < L_r
-  double* post_w;      // read by the standalone draw; written by the fused tail
-  double* q_at_draft;  // written by the fused tail
-  const uint64_t* seed;
-  const int32_t* n_acc_in;
-  int32_t* n_acc;
-  int32_t* token;
-  int32_t* is_bonus;
-  double* p_out;
-  double* q_out;
-  float* u_out;
-  DrawRec* rec;  // [R] draw records
-  double* sub;   // [R * NSUB * 2] sub-chunk sums {draw weight, p}
-  int NSUB;      // sub-chunks per row
-  int S;         // chunks per row
-  uint32_t* status;
-  const void* comp;        // soft branches: component rows [R*K*b, comp_ld], target dtype
-  int64_t comp_ld;
-  const float* branch_T;   // soft branches: T_b per request
-  const double* blse;      // soft branches: lse(c / T_b) per component row (rows launch)
-  const int32_t* barg;     // soft branches: argmax per component row (rows launch)
-};
 
 __device__ __forceinline__ const char* row_ptr(const void* base, int dtype, int64_t row, int64_t ld) {
   return static_cast<const char*>(base) + static_cast<size_t>(row) * static_cast<size_t>(ld) * (dtype == SV_BF16 ? 2 : 4);
@@ -1364,6 +1318,41 @@ __global__ __launch_bounds__(kWave) void k_pick(SampleArgs a) {
     a.token[r] = tok;
     a.is_bonus[r] = bonus;
   }
+}
+
+// ------------------------------------------------------------------ draws from prepared records
+// The sums of a draw whose record (a.rec[r]) an earlier kernel wrote: the
+// tree verification's walk.  Dense proposals only (SV_Q_DENSE weights).
+template <int DT, int DDT>
+__global__ __launch_bounds__(kSumNT) void k_rec_sums(SampleArgs a) {
+  __shared__ double etab[kExpTab];
+  __shared__ DrawCtx c;
+  extern __shared__ __align__(16) int dyn[];
+  const int r = blockIdx.x / a.S, ch = blockIdx.x % a.S;
+  exp_table_init(etab);
+  if (threadIdx.x == 0) {
+    const DrawRec& d = a.rec[r];
+    c.mode = d.mode; c.n = d.n; c.bonus = d.bonus; c.token = d.token; c.ncorr = 0;
+    c.trow = d.trow; c.drow = d.drow; c.cut = d.cut; c.invT = d.invT; c.kept = d.kept; c.dlse = d.dlse;
+    c.invTb = 0.0;
+  }
+  __syncthreads();
+  if (c.mode != kDrawResidual && c.mode != kDrawP) return;  // greedy (the pick takes the argmax), or none
+  sub_sums<DT, DDT, true>(a, c, r, ch, reinterpret_cast<float*>(dyn), etab);
+}
+
+template <int DT, int DDT>
+static int32_t launch_record_draw_t(const SampleArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((k_rec_sums<DT, DDT>), dim3(a.R * a.S), dim3(kSumNT), DLists<true>::kBytes, s, a);
+  if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
+  hipLaunchKernelGGL((k_pick<DT, DDT, true, false>), dim3(a.R), dim3(kWave), 0, s, a);
+  return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
+}
+
+int32_t launch_record_draw(const SampleArgs& a, hipStream_t s) {
+  const bool bf = a.dtype == SV_BF16, dbf = a.ddtype == SV_BF16;
+  if (bf) return dbf ? launch_record_draw_t<SV_BF16, SV_BF16>(a, s) : launch_record_draw_t<SV_BF16, SV_F32>(a, s);
+  return dbf ? launch_record_draw_t<SV_F32, SV_BF16>(a, s) : launch_record_draw_t<SV_F32, SV_F32>(a, s);
 }
 
 }  // namespace sv

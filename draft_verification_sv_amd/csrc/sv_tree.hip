@@ -1,0 +1,428 @@
+// sv_tree.hip -- tree verification: multi-round speculative sampling over the
+// candidates of each node of a draft tree.
+//
+// The pages name tree drafters (wispaper Q&A on block-diffusion decode
+// failures, section "Why is a fixed block size a failure mode in
+// production?": Bastion's budget-aware draft trees; its source list: D2SD's
+// confidence-guided prefix trees) but give no rule for verifying several
+// candidates.  The rule here is multi-round speculative sampling (Miao et al.,
+// SpecInfer, ASPLOS 2024): the children of a node were drawn independently
+// from the drafter's distribution q of that position (a block drafter's
+// position-wise marginal: dense draft row depth(u) of the request) and are
+// tested in turn against the current target r, starting from r = p (the
+// node's target row); a rejection replaces r by norm(max(0, r - q)); when
+// every child fails the token is drawn from that residual, and at a leaf a
+// bonus token from p.  Rejection correction keeps the target distribution
+// ("Pith review of DBLAST", "Assumptions & free parameters").
+//
+// After k rejections at a node the target is max(0, p - c_k q) / Z_k with
+// c_1 = 1, c_{k+1} = c_k + Z_k and Z_k = sum_v max(0, p_v - c_k q_v): one
+// scalar per rejection instead of a vector (a residual emptied by rounding
+// resets the target to p, as the block rule does: c_k = 0, Z_k = 1).  The c_k
+// do not depend on the walk's random tests, so the masses Z_k of every node
+// are formed beforehand, one launch per k, over blocks of (node, chunk of the
+// rows); one wave per request then walks the tree, and the token is drawn by
+// the block draw's sums and pick with the draft row scaled by c (its
+// log-normaliser lowered by ln c).
+//
+// Launches: k_tree_prep (a block per request: depths, child counts, checks),
+// k_tree_mass for k = 1 .. max_kids - 1, k_tree_walk (a wave per request), and
+// the record draw (sums, pick) of sv_sample.hip.
+#include <math.h>
+
+#include "sv_device.hpp"
+#include "sv_draw.hpp"
+#include "sv_host.hpp"
+
+namespace sv {
+
+constexpr int kTreeNT = 256;
+constexpr int kTreeMaxKids = 16;    // children tested per node
+constexpr int kTreeMaxNodes = 1024; // nodes of one request (staged in LDS by the walk)
+
+struct TreeNode {
+  int32_t depth, kids, req, valid;
+};
+
+struct TreeArgs {
+  const void* tgt;
+  int dtype;
+  int64_t tgt_ld;
+  int V;
+  const int32_t* node_off;
+  const int32_t* parent;
+  const int32_t* token;
+  int R, b, max_nodes, max_kids, S;
+  const float* T;
+  const int32_t* row_argmax;
+  const float* row_cut;
+  const double* row_kept;
+  const void* draft;
+  int ddtype;
+  int64_t draft_ld;
+  const int32_t* dargmax;
+  const double* dlse;
+  const uint64_t* seed;
+  int32_t* n_acc;
+  int32_t* path;
+  int32_t* stop_node;
+  double* p_out;
+  double* q_out;
+  float* u_out;
+  TreeNode* nodes;  // [max_nodes]
+  double* zpart;    // [max_nodes][max_kids - 1][S]: partial masses Z_k per chunk
+  DrawRec* rec;     // [R]
+  uint32_t* status;
+};
+
+__device__ __forceinline__ const char* tree_row(const void* base, int dtype, int64_t row, int64_t ld) {
+  return static_cast<const char*>(base) + static_cast<size_t>(row) * static_cast<size_t>(ld) * (dtype == SV_BF16 ? 2 : 4);
+}
+
+// Whether request r's node range is usable: n0 >= 0, 1 <= N <= kTreeMaxNodes,
+// inside the node count node_off[R] and the capacity max_nodes.
+__device__ __forceinline__ bool tree_range_ok(const TreeArgs& a, int r, int& n0, int& N) {
+  n0 = a.node_off[r];
+  N = a.node_off[r + 1] - n0;
+  const long long end = static_cast<long long>(n0) + N;
+  return n0 >= 0 && N >= 1 && N <= kTreeMaxNodes && end <= a.max_nodes && end <= a.node_off[a.R];
+}
+
+// Whether a node record is usable by request r: written by r's checks, with
+// depth and child count in range (a node with children lies above depth b).
+// Records of requests whose offsets overlap (malformed node_off) or left from
+// an earlier call fail it, so no index below is taken from unchecked data.
+__device__ __forceinline__ bool tree_node_ok(const TreeArgs& a, const TreeNode& nd, int r) {
+  return nd.valid == 1 && nd.req == r && nd.depth >= 0 && nd.depth <= a.b && nd.kids >= 0 &&
+         nd.kids <= a.max_kids && (nd.kids == 0 || nd.depth < a.b);
+}
+
+// Depths (by climbing the parents: at most b + 1 steps) and child counts of
+// request r's nodes, and the checks: the root's parent is -1, every other
+// parent precedes its child, depth <= b, at most max_kids children.
+__global__ __launch_bounds__(kTreeNT) void k_tree_prep(TreeArgs a) {
+  __shared__ int kids[kTreeMaxNodes];
+  __shared__ int bad;
+  const int r = blockIdx.x, tid = threadIdx.x;
+  int n0, N;
+  const bool range = tree_range_ok(a, r, n0, N);
+  if (!range) {
+    if (tid == 0) raise_status(a.status, SV_ST_BAD_TREE);
+    return;
+  }
+  if (tid == 0) bad = 0;
+  for (int j = tid; j < N; j += kTreeNT) kids[j] = 0;
+  __syncthreads();
+  const int32_t* par = a.parent + n0;
+  for (int j = tid; j < N; j += kTreeNT) {
+    const int pj = par[j];
+    if (j == 0 ? pj != -1 : (pj < 0 || pj >= j)) {
+      bad = 1;
+      continue;
+    }
+    if (j > 0) atomicAdd(&kids[pj], 1);
+  }
+  __syncthreads();
+  if (bad) {  // climbing a malformed tree could loop; every node is marked unusable
+    for (int j = tid; j < N; j += kTreeNT) a.nodes[n0 + j] = TreeNode{0, 0, r, 0};
+    if (tid == 0) raise_status(a.status, SV_ST_BAD_TREE);
+    return;
+  }
+  for (int j = tid; j < N; j += kTreeNT) {
+    int d = 0, u = j;
+    while (u > 0 && d <= a.b) {  // parents precede children, so this ends
+      u = par[u];
+      ++d;
+    }
+    if (d > a.b || kids[j] > a.max_kids) bad = 1;
+    a.nodes[n0 + j] = TreeNode{d, kids[j], r, 1};
+  }
+  __syncthreads();
+  if (bad) {
+    for (int j = tid; j < N; j += kTreeNT) a.nodes[n0 + j].valid = 0;
+    if (tid == 0) raise_status(a.status, SV_ST_BAD_TREE);
+  }
+}
+
+// c_k of node g from the masses of the passes before k (lanes sum the partials).
+// Returns c_k; the masses Z_1 .. Z_{k-1} are those of the earlier passes.
+__device__ __forceinline__ double tree_c(const TreeArgs& a, int g, int k, double* red) {
+  double c = 1.0;  // c_1
+  for (int m = 1; m < k; ++m) {
+    const double* zp = a.zpart + (static_cast<size_t>(g) * (a.max_kids - 1) + (m - 1)) * a.S;
+    double part = 0.0;
+    for (int s = threadIdx.x; s < a.S; s += kTreeNT) part += zp[s];
+    const double Z = block_sum_f64<kTreeNT>(part, red);
+    c = Z > 0.0 ? c + Z : 1.0;  // emptied by rounding: the target resets to p (c = 0, Z = 1)
+  }
+  return c;
+}
+
+// Pass k: for every node with more than k children, the partial masses over
+// chunk ch of sum_v max(0, p_v - c_k q_v) (p: the node's target row with its
+// cut; q: the draft row of the node's depth).  Greedy requests (T = 0) need
+// no masses.
+template <int DT, int DDT>
+__global__ __launch_bounds__(kTreeNT) void k_tree_mass(TreeArgs a, int k) {
+  __shared__ double etab[kExpTab];
+  __shared__ double red[kTreeNT / kWave];
+  const int g = blockIdx.x / a.S, ch = blockIdx.x % a.S;
+  if (g >= a.node_off[a.R]) return;
+  const TreeNode nd = a.nodes[g];
+  if (nd.req < 0 || nd.req >= a.R || !tree_node_ok(a, nd, nd.req) || nd.kids <= k) return;
+  const int r = nd.req;
+  const float T = a.T[r];
+  if (!(T > 0.0f)) return;
+  exp_table_init(etab);
+  __syncthreads();
+  const double c = tree_c(a, g, k, red);
+  const double invT = 1.0 / static_cast<double>(T);
+  const float cut = a.row_cut[g];
+  const double kept = a.row_kept[g];
+  const int64_t drow = static_cast<int64_t>(r) * a.b + nd.depth;
+  const double dl = a.dlse[drow] - log(c);  // c q = exp(d / T - (lse - ln c))
+  const char* tp = tree_row(a.tgt, DT, g, a.tgt_ld);
+  const char* dp = tree_row(a.draft, DDT, drow, a.draft_ld);
+  // this block's 4096 values: 8 per thread, in two 8-value groups
+  const int V = a.V;
+  double part = 0.0;
+  for (int e = ch * 4096 + threadIdx.x; e < min(V, (ch + 1) * 4096); e += kTreeNT) {
+    const float l = load_val<DT>(tp, e);
+    const double p = l >= cut ? exp_tab(static_cast<double>(l) * invT - kept, etab) : 0.0;
+    const double w = p - exp_tab(static_cast<double>(load_val<DDT>(dp, e)) * invT - dl, etab);
+    part += w > 0.0 ? w : 0.0;
+  }
+  const double tot = block_sum_f64<kTreeNT>(part, red);
+  if (threadIdx.x == 0) a.zpart[(static_cast<size_t>(g) * (a.max_kids - 1) + (k - 1)) * a.S + ch] = tot;
+}
+
+// The walk, one wave per request: from the root, each node's children in
+// index order are tested against the current target; an acceptance moves to
+// the child, and the walk ends at a leaf (bonus draw from its p) or when every
+// child fails (residual draw).  The test of node j takes Philox word 0 at
+// counter (j - 1, r, 0, 0); the draw record's n is the stopping node, whose
+// word 1 the pick takes.
+template <int DT, int DDT>
+__global__ __launch_bounds__(kWave) void k_tree_walk(TreeArgs a) {
+  __shared__ int par[kTreeMaxNodes];
+  __shared__ double etab[kExpTab];
+  __shared__ double Zs[kTreeMaxKids];
+  const int r = blockIdx.x, lane = threadIdx.x;
+  int n0, N;
+  DrawRec& rec = a.rec[r];
+  exp_table_init(etab);
+  const bool range = tree_range_ok(a, r, n0, N);
+  const bool ok = range && a.nodes[n0].valid;
+  if (!ok) {
+    if (lane == 0) {
+      a.n_acc[r] = 0;
+      a.stop_node[r] = 0;
+      rec.mode = kDrawNone;
+    }
+    return;
+  }
+  for (int j = lane; j < N; j += kWave) par[j] = a.parent[n0 + j];
+  __syncwarp();
+  const float T = a.T[r];
+  const bool greedy = T == 0.0f;
+  const double invT = 1.0 / static_cast<double>(T);
+  const uint64_t seed = *a.seed;
+  const int V = a.V;
+  int u = 0, n = 0;
+  double cdraw = 0.0;  // > 0: residual draw at node u with draft row scale cdraw
+  bool leaf = false;
+  for (;;) {
+    const int g = n0 + u;
+    const TreeNode nd = a.nodes[g];
+    if (!tree_node_ok(a, nd, r) || n >= a.b + (nd.kids == 0 ? 1 : 0)) {  // overlapping or stale records
+      if (lane == 0) {
+        raise_status(a.status, SV_ST_BAD_TREE);
+        a.n_acc[r] = 0;
+        a.stop_node[r] = 0;
+        rec.mode = kDrawNone;
+      }
+      return;
+    }
+    const float cut = a.row_cut[g];
+    const double kept = a.row_kept[g];
+    const int am = a.row_argmax[g];
+    if (nd.kids == 0) {
+      leaf = true;
+      break;
+    }
+    const int64_t drow = static_cast<int64_t>(r) * a.b + nd.depth;
+    const double dlse = greedy ? 0.0 : a.dlse[drow];
+    const int dam = greedy ? a.dargmax[drow] : 0;
+    // the masses Z_1 .. Z_{kids-1} of this node (lane-parallel sums of the partials)
+    for (int m = 1; m < nd.kids; ++m) {
+      const double* zp = a.zpart + (static_cast<size_t>(g) * (a.max_kids - 1) + (m - 1)) * a.S;
+      double part = 0.0;
+      if (!greedy)
+        for (int s = lane; s < a.S; s += kWave) part += zp[s];
+      const double tot = wave_sum_f64(part);
+      if (lane == 0) Zs[m] = tot;
+    }
+    __syncwarp();
+    double c = 0.0, Z = 1.0;  // the current target: max(0, p - c q) / Z
+    int m = 0, next = -1;
+    const char* tp = tree_row(a.tgt, DT, g, a.tgt_ld);
+    const char* dp = tree_row(a.draft, DDT, drow, a.draft_ld);
+    for (int j0 = u + 1; j0 < N && next < 0 && m < nd.kids; j0 += kWave) {
+      const int j = j0 + lane;
+      uint64_t mine = __ballot(j < N && par[min(j, N - 1)] == u);
+      while (mine && next < 0) {
+        const int jl = __ffsll(static_cast<long long>(mine)) - 1;
+        mine &= mine - 1;
+        const int jc = j0 + jl;  // the next child in index order
+        ++m;
+        const int x = a.token[n0 + jc];
+        const bool xok = x >= 0 && x < V;
+        double p = 0.0, q = 0.0;
+        if (xok) {
+          if (greedy) {  // p and q one-hot; every residual is p again, so each child is tested against p
+            p = x == am ? 1.0 : 0.0;
+            q = x == dam ? 1.0 : 0.0;
+          } else {
+            const float l = load_val<DT>(tp, x);
+            const double p0 = l >= cut ? exp_tab(static_cast<double>(l) * invT - kept, etab) : 0.0;
+            q = exp_tab(static_cast<double>(load_val<DDT>(dp, x)) * invT - dlse, etab);
+            const double w = p0 - c * q;
+            p = c == 0.0 ? p0 : (w > 0.0 ? w / Z : 0.0);
+          }
+        } else if (lane == 0) {
+          raise_status(a.status, SV_ST_BAD_TOKEN);
+        }
+        const double uu = u24(philox_at(seed, static_cast<uint32_t>(jc - 1), static_cast<uint32_t>(r)).x);
+        const bool accept = q > 0.0 ? uu < p / q : p > 0.0;
+        if (lane == 0) {
+          if (a.p_out) a.p_out[n0 + jc] = p;
+          if (a.q_out) a.q_out[n0 + jc] = q;
+          if (a.u_out) a.u_out[n0 + jc] = static_cast<float>(uu);
+        }
+        if (accept) {
+          next = jc;
+        } else if (!greedy) {
+          // the next target: c_{m+1} = c_m + Z_m (c_1 = 1); a mass emptied by rounding resets it to p
+          c = c == 0.0 ? 1.0 : c + Z;
+          Z = m < nd.kids ? Zs[m] : 0.0;
+          if (m < nd.kids && !(Z > 0.0)) {
+            c = 0.0;
+            Z = 1.0;
+          }
+        }
+      }
+    }
+    if (next < 0) {  // every child failed: the residual at u
+      cdraw = greedy ? 1.0 : c;
+      break;
+    }
+    if (lane == 0) a.path[static_cast<size_t>(r) * a.b + n] = next;
+    ++n;
+    u = next;
+  }
+  if (lane == 0) {
+    a.n_acc[r] = n;
+    a.stop_node[r] = u;
+    const int g = n0 + u;
+    const TreeNode nd = a.nodes[g];
+    rec.n = u;  // the pick's uniform: word 1 at counter (u, r, 0, 0)
+    rec.bonus = leaf ? 1 : 0;
+    rec.token = a.row_argmax[g];
+    rec.ncorr = 0;
+    rec.trow = g;
+    rec.drow = static_cast<int64_t>(r) * a.b + (leaf ? 0 : nd.depth);
+    rec.cut = a.row_cut[g];
+    rec.invT = invT;
+    rec.kept = a.row_kept[g];
+    rec.invTb = 0.0;
+    if (greedy) {
+      rec.mode = kDrawGreedy;
+      rec.dlse = 0.0;
+    } else if (leaf || !(cdraw > 0.0)) {
+      rec.mode = kDrawP;
+      rec.dlse = 0.0;
+    } else {
+      rec.mode = kDrawResidual;
+      rec.dlse = a.dlse[rec.drow] - log(cdraw);
+    }
+  }
+}
+
+size_t tree_ws_needed(int max_nodes, int max_kids, int V) {
+  const size_t S = static_cast<size_t>(res_chunks(V));
+  return align256(sizeof(TreeNode) * static_cast<size_t>(max_nodes)) +
+         align256(sizeof(double) * static_cast<size_t>(max_nodes) * (max_kids > 1 ? max_kids - 1 : 1) * S);
+}
+
+}  // namespace sv
+
+using namespace sv;
+
+extern "C" int32_t sv_tree_workspace_bytes(int32_t max_nodes, int32_t max_kids, int32_t V, size_t* out_bytes) {
+  if (!out_bytes || max_nodes < 1 || max_kids < 1 || max_kids > kTreeMaxKids || V < 1) return SV_ERR_ARG;
+  *out_bytes = tree_ws_needed(max_nodes, max_kids, V);
+  return SV_OK;
+}
+
+template <int DT, int DDT>
+static int32_t launch_tree(const TreeArgs& t, hipStream_t s) {
+  for (int k = 1; k < t.max_kids; ++k) {
+    hipLaunchKernelGGL((k_tree_mass<DT, DDT>), dim3(static_cast<unsigned>(t.max_nodes) * t.S), dim3(kTreeNT), 0, s,
+                       t, k);
+    if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
+  }
+  hipLaunchKernelGGL((k_tree_walk<DT, DDT>), dim3(t.R), dim3(kWave), 0, s, t);
+  return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
+}
+
+extern "C" int32_t sv_tree_verify(const void* tgt_logits, int32_t dtype, int64_t tgt_ld, int32_t V,
+                                  const int32_t* node_off, const int32_t* parent, const int32_t* token, int32_t R,
+                                  int32_t b, int32_t max_nodes, int32_t max_kids, const float* temperature,
+                                  const int32_t* row_argmax, const float* row_cut, const double* row_kept_lse,
+                                  const void* draft_logits, int32_t draft_dtype, int64_t draft_ld,
+                                  const int32_t* draft_argmax, const double* draft_lse, const uint64_t* seed,
+                                  int32_t* n_acc, int32_t* path, int32_t* stop_node, int32_t* token_out,
+                                  int32_t* is_bonus, double* p_out, double* q_out, float* u_out, void* ws,
+                                  size_t ws_bytes, void* tree_ws, size_t tree_ws_bytes, void* stream) {
+  if (!tgt_logits || !node_off || !parent || !token || !temperature || !row_argmax || !row_cut || !row_kept_lse)
+    return SV_ERR_ARG;
+  if (!draft_logits || !draft_argmax || !draft_lse || !seed || !n_acc || !path || !stop_node || !token_out ||
+      !is_bonus || !ws || !tree_ws)
+    return SV_ERR_ARG;
+  if (R < 1 || b < 1 || b > 64 || V < 1 || max_nodes < R || max_kids < 1 || max_kids > kTreeMaxKids) return SV_ERR_ARG;
+  if (tgt_ld < V || draft_ld < V) return SV_ERR_ARG;
+  if ((dtype != SV_F32 && dtype != SV_BF16) || (draft_dtype != SV_F32 && draft_dtype != SV_BF16)) return SV_ERR_ARG;
+  if (!rows_aligned(tgt_logits, dtype, tgt_ld) || !rows_aligned(draft_logits, draft_dtype, draft_ld)) return SV_ERR_ARG;
+  if (static_cast<long long>(max_nodes) * res_chunks(V) > 0x7FFFFFFFLL) return SV_ERR_ARG;
+  const WsLayout l = ws_layout(R, b, 0, V);
+  if (ws_bytes < l.total || tree_ws_bytes < tree_ws_needed(max_nodes, max_kids, V)) return SV_ERR_WORKSPACE;
+  TreeArgs t{};
+  t.tgt = tgt_logits; t.dtype = dtype; t.tgt_ld = tgt_ld; t.V = V;
+  t.node_off = node_off; t.parent = parent; t.token = token;
+  t.R = R; t.b = b; t.max_nodes = max_nodes; t.max_kids = max_kids; t.S = res_chunks(V);
+  t.T = temperature; t.row_argmax = row_argmax; t.row_cut = row_cut; t.row_kept = row_kept_lse;
+  t.draft = draft_logits; t.ddtype = draft_dtype; t.draft_ld = draft_ld; t.dargmax = draft_argmax; t.dlse = draft_lse;
+  t.seed = seed; t.n_acc = n_acc; t.path = path; t.stop_node = stop_node;
+  t.p_out = p_out; t.q_out = q_out; t.u_out = u_out;
+  t.nodes = static_cast<TreeNode*>(tree_ws);
+  t.zpart = reinterpret_cast<double*>(static_cast<char*>(tree_ws) + align256(sizeof(TreeNode) * static_cast<size_t>(max_nodes)));
+  t.rec = reinterpret_cast<DrawRec*>(static_cast<char*>(ws) + l.rec);
+  t.status = status_word(ws);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(k_tree_prep, dim3(R), dim3(kTreeNT), 0, s, t);
+  if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
+  const bool t16 = dtype == SV_BF16, d16 = draft_dtype == SV_BF16;
+  const int32_t st = t16 ? (d16 ? launch_tree<SV_BF16, SV_BF16>(t, s) : launch_tree<SV_BF16, SV_F32>(t, s))
+                         : (d16 ? launch_tree<SV_F32, SV_BF16>(t, s) : launch_tree<SV_F32, SV_F32>(t, s));
+  if (st != SV_OK) return st;
+  // the draw from the walk's records (dense weights max(0, p - c q))
+  SampleArgs a{};
+  a.tgt = tgt_logits; a.dtype = dtype; a.tgt_ld = tgt_ld; a.V = V; a.R = R; a.b = b; a.T = temperature;
+  a.q_mode = SV_Q_DENSE; a.draft = draft_logits; a.ddtype = draft_dtype; a.draft_ld = draft_ld; a.seed = seed;
+  a.token = token_out; a.is_bonus = is_bonus; a.status = status_word(ws);
+  a.rec = t.rec;
+  a.sub = reinterpret_cast<double*>(static_cast<char*>(ws) + l.sub);
+  a.NSUB = sub_chunks(V);
+  a.S = res_chunks(V);
+  return launch_record_draw(a, s);
+}

@@ -91,6 +91,7 @@ extern "C" {
 #define SV_ST_BAD_BUDGET 0x080u      /* DVL budget < 0 */
 #define SV_ST_BAD_NACC 0x100u        /* n_acc outside [0, L_r] */
 #define SV_ST_BAD_BLOCK 0x200u       /* DVL block length outside [0, b] (clamped) */
+#define SV_ST_BAD_TREE 0x400u        /* a draft tree whose parents, depths, node count or child counts are out of range */
 
 /* ---------------------------------------------------------------- workspace */
 
@@ -358,6 +359,67 @@ int32_t sv_accept_sample(const void* tgt_logits, int32_t dtype, int64_t tgt_ld, 
                          double* q_at_draft, const uint64_t* seed, int32_t* n_acc, int32_t* token,
                          int32_t* is_bonus, double* p_out, double* q_out, float* u_out, void* ws,
                          size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- tree verification */
+
+/* Bytes of tree workspace for up to max_nodes tree nodes (all requests), at
+ * most max_kids children per node and vocabulary V.  Host-only. */
+int32_t sv_tree_workspace_bytes(int32_t max_nodes, int32_t max_kids, int32_t V, size_t* out_bytes);
+
+/* sv_tree_verify: verification of a draft TREE per request [wispaper Q&A on
+ * block-diffusion decode failures, section "Why is a fixed block size a
+ * failure mode in production?": tree drafters (Bastion; D2SD's prefix trees);
+ * rule: multi-round speculative sampling (Miao et al., SpecInfer, ASPLOS
+ * 2024), whose rejection correction keeps the target distribution, DBLast
+ * review "Assumptions & free parameters"].
+ *   node_off[R+1]  exclusive scan of the node counts: request r's nodes are
+ *                  k = node_off[r] + j, j = 0 .. N_r - 1 (1 <= N_r <= 1024,
+ *                  node_off[R] <= max_nodes); node j = 0 is the root (the
+ *                  context so far)
+ *   parent[k]      parent of node j, as a local index: -1 for the root, in
+ *                  [0, j) otherwise; depth(j) <= b
+ *   token[k]       the draft token of node j >= 1
+ *   Target rows: row k of tgt_logits is p(. | context, node j's path), with
+ *   its statistics row_argmax / row_cut / row_kept_lse[k] (sv_topp_threshold
+ *   with row_off = node_off, row_stride 0).
+ *   Drafter: the children of a node at depth d were drawn independently from
+ *   q_d = softmax(row r*b + d of draft_logits / T_r) (one-hot at its argmax at
+ *   T_r = 0), with draft_argmax / draft_lse[r*b + d] (sv_softmax_stats with
+ *   row_off = (0, b, 2b, ...), row_stride = b).
+ *   Rule, from the root: node u's children, in index order, are tested
+ *   against the current target t (first t = p_u): child j with token x is
+ *   accepted iff u_j < t(x) / q(x) (q = 0: iff t(x) > 0), u_j from word 0 of
+ *   Philox at counter (j - 1, r, 0, 0); on acceptance the walk moves to j
+ *   with t = p_j; on rejection t becomes norm(max(0, t - q)) (p_u if that is
+ *   empty from rounding); if every child fails, the token is drawn from
+ *   norm(max(0, t - q)) of the last rejection; at a node without children a
+ *   bonus token is drawn from its p; draws as sv_residual_sample, with word 1
+ *   at counter (s, r, 0, 0), s the stopping node.  A chain (parent j - 1) is
+ *   exactly sv_accept + sv_residual_sample.  At most max_kids (<= 16)
+ *   children per node.
+ *   n_acc[R], path[R*b] (the accepted nodes' local indices in order),
+ *   stop_node[R], token_out[R], is_bonus[R]  out
+ *   p_out, q_out (double), u_out (float)  optional, [max_nodes] per node: the
+ *                  current target's and the draft's probability of the node's
+ *                  token and its uniform, for the nodes whose test was reached
+ *   ws             workspace of sv_workspace_bytes(R, b, 0, V) (status word,
+ *                  draw records, sub-chunk sums)
+ *   tree_ws        workspace of sv_tree_workspace_bytes(max_nodes, max_kids, V)
+ * Malformed trees (a parent not before its child, depth > b, more than
+ * max_kids children, node counts out of range) set SV_ST_BAD_TREE; their
+ * request gets n_acc = 0 and no token.  Launches: one block per request
+ * (depths, checks), max_kids - 1 passes over (node, 4096-value chunk) that
+ * form the residual masses sum_v max(0, p - c q), one wave per request (the
+ * walk), then the draw's sums and pick. */
+int32_t sv_tree_verify(const void* tgt_logits, int32_t dtype, int64_t tgt_ld, int32_t V, const int32_t* node_off,
+                       const int32_t* parent, const int32_t* token, int32_t R, int32_t b, int32_t max_nodes,
+                       int32_t max_kids, const float* temperature, const int32_t* row_argmax,
+                       const float* row_cut, const double* row_kept_lse, const void* draft_logits,
+                       int32_t draft_dtype, int64_t draft_ld, const int32_t* draft_argmax,
+                       const double* draft_lse, const uint64_t* seed, int32_t* n_acc, int32_t* path,
+                       int32_t* stop_node, int32_t* token_out, int32_t* is_bonus, double* p_out,
+                       double* q_out, float* u_out, void* ws, size_t ws_bytes, void* tree_ws,
+                       size_t tree_ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------- Philox (test export) */
 

@@ -86,6 +86,25 @@ class _StepOut(C.Structure):
     ]
 
 
+class _TreeIn(C.Structure):
+    _fields_ = [
+        ("R", C.c_int32), ("b", C.c_int32), ("V", C.c_int32), ("dtype", C.c_int32),
+        ("node_off", C.c_void_p), ("parent", C.c_void_p), ("token", C.c_void_p),
+        ("tgt", C.c_void_p), ("tgt_ld", C.c_int64), ("tgt_row", C.c_void_p),
+        ("T", C.c_void_p), ("top_p", C.c_void_p),
+        ("draft", C.c_void_p), ("draft_ld", C.c_int64), ("draft_row0", C.c_void_p),
+        ("seed", C.c_uint64),
+    ]
+
+
+class _TreeOut(C.Structure):
+    _fields_ = [
+        ("n_acc", C.c_void_p), ("path", C.c_void_p), ("stop_node", C.c_void_p), ("token", C.c_void_p),
+        ("is_bonus", C.c_void_p), ("sample_margin", C.c_void_p), ("u_res", C.c_void_p),
+        ("u_acc", C.c_void_p), ("p_x", C.c_void_p), ("q_x", C.c_void_p), ("acc_margin", C.c_void_p),
+    ]
+
+
 def _declare(L):
     vp, i32, i64, u64, dbl = C.c_void_p, C.c_int32, C.c_int64, C.c_uint64, C.c_double
     L.orc_philox4x32_10.argtypes = [vp, vp, vp]
@@ -108,6 +127,8 @@ def _declare(L):
     L.orc_argmax_rows.restype = None
     L.orc_step.argtypes = [C.POINTER(_StepIn), C.POINTER(_StepOut)]
     L.orc_step.restype = C.c_int
+    L.orc_tree_step.argtypes = [C.POINTER(_TreeIn), C.POINTER(_TreeOut)]
+    L.orc_tree_step.restype = C.c_int
     L.orc_num_threads.argtypes = []
     L.orc_num_threads.restype = C.c_int
     L.orc_set_num_threads.argtypes = [C.c_int]
@@ -274,4 +295,47 @@ def step(*, tgt, tgt_row0, L, T, x, seed, top_p=None, draft=None, draft_row0=Non
     if rc != 0:
         raise ValueError(f"orc_step rejected its input (code {rc})")
     del keep
+    return out
+
+
+# ---------------------------------------------------------------- tree verification
+def tree_step(*, tgt, tgt_row, node_off, parent, token, T, b, seed, draft, draft_row0, top_p=None) -> dict:
+    """Tree verification of R requests (orc_tree_step).
+
+    node_off: [R+1] exclusive scan of the node counts; parent, token, tgt_row:
+    one entry per node (request r's nodes at node_off[r] + j, j = 0 the root,
+    parent -1); tgt: [rows, V] target rows (row tgt_row[k] for node k); draft:
+    [rows, V] with the children of a depth-d node of request r drawn from row
+    draft_row0[r] + d.  Per-node outputs are NaN for nodes never tested."""
+    tgt = np.ascontiguousarray(tgt)
+    dt = _rows_dtype(tgt)
+    draft = np.ascontiguousarray(draft)
+    assert _rows_dtype(draft) == dt
+    node_off = _c(node_off, np.int32)
+    R = len(node_off) - 1
+    n = int(node_off[-1])
+    par, tok = _c(parent, np.int32), _c(token, np.int32)
+    trow, d0 = _c(tgt_row, np.int64), _c(draft_row0, np.int64)
+    Tr = _c(np.broadcast_to(np.asarray(T, np.float32), (R,)), np.float32)
+    tp = None if top_p is None else _c(np.broadcast_to(np.asarray(top_p, np.float32), (R,)), np.float32)
+    ti = _TreeIn()
+    ti.R, ti.b, ti.V, ti.dtype = R, int(b), tgt.shape[-1], dt
+    ti.node_off, ti.parent, ti.token = _ptr(node_off), _ptr(par), _ptr(tok)
+    ti.tgt, ti.tgt_ld, ti.tgt_row = _ptr(tgt), tgt.shape[-1], _ptr(trow)
+    ti.T, ti.top_p = _ptr(Tr), _ptr(tp)
+    ti.draft, ti.draft_ld, ti.draft_row0 = _ptr(draft), draft.shape[-1], _ptr(d0)
+    ti.seed = int(seed) & (2**64 - 1)
+    out = {"n_acc": np.zeros(R, np.int32), "path": np.full((R, int(b)), -1, np.int32),
+           "stop_node": np.zeros(R, np.int32), "token": np.zeros(R, np.int32), "is_bonus": np.zeros(R, np.int32),
+           "sample_margin": np.zeros(R), "u_res": np.zeros(R),
+           "u_acc": np.full(n, np.nan), "p_x": np.full(n, np.nan), "q_x": np.full(n, np.nan),
+           "acc_margin": np.full(n, np.nan)}
+    to = _TreeOut()
+    for k in out:
+        setattr(to, k, _ptr(out[k]))
+    keep = [tgt, draft, node_off, par, tok, trow, d0, Tr, tp]
+    rc = lib().orc_tree_step(C.byref(ti), C.byref(to))
+    del keep
+    if rc != 0:
+        raise ValueError(f"orc_tree_step rejected its input (code {rc})")
     return out

@@ -580,3 +580,157 @@ int orc_step(const orc_step_in_t* in, const orc_step_out_t* out) {
   }
   return err;
 }
+
+
+/* ------------------------------------------------------------------------ */
+/* Tree verification.  The pages name tree drafters (wispaper Q&A on         */
+/* block-diffusion decode failures, section "Why is a fixed block size a      */
+/* failure mode in production?": Bastion's budget-aware draft trees; its      */
+/* source list: D2SD's confidence-guided prefix trees) but give no rule for   */
+/* verifying several candidates.  Reading: multi-round speculative sampling   */
+/* (Miao et al., SpecInfer, ASPLOS 2024) -- the candidates at a node were     */
+/* drawn independently from the drafter's distribution q of that position,    */
+/* and are tested in turn:                                                    */
+/*   start at the root with the current target r = p (the node's target);   */
+/*   child j with token x: accept iff u_j < r(x) / q(x) (q = 0: iff r(x) > 0); */
+/*   on acceptance move to j and start again with p of node j;                */
+/*   on rejection replace r by norm(max(0, r - q)) and try the next child;    */
+/*   when every child is rejected, draw the token from that residual;         */
+/*   at a node without children, draw a bonus token from its p.              */
+/* Each round is one speculative-sampling step between r and q, so the        */
+/* emitted token follows p whatever q is ("Pith review of DBLAST",            */
+/* "Assumptions & free parameters": rejection correction keeps the target).  */
+/* Uniforms: the test of node j takes word 0 at counter (j - 1, r, 0, 0), the */
+/* draw at the stopping node s word 1 at (s, r, 0, 0) -- for a chain          */
+/* (p(j) = j - 1) the counters and arithmetic of orc_step.  A residual that   */
+/* rounding leaves empty is replaced by p (as in orc_step).                  */
+/* ------------------------------------------------------------------------ */
+int orc_tree_step(const orc_tree_in_t* in, const orc_tree_out_t* out) {
+  const int32_t R = in->R, b = in->b, V = in->V;
+  if (R < 0 || b < 1 || V < 1 || !in->node_off || in->node_off[0] != 0) return 1;
+  for (int32_t r = 0; r < R; ++r) {
+    const int32_t n0 = in->node_off[r], N = in->node_off[r + 1] - n0;
+    if (N < 1 || in->parent[n0] != -1) return 2;
+    for (int32_t j = 1; j < N; ++j) {
+      const int32_t pj = in->parent[n0 + j], tj = in->token[n0 + j];
+      if (pj < 0 || pj >= j || tj < 0 || tj >= V) return 2;
+    }
+  }
+  int err = 0;
+#pragma omp parallel
+  {
+    double* pcur = (double*)malloc(sizeof(double) * (size_t)V);
+    double* wbuf = (double*)malloc(sizeof(double) * (size_t)V);
+#pragma omp for schedule(dynamic, 64)
+    for (int32_t r = 0; r < R; ++r) {
+      const int32_t n0 = in->node_off[r], N = in->node_off[r + 1] - n0;
+      const int32_t* par = in->parent + n0;
+      const int32_t* tok = in->token + n0;
+      const double T = (double)in->T[r];
+      const double tp = in->top_p ? (double)in->top_p[r] : 1.0;
+      int32_t* depth = (int32_t*)malloc(sizeof(int32_t) * (size_t)N);
+      depth[0] = 0;
+      int bad = 0;
+      for (int32_t j = 1; j < N; ++j) {
+        depth[j] = depth[par[j]] + 1;
+        if (depth[j] > b) bad = 1;
+      }
+      if (bad) {
+        free(depth);
+#pragma omp atomic write
+        err = 3;
+        continue;
+      }
+      int32_t u = 0, n = 0;
+      for (;;) {
+        const void* trow = orc_row(in->tgt, in->dtype, in->tgt_row[n0 + u], in->tgt_ld);
+        orc_row_stats_t st;
+        orc_row_stats(trow, in->dtype, V, T, tp, &st);
+        int32_t first = -1;
+        for (int32_t j = u + 1; j < N; ++j)
+          if (par[j] == u) {
+            first = j;
+            break;
+          }
+        uint32_t w4[4];
+        if (first < 0) { /* a leaf: bonus token from p */
+          for (int32_t v = 0; v < V; ++v) wbuf[v] = orc_p_of(trow, in->dtype, v, T, &st);
+          orc_words_at(in->seed, r, u, w4);
+          double sm;
+          out->token[r] = orc_inverse_cdf(wbuf, V, orc_u24(w4[1]), &sm);
+          out->is_bonus[r] = 1;
+          if (out->sample_margin) out->sample_margin[r] = sm;
+          if (out->u_res) out->u_res[r] = orc_u24(w4[1]);
+          break;
+        }
+        /* the drafter's distribution of this position: draft row depth(u) */
+        const void* drow = orc_row(in->draft, in->dtype, in->draft_row0[r] + depth[u], in->draft_ld);
+        orc_row_stats_t dst;
+        orc_row_stats(drow, in->dtype, V, T, 1.0, &dst);
+#define ORC_TREE_Q(v) (T == 0.0 ? ((v) == dst.argmax ? 1.0 : 0.0) : exp(orc_val(drow, in->dtype, (v)) / T - dst.lse))
+        int have_res = 0; /* 0: the current target r is p itself */
+        double W = 0.0;
+        int32_t acc = -1;
+        for (int32_t j = first; j < N; ++j) {
+          if (par[j] != u) continue;
+          const int32_t x = tok[j];
+          const double px = have_res ? pcur[x] : orc_p_of(trow, in->dtype, x, T, &st);
+          const double qx = ORC_TREE_Q(x);
+          orc_words_at(in->seed, r, j - 1, w4);
+          const double uu = orc_u24(w4[0]);
+          int accept;
+          double margin;
+          if (qx > 0.0) {
+            const double rho = px / qx;
+            accept = uu < rho;
+            margin = fabs(uu - fmin(1.0, rho));
+          } else {
+            accept = px > 0.0;
+            margin = accept ? 1.0 - uu : uu;
+          }
+          if (out->u_acc) out->u_acc[n0 + j] = uu;
+          if (out->p_x) out->p_x[n0 + j] = px;
+          if (out->q_x) out->q_x[n0 + j] = qx;
+          if (out->acc_margin) out->acc_margin[n0 + j] = margin;
+          if (accept) {
+            acc = j;
+            break;
+          }
+          /* rejected: the residual max(0, r - q), normalised for the next child */
+          W = 0.0;
+          for (int32_t v = 0; v < V; ++v) {
+            const double base = have_res ? pcur[v] : orc_p_of(trow, in->dtype, v, T, &st);
+            const double d = base - ORC_TREE_Q(v);
+            wbuf[v] = d > 0.0 ? d : 0.0;
+            W += wbuf[v];
+          }
+          for (int32_t v = 0; v < V; ++v) pcur[v] = W > 0.0 ? wbuf[v] / W : orc_p_of(trow, in->dtype, v, T, &st);
+          have_res = 1;
+        }
+#undef ORC_TREE_Q
+        if (acc >= 0) {
+          if (out->path) out->path[(size_t)r * b + n] = acc;
+          ++n;
+          u = acc;
+          continue;
+        }
+        /* every child rejected: the token from the last residual (from p if rounding emptied it) */
+        if (!(W > 0.0))
+          for (int32_t v = 0; v < V; ++v) wbuf[v] = orc_p_of(trow, in->dtype, v, T, &st);
+        orc_words_at(in->seed, r, u, w4);
+        double sm;
+        out->token[r] = orc_inverse_cdf(wbuf, V, orc_u24(w4[1]), &sm);
+        out->is_bonus[r] = 0;
+        if (out->sample_margin) out->sample_margin[r] = sm;
+        if (out->u_res) out->u_res[r] = orc_u24(w4[1]);
+        break;
+      }
+      out->n_acc[r] = n;
+      out->stop_node[r] = u;
+      free(depth);
+    }
+    free(pcur);
+    free(wbuf);
+  }
+  return err;
+}

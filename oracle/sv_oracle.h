@@ -143,6 +143,46 @@ typedef struct {
 /* Returns 0, or a nonzero code for malformed input. */
 int orc_step(const orc_step_in_t* in, const orc_step_out_t* out);
 
+/* ---- tree verification (multi-candidate speculative sampling) -------- */
+/* A request's draft is a tree: node 0 is the root (the context so far),
+ * node j >= 1 holds a draft token and a parent p(j) < j; the children of a
+ * node are tried in increasing index order.  The children of a node at depth
+ * d were drawn independently from the drafter's distribution of position
+ * d + 1 (a block drafter's position-wise marginal: dense draft row d). */
+typedef struct {
+  int32_t R, b, V;
+  int32_t dtype;             /* ORC_F32 / ORC_BF16 for both logit buffers */
+  const int32_t* node_off;   /* [R+1] exclusive scan: request r's nodes are node_off[r] .. node_off[r+1]-1 */
+  const int32_t* parent;     /* [node_off[R]] parent of node j (0-based within its request); -1 for the root */
+  const int32_t* token;      /* [node_off[R]] draft token of node j (the root's is unused) */
+  const void* tgt; int64_t tgt_ld;
+  const int64_t* tgt_row;    /* [node_off[R]] target row of node j: p(. | the context and node j's path) */
+  const float* T;            /* [R] */
+  const float* top_p;        /* [R] or NULL */
+  const void* draft; int64_t draft_ld;
+  const int64_t* draft_row0; /* [R] children of a node at depth d were drawn from row draft_row0[r] + d */
+  uint64_t seed;
+} orc_tree_in_t;
+
+typedef struct {
+  int32_t* n_acc;        /* [R] accepted nodes */
+  int32_t* path;         /* [R*b] the accepted nodes in order (first n_acc[r] entries) */
+  int32_t* stop_node;    /* [R] the last accepted node (0: none) */
+  int32_t* token;        /* [R] residual or bonus token */
+  int32_t* is_bonus;     /* [R] */
+  double* sample_margin; /* [R] */
+  double* u_res;         /* [R] */
+  /* per node ([node_off[R]]), written for the nodes whose test was reached */
+  double* u_acc;
+  double* p_x;           /* the current target's probability of the node's token */
+  double* q_x;           /* the draft's probability of it */
+  double* acc_margin;
+} orc_tree_out_t;
+
+/* Returns 0, or a nonzero code for malformed input (nothing is written then
+ * for the request concerned). */
+int orc_tree_step(const orc_tree_in_t* in, const orc_tree_out_t* out);
+
 int orc_num_threads(void);
 /* threads for the oracle's later parallel loops (OpenMP); n <= 0 is ignored */
 void orc_set_num_threads(int n);

@@ -232,3 +232,90 @@ def pack_target(w: Workload, L: np.ndarray) -> np.ndarray:
     """Target rows as the target forward would emit them for allocation L:
     request r contributes its first L[r] + 1 rows, requests in order."""
     return np.concatenate([w.tgt[r, : int(L[r]) + 1] for r in range(w.R)], axis=0)
+
+
+# ------------------------------------------------------------ draft trees
+@dataclasses.dataclass
+class TreeWorkload:
+    name: str
+    R: int
+    b: int                      # depth limit (draft positions)
+    V: int
+    dtype: str
+    max_kids: int               # most children of any node
+    node_off: np.ndarray        # [R+1] int32 exclusive scan of the node counts
+    parent: np.ndarray          # [n] int32 local parent index (-1 for each root)
+    token: np.ndarray           # [n] int32 draft token of each node (0 for the roots)
+    depth: np.ndarray           # [n] int32
+    tgt: np.ndarray             # [n, V] target row of every node (stored dtype)
+    draft: np.ndarray           # [R, b, V] the drafter's row per depth (stored dtype)
+    T: np.ndarray               # [R] float32
+    top_p: Optional[np.ndarray]  # [R] float32 or None
+    seed: int                   # verification seed
+
+
+def tree(name: str, *, R: int, b: int = 16, V: int = QWEN3_VOCAB, width: int = 4, nodes: int = 64,
+         dtype: str = "bf16", T=1.0, top_p: Optional[float] = None, shape: str = "random",
+         draft_sigma: float = 1.0, seed: int = 3000, vseed: int = 11, threads: Optional[int] = None) -> TreeWorkload:
+    """Draft trees per request (the budget-aware trees of tree drafters).
+
+    ``shape`` "random": a node budget N_r uniform on 1..``nodes``; nodes are
+    expanded breadth-first (so every parent precedes its children), the root
+    with 1..``width`` children and every other node with 0..``width``, within
+    depth b and the budget.  "chain": a chain of L_r uniform on 0..b draft
+    nodes.  "wide": the root alone with ``width`` children (the multi-candidate
+    case at its simplest).
+    Target row of a node at depth d: the request's Zipfian base for position d
+    plus N(0, 1) noise of the node's own (a target's rows depend on the path).
+    Drafter row d: that base plus N(0, ``draft_sigma``^2); the children of a
+    depth-d node are independent samples of softmax(draft row d / T_r)
+    (Gumbel-max), its argmax at T_r = 0."""
+    threads = threads or _default_threads()
+    ss = np.random.SeedSequence([seed, R, b, V, width, nodes])
+    kids_ss = ss.spawn(R)
+    Tr = np.broadcast_to(np.asarray(T, dtype=np.float32), (R,)).copy()
+    logtab = (-1.1 * np.log(np.arange(1, V + 1, dtype=np.float64))).astype(np.float32)
+    store = f32_to_bf16_bits if dtype == "bf16" else (lambda v: np.asarray(v, np.float32))
+
+    def shape_of(rng):
+        if shape == "chain":
+            L = int(rng.integers(0, b + 1))
+            return [-1] + list(range(L)), [0] + list(range(1, L + 1))
+        if shape == "wide":
+            return [-1] + [0] * width, [0] + [1] * width
+        if shape != "random":
+            raise ValueError(shape)
+        budget = int(rng.integers(1, nodes + 1))
+        par, dep = [-1], [0]
+        u = 0
+        while u < len(par) and len(par) < budget:
+            if dep[u] < b:
+                k = int(rng.integers(1 if u == 0 else 0, width + 1))
+                for _ in range(min(k, budget - len(par))):
+                    par.append(u)
+                    dep.append(dep[u] + 1)
+            u += 1
+        return par, dep
+
+    def per_request(r):
+        rng = np.random.default_rng(kids_ss[r])
+        par, dep = shape_of(rng)
+        base = _zipf_base(rng, b + 1, V, logtab)
+        d = np.asarray(dep)
+        tgt = store(base[d] + rng.standard_normal((len(par), V), dtype=np.float32))
+        draft = store(base[:b] + np.float32(draft_sigma) * rng.standard_normal((b, V), dtype=np.float32))
+        dv = values(draft)
+        tok = np.zeros(len(par), np.int32)
+        for j in range(1, len(par)):
+            tok[j] = _gumbel_argmax(rng, dv[dep[par[j]]], float(Tr[r]))
+        return np.asarray(par, np.int32), d.astype(np.int32), tok, tgt, draft
+
+    parts = _pool_map(per_request, list(range(R)), threads)
+    node_off = np.concatenate([[0], np.cumsum([len(p[0]) for p in parts])]).astype(np.int32)
+    parent = np.concatenate([p[0] for p in parts])
+    kidc = max(int(np.bincount(p[0][1:], minlength=1).max()) if len(p[0]) > 1 else 0 for p in parts)
+    tp = None if top_p is None else np.full(R, top_p, np.float32)
+    return TreeWorkload(name=name, R=R, b=b, V=V, dtype=dtype, max_kids=max(1, kidc), node_off=node_off,
+                        parent=parent, token=np.concatenate([p[2] for p in parts]),
+                        depth=np.concatenate([p[1] for p in parts]), tgt=np.concatenate([p[3] for p in parts]),
+                        draft=np.stack([p[4] for p in parts]), T=Tr, top_p=tp, seed=int(vseed))

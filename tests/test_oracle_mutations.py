@@ -2,8 +2,8 @@
 
 Each case plants one plausible mistake in a copy of ``oracle/sv_oracle.c``,
 builds that copy with the oracle's own compile line, and runs the named pins
-of ``tests/test_oracle_pins.py`` against it in a child process: the pins must
-fail.  The unmutated oracle passing the same pins is the ordinary pin run.
+of ``tests/test_oracle_pins.py`` and ``tests/test_oracle_tree.py`` against it
+in a child process: the pins must fail.  The unmutated oracle passing the same pins is the ordinary pin run.
 Nothing here touches the GPU library; the planted mistakes live only in a
 temporary directory.
 """
@@ -45,6 +45,16 @@ MUTATIONS = [
      "S += exp(orc_val(row, dtype, v) - m);\n  double lse = m + log(S);", "row_stats_vs_library"),
     ("draw-from-next-slot", "const int32_t j = n_acc;", "const int32_t j = n_acc < Lr ? n_acc + 1 : n_acc;",
      "chi2_residual or greedy_is_longest"),
+    # tree verification
+    ("tree-no-residual-between-siblings",
+     "const double px = have_res ? pcur[x] : orc_p_of(trow, in->dtype, x, T, &st);",
+     "const double px = orc_p_of(trow, in->dtype, x, T, &st);", "tree"),
+    ("tree-final-draw-from-p", "        if (!(W > 0.0))\n          for (int32_t v = 0; v < V; ++v) wbuf[v] = orc_p_of",
+     "        if (1)\n          for (int32_t v = 0; v < V; ++v) wbuf[v] = orc_p_of", "tree"),
+    ("tree-draft-row-of-the-child", "in->draft_row0[r] + depth[u], in->draft_ld);",
+     "in->draft_row0[r] + depth[u] + 1, in->draft_ld);", "tree"),
+    ("tree-uniform-counter-shifted", "orc_words_at(in->seed, r, j - 1, w4);", "orc_words_at(in->seed, r, j, w4);",
+     "tree"),
 ]
 
 
@@ -61,7 +71,8 @@ def test_planted_mistake_fails_its_pins(name, old, new, pins, tmp_path):
     subprocess.check_call(cmd)
     env = dict(os.environ, SV_ORACLE_LIB=str(lib))
     run = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                          os.path.join(ROOT, "tests", "test_oracle_pins.py"), "-k", pins],
+                          os.path.join(ROOT, "tests", "test_oracle_pins.py"),
+                          os.path.join(ROOT, "tests", "test_oracle_tree.py"), "-k", pins],
                          cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     tail = run.stdout[-1500:]
     assert "passed" in tail or "failed" in tail, tail
