@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--config", type=int, default=5, choices=(1, 2, 3, 4, 5),
                     help="5: conc 32 K=8 mixture with top-p and DVL (the headline workload); 1-4: the other "
                          "workloads")
+    ap.add_argument("--tree", action="store_true",
+                    help="tree verification instead of a block: conc 32, depth 16, random draft trees of at most 64 "
+                         "nodes (at most 4 children per node), V 151936 bf16, T 1, top-p 0.95")
     ap.add_argument("--branch-T", type=float, default=0.0,
                     help="soft-branch mixture: the drafter samples each branch from softmax(c / T_b) and "
                          "verification uses those branch distributions (0: greedy branches, the default)")
@@ -250,6 +253,9 @@ def main():
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this path runs on a single GPU)",
               file=sys.stderr)
         sys.exit(2)
+    if args.tree:
+        main_tree(args)
+        return
     import numpy as np
     import torch
 
@@ -444,6 +450,152 @@ def main():
         "device_status": status,
     }
     print(json.dumps(out), flush=True)
+
+
+TREE_SHAPE = dict(R=32, b=16, width=4, nodes=64, T=1.0, top_p=0.95)
+
+
+def main_tree(args):
+    """Tree verification step: the node rows' statistics with top-p
+    (sv_topp_threshold, row_off = node offsets), the drafter's rows'
+    statistics (sv_softmax_stats), and sv_tree_verify (checks, residual
+    masses, the walk, the draw).  The trees and logits are fixed; the
+    verification seed advances per step.  A verified draft position is a
+    draft node (every node but the roots)."""
+    import numpy as np
+    import torch
+
+    import draft_verification_sv_amd as sv
+    import synth
+    from draft_verification_sv_amd.step import row_pitch, to_device_rows
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    S = args.steps
+    t_gen = time.time()
+    sh = TREE_SHAPE
+    w = synth.tree("tree-conc32-d16-n64-w4-topp", R=sh["R"], b=sh["b"], V=synth.QWEN3_VOCAB, width=sh["width"],
+                   nodes=sh["nodes"], T=sh["T"], top_p=sh["top_p"], seed=3900)
+    R, b, V = w.R, w.b, w.V
+    n = int(w.node_off[-1])
+    print(f"[bench] tree data generated in {time.time() - t_gen:.1f}s: {n} nodes, at most {w.max_kids} children",
+          file=sys.stderr, flush=True)
+    ld = row_pitch(V, "bf16")
+    row_bytes = V * 2
+    dt = sv.SV_BF16
+    n_t = copies_for(n * row_bytes, args.copies)
+    n_d = copies_for(R * b * row_bytes, args.copies)
+    tg = [to_device_rows(w.tgt, ld, dev) for _ in range(n_t)]
+    dr = [to_device_rows(w.draft.reshape(R * b, V), ld, dev) for _ in range(n_d)]
+    i32, f32, f64 = torch.int32, torch.float32, torch.float64
+    z = lambda k, t: torch.zeros(k, dtype=t, device=dev)  # noqa: E731
+    T = torch.from_numpy(w.T).to(dev)
+    tp = torch.from_numpy(w.top_p).to(dev)
+    node_off = torch.from_numpy(w.node_off).to(dev)
+    parent = torch.from_numpy(w.parent).to(dev)
+    token = torch.from_numpy(w.token).to(dev)
+    pos_off = torch.arange(R + 1, dtype=i32, device=dev) * b
+    seeds = torch.arange(S, dtype=torch.int64, device=dev) + w.seed
+    ws, nb = sv.make_workspace(R, b, 0, V, dev)
+    st = [z(n, t) for t in (f32, i32, f64, f32, f64)]
+    ds = [z(R * b, t) for t in (f32, i32, f64)]
+    tb = sv.sv_tree_workspace_bytes(n, w.max_kids, V)
+    tws = torch.zeros(tb, dtype=torch.uint8, device=dev)
+    n_acc, path, stop, token_out, is_bonus = z(R, i32), z(R * b, i32), z(R, i32), z(R, i32), z(R, i32)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+
+    def step(s, ev=None):
+        t, d = tg[s % n_t], dr[s % n_d]
+        if ev is not None:
+            ev[0].record(stream)
+        sv.sv_topp_threshold(t, dt, ld, V, node_off, 0, R, n, T, tp, *st, ws, nb, sp)
+        if ev is not None:
+            ev[1].record(stream)
+        sv.sv_softmax_stats(d, dt, ld, V, pos_off, b, R, R * b, T, *ds, ws, nb, sp)
+        sv.sv_tree_verify(t, dt, ld, V, node_off, parent, token, R, b, n, w.max_kids, T, st[1], st[3], st[4], d, dt,
+                          ld, ds[1], ds[2], seeds[s:s + 1], n_acc, path, stop, token_out, is_bonus, None, None, None,
+                          ws, nb, tws, tb, sp)
+
+    for k in range(args.warmup):
+        step(k % S)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(S):
+        step(s)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    status = sv.sv_get_status(ws, sp)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(S)]
+    acc = np.zeros(S)
+    for s in range(S):
+        step(s, evs[s])
+        acc[s] = float(n_acc.sum().item())
+    torch.cuda.synchronize()
+    stats_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    ms_per_step = elapsed / S * 1e3
+    positions = n - R
+    stats_bytes = float(n * row_bytes)
+    achieved = stats_bytes / (stats_ms * 1e-3) / 1e9
+    # node rows and drafter rows read once, plus each request's drawn row (and, for a residual, its draft row)
+    step_bytes = (n + R * b + 2 * R) * row_bytes
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline_tree(w, args.cpu_seconds)
+    out = {
+        "metric": "verified draft positions/sec at V=151936, conc 32; % of peak HBM GB/s",
+        "value": round(positions * S / elapsed, 1),
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": S,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Zipfian logits, random draft trees)",
+        "config": {"workload": f"tree: conc{R} depth{b} V{V} bf16, random draft trees of at most {sh['nodes']} nodes "
+                               f"(at most {sh['width']} children), {n} nodes ({positions} draft nodes) per step, "
+                               f"T{sh['T']:g} top-p{sh['top_p']:g}, multi-round speculative sampling, seeds advancing "
+                               f"per step",
+                   "requests": R, "depth": b, "vocab": V, "nodes": n, "max_children": w.max_kids,
+                   "copies": {"node_rows": n_t, "draft_rows": n_d}},
+        "accepted_per_step": round(float(acc.mean()), 2),
+        "step_gbps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "step_frac_of_peak": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "roofline": {"kernel": "k_row_stats (sv_topp_threshold over the node rows)", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "avg_launch_us": round(stats_ms * 1e3, 2), "algorithmic_bytes_per_launch": stats_bytes},
+        "cpu_baseline": cpu,
+        "device_status": status,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_tree(w, seconds: float):
+    """The CPU oracle's tree step on the same trees and rows, seeds advancing,
+    until `seconds` pass (every OpenMP thread the oracle uses)."""
+    import oracle
+
+    import numpy as np
+
+    n = int(w.node_off[-1])
+    threads = oracle.num_threads()
+    t0 = time.perf_counter()
+    k = 0
+    while True:
+        oracle.tree_step(tgt=w.tgt, tgt_row=np.arange(n), node_off=w.node_off, parent=w.parent, token=w.token, T=w.T,
+                         b=w.b, seed=w.seed + k, draft=w.draft.reshape(w.R * w.b, w.V),
+                         draft_row0=np.arange(w.R) * w.b, top_p=w.top_p)
+        k += 1
+        if time.perf_counter() - t0 > seconds:
+            break
+    el = time.perf_counter() - t0
+    return {"value": round(k * (n - w.R) / el, 2), "unit": "positions/s", "cores": min(threads, w.R), "kind": "oracle",
+            "sample": f"{k} whole tree steps of the same workload ({k * (n - w.R)} draft nodes) in {el:.1f}s",
+            "nproc": os.cpu_count(), "omp_threads": threads}
 
 
 def cpu_baseline(w, seconds: float):

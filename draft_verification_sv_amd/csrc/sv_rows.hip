@@ -6,7 +6,7 @@
 namespace sv {
 
 constexpr int kRowNT = 512;
-constexpr int kRowBatch = 8;  // 16-byte loads per thread per batch (x2 in flight)
+constexpr int kRowBatch = 4;  // 16-byte loads per thread per batch (x2 in flight): 114 VGPRs, two blocks per CU
 constexpr int kDenseNT = 256;  // sv_verify_rows_dense: P blocks of 256 per split row
 constexpr int kDenseBatch = 4;
 constexpr int kDensePartVec = 6400;  // vectors per part (100 KiB of bf16) without a cut

@@ -39,6 +39,9 @@ namespace sv {
 constexpr int kTreeNT = 256;
 constexpr int kTreeMaxKids = 16;    // children tested per node
 constexpr int kTreeMaxNodes = 1024; // nodes of one request (staged in LDS by the walk)
+constexpr int kTreeChunk = 4096;    // values of a row per mass block (the draw's chunk)
+constexpr int kTreeMaxReq = 1024;   // requests of one call (the mass kernel scans their counts in LDS)
+constexpr int kTreeMassGrid = 1024; // mass blocks: four 256-thread blocks per compute unit
 
 struct TreeNode {
   int32_t depth, kids, req, valid;
@@ -71,13 +74,12 @@ struct TreeArgs {
   float* u_out;
   TreeNode* nodes;  // [max_nodes]
   double* zpart;    // [max_nodes][max_kids - 1][S]: partial masses Z_k per chunk
+  int2* order;      // [max_nodes]: request r's nodes with >= 2 children, by child count descending,
+                    // at node_off[r] ...: {local index, depth}
+  int32_t* khist;   // [R][kTreeMaxKids + 1]: request r's count of such nodes per child count
   DrawRec* rec;     // [R]
   uint32_t* status;
 };
-
-__device__ __forceinline__ const char* tree_row(const void* base, int dtype, int64_t row, int64_t ld) {
-  return static_cast<const char*>(base) + static_cast<size_t>(row) * static_cast<size_t>(ld) * (dtype == SV_BF16 ? 2 : 4);
-}
 
 // Whether request r's node range is usable: n0 >= 0, 1 <= N <= kTreeMaxNodes,
 // inside the node count node_off[R] and the capacity max_nodes.
@@ -102,10 +104,13 @@ __device__ __forceinline__ bool tree_node_ok(const TreeArgs& a, const TreeNode& 
 // parent precedes its child, depth <= b, at most max_kids children.
 __global__ __launch_bounds__(kTreeNT) void k_tree_prep(TreeArgs a) {
   __shared__ int kids[kTreeMaxNodes];
+  __shared__ int depth[kTreeMaxNodes];
+  __shared__ int hist[kTreeMaxKids + 1], cursor[kTreeMaxKids + 1];
   __shared__ int bad;
   const int r = blockIdx.x, tid = threadIdx.x;
   int n0, N;
   const bool range = tree_range_ok(a, r, n0, N);
+  if (tid <= kTreeMaxKids) a.khist[r * (kTreeMaxKids + 1) + tid] = 0;  // rewritten below for a usable request
   if (!range) {
     if (tid == 0) raise_status(a.status, SV_ST_BAD_TREE);
     return;
@@ -136,64 +141,161 @@ __global__ __launch_bounds__(kTreeNT) void k_tree_prep(TreeArgs a) {
     }
     if (d > a.b || kids[j] > a.max_kids) bad = 1;
     a.nodes[n0 + j] = TreeNode{d, kids[j], r, 1};
+    depth[j] = d;
+  }
+  if (tid <= kTreeMaxKids) {
+    hist[tid] = 0;
+    cursor[tid] = 0;
   }
   __syncthreads();
   if (bad) {
     for (int j = tid; j < N; j += kTreeNT) a.nodes[n0 + j].valid = 0;
     if (tid == 0) raise_status(a.status, SV_ST_BAD_TREE);
   }
-}
-
-// c_k of node g from the masses of the passes before k (lanes sum the partials).
-// Returns c_k; the masses Z_1 .. Z_{k-1} are those of the earlier passes.
-__device__ __forceinline__ double tree_c(const TreeArgs& a, int g, int k, double* red) {
-  double c = 1.0;  // c_1
-  for (int m = 1; m < k; ++m) {
-    const double* zp = a.zpart + (static_cast<size_t>(g) * (a.max_kids - 1) + (m - 1)) * a.S;
-    double part = 0.0;
-    for (int s = threadIdx.x; s < a.S; s += kTreeNT) part += zp[s];
-    const double Z = block_sum_f64<kTreeNT>(part, red);
-    c = Z > 0.0 ? c + Z : 1.0;  // emptied by rounding: the target resets to p (c = 0, Z = 1)
-  }
-  return c;
+  // the nodes the mass passes take (>= 2 children; none for a greedy or
+  // malformed request), grouped by child count, most children first: pass k
+  // takes the first sum_{v > k} hist[v] of them
+  const bool masses = !bad && a.T[r] > 0.0f;
+  if (masses)
+    for (int j = tid; j < N; j += kTreeNT)
+      if (kids[j] >= 2) atomicAdd(&hist[kids[j]], 1);
+  __syncthreads();
+  if (tid <= kTreeMaxKids) a.khist[r * (kTreeMaxKids + 1) + tid] = masses && tid >= 2 ? hist[tid] : 0;
+  if (masses)
+    for (int j = tid; j < N; j += kTreeNT) {
+      const int v = kids[j];
+      if (v < 2) continue;
+      int start = 0;
+      for (int u = v + 1; u <= kTreeMaxKids; ++u) start += hist[u];
+      a.order[n0 + start + atomicAdd(&cursor[v], 1)] = make_int2(j, depth[j]);
+    }
 }
 
 // Pass k: for every node with more than k children, the partial masses over
-// chunk ch of sum_v max(0, p_v - c_k q_v) (p: the node's target row with its
-// cut; q: the draft row of the node's depth).  Greedy requests (T = 0) need
-// no masses.
+// each chunk of 4096 values of sum_v max(0, p_v - c_k q_v) (p: the node's
+// target row with its cut; q: the draft row of the node's depth).  Greedy
+// requests (T = 0) need no masses.  A fixed grid walks the pass's (node,
+// chunk) items: each block first scans the requests' counts of nodes with
+// more than k children (from the prep's per-count histograms), then takes
+// items blockIdx.x, blockIdx.x + gridDim.x, ...; so no block is launched for
+// a node without work.  Per item each thread takes two 8-value groups of both
+// rows, all four 16-byte loads (and the earlier passes' partials, for c_k)
+// issued before any is used, and every wave forms c_k itself from those
+// partials.
 template <int DT, int DDT>
 __global__ __launch_bounds__(kTreeNT) void k_tree_mass(TreeArgs a, int k) {
   __shared__ double etab[kExpTab];
   __shared__ double red[kTreeNT / kWave];
-  const int g = blockIdx.x / a.S, ch = blockIdx.x % a.S;
-  if (g >= a.node_off[a.R]) return;
-  const TreeNode nd = a.nodes[g];
-  if (nd.req < 0 || nd.req >= a.R || !tree_node_ok(a, nd, nd.req) || nd.kids <= k) return;
-  const int r = nd.req;
-  const float T = a.T[r];
-  if (!(T > 0.0f)) return;
+  __shared__ int scan[kTreeMaxReq + 1];  // exclusive scan of the requests' active node counts
+  __shared__ int wtot[kTreeNT / kWave];
+  __shared__ float2 list[kTreeNT * 16];  // per wave: the (l, d) pairs of its values with p > c q
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), R = a.R;
   exp_table_init(etab);
-  __syncthreads();
-  const double c = tree_c(a, g, k, red);
-  const double invT = 1.0 / static_cast<double>(T);
-  const float cut = a.row_cut[g];
-  const double kept = a.row_kept[g];
-  const int64_t drow = static_cast<int64_t>(r) * a.b + nd.depth;
-  const double dl = a.dlse[drow] - log(c);  // c q = exp(d / T - (lse - ln c))
-  const char* tp = tree_row(a.tgt, DT, g, a.tgt_ld);
-  const char* dp = tree_row(a.draft, DDT, drow, a.draft_ld);
-  // this block's 4096 values: 8 per thread, in two 8-value groups
-  const int V = a.V;
-  double part = 0.0;
-  for (int e = ch * 4096 + threadIdx.x; e < min(V, (ch + 1) * 4096); e += kTreeNT) {
-    const float l = load_val<DT>(tp, e);
-    const double p = l >= cut ? exp_tab(static_cast<double>(l) * invT - kept, etab) : 0.0;
-    const double w = p - exp_tab(static_cast<double>(load_val<DDT>(dp, e)) * invT - dl, etab);
-    part += w > 0.0 ? w : 0.0;
+  // requests' counts in contiguous runs per thread, then a block scan
+  const int per = (R + kTreeNT - 1) / kTreeNT;
+  const int r0 = min(R, tid * per), r1 = min(R, r0 + per);
+  int mine = 0;
+  for (int r = r0; r < r1; ++r) {
+    const int32_t* h = a.khist + r * (kTreeMaxKids + 1);
+    int c = 0;
+    for (int v = k + 1; v <= kTreeMaxKids; ++v) c += h[v];
+    scan[r] = c;  // the count, turned into its exclusive prefix below
+    mine += c;
   }
-  const double tot = block_sum_f64<kTreeNT>(part, red);
-  if (threadIdx.x == 0) a.zpart[(static_cast<size_t>(g) * (a.max_kids - 1) + (k - 1)) * a.S + ch] = tot;
+  const int total_items = [&] {
+    int tot;
+    int run = block_excl_scan_i32<kTreeNT>(mine, wtot, &tot);
+    for (int r = r0; r < r1; ++r) {
+      const int c = scan[r];
+      scan[r] = run;
+      run += c;
+    }
+    if (tid == 0) scan[R] = tot;
+    return tot;
+  }();
+  __syncthreads();  // scan and table
+  const int S = a.S, V = a.V, NG = groups_of(V);
+  const long long items = static_cast<long long>(total_items) * S;
+  for (long long it = blockIdx.x; it < items; it += gridDim.x) {
+    const int pos = static_cast<int>(it / S), ch = static_cast<int>(it % S);
+    int lo = 0, hi = R;  // the request r with scan[r] <= pos < scan[r + 1]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (scan[mid] <= pos) lo = mid;
+      else hi = mid;
+    }
+    const int r = lo;
+    const int n0 = a.node_off[r];
+    const int2 e = a.order[n0 + (pos - scan[r])];
+    const int g = n0 + e.x;
+    const int64_t drow = static_cast<int64_t>(r) * a.b + min(max(e.y, 0), a.b - 1);
+    const char* tp = row_ptr(a.tgt, DT, g, a.tgt_ld);
+    const char* dp = row_ptr(a.draft, DDT, drow, a.draft_ld);
+    const int g0 = ch * (kTreeChunk / 8) + tid, g1 = g0 + kTreeNT;
+    uint4 t00, t01, t10, t11, d00, d01, d10, d11;
+    raw8<DT>(tp, min(g0, NG - 1), V, t00, t01);
+    raw8<DT>(tp, min(g1, NG - 1), V, t10, t11);
+    raw8<DDT>(dp, min(g0, NG - 1), V, d00, d01);
+    raw8<DDT>(dp, min(g1, NG - 1), V, d10, d11);
+    const size_t zbase = static_cast<size_t>(g) * (a.max_kids - 1) * S;
+    constexpr int kPre = 3;  // the first passes' partials are loaded with the rows (lane < S; S <= 64 chunks)
+    double zl[kPre];
+#pragma unroll
+    for (int m = 1; m <= kPre; ++m)
+      zl[m - 1] = m < k && lane < S ? a.zpart[zbase + static_cast<size_t>(m - 1) * S + lane] : 0.0;
+    const float T = a.T[r];
+    const float cut = a.row_cut[g];
+    const double kept = a.row_kept[g];
+    const double dlse = a.dlse[drow];
+    // c_k: c_1 = 1, c_{m+1} = c_m + Z_m (a mass emptied by rounding resets the target to p: c = 0, Z = 1)
+    double c = 1.0;
+#pragma unroll
+    for (int m = 1; m < kTreeMaxKids; ++m) {
+      if (m < k) {  // uniform over the block
+        double part = m <= kPre ? zl[min(m, kPre) - 1]
+                                : (lane < S ? a.zpart[zbase + static_cast<size_t>(m - 1) * S + lane] : 0.0);
+        for (int s2 = lane + kWave; s2 < S; s2 += kWave) part += a.zpart[zbase + static_cast<size_t>(m - 1) * S + s2];
+        const double Z = wave_sum_f64(part);
+        c = Z > 0.0 ? c + Z : 1.0;
+      }
+    }
+    const double invT = 1.0 / static_cast<double>(T);
+    const double dl = dlse - log(c);  // c q = exp(d / T - (lse - ln c))
+    // only values with p > c q carry mass: ln p = l / T - kept against
+    // ln(c q) = d / T - (lse - ln c), two FMAs in double; their (l, d) pairs
+    // are packed into the wave's list, and the exponentials run over the list
+    // with every lane busy
+    float l[16], d[16];
+    decode8<DT>(t00, t01, g0, V, g0 < NG, l);
+    decode8<DT>(t10, t11, g1, V, g1 < NG, l + 8);
+    decode8<DDT>(d00, d01, g0, V, g0 < NG, d);
+    decode8<DDT>(d10, d11, g1, V, g1 < NG, d + 8);
+    int cnt = 0;
+    bool keep[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      keep[q] = l[q] > -INFINITY && l[q] >= cut &&
+                fma(static_cast<double>(l[q]), invT, -kept) > fma(static_cast<double>(d[q]), invT, -dl);
+      cnt += keep[q] ? 1 : 0;
+    }
+    const int inc = wave_incl_scan_i32(cnt);
+    const int n_list = bcast_i32(inc, kWave - 1);
+    float2* mine_list = list + (tid / kWave) * (kWave * 16);
+    int o = inc - cnt;
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+      if (keep[q]) mine_list[o++] = make_float2(l[q], d[q]);
+    __syncwarp();
+    double part = 0.0;
+    for (int e = lane; e < n_list; e += kWave) {
+      const float2 v = mine_list[e];
+      const double w = exp_tab(fma(static_cast<double>(v.x), invT, -kept), etab) -
+                       exp_tab(fma(static_cast<double>(v.y), invT, -dl), etab);
+      part += w > 0.0 ? w : 0.0;
+    }
+    const double tot = block_sum_f64<kTreeNT>(part, red);  // its leading barrier also ends this item's list reads
+    if (tid == 0) a.zpart[zbase + static_cast<size_t>(k - 1) * S + ch] = tot;
+  }
 }
 
 // The walk, one wave per request: from the root, each node's children in
@@ -265,8 +367,8 @@ __global__ __launch_bounds__(kWave) void k_tree_walk(TreeArgs a) {
     __syncwarp();
     double c = 0.0, Z = 1.0;  // the current target: max(0, p - c q) / Z
     int m = 0, next = -1;
-    const char* tp = tree_row(a.tgt, DT, g, a.tgt_ld);
-    const char* dp = tree_row(a.draft, DDT, drow, a.draft_ld);
+    const char* tp = row_ptr(a.tgt, DT, g, a.tgt_ld);
+    const char* dp = row_ptr(a.draft, DDT, drow, a.draft_ld);
     for (int j0 = u + 1; j0 < N && next < 0 && m < nd.kids; j0 += kWave) {
       const int j = j0 + lane;
       uint64_t mine = __ballot(j < N && par[min(j, N - 1)] == u);
@@ -348,11 +450,24 @@ __global__ __launch_bounds__(kWave) void k_tree_walk(TreeArgs a) {
   }
 }
 
-size_t tree_ws_needed(int max_nodes, int max_kids, int V) {
-  const size_t S = static_cast<size_t>(res_chunks(V));
-  return align256(sizeof(TreeNode) * static_cast<size_t>(max_nodes)) +
-         align256(sizeof(double) * static_cast<size_t>(max_nodes) * (max_kids > 1 ? max_kids - 1 : 1) * S);
+// tree workspace: node records, partial masses, the mass passes' node order
+// and per-request child-count histograms (at most max_nodes requests)
+struct TreeWs {
+  size_t nodes, zpart, order, khist, total;
+};
+
+TreeWs tree_ws_layout(int max_nodes, int max_kids, int V) {
+  const size_t S = static_cast<size_t>(res_chunks(V)), n = static_cast<size_t>(max_nodes);
+  TreeWs l;
+  l.nodes = 0;
+  l.zpart = align256(sizeof(TreeNode) * n);
+  l.order = l.zpart + align256(sizeof(double) * n * (max_kids > 1 ? max_kids - 1 : 1) * S);
+  l.khist = l.order + align256(sizeof(int2) * n);
+  l.total = l.khist + align256(sizeof(int32_t) * n * (kTreeMaxKids + 1));
+  return l;
 }
+
+size_t tree_ws_needed(int max_nodes, int max_kids, int V) { return tree_ws_layout(max_nodes, max_kids, V).total; }
 
 }  // namespace sv
 
@@ -367,8 +482,7 @@ extern "C" int32_t sv_tree_workspace_bytes(int32_t max_nodes, int32_t max_kids, 
 template <int DT, int DDT>
 static int32_t launch_tree(const TreeArgs& t, hipStream_t s) {
   for (int k = 1; k < t.max_kids; ++k) {
-    hipLaunchKernelGGL((k_tree_mass<DT, DDT>), dim3(static_cast<unsigned>(t.max_nodes) * t.S), dim3(kTreeNT), 0, s,
-                       t, k);
+    hipLaunchKernelGGL((k_tree_mass<DT, DDT>), dim3(kTreeMassGrid), dim3(kTreeNT), 0, s, t, k);
     if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
   }
   hipLaunchKernelGGL((k_tree_walk<DT, DDT>), dim3(t.R), dim3(kWave), 0, s, t);
@@ -389,7 +503,9 @@ extern "C" int32_t sv_tree_verify(const void* tgt_logits, int32_t dtype, int64_t
   if (!draft_logits || !draft_argmax || !draft_lse || !seed || !n_acc || !path || !stop_node || !token_out ||
       !is_bonus || !ws || !tree_ws)
     return SV_ERR_ARG;
-  if (R < 1 || b < 1 || b > 64 || V < 1 || max_nodes < R || max_kids < 1 || max_kids > kTreeMaxKids) return SV_ERR_ARG;
+  if (R < 1 || R > kTreeMaxReq || b < 1 || b > 64 || V < 1 || max_nodes < R || max_kids < 1 ||
+      max_kids > kTreeMaxKids)
+    return SV_ERR_ARG;
   if (tgt_ld < V || draft_ld < V) return SV_ERR_ARG;
   if ((dtype != SV_F32 && dtype != SV_BF16) || (draft_dtype != SV_F32 && draft_dtype != SV_BF16)) return SV_ERR_ARG;
   if (!rows_aligned(tgt_logits, dtype, tgt_ld) || !rows_aligned(draft_logits, draft_dtype, draft_ld)) return SV_ERR_ARG;
@@ -404,8 +520,12 @@ extern "C" int32_t sv_tree_verify(const void* tgt_logits, int32_t dtype, int64_t
   t.draft = draft_logits; t.ddtype = draft_dtype; t.draft_ld = draft_ld; t.dargmax = draft_argmax; t.dlse = draft_lse;
   t.seed = seed; t.n_acc = n_acc; t.path = path; t.stop_node = stop_node;
   t.p_out = p_out; t.q_out = q_out; t.u_out = u_out;
-  t.nodes = static_cast<TreeNode*>(tree_ws);
-  t.zpart = reinterpret_cast<double*>(static_cast<char*>(tree_ws) + align256(sizeof(TreeNode) * static_cast<size_t>(max_nodes)));
+  const TreeWs tl = tree_ws_layout(max_nodes, max_kids, V);
+  char* twb = static_cast<char*>(tree_ws);
+  t.nodes = reinterpret_cast<TreeNode*>(twb + tl.nodes);
+  t.zpart = reinterpret_cast<double*>(twb + tl.zpart);
+  t.order = reinterpret_cast<int2*>(twb + tl.order);
+  t.khist = reinterpret_cast<int32_t*>(twb + tl.khist);
   t.rec = reinterpret_cast<DrawRec*>(static_cast<char*>(ws) + l.rec);
   t.status = status_word(ws);
   hipStream_t s = static_cast<hipStream_t>(stream);

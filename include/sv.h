@@ -396,7 +396,7 @@ int32_t sv_tree_workspace_bytes(int32_t max_nodes, int32_t max_kids, int32_t V, 
  *   bonus token is drawn from its p; draws as sv_residual_sample, with word 1
  *   at counter (s, r, 0, 0), s the stopping node.  A chain (parent j - 1) is
  *   exactly sv_accept + sv_residual_sample.  At most max_kids (<= 16)
- *   children per node.
+ *   children per node; at most 1024 requests per call (SV_ERR_ARG beyond).
  *   n_acc[R], path[R*b] (the accepted nodes' local indices in order),
  *   stop_node[R], token_out[R], is_bonus[R]  out
  *   p_out, q_out (double), u_out (float)  optional, [max_nodes] per node: the
@@ -408,9 +408,10 @@ int32_t sv_tree_workspace_bytes(int32_t max_nodes, int32_t max_kids, int32_t V, 
  * Malformed trees (a parent not before its child, depth > b, more than
  * max_kids children, node counts out of range) set SV_ST_BAD_TREE; their
  * request gets n_acc = 0 and no token.  Launches: one block per request
- * (depths, checks), max_kids - 1 passes over (node, 4096-value chunk) that
- * form the residual masses sum_v max(0, p - c q), one wave per request (the
- * walk), then the draw's sums and pick. */
+ * (depths, checks, the nodes with several children ordered by their count),
+ * max_kids - 1 passes over the (node, 4096-value chunk) items that need them,
+ * forming the residual masses sum_v max(0, p - c q), one wave per request
+ * (the walk), then the draw's sums and pick. */
 int32_t sv_tree_verify(const void* tgt_logits, int32_t dtype, int64_t tgt_ld, int32_t V, const int32_t* node_off,
                        const int32_t* parent, const int32_t* token, int32_t R, int32_t b, int32_t max_nodes,
                        int32_t max_kids, const float* temperature, const int32_t* row_argmax,

@@ -621,7 +621,7 @@ int orc_tree_step(const orc_tree_in_t* in, const orc_tree_out_t* out) {
   {
     double* pcur = (double*)malloc(sizeof(double) * (size_t)V);
     double* wbuf = (double*)malloc(sizeof(double) * (size_t)V);
-#pragma omp for schedule(dynamic, 64)
+#pragma omp for schedule(dynamic, 1)
     for (int32_t r = 0; r < R; ++r) {
       const int32_t n0 = in->node_off[r], N = in->node_off[r + 1] - n0;
       const int32_t* par = in->parent + n0;

@@ -285,3 +285,6 @@ def test_tree_host_argument_errors():
     with pytest.raises(sv.SvError):  # max_nodes below R
         sv.sv_tree_verify(z, sv.SV_F32, 64, 60, z, z, z, 2, 4, 1, 2, z, z, z, z, z, sv.SV_F32, 64, z, z, z, z, z,
                           z, z, z, None, None, None, ws, nb, z, 1 << 20)
+    with pytest.raises(sv.SvError):  # more than 1024 requests
+        sv.sv_tree_verify(z, sv.SV_F32, 64, 60, z, z, z, 1025, 4, 2000, 2, z, z, z, z, z, sv.SV_F32, 64, z, z, z, z,
+                          z, z, z, z, None, None, None, ws, nb, z, 1 << 20)
