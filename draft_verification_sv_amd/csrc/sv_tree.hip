@@ -81,6 +81,22 @@ struct TreeArgs {
   uint32_t* status;
 };
 
+// Z_m of a node from its pass-m chunk partials zp[0 .. S-1], summed in chunk
+// order (the mass passes and the walk form it alike, bit for bit); loads in
+// batches of 16, all of a batch in flight before any is added.
+__device__ __forceinline__ double zsum(const double* zp, int S) {
+  double z = 0.0;
+  for (int s0 = 0; s0 < S; s0 += 16) {
+    double v[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) v[k] = s0 + k < S ? zp[s0 + k] : 0.0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      if (s0 + k < S) z += v[k];
+  }
+  return z;
+}
+
 // Whether request r's node range is usable: n0 >= 0, 1 <= N <= kTreeMaxNodes,
 // inside the node count node_off[R] and the capacity max_nodes.
 __device__ __forceinline__ bool tree_range_ok(const TreeArgs& a, int r, int& n0, int& N) {
@@ -175,19 +191,33 @@ __global__ __launch_bounds__(kTreeNT) void k_tree_prep(TreeArgs a) {
 // each chunk of 4096 values of sum_v max(0, p_v - c_k q_v) (p: the node's
 // target row with its cut; q: the draft row of the node's depth).  Greedy
 // requests (T = 0) need no masses.  A fixed grid walks the pass's (node,
-// chunk) items: each block first scans the requests' counts of nodes with
-// more than k children (from the prep's per-count histograms), then takes
-// items blockIdx.x, blockIdx.x + gridDim.x, ...; so no block is launched for
-// a node without work.  Per item each thread takes two 8-value groups of both
-// rows, all four 16-byte loads (and the earlier passes' partials, for c_k)
-// issued before any is used, and every wave forms c_k itself from those
-// partials.
+// chunk) items: each block scans the requests' counts of nodes with more than
+// k children (from the prep's per-count histograms) and takes items
+// blockIdx.x, blockIdx.x + gridDim.x, ...; so no block is launched for a node
+// without work.  Per block, up to kMassBatch of its items are set up at once
+// (one item per thread: node, rows, cut, normalisers, c_k into LDS), then
+// walked in order with the next item's four 16-byte loads per thread issued
+// before the current item is computed.  Only values with p > c q carry mass:
+// ln p = l / T - kept against ln(c q) = d / T - (lse - ln c), two FMAs in
+// double; their (l, d) pairs are packed into the wave's list, and the double
+// exponentials run over the list with every lane busy.
+constexpr int kMassBatch = 64;  // items set up at once per block (LDS for four blocks per CU)
+
+struct MassItem {
+  const char* tp;  // target row
+  const char* dp;  // draft row
+  double kept, dl, invT;
+  float cut;
+  int zslot;       // index of this item's partial in zpart
+};
+
 template <int DT, int DDT>
 __global__ __launch_bounds__(kTreeNT) void k_tree_mass(TreeArgs a, int k) {
   __shared__ double etab[kExpTab];
   __shared__ double red[kTreeNT / kWave];
   __shared__ int scan[kTreeMaxReq + 1];  // exclusive scan of the requests' active node counts
   __shared__ int wtot[kTreeNT / kWave];
+  __shared__ MassItem items[kMassBatch];
   __shared__ float2 list[kTreeNT * 16];  // per wave: the (l, d) pairs of its values with p > c q
   const int tid = threadIdx.x, lane = tid & (kWave - 1), R = a.R;
   exp_table_init(etab);
@@ -202,99 +232,109 @@ __global__ __launch_bounds__(kTreeNT) void k_tree_mass(TreeArgs a, int k) {
     scan[r] = c;  // the count, turned into its exclusive prefix below
     mine += c;
   }
-  const int total_items = [&] {
-    int tot;
-    int run = block_excl_scan_i32<kTreeNT>(mine, wtot, &tot);
-    for (int r = r0; r < r1; ++r) {
-      const int c = scan[r];
-      scan[r] = run;
-      run += c;
-    }
-    if (tid == 0) scan[R] = tot;
-    return tot;
-  }();
+  int total;
+  int run = block_excl_scan_i32<kTreeNT>(mine, wtot, &total);
+  for (int r = r0; r < r1; ++r) {
+    const int c = scan[r];
+    scan[r] = run;
+    run += c;
+  }
+  if (tid == 0) scan[R] = total;
   __syncthreads();  // scan and table
   const int S = a.S, V = a.V, NG = groups_of(V);
-  const long long items = static_cast<long long>(total_items) * S;
-  for (long long it = blockIdx.x; it < items; it += gridDim.x) {
-    const int pos = static_cast<int>(it / S), ch = static_cast<int>(it % S);
-    int lo = 0, hi = R;  // the request r with scan[r] <= pos < scan[r + 1]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (scan[mid] <= pos) lo = mid;
-      else hi = mid;
-    }
-    const int r = lo;
-    const int n0 = a.node_off[r];
-    const int2 e = a.order[n0 + (pos - scan[r])];
-    const int g = n0 + e.x;
-    const int64_t drow = static_cast<int64_t>(r) * a.b + min(max(e.y, 0), a.b - 1);
-    const char* tp = row_ptr(a.tgt, DT, g, a.tgt_ld);
-    const char* dp = row_ptr(a.draft, DDT, drow, a.draft_ld);
-    const int g0 = ch * (kTreeChunk / 8) + tid, g1 = g0 + kTreeNT;
-    uint4 t00, t01, t10, t11, d00, d01, d10, d11;
-    raw8<DT>(tp, min(g0, NG - 1), V, t00, t01);
-    raw8<DT>(tp, min(g1, NG - 1), V, t10, t11);
-    raw8<DDT>(dp, min(g0, NG - 1), V, d00, d01);
-    raw8<DDT>(dp, min(g1, NG - 1), V, d10, d11);
-    const size_t zbase = static_cast<size_t>(g) * (a.max_kids - 1) * S;
-    constexpr int kPre = 3;  // the first passes' partials are loaded with the rows (lane < S; S <= 64 chunks)
-    double zl[kPre];
-#pragma unroll
-    for (int m = 1; m <= kPre; ++m)
-      zl[m - 1] = m < k && lane < S ? a.zpart[zbase + static_cast<size_t>(m - 1) * S + lane] : 0.0;
-    const float T = a.T[r];
-    const float cut = a.row_cut[g];
-    const double kept = a.row_kept[g];
-    const double dlse = a.dlse[drow];
-    // c_k: c_1 = 1, c_{m+1} = c_m + Z_m (a mass emptied by rounding resets the target to p: c = 0, Z = 1)
-    double c = 1.0;
-#pragma unroll
-    for (int m = 1; m < kTreeMaxKids; ++m) {
-      if (m < k) {  // uniform over the block
-        double part = m <= kPre ? zl[min(m, kPre) - 1]
-                                : (lane < S ? a.zpart[zbase + static_cast<size_t>(m - 1) * S + lane] : 0.0);
-        for (int s2 = lane + kWave; s2 < S; s2 += kWave) part += a.zpart[zbase + static_cast<size_t>(m - 1) * S + s2];
-        const double Z = wave_sum_f64(part);
+  const long long n_items = static_cast<long long>(total) * S;
+  const long long mine_items = n_items > blockIdx.x ? (n_items - 1 - blockIdx.x) / gridDim.x + 1 : 0;
+  for (long long j0 = 0; j0 < mine_items; j0 += kMassBatch) {
+    const int nj = static_cast<int>(min<long long>(kMassBatch, mine_items - j0));
+    // set-up of items j0 .. j0 + nj - 1, one per thread
+    if (tid < nj) {
+      const long long it = blockIdx.x + (j0 + tid) * gridDim.x;
+      const int pos = static_cast<int>(it / S), ch = static_cast<int>(it % S);
+      int lo = 0, hi = R;  // the request r with scan[r] <= pos < scan[r + 1]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (scan[mid] <= pos) lo = mid;
+        else hi = mid;
+      }
+      const int r = lo;
+      const int n0 = a.node_off[r];
+      const int2 e = a.order[n0 + (pos - scan[r])];
+      const int g = n0 + e.x;
+      const int64_t drow = static_cast<int64_t>(r) * a.b + min(max(e.y, 0), a.b - 1);
+      const float T = a.T[r];
+      const float cut = a.row_cut[g];
+      const double kept = a.row_kept[g];
+      const double dlse = a.dlse[drow];
+      // c_k: c_1 = 1, c_{m+1} = c_m + Z_m (a mass emptied by rounding resets the target to p: c = 0, Z = 1)
+      const size_t zbase = static_cast<size_t>(g) * (a.max_kids - 1) * S;
+      double c = 1.0;
+      for (int m = 1; m < k; ++m) {
+        const double Z = zsum(a.zpart + zbase + static_cast<size_t>(m - 1) * S, S);
         c = Z > 0.0 ? c + Z : 1.0;
       }
+      MassItem I;
+      I.tp = row_ptr(a.tgt, DT, g, a.tgt_ld);
+      I.dp = row_ptr(a.draft, DDT, drow, a.draft_ld);
+      I.kept = kept;
+      I.dl = dlse - log(c);  // c q = exp(d / T - (lse - ln c))
+      I.invT = 1.0 / static_cast<double>(T);
+      I.cut = cut;
+      I.zslot = static_cast<int>(zbase + static_cast<size_t>(k - 1) * S + ch);
+      items[tid] = I;
     }
-    const double invT = 1.0 / static_cast<double>(T);
-    const double dl = dlse - log(c);  // c q = exp(d / T - (lse - ln c))
-    // only values with p > c q carry mass: ln p = l / T - kept against
-    // ln(c q) = d / T - (lse - ln c), two FMAs in double; their (l, d) pairs
-    // are packed into the wave's list, and the exponentials run over the list
-    // with every lane busy
-    float l[16], d[16];
-    decode8<DT>(t00, t01, g0, V, g0 < NG, l);
-    decode8<DT>(t10, t11, g1, V, g1 < NG, l + 8);
-    decode8<DDT>(d00, d01, g0, V, g0 < NG, d);
-    decode8<DDT>(d10, d11, g1, V, g1 < NG, d + 8);
-    int cnt = 0;
-    bool keep[16];
+    __syncthreads();
+    // this thread's two 8-value groups of item j's chunk
+    auto gabs = [&](int j, int cg) {
+      const long long it = blockIdx.x + (j0 + j) * gridDim.x;
+      return static_cast<int>(it % S) * (kTreeChunk / 8) + cg;
+    };
+    const int c0 = tid, c1 = tid + kTreeNT;
+    uint4 t00, t01, t10, t11, d00, d01, d10, d11;
+    auto issue = [&](int j) {
+      const MassItem& I = items[j];
+      const int ga = min(gabs(j, c0), NG - 1), gb = min(gabs(j, c1), NG - 1);  // clamped in-bounds (unused there)
+      raw8<DT>(I.tp, ga, V, t00, t01);
+      raw8<DT>(I.tp, gb, V, t10, t11);
+      raw8<DDT>(I.dp, ga, V, d00, d01);
+      raw8<DDT>(I.dp, gb, V, d10, d11);
+    };
+    issue(0);
+    for (int j = 0; j < nj; ++j) {
+      const MassItem I = items[j];
+      const int ga = gabs(j, c0), gb = gabs(j, c1);
+      float l[16], d[16];
+      decode8<DT>(t00, t01, ga, V, ga < NG, l);
+      decode8<DT>(t10, t11, gb, V, gb < NG, l + 8);
+      decode8<DDT>(d00, d01, ga, V, ga < NG, d);
+      decode8<DDT>(d10, d11, gb, V, gb < NG, d + 8);
+      if (j + 1 < nj) issue(j + 1);  // the next item's loads, in flight while this one is formed
+      int cnt = 0;
+      bool keep[16];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      keep[q] = l[q] > -INFINITY && l[q] >= cut &&
-                fma(static_cast<double>(l[q]), invT, -kept) > fma(static_cast<double>(d[q]), invT, -dl);
-      cnt += keep[q] ? 1 : 0;
-    }
-    const int inc = wave_incl_scan_i32(cnt);
-    const int n_list = bcast_i32(inc, kWave - 1);
-    float2* mine_list = list + (tid / kWave) * (kWave * 16);
-    int o = inc - cnt;
+      for (int q = 0; q < 16; ++q) {
+        keep[q] = l[q] > -INFINITY && l[q] >= I.cut &&
+                  fma(static_cast<double>(l[q]), I.invT, -I.kept) > fma(static_cast<double>(d[q]), I.invT, -I.dl);
+        cnt += keep[q] ? 1 : 0;
+      }
+      const int inc = wave_incl_scan_i32(cnt);
+      const int n_list = bcast_i32(inc, kWave - 1);
+      float2* wl = list + (tid / kWave) * (kWave * 16);
+      int o = inc - cnt;
 #pragma unroll
-    for (int q = 0; q < 16; ++q)
-      if (keep[q]) mine_list[o++] = make_float2(l[q], d[q]);
-    __syncwarp();
-    double part = 0.0;
-    for (int e = lane; e < n_list; e += kWave) {
-      const float2 v = mine_list[e];
-      const double w = exp_tab(fma(static_cast<double>(v.x), invT, -kept), etab) -
-                       exp_tab(fma(static_cast<double>(v.y), invT, -dl), etab);
-      part += w > 0.0 ? w : 0.0;
+      for (int q = 0; q < 16; ++q)
+        if (keep[q]) wl[o++] = make_float2(l[q], d[q]);
+      __syncwarp();
+      double part = 0.0;
+      for (int e = lane; e < n_list; e += kWave) {
+        const float2 v = wl[e];
+        const double w = exp_tab(fma(static_cast<double>(v.x), I.invT, -I.kept), etab) -
+                         exp_tab(fma(static_cast<double>(v.y), I.invT, -I.dl), etab);
+        part += w > 0.0 ? w : 0.0;
+      }
+      const double tot = block_sum_f64<kTreeNT>(part, red);  // its leading barrier also ends the list's reads
+      if (tid == 0) a.zpart[I.zslot] = tot;
     }
-    const double tot = block_sum_f64<kTreeNT>(part, red);  // its leading barrier also ends this item's list reads
-    if (tid == 0) a.zpart[zbase + static_cast<size_t>(k - 1) * S + ch] = tot;
+    __syncthreads();  // items[] is rewritten by the next set-up
   }
 }
 
@@ -304,72 +344,101 @@ __global__ __launch_bounds__(kTreeNT) void k_tree_mass(TreeArgs a, int k) {
 // child fails (residual draw).  The test of node j takes Philox word 0 at
 // counter (j - 1, r, 0, 0); the draw record's n is the stopping node, whose
 // word 1 the pick takes.
+// Everything a test reads is staged in LDS first, in two load rounds over the
+// request's nodes (lanes over nodes): parents, tokens, node records, cuts,
+// normalisers and argmaxes, the drafter's per-depth statistics; then, per
+// node, its token's logit in its parent's target row and in the draft row of
+// the parent's depth.  The walk itself reads LDS only, apart from the masses
+// Z_m of a node at which m children have been rejected (summed in chunk
+// order, as the mass passes form c_k).
 template <int DT, int DDT>
 __global__ __launch_bounds__(kWave) void k_tree_walk(TreeArgs a) {
-  __shared__ int par[kTreeMaxNodes];
+  __shared__ int par[kTreeMaxNodes], tok[kTreeMaxNodes], am[kTreeMaxNodes];
+  __shared__ int2 kd[kTreeMaxNodes];      // {kids, depth}; kids = -1: the record fails its checks
+  __shared__ float cutv[kTreeMaxNodes];
+  __shared__ double keptv[kTreeMaxNodes];
+  __shared__ float2 lx[kTreeMaxNodes];    // node j's token: its logit in the parent's target row, in the draft row
+  __shared__ double dlse_d[64];           // the drafter's statistics per depth (b <= 64)
+  __shared__ int dam_d[64];
   __shared__ double etab[kExpTab];
-  __shared__ double Zs[kTreeMaxKids];
   const int r = blockIdx.x, lane = threadIdx.x;
   int n0, N;
   DrawRec& rec = a.rec[r];
   exp_table_init(etab);
   const bool range = tree_range_ok(a, r, n0, N);
   const bool ok = range && a.nodes[n0].valid;
-  if (!ok) {
+  auto fail = [&](bool bad_tree) {
     if (lane == 0) {
+      if (bad_tree) raise_status(a.status, SV_ST_BAD_TREE);
       a.n_acc[r] = 0;
       a.stop_node[r] = 0;
       rec.mode = kDrawNone;
     }
+  };
+  if (!ok) {
+    fail(false);  // reported by the checks
     return;
   }
-  for (int j = lane; j < N; j += kWave) par[j] = a.parent[n0 + j];
-  __syncwarp();
   const float T = a.T[r];
   const bool greedy = T == 0.0f;
   const double invT = 1.0 / static_cast<double>(T);
   const uint64_t seed = *a.seed;
-  const int V = a.V;
+  const int V = a.V, b = a.b;
+  // round 1: per node and per depth
+  for (int j = lane; j < N; j += kWave) {
+    const int g = n0 + j;
+    const TreeNode nd = a.nodes[g];
+    par[j] = a.parent[g];
+    tok[j] = a.token[g];
+    am[j] = a.row_argmax[g];
+    cutv[j] = a.row_cut[g];
+    keptv[j] = a.row_kept[g];
+    kd[j] = tree_node_ok(a, nd, r) ? make_int2(nd.kids, nd.depth) : make_int2(-1, 0);
+  }
+  if (lane < b) {
+    dlse_d[lane] = greedy ? 0.0 : a.dlse[static_cast<int64_t>(r) * b + lane];
+    dam_d[lane] = greedy ? a.dargmax[static_cast<int64_t>(r) * b + lane] : 0;
+  }
+  __syncwarp();
+  // round 2: each node's token in its parent's target row and in the draft row of the parent's depth
+  bool bad_tok = false;
+  for (int j = lane; j < N; j += kWave) {
+    float2 v = make_float2(-INFINITY, -INFINITY);
+    const int pj = par[j], x = tok[j];
+    if (j > 0 && pj >= 0 && pj < j && !greedy) {
+      const int dep = min(max(kd[pj].y, 0), b - 1);
+      if (x >= 0 && x < V) {
+        v.x = load_val<DT>(row_ptr(a.tgt, DT, n0 + pj, a.tgt_ld), x);
+        v.y = load_val<DDT>(row_ptr(a.draft, DDT, static_cast<int64_t>(r) * b + dep, a.draft_ld), x);
+      }
+    }
+    if (j > 0 && !(x >= 0 && x < V)) bad_tok = true;
+    lx[j] = v;
+  }
+  if (__ballot(bad_tok) && lane == 0) raise_status(a.status, SV_ST_BAD_TOKEN);
+  __syncwarp();
   int u = 0, n = 0;
   double cdraw = 0.0;  // > 0: residual draw at node u with draft row scale cdraw
   bool leaf = false;
   for (;;) {
-    const int g = n0 + u;
-    const TreeNode nd = a.nodes[g];
-    if (!tree_node_ok(a, nd, r) || n >= a.b + (nd.kids == 0 ? 1 : 0)) {  // overlapping or stale records
-      if (lane == 0) {
-        raise_status(a.status, SV_ST_BAD_TREE);
-        a.n_acc[r] = 0;
-        a.stop_node[r] = 0;
-        rec.mode = kDrawNone;
-      }
+    const int2 nk = kd[u];
+    if (nk.x < 0 || n >= b + (nk.x == 0 ? 1 : 0)) {  // overlapping or stale records
+      fail(true);
       return;
     }
-    const float cut = a.row_cut[g];
-    const double kept = a.row_kept[g];
-    const int am = a.row_argmax[g];
-    if (nd.kids == 0) {
+    if (nk.x == 0) {
       leaf = true;
       break;
     }
-    const int64_t drow = static_cast<int64_t>(r) * a.b + nd.depth;
-    const double dlse = greedy ? 0.0 : a.dlse[drow];
-    const int dam = greedy ? a.dargmax[drow] : 0;
-    // the masses Z_1 .. Z_{kids-1} of this node (lane-parallel sums of the partials)
-    for (int m = 1; m < nd.kids; ++m) {
-      const double* zp = a.zpart + (static_cast<size_t>(g) * (a.max_kids - 1) + (m - 1)) * a.S;
-      double part = 0.0;
-      if (!greedy)
-        for (int s = lane; s < a.S; s += kWave) part += zp[s];
-      const double tot = wave_sum_f64(part);
-      if (lane == 0) Zs[m] = tot;
-    }
-    __syncwarp();
+    const float cut = cutv[u];
+    const double kept = keptv[u];
+    const int amu = am[u];
+    const double dlse = dlse_d[nk.y];
+    const int dam = dam_d[nk.y];
+    const size_t zbase = static_cast<size_t>(n0 + u) * (a.max_kids - 1) * a.S;
     double c = 0.0, Z = 1.0;  // the current target: max(0, p - c q) / Z
     int m = 0, next = -1;
-    const char* tp = row_ptr(a.tgt, DT, g, a.tgt_ld);
-    const char* dp = row_ptr(a.draft, DDT, drow, a.draft_ld);
-    for (int j0 = u + 1; j0 < N && next < 0 && m < nd.kids; j0 += kWave) {
+    for (int j0 = u + 1; j0 < N && next < 0 && m < nk.x; j0 += kWave) {
       const int j = j0 + lane;
       uint64_t mine = __ballot(j < N && par[min(j, N - 1)] == u);
       while (mine && next < 0) {
@@ -377,22 +446,20 @@ __global__ __launch_bounds__(kWave) void k_tree_walk(TreeArgs a) {
         mine &= mine - 1;
         const int jc = j0 + jl;  // the next child in index order
         ++m;
-        const int x = a.token[n0 + jc];
+        const int x = tok[jc];
         const bool xok = x >= 0 && x < V;
         double p = 0.0, q = 0.0;
         if (xok) {
           if (greedy) {  // p and q one-hot; every residual is p again, so each child is tested against p
-            p = x == am ? 1.0 : 0.0;
+            p = x == amu ? 1.0 : 0.0;
             q = x == dam ? 1.0 : 0.0;
           } else {
-            const float l = load_val<DT>(tp, x);
-            const double p0 = l >= cut ? exp_tab(static_cast<double>(l) * invT - kept, etab) : 0.0;
-            q = exp_tab(static_cast<double>(load_val<DDT>(dp, x)) * invT - dlse, etab);
+            const float2 v = lx[jc];
+            const double p0 = v.x >= cut ? exp_tab(static_cast<double>(v.x) * invT - kept, etab) : 0.0;
+            q = exp_tab(static_cast<double>(v.y) * invT - dlse, etab);
             const double w = p0 - c * q;
             p = c == 0.0 ? p0 : (w > 0.0 ? w / Z : 0.0);
           }
-        } else if (lane == 0) {
-          raise_status(a.status, SV_ST_BAD_TOKEN);
         }
         const double uu = u24(philox_at(seed, static_cast<uint32_t>(jc - 1), static_cast<uint32_t>(r)).x);
         const bool accept = q > 0.0 ? uu < p / q : p > 0.0;
@@ -406,10 +473,12 @@ __global__ __launch_bounds__(kWave) void k_tree_walk(TreeArgs a) {
         } else if (!greedy) {
           // the next target: c_{m+1} = c_m + Z_m (c_1 = 1); a mass emptied by rounding resets it to p
           c = c == 0.0 ? 1.0 : c + Z;
-          Z = m < nd.kids ? Zs[m] : 0.0;
-          if (m < nd.kids && !(Z > 0.0)) {
-            c = 0.0;
-            Z = 1.0;
+          if (m < nk.x) {
+            Z = zsum(a.zpart + zbase + static_cast<size_t>(m - 1) * a.S, a.S);
+            if (!(Z > 0.0)) {
+              c = 0.0;
+              Z = 1.0;
+            }
           }
         }
       }
@@ -418,7 +487,7 @@ __global__ __launch_bounds__(kWave) void k_tree_walk(TreeArgs a) {
       cdraw = greedy ? 1.0 : c;
       break;
     }
-    if (lane == 0) a.path[static_cast<size_t>(r) * a.b + n] = next;
+    if (lane == 0) a.path[static_cast<size_t>(r) * b + n] = next;
     ++n;
     u = next;
   }
@@ -426,16 +495,15 @@ __global__ __launch_bounds__(kWave) void k_tree_walk(TreeArgs a) {
     a.n_acc[r] = n;
     a.stop_node[r] = u;
     const int g = n0 + u;
-    const TreeNode nd = a.nodes[g];
     rec.n = u;  // the pick's uniform: word 1 at counter (u, r, 0, 0)
     rec.bonus = leaf ? 1 : 0;
-    rec.token = a.row_argmax[g];
+    rec.token = am[u];
     rec.ncorr = 0;
     rec.trow = g;
-    rec.drow = static_cast<int64_t>(r) * a.b + (leaf ? 0 : nd.depth);
-    rec.cut = a.row_cut[g];
+    rec.drow = static_cast<int64_t>(r) * b + (leaf ? 0 : kd[u].y);
+    rec.cut = cutv[u];
     rec.invT = invT;
-    rec.kept = a.row_kept[g];
+    rec.kept = keptv[u];
     rec.invTb = 0.0;
     if (greedy) {
       rec.mode = kDrawGreedy;
@@ -445,7 +513,7 @@ __global__ __launch_bounds__(kWave) void k_tree_walk(TreeArgs a) {
       rec.dlse = 0.0;
     } else {
       rec.mode = kDrawResidual;
-      rec.dlse = a.dlse[rec.drow] - log(cdraw);
+      rec.dlse = dlse_d[kd[u].y] - log(cdraw);
     }
   }
 }

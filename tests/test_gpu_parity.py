@@ -378,7 +378,7 @@ def test_host_argument_errors():
 
 # ---------------------------------------------------------------- whole steps
 SMALL = [
-    (1, dict()),                                   # tiny fp32, T=1 x3 and greedy
+    (1, dict(steps=20)),                           # tiny fp32, T=1 x3 and greedy (the full workload)
     (2, dict(V=2053, R=4)),                        # independent draft, ragged V
     (3, dict(V=2053, R=8, steps=3)),               # DVL + independent draft
     (4, dict(V=4099, R=4)),                        # mixture, T=1.5, top-p
@@ -396,6 +396,8 @@ def test_config_small(c, kw):
         banner(f"{w.name} V={w.V} R={w.R} step={s}")
         g = run(s)
         rep = compare_step(w, g, oracle_step(w, s), rep)
+    if c == 1:  # cfg1 at its own size
+        log_parity(f"{w.name} full size, standalone, {w.steps} steps", rep)
     assert_rate(rep)
     assert _sv().sv_get_status(vs.ws) == 0
 
