@@ -504,6 +504,12 @@ def main_tree(args):
     n_acc, path, stop, token_out, is_bonus = z(R, i32), z(R * b, i32), z(R, i32), z(R, i32), z(R, i32)
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
+    if args.copy_calibration > 0:  # known-size reference for the HBM counters (untimed), as in main()
+        src = torch.ones(args.copy_calibration << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step(s, ev=None):
         t, d = tg[s % n_t], dr[s % n_d]
