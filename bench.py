@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--config", type=int, default=5, choices=(1, 2, 3, 4, 5),
                     help="5: conc 32 K=8 mixture with top-p and DVL (the headline workload); 1-4: the other "
                          "workloads")
+    ap.add_argument("--graph", action="store_true",
+                    help="also capture each step's calls as a HIP graph (one graph per step, same buffers) and time "
+                         "the replays back to back (reported as graph_ms_per_step; value stays the eager rate)")
     ap.add_argument("--tree", action="store_true",
                     help="tree verification instead of a block: conc 32, depth 16, random draft trees of at most 64 "
                          "nodes (at most 4 children per node), V 151936 bf16, T 1, top-p 0.95")
@@ -345,6 +348,7 @@ def main():
     positions = L_host.sum(axis=1)  # verified positions per step
 
     def step(s, ev=None):
+        sp = torch.cuda.current_stream(dev).cuda_stream  # the capture stream while a graph records
         tg = packed[s % n_tgt]
         pr = prop[s % n_prop]
         if dvl:
@@ -408,6 +412,21 @@ def main():
     ms_per_step = elapsed / S * 1e3
     value = float(positions.sum()) / elapsed
 
+    graph_ms = None
+    if args.graph:  # one HIP graph per step over the same buffers; replays timed back to back
+        from draft_verification_sv_amd.step import capture_graph
+
+        graphs = [capture_graph(lambda s=s: step(s)) for s in range(S)]
+        for g in graphs[:min(S, args.warmup)]:
+            g.replay()
+        torch.cuda.synchronize()
+        tg0 = time.perf_counter()
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - tg0) / S * 1e3
+        del graphs
+
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(w, args.cpu_seconds)
@@ -449,6 +468,8 @@ def main():
         "cpu_baseline": cpu,
         "device_status": status,
     }
+    if graph_ms is not None:
+        out["graph_ms_per_step"] = round(graph_ms, 5)
     print(json.dumps(out), flush=True)
 
 
