@@ -256,7 +256,8 @@ class TreeWorkload:
 
 def tree(name: str, *, R: int, b: int = 16, V: int = QWEN3_VOCAB, width: int = 4, nodes: int = 64,
          dtype: str = "bf16", T=1.0, top_p: Optional[float] = None, shape: str = "random",
-         draft_sigma: float = 1.0, seed: int = 3000, vseed: int = 11, threads: Optional[int] = None) -> TreeWorkload:
+         draft_sigma: float = 1.0, seed: int = 3000, vseed: int = 11, threads: Optional[int] = None,
+         fill: bool = False) -> TreeWorkload:
     """Draft trees per request (the budget-aware trees of tree drafters).
 
     ``shape`` "random": a node budget N_r uniform on 1..``nodes``; nodes are
@@ -269,7 +270,9 @@ def tree(name: str, *, R: int, b: int = 16, V: int = QWEN3_VOCAB, width: int = 4
     plus N(0, 1) noise of the node's own (a target's rows depend on the path).
     Drafter row d: that base plus N(0, ``draft_sigma``^2); the children of a
     depth-d node are independent samples of softmax(draft row d / T_r)
-    (Gumbel-max), its argmax at T_r = 0."""
+    (Gumbel-max), its argmax at T_r = 0.  ``fill``: every request's tree has
+    exactly ``nodes`` nodes (each node below depth b gets 1..``width``
+    children until the budget is spent)."""
     threads = threads or _default_threads()
     ss = np.random.SeedSequence([seed, R, b, V, width, nodes])
     kids_ss = ss.spawn(R)
@@ -285,12 +288,12 @@ def tree(name: str, *, R: int, b: int = 16, V: int = QWEN3_VOCAB, width: int = 4
             return [-1] + [0] * width, [0] + [1] * width
         if shape != "random":
             raise ValueError(shape)
-        budget = int(rng.integers(1, nodes + 1))
+        budget = nodes if fill else int(rng.integers(1, nodes + 1))
         par, dep = [-1], [0]
         u = 0
         while u < len(par) and len(par) < budget:
             if dep[u] < b:
-                k = int(rng.integers(1 if u == 0 else 0, width + 1))
+                k = int(rng.integers(1 if (u == 0 or fill) else 0, width + 1))
                 for _ in range(min(k, budget - len(par))):
                     par.append(u)
                     dep.append(dep[u] + 1)

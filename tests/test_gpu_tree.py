@@ -208,6 +208,19 @@ def test_tree_greedy_full_size_matches_oracle():
     assert rep["mismatches"] == 0
 
 
+def test_tree_maximum_sizes_match_oracle():
+    """Requests at the node cap (1024 nodes each), up to 16 children per node,
+    bf16 and top-p: the walk's and the checks' LDS arrays filled to their
+    ends."""
+    w = synth.tree("tree-max", R=2, b=32, V=1031, width=16, nodes=1024, T=1.0, top_p=0.9, seed=3600, fill=True)
+    assert list(np.diff(w.node_off)) == [1024, 1024] and w.max_kids <= 16
+    banner(f"sv_tree_verify maximum sizes nodes per request {list(np.diff(w.node_off))} max_kids={w.max_kids}")
+    g = gpu_tree(w)
+    assert g["status"] == 0
+    o = oracle_tree(w)
+    assert_rate(compare_tree(g, o, w.node_off, w.parent))
+
+
 def test_tree_reused_workspace_and_repeat_calls():
     """Two calls on one tree workspace left over from a different tree (and one
     filled with garbage bytes): results as from a fresh one."""
