@@ -474,6 +474,8 @@ def main():
 
 
 TREE_SHAPE = dict(R=32, b=16, width=4, nodes=64, T=1.0, top_p=0.95)
+TREE_DATA_SEED = 3900        # trees and logits
+TREE_DATA_SEED_VERIFY = 11   # verification seed of step 0 (advancing per step)
 
 
 def main_tree(args):
@@ -496,7 +498,7 @@ def main_tree(args):
     t_gen = time.time()
     sh = TREE_SHAPE
     w = synth.tree("tree-conc32-d16-n64-w4-topp", R=sh["R"], b=sh["b"], V=synth.QWEN3_VOCAB, width=sh["width"],
-                   nodes=sh["nodes"], T=sh["T"], top_p=sh["top_p"], seed=3900)
+                   nodes=sh["nodes"], T=sh["T"], top_p=sh["top_p"], seed=TREE_DATA_SEED, vseed=TREE_DATA_SEED_VERIFY)
     R, b, V = w.R, w.b, w.V
     n = int(w.node_off[-1])
     print(f"[bench] tree data generated in {time.time() - t_gen:.1f}s: {n} nodes, at most {w.max_kids} children",

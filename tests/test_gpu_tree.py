@@ -198,6 +198,26 @@ def test_tree_full_size_matches_oracle():
     assert_rate(rep)
 
 
+def test_tree_bench_workload_over_steps():
+    """The tree benchmark's own workload (bench.py --tree: its shape and data
+    seed) verified with five successive seeds, every step against the
+    oracle."""
+    import bench
+
+    sh = bench.TREE_SHAPE
+    w = synth.tree("tree-bench", R=sh["R"], b=sh["b"], V=synth.QWEN3_VOCAB, width=sh["width"], nodes=sh["nodes"],
+                   T=sh["T"], top_p=sh["top_p"], seed=bench.TREE_DATA_SEED)
+    rep = None
+    for k in range(5):
+        w.seed = bench.TREE_DATA_SEED_VERIFY + k
+        banner(f"sv_tree_verify bench workload nodes={int(w.node_off[-1])} seed={w.seed}")
+        g = gpu_tree(w)
+        assert g["status"] == 0
+        rep = compare_tree(g, oracle_tree(w), w.node_off, w.parent, report=rep)
+    log_parity(f"{w.name} (the benchmark's trees), 5 seeds", rep)
+    assert_rate(rep)
+
+
 def test_tree_greedy_full_size_matches_oracle():
     w = synth.tree("tree-conc32-greedy", R=32, b=16, V=synth.QWEN3_VOCAB, width=3, nodes=48, T=0.0, seed=3300)
     banner(f"sv_tree_verify greedy full size nodes={int(w.node_off[-1])}")
