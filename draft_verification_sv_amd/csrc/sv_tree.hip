@@ -347,17 +347,20 @@ __global__ __launch_bounds__(kTreeNT) void k_tree_mass(TreeArgs a, int k) {
 // Everything a test reads is staged in LDS first, in two load rounds over the
 // request's nodes (lanes over nodes): parents, tokens, node records, cuts,
 // normalisers and argmaxes, the drafter's per-depth statistics; then, per
-// node, its token's logit in its parent's target row and in the draft row of
-// the parent's depth.  The walk itself reads LDS only, apart from the masses
-// Z_m of a node at which m children have been rejected (summed in chunk
-// order, as the mass passes form c_k).
+// node, p of its token in its parent's target row (with the cut), q in the
+// draft row of the parent's depth, and its uniform -- none of which depends
+// on the walk.  The walk itself rescales p by the current residual (c, Z)
+// and reads LDS only, apart from the masses Z_m of a node at which m
+// children have been rejected (summed in chunk order, as the mass passes
+// form c_k).
 template <int DT, int DDT>
 __global__ __launch_bounds__(kWave) void k_tree_walk(TreeArgs a) {
   __shared__ int par[kTreeMaxNodes], tok[kTreeMaxNodes], am[kTreeMaxNodes];
   __shared__ int2 kd[kTreeMaxNodes];      // {kids, depth}; kids = -1: the record fails its checks
   __shared__ float cutv[kTreeMaxNodes];
   __shared__ double keptv[kTreeMaxNodes];
-  __shared__ float2 lx[kTreeMaxNodes];    // node j's token: its logit in the parent's target row, in the draft row
+  __shared__ double2 pq[kTreeMaxNodes];   // node j's token: p in its parent's target row (with the cut), q in the draft row
+  __shared__ float uv[kTreeMaxNodes];     // node j's uniform (word 0 of Philox at counter (j - 1, r, 0, 0))
   __shared__ double dlse_d[64];           // the drafter's statistics per depth (b <= 64)
   __shared__ int dam_d[64];
   __shared__ double etab[kExpTab];
@@ -400,20 +403,30 @@ __global__ __launch_bounds__(kWave) void k_tree_walk(TreeArgs a) {
     dam_d[lane] = greedy ? a.dargmax[static_cast<int64_t>(r) * b + lane] : 0;
   }
   __syncwarp();
-  // round 2: each node's token in its parent's target row and in the draft row of the parent's depth
+  // round 2: each node's token in its parent's target row and in the draft row of the parent's depth,
+  // and from them, lane-parallel, everything a test needs that does not depend on the walk: p (with the
+  // parent's cut) and q of the token, and the node's uniform
   bool bad_tok = false;
   for (int j = lane; j < N; j += kWave) {
-    float2 v = make_float2(-INFINITY, -INFINITY);
+    double p0 = 0.0, q = 0.0;
     const int pj = par[j], x = tok[j];
-    if (j > 0 && pj >= 0 && pj < j && !greedy) {
+    const bool xok = x >= 0 && x < V;
+    if (j > 0 && pj >= 0 && pj < j && xok) {
       const int dep = min(max(kd[pj].y, 0), b - 1);
-      if (x >= 0 && x < V) {
-        v.x = load_val<DT>(row_ptr(a.tgt, DT, n0 + pj, a.tgt_ld), x);
-        v.y = load_val<DDT>(row_ptr(a.draft, DDT, static_cast<int64_t>(r) * b + dep, a.draft_ld), x);
+      if (greedy) {  // p and q one-hot
+        p0 = x == am[pj] ? 1.0 : 0.0;
+        q = x == dam_d[dep] ? 1.0 : 0.0;
+      } else {
+        const float l = load_val<DT>(row_ptr(a.tgt, DT, n0 + pj, a.tgt_ld), x);
+        const float d = load_val<DDT>(row_ptr(a.draft, DDT, static_cast<int64_t>(r) * b + dep, a.draft_ld), x);
+        p0 = l >= cutv[pj] ? exp_tab(static_cast<double>(l) * invT - keptv[pj], etab) : 0.0;
+        q = exp_tab(static_cast<double>(d) * invT - dlse_d[dep], etab);
       }
     }
-    if (j > 0 && !(x >= 0 && x < V)) bad_tok = true;
-    lx[j] = v;
+    if (j > 0 && !xok) bad_tok = true;
+    pq[j] = make_double2(p0, q);
+    uv[j] = j > 0 ? static_cast<float>(u24(philox_at(seed, static_cast<uint32_t>(j - 1), static_cast<uint32_t>(r)).x))
+                  : 0.0f;
   }
   if (__ballot(bad_tok) && lane == 0) raise_status(a.status, SV_ST_BAD_TOKEN);
   __syncwarp();
@@ -430,11 +443,6 @@ __global__ __launch_bounds__(kWave) void k_tree_walk(TreeArgs a) {
       leaf = true;
       break;
     }
-    const float cut = cutv[u];
-    const double kept = keptv[u];
-    const int amu = am[u];
-    const double dlse = dlse_d[nk.y];
-    const int dam = dam_d[nk.y];
     const size_t zbase = static_cast<size_t>(n0 + u) * (a.max_kids - 1) * a.S;
     double c = 0.0, Z = 1.0;  // the current target: max(0, p - c q) / Z
     int m = 0, next = -1;
@@ -446,22 +454,12 @@ __global__ __launch_bounds__(kWave) void k_tree_walk(TreeArgs a) {
         mine &= mine - 1;
         const int jc = j0 + jl;  // the next child in index order
         ++m;
-        const int x = tok[jc];
-        const bool xok = x >= 0 && x < V;
-        double p = 0.0, q = 0.0;
-        if (xok) {
-          if (greedy) {  // p and q one-hot; every residual is p again, so each child is tested against p
-            p = x == amu ? 1.0 : 0.0;
-            q = x == dam ? 1.0 : 0.0;
-          } else {
-            const float2 v = lx[jc];
-            const double p0 = v.x >= cut ? exp_tab(static_cast<double>(v.x) * invT - kept, etab) : 0.0;
-            q = exp_tab(static_cast<double>(v.y) * invT - dlse, etab);
-            const double w = p0 - c * q;
-            p = c == 0.0 ? p0 : (w > 0.0 ? w / Z : 0.0);
-          }
-        }
-        const double uu = u24(philox_at(seed, static_cast<uint32_t>(jc - 1), static_cast<uint32_t>(r)).x);
+        // greedy: p and q one-hot, and every residual is p again (c stays 0), so each child is tested against p
+        const double2 v = pq[jc];
+        const double q = v.y;
+        const double w = v.x - c * q;
+        const double p = c == 0.0 ? v.x : (w > 0.0 ? w / Z : 0.0);
+        const double uu = static_cast<double>(uv[jc]);
         const bool accept = q > 0.0 ? uu < p / q : p > 0.0;
         if (lane == 0) {
           if (a.p_out) a.p_out[n0 + jc] = p;
