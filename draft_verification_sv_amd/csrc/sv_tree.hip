@@ -387,7 +387,7 @@ __global__ __launch_bounds__(kWave) void k_tree_walk(TreeArgs a) {
   const double invT = 1.0 / static_cast<double>(T);
   const uint64_t seed = *a.seed;
   const int V = a.V, b = a.b;
-  // round 1: per node and per depth
+  // first loads: per node and per depth
   for (int j = lane; j < N; j += kWave) {
     const int g = n0 + j;
     const TreeNode nd = a.nodes[g];
@@ -403,7 +403,7 @@ __global__ __launch_bounds__(kWave) void k_tree_walk(TreeArgs a) {
     dam_d[lane] = greedy ? a.dargmax[static_cast<int64_t>(r) * b + lane] : 0;
   }
   __syncwarp();
-  // round 2: each node's token in its parent's target row and in the draft row of the parent's depth,
+  // second loads: each node's token in its parent's target row and in the draft row of the parent's depth,
   // and from them, lane-parallel, everything a test needs that does not depend on the walk: p (with the
   // parent's cut) and q of the token, and the node's uniform
   bool bad_tok = false;
