@@ -87,7 +87,9 @@ def rows_kernel(config: int) -> str:
 KERNEL_SOURCES = {
     "k_rows_mix": ("sv_mix.hip", "sv_rows_dev.hpp", "sv_device.hpp"),
     "k_rows_dense": ("sv_rows.hip", "sv_rows_dev.hpp", "sv_device.hpp"),
+    "k_row_stats": ("sv_rows.hip", "sv_rows_dev.hpp", "sv_device.hpp"),
 }
+TREE_TRAFFIC_KEY = "tree:k_row_stats"  # the tree step's node-row statistics launch
 
 
 def kernel_source_hash(kernel: str) -> str:
@@ -101,23 +103,26 @@ def traffic_key(config: int) -> str:
     return f"cfg{config}:{rows_kernel(config)}"
 
 
-def load_traffic(config: int):
+def load_traffic(config: int, key: str | None = None, kernel: str | None = None):
     """HBM traffic per launch of the rows kernel from committed rocprofv3 counter
     runs of this workload, if they were taken on the current kernel source; else None."""
+    key = key or traffic_key(config)
+    kernel = kernel or rows_kernel(config)
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
     try:
-        rec = json.load(open(p)).get(traffic_key(config))
+        rec = json.load(open(p)).get(key)
     except (ValueError, AttributeError):
         return None
-    if not rec or rec.get("source_sha") != kernel_source_hash(rows_kernel(config)):
+    if not rec or rec.get("source_sha") != kernel_source_hash(kernel):
         return None
     return rec.get("bytes_per_launch")
 
 
-def _counter_rows(path: str, counter: str):
-    """(kernel name, value) per dispatch of one counter in a rocprofv3 CSV or result database."""
+def _counter_rows(path: str, counter: str, grid: int | None = None):
+    """(kernel name, value) per dispatch of one counter in a rocprofv3 CSV or result database
+    (databases: only dispatches of `grid` threads when given)."""
     import csv
 
     per = {}
@@ -125,8 +130,10 @@ def _counter_rows(path: str, counter: str):
         import sqlite3
 
         con = sqlite3.connect(path)
-        for key, name, val in con.execute("select dispatch_id, kernel_name, value from counters_collection "
-                                          "where counter_name = ?", (counter,)):
+        for key, name, val, gs in con.execute("select dispatch_id, kernel_name, value, grid_size from "
+                                              "counters_collection where counter_name = ?", (counter,)):
+            if grid is not None and gs != grid and "neg_kernel" not in name:
+                continue
             k0 = per.get(key)
             per[key] = (name, float(val) + (k0[1] if k0 else 0.0))
         return list(per.values())
@@ -155,13 +162,23 @@ def algorithmic_rows_bytes(config: int) -> float:
     return float((pos + R) * V * esz + pos * max(K, 1) * V * esz)
 
 
-def summarize_counters(config: int, fetch_csv: str, write_csv: str, copy_bytes: int):
+def summarize_counters(config: int, fetch_csv: str, write_csv: str, copy_bytes: int, tree: bool = False):
     """Per-launch HBM traffic of the rows kernel: FETCH_SIZE and WRITE_SIZE (KiB per
     dispatch), each scaled by what the same counter reads for the calibration kernel
-    (torch.neg over copy_bytes: copy_bytes read and copy_bytes written)."""
+    (torch.neg over copy_bytes: copy_bytes read and copy_bytes written).  tree: the
+    tree step's node-row statistics launch (k_row_stats over the node rows)."""
     import numpy as np
 
-    kernel = rows_kernel(config)
+    kernel = "k_row_stats" if tree else rows_kernel(config)
+    grid = None
+    if tree:
+        import synth
+
+        sh = TREE_SHAPE
+        tw = synth.tree("shape", R=sh["R"], b=sh["b"], V=synth.QWEN3_VOCAB, width=sh["width"], nodes=sh["nodes"],
+                        T=sh["T"], top_p=sh["top_p"], seed=TREE_DATA_SEED, vseed=TREE_DATA_SEED_VERIFY)
+        n_nodes = int(tw.node_off[-1])
+        grid = n_nodes * 512  # one 512-thread block per node row
 
     def split(rows):
         copy = [v for n, v in rows if "neg_kernel" in n]
@@ -171,9 +188,9 @@ def summarize_counters(config: int, fetch_csv: str, write_csv: str, copy_bytes: 
                              f"{sorted(set(n for n, _ in rows))}")
         return max(copy), kern
 
-    algorithmic = algorithmic_rows_bytes(config)
-    cf, kf = split(_counter_rows(fetch_csv, "FETCH_SIZE"))
-    cw, kw = split(_counter_rows(write_csv, "WRITE_SIZE"))
+    algorithmic = float(n_nodes * 151936 * 2) if tree else algorithmic_rows_bytes(config)
+    cf, kf = split(_counter_rows(fetch_csv, "FETCH_SIZE", grid))
+    cw, kw = split(_counter_rows(write_csv, "WRITE_SIZE", grid))
     known_kib = copy_bytes / 1024.0
     sf, sw = known_kib / cf, known_kib / cw
     fetch_b = float(np.mean(kf)) * 1024.0 * sf
@@ -191,7 +208,7 @@ def summarize_counters(config: int, fetch_csv: str, write_csv: str, copy_bytes: 
             allrec = json.load(open(path))
         except ValueError:
             allrec = {}
-    allrec[traffic_key(config)] = rec
+    allrec[TREE_TRAFFIC_KEY if tree else traffic_key(config)] = rec
     with open(path, "w") as f:
         json.dump(allrec, f, indent=1)
     print(json.dumps(rec, indent=1))
@@ -250,7 +267,7 @@ def main():
         summarize_db(args.summarize_db)
         return
     if args.summarize_counters:
-        summarize_counters(args.config, *args.summarize_counters, args.copy_calibration << 20)
+        summarize_counters(args.config, *args.summarize_counters, args.copy_calibration << 20, tree=args.tree)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this path runs on a single GPU)",
@@ -595,7 +612,8 @@ def main_tree(args):
         "step_frac_of_peak": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
         "roofline": {"kernel": "k_row_stats (sv_topp_threshold over the node rows)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": load_traffic(0, TREE_TRAFFIC_KEY, "k_row_stats"),
                      "avg_launch_us": round(stats_ms * 1e3, 2), "algorithmic_bytes_per_launch": stats_bytes},
         "cpu_baseline": cpu,
         "device_status": status,
