@@ -72,6 +72,45 @@ def test_every_declared_symbol_is_exported(sv):
     assert sorted(sv.EXPORTS) == sorted(declared_functions())
 
 
+C_CONSUMER = r"""
+#include <stdio.h>
+#include "sv.h"
+int main(void) {
+  size_t ws = 0, tws = 0;
+  if (sv_workspace_bytes(32, 16, 8, 151936, &ws) != SV_OK || ws == 0) return 1;
+  if (sv_tree_workspace_bytes(1024, 4, 151936, &tws) != SV_OK || tws == 0) return 2;
+  if (sv_tree_workspace_bytes(1024, 17, 151936, &tws) != SV_ERR_ARG) return 3;
+  if (sv_selftest_philox_host() != 0 || sv_selftest_rows_host() != 0) return 4;
+  /* every pointer NULL: rejected on the host, nothing launched */
+  if (sv_accept(NULL, SV_BF16, 64, 60, NULL, NULL, 1, 1, NULL, NULL, NULL, NULL, NULL, SV_Q_DENSE, NULL, SV_BF16, 64,
+                NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL) != SV_ERR_ARG) return 5;
+  printf("%s\n", sv_status_string(SV_ERR_WORKSPACE));
+  return 0;
+}
+"""
+
+
+def test_header_compiles_as_c_and_links(sv, tmp_path):
+    """A C99 program that includes include/sv.h (strict, -pedantic, warnings as
+    errors) links against libsv.so and calls its host-side entry points: the
+    boundary needs no C++ and no torch."""
+    import shutil
+    import subprocess
+
+    if shutil.which("gcc") is None:
+        pytest.skip("no gcc")
+    src = tmp_path / "consumer.c"
+    src.write_text(C_CONSUMER)
+    exe = tmp_path / "consumer"
+    libdir = os.path.dirname(sv.LIB_PATH)
+    subprocess.check_call(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I",
+                           os.path.join(ROOT, "include"), str(src), "-o", str(exe), "-L", libdir, "-lsv",
+                           f"-Wl,-rpath,{libdir}"])
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0, (out.returncode, out.stderr)
+    assert out.stdout.strip() == "workspace too small"
+
+
 def test_host_selftests(sv):
     assert sv.selftest_host() == {"rows": 0, "philox": 0}
 
