@@ -50,7 +50,8 @@ def _dvl_cases():
     rng = np.random.default_rng(7)
     cases = []
     # R*b up to 8192 keeps the scores in LDS, beyond that in global memory
-    for R, b in [(1, 1), (3, 5), (32, 16), (7, 64), (64, 16), (65, 16), (300, 16), (600, 16)]:
+    # (8192 and 8193: the two sides of that switch)
+    for R, b in [(1, 1), (3, 5), (32, 16), (7, 64), (64, 16), (65, 16), (300, 16), (512, 16), (8193, 1), (600, 16)]:
         for kind in ("beta", "ties", "signed_zeros"):
             if kind == "beta":
                 a = rng.beta(8, 2, size=(R, b)).astype(np.float32)

@@ -241,6 +241,26 @@ def test_tree_maximum_sizes_match_oracle():
     assert_rate(compare_tree(g, o, w.node_off, w.parent))
 
 
+def test_tree_deepest_accepted_paths():
+    """Chains as deep as the block allows (b = 64) whose every token is its
+    parent's target argmax, at T = 0: every test accepts, so the walk runs the
+    whole chain, fills the path array to its end and draws the bonus token at
+    depth 64 (the chains of other lengths stop earlier, at their leaves)."""
+    w = synth.tree("tree-deep", R=8, b=64, V=1031, T=0.0, shape="chain", seed=3800)
+    vals = synth.values(w.tgt)
+    for r in range(w.R):
+        n0, n1 = int(w.node_off[r]), int(w.node_off[r + 1])
+        for j in range(n0 + 1, n1):
+            w.token[j] = int(np.argmax(vals[j - 1]))  # the parent of node j is node j - 1
+    lengths = np.diff(w.node_off) - 1
+    banner(f"sv_tree_verify deepest accepted paths, chain lengths {list(lengths)}")
+    g = gpu_tree(w)
+    assert g["status"] == 0
+    o = oracle_tree(w)
+    assert np.array_equal(o["n_acc"], lengths) and np.array_equal(g["n_acc"], lengths)
+    assert_rate(compare_tree(g, o, w.node_off, w.parent))
+
+
 def test_tree_reused_workspace_and_repeat_calls():
     """Two calls on one tree workspace left over from a different tree (and one
     filled with garbage bytes): results as from a fresh one."""
