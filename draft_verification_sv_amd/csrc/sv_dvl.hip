@@ -241,6 +241,141 @@ __global__ __launch_bounds__(kDvlNT) void k_dvl(const float* __restrict__ a, int
   }
 }
 
+// ------------------------------------------------------------------ short-block path
+// When b divides 64, R <= 64 and R * b <= NT (R = 32, b = 16 at the largest
+// configuration), each request's positions are consecutive lanes of one
+// wave, and the whole call is a few wave-level steps with seven block
+// barriers (the general kernel above takes about twenty):
+//   1. running products along each request's lanes: step t hands the
+//      products one lane to the right (DPP wave shift) and lane i = t
+//      multiplies by its own estimate, so every product is formed with the
+//      same roundings as one running product over the request;
+//   2. a histogram of the candidates' keys by their top 12 bits; a block scan
+//      from the top finds the digit holding the B-th largest and how many of
+//      its keys are taken;
+//   3. that digit's candidates are listed in LDS, and the one whose rank among
+//      them (selection key, then position: (s desc, r asc, i asc)) is the
+//      remainder minus one is the threshold; a candidate is taken iff its
+//      (key, position) order word is at or above the threshold's;
+//   4. L_r by ballot over the request's lanes; offsets by a wave scan.
+constexpr int kFastDigitBits = 12;                       // first digit: key bits 29..18
+constexpr int kFastBins = 1 << kFastDigitBits;
+constexpr int kFastShift = 30 - kFastDigitBits;
+
+template <int NT>
+__global__ __launch_bounds__(NT) void k_dvl_lanes(const float* __restrict__ a, int R, int b,
+                                                 const int32_t* __restrict__ block_len,
+                                                 const int32_t* __restrict__ budget, float* __restrict__ s,
+                                                 int32_t* __restrict__ L, int32_t* __restrict__ pos_off,
+                                                 int32_t* __restrict__ tgt_off, uint32_t* status) {
+  constexpr int NW = NT / kWave, kPer = kFastBins / NT;
+  static_assert(kPer * NT == kFastBins, "digits must split evenly over the block");
+  __shared__ uint32_t hist[kFastBins];
+  __shared__ uint64_t listed[NT];
+  __shared__ int wtot[NW];
+  __shared__ int lens[kWave];
+  __shared__ int sh_listed, sh_digit, sh_rem;
+  __shared__ uint64_t sh_thr;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+  const int n = R * b;
+  const bool in = tid < n;
+  const int r = tid / b, i = tid - r * b;
+  // every global load issued before any is used
+  const float av = in ? a[tid] : 0.0f;
+  const int blr = block_len && in ? block_len[r] : b;
+  int B = *budget;
+  for (int k = tid; k < kFastBins; k += NT) hist[k] = 0u;
+  if (tid == 0) sh_listed = 0;
+  if (B < 0) {
+    if (tid == 0) raise_status(status, SV_ST_BAD_BUDGET);
+    B = 0;
+  }
+  const int br = min(max(blr, 0), b);
+  const bool cand = in && i < br;
+  if (__ballot(in && i == 0 && block_len && (blr < 0 || blr > b)) && lane == 0) raise_status(status, SV_ST_BAD_BLOCK);
+  if (__ballot(cand && !(av >= 0.0f && av <= 1.0f)) && lane == 0) raise_status(status, SV_ST_BAD_SCORE);
+  // 1. running products (lanes of one request are consecutive in the wave)
+  float run = 1.0f * av;
+  for (int t = 1; t < b; ++t) {
+    const float left = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(run), 0x138, 0xF, 0xF, false));
+    run = i == t ? left * av : run;  // wave_shr:1: lane l reads lane l - 1
+  }
+  const float score = cand ? run : 0.0f;
+  const uint32_t key = cand ? select_key(run) : 0u;
+  const uint32_t digit = key >> kFastShift;
+  const uint64_t ord = cand ? (static_cast<uint64_t>(key) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(tid)) : 0ull;
+  __syncthreads();  // the histogram and the list are cleared
+  // 2. histogram of the candidates' first digits, crossing digit from the top
+  if (cand) atomicAdd(&hist[digit], 1u);
+  __syncthreads();
+  int hv[kPer], hs = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    hv[j] = static_cast<int>(hist[kFastBins - 1 - (tid * kPer + j)]);
+    hs += hv[j];
+  }
+  const int inc = wave_incl_scan_i32(hs);
+  if (lane == kWave - 1) wtot[wv] = inc;
+  __syncthreads();
+  int base = 0, ncand = 0;
+#pragma unroll
+  for (int k = 0; k < NW; ++k) {
+    base += k < wv ? wtot[k] : 0;
+    ncand += wtot[k];
+  }
+  const bool all = B >= ncand, none = B == 0;
+  const int excl = base + inc - hs;
+  if (!all && !none && excl < B && B <= excl + hs) {
+    int run_c = excl;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      if (run_c < B && B <= run_c + hv[j]) {
+        sh_digit = kFastBins - 1 - (tid * kPer + j);
+        sh_rem = B - run_c;
+      }
+      run_c += hv[j];
+    }
+  }
+  __syncthreads();
+  // 3. the threshold among the crossing digit's candidates
+  uint64_t thr = 0;
+  if (!all && !none) {
+    const bool mine = cand && digit == static_cast<uint32_t>(sh_digit);
+    if (mine) listed[atomicAdd(&sh_listed, 1)] = ord;
+    __syncthreads();
+    const int m = sh_listed, rem = sh_rem;
+    if (mine) {
+      int rank = 0;
+      for (int k = 0; k < m; ++k) rank += listed[k] > ord ? 1 : 0;
+      if (rank == rem - 1) sh_thr = ord;
+    }
+    __syncthreads();
+    thr = sh_thr;
+  }
+  const bool take = cand && (all || (!none && ord >= thr));
+  // 4. L_r by ballot over the request's lanes, then the offsets
+  const uint64_t tk = __ballot(take);
+  if (in && i == 0) {
+    const uint64_t seg = b == kWave ? ~0ull : ((1ull << b) - 1ull) << lane;
+    lens[r] = __popcll(tk & seg);
+  }
+  __syncthreads();
+  if (wv == 0) {
+    const int Lr = lane < R ? lens[lane] : 0;
+    const int incl = wave_incl_scan_i32(Lr);
+    if (lane < R) {
+      L[lane] = Lr;
+      pos_off[lane] = incl - Lr;
+      tgt_off[lane] = incl - Lr + lane;
+    }
+    if (lane == R - 1) {
+      pos_off[R] = incl;
+      tgt_off[R] = incl + R;
+    }
+  }
+  if (in) s[tid] = score;
+}
+
 }  // namespace sv
 
 using namespace sv;
@@ -252,6 +387,20 @@ extern "C" int32_t dvl_alloc_pack(const float* a, int32_t R, int32_t b, const in
   if (R < 1 || b < 1 || b > 64 || static_cast<long long>(R) * b > (1LL << 24)) return SV_ERR_ARG;
   if (ws_bytes < 256) return SV_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  const int n = R * b;
+  if ((b & (b - 1)) == 0 && R <= kWave && n <= 1024) {  // b divides 64: the short-block path
+    uint32_t* stw = status_word(ws);
+    if (n <= 256)
+      hipLaunchKernelGGL(k_dvl_lanes<256>, dim3(1), dim3(256), 0, st, a, R, b, block_len, budget, s, L, pos_off,
+                         tgt_off, stw);
+    else if (n <= 512)
+      hipLaunchKernelGGL(k_dvl_lanes<512>, dim3(1), dim3(512), 0, st, a, R, b, block_len, budget, s, L, pos_off,
+                         tgt_off, stw);
+    else
+      hipLaunchKernelGGL(k_dvl_lanes<1024>, dim3(1), dim3(1024), 0, st, a, R, b, block_len, budget, s, L, pos_off,
+                         tgt_off, stw);
+    return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
+  }
   if (R * b <= kDvlLds)
     hipLaunchKernelGGL(k_dvl<true>, dim3(1), dim3(kDvlNT), 0, st, a, R, b, block_len, budget, s, L, pos_off,
                        tgt_off, status_word(ws));
