@@ -370,11 +370,12 @@ struct RowPart {
 // [branch argmax parts, R * K * b * kMixParts keys]
 // [soft branch rows, R * K * b each: lse (double), argmax (int32), max (float)]
 // [split-row parts, (R * (b + 1) + R * b) * kDenseMaxParts RowPart records]
+// [split-row arrival counts, R * (b + 1) + R * b; zero between launches]
 // Cross-block results travel through kernel boundaries (stream order), not
 // through in-kernel fences: a device-scope release on gfx950 writes back the
 // L2, which is far too costly to pay once per block.
 struct WsLayout {
-  size_t status, rec, sub, bkey, blse, barg, bmax, rpart, total;
+  size_t status, rec, sub, bkey, blse, barg, bmax, rpart, rcount, total;
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -390,7 +391,8 @@ __host__ __device__ inline WsLayout ws_layout(int R, int b, int K, int V) {
   l.barg = l.blse + align256(sizeof(double) * kb);
   l.bmax = l.barg + align256(sizeof(int32_t) * kb);
   l.rpart = l.bmax + align256(sizeof(float) * kb);
-  l.total = l.rpart + align256(sizeof(RowPart) * static_cast<size_t>(R) * (2 * b + 1) * kDenseMaxParts);
+  l.rcount = l.rpart + align256(sizeof(RowPart) * static_cast<size_t>(R) * (2 * b + 1) * kDenseMaxParts);
+  l.total = l.rcount + align256(sizeof(uint32_t) * static_cast<size_t>(R) * (2 * b + 1));
   return l;
 }
 

@@ -29,14 +29,59 @@ __global__ __launch_bounds__(kRowNT) void k_row_stats(RowArgs a) {
   stats_block<DT>(a, blockIdx.x, hist, sh);
 }
 
+// A part record through agent-scope atomics: the parts of a row are written
+// and read by different blocks of one launch, which may sit on different
+// compute dies (the stores reach the device-coherent level; the loads read it).
+__device__ __forceinline__ void store_part(RowPart* dst, const RowPart& o) {
+  static_assert(sizeof(RowPart) == 32, "a part record is four 8-byte words");
+  const uint64_t* w = reinterpret_cast<const uint64_t*>(&o);
+  uint64_t* d = reinterpret_cast<uint64_t*>(dst);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) __hip_atomic_store(d + k, w[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The row's statistics from its P parts, by one wave (lane k < P reads part
+// k's record with agent-scope atomic loads): maximum and argmax key by max,
+// the sums rescaled to the row maximum in double with the parts' own scale
+// constant, lse = M / T + log(S).
+__device__ __forceinline__ void merge_parts_wave(const RowArgs& a, int p, int P, const RowPart* rec) {
+  const int lane = threadIdx.x & (kWave - 1);
+  uint64_t w[4] = {0, 0, 0, 0};
+  if (lane < P)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w[j] = __hip_atomic_load(reinterpret_cast<const uint64_t*>(rec + lane) + j, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+  RowPart r;
+  __builtin_memcpy(&r, w, sizeof(RowPart));
+  const float Mk = lane < P ? r.M : -INFINITY;
+  const float M = wave_max_f32(Mk);
+  const uint64_t key = wave_max_u64(lane < P ? r.key : 0ull);
+  const float T = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(r.T)));  // lane 0: part 0
+  const int am = static_cast<int>(argmax_token(key));
+  if (T == 0.0f) {
+    if (lane == 0) write_row(a, p, M, am, 0.0, M, 0.0);
+    return;
+  }
+  const double c2 = static_cast<double>(soft_c2(T));
+  const double term = Mk > -INFINITY ? r.S * exp2((static_cast<double>(Mk) - static_cast<double>(M)) * c2) : 0.0;
+  const double S = wave_sum_f64(term);
+  if (lane == 0) {
+    const double lse = static_cast<double>(M) / static_cast<double>(T) + log(S);
+    write_row(a, p, M, am, lse, -INFINITY, lse);
+  }
+}
+
 // Part `part` of row p of a (sv_verify_rows_dense).  A bf16 row without a
 // top-p cut is streamed as P blocks, each leaving its partial statistics in
-// parts[p * P + part]; any other row is done whole by part 0, which marks it
-// unsplit.  kCut = false: no row of a has a top-p value (a.top_p is null), so
-// the cut's histogram code, table and LDS are left out.
+// parts[p * P + part] and counting itself in count[p]; the block that arrives
+// last merges the parts and writes the row (and sets count[p] back to 0).  Any
+// other row is done whole by part 0, which marks it unsplit.  kCut = false: no
+// row of a has a top-p value (a.top_p is null), so the cut's histogram code,
+// table and LDS are left out.
 template <int DT, int NT, int BATCH, bool kCut>
-__device__ __forceinline__ void stats_part(const RowArgs& a, int p, int part, int P, RowPart* parts, uint32_t* hist,
-                                           RowShared<NT>& sh) {
+__device__ __forceinline__ void stats_part(const RowArgs& a, int p, int part, int P, RowPart* parts, uint32_t* count,
+                                           uint32_t* hist, RowShared<NT>& sh) {
   const int total = a.row_off[a.R];
   if (p == 0 && part == 0 && threadIdx.x == 0 && (a.row_off[0] != 0 || total > a.max_rows || total < 0))
     raise_status(a.status, SV_ST_BAD_OFFSETS);
@@ -57,15 +102,24 @@ __device__ __forceinline__ void stats_part(const RowArgs& a, int p, int part, in
   const int v1 = static_cast<int>(static_cast<int64_t>(nvec) * (part + 1) / P);
   const StreamPart sp = stream_part_bf16<NT, BATCH>(static_cast<const uint16_t*>(l.rowp), a.V, v0, v1, part == P - 1,
                                                      l.T, a.status, sh);
-  if (threadIdx.x == 0) {
-    RowPart o;
-    o.S = sp.S;
-    o.key = sp.key;
-    o.M = sp.M;
-    o.T = l.T;
-    o.split = 1;
-    o.pad = 0;
-    rec[part] = o;
+  if (threadIdx.x < kWave) {  // wave 0
+    uint32_t arrived = 0;
+    if (threadIdx.x == 0) {
+      RowPart o;
+      o.S = sp.S;
+      o.key = sp.key;
+      o.M = sp.M;
+      o.T = l.T;
+      o.split = 1;
+      o.pad = 0;
+      store_part(rec + part, o);
+      __builtin_amdgcn_s_waitcnt(0);  // the record is at the device-coherent level before the part counts itself in
+      arrived = __hip_atomic_fetch_add(count + p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (__builtin_amdgcn_readfirstlane(arrived) == static_cast<uint32_t>(P - 1)) {  // the row's last part
+      if (threadIdx.x == 0) __hip_atomic_store(count + p, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      merge_parts_wave(a, p, P, rec);
+    }
   }
 }
 
@@ -78,48 +132,14 @@ __device__ __forceinline__ void stats_part(const RowArgs& a, int p, int part, in
 // kCut is false when no target row can either.
 template <int DT, int DDT, bool kCut>
 __global__ __launch_bounds__(kDenseNT) void k_rows_dense(RowArgs ta, RowArgs da, int n_tgt, int P, RowPart* tparts,
-                                                         RowPart* dparts) {
+                                                         RowPart* dparts, uint32_t* tcount, uint32_t* dcount) {
   __shared__ RowShared<kDenseNT> sh;
   __shared__ uint32_t hist[kCut && DT == SV_BF16 ? kHistWords : 1];
   const int q = blockIdx.x / P, part = blockIdx.x % P;
   if (q < n_tgt)
-    stats_part<DT, kDenseNT, kDenseBatch, kCut>(ta, q, part, P, tparts, hist, sh);
+    stats_part<DT, kDenseNT, kDenseBatch, kCut>(ta, q, part, P, tparts, tcount, hist, sh);
   else
-    stats_part<DDT, kDenseNT, kDenseBatch, false>(da, q - n_tgt, part, P, dparts, hist, sh);
-}
-
-// Merge of the split rows' parts (one thread per row): maximum and argmax key
-// by max, the sums rescaled to the row maximum in double with the parts' own
-// scale constant, lse = M / T + log(S).
-__global__ __launch_bounds__(256) void k_rows_merge(RowArgs ta, RowArgs da, int n_tgt, int n_all, int P,
-                                                    RowPart* tparts, RowPart* dparts) {
-  const int q = blockIdx.x * blockDim.x + threadIdx.x;
-  if (q >= n_all) return;
-  const bool tgt = q < n_tgt;
-  const RowArgs& a = tgt ? ta : da;
-  const int p = tgt ? q : q - n_tgt;
-  const int total = a.row_off[a.R];
-  if (p >= total || total > a.max_rows) return;
-  const RowPart* rec = (tgt ? tparts : dparts) + static_cast<size_t>(p) * P;
-  if (!rec[0].split) return;
-  float M = -INFINITY;
-  uint64_t key = 0;
-  for (int k = 0; k < P; ++k) {
-    M = fmaxf(M, rec[k].M);
-    key = rec[k].key > key ? rec[k].key : key;
-  }
-  const float T = rec[0].T;
-  const int am = static_cast<int>(argmax_token(key));
-  if (T == 0.0f) {
-    write_row(a, p, M, am, 0.0, M, 0.0);
-    return;
-  }
-  const double c2 = static_cast<double>(soft_c2(T));
-  double S = 0.0;
-  for (int k = 0; k < P; ++k)
-    if (rec[k].M > -INFINITY) S += rec[k].S * exp2((static_cast<double>(rec[k].M) - static_cast<double>(M)) * c2);
-  const double lse = static_cast<double>(M) / static_cast<double>(T) + log(S);
-  write_row(a, p, M, am, lse, -INFINITY, lse);
+    stats_part<DDT, kDenseNT, kDenseBatch, false>(da, q - n_tgt, part, P, dparts, dcount, hist, sh);
 }
 
 }  // namespace sv
@@ -202,13 +222,13 @@ extern "C" int32_t sv_selftest_rows_host(void) {
 // The cut's histogram (and its LDS, table and registers) only where a top-p value is given.
 template <int DT, int DDT>
 static int32_t launch_dense(const RowArgs& ta, const RowArgs& da, int32_t n_tgt, int P, RowPart* tparts,
-                            RowPart* dparts, unsigned grid, hipStream_t s) {
+                            RowPart* dparts, uint32_t* tcount, uint32_t* dcount, unsigned grid, hipStream_t s) {
   if (ta.top_p)
     hipLaunchKernelGGL((k_rows_dense<DT, DDT, true>), dim3(grid), dim3(kDenseNT), 0, s, ta, da, n_tgt, P, tparts,
-                       dparts);
+                       dparts, tcount, dcount);
   else
     hipLaunchKernelGGL((k_rows_dense<DT, DDT, false>), dim3(grid), dim3(kDenseNT), 0, s, ta, da, n_tgt, P, tparts,
-                       dparts);
+                       dparts, tcount, dcount);
   return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
 }
 
@@ -242,18 +262,17 @@ extern "C" int32_t sv_verify_rows_dense(const void* tgt_logits, int32_t dtype, i
   const unsigned grid = n_all * static_cast<unsigned>(P);
   RowPart* tparts = reinterpret_cast<RowPart*>(static_cast<char*>(ws) + l.rpart);
   RowPart* dparts = tparts + static_cast<size_t>(R) * (b + 1) * P;
+  uint32_t* tcount = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + l.rcount);
+  uint32_t* dcount = tcount + static_cast<size_t>(R) * (b + 1);
   RowArgs ta{tgt_logits, tgt_ld, V, tgt_off, 0, R, max_rows, temperature, top_p, row_max, row_argmax, row_lse,
              row_cut, row_kept_lse, status_word(ws)};
   RowArgs da{draft_logits, draft_ld, V, pos_off, b, R, max_pos, temperature, nullptr, draft_max, draft_argmax,
              draft_lse, nullptr, nullptr, status_word(ws)};
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool t16 = dtype == SV_BF16, d16 = draft_dtype == SV_BF16;
-  const int32_t st = t16 ? (d16 ? launch_dense<SV_BF16, SV_BF16>(ta, da, max_rows, P, tparts, dparts, grid, s)
-                                : launch_dense<SV_BF16, SV_F32>(ta, da, max_rows, P, tparts, dparts, grid, s))
-                         : (d16 ? launch_dense<SV_F32, SV_BF16>(ta, da, max_rows, P, tparts, dparts, grid, s)
-                                : launch_dense<SV_F32, SV_F32>(ta, da, max_rows, P, tparts, dparts, grid, s));
-  if (st != SV_OK) return st;
-  hipLaunchKernelGGL(k_rows_merge, dim3((n_all + 255) / 256), dim3(256), 0, s, ta, da, max_rows,
-                     static_cast<int>(n_all), P, tparts, dparts);
-  return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
+  const int32_t st = t16 ? (d16 ? launch_dense<SV_BF16, SV_BF16>(ta, da, max_rows, P, tparts, dparts, tcount, dcount, grid, s)
+                                : launch_dense<SV_BF16, SV_F32>(ta, da, max_rows, P, tparts, dparts, tcount, dcount, grid, s))
+                         : (d16 ? launch_dense<SV_F32, SV_BF16>(ta, da, max_rows, P, tparts, dparts, tcount, dcount, grid, s)
+                                : launch_dense<SV_F32, SV_F32>(ta, da, max_rows, P, tparts, dparts, tcount, dcount, grid, s));
+  return st;
 }

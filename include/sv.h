@@ -39,7 +39,10 @@
  *    so calls on different streams may share it), one draw record per
  *    request and the draw's sums per 512-value sub-chunk of the drawn row
  *    (two draws -- sv_residual_sample or sv_accept_sample -- that share a
- *    workspace must not overlap).  Only the status word outlives a call.
+ *    workspace must not overlap), and sv_verify_rows_dense's split-row part
+ *    records and arrival counts (two such calls that share a workspace must
+ *    not overlap either).  Only the status word and the arrival counts
+ *    (zero between calls, from sv_workspace_init on) outlive a call.
  *  - Requests r = 0..R-1, draft block of b positions, vocabulary V.
  *    L_r = pos_off[r+1] - pos_off[r] is the number of verified positions of
  *    request r (0 <= L_r <= b).  The target gives L_r + 1 rows per request:
@@ -236,8 +239,11 @@ int32_t sv_verify_rows(const void* tgt_logits, int32_t dtype, int64_t tgt_ld, in
  * its blocks take target rows first and draft rows after, so both read
  * streams share every compute unit.  Same method and pages as those two calls;
  * outputs as theirs (draft_max, draft_argmax, draft_lse[max_pos] indexed by
- * pos_off[r] + i).  draft_dtype may differ from dtype.  Uses the workspace's
- * status word only. */
+ * pos_off[r] + i).  draft_dtype may differ from dtype.  A bf16 row without a
+ * cut is streamed in parts by several blocks; the block that finishes a row
+ * last merges them (part records and per-row arrival counts in the workspace,
+ * the counts back at zero when the call ends).  Uses the workspace's status
+ * word, part records and arrival counts. */
 int32_t sv_verify_rows_dense(const void* tgt_logits, int32_t dtype, int64_t tgt_ld, int32_t V,
                              const int32_t* tgt_off, int32_t R, int32_t max_rows, const float* temperature,
                              const float* top_p, float* row_max, int32_t* row_argmax, double* row_lse,
