@@ -378,7 +378,7 @@ def main():
                                     sp)
         else:  # target rows (statistics, top-p) and component rows (branch argmax) in one launch
             sv.sv_verify_rows(tg, dt, ld, V, tgt_off, R, max_rows, T, top_p, row_max, row_arg, row_lse, row_cut,
-                              row_kept, pr, ld, K, b, pos_off, max_pos, branch_T, ws, nb, sp)
+                              row_kept, pr, ld, K, b, pos_off, max_pos, x_all[s], branch_T, ws, nb, sp)
         if ev is not None:
             ev[1].record(stream)
         # (mixture: category posterior), acceptance, residual / bonus draw

@@ -331,8 +331,21 @@ struct DrawRec {
   double invT, kept, dlse;
   double invTb;      // soft branches: 1 / T_b
   int32_t ctok[64];  // greedy-branch residual: the distinct branch tokens at the slot
-  double cw[64];     // and their draw weight max(0, p - q); soft: lse_z - log w_z per branch z
-  double cp[64];     // greedy-branch residual: p at those tokens
+  double cw[64];     // soft: lse_z - log w_z per branch z
+  double cq[64];     // greedy-branch residual: q at those tokens (the summed weights of
+                     // the branches on each); the draw weight there is max(0, p - q)
+};
+
+// What the fused rows launch leaves for the draw, per request r and target row
+// j <= L_r, at slot r * (b + 1) + j: the row's statistics and, for j < L_r,
+// the target logit at draft token j (as fp32), so that the draw reads them by
+// request and position without first reading the row offsets.
+struct SlotRec {
+  double kept;
+  float cut;
+  int32_t argmax;
+  float lx;
+  int32_t pad;
 };
 
 // ------------------------------------------------------------------ branch argmax parts
@@ -375,7 +388,7 @@ struct RowPart {
 // through in-kernel fences: a device-scope release on gfx950 writes back the
 // L2, which is far too costly to pay once per block.
 struct WsLayout {
-  size_t status, rec, sub, bkey, blse, barg, bmax, rpart, rcount, total;
+  size_t status, rec, sub, bkey, blse, barg, bmax, rpart, rcount, slot, total;
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -392,7 +405,8 @@ __host__ __device__ inline WsLayout ws_layout(int R, int b, int K, int V) {
   l.bmax = l.barg + align256(sizeof(int32_t) * kb);
   l.rpart = l.bmax + align256(sizeof(float) * kb);
   l.rcount = l.rpart + align256(sizeof(RowPart) * static_cast<size_t>(R) * (2 * b + 1) * kDenseMaxParts);
-  l.total = l.rcount + align256(sizeof(uint32_t) * static_cast<size_t>(R) * (2 * b + 1));
+  l.slot = l.rcount + align256(sizeof(uint32_t) * static_cast<size_t>(R) * (2 * b + 1));
+  l.total = l.slot + align256(sizeof(SlotRec) * static_cast<size_t>(R) * (b + 1));
   return l;
 }
 

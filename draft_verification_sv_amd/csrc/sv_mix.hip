@@ -382,10 +382,11 @@ extern "C" int32_t sv_verify_rows(const void* tgt_logits, int32_t dtype, int64_t
                                   const float* top_p, float* row_max, int32_t* row_argmax, double* row_lse,
                                   float* row_cut, double* row_kept_lse, const void* comp_logits, int64_t comp_ld,
                                   int32_t K, int32_t b, const int32_t* pos_off, int32_t max_pos,
-                                  const float* branch_T, void* ws, size_t ws_bytes, void* stream) {
+                                  const int32_t* draft_tok, const float* branch_T, void* ws, size_t ws_bytes,
+                                  void* stream) {
   if (!tgt_logits || !tgt_off || !temperature || !row_max || !row_argmax || !row_lse || !row_cut || !row_kept_lse)
     return SV_ERR_ARG;
-  if (!comp_logits || !pos_off || !ws) return SV_ERR_ARG;
+  if (!comp_logits || !pos_off || !draft_tok || !ws) return SV_ERR_ARG;
   if (R < 1 || V < 1 || K < 1 || K > 64 || b < 1 || b > 64 || max_rows < 0 || max_pos < 0) return SV_ERR_ARG;
   if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_ARG;
   if (tgt_ld < V || comp_ld < V || !rows_aligned(tgt_logits, dtype, tgt_ld) || !rows_aligned(comp_logits, dtype, comp_ld))
@@ -397,6 +398,9 @@ extern "C" int32_t sv_verify_rows(const void* tgt_logits, int32_t dtype, int64_t
   if (ws_bytes < l.total) return SV_ERR_WORKSPACE;
   RowArgs ra{tgt_logits, tgt_ld, V, tgt_off, 0, R, max_rows, temperature, top_p, row_max, row_argmax, row_lse,
              row_cut, row_kept_lse, status_word(ws)};
+  ra.slot = reinterpret_cast<SlotRec*>(static_cast<char*>(ws) + l.slot);
+  ra.gx = draft_tok;
+  ra.slot_b = b;
   MixArgs ma{comp_logits, comp_ld, V, K, b, nullptr, pos_off, R, max_pos, nullptr, nullptr,
              reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + l.bkey), kMixParts, nullptr, nullptr,
              status_word(ws)};

@@ -101,6 +101,14 @@ struct RowArgs {
   float* row_cut;        // NULL when only statistics are wanted
   double* row_kept_lse;  // NULL when only statistics are wanted
   uint32_t* status;
+  // Optional copies for the fused draw (row_off = the target offsets): row j
+  // of request r also goes to slot[r * (slot_b + 1) + j] (j <= slot_b), with
+  // the logit at draft token gx[r * slot_b + j] for j < L_r.  slot_at: the
+  // slot of the block's row (set per block; -1: none).
+  SlotRec* slot;
+  const int32_t* gx;
+  int slot_b;
+  int slot_at = -1;
 };
 
 template <int NT>
@@ -121,6 +129,12 @@ __device__ inline void write_row(const RowArgs& a, int p, float mx, int am, doub
   a.row_lse[p] = lse;
   if (a.row_cut) a.row_cut[p] = cut;
   if (a.row_kept_lse) a.row_kept_lse[p] = kept;
+  if (a.slot != nullptr && a.slot_at >= 0) {
+    SlotRec& sr = a.slot[a.slot_at];
+    sr.kept = kept;
+    sr.cut = cut;
+    sr.argmax = am;
+  }
 }
 
 __device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin) {
@@ -228,11 +242,12 @@ struct RowLoc {
   bool ok, topp_on;
   const void* rowp;
   float T, tp;
+  int r, j;  // request, and the row's index within it
 };
 
 template <int DT, int NT>
 __device__ __forceinline__ RowLoc row_locate(const RowArgs& a, int p, RowShared<NT>& sh) {
-  RowLoc l{false, false, nullptr, 0.0f, 1.0f};
+  RowLoc l{false, false, nullptr, 0.0f, 1.0f, -1, -1};
   const int tid = threadIdx.x;
   const int r = find_request<NT>(a.row_off, a.R, p, &sh.req);
   if (r < 0) {
@@ -240,6 +255,8 @@ __device__ __forceinline__ RowLoc row_locate(const RowArgs& a, int p, RowShared<
     return l;
   }
   const int j = p - a.row_off[r];
+  l.r = r;
+  l.j = j;
   if (a.row_stride > 0 && j >= a.row_stride) {
     if (tid == 0) raise_status(a.status, SV_ST_BAD_OFFSETS);
     return l;
@@ -264,7 +281,17 @@ __device__ __forceinline__ RowLoc row_locate(const RowArgs& a, int p, RowShared<
 template <int DT, int NT, int BATCH, bool kBatchCheck = true>
 __device__ void row_block(const RowArgs& a, int p, uint32_t* hist, RowShared<NT>& sh) {
   const RowLoc l = row_locate<DT, NT>(a, p, sh);
-  if (l.ok) row_stats_at<DT, NT, BATCH, kBatchCheck>(a, l.rowp, p, l.T, l.tp, l.topp_on, hist, sh);
+  if (!l.ok) return;
+  RowArgs s = a;  // the block's slot (uniform, so kept in scalar registers)
+  const bool slotted = a.slot != nullptr && l.j >= 0 && l.j <= a.slot_b;
+  s.slot_at = slotted ? __builtin_amdgcn_readfirstlane(l.r * (a.slot_b + 1) + l.j) : -1;
+  row_stats_at<DT, NT, BATCH, kBatchCheck>(s, l.rowp, p, l.T, l.tp, l.topp_on, hist, sh);
+  // the logit at the draft token, by the last wave (the first to finish its
+  // part of the statistics), after the streaming
+  if (slotted && threadIdx.x == NT - 1 && l.j < a.slot_b && l.j < a.row_off[l.r + 1] - a.row_off[l.r] - 1) {
+    const int x = a.gx[static_cast<size_t>(l.r) * a.slot_b + l.j];
+    a.slot[s.slot_at].lx = load_val<DT>(l.rowp, x >= 0 && x < a.V ? x : 0);  // the draw reports a bad token
+  }
 }
 
 // ------------------------------------------------------------------ bf16 streaming path (no cut)

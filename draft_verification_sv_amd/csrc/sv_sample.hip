@@ -138,8 +138,8 @@ struct DrawCtx {
   double invT, kept, dlse, invTb;
   int64_t trow, drow;
   int ctok[64];
-  double cp[64];  // p at ctok
-  double cw[64];  // draw weight at ctok
+  double cq[64];  // greedy-branch residual: q at ctok
+  double cw[64];  // soft branches: lse_z - log w_z per branch z
 };
 
 struct TailShared {
@@ -178,11 +178,12 @@ struct DLists {
 };
 
 // Mixture residual at the draw slot (wave 0): lane z < K holds branch z (whether
-// it is consistent with the accepted prefix, its token v, its posterior weight
-// w and the target probability p at v).  q(v) is the summed weight of the
-// branches with token v; the draw weight at v is max(0, p(v) - q(v)); every
-// other token keeps p.  The distinct tokens go to c.ctok in lane order.
-__device__ __forceinline__ void build_corrections(DrawCtx& c, int K, bool act, int v, double w, double p) {
+// it is consistent with the accepted prefix, its token v and its posterior
+// weight w).  q(v) is the summed weight of the branches with token v; the draw
+// weight at v is max(0, p(v) - q(v)), formed by the kernels that read v's
+// logit with the rest of its sub-chunk; every other token keeps p.  The
+// distinct tokens and their q go to c.ctok, c.cq in lane order.
+__device__ __forceinline__ void build_corrections(DrawCtx& c, int K, bool act, int v, double w) {
   const int lane = threadIdx.x & (kWave - 1);
   const int va = act ? v : -1;
   const double wa = act ? w : 0.0;
@@ -199,10 +200,8 @@ __device__ __forceinline__ void build_corrections(DrawCtx& c, int K, bool act, i
   const uint64_t fm = __ballot(first);
   if (first) {
     const int idx = __popcll(fm & ((1ull << lane) - 1ull));
-    const double d = p - q;
     c.ctok[idx] = v;
-    c.cp[idx] = p;
-    c.cw[idx] = d > 0.0 ? d : 0.0;
+    c.cq[idx] = q;
   }
   if (lane == 0) c.ncorr = __popcll(fm);
 }
@@ -219,7 +218,7 @@ __device__ __forceinline__ void write_record(const SampleArgs& a, int r, const D
   if (lane < c.ncorr) {
     d.ctok[lane] = c.ctok[lane];
     d.cw[lane] = c.cw[lane];
-    d.cp[lane] = c.cp[lane];
+    d.cq[lane] = c.cq[lane];
   }
 }
 
@@ -233,6 +232,24 @@ __device__ __forceinline__ void posterior_mass(const TailShared& sh, int K, int 
     const int fz = sh.f[z];
     Ai += fz >= i ? pz : 0.0;
     Ai1 += fz > i ? pz : 0.0;
+  }
+}
+
+// Value e (0..7) of the 8-value group that lane src of the wave loaded as raw
+// words (w0, w1 as raw8 loads them); every lane of the wave calls it.
+template <int DT>
+__device__ __forceinline__ float value_from_lane(const uint4& w0, const uint4& w1, int src, int e) {
+  const uint32_t a0 = __shfl(w0.x, src), a1 = __shfl(w0.y, src), a2 = __shfl(w0.z, src), a3 = __shfl(w0.w, src);
+  if constexpr (DT == SV_BF16) {
+    const int wi = e >> 1;
+    const uint32_t w = wi == 0 ? a0 : wi == 1 ? a1 : wi == 2 ? a2 : a3;
+    return (e & 1) ? bf16_hi(w) : bf16_lo(w);
+  } else {
+    const uint32_t b0 = __shfl(w1.x, src), b1 = __shfl(w1.y, src), b2 = __shfl(w1.z, src), b3 = __shfl(w1.w, src);
+    const int wi = e & 3;
+    const uint32_t lo = wi == 0 ? a0 : wi == 1 ? a1 : wi == 2 ? a2 : a3;
+    const uint32_t hi = wi == 0 ? b0 : wi == 1 ? b1 : wi == 2 ? b2 : b3;
+    return __uint_as_float(e < 4 ? lo : hi);
   }
 }
 
@@ -268,15 +285,21 @@ __device__ __forceinline__ void sub_sums(const SampleArgs& a, const DrawCtx& c, 
   }
   // corrections of the mixture residual: lane t < ncorr holds branch token t
   const int ctok = mix_res && lane < c.ncorr ? c.ctok[lane] : -1;
-  const double cdel = mix_res && lane < c.ncorr ? c.cw[lane] - c.cp[lane] : 0.0;
-  // one sub-chunk's two sums, the branch-token corrections added, by lane 0
-  auto publish = [&](int sub, double sp, double sw) {
+  const double cq = mix_res && lane < c.ncorr ? c.cq[lane] : 0.0;
+  // one sub-chunk (the k-th of the wave)'s two sums, the branch-token
+  // corrections added, by lane 0
+  auto publish = [&](int sub, int k, double sp, double sw) {
     const double tp = wave_sum_f64(sp);
     double tw = dense_res ? wave_sum_f64(sw) : tp;
     if (mix_res) {  // branch tokens in this sub-chunk: weight max(0, p - q) instead of p
       const int v0 = sub * kLen;
-      const bool here = ctok >= v0 && ctok < v0 + kLen;
-      if (__ballot(here)) tw += wave_sum_f64(here ? cdel : 0.0);
+      const bool here = ctok >= v0 && ctok < v0 + kLen && ctok < V;
+      if (__ballot(here)) {  // p at the token, from the lane that loaded its group
+        const int o = here ? ctok - v0 : 0;
+        const double p = p_of(value_from_lane<DT>(t0[k], t1[k], o >> 3, o & 7), cut, invT, kept, tab);
+        const double d = p - cq;
+        tw += wave_sum_f64(here ? (d > 0.0 ? d : 0.0) - p : 0.0);
+      }
     }
     if (lane == 0) {
       double* pp = a.sub + (static_cast<size_t>(r) * a.NSUB + sub) * 2;
@@ -305,7 +328,7 @@ __device__ __forceinline__ void sub_sums(const SampleArgs& a, const DrawCtx& c, 
           sw += t > 0.0 ? t : 0.0;
         }
       }
-      publish(sub, sp, sw);
+      publish(sub, k, sp, sw);
     }
     return;
   }
@@ -364,7 +387,7 @@ __device__ __forceinline__ void sub_sums(const SampleArgs& a, const DrawCtx& c, 
     for (int j = 0; j < kL; ++j) {
       const int sub = sub0 + (k0 + j) * (kSumNT / kWave);
       if (sub >= a.NSUB) break;  // wave-uniform
-      publish(sub, sp[j], sw[j]);
+      publish(sub, k0 + j, sp[j], sw[j]);
     }
   }
 }
@@ -375,11 +398,9 @@ __device__ __forceinline__ void sub_sums(const SampleArgs& a, const DrawCtx& c, 
 template <int DT, int DDT, bool kDense, bool kAccept>
 __global__ __launch_bounds__(kSumNT) void k_draw_sums(SampleArgs a) {
   __shared__ TailShared sh;
-  // dynamic LDS: the mixture's branch tokens [K][b] and the target
-  // probabilities at them [K][b] (double) through phase C, then D's lists
+  // dynamic LDS: the mixture's branch tokens [K][b] through phase C, then D's lists
   extern __shared__ __align__(16) int dyn[];
   int* g = dyn;
-  double* gp = reinterpret_cast<double*>(dyn + ((a.K * a.b + 1) & ~1));
   const int r = blockIdx.x / a.S, ch = blockIdx.x % a.S;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
   const bool report = ch == 0;
@@ -388,7 +409,10 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums(SampleArgs a) {
 
   // A. the request header (uniform: scalar loads) and the draft tokens, mixing
   // logits and branch tokens (one per thread, clamped in-bounds), all issued
-  // before any is used; the offsets are checked after the barrier
+  // before any is used; the offsets are checked after the barrier.  With the
+  // mixture, also the statistics of target row i = thread (i <= b, clamped)
+  // and the logit at its draft token, from the rows launch's slot records:
+  // they need no offset, so no load waits for another.
   const int pb = a.pos_off[r], pe = a.pos_off[r + 1], tb = a.tgt_off[r], te = a.tgt_off[r + 1];
   const float T = a.T[r];
   const int nin = kAccept ? 0 : a.n_acc_in[r];
@@ -398,12 +422,22 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums(SampleArgs a) {
 #pragma unroll
   for (int q = 0; q < kMixParts; ++q) k0[q] = 0;
   const uint64_t* kr = a.bkey + static_cast<size_t>(r) * K * b * kMixParts;
+  float s_cut = 0.0f, s_lx = 0.0f;
+  double s_kept = 0.0;
+  int s_arg = 0;
+  uint64_t seed = 0;
   if (kAccept) {
     x0 = a.x[static_cast<size_t>(r) * b + min(tid, b - 1)];
     if (!kDense) {
       m0 = a.mix[static_cast<size_t>(r) * K + min(tid, K - 1)];
 #pragma unroll
       for (int q = 0; q < kMixParts; ++q) k0[q] = kr[static_cast<size_t>(min(tid, K * b - 1)) * kMixParts + q];
+      const SlotRec& sr = a.slot[static_cast<size_t>(r) * (b + 1) + min(tid, b)];
+      s_cut = sr.cut;
+      s_kept = sr.kept;
+      s_arg = sr.argmax;
+      s_lx = sr.lx;
+      seed = *a.seed;
     }
   }
   asm volatile("" ::: "memory");  // the compiler keeps every load above ahead of what follows
@@ -442,46 +476,42 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums(SampleArgs a) {
   const double invT = 1.0 / static_cast<double>(T);
 
   if (kAccept) {
-    // B. row statistics of the candidate rows, values at the draft and branch
-    // tokens (clamped in-bounds, all issued together); f_z by LDS atomicMin.
-    // Thread i (< L_r) keeps p(x_i), the dense q(x_i) and u_i in registers for
-    // phase C; wave 1 forms q(z | y).
+    // B. dense: row statistics of the candidate rows and the values at the
+    // draft tokens (clamped in-bounds, all issued together).  Mixture: the
+    // slot records of phase A; f_z by LDS atomicMin.  Thread i (< L_r) keeps
+    // p(x_i), the dense q(x_i) and u_i in registers for phase C; wave 1 forms
+    // q(z | y).
     const int is = min(tid, Lr);
-    const float rc0 = a.row_cut[tb + is];
-    const double rk0 = a.row_kept[tb + is];
-    const int ra0 = a.row_argmax[tb + is];
     const int il = min(tid, Lr > 0 ? Lr - 1 : 0);
-    const int xl = sh.x[il];
+    const int xl = kDense ? sh.x[il] : x0;  // mixture: thread i < L_r loaded x_i itself
     const bool xok = xl >= 0 && xl < V;
     const int xc = xok ? xl : 0;
-    const uint32_t lx0 = raw1<DT>(row_ptr(a.tgt, DT, tb + il, a.tgt_ld), xc);
+    float rc0 = s_cut, lxv = s_lx;
+    double rk0 = s_kept;
+    int ra0 = s_arg;
     uint32_t dx0 = 0;
     double dl0 = 0.0;
     int da0 = 0;
-    if (kDense && Lr > 0) {
-      dx0 = raw1<DDT>(row_ptr(a.draft, DDT, static_cast<int64_t>(r) * b + il, a.draft_ld), xc);
-      dl0 = a.dlse[pb + il];
-      da0 = a.dargmax[pb + il];
+    if constexpr (kDense) {
+      rc0 = a.row_cut[tb + is];
+      rk0 = a.row_kept[tb + is];
+      ra0 = a.row_argmax[tb + is];
+      const uint32_t lx0 = raw1<DT>(row_ptr(a.tgt, DT, tb + il, a.tgt_ld), xc);
+      if (Lr > 0) {
+        dx0 = raw1<DDT>(row_ptr(a.draft, DDT, static_cast<int64_t>(r) * b + il, a.draft_ld), xc);
+        dl0 = a.dlse[pb + il];
+        da0 = a.dargmax[pb + il];
+      }
+      seed = *a.seed;  // last: it is moved to scalar registers at once
+      asm volatile("" ::: "memory");  // every load above is issued before the stores below
+      lxv = raw_f32<DT>(lx0);
     }
     const int KL = K * Lr, Lq = Lr > 0 ? Lr : 1;
-    int gz = 0, gi = 0;
-    bool gok = false;
-    uint32_t gl0 = 0;
-    float grc = 0.0f;
-    double grk = 0.0;
     if (!kDense) {  // clamped in-bounds also when K * L_r = 0
       const int k = min(tid, KL > 0 ? KL - 1 : 0);
-      gz = k / Lq;
-      gi = k - gz * Lq;
-      const int v = g[gz * b + gi];
-      gok = v >= 0 && v < V;
-      gl0 = raw1<DT>(row_ptr(a.tgt, DT, tb + gi, a.tgt_ld), gok ? v : 0);
-      grc = a.row_cut[tb + gi];  // the row's statistics again, for p at this branch token
-      grk = a.row_kept[tb + gi];
-      if (tid < KL && v != sh.x[gi]) atomicMin(&sh.f[gz], gi);
+      const int gz = k / Lq, gi = k - gz * Lq;
+      if (tid < KL && g[gz * b + gi] != sh.x[gi]) atomicMin(&sh.f[gz], gi);
     }
-    const uint64_t seed = *a.seed;  // last: it is moved to scalar registers at once
-    asm volatile("" ::: "memory");  // every load above is issued before the stores below
     if (!kDense && report)  // the merged branch argmax, i < L_r
       for (int k = tid; k < K * b; k += kSumNT)
         if (k % b < Lr) a.branch_out[static_cast<size_t>(r) * K * b + k] = g[k];
@@ -491,17 +521,9 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums(SampleArgs a) {
       sh.ra[tid] = ra0;
     }
     if (!kDense) {
-      // p at every branch token of every candidate slot (used at the draw slot)
-      if (tid < KL && !greedy) gp[gz * b + gi] = gok ? p_of(raw_f32<DT>(gl0), grc, invT, grk, sh.etab) : 0.0;
       for (int k = tid + kSumNT; k < KL; k += kSumNT) {  // K * L_r > kSumNT only
         const int z = k / Lr, i = k - z * Lr;
-        const int v = g[z * b + i];
-        const bool ok = v >= 0 && v < V;
-        if (v != sh.x[i]) atomicMin(&sh.f[z], i);
-        if (!greedy)
-          gp[z * b + i] = ok ? p_of(load_val<DT>(row_ptr(a.tgt, DT, tb + i, a.tgt_ld), v), a.row_cut[tb + i], invT,
-                                    a.row_kept[tb + i], sh.etab)
-                             : 0.0;
+        if (g[z * b + i] != sh.x[i]) atomicMin(&sh.f[z], i);
       }
       if (wv == 1) {  // q(z | y) = softmax of the mixing logits
         const bool act = lane < K;
@@ -517,7 +539,7 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums(SampleArgs a) {
     if (tid < kWave) {
       u = u24(philox_at(seed, static_cast<uint32_t>(lane), static_cast<uint32_t>(r)).x);
       if (pos && xok) {
-        p = greedy ? (xl == ra0 ? 1.0 : 0.0) : p_of(raw_f32<DT>(lx0), rc0, invT, rk0, sh.etab);
+        p = greedy ? (xl == ra0 ? 1.0 : 0.0) : p_of(lxv, rc0, invT, rk0, sh.etab);
         if (kDense)
           qd = greedy ? (xl == da0 ? 1.0 : 0.0) : exp_tab(static_cast<double>(raw_f32<DDT>(dx0)) * invT - dl0, sh.etab);
       }
@@ -568,8 +590,7 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums(SampleArgs a) {
         const double An = bcast_f64(A, n);
         const int f = lane < K ? min(sh.f[lane], Lr) : -1;
         const bool act = lane < K && f >= n;
-        build_corrections(c, K, act, act ? g[lane * b + n] : -1, act ? sh.pi[lane] / An : 0.0,
-                          act ? gp[lane * b + n] : 0.0);
+        build_corrections(c, K, act, act ? g[lane * b + n] : -1, act ? sh.pi[lane] / An : 0.0);
       }
       __syncwarp();
       if (report) write_record(a, r, c);
@@ -616,9 +637,7 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums(SampleArgs a) {
         const bool in = lane < K;
         const int v = in ? sh.tv[lane] : -1;
         const double w = in ? sh.tw[lane] : 0.0;
-        const bool act = in && w > 0.0 && v >= 0 && v < V;
-        const float lv = act ? load_val<DT>(row_ptr(a.tgt, DT, tb + n, a.tgt_ld), v) : -INFINITY;
-        build_corrections(c, K, act, v, w, act ? p_of(lv, c.cut, c.invT, c.kept, sh.etab) : 0.0);
+        build_corrections(c, K, in && w > 0.0 && v >= 0 && v < V, v, w);
       }
       __syncwarp();
       if (report) write_record(a, r, c);
@@ -1007,9 +1026,7 @@ __global__ __launch_bounds__(kSumNT) void k_soft_head(SampleArgs a) {
         if (lane == 0) c.ncorr = K;
       } else {
         const int v = in ? g[lane * b + n] : -1;
-        const bool act = in && w > 0.0 && v >= 0 && v < V;
-        const float lv = act ? load_val<DT>(row_ptr(a.tgt, DT, tb + n, a.tgt_ld), v) : -INFINITY;
-        build_corrections(c, K, act, v, w, act ? p_of(lv, sh.rc[n], invT, sh.rk[n], sh.etab) : 0.0);
+        build_corrections(c, K, in && w > 0.0 && v >= 0 && v < V, v, w);
       }
     }
     __syncwarp();
@@ -1041,7 +1058,7 @@ __global__ __launch_bounds__(kSumNT) void k_soft_body(SampleArgs a) {
     if (lane < nc) {
       c.ctok[lane] = d.ctok[lane];
       c.cw[lane] = d.cw[lane];
-      c.cp[lane] = d.cp[lane];
+      c.cq[lane] = d.cq[lane];
     }
   }
   __syncthreads();
@@ -1087,7 +1104,7 @@ __global__ __launch_bounds__(kWave) void k_pick(SampleArgs a) {
     cp_[k] = subp[2 * s + 1];
   }
   const int ctok = kDense ? -1 : rec.ctok[lane];
-  const double cwt = kDense ? 0.0 : rec.cw[lane];
+  const double cqt = kDense ? 0.0 : rec.cq[lane];
   asm volatile("" ::: "memory");  // every load above is issued before any is used
   __shared__ double etab[kExpTab];
   __shared__ __align__(16) char plists[kSoft ? SoftLists::kPerWave : 16];  // soft residual: the nucleus list
@@ -1228,13 +1245,16 @@ __global__ __launch_bounds__(kWave) void k_pick(SampleArgs a) {
       }
       w8[q] = w;
     }
-    if (!kDense && !use_p) {
+    if (!kDense && !use_p) {  // branch tokens: max(0, p - q)
       for (int t2 = 0; t2 < nc; ++t2) {
         const int v = bcast_i32(ctok, t2);
-        const double wv = bcast_f64(cwt, t2);
+        const double qv = bcast_f64(cqt, t2);
 #pragma unroll
         for (int q = 0; q < 8; ++q)
-          if (v == g * 8 + q) w8[q] = wv;
+          if (v == g * 8 + q) {
+            const double d = w8[q] - qv;
+            w8[q] = d > 0.0 ? d : 0.0;
+          }
       }
     }
   }
@@ -1513,6 +1533,7 @@ extern "C" int32_t sv_accept_sample(const void* tgt_logits, int32_t dtype, int64
                              ws);
   a.x = draft_tok; a.K = q_mode == SV_Q_MIXTURE ? K : 0; a.mix = mix_logits; a.branch_out = branch_tok;
   a.bkey = reinterpret_cast<const uint64_t*>(static_cast<char*>(ws) + l.bkey);
+  a.slot = reinterpret_cast<const SlotRec*>(static_cast<char*>(ws) + l.slot);
   a.post_w = post_w; a.q_at_draft = q_at_draft; a.n_acc = n_acc; a.n_acc_in = n_acc; a.token = token;
   a.is_bonus = is_bonus; a.p_out = p_out; a.q_out = q_out; a.u_out = u_out;
   if (soft) {

@@ -163,7 +163,7 @@ class VerifyStep:
         sv_verify_rows(tgt, self.dt, tgt_ld, self.V, self.tgt_off, self.R, self.max_rows, self.T,
                        self.top_p if self.use_topp else None, self.row_max, self.row_argmax, self.row_lse,
                        self.row_cut, self.row_kept, comp, comp_ld, self.K, self.b, self.pos_off, self.max_pos,
-                       self.branch_T, self.ws, self.ws_bytes, stream)
+                       self.x, self.branch_T, self.ws, self.ws_bytes, stream)
 
     def run_rows_dense(self, tgt, tgt_ld, draft, draft_ld, stream=None):
         """Target rows and the dense draft's rows in one launch."""

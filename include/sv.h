@@ -213,6 +213,11 @@ int32_t sv_mixture_q(const void* comp_logits, int32_t dtype, int64_t ld, int32_t
  * parts into branch_tok and forms the category posterior.  Arguments as in
  * those two calls (one dtype).  Same method and pages as sv_topp_threshold and
  * sv_mixture_q.
+ *   draft_tok[R*b]  the draft tokens (as for sv_accept_sample): the block of
+ *                target row j < L_r of request r also keeps the target logit
+ *                at draft token j, and every target row's statistics, by
+ *                request and position in the workspace, so that the draw of
+ *                sv_accept_sample reads them without first reading tgt_off.
  *   branch_T[R]  soft branches [DBLast, "What carries the argument": each
  *                branch is a distribution q_i(. | y, z)], here
  *                softmax(c / T_b,r) (float, device): each component row is
@@ -230,7 +235,8 @@ int32_t sv_verify_rows(const void* tgt_logits, int32_t dtype, int64_t tgt_ld, in
                        const float* top_p, float* row_max, int32_t* row_argmax, double* row_lse,
                        float* row_cut, double* row_kept_lse, const void* comp_logits, int64_t comp_ld,
                        int32_t K, int32_t b, const int32_t* pos_off, int32_t max_pos,
-                       const float* branch_T, void* ws, size_t ws_bytes, void* stream);
+                       const int32_t* draft_tok, const float* branch_T, void* ws, size_t ws_bytes,
+                       void* stream);
 
 /* sv_verify_rows_dense: sv_topp_threshold over the packed target rows (row_off
  * = tgt_off, row_stride 0) and sv_softmax_stats over the dense draft's rows
@@ -340,7 +346,10 @@ int32_t sv_residual_sample_noalloc(const void* tgt_logits, int32_t dtype, int64_
  * q_at_draft), then sv_accept and sv_residual_sample (n_acc, token, is_bonus;
  * optional p_out, q_out, u_out as in sv_accept).  Same method and pages as
  * those calls.  Every chunk block of the draw recomputes its request's
- * posterior and acceptance, so no block waits for another.  SV_Q_DENSE takes
+ * posterior and acceptance, so no block waits for another.  With greedy
+ * branches the target rows' statistics (row_argmax, row_cut, row_kept_lse)
+ * and the target logit at each draft token are read from the copies the
+ * preceding sv_verify_rows left in the workspace (the same values).  SV_Q_DENSE takes
  * the draft arguments of sv_accept; K, mix_logits, branch_tok, post_w,
  * q_at_draft may then be NULL.
  *   branch_T[R], comp_logits, comp_ld  soft branches (NULL: greedy; then
