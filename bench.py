@@ -374,8 +374,8 @@ def main():
             ev[0].record(stream)
         if dense:  # target-row and draft-row statistics in one launch
             sv.sv_verify_rows_dense(tg, dt, ld, V, tgt_off, R, max_rows, T, top_p, row_max, row_arg, row_lse,
-                                    row_cut, row_kept, pr, dt, ld, b, pos_off, max_pos, d_max, d_arg, d_lse, ws, nb,
-                                    sp)
+                                    row_cut, row_kept, pr, dt, ld, b, pos_off, max_pos, x_all[s], d_max, d_arg,
+                                    d_lse, ws, nb, sp)
         else:  # target rows (statistics, top-p) and component rows (branch argmax) in one launch
             sv.sv_verify_rows(tg, dt, ld, V, tgt_off, R, max_rows, T, top_p, row_max, row_arg, row_lse, row_cut,
                               row_kept, pr, ld, K, b, pos_off, max_pos, x_all[s], branch_T, ws, nb, sp)

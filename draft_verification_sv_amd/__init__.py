@@ -83,7 +83,7 @@ _SIGS = {
                        _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _sz, _vp],
     "sv_selftest_exp": [_vp, _vp, _i32, _vp],
     "sv_verify_rows_dense": [_vp, _i32, _i64, _i32, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
-                             _i64, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _sz, _vp],
+                             _i64, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "sv_verify_rows": [_vp, _i32, _i64, _i32, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32,
                        _i32, _vp, _i32, _vp, _vp, _vp, _sz, _vp],
     "sv_accept_sample": [_vp, _i32, _i64, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i64,
@@ -206,12 +206,12 @@ def sv_verify_rows(tgt_logits, dtype, tgt_ld, V, tgt_off, R, max_rows, temperatu
 
 def sv_verify_rows_dense(tgt_logits, dtype, tgt_ld, V, tgt_off, R, max_rows, temperature, top_p, row_max,
                          row_argmax, row_lse, row_cut, row_kept_lse, draft_logits, draft_dtype, draft_ld, b, pos_off,
-                         max_pos, draft_max, draft_argmax, draft_lse, ws, ws_bytes, stream=None):
+                         max_pos, draft_tok, draft_max, draft_argmax, draft_lse, ws, ws_bytes, stream=None):
     _check(_lib.sv_verify_rows_dense(_p(tgt_logits), dtype, tgt_ld, V, _p(tgt_off), R, max_rows, _p(temperature),
                                      _p(top_p), _p(row_max), _p(row_argmax), _p(row_lse), _p(row_cut),
                                      _p(row_kept_lse), _p(draft_logits), draft_dtype, draft_ld, b, _p(pos_off),
-                                     max_pos, _p(draft_max), _p(draft_argmax), _p(draft_lse), _p(ws), ws_bytes,
-                                     _stream(stream)), "sv_verify_rows_dense")
+                                     max_pos, _p(draft_tok), _p(draft_max), _p(draft_argmax), _p(draft_lse), _p(ws),
+                                     ws_bytes, _stream(stream)), "sv_verify_rows_dense")
 
 
 def sv_accept_sample(tgt_logits, dtype, tgt_ld, V, tgt_off, pos_off, R, b, temperature, row_argmax, row_cut,

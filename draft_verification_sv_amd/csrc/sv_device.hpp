@@ -336,10 +336,12 @@ struct DrawRec {
                      // the branches on each); the draw weight there is max(0, p - q)
 };
 
-// What the fused rows launch leaves for the draw, per request r and target row
+// What the fused rows launches leave for the draw, per request r and target row
 // j <= L_r, at slot r * (b + 1) + j: the row's statistics and, for j < L_r,
 // the target logit at draft token j (as fp32), so that the draw reads them by
-// request and position without first reading the row offsets.
+// request and position without first reading the row offsets.  The dense
+// draft's row for position j has a slot of its own (kept = its lse, argmax,
+// lx = its logit at the draft token).
 struct SlotRec {
   double kept;
   float cut;
@@ -388,7 +390,7 @@ struct RowPart {
 // through in-kernel fences: a device-scope release on gfx950 writes back the
 // L2, which is far too costly to pay once per block.
 struct WsLayout {
-  size_t status, rec, sub, bkey, blse, barg, bmax, rpart, rcount, slot, total;
+  size_t status, rec, sub, bkey, blse, barg, bmax, rpart, rcount, slot, dslot, total;
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -406,7 +408,8 @@ __host__ __device__ inline WsLayout ws_layout(int R, int b, int K, int V) {
   l.rpart = l.bmax + align256(sizeof(float) * kb);
   l.rcount = l.rpart + align256(sizeof(RowPart) * static_cast<size_t>(R) * (2 * b + 1) * kDenseMaxParts);
   l.slot = l.rcount + align256(sizeof(uint32_t) * static_cast<size_t>(R) * (2 * b + 1));
-  l.total = l.slot + align256(sizeof(SlotRec) * static_cast<size_t>(R) * (b + 1));
+  l.dslot = l.slot + align256(sizeof(SlotRec) * static_cast<size_t>(R) * (b + 1));
+  l.total = l.dslot + align256(sizeof(SlotRec) * static_cast<size_t>(R) * (b + 1));
   return l;
 }
 

@@ -86,6 +86,7 @@ struct SampleArgs {
   const int32_t* branch_tok;  // standalone draw: the branch argmax
   const uint64_t* bkey;       // fused tail: the partial argmax keys of the rows launch
   const SlotRec* slot;        // fused tail: the rows launch's statistics by (request, row)
+  const SlotRec* dslot;       // fused dense tail: the draft rows' lse, argmax and x logit by (request, position)
   int32_t* branch_out;        // fused tail: the branch argmax, written for i < L_r
   double* post_w;      // read by the standalone draw; written by the fused tail
   double* q_at_draft;  // written by the fused tail

@@ -89,12 +89,14 @@ __device__ __forceinline__ void stats_part(const RowArgs& a, int p, int part, in
   if (kCut) exp_table_init(sh.etab);  // published by row_locate's barriers
   const RowLoc l = row_locate<DT, NT>(a, p, sh);
   if (!l.ok) return;
+  const RowArgs s = with_slot(a, l);  // the row's slot record goes with its statistics
   RowPart* rec = parts + static_cast<size_t>(p) * P;
   const bool topp_on = kCut && l.topp_on;
   if (DT != SV_BF16 || topp_on) {
     if (part != 0) return;
-    row_stats_at<DT, NT, BATCH>(a, l.rowp, p, l.T, l.tp, topp_on, hist, sh);
+    row_stats_at<DT, NT, BATCH>(s, l.rowp, p, l.T, l.tp, topp_on, hist, sh);
     if (threadIdx.x == 0) rec[0].split = 0;
+    if (threadIdx.x == NT - 1) slot_gather<DT>(s, l);
     return;
   }
   const int nvec = a.V >> 3;
@@ -102,6 +104,7 @@ __device__ __forceinline__ void stats_part(const RowArgs& a, int p, int part, in
   const int v1 = static_cast<int>(static_cast<int64_t>(nvec) * (part + 1) / P);
   const StreamPart sp = stream_part_bf16<NT, BATCH>(static_cast<const uint16_t*>(l.rowp), a.V, v0, v1, part == P - 1,
                                                      l.T, a.status, sh);
+  if (part == 0 && threadIdx.x == NT - 1) slot_gather<DT>(s, l);  // a wave that is otherwise done
   if (threadIdx.x < kWave) {  // wave 0
     uint32_t arrived = 0;
     if (threadIdx.x == 0) {
@@ -118,7 +121,7 @@ __device__ __forceinline__ void stats_part(const RowArgs& a, int p, int part, in
     }
     if (__builtin_amdgcn_readfirstlane(arrived) == static_cast<uint32_t>(P - 1)) {  // the row's last part
       if (threadIdx.x == 0) __hip_atomic_store(count + p, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      merge_parts_wave(a, p, P, rec);
+      merge_parts_wave(s, p, P, rec);
     }
   }
 }
@@ -238,11 +241,11 @@ extern "C" int32_t sv_verify_rows_dense(const void* tgt_logits, int32_t dtype, i
                                         int32_t* row_argmax, double* row_lse, float* row_cut,
                                         double* row_kept_lse, const void* draft_logits, int32_t draft_dtype,
                                         int64_t draft_ld, int32_t b, const int32_t* pos_off, int32_t max_pos,
-                                        float* draft_max, int32_t* draft_argmax, double* draft_lse, void* ws,
-                                        size_t ws_bytes, void* stream) {
+                                        const int32_t* draft_tok, float* draft_max, int32_t* draft_argmax,
+                                        double* draft_lse, void* ws, size_t ws_bytes, void* stream) {
   if (!tgt_logits || !tgt_off || !temperature || !row_max || !row_argmax || !row_lse || !row_cut || !row_kept_lse)
     return SV_ERR_ARG;
-  if (!draft_logits || !pos_off || !draft_max || !draft_argmax || !draft_lse || !ws) return SV_ERR_ARG;
+  if (!draft_logits || !pos_off || !draft_tok || !draft_max || !draft_argmax || !draft_lse || !ws) return SV_ERR_ARG;
   if (R < 1 || V < 1 || b < 1 || b > 64 || max_rows < 0 || max_pos < 0 || tgt_ld < V || draft_ld < V)
     return SV_ERR_ARG;
   if ((dtype != SV_F32 && dtype != SV_BF16) || (draft_dtype != SV_F32 && draft_dtype != SV_BF16)) return SV_ERR_ARG;
@@ -268,6 +271,13 @@ extern "C" int32_t sv_verify_rows_dense(const void* tgt_logits, int32_t dtype, i
              row_cut, row_kept_lse, status_word(ws)};
   RowArgs da{draft_logits, draft_ld, V, pos_off, b, R, max_pos, temperature, nullptr, draft_max, draft_argmax,
              draft_lse, nullptr, nullptr, status_word(ws)};
+  // slot records for the draw: target rows (statistics, logit at the draft
+  // token) and draft rows (lse, argmax and logit at the draft token, in the
+  // fields kept, argmax and lx)
+  ta.slot = reinterpret_cast<SlotRec*>(static_cast<char*>(ws) + l.slot);
+  da.slot = reinterpret_cast<SlotRec*>(static_cast<char*>(ws) + l.dslot);
+  ta.gx = da.gx = draft_tok;
+  ta.slot_b = da.slot_b = b;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool t16 = dtype == SV_BF16, d16 = draft_dtype == SV_BF16;
   const int32_t st = t16 ? (d16 ? launch_dense<SV_BF16, SV_BF16>(ta, da, max_rows, P, tparts, dparts, tcount, dcount, grid, s)

@@ -101,10 +101,11 @@ struct RowArgs {
   float* row_cut;        // NULL when only statistics are wanted
   double* row_kept_lse;  // NULL when only statistics are wanted
   uint32_t* status;
-  // Optional copies for the fused draw (row_off = the target offsets): row j
-  // of request r also goes to slot[r * (slot_b + 1) + j] (j <= slot_b), with
-  // the logit at draft token gx[r * slot_b + j] for j < L_r.  slot_at: the
-  // slot of the block's row (set per block; -1: none).
+  // Optional copies for the fused draw: row j of request r also goes to
+  // slot[r * (slot_b + 1) + j] (j <= slot_b), with the logit at draft token
+  // gx[r * slot_b + j] when the row has one (target rows, row_stride 0: j <
+  // L_r; draft rows, row_stride b: every row).  slot_at: the slot of the
+  // block's row (set per block; -1: none).
   SlotRec* slot;
   const int32_t* gx;
   int slot_b;
@@ -278,20 +279,34 @@ __device__ __forceinline__ RowLoc row_locate(const RowArgs& a, int p, RowShared<
 
 // Statistics of row p (work item p of the request found from row_off), by one
 // block of NT threads.  `hist` holds kHistWords words of LDS (bf16 rows only).
+// a with the slot of the located row (uniform, so kept in scalar registers)
+__device__ __forceinline__ RowArgs with_slot(const RowArgs& a, const RowLoc& l) {
+  RowArgs s = a;
+  s.slot_at = a.slot != nullptr && l.j >= 0 && l.j <= a.slot_b
+                  ? __builtin_amdgcn_readfirstlane(l.r * (a.slot_b + 1) + l.j)
+                  : -1;
+  return s;
+}
+
+// The located row's logit at its draft token into its slot, if it has one
+// (one thread; the draw reports a bad token, which reads value 0 here).
+template <int DT>
+__device__ __forceinline__ void slot_gather(const RowArgs& s, const RowLoc& l) {
+  if (s.slot_at < 0 || l.j >= s.slot_b) return;
+  const int n = s.row_off[l.r + 1] - s.row_off[l.r] - (s.row_stride > 0 ? 0 : 1);  // rows with a draft token
+  if (l.j >= n) return;
+  const int x = s.gx[static_cast<size_t>(l.r) * s.slot_b + l.j];
+  s.slot[s.slot_at].lx = load_val<DT>(l.rowp, x >= 0 && x < s.V ? x : 0);
+}
+
 template <int DT, int NT, int BATCH, bool kBatchCheck = true>
 __device__ void row_block(const RowArgs& a, int p, uint32_t* hist, RowShared<NT>& sh) {
   const RowLoc l = row_locate<DT, NT>(a, p, sh);
   if (!l.ok) return;
-  RowArgs s = a;  // the block's slot (uniform, so kept in scalar registers)
-  const bool slotted = a.slot != nullptr && l.j >= 0 && l.j <= a.slot_b;
-  s.slot_at = slotted ? __builtin_amdgcn_readfirstlane(l.r * (a.slot_b + 1) + l.j) : -1;
+  const RowArgs s = with_slot(a, l);
   row_stats_at<DT, NT, BATCH, kBatchCheck>(s, l.rowp, p, l.T, l.tp, l.topp_on, hist, sh);
-  // the logit at the draft token, by the last wave (the first to finish its
-  // part of the statistics), after the streaming
-  if (slotted && threadIdx.x == NT - 1 && l.j < a.slot_b && l.j < a.row_off[l.r + 1] - a.row_off[l.r] - 1) {
-    const int x = a.gx[static_cast<size_t>(l.r) * a.slot_b + l.j];
-    a.slot[s.slot_at].lx = load_val<DT>(l.rowp, x >= 0 && x < a.V ? x : 0);  // the draw reports a bad token
-  }
+  // by the last wave (the first to finish its part of the statistics)
+  if (threadIdx.x == NT - 1) slot_gather<DT>(s, l);
 }
 
 // ------------------------------------------------------------------ bf16 streaming path (no cut)

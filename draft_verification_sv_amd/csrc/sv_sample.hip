@@ -409,10 +409,11 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums(SampleArgs a) {
 
   // A. the request header (uniform: scalar loads) and the draft tokens, mixing
   // logits and branch tokens (one per thread, clamped in-bounds), all issued
-  // before any is used; the offsets are checked after the barrier.  With the
-  // mixture, also the statistics of target row i = thread (i <= b, clamped)
-  // and the logit at its draft token, from the rows launch's slot records:
-  // they need no offset, so no load waits for another.
+  // before any is used; the offsets are checked after the barrier.  Also the
+  // statistics of target row i = thread (i <= b, clamped) and the logit at
+  // its draft token, and for a dense draft its row's lse, argmax and logit at
+  // the token, from the rows launch's slot records: they need no offset, so
+  // no load waits for another.
   const int pb = a.pos_off[r], pe = a.pos_off[r + 1], tb = a.tgt_off[r], te = a.tgt_off[r + 1];
   const float T = a.T[r];
   const int nin = kAccept ? 0 : a.n_acc_in[r];
@@ -422,9 +423,9 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums(SampleArgs a) {
 #pragma unroll
   for (int q = 0; q < kMixParts; ++q) k0[q] = 0;
   const uint64_t* kr = a.bkey + static_cast<size_t>(r) * K * b * kMixParts;
-  float s_cut = 0.0f, s_lx = 0.0f;
-  double s_kept = 0.0;
-  int s_arg = 0;
+  float s_cut = 0.0f, s_lx = 0.0f, s_dx = 0.0f;
+  double s_kept = 0.0, s_dl = 0.0;
+  int s_arg = 0, s_da = 0;
   uint64_t seed = 0;
   if (kAccept) {
     x0 = a.x[static_cast<size_t>(r) * b + min(tid, b - 1)];
@@ -432,13 +433,18 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums(SampleArgs a) {
       m0 = a.mix[static_cast<size_t>(r) * K + min(tid, K - 1)];
 #pragma unroll
       for (int q = 0; q < kMixParts; ++q) k0[q] = kr[static_cast<size_t>(min(tid, K * b - 1)) * kMixParts + q];
-      const SlotRec& sr = a.slot[static_cast<size_t>(r) * (b + 1) + min(tid, b)];
-      s_cut = sr.cut;
-      s_kept = sr.kept;
-      s_arg = sr.argmax;
-      s_lx = sr.lx;
-      seed = *a.seed;
+    } else {
+      const SlotRec& dr = a.dslot[static_cast<size_t>(r) * (b + 1) + min(tid, b - 1)];
+      s_dl = dr.kept;
+      s_da = dr.argmax;
+      s_dx = dr.lx;
     }
+    const SlotRec& sr = a.slot[static_cast<size_t>(r) * (b + 1) + min(tid, b)];
+    s_cut = sr.cut;
+    s_kept = sr.kept;
+    s_arg = sr.argmax;
+    s_lx = sr.lx;
+    seed = *a.seed;
   }
   asm volatile("" ::: "memory");  // the compiler keeps every load above ahead of what follows
   exp_table_init(sh.etab);
@@ -476,36 +482,14 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums(SampleArgs a) {
   const double invT = 1.0 / static_cast<double>(T);
 
   if (kAccept) {
-    // B. dense: row statistics of the candidate rows and the values at the
-    // draft tokens (clamped in-bounds, all issued together).  Mixture: the
-    // slot records of phase A; f_z by LDS atomicMin.  Thread i (< L_r) keeps
-    // p(x_i), the dense q(x_i) and u_i in registers for phase C; wave 1 forms
-    // q(z | y).
-    const int is = min(tid, Lr);
-    const int il = min(tid, Lr > 0 ? Lr - 1 : 0);
-    const int xl = kDense ? sh.x[il] : x0;  // mixture: thread i < L_r loaded x_i itself
+    // B. everything from phase A's loads (the slot records); mixture: f_z by
+    // LDS atomicMin.  Thread i (< L_r) keeps p(x_i), the dense q(x_i) and u_i
+    // in registers for phase C; wave 1 forms q(z | y).
+    const int xl = x0;  // thread i < L_r loaded x_i itself
     const bool xok = xl >= 0 && xl < V;
-    const int xc = xok ? xl : 0;
-    float rc0 = s_cut, lxv = s_lx;
-    double rk0 = s_kept;
-    int ra0 = s_arg;
-    uint32_t dx0 = 0;
-    double dl0 = 0.0;
-    int da0 = 0;
-    if constexpr (kDense) {
-      rc0 = a.row_cut[tb + is];
-      rk0 = a.row_kept[tb + is];
-      ra0 = a.row_argmax[tb + is];
-      const uint32_t lx0 = raw1<DT>(row_ptr(a.tgt, DT, tb + il, a.tgt_ld), xc);
-      if (Lr > 0) {
-        dx0 = raw1<DDT>(row_ptr(a.draft, DDT, static_cast<int64_t>(r) * b + il, a.draft_ld), xc);
-        dl0 = a.dlse[pb + il];
-        da0 = a.dargmax[pb + il];
-      }
-      seed = *a.seed;  // last: it is moved to scalar registers at once
-      asm volatile("" ::: "memory");  // every load above is issued before the stores below
-      lxv = raw_f32<DT>(lx0);
-    }
+    const float rc0 = s_cut, lxv = s_lx;
+    const double rk0 = s_kept, dl0 = s_dl;
+    const int ra0 = s_arg, da0 = s_da;
     const int KL = K * Lr, Lq = Lr > 0 ? Lr : 1;
     if (!kDense) {  // clamped in-bounds also when K * L_r = 0
       const int k = min(tid, KL > 0 ? KL - 1 : 0);
@@ -541,7 +525,7 @@ __global__ __launch_bounds__(kSumNT) void k_draw_sums(SampleArgs a) {
       if (pos && xok) {
         p = greedy ? (xl == ra0 ? 1.0 : 0.0) : p_of(lxv, rc0, invT, rk0, sh.etab);
         if (kDense)
-          qd = greedy ? (xl == da0 ? 1.0 : 0.0) : exp_tab(static_cast<double>(raw_f32<DDT>(dx0)) * invT - dl0, sh.etab);
+          qd = greedy ? (xl == da0 ? 1.0 : 0.0) : exp_tab(static_cast<double>(s_dx) * invT - dl0, sh.etab);
       }
       if (report && pos && !xok) raise_status(a.status, SV_ST_BAD_TOKEN);
     }
@@ -1534,6 +1518,7 @@ extern "C" int32_t sv_accept_sample(const void* tgt_logits, int32_t dtype, int64
   a.x = draft_tok; a.K = q_mode == SV_Q_MIXTURE ? K : 0; a.mix = mix_logits; a.branch_out = branch_tok;
   a.bkey = reinterpret_cast<const uint64_t*>(static_cast<char*>(ws) + l.bkey);
   a.slot = reinterpret_cast<const SlotRec*>(static_cast<char*>(ws) + l.slot);
+  a.dslot = reinterpret_cast<const SlotRec*>(static_cast<char*>(ws) + l.dslot);
   a.post_w = post_w; a.q_at_draft = q_at_draft; a.n_acc = n_acc; a.n_acc_in = n_acc; a.token = token;
   a.is_bonus = is_bonus; a.p_out = p_out; a.q_out = q_out; a.u_out = u_out;
   if (soft) {

@@ -170,7 +170,8 @@ class VerifyStep:
         sv_verify_rows_dense(tgt, self.dt, tgt_ld, self.V, self.tgt_off, self.R, self.max_rows, self.T,
                              self.top_p if self.use_topp else None, self.row_max, self.row_argmax, self.row_lse,
                              self.row_cut, self.row_kept, draft, self.dt, draft_ld, self.b, self.pos_off,
-                             self.max_pos, self.d_max, self.d_argmax, self.d_lse, self.ws, self.ws_bytes, stream)
+                             self.max_pos, self.x, self.d_max, self.d_argmax, self.d_lse, self.ws, self.ws_bytes,
+                             stream)
 
     def run_accept_sample(self, tgt, tgt_ld, *, draft=None, draft_ld=0, comp=None, comp_ld=0, stream=None):
         """Posterior (mixture), acceptance and the draw: two launches.  Soft

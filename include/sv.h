@@ -248,15 +248,18 @@ int32_t sv_verify_rows(const void* tgt_logits, int32_t dtype, int64_t tgt_ld, in
  * pos_off[r] + i).  draft_dtype may differ from dtype.  A bf16 row without a
  * cut is streamed in parts by several blocks; the block that finishes a row
  * last merges them (part records and per-row arrival counts in the workspace,
- * the counts back at zero when the call ends).  Uses the workspace's status
- * word, part records and arrival counts. */
+ * the counts back at zero when the call ends).  draft_tok[R*b]: the draft
+ * tokens (as for sv_accept_sample); the statistics of every target and draft
+ * row, and each row's logit at its draft token, are also kept by request and
+ * position in the workspace for the draw of sv_accept_sample.  Uses the
+ * workspace's status word, part records and arrival counts. */
 int32_t sv_verify_rows_dense(const void* tgt_logits, int32_t dtype, int64_t tgt_ld, int32_t V,
                              const int32_t* tgt_off, int32_t R, int32_t max_rows, const float* temperature,
                              const float* top_p, float* row_max, int32_t* row_argmax, double* row_lse,
                              float* row_cut, double* row_kept_lse, const void* draft_logits,
                              int32_t draft_dtype, int64_t draft_ld, int32_t b, const int32_t* pos_off,
-                             int32_t max_pos, float* draft_max, int32_t* draft_argmax, double* draft_lse,
-                             void* ws, size_t ws_bytes, void* stream);
+                             int32_t max_pos, const int32_t* draft_tok, float* draft_max, int32_t* draft_argmax,
+                             double* draft_lse, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------- acceptance */
 
@@ -347,9 +350,10 @@ int32_t sv_residual_sample_noalloc(const void* tgt_logits, int32_t dtype, int64_
  * optional p_out, q_out, u_out as in sv_accept).  Same method and pages as
  * those calls.  Every chunk block of the draw recomputes its request's
  * posterior and acceptance, so no block waits for another.  With greedy
- * branches the target rows' statistics (row_argmax, row_cut, row_kept_lse)
- * and the target logit at each draft token are read from the copies the
- * preceding sv_verify_rows left in the workspace (the same values).  SV_Q_DENSE takes
+ * branches or a dense draft the rows' statistics (row_argmax, row_cut,
+ * row_kept_lse; draft_argmax, draft_lse) and the logits at the draft tokens
+ * are read from the copies the preceding sv_verify_rows or
+ * sv_verify_rows_dense left in the workspace (the same values).  SV_Q_DENSE takes
  * the draft arguments of sv_accept; K, mix_logits, branch_tok, post_w,
  * q_at_draft may then be NULL.
  *   branch_T[R], comp_logits, comp_ld  soft branches (NULL: greedy; then

@@ -239,8 +239,9 @@ def test_dense_rows_edges(V):
     ro = [torch.zeros(R * n, dtype=x, **d) for x in (f32, i32, f64, f32, f64)]
     do = [torch.zeros(R * b, dtype=x, **d) for x in (f32, i32, f64)]
     banner(f"sv_verify_rows_dense edges V={V}")
+    x = torch.from_numpy(rng.integers(0, V, R * b, dtype=np.int32)).cuda()  # draft tokens (slot records)
     sv.sv_verify_rows_dense(dt, sv.SV_BF16, ld, V, tgt_off, R, R * n, torch.from_numpy(T).cuda(), None, *ro, dd,
-                            sv.SV_BF16, ld, b, pos_off, R * b, *do, ws, nb)
+                            sv.SV_BF16, ld, b, pos_off, R * b, x, *do, ws, nb)
     torch.cuda.synchronize()
     for got, rows_, per in ((ro, tgt, n), (do, dft, b)):
         o = oracle.row_stats_batch(rows_, np.repeat(np.arange(R), per), T)
@@ -297,6 +298,7 @@ def test_dense_rows_shapes(V, b, Ls):
     d = dict(device="cuda")
     tgt_off = torch.from_numpy(np.concatenate([[0], np.cumsum(L + 1)]).astype(np.int32)).cuda()
     pos_off = torch.from_numpy(np.concatenate([[0], np.cumsum(L)]).astype(np.int32)).cuda()
+    x = torch.from_numpy(rng.integers(0, V, R * b, dtype=np.int32)).cuda()  # draft tokens (slot records)
     ws, nb = sv.make_workspace(R, b, 0, V)
     f32, i32, f64 = torch.float32, torch.int32, torch.float64
     cap_t, cap_d = R * (b + 1), R * b
@@ -306,7 +308,7 @@ def test_dense_rows_shapes(V, b, Ls):
         do = [torch.zeros(cap_d, dtype=x, **d) for x in (f32, i32, f64)]
         banner(f"sv_verify_rows_dense V={V} R={R} rows {nt}+{nd} run {rep}")
         sv.sv_verify_rows_dense(dt, sv.SV_BF16, ld, V, tgt_off, R, cap_t, torch.from_numpy(T).cuda(), None, *ro, dd,
-                                sv.SV_BF16, ld, b, pos_off, cap_d, *do, ws, nb)
+                                sv.SV_BF16, ld, b, pos_off, cap_d, x, *do, ws, nb)
         torch.cuda.synchronize()
         runs.append([x.cpu().numpy() for x in ro[:3] + do[:3]])
     for a, c in zip(runs[0], runs[1]):
@@ -330,7 +332,7 @@ def test_dense_rows_shapes(V, b, Ls):
         ws2, nb2 = sv.make_workspace(R, b, 0, V)
         T2 = torch.ones(R, **d)
         sv.sv_verify_rows_dense(d2, sv.SV_BF16, ld, V, tgt_off, R, cap_t, T2, None, *ro, dd, sv.SV_BF16, ld, b,
-                                pos_off, cap_d, *do, ws2, nb2)
+                                pos_off, cap_d, x, *do, ws2, nb2)
         assert sv.sv_get_status(ws2) & 0x004, bad
 
 
