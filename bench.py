@@ -92,10 +92,21 @@ KERNEL_SOURCES = {
 TREE_TRAFFIC_KEY = "tree:k_row_stats"  # the tree step's node-row statistics launch
 
 
+def _code_only(text: str) -> str:
+    """A source file's code: comments, trailing spaces and blank lines removed,
+    so that a record stays tied to the code that was measured, not its comments."""
+    import re
+
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def kernel_source_hash(kernel: str) -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel]:
-        h.update(open(os.path.join(ROOT, "draft_verification_sv_amd", "csrc", f), "rb").read())
+        with open(os.path.join(ROOT, "draft_verification_sv_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

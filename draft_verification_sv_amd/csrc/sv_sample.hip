@@ -166,8 +166,8 @@ struct TailShared {
 // lane), so that exp runs over the pass's kept values with no idle slots.  The
 // lists share the dynamic LDS with the mixture's branch tables, which are dead
 // by then.  Dense proposals keep one sub-chunk per pass (two lists of it, p
-// and q): 18 KiB of lists, so that six blocks fit on a compute unit and a
-// cfg3-sized grid (1216 blocks) is resident at once; two sub-chunks per pass
+// and q): 18 KiB of lists, so that six blocks fit on a compute unit and the
+// grid of 32 requests at V = 151936 (1216 blocks) is resident at once; two sub-chunks per pass
 // took 34 KiB, four blocks per compute unit and a second round of blocks.
 template <bool kDense>
 struct DLists {
