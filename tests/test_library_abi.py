@@ -175,3 +175,32 @@ def test_one_hip_runtime_when_the_package_is_imported_first():
     assert out.returncode == 0, out.stderr
     paths = ast.literal_eval(out.stdout.strip().splitlines()[-1])
     assert len(paths) == 1, paths
+
+
+def _prototype_params(text: str, name: str) -> list:
+    """The parameter declarations of `name`'s prototype in the (comment-free) header."""
+    m = re.search(r"\b" + name + r"\s*\(", text)
+    assert m, name
+    depth, i = 1, m.end()
+    while depth:
+        depth += {"(": 1, ")": -1}.get(text[i], 0)
+        i += 1
+    body = " ".join(text[m.end():i - 1].split())
+    return [] if body in ("", "void") else [p.strip() for p in body.split(",")]
+
+
+def test_binding_signatures_match_header(sv):
+    """Every ctypes signature the binding sets has the header's parameter count
+    and, position by position, a matching kind: pointers for pointers, and the
+    same width for int32_t, int64_t and size_t."""
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "sv.h")).read(), flags=re.S)
+    scalar = {"int32_t": C.c_int32, "int64_t": C.c_int64, "size_t": C.c_size_t}
+    for name, args in sv._SIGS.items():
+        params = _prototype_params(text, name)
+        assert len(params) == len(args), f"{name}: header {len(params)} parameters, binding {len(args)}"
+        for k, (decl, ct) in enumerate(zip(params, args)):
+            if "*" in decl:
+                assert ct is C.c_void_p or issubclass(ct, C._Pointer), f"{name} parameter {k}: {decl} vs {ct}"
+            else:
+                base = decl.split()[0]
+                assert scalar.get(base) is ct, f"{name} parameter {k}: {decl} vs {ct}"
