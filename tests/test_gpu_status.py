@@ -162,15 +162,19 @@ def test_bad_block_lengths():
 
 
 @CHAINS
-def test_bad_draft_tokens(fused):
-    w = synth.config(5, V=1031, R=8, steps=1)
+@pytest.mark.parametrize("cfg", [5, 3], ids=["mixture", "dense"])
+def test_bad_draft_tokens(fused, cfg):
+    """Draft tokens outside the vocabulary in two requests (the rows launches
+    clamp them for their gathers; the draw reports them): the bit is set, and
+    the other requests match the oracle."""
+    w = synth.config(cfg, V=1031, R=8, steps=1)
     wg = copy.copy(w)
     wg.x = w.x.copy()
     wg.x[0, 2, 1], wg.x[0, 5, 0] = w.V + 3, -1
     wg.budget = w.R * w.b  # every position verified, so both tokens are read
     wo = copy.copy(w)
     wo.budget = wg.budget
-    banner(f"status BAD_TOKEN fused={fused}")
+    banner(f"status BAD_TOKEN config {cfg} fused={fused}")
     vs, g, st = _step(wg, fused)
     assert st & BAD_TOKEN, st
     assert_rate(compare_step(wo, g, oracle_step(wo, 0), skip={2, 5}))
