@@ -277,8 +277,6 @@ __device__ __forceinline__ RowLoc row_locate(const RowArgs& a, int p, RowShared<
   return l;
 }
 
-// Statistics of row p (work item p of the request found from row_off), by one
-// block of NT threads.  `hist` holds kHistWords words of LDS (bf16 rows only).
 // a with the slot of the located row (uniform, so kept in scalar registers)
 __device__ __forceinline__ RowArgs with_slot(const RowArgs& a, const RowLoc& l) {
   RowArgs s = a;
@@ -289,7 +287,8 @@ __device__ __forceinline__ RowArgs with_slot(const RowArgs& a, const RowLoc& l) 
 }
 
 // The located row's logit at its draft token into its slot, if it has one
-// (one thread; the draw reports a bad token, which reads value 0 here).
+// (one thread; a token outside the vocabulary reads element 0 here, and the
+// draw reports it).
 template <int DT>
 __device__ __forceinline__ void slot_gather(const RowArgs& s, const RowLoc& l) {
   if (s.slot_at < 0 || l.j >= s.slot_b) return;
@@ -299,6 +298,8 @@ __device__ __forceinline__ void slot_gather(const RowArgs& s, const RowLoc& l) {
   s.slot[s.slot_at].lx = load_val<DT>(l.rowp, x >= 0 && x < s.V ? x : 0);
 }
 
+// Statistics of row p (work item p of the request found from row_off), by one
+// block of NT threads.  `hist` holds kHistWords words of LDS (bf16 rows only).
 template <int DT, int NT, int BATCH, bool kBatchCheck = true>
 __device__ void row_block(const RowArgs& a, int p, uint32_t* hist, RowShared<NT>& sh) {
   const RowLoc l = row_locate<DT, NT>(a, p, sh);
